@@ -1,0 +1,367 @@
+"""CPU oracle for MLA latent-KV attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this module.  The HIP library never calls it and shares no code with
+it.  Everything here is plain float64 numpy (or pure Python loops for the
+brute-force form); it is slow on purpose and follows the pages' equations
+in their own order.
+
+Sources (page title, then the part of it followed):
+  [R2]  jiphyeonjeon.kr deep review "DeepSeek-V2: A Strong, Economical, and
+        Efficient Mixture-of-Experts Language Model", section 2 -- joint
+        low-rank compression c^KV = W^DKV h, k^C = W^UK c^KV, v^C = W^UV c^KV;
+        the absorption identity (q^C)^T U^K_i c = ((U^K_i)^T q^C)^T c and
+        sum_j a_ij U^V_i c_j = U^V_i sum_j a_ij c_j.
+  [R3]  same review, section 3 -- decoupled RoPE: per-head 128-d content
+        query/key, per-head 64-d RoPE query, ONE 64-d RoPE key per token;
+        score l_ij = ((q^C_ti)^T k^C_ji + (q^R_ti)^T k^R_j) / sqrt(128 + 64),
+        a_ij = softmax_j(l_ij); the scale stays sqrt(128+64) after absorption.
+  [R4]  same review, section 4 -- per-token cache element counts (MHA 2 H d_h L,
+        GQA 2 G d_h L, MQA 2 d_h L, MLA (d_c + d_h^R) L) and the worked
+        byte counts behind the 93.3% figure.
+  [L1]  irregular6612.github.io notes on the same paper, section 2.1.2
+        (Low-Rank Key-Value Joint Compression).
+  [V3]  xyznot.com "Laporan Teknis DeepSeek-V3", Metode 1 (MLA):
+        k^R_t = RoPE(W^KR h_t), k_{t,i} = [k^C_{t,i}; k^R_t]; only c^KV and
+        k^R are cached.
+
+Readings where the pages are silent (the decoupled-RoPE section of [L1] has
+no body, and no page defines RoPE itself):
+  * RoPE rotates interleaved pairs (x[2k], x[2k+1]) by angle p * theta_k,
+    theta_k = base ** (-2k / d_h^R), base 10000, angle formed in float64.
+  * Decode: the new token's row is already in the cache; the query sits at
+    position len-1 and attends to rows 0..len-1 (itself included).
+  * Prefill: query i of a chunk sits at position prefix+i and attends to rows
+    0..prefix+i (inclusive causal mask).
+  * W^UK and W^UV are stored per head as [n_h][d_h][d_c]; U^K_i = w_uk[i].
+
+Parity: every function below is pinned by tests that do not re-type its
+formula (closed forms, brute force, a library attention routine, identities,
+the pages' printed cache numbers).
+"""
+from __future__ import annotations
+
+import math
+import numpy as np
+
+ROPE_BASE = 10000.0
+
+
+# ---------------------------------------------------------------------------
+# RoPE ([R3] rotates query and key by position; convention: see header)
+# ---------------------------------------------------------------------------
+def rope(x: np.ndarray, pos, base: float = ROPE_BASE) -> np.ndarray:
+    """Rotate the last axis of x (even length d) by position(s) `pos`.
+
+    x: [..., d]; pos broadcasts against x.shape[:-1].
+    Pair k = (x[2k], x[2k+1]) is rotated by angle pos * base**(-2k/d).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if d % 2:
+        raise ValueError("RoPE needs an even width")
+    k = np.arange(d // 2, dtype=np.float64)
+    theta = np.power(float(base), -2.0 * k / d)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * theta
+    cos, sin = np.cos(ang), np.sin(ang)
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    out = np.empty(np.broadcast_shapes(x.shape, ang.shape[:-1] + (d,)), dtype=np.float64)
+    out[..., 0::2] = xe * cos - xo * sin
+    out[..., 1::2] = xe * sin + xo * cos
+    return out
+
+
+def softmax(logits: np.ndarray, axis: int = -1) -> np.ndarray:
+    """Max-subtracted softmax in float64 ([R3] a_ij = softmax_j(l_ij))."""
+    logits = np.asarray(logits, dtype=np.float64)
+    m = np.max(logits, axis=axis, keepdims=True)
+    e = np.exp(logits - m)
+    return e / np.sum(e, axis=axis, keepdims=True)
+
+
+def default_scale(d_h: int, d_r: int) -> float:
+    """[R3]: 1/sqrt(d_h + d_h^R) -- 1/sqrt(128+64) for V2 -- also after absorption."""
+    return 1.0 / math.sqrt(d_h + d_r)
+
+
+# ---------------------------------------------------------------------------
+# A1: the cached row of a token ([V3] only c^KV and k^R are cached)
+# ---------------------------------------------------------------------------
+def append_rows(c_kv: np.ndarray, k_raw: np.ndarray, pos, base: float = ROPE_BASE) -> np.ndarray:
+    """Cache rows [c^KV_t ; RoPE(k_raw_t, pos_t)] -> [N, d_c + d_h^R]."""
+    c_kv = np.asarray(c_kv, dtype=np.float64)
+    return np.concatenate([c_kv, rope(k_raw, pos, base)], axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# A2: the absorbed query ([R2] (U^K_i)^T q^C; [R3] RoPE query per head)
+# ---------------------------------------------------------------------------
+def absorb_query(q_c: np.ndarray, q_r: np.ndarray, q_pos, w_uk: np.ndarray,
+                 base: float = ROPE_BASE) -> np.ndarray:
+    """q_lat[n, i] = [(U^K_i)^T q^C_{n,i} ; RoPE(q^R_{n,i}, pos_n)].
+
+    q_c [n, n_h, d_h], q_r [n, n_h, d_r], q_pos [n], w_uk [n_h, d_h, d_c]
+    -> [n, n_h, d_c + d_r].
+    """
+    q_c = np.asarray(q_c, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    n, n_h, _ = q_c.shape
+    lat = np.empty((n, n_h, w_uk.shape[2]), dtype=np.float64)
+    for i in range(n_h):
+        lat[:, i, :] = q_c[:, i, :] @ w_uk[i]           # ((U^K_i)^T q)^T = q^T U^K_i
+    pos = np.asarray(q_pos, dtype=np.float64)[:, None]  # same position for all heads
+    return np.concatenate([lat, rope(q_r, pos, base)], axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# The definition: unabsorbed MLA attention for one query token
+# ---------------------------------------------------------------------------
+def attend_unabsorbed(q_c, q_r_rot, c, k_r_rot, w_uk, w_uv, scale=None):
+    """Standard softmax attention with explicit per-head keys and values.
+
+    q_c [n_h, d_h], q_r_rot [n_h, d_r] (already rotated), c [T, d_c],
+    k_r_rot [T, d_r] (already rotated), w_uk / w_uv [n_h, d_h, d_c].
+    For head i ([R2], [R3], [V3]):
+        k^C_{j,i} = U^K_i c_j,  v^C_{j,i} = U^V_i c_j,  k_{j,i} = [k^C_{j,i}; k^R_j]
+        q_i = [q^C_i ; q^R_i],  l_ij = q_i . k_{j,i} * scale,  a_i = softmax(l_i)
+        o_i = sum_j a_ij v^C_{j,i}
+    Returns (o [n_h, d_h], a [n_h, T]).
+    """
+    q_c = np.asarray(q_c, dtype=np.float64)
+    q_r_rot = np.asarray(q_r_rot, dtype=np.float64)
+    c = np.asarray(c, dtype=np.float64)
+    k_r_rot = np.asarray(k_r_rot, dtype=np.float64)
+    n_h, d_h = q_c.shape
+    d_r = q_r_rot.shape[1]
+    if scale is None:
+        scale = default_scale(d_h, d_r)
+    T = c.shape[0]
+    out = np.empty((n_h, d_h), dtype=np.float64)
+    probs = np.empty((n_h, T), dtype=np.float64)
+    for i in range(n_h):
+        u_k = np.asarray(w_uk[i], dtype=np.float64)       # [d_h, d_c]
+        u_v = np.asarray(w_uv[i], dtype=np.float64)
+        k_c = c @ u_k.T                                    # rows: U^K_i c_j
+        v_c = c @ u_v.T                                    # rows: U^V_i c_j
+        keys = np.concatenate([k_c, k_r_rot], axis=1)      # [T, d_h + d_r]
+        q = np.concatenate([q_c[i], q_r_rot[i]])
+        a = softmax(keys @ q * scale)
+        out[i] = a @ v_c
+        probs[i] = a
+    return out, probs
+
+
+def attend_absorbed(q_c, q_r_rot, c, k_r_rot, w_uk, w_uv, scale=None):
+    """The same attention computed after absorption ([R2]).
+
+    q~_i = (U^K_i)^T q^C_i, l_ij = (q~_i . c_j + q^R_i . k^R_j) * scale,
+    z_i = sum_j a_ij c_j, o_i = U^V_i z_i.
+    Returns (o [n_h, d_h], z [n_h, d_c], a [n_h, T]).
+    """
+    q_c = np.asarray(q_c, dtype=np.float64)
+    q_r_rot = np.asarray(q_r_rot, dtype=np.float64)
+    c = np.asarray(c, dtype=np.float64)
+    k_r_rot = np.asarray(k_r_rot, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    n_h, d_h = q_c.shape
+    if scale is None:
+        scale = default_scale(d_h, q_r_rot.shape[1])
+    q_lat = np.einsum("hd,hdc->hc", q_c, w_uk)
+    logits = (q_lat @ c.T + q_r_rot @ k_r_rot.T) * scale
+    a = softmax(logits, axis=1)
+    z = a @ c
+    out = np.einsum("hdc,hc->hd", w_uv, z)
+    return out, z, a
+
+
+# ---------------------------------------------------------------------------
+# Decode over a batch (the spec step) and causal prefill
+# ---------------------------------------------------------------------------
+def decode(q_c, q_r, seq_lens, c_kv, k_raw, w_uk, w_uv, base=ROPE_BASE, scale=None,
+           batch_idx=None, absorbed=False):
+    """Decode one token per sequence.
+
+    q_c [B, n_h, d_h], q_r [B, n_h, d_r] (pre-RoPE), seq_lens [B],
+    c_kv [B, S, d_c], k_raw [B, S, d_r] (pre-RoPE; row j sits at position j).
+    The query of sequence b sits at position len_b - 1 and attends rows
+    0..len_b-1.  Returns (out [B', n_h, d_h], z [B', n_h, d_c]) for the
+    sequences in `batch_idx` (all by default).  z is sum_j a_ij c_j.
+    """
+    idx = range(len(seq_lens)) if batch_idx is None else list(batch_idx)
+    outs, zs = [], []
+    for b in idx:
+        T = int(seq_lens[b])
+        c = np.asarray(c_kv[b, :T], dtype=np.float64)
+        k_rot = rope(k_raw[b, :T], np.arange(T), base)
+        q_rot = rope(q_r[b], T - 1, base)
+        if absorbed:
+            o, z, _ = attend_absorbed(q_c[b], q_rot, c, k_rot, w_uk, w_uv, scale)
+        else:
+            o, a = attend_unabsorbed(q_c[b], q_rot, c, k_rot, w_uk, w_uv, scale)
+            z = a @ c
+        outs.append(o)
+        zs.append(z)
+    return np.stack(outs), np.stack(zs)
+
+
+def prefill(q_c, q_r, prefix, c_kv, k_raw, w_uk, w_uv, base=ROPE_BASE, scale=None,
+            query_idx=None):
+    """Causal prefill of one sequence.
+
+    Rows 0..prefix+chunk-1 of (c_kv, k_raw) are cached (row j at position j).
+    Query i (q_c [chunk, n_h, d_h], q_r pre-RoPE) sits at position prefix+i and
+    attends rows 0..prefix+i.  Returns out [n, n_h, d_h] for the queries in
+    `query_idx` (all by default), computed unabsorbed.
+    """
+    chunk = q_c.shape[0]
+    idx = range(chunk) if query_idx is None else list(query_idx)
+    total = prefix + chunk
+    c = np.asarray(c_kv[:total], dtype=np.float64)
+    k_rot = rope(k_raw[:total], np.arange(total), base)
+    n_h, d_h = q_c.shape[1], q_c.shape[2]
+    d_r = q_r.shape[2]
+    if scale is None:
+        scale = default_scale(d_h, d_r)
+    idx = list(idx)
+    out = np.empty((len(idx), n_h, d_h), dtype=np.float64)
+    q_rot = rope(np.asarray(q_r, dtype=np.float64)[idx],
+                 (prefix + np.asarray(idx, dtype=np.float64))[:, None], base)
+    for i in range(n_h):
+        u_k = np.asarray(w_uk[i], dtype=np.float64)
+        u_v = np.asarray(w_uv[i], dtype=np.float64)
+        keys = np.concatenate([c @ u_k.T, k_rot], axis=1)          # [total, d_h + d_r]
+        vals = c @ u_v.T                                           # [total, d_h]
+        q = np.concatenate([np.asarray(q_c, dtype=np.float64)[idx, i], q_rot[:, i]], axis=1)
+        logits = (q @ keys.T) * scale                              # [n, total]
+        pos = prefix + np.asarray(idx)[:, None]
+        logits = np.where(np.arange(total)[None, :] <= pos, logits, -np.inf)
+        out[:, i, :] = softmax(logits, axis=1) @ vals
+    return out
+
+
+# ---------------------------------------------------------------------------
+# A3/A4/A5 in latent space: split-KV partials, their combine, the W^UV step
+# ---------------------------------------------------------------------------
+def split_partials(q_lat, rows, seq_len, chunk, num_splits, scale, d_c=512):
+    """Per split s (rows [s*chunk, min((s+1)*chunk, seq_len))), per head:
+        lse_s = log sum_j exp(l_j),  Z_s = sum_j exp(l_j - lse_s) c_j,
+    with l_j = (q_lat . row_j) * scale.  Empty split: lse = -inf, Z = 0.
+    This is softmax_j of [R3] restricted to a range of j (re-associated).
+    q_lat [n_h, d_c + d_r], rows [>= seq_len, d_c + d_r].
+    Returns Z [S, n_h, d_c], lse [S, n_h].
+    """
+    q_lat = np.asarray(q_lat, dtype=np.float64)
+    n_h = q_lat.shape[0]
+    Z = np.zeros((num_splits, n_h, d_c), dtype=np.float64)
+    lse = np.full((num_splits, n_h), -np.inf, dtype=np.float64)
+    for s in range(num_splits):
+        lo, hi = s * chunk, min((s + 1) * chunk, int(seq_len))
+        if lo >= hi:
+            continue
+        r = np.asarray(rows[lo:hi], dtype=np.float64)
+        logits = (q_lat @ r.T) * scale
+        m = logits.max(axis=1, keepdims=True)
+        e = np.exp(logits - m)
+        l = e.sum(axis=1, keepdims=True)
+        lse[s] = (m + np.log(l))[:, 0]
+        Z[s] = (e / l) @ r[:, :d_c]
+    return Z, lse
+
+
+def combine_partials(Z, lse):
+    """LSE = log sum_s exp(lse_s); z = sum_s exp(lse_s - LSE) Z_s.  [S, n_h, *] -> [n_h, *]."""
+    Z = np.asarray(Z, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    m = lse.max(axis=0)
+    w = np.exp(lse - m[None, :])
+    tot = w.sum(axis=0)
+    return np.einsum("sh,shc->hc", w / tot[None, :], Z), m + np.log(tot)
+
+
+def project_uv(z, w_uv):
+    """o_i = U^V_i z_i ([R2] value up-projection after the weighted sum)."""
+    return np.einsum("hdc,...hc->...hd", np.asarray(w_uv, dtype=np.float64),
+                     np.asarray(z, dtype=np.float64))
+
+
+def latent_attention(q_lat, rows, seq_len, scale, d_c=512):
+    """Absorbed attention straight from stored q_lat and cache rows:
+    a = softmax((q_lat . row_j) * scale, j < seq_len); z = sum_j a_j c_j."""
+    r = np.asarray(rows[:seq_len], dtype=np.float64)
+    a = softmax((np.asarray(q_lat, dtype=np.float64) @ r.T) * scale, axis=1)
+    return a @ r[:, :d_c]
+
+
+# ---------------------------------------------------------------------------
+# Brute force: pure Python scalar loops, tiny inputs only
+# ---------------------------------------------------------------------------
+def decode_bruteforce(q_c, q_r, pos_q, c, k_raw, w_uk, w_uv, base=ROPE_BASE, scale=None):
+    """One query, one sequence, every step a scalar loop.  Rows 0..T-1 at positions 0..T-1."""
+    n_h, d_h = len(q_c), len(q_c[0])
+    d_r = len(q_r[0])
+    d_c = len(c[0])
+    T = len(c)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_h + d_r)
+
+    def rot(vec, p):
+        outv = [0.0] * d_r
+        for k in range(d_r // 2):
+            ang = p * (base ** (-2.0 * k / d_r))
+            cs, sn = math.cos(ang), math.sin(ang)
+            a0, a1 = float(vec[2 * k]), float(vec[2 * k + 1])
+            outv[2 * k] = a0 * cs - a1 * sn
+            outv[2 * k + 1] = a0 * sn + a1 * cs
+        return outv
+
+    krot = [rot(k_raw[j], j) for j in range(T)]
+    out = [[0.0] * d_h for _ in range(n_h)]
+    for i in range(n_h):
+        qr = rot(q_r[i], pos_q)
+        logit = []
+        vals = []
+        for j in range(T):
+            s = 0.0
+            v = [0.0] * d_h
+            for r in range(d_h):
+                kc = 0.0
+                vc = 0.0
+                for e in range(d_c):
+                    kc += float(w_uk[i][r][e]) * float(c[j][e])
+                    vc += float(w_uv[i][r][e]) * float(c[j][e])
+                s += float(q_c[i][r]) * kc
+                v[r] = vc
+            for r in range(d_r):
+                s += qr[r] * krot[j][r]
+            logit.append(s * scale)
+            vals.append(v)
+        mx = max(logit)
+        ws = [math.exp(x - mx) for x in logit]
+        tot = sum(ws)
+        for j in range(T):
+            for r in range(d_h):
+                out[i][r] += ws[j] / tot * vals[j][r]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Cache accounting ([R4] per-token elements; bytes at a given bit width)
+# ---------------------------------------------------------------------------
+def cache_elements(kind: str, layers: int, d_h: int = 128, heads: int = 0, groups: int = 0,
+                   d_c: int = 512, d_r: int = 64) -> int:
+    """Per-token KV-cache elements: MHA 2*H*d_h*L, GQA 2*G*d_h*L, MQA 2*d_h*L,
+    MLA (d_c + d_h^R)*L."""
+    if kind == "mha":
+        return 2 * heads * d_h * layers
+    if kind == "gqa":
+        return 2 * groups * d_h * layers
+    if kind == "mqa":
+        return 2 * d_h * layers
+    if kind == "mla":
+        return (d_c + d_r) * layers
+    raise ValueError(kind)
+
+
+def cache_bytes(elements: int, bits_per_element: float) -> float:
+    return elements * bits_per_element / 8.0

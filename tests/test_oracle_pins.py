@@ -1,0 +1,377 @@
+"""Pins for the CPU oracle: each check comes from something other than the
+oracle's own formula (closed forms, brute-force loops, a library attention
+routine, algebraic identities, and the numbers the pages print)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from mla_latent_kv_24_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+def _case(T, n_h, d_c=512, d_h=128, d_r=64, seed=0, wscale=None):
+    r = _rng(seed)
+    ws = (1.0 / math.sqrt(d_c)) if wscale is None else wscale
+    return dict(
+        q_c=r.standard_normal((n_h, d_h)),
+        q_r=r.standard_normal((n_h, d_r)),
+        c=r.standard_normal((T, d_c)),
+        k_raw=r.standard_normal((T, d_r)),
+        w_uk=r.standard_normal((n_h, d_h, d_c)) * ws,
+        w_uv=r.standard_normal((n_h, d_h, d_c)) * ws,
+    )
+
+
+def _rel(a, b):
+    return np.max(np.abs(a - b)) / np.sqrt(np.mean(np.square(b)))
+
+
+def _attend(cs, pos_q=None, pos_k=None, absorbed=False, scale=None):
+    T = cs["c"].shape[0]
+    pos_k = np.arange(T) if pos_k is None else pos_k
+    pos_q = T - 1 if pos_q is None else pos_q
+    qr = O.rope(cs["q_r"], pos_q)
+    kr = O.rope(cs["k_raw"], pos_k)
+    if absorbed:
+        return O.attend_absorbed(cs["q_c"], qr, cs["c"], kr, cs["w_uk"], cs["w_uv"], scale)
+    return O.attend_unabsorbed(cs["q_c"], qr, cs["c"], kr, cs["w_uk"], cs["w_uv"], scale)
+
+
+# --------------------------------------------------------------- identities
+@pytest.mark.parametrize("T,n_h", [(1, 16), (2, 16), (37, 16), (300, 16), (64, 128)])
+def test_absorption_identity(T, n_h):
+    """Absorbed and unabsorbed forms agree to 1e-10 (review section 2 identity)."""
+    cs = _case(T, n_h, seed=T + n_h)
+    o_u, a_u = _attend(cs)
+    o_a, z, a_a = _attend(cs, absorbed=True)
+    assert _rel(o_a, o_u) < 1e-10
+    assert np.max(np.abs(a_a - a_u)) < 1e-12
+    # the latent sum carries the value path: U^V (sum a c) == sum a (U^V c)
+    assert _rel(O.project_uv(z, cs["w_uv"]), o_u) < 1e-10
+
+
+def test_softmax_rows_and_shift():
+    cs = _case(200, 16, seed=3)
+    _, a = _attend(cs)
+    assert np.max(np.abs(a.sum(axis=1) - 1.0)) < 1e-14
+    assert np.all(a >= 0)
+    x = _rng(4).standard_normal((5, 9)) * 30
+    assert np.max(np.abs(O.softmax(x) - O.softmax(x + 123.25))) < 1e-13  # the shift itself rounds
+    # large logits do not overflow (max subtraction)
+    big = O.softmax(np.array([1000.0, 1000.0, -1000.0]))
+    assert np.allclose(big, [0.5, 0.5, 0.0])
+
+
+# ------------------------------------------------------------- closed forms
+def test_single_token_is_value_of_that_token():
+    """T=1: softmax over one key is 1, so o_i = U^V_i c_0 whatever q, scale, RoPE."""
+    cs = _case(1, 16, seed=5)
+    o, _ = _attend(cs)
+    expect = np.stack([cs["w_uv"][i] @ cs["c"][0] for i in range(16)])
+    assert _rel(o, expect) < 1e-13
+
+
+def test_zero_query_gives_mean_value():
+    cs = _case(50, 4, seed=6)
+    cs["q_c"][:] = 0
+    cs["q_r"][:] = 0
+    o, a = _attend(cs)
+    assert np.allclose(a, 1.0 / 50, atol=1e-15)
+    mean_c = cs["c"].mean(axis=0)
+    assert _rel(o, np.stack([cs["w_uv"][i] @ mean_c for i in range(4)])) < 1e-13
+
+
+def test_identical_rows_give_that_value():
+    cs = _case(40, 4, seed=7)
+    cs["c"][:] = cs["c"][0]
+    cs["k_raw"][:] = 0.0          # RoPE(0) = 0, so every key is the same
+    o, a = _attend(cs)
+    assert np.allclose(a, 1.0 / 40, atol=1e-15)
+    assert _rel(o, np.stack([cs["w_uv"][i] @ cs["c"][0] for i in range(4)])) < 1e-13
+
+
+def _identity_weights(n_h, d_h=128, d_c=512):
+    w = np.zeros((n_h, d_h, d_c))
+    for i in range(n_h):
+        w[i, :, :d_h] = np.eye(d_h)
+    return w
+
+
+def test_content_logit_scale_is_sqrt_192():
+    """Two keys, content logits alpha/sqrt(128+64) and 0: o_0 = sigmoid(alpha/sqrt(192)).
+
+    Review section 3: the scale stays sqrt(128+64) after absorption; a
+    sqrt(512+64) scale would give sigmoid(alpha/24) instead.
+    """
+    alpha = 3.0
+    n_h = 2
+    w = _identity_weights(n_h)
+    c = np.zeros((2, 512))
+    c[0, 0] = 1.0
+    q_c = np.zeros((n_h, 128))
+    q_c[:, 0] = alpha
+    q_r = np.zeros((n_h, 64))
+    k_raw = np.zeros((2, 64))
+    for absorbed in (False, True):
+        fn = O.attend_absorbed if absorbed else O.attend_unabsorbed
+        o = fn(q_c, O.rope(q_r, 1), c, O.rope(k_raw, np.arange(2)), w, w)[0]
+        expect = 1.0 / (1.0 + math.exp(-alpha / math.sqrt(192.0)))
+        assert abs(o[0, 0] - expect) < 1e-14 and abs(o[1, 0] - expect) < 1e-14
+        assert np.max(np.abs(o[:, 1:])) == 0.0
+        assert abs(expect - 1.0 / (1.0 + math.exp(-alpha / 24.0))) > 1e-3
+
+
+def test_rope_logit_uses_relative_angle():
+    """Key at position 0 = e_0, query RoPE part beta*e_0 at position 1: the
+    RoPE logit is beta*cos(1)/sqrt(192) (theta_0 = 1, relative angle 1 rad)."""
+    beta = 5.0
+    w = _identity_weights(1)
+    c = np.zeros((2, 512))
+    c[0, 0] = 1.0                 # marks key 0 in the value path only
+    q_c = np.zeros((1, 128))      # content logits are all zero
+    k_raw = np.zeros((2, 64))
+    k_raw[0, 0] = 1.0
+    q_r = np.zeros((1, 64))
+    q_r[0, 0] = beta
+    o = O.attend_unabsorbed(q_c, O.rope(q_r, 1), c, O.rope(k_raw, np.arange(2)), w, w)[0]
+    expect = 1.0 / (1.0 + math.exp(-beta * math.cos(1.0) / math.sqrt(192.0)))
+    assert abs(o[0, 0] - expect) < 1e-14
+
+
+# -------------------------------------------------------------------- RoPE
+def test_rope_closed_forms():
+    x = _rng(8).standard_normal((7, 64))
+    assert np.array_equal(O.rope(x, 0), x)
+    p = np.array([0, 1, 5, 100, 4096, 131071, 8191])
+    y = O.rope(x, p)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
+    # unit vector on pair k rotates by p * 10000**(-2k/64), interleaved pairs
+    for k in (0, 1, 17, 31):
+        e = np.zeros(64)
+        e[2 * k] = 1.0
+        th = 10000.0 ** (-2.0 * k / 64)
+        for pos in (1, 3, 131071):
+            r = O.rope(e, pos)
+            tol = 1e-15 + pos * 4e-16     # one ulp of theta, times the position
+            assert abs(r[2 * k] - math.cos(pos * th)) < tol
+            assert abs(r[2 * k + 1] - math.sin(pos * th)) < tol
+            assert np.count_nonzero(np.delete(r, [2 * k, 2 * k + 1])) == 0
+    # composition: rotating by p then q == rotating by p+q
+    assert np.allclose(O.rope(O.rope(x, 37), 1000), O.rope(x, 1037), atol=1e-12)
+
+
+def test_relative_position_invariance():
+    """Shifting every position (query and keys) by the same offset leaves the output unchanged."""
+    cs = _case(64, 8, seed=9)
+    T = 64
+    o0, _ = _attend(cs)
+    for shift in (1, 1000, 100000):
+        o1, _ = _attend(cs, pos_q=T - 1 + shift, pos_k=np.arange(T) + shift)
+        # angles p*theta round at ~1e-16 relative, so large shifts move logits by ~p*1e-16
+        assert _rel(o1, o0) < 1e-12 * max(1.0, shift / 1000.0)
+
+
+def test_key_permutation_invariance():
+    """Rows carry their own rotated k^R: permuting rows after RoPE changes nothing."""
+    cs = _case(50, 8, seed=10)
+    T = 50
+    qr = O.rope(cs["q_r"], T - 1)
+    kr = O.rope(cs["k_raw"], np.arange(T))
+    perm = _rng(11).permutation(T)
+    o0, _ = O.attend_unabsorbed(cs["q_c"], qr, cs["c"], kr, cs["w_uk"], cs["w_uv"])
+    o1, _ = O.attend_unabsorbed(cs["q_c"], qr, cs["c"][perm], kr[perm], cs["w_uk"], cs["w_uv"])
+    assert _rel(o1, o0) < 1e-13
+
+
+# -------------------------------------------------------------- brute force
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_bruteforce_small_dims(T):
+    cs = _case(T, 2, d_c=16, d_h=8, d_r=4, seed=20 + T)
+    bf = np.array(O.decode_bruteforce(cs["q_c"], cs["q_r"], T - 1, cs["c"], cs["k_raw"],
+                                      cs["w_uk"], cs["w_uv"]))
+    o, _ = _attend(cs)
+    assert np.max(np.abs(bf - o)) < 1e-12
+
+
+def test_bruteforce_full_dims():
+    cs = _case(2, 1, seed=30)
+    bf = np.array(O.decode_bruteforce(cs["q_c"], cs["q_r"], 1, cs["c"], cs["k_raw"],
+                                      cs["w_uk"], cs["w_uv"]))
+    o, _ = _attend(cs)
+    assert np.max(np.abs(bf - o)) < 1e-12
+
+
+# ------------------------------------------------------- library reduction
+def test_matches_library_attention():
+    """Per head the unabsorbed form is textbook attention: compare with
+    torch's scaled_dot_product_attention in float64 on the CPU."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    cs = _case(96, 6, seed=40)
+    T = 96
+    qr = O.rope(cs["q_r"], T - 1)
+    kr = O.rope(cs["k_raw"], np.arange(T))
+    o, _ = O.attend_unabsorbed(cs["q_c"], qr, cs["c"], kr, cs["w_uk"], cs["w_uv"])
+    c = torch.from_numpy(cs["c"])
+    for i in range(6):
+        k = torch.cat([c @ torch.from_numpy(cs["w_uk"][i]).T, torch.from_numpy(kr)], dim=1)
+        v = c @ torch.from_numpy(cs["w_uv"][i]).T
+        q = torch.cat([torch.from_numpy(cs["q_c"][i]), torch.from_numpy(qr[i])])[None, None]
+        ref = F.scaled_dot_product_attention(q, k[None], v[None], scale=1.0 / math.sqrt(192.0))
+        assert np.max(np.abs(ref[0, 0].numpy() - o[i])) < 1e-12
+
+
+# ------------------------------------------------------------------ prefill
+def _prefill_case(prefix, chunk, n_h=4, seed=50):
+    r = _rng(seed)
+    tot = prefix + chunk
+    return dict(
+        c=r.standard_normal((tot, 512)), k_raw=r.standard_normal((tot, 64)),
+        q_c=r.standard_normal((chunk, n_h, 128)), q_r=r.standard_normal((chunk, n_h, 64)),
+        w_uk=r.standard_normal((n_h, 128, 512)) / math.sqrt(512),
+        w_uv=r.standard_normal((n_h, 128, 512)) / math.sqrt(512))
+
+
+def test_prefill_matches_decode():
+    p = _prefill_case(20, 12)
+    out = O.prefill(p["q_c"], p["q_r"], 20, p["c"], p["k_raw"], p["w_uk"], p["w_uv"])
+    for i in (0, 5, 11):
+        # query i is a decode step of a sequence of length 20+i+1
+        L = 20 + i + 1
+        o, _ = O.decode(p["q_c"][i:i + 1], p["q_r"][i:i + 1], np.array([L]),
+                        p["c"][None, :L], p["k_raw"][None, :L], p["w_uk"], p["w_uv"])
+        assert _rel(out[i], o[0]) < 1e-13
+    # prefix 0: the first query sees only row 0
+    p0 = _prefill_case(0, 3, seed=51)
+    out0 = O.prefill(p0["q_c"], p0["q_r"], 0, p0["c"], p0["k_raw"], p0["w_uk"], p0["w_uv"])
+    expect = np.stack([p0["w_uv"][i] @ p0["c"][0] for i in range(4)])
+    assert _rel(out0[0], expect) < 1e-13
+
+
+def test_prefill_causality():
+    """Changing row j moves exactly the queries at positions >= j."""
+    p = _prefill_case(8, 8, seed=52)
+    base = O.prefill(p["q_c"], p["q_r"], 8, p["c"], p["k_raw"], p["w_uk"], p["w_uv"])
+    j = 11
+    p["c"][j] += 1.0
+    p["k_raw"][j] -= 0.5
+    moved = O.prefill(p["q_c"], p["q_r"], 8, p["c"], p["k_raw"], p["w_uk"], p["w_uv"])
+    for i in range(8):
+        same = np.array_equal(base[i], moved[i])
+        assert same == (8 + i < j)
+
+
+# ------------------------------------------------------ split-KV re-association
+@pytest.mark.parametrize("splits,chunk", [(1, 128), (2, 64), (7, 32), (5, 64), (40, 4)])
+def test_split_combine_is_exact(splits, chunk):
+    r = _rng(60)
+    T = 101
+    q_lat = r.standard_normal((8, 576)) * 0.05
+    rows = r.standard_normal((160, 576))
+    rows[T:] = np.nan                              # nothing past the length may be read
+    scale = 1.0 / math.sqrt(192.0)
+    Z, lse = O.split_partials(q_lat, rows, T, chunk, splits, scale)
+    z, LSE = O.combine_partials(Z, lse)
+    ref = O.latent_attention(q_lat, rows, T, scale)
+    assert _rel(z, ref) < 1e-13
+    logits = (q_lat @ rows[:T].T) * scale
+    m = logits.max(axis=1)
+    assert np.max(np.abs(LSE - (m + np.log(np.exp(logits - m[:, None]).sum(axis=1))))) < 1e-12
+    empty = [s for s in range(splits) if s * chunk >= T]
+    for s in empty:
+        assert np.all(np.isneginf(lse[s])) and np.all(Z[s] == 0)
+
+
+def test_absorbed_query_reproduces_content_logit():
+    """(U^K_i)^T q . c == q . (U^K_i c) (review section 2), RoPE part = RoPE(q_r, pos)."""
+    r = _rng(70)
+    q_c = r.standard_normal((3, 4, 128))
+    q_r = r.standard_normal((3, 4, 64))
+    w_uk = r.standard_normal((4, 128, 512)) / math.sqrt(512)
+    pos = np.array([0, 7, 131071])
+    lat = O.absorb_query(q_c, q_r, pos, w_uk)
+    c = r.standard_normal(512)
+    for n in range(3):
+        for i in range(4):
+            assert abs(lat[n, i, :512] @ c - q_c[n, i] @ (w_uk[i] @ c)) < 1e-11
+            assert np.allclose(lat[n, i, 512:], O.rope(q_r[n, i], pos[n]), atol=0, rtol=0)
+
+
+def test_latent_path_equals_definition():
+    """append_rows + absorb_query + latent_attention + project_uv == unabsorbed attention."""
+    cs = _case(77, 8, seed=80)
+    T = 77
+    rows = O.append_rows(cs["c"], cs["k_raw"], np.arange(T))
+    lat = O.absorb_query(cs["q_c"][None], cs["q_r"][None], np.array([T - 1]), cs["w_uk"])[0]
+    z = O.latent_attention(lat, rows, T, 1.0 / math.sqrt(192.0))
+    o_u, _ = _attend(cs)
+    assert _rel(O.project_uv(z, cs["w_uv"]), o_u) < 1e-10
+
+
+# ------------------------------------------------------------ page numbers
+def test_cache_accounting_matches_pages():
+    g = json.load(open(os.path.join(GOLDEN, "cache_accounting.json")))
+    v2 = O.cache_elements("mla", 60)
+    assert v2 == g["v2_mla_elements_per_token"]["value"]
+    assert v2 / (2 * 128 * 60) == g["v2_gqa_equivalent_groups"]["value"]
+    assert round(100 * 576 / (2 * 128 * 128), 2) == g["mla_vs_mha128_element_ratio_percent"]["value"]
+    b67 = O.cache_bytes(O.cache_elements("gqa", 95, groups=8), 16)
+    assert b67 == g["dsk67b_gqa_bytes_per_token_16bit"]["value"]
+    b6 = O.cache_bytes(v2, 6)
+    assert b6 == g["v2_bytes_per_token_6bit"]["value"]
+    assert round(100 * (1 - b6 / b67), 2) == g["reduction_percent_6bit"]["value"]
+    b16 = O.cache_bytes(v2, 16)
+    assert b16 == g["v2_bytes_per_token_16bit"]["value"]
+    assert round(100 * (1 - b16 / b67), 2) == g["reduction_percent_16bit"]["value"]
+    assert round(O.cache_elements("mha", 27, heads=16) / 1000, 1) == g["table9_small_mha_elements_k"]["value"]
+    assert round(O.cache_elements("mla", 27) / 1000, 1) == g["table9_small_mla_elements_k"]["value"]
+    assert round(O.cache_elements("mla", 60) / 1000, 1) == g["table9_large_mla_elements_k"]["value"]
+
+
+# -------------------------------------------------------------- generators
+def test_bf16_rounding_is_rne():
+    vals = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, 1.0 + 2**-8 + 2**-20, -2.5,
+                     3.0e38, 1e-40], dtype=np.float32)
+    bits = W.f32_to_bf16_bits(vals)
+    assert list(bits[:5]) == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC020]
+    back = W.bf16_bits_to_f32(bits)
+    normal = np.abs(vals) > 1e-37            # half-ulp bound holds for normal numbers
+    assert np.all(np.abs(back - vals)[normal] <= np.abs(vals)[normal] * 2**-8)
+    assert bits[6] == 0x0001                  # 1e-40 is the smallest bf16 subnormal after RNE
+
+
+def test_generators_are_deterministic_and_shaped():
+    w = W.scaled(W.WORKLOADS["lite_ragged"], batch=6, seq_len=300)
+    a = W.make_decode_inputs(w)
+    b = W.make_decode_inputs(w)
+    for f in ("seq_lens", "c_kv", "k_raw", "q_c", "q_r", "w_uk", "w_uv"):
+        assert np.array_equal(getattr(a, f), getattr(b, f))
+    assert a.c_kv.shape == (6, 300, 512) and a.q_c.shape == (6, 16, 128)
+    assert np.all((a.seq_lens >= 1) & (a.seq_lens <= 300))
+    for i, L in enumerate(a.seq_lens):
+        tail = W.bf16_bits_to_f32(a.c_kv[i, L:])
+        assert np.all(np.isnan(tail))
+        assert not np.any(np.isnan(W.bf16_bits_to_f32(a.c_kv[i, :L])))
+    # a sequence's rows do not depend on the batch it is drawn with
+    c, _ = W.draw_sequence_rows(w, 2, int(a.seq_lens[2]))
+    assert np.array_equal(W.f32_to_bf16_bits(c), a.c_kv[2, :a.seq_lens[2]])
+
+
+def test_query_scale_keeps_logits_order_one():
+    """The recipe aims at N(0,1)-sized logits: check on the V2 query path."""
+    w = W.scaled(W.WORKLOADS["v2_decode"], batch=2, seq_len=256)
+    inp = W.make_decode_inputs(w)
+    f = lambda x: W.to_f64(x, "bf16")
+    lat = O.absorb_query(f(inp.q_c), f(inp.q_r), inp.q_pos, f(inp.w_uk))
+    rows = O.append_rows(f(inp.c_kv[0]), f(inp.k_raw[0]), np.arange(256))
+    logits = lat[0] @ rows.T / math.sqrt(192.0)
+    assert 0.3 < np.std(logits) < 3.0
