@@ -1,0 +1,168 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) MLA latent-KV attention library.
+ *
+ * Multi-head Latent Attention keeps, per token and layer, one cache row
+ *     row_t = [ c^KV_t (d_c) ; k^R_t (d_hR) ]
+ * (jiphyeonjeon.kr DeepSeek-V2 review, sections 2-3; xyznot.com DeepSeek-V3
+ * report, Metode 1: only c^KV and k^R are cached).  A head's query is folded
+ * through W^UK into latent space, scored against whole rows, and the weighted
+ * sum of c^KV is lifted by W^UV only at the end (review section 2, the
+ * absorption identities).  The score of head i against row j is
+ *     l_ij = (q~_i . c_j + q^R_i . k^R_j) * scale,   scale = 1/sqrt(d_h + d_hR)
+ * (review section 3: the scale stays sqrt(128 + 64) after absorption).
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns all
+ *     buffers; the library never allocates, frees or retains device memory.
+ *   - Every launch is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     null stream).  The return value only reports argument validation and
+ *     launch errors; faults surface at the caller's next synchronisation.
+ *   - Arguments are validated on the host BEFORE any launch.  On an error no
+ *     kernel runs and no output is written.  mla_last_error() then returns a
+ *     thread-local description.
+ *   - Outputs must not alias inputs.
+ *   - Storage dtype is MLA_BF16 (bfloat16 bits) or MLA_F32 for the cache,
+ *     queries and weights; accumulation is always fp32; outputs marked
+ *     "float" are fp32.
+ *   - Identical inputs and launch arguments give bitwise-identical outputs.
+ *   - RoPE (pages give no formula; the decoupled-RoPE section of the
+ *     irregular6612 notes has no body): interleaved pairs (x[2k], x[2k+1])
+ *     rotated by angle pos * rope_base^(-2k/d_hR); the angle and its sine and
+ *     cosine are formed in fp64, the rotation in fp32.
+ *   - Fast paths: d_c = 512, d_h = 128, d_hR = 64.  n_h in {16, 32, 64, 128}
+ *     runs the MFMA kernels for MLA_BF16; any other n_h, and MLA_F32, run the
+ *     generic fp32 kernels.  Other d_c / d_h / d_hR return MLA_ERR_UNSUPPORTED.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = 1,
+  MLA_ERR_UNSUPPORTED = 2,
+  MLA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MLA_ERR_HIP = 4
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+/* Model dimensions in the pages' notation (review sections 2-4):
+ * d_c  latent width of c^KV (512 for V2 and V2-Lite)
+ * d_h  per-head content dim of keys/values (128)
+ * d_hR decoupled RoPE dim (64), even
+ * n_h  number of query heads (V2: 128, V2-Lite: 16)
+ * rope_base   RoPE frequency base (10000)
+ * softmax_scale  0 selects 1/sqrt(d_h + d_hR) */
+typedef struct {
+  int32_t d_c, d_h, d_hR, n_h;
+  double rope_base;
+  double softmax_scale;
+} mla_dims;
+
+int32_t mla_abi_version(void);
+const char* mla_status_string(mla_status s);
+const char* mla_last_error(void);
+
+/* A1 -- write cache rows of new tokens (review section 3; DeepSeek-V3 report,
+ * Metode 1: k^R_t = RoPE(W^KR h_t), cached next to c^KV_t).
+ *   c_kv [n_tok][d_c], k_r [n_tok][d_hR] (pre-RoPE), pos [n_tok] (int32 >= 0),
+ *   row [n_tok] (int64, destination row index into `cache`, >= 0)
+ *   cache [*][d_c + d_hR]: row[t] receives [c_kv[t] ; RoPE(k_r[t], pos[t])].
+ * Rows must be distinct.  n_tok = 0 is a no-op.  Errors: null pointer with
+ * n_tok > 0, n_tok < 0, bad dims. */
+mla_status mla_append_kv(const mla_dims* dims, mla_dtype dtype, int32_t n_tok,
+                         const void* c_kv, const void* k_r, const int32_t* pos,
+                         const int64_t* row, void* cache, void* stream);
+
+/* A2 -- absorbed query (review section 2: (U^K_i)^T q^C folded into the
+ * query; section 3: per-head RoPE query).
+ *   q_c [n_q][n_h][d_h], q_r [n_q][n_h][d_hR] (pre-RoPE), q_pos [n_q],
+ *   w_uk [n_h][d_h][d_c] (U^K_i = w_uk[i], so k^C = U^K_i c)
+ *   q_lat [n_q][n_h][d_c + d_hR]:
+ *     q_lat[n][i][0:d_c]   = sum_d q_c[n][i][d] * w_uk[i][d][:]
+ *     q_lat[n][i][d_c:]    = RoPE(q_r[n][i], q_pos[n])
+ * q_lat has the storage dtype (bf16 rounding for MLA_BF16). */
+mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q,
+                        const void* q_c, const void* q_r, const int32_t* q_pos,
+                        const void* w_uk, void* q_lat, void* stream);
+
+/* Split-KV plan.  Sequence rows [0, len) are cut into `num_splits` ranges of
+ * mla_split_rows(max_seq_len, num_splits) rows each (split s covers
+ * [s*R, min((s+1)*R, len)); trailing splits may be empty).
+ * mla_decode_num_splits() is the split count mla_decode() uses. */
+int32_t mla_decode_num_splits(const mla_dims* dims, mla_dtype dtype, int32_t batch,
+                              int32_t max_seq_len);
+int64_t mla_split_rows(int32_t max_seq_len, int32_t num_splits);
+
+/* A3 -- split-KV latent attention.  For query n (one per sequence), split s
+ * and head i, over rows j of split s (review section 3, softmax_j restricted
+ * to a range of j and re-associated):
+ *   lse_part[n][s][i]      = log sum_j exp(l_ij)                (natural log)
+ *   z_part[n][s][i][0:d_c] = sum_j exp(l_ij - lse) * c_j        (fp32)
+ * An empty split stores lse = -inf and z = 0.
+ *   q_lat [batch][n_h][d_c + d_hR]   (output of A2)
+ *   cache rows of sequence b start at row b * cache_seq_stride
+ *   seq_lens [batch]: 1 <= len <= min(max_seq_len, cache_seq_stride)
+ *   max_seq_len (host) bounds every len; it fixes the split rows.
+ *   z_part [batch][num_splits][n_h][d_c], lse_part [batch][num_splits][n_h]
+ * The query of sequence b attends to rows 0..len_b-1 (the new token's row is
+ * appended first, so the query at position len_b-1 sees itself).
+ * A device-side length outside [1, stride] is clamped for memory safety
+ * (len < 1 behaves as an empty sequence: lse = -inf for every split). */
+mla_status mla_decode_partials(const mla_dims* dims, mla_dtype dtype, int32_t batch,
+                               const void* q_lat, const void* cache,
+                               int64_t cache_seq_stride, const int32_t* seq_lens,
+                               int32_t max_seq_len, int32_t num_splits,
+                               float* z_part, float* lse_part, void* stream);
+
+/* A4 + A5 -- combine split partials and lift by W^UV (review section 2:
+ * sum_j a_ij U^V_i c_j = U^V_i sum_j a_ij c_j).
+ *   LSE = log sum_s exp(lse_s);  z = sum_s exp(lse_s - LSE) z_s
+ *   out[n][i][:] = w_uv[i] @ z      (w_uv [n_h][d_h][d_c]; out fp32 [n_q][n_h][d_h])
+ *   out_latent (optional, may be NULL): z, fp32 [n_q][n_h][d_c]
+ * n_q queries, each with num_splits partials laid out as in A3. */
+mla_status mla_combine_project(const mla_dims* dims, mla_dtype dtype, int32_t n_q,
+                               int32_t num_splits, const float* z_part,
+                               const float* lse_part, const void* w_uv, float* out,
+                               float* out_latent, void* stream);
+
+/* A3 + A4 + A5 in one call with the automatic split plan.  `workspace` holds
+ * the partials; its size must be at least mla_decode_workspace_bytes(). */
+size_t mla_decode_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t batch,
+                                  int32_t max_seq_len);
+mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch,
+                      const void* q_lat, const void* cache, int64_t cache_seq_stride,
+                      const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv,
+                      float* out, float* out_latent, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* A6 -- causal prefill of a chunk of `chunk` new tokens per sequence.  Their
+ * rows must already be in the cache (mla_append_kv).  Query i of sequence b
+ * sits at position prefix_lens[b] + i and attends to rows 0..prefix_lens[b]+i
+ * (inclusive causal mask), with the same score, softmax and W^UV lift as
+ * decode (review section 3).
+ *   q_lat [batch][chunk][n_h][d_c + d_hR], prefix_lens [batch] (device,
+ *   0 <= prefix <= max_prefix_len), max_prefix_len (host) with
+ *   max_prefix_len + chunk <= cache_seq_stride,
+ *   out fp32 [batch][chunk][n_h][d_h]. */
+size_t mla_prefill_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t batch,
+                                   int32_t chunk, int32_t max_prefix_len);
+mla_status mla_prefill(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk,
+                       const void* q_lat, const void* cache, int64_t cache_seq_stride,
+                       const int32_t* prefix_lens, int32_t max_prefix_len,
+                       const void* w_uv, float* out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H */

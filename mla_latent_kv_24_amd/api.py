@@ -1,0 +1,178 @@
+"""Thin Python binding of the MLA C ABI (include/mla.h).
+
+Argument marshalling only: tensors -> device pointers, torch's current HIP
+stream -> hipStream_t.  Every step runs in the HIP library; if the library is
+missing this module raises on import instead of falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB
+
+if not os.path.exists(LIB):
+    raise ImportError(f"MLA HIP library not built ({LIB}); run __graft_entry__.build()")
+
+_lib = ctypes.CDLL(LIB)
+
+MLA_OK = 0
+STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARGUMENT", 2: "MLA_ERR_UNSUPPORTED",
+          3: "MLA_ERR_WORKSPACE_TOO_SMALL", 4: "MLA_ERR_HIP"}
+F32, BF16 = 0, 1
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("d_c", ctypes.c_int32), ("d_h", ctypes.c_int32), ("d_hR", ctypes.c_int32),
+                ("n_h", ctypes.c_int32), ("rope_base", ctypes.c_double),
+                ("softmax_scale", ctypes.c_double)]
+
+
+def dims(n_h: int, d_c: int = 512, d_h: int = 128, d_hR: int = 64, rope_base: float = 10000.0,
+         softmax_scale: float = 0.0) -> Dims:
+    return Dims(d_c, d_h, d_hR, n_h, rope_base, softmax_scale)
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, func: str):
+        detail = _lib.mla_last_error().decode()
+        super().__init__(f"{func}: {STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_P = ctypes.POINTER(Dims)
+_SIGS = {
+    "mla_abi_version": (_i32, []),
+    "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mla_last_error": (ctypes.c_char_p, []),
+    "mla_append_kv": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mla_absorb_q": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mla_decode_num_splits": (_i32, [_P, ctypes.c_int, _i32, _i32]),
+    "mla_split_rows": (_i64, [_i32, _i32]),
+    "mla_decode_partials": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _i64, _vp, _i32, _i32,
+                                           _vp, _vp, _vp]),
+    "mla_combine_project": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mla_decode_workspace_bytes": (_sz, [_P, ctypes.c_int, _i32, _i32]),
+    "mla_decode": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp,
+                                  _vp, _sz, _vp]),
+    "mla_prefill_workspace_bytes": (_sz, [_P, ctypes.c_int, _i32, _i32, _i32]),
+    "mla_prefill": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _i64, _vp, _i32, _vp, _vp,
+                                   _vp, _sz, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+def raw():
+    """The ctypes handle (for tests of the C ABI itself)."""
+    return _lib
+
+
+def _check(status: int, func: str) -> None:
+    if status != MLA_OK:
+        raise MLAError(status, func)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"storage dtype must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def append_kv(d: Dims, c_kv, k_r, pos, row, cache) -> None:
+    """A1: cache[row[t]] = [c_kv[t]; RoPE(k_r[t], pos[t])]."""
+    n = c_kv.shape[0]
+    assert pos.dtype == torch.int32 and row.dtype == torch.int64
+    _check(_lib.mla_append_kv(ctypes.byref(d), _dtype(cache), n, _ptr(c_kv), _ptr(k_r), _ptr(pos),
+                              _ptr(row), _ptr(cache), _stream(cache.device)), "mla_append_kv")
+
+
+def absorb_q(d: Dims, q_c, q_r, q_pos, w_uk, q_lat) -> None:
+    """A2: q_lat[n, i] = [q_c[n, i] @ w_uk[i]; RoPE(q_r[n, i], q_pos[n])]."""
+    assert q_pos.dtype == torch.int32
+    _check(_lib.mla_absorb_q(ctypes.byref(d), _dtype(q_lat), q_c.shape[0], _ptr(q_c), _ptr(q_r),
+                             _ptr(q_pos), _ptr(w_uk), _ptr(q_lat), _stream(q_lat.device)),
+           "mla_absorb_q")
+
+
+def num_splits(d: Dims, dtype: int, batch: int, max_seq_len: int) -> int:
+    return _lib.mla_decode_num_splits(ctypes.byref(d), dtype, batch, max_seq_len)
+
+
+def split_rows(max_seq_len: int, splits: int) -> int:
+    return _lib.mla_split_rows(max_seq_len, splits)
+
+
+def decode_partials(d: Dims, q_lat, cache, stride: int, seq_lens, max_seq_len: int, splits: int,
+                    z_part, lse_part) -> None:
+    """A3: split-KV partials (z_part [B, S, n_h, d_c] fp32, lse_part [B, S, n_h] fp32)."""
+    assert seq_lens.dtype == torch.int32
+    _check(_lib.mla_decode_partials(ctypes.byref(d), _dtype(cache), q_lat.shape[0], _ptr(q_lat),
+                                    _ptr(cache), stride, _ptr(seq_lens), max_seq_len, splits,
+                                    _ptr(z_part), _ptr(lse_part), _stream(cache.device)),
+           "mla_decode_partials")
+
+
+def combine_project(d: Dims, z_part, lse_part, w_uv, out, out_latent=None) -> None:
+    """A4 + A5: out[n, i] = w_uv[i] @ combine_s(z_part[n, s, i])."""
+    n_q, S = z_part.shape[0], z_part.shape[1]
+    _check(_lib.mla_combine_project(ctypes.byref(d), _dtype(w_uv), n_q, S, _ptr(z_part),
+                                    _ptr(lse_part), _ptr(w_uv), _ptr(out), _ptr(out_latent),
+                                    _stream(out.device)), "mla_combine_project")
+
+
+def decode_workspace_bytes(d: Dims, dtype: int, batch: int, max_seq_len: int) -> int:
+    return _lib.mla_decode_workspace_bytes(ctypes.byref(d), dtype, batch, max_seq_len)
+
+
+def decode(d: Dims, q_lat, cache, stride: int, seq_lens, max_seq_len: int, w_uv, out,
+           out_latent=None, workspace=None) -> None:
+    """A3 + A4 + A5 with the automatic split plan."""
+    assert seq_lens.dtype == torch.int32
+    dt = _dtype(cache)
+    need = decode_workspace_bytes(d, dt, q_lat.shape[0], max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=cache.device)
+    _check(_lib.mla_decode(ctypes.byref(d), dt, q_lat.shape[0], _ptr(q_lat), _ptr(cache), stride,
+                           _ptr(seq_lens), max_seq_len, _ptr(w_uv), _ptr(out), _ptr(out_latent),
+                           _ptr(workspace), workspace.numel(), _stream(cache.device)), "mla_decode")
+
+
+def prefill_workspace_bytes(d: Dims, dtype: int, batch: int, chunk: int, max_prefix_len: int) -> int:
+    return _lib.mla_prefill_workspace_bytes(ctypes.byref(d), dtype, batch, chunk, max_prefix_len)
+
+
+def prefill(d: Dims, q_lat, cache, stride: int, prefix_lens, max_prefix_len: int, w_uv, out,
+            workspace=None) -> None:
+    """A6: causal prefill; q_lat [B, chunk, n_h, d_c + d_hR], out [B, chunk, n_h, d_h]."""
+    assert prefix_lens.dtype == torch.int32
+    dt = _dtype(cache)
+    B, chunk = q_lat.shape[0], q_lat.shape[1]
+    need = prefill_workspace_bytes(d, dt, B, chunk, max_prefix_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=cache.device)
+    _check(_lib.mla_prefill(ctypes.byref(d), dt, B, chunk, _ptr(q_lat), _ptr(cache), stride,
+                            _ptr(prefix_lens), max_prefix_len, _ptr(w_uv), _ptr(out),
+                            _ptr(workspace), workspace.numel(), _stream(cache.device)),
+           "mla_prefill")

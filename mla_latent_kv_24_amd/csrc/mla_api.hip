@@ -1,0 +1,283 @@
+// Host side of the C ABI declared in include/mla.h: argument validation (always
+// before any launch), the split-KV plan, workspace layout and launches.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/mla.h"
+#include "mla_common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status fail(mla_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+mla_status fail(mla_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+mla_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return MLA_OK;
+  return fail(MLA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int kNumCUs = 256;     // MI355X compute units (the plan is device independent)
+constexpr int kMinSplitRows = 256;
+constexpr int kMaxSplits = 65535;
+
+mla_status check_dims(const mla_dims* d, mla_dtype dt) {
+  if (!d) return fail(MLA_ERR_INVALID_ARGUMENT, "dims is NULL");
+  if (dt != MLA_F32 && dt != MLA_BF16) return fail(MLA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dt);
+  if (d->n_h < 1 || d->n_h > 4096) return fail(MLA_ERR_INVALID_ARGUMENT, "n_h=%d out of range [1,4096]", d->n_h);
+  if (d->d_hR <= 0 || (d->d_hR & 1)) return fail(MLA_ERR_INVALID_ARGUMENT, "d_hR=%d must be positive and even", d->d_hR);
+  if (d->d_c <= 0 || d->d_h <= 0) return fail(MLA_ERR_INVALID_ARGUMENT, "d_c=%d, d_h=%d must be positive", d->d_c, d->d_h);
+  if (d->d_c != mla::D_C || d->d_h != mla::D_H || d->d_hR != mla::D_R)
+    return fail(MLA_ERR_UNSUPPORTED, "only d_c=512, d_h=128, d_hR=64 are built (got %d, %d, %d)", d->d_c, d->d_h, d->d_hR);
+  if (!(d->rope_base > 0.0) || !std::isfinite(d->rope_base))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "rope_base must be finite and > 0");
+  if (!(d->softmax_scale >= 0.0) || !std::isfinite(d->softmax_scale))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  return MLA_OK;
+}
+
+double scale_of(const mla_dims* d) {
+  return d->softmax_scale > 0.0 ? d->softmax_scale : 1.0 / std::sqrt(static_cast<double>(d->d_h + d->d_hR));
+}
+
+void fill_rope(const mla_dims* d, mla::RopeTable& t) {
+  std::memset(&t, 0, sizeof(t));
+  for (int k = 0; k < d->d_hR / 2; ++k) t.theta[k] = std::pow(d->rope_base, -2.0 * k / d->d_hR);
+}
+
+
+int64_t split_rows(int32_t max_seq_len, int32_t num_splits) {
+  if (max_seq_len <= 0 || num_splits <= 0) return 0;
+  int64_t r = (static_cast<int64_t>(max_seq_len) + num_splits - 1) / num_splits;
+  return (r + mla::TILE - 1) / mla::TILE * mla::TILE;
+}
+
+int32_t plan_splits(const mla_dims* d, mla_dtype dt, int64_t n_q, int64_t max_len) {
+  if (n_q <= 0 || max_len <= 0) return 1;
+  const bool wide = mla::splitkv_has_fast_path(d->n_h, dt == MLA_BF16, d->d_c, d->d_hR) && d->n_h >= 32;
+  const int64_t target = static_cast<int64_t>(kNumCUs) * (wide ? 1 : 2);
+  int64_t s = (target + n_q - 1) / n_q;
+  const int64_t max_s = std::max<int64_t>(1, (max_len + kMinSplitRows - 1) / kMinSplitRows);
+  s = std::min(std::max<int64_t>(s, 1), max_s);
+  return static_cast<int32_t>(std::min<int64_t>(s, kMaxSplits));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t partial_bytes(const mla_dims* d, int64_t n_q, int32_t S) {
+  return align256(static_cast<size_t>(n_q) * S * d->n_h * d->d_c * sizeof(float)) +
+         align256(static_cast<size_t>(n_q) * S * d->n_h * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARGUMENT: return "MLA_ERR_INVALID_ARGUMENT";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+mla_status mla_append_kv(const mla_dims* dims, mla_dtype dtype, int32_t n_tok, const void* c_kv,
+                         const void* k_r, const int32_t* pos, const int64_t* row, void* cache,
+                         void* stream) {
+  mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  if (n_tok < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "n_tok=%d < 0", n_tok);
+  if (n_tok == 0) return MLA_OK;
+  if (!c_kv || !k_r || !pos || !row || !cache) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  mla::AppendArgs a{};
+  a.c_kv = c_kv;
+  a.k_r = k_r;
+  a.pos = pos;
+  a.row = row;
+  a.cache = cache;
+  a.n_tok = n_tok;
+  a.d_c = dims->d_c;
+  a.d_r = dims->d_hR;
+  fill_rope(dims, a.rope);
+  return hip_status(mla::launch_append(a, dtype == MLA_BF16, static_cast<hipStream_t>(stream)), "mla_append_kv");
+}
+
+mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q, const void* q_c,
+                        const void* q_r, const int32_t* q_pos, const void* w_uk, void* q_lat,
+                        void* stream) {
+  mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  if (n_q < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "n_q=%d < 0", n_q);
+  if (n_q == 0) return MLA_OK;
+  if (n_q > 65535 * 256) return fail(MLA_ERR_INVALID_ARGUMENT, "n_q=%d too large", n_q);
+  if (!q_c || !q_r || !q_pos || !w_uk || !q_lat) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const int bf = dtype == MLA_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  mla::AbsorbArgs a{q_c, w_uk, q_lat, n_q, dims->n_h, dims->d_c, dims->d_h, dims->d_hR};
+  mla_status r = hip_status(mla::launch_absorb(a, bf, s), "mla_absorb_q (latent)");
+  if (r != MLA_OK) return r;
+  mla::RopeQArgs ra{};
+  ra.q_r = q_r;
+  ra.q_pos = q_pos;
+  ra.q_lat = q_lat;
+  ra.n_q = n_q;
+  ra.n_h = dims->n_h;
+  ra.d_c = dims->d_c;
+  ra.d_r = dims->d_hR;
+  fill_rope(dims, ra.rope);
+  return hip_status(mla::launch_rope_q(ra, bf, s), "mla_absorb_q (rope)");
+}
+
+int32_t mla_decode_num_splits(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t max_seq_len) {
+  if (check_dims(dims, dtype) != MLA_OK) return 1;
+  return plan_splits(dims, dtype, batch, max_seq_len);
+}
+
+int64_t mla_split_rows(int32_t max_seq_len, int32_t num_splits) { return split_rows(max_seq_len, num_splits); }
+
+static mla_status run_partials(const mla_dims* dims, mla_dtype dtype, int64_t n_q, const void* q_lat,
+                               const void* cache, int64_t stride, const int32_t* lens, int32_t max_len,
+                               int32_t q_per_seq, int prefill, int32_t num_splits, float* z_part,
+                               float* lse_part, hipStream_t s, const char* who) {
+  mla::SplitArgs a{};
+  a.q_lat = q_lat;
+  a.cache = cache;
+  a.lens = lens;
+  a.z_part = z_part;
+  a.lse_part = lse_part;
+  a.stride = stride;
+  a.split_rows = split_rows(max_len, num_splits);
+  a.n_q = static_cast<int32_t>(n_q);
+  a.n_h = dims->n_h;
+  a.d_c = dims->d_c;
+  a.d_r = dims->d_hR;
+  a.num_splits = num_splits;
+  a.max_len = max_len;
+  a.q_per_seq = q_per_seq;
+  a.prefill = prefill;
+  a.qscale = static_cast<float>(scale_of(dims) * 1.4426950408889634);
+  return hip_status(mla::launch_splitkv(a, dtype == MLA_BF16, s), who);
+}
+
+mla_status mla_decode_partials(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat,
+                               const void* cache, int64_t cache_seq_stride, const int32_t* seq_lens,
+                               int32_t max_seq_len, int32_t num_splits, float* z_part, float* lse_part,
+                               void* stream) {
+  mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  if (batch < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d < 1", batch);
+  if (max_seq_len < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "max_seq_len=%d < 1", max_seq_len);
+  if (cache_seq_stride < max_seq_len)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "cache_seq_stride=%lld < max_seq_len=%d", (long long)cache_seq_stride, max_seq_len);
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "num_splits=%d out of range [1,%d]", num_splits, kMaxSplits);
+  if (!q_lat || !cache || !seq_lens || !z_part || !lse_part) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  return run_partials(dims, dtype, batch, q_lat, cache, cache_seq_stride, seq_lens, max_seq_len, 1, 0,
+                      num_splits, z_part, lse_part, static_cast<hipStream_t>(stream), "mla_decode_partials");
+}
+
+mla_status mla_combine_project(const mla_dims* dims, mla_dtype dtype, int32_t n_q, int32_t num_splits,
+                               const float* z_part, const float* lse_part, const void* w_uv, float* out,
+                               float* out_latent, void* stream) {
+  mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  if (n_q < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "n_q=%d < 1", n_q);
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "num_splits=%d out of range [1,%d]", num_splits, kMaxSplits);
+  if (!z_part || !lse_part || !w_uv || !out) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  mla::CombineArgs a{z_part, lse_part, w_uv, out, out_latent, n_q, dims->n_h, dims->d_c, dims->d_h, num_splits};
+  return hip_status(mla::launch_combine(a, dtype == MLA_BF16, static_cast<hipStream_t>(stream)), "mla_combine_project");
+}
+
+size_t mla_decode_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t max_seq_len) {
+  if (check_dims(dims, dtype) != MLA_OK || batch < 1 || max_seq_len < 1) return 0;
+  return partial_bytes(dims, batch, plan_splits(dims, dtype, batch, max_seq_len));
+}
+
+mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat, const void* cache,
+                      int64_t cache_seq_stride, const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv,
+                      float* out, float* out_latent, void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  if (batch < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d < 1", batch);
+  if (max_seq_len < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "max_seq_len=%d < 1", max_seq_len);
+  if (cache_seq_stride < max_seq_len)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "cache_seq_stride=%lld < max_seq_len=%d", (long long)cache_seq_stride, max_seq_len);
+  if (!q_lat || !cache || !seq_lens || !w_uv || !out || !workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const int32_t S = plan_splits(dims, dtype, batch, max_seq_len);
+  const size_t need = partial_bytes(dims, batch, S);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", workspace_bytes, need);
+  float* z = static_cast<float*>(workspace);
+  float* lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        align256(static_cast<size_t>(batch) * S * dims->n_h * dims->d_c * sizeof(float)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_partials(dims, dtype, batch, q_lat, cache, cache_seq_stride, seq_lens, max_seq_len, 1, 0, S, z, lse, s,
+                    "mla_decode (partials)");
+  if (st != MLA_OK) return st;
+  mla::CombineArgs a{z, lse, w_uv, out, out_latent, batch, dims->n_h, dims->d_c, dims->d_h, S};
+  return hip_status(mla::launch_combine(a, dtype == MLA_BF16, s), "mla_decode (combine)");
+}
+
+size_t mla_prefill_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk,
+                                   int32_t max_prefix_len) {
+  if (check_dims(dims, dtype) != MLA_OK || batch < 1 || chunk < 1 || max_prefix_len < 0) return 0;
+  const int64_t n_q = static_cast<int64_t>(batch) * chunk;
+  const int64_t max_len = static_cast<int64_t>(max_prefix_len) + chunk;
+  return partial_bytes(dims, n_q, plan_splits(dims, dtype, n_q, max_len));
+}
+
+mla_status mla_prefill(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk, const void* q_lat,
+                       const void* cache, int64_t cache_seq_stride, const int32_t* prefix_lens,
+                       int32_t max_prefix_len, const void* w_uv, float* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  if (batch < 1 || chunk < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d, chunk=%d must be >= 1", batch, chunk);
+  if (max_prefix_len < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "max_prefix_len=%d < 0", max_prefix_len);
+  const int64_t max_len = static_cast<int64_t>(max_prefix_len) + chunk;
+  if (max_len > cache_seq_stride)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "max_prefix_len + chunk = %lld > cache_seq_stride=%lld",
+                (long long)max_len, (long long)cache_seq_stride);
+  if (max_len > 0x7fffffff) return fail(MLA_ERR_INVALID_ARGUMENT, "prefix + chunk too large");
+  const int64_t n_q = static_cast<int64_t>(batch) * chunk;
+  if (n_q > 0x7fffffff / 2) return fail(MLA_ERR_INVALID_ARGUMENT, "batch*chunk too large");
+  if (!q_lat || !cache || !prefix_lens || !w_uv || !out || !workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const int32_t S = plan_splits(dims, dtype, n_q, max_len);
+  const size_t need = partial_bytes(dims, n_q, S);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", workspace_bytes, need);
+  float* z = static_cast<float*>(workspace);
+  float* lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        align256(static_cast<size_t>(n_q) * S * dims->n_h * dims->d_c * sizeof(float)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_partials(dims, dtype, n_q, q_lat, cache, cache_seq_stride, prefix_lens, static_cast<int32_t>(max_len),
+                    chunk, 1, S, z, lse, s, "mla_prefill (partials)");
+  if (st != MLA_OK) return st;
+  mla::CombineArgs a{z, lse, w_uv, out, nullptr, static_cast<int32_t>(n_q), dims->n_h, dims->d_c, dims->d_h, S};
+  return hip_status(mla::launch_combine(a, dtype == MLA_BF16, s), "mla_prefill (combine)");
+}
+
+}  // extern "C"

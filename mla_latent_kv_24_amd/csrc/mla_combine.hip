@@ -1,0 +1,159 @@
+// A4 + A5 -- combine split-KV partials and lift the latent by W^UV, gfx950.
+//
+//   LSE = log sum_s exp(lse_s),   z = sum_s exp(lse_s - LSE) Z_s
+// is softmax_j over all rows re-associated from per-split pieces, and
+//   o_i = U^V_i z_i
+// is the value up-projection moved outside the weighted sum
+// (jiphyeonjeon.kr DeepSeek-V2 review, section 2: sum_j a_ij U^V_i c_j =
+// U^V_i sum_j a_ij c_j).
+#include "mla_common.h"
+
+namespace mla {
+
+constexpr float CNEG_INF = -__builtin_huge_valf();
+constexpr int CMB_MAX_SPLITS = 128;   // weights staged in LDS for the MFMA path
+constexpr int ZSTRIDE = 1040;        // bytes per staged z row (512 bf16 + 16 B pad)
+
+// ------------------------------------------------------------------------
+// bf16 MFMA path.  Grid (head, block of 32 queries); 4 waves, wave w owns the
+// 32 output dims d = 32w..32w+31.  z is combined in fp32, optionally written
+// out, then split into bf16 hi + lo parts (z = hi + lo to ~2^-16 relative) so
+// the 32x32x16 MFMA lift keeps fp32-level accuracy:
+//   out[n][d] = sum_c (hi[n][c] + lo[n][c]) * w_uv[h][d][c]
+// A = z rows from LDS (c contiguous), B = w_uv rows from global (c contiguous).
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_mfma_kernel(CombineArgs a) {
+  __shared__ float wts[32][CMB_MAX_SPLITS];
+  __shared__ __attribute__((aligned(16))) uint8_t zhi[32 * ZSTRIDE];
+  __shared__ __attribute__((aligned(16))) uint8_t zlo[32 * ZSTRIDE];
+  const int h = blockIdx.x, n0 = blockIdx.y * 32;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int S = a.num_splits;
+
+  // split weights: one thread per query
+  if (tid < 32) {
+    const int n = n0 + tid;
+    if (n < a.n_q) {
+      const float* ls = a.lse_part + static_cast<int64_t>(n) * S * a.n_h + h;
+      float m = CNEG_INF;
+      for (int s = 0; s < S; ++s) m = fmaxf(m, ls[static_cast<int64_t>(s) * a.n_h]);
+      float tot = 0.f;
+      for (int s = 0; s < S; ++s) {
+        const float e = (m == CNEG_INF) ? 0.f : expf(ls[static_cast<int64_t>(s) * a.n_h] - m);
+        wts[tid][s] = e;
+        tot += e;
+      }
+      const float inv = (tot > 0.f) ? 1.f / tot : 0.f;
+      for (int s = 0; s < S; ++s) wts[tid][s] *= inv;
+    } else {
+      for (int s = 0; s < S; ++s) wts[tid][s] = 0.f;
+    }
+  }
+  __syncthreads();
+
+  // combined latent: thread -> (query row, 4-column group), 128 groups per row
+  for (int idx = tid; idx < 32 * 128; idx += 256) {
+    const int r = idx >> 7, c4 = (idx & 127) * 4;
+    const int n = n0 + r;
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    if (n < a.n_q) {
+      const float* zp = a.z_part + (static_cast<int64_t>(n) * S * a.n_h + h) * D_C + c4;
+      for (int s = 0; s < S; ++s) {
+        const float wv = wts[r][s];
+        if (wv != 0.f) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(zp + static_cast<int64_t>(s) * a.n_h * D_C);
+          z += wv * v;
+        }
+      }
+      if (a.out_latent)
+        *reinterpret_cast<f32x4*>(a.out_latent + (static_cast<int64_t>(n) * a.n_h + h) * D_C + c4) = z;
+    }
+    uint16_t hi4[4], lo4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hi4[i] = f32_to_bf16(z[i]);
+      lo4[i] = f32_to_bf16(z[i] - bf16_to_f32(hi4[i]));
+    }
+    uint2 hv = make_uint2(hi4[0] | (static_cast<uint32_t>(hi4[1]) << 16),
+                          hi4[2] | (static_cast<uint32_t>(hi4[3]) << 16));
+    uint2 lv = make_uint2(lo4[0] | (static_cast<uint32_t>(lo4[1]) << 16),
+                          lo4[2] | (static_cast<uint32_t>(lo4[3]) << 16));
+    *reinterpret_cast<uint2*>(zhi + r * ZSTRIDE + 2 * c4) = hv;
+    *reinterpret_cast<uint2*>(zlo + r * ZSTRIDE + 2 * c4) = lv;
+  }
+  __syncthreads();
+
+  const int g = l >> 5;
+  const int d = 32 * w + (l & 31);
+  const uint16_t* wrow = static_cast<const uint16_t*>(a.w_uv) + (static_cast<int64_t>(h) * D_H + d) * D_C;
+  const int arow = (l & 31) * ZSTRIDE + 16 * g;
+  f32x16 acc = {0};
+#pragma unroll 4
+  for (int s = 0; s < D_C / 16; ++s) {
+    const u32x4 bw = *reinterpret_cast<const u32x4*>(wrow + 16 * s + 8 * g);
+    const u32x4 ah = *reinterpret_cast<const u32x4*>(zhi + arow + 32 * s);
+    const u32x4 al = *reinterpret_cast<const u32x4*>(zlo + arow + 32 * s);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah),
+                                                  __builtin_bit_cast(bf16x8, bw), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, al),
+                                                  __builtin_bit_cast(bf16x8, bw), acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int n = n0 + 8 * (j >> 2) + 4 * g + (j & 3);
+    if (n < a.n_q) a.out[(static_cast<int64_t>(n) * a.n_h + h) * D_H + d] = acc[j];
+  }
+}
+
+// ------------------------------------------------------------------------
+// Generic fp32 path: one workgroup per (query, head).
+// ------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void combine_generic_kernel(CombineArgs a) {
+  __shared__ float z[1024];
+  __shared__ float lsum[2];
+  const int n = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int S = a.num_splits;
+  const float* ls = a.lse_part + static_cast<int64_t>(n) * S * a.n_h + h;
+  if (tid == 0) {
+    float m = CNEG_INF;
+    for (int s = 0; s < S; ++s) m = fmaxf(m, ls[static_cast<int64_t>(s) * a.n_h]);
+    float tot = 0.f;
+    for (int s = 0; s < S; ++s)
+      tot += (m == CNEG_INF) ? 0.f : expf(ls[static_cast<int64_t>(s) * a.n_h] - m);
+    lsum[0] = m;
+    lsum[1] = tot;
+  }
+  __syncthreads();
+  const float m = lsum[0], tot = lsum[1];
+  for (int c = tid; c < a.d_c; c += 256) {
+    float acc = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float e = (m == CNEG_INF) ? 0.f : expf(ls[static_cast<int64_t>(s) * a.n_h] - m) / tot;
+      if (e != 0.f) acc = fmaf(e, a.z_part[((static_cast<int64_t>(n) * S + s) * a.n_h + h) * a.d_c + c], acc);
+    }
+    z[c] = acc;
+    if (a.out_latent) a.out_latent[(static_cast<int64_t>(n) * a.n_h + h) * a.d_c + c] = acc;
+  }
+  __syncthreads();
+  const T* wv = static_cast<const T*>(a.w_uv) + static_cast<int64_t>(h) * a.d_h * a.d_c;
+  for (int d = tid; d < a.d_h; d += 256) {
+    float acc = 0.f;
+    for (int c = 0; c < a.d_c; ++c) acc = fmaf(load_as_f32(wv, static_cast<int64_t>(d) * a.d_c + c), z[c], acc);
+    a.out[(static_cast<int64_t>(n) * a.n_h + h) * a.d_h + d] = acc;
+  }
+}
+
+hipError_t launch_combine(const CombineArgs& a, int bf16, hipStream_t st) {
+  if (a.n_q <= 0) return hipSuccess;
+  if (bf16 && a.d_c == D_C && a.d_h == D_H && a.num_splits <= CMB_MAX_SPLITS) {
+    combine_mfma_kernel<<<dim3(a.n_h, (a.n_q + 31) / 32), 256, 0, st>>>(a);
+  } else if (bf16) {
+    combine_generic_kernel<uint16_t><<<dim3(a.n_q, a.n_h), 256, 0, st>>>(a);
+  } else {
+    combine_generic_kernel<float><<<dim3(a.n_q, a.n_h), 256, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,111 @@
+// Shared device/host definitions of the gfx950 MLA kernels (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int D_C = 512;           // latent width d_c (fast path)
+constexpr int D_H = 128;           // per-head content dim d_h
+constexpr int D_R = 64;            // decoupled RoPE dim d_hR
+constexpr int ROWE = D_C + D_R;    // elements per cache row
+constexpr int ROWB = ROWE * 2;     // bytes per bf16 cache row (1152)
+constexpr int TILE = 32;           // cache rows per LDS tile
+constexpr int TILE_BYTES = TILE * ROWB;
+constexpr int MAX_PAIRS = 64;      // RoPE pairs supported by the generic kernels (d_hR <= 128)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// RoPE frequencies theta_k = base^(-2k/d_hR), formed on the host in fp64.
+struct RopeTable {
+  double theta[MAX_PAIRS];
+};
+
+struct AppendArgs {
+  const void* c_kv;
+  const void* k_r;
+  const int32_t* pos;
+  const int64_t* row;
+  void* cache;
+  int32_t n_tok, d_c, d_r;
+  RopeTable rope;
+};
+
+struct RopeQArgs {
+  const void* q_r;       // [n_q][n_h][d_r]
+  const int32_t* q_pos;  // [n_q]
+  void* q_lat;           // [n_q][n_h][d_c + d_r]
+  int32_t n_q, n_h, d_c, d_r;
+  RopeTable rope;
+};
+
+struct AbsorbArgs {
+  const void* q_c;   // [n_q][n_h][d_h]
+  const void* w_uk;  // [n_h][d_h][d_c]
+  void* q_lat;       // [n_q][n_h][d_c + d_r]
+  int32_t n_q, n_h, d_c, d_h, d_r;
+};
+
+struct SplitArgs {
+  const void* q_lat;      // [n_q][n_h][d_c + d_r]
+  const void* cache;      // rows of d_c + d_r
+  const int32_t* lens;    // decode: seq_lens[batch]; prefill: prefix_lens[batch]
+  float* z_part;          // [n_q][num_splits][n_h][d_c]
+  float* lse_part;        // [n_q][num_splits][n_h]
+  int64_t stride;         // rows per sequence slot
+  int64_t split_rows;     // rows per split
+  int32_t n_q, n_h, d_c, d_r;
+  int32_t num_splits;
+  int32_t max_len;        // host bound on the attended length
+  int32_t q_per_seq;      // 1 for decode, chunk for prefill
+  int32_t prefill;        // 0 decode, 1 causal prefill
+  float qscale;           // softmax_scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* z_part;
+  const float* lse_part;
+  const void* w_uv;       // [n_h][d_h][d_c]
+  float* out;             // [n_q][n_h][d_h]
+  float* out_latent;      // optional [n_q][n_h][d_c]
+  int32_t n_q, n_h, d_c, d_h, num_splits;
+};
+
+// host launchers (defined in the .hip files); return hipGetLastError() after launch
+hipError_t launch_append(const AppendArgs& a, int bf16, hipStream_t st);
+hipError_t launch_rope_q(const RopeQArgs& a, int bf16, hipStream_t st);
+hipError_t launch_absorb(const AbsorbArgs& a, int bf16, hipStream_t st);
+hipError_t launch_splitkv(const SplitArgs& a, int bf16, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, int bf16, hipStream_t st);
+bool splitkv_has_fast_path(int n_h, int bf16, int d_c, int d_r);
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {  // round to nearest even
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+template <typename T>
+__device__ __forceinline__ float load_as_f32(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_to_f32(p[i]);
+}
+template <typename T>
+__device__ __forceinline__ T store_from_f32(float v);
+template <>
+__device__ __forceinline__ float store_from_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ uint16_t store_from_f32<uint16_t>(float v) { return f32_to_bf16(v); }
+
+}  // namespace mla

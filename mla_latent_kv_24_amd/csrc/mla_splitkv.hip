@@ -1,0 +1,466 @@
+// A3 -- split-KV latent attention for gfx950 (MI355X).
+//
+// For one query token and all its heads, over the rows j of one split:
+//   l_ij = (q~_i . c_j + q^R_i . k^R_j) * scale        (jiphyeonjeon.kr DeepSeek-V2
+//                                                       review, section 3)
+//   lse_i = log sum_j exp(l_ij),  Z_i = sum_j exp(l_ij - lse_i) c_j
+// i.e. softmax_j restricted to the split; the combine (A4) re-associates the
+// splits exactly.  Every head reads the same cache row (review section 2: the
+// latent is shared, but a_ij differs per head), so one LDS tile of rows feeds
+// all heads of the query and both contractions are dense:
+//   S^T[t][i] = sum_e row[t][e] q_lat[i][e]    (e over d_c + d_hR = 576)
+//   Z^T[c][i] += sum_t row[t][c] P^T[t][i]    (t over the tile's rows)
+//
+// MFMA fast path (bf16, d_c=512, d_hR=64, n_h in {16,32,64,128}):
+//   * 4 waves; a wave owns HPW heads (32, or 16 when n_h=16) and a slice of the
+//     512 latent columns.  n_h=128: 4 head groups x all columns.  n_h=16:
+//     1 head group x 4 column quarters (the score is recomputed per wave; it
+//     is cheap next to the HBM stream at 16 heads).
+//   * Tiles of 32 rows (36,864 B) stream into a ring of 4 LDS buffers by
+//     buffer_load ... lds (global -> LDS DMA, no staging registers), three tiles
+//     in flight while one is computed.  Rows keep their natural 1152-B stride;
+//     16-B chunks are XOR-swizzled by row (by choosing each lane's source
+//     chunk) so the score reads and the transpose reads are conflict free.
+//     The buffer resource spans exactly the split's rows, so rows past the
+//     split end arrive as zeros: no masking code on the load side.
+//   * Score: A = tile rows (ds_read_b128, e contiguous), B = the wave's
+//     absorbed queries, held in VGPRs for the whole split.
+//   * Value: A = tile columns via ds_read_b64_tr_b16 (the LDS transpose read
+//     turns 4 rows x 16 columns into per-lane columns), B = P^T taken straight
+//     from the score accumulators: each transpose read fetches exactly the
+//     rows whose scores the lane holds, so no shuffle is needed.
+//   * Online softmax in the log2 domain with a lazy rescale: the reference max
+//     only moves when a tile max exceeds it by more than 8 (so p <= 2^8), and
+//     the Z accumulators are rescaled only then.  Exact up to rounding.
+#include <type_traits>
+
+#include "mla_common.h"
+
+namespace mla {
+
+constexpr float NEG_INF = -__builtin_huge_valf();
+constexpr float RESCALE_TAU = 8.0f;
+
+// 16-byte chunk swizzle of tile row t: chunk k of the row lives at k ^ swz(t).
+__device__ __forceinline__ int swz(int t) {
+  const int m = (t >> 1) & 7;
+  return ((m & 1) << 2) | (m >> 1);
+}
+// byte offset of element e of tile row t
+__device__ __forceinline__ int tile_off(int t, int e) {
+  return t * ROWB + 16 * ((e >> 3) ^ swz(t)) + 2 * (e & 7);
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+// One 16-B-per-lane global -> LDS copy: lane L's bytes from rsrc + soff + voff land
+// at LDS address m0 + 16 L.  Issued from asm so that the compiler does not fence
+// every later LDS read on it; the waits are explicit (vm_wait) at tile boundaries.
+__device__ __forceinline__ void dma16(uint32_t lds_addr, int voff, i32x4 rsrc, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ i16x4 tr_read(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+__device__ __forceinline__ bf16x8 cat(i16x4 a, i16x4 b) {
+  struct {
+    i16x4 lo, hi;
+  } v = {a, b};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Query n -> (sequence, attended length), the length clamped to [0, min(max_len, stride)].
+__device__ __forceinline__ void query_range(const SplitArgs& a, int n, int& b, int64_t& len) {
+  b = n / a.q_per_seq;
+  int64_t L = a.prefill ? static_cast<int64_t>(a.lens[b]) + (n % a.q_per_seq) + 1
+                        : static_cast<int64_t>(a.lens[b]);
+  L = min(L, static_cast<int64_t>(a.max_len));
+  L = min(L, a.stride);
+  len = max(L, static_cast<int64_t>(0));
+}
+
+template <int HPW, int CG>
+__global__ __launch_bounds__(256, (HPW == 32 && CG == 1) ? 1 : 2) void splitkv_mfma_kernel(
+    SplitArgs a) {
+  constexpr int NHG = 4 / CG;                    // head groups per workgroup
+  constexpr int COLS = D_C / CG;                 // latent columns per wave
+  constexpr int CB = COLS / HPW;                 // value c-blocks per wave
+  constexpr int ZR = (HPW == 32) ? 16 : 4;       // accumulator registers per c-block
+  constexpr int NQ = (HPW == 32) ? 36 : 18;      // score k-steps: 576/16 or 576/32
+  constexpr int NSC = (HPW == 32) ? 16 : 8;      // scores held per lane per tile
+  constexpr int LOADS = TILE_BYTES / (16 * 256);  // 9 chunk loads per thread per tile
+  static_assert(TILE_BYTES == LOADS * 16 * 256, "tile must split evenly over 256 threads");
+  typedef typename std::conditional<HPW == 32, f32x16, f32x4>::type acc_t;
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_BYTES];
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int hg = w % NHG, cg = w / NHG;
+  const int n = blockIdx.x, split = blockIdx.y;
+  int b;
+  int64_t len;
+  query_range(a, n, b, len);
+  const int64_t lo = static_cast<int64_t>(split) * a.split_rows;
+  const int64_t hi = min(lo + a.split_rows, len);
+  const int h0 = hg * HPW;
+  float* zo = a.z_part + (static_cast<int64_t>(n) * a.num_splits + split) * a.n_h * D_C;
+  float* lse_o = a.lse_part + (static_cast<int64_t>(n) * a.num_splits + split) * a.n_h;
+
+  if (lo >= hi) {  // empty split (uniform over the workgroup)
+    for (int idx = l; idx < HPW * COLS; idx += 64) {
+      const int hh = idx / COLS, c = cg * COLS + idx % COLS;
+      zo[static_cast<int64_t>(h0 + hh) * D_C + c] = 0.f;
+    }
+    if (cg == 0 && l < HPW) lse_o[h0 + l] = NEG_INF;
+    return;
+  }
+
+  const int g32 = l >> 5, q16 = l >> 4, j16 = l & 15;
+
+  // ---- absorbed queries of this wave's heads -> B-operand registers
+  u32x4 qreg[NQ];
+  {
+    const uint16_t* q =
+        static_cast<const uint16_t*>(a.q_lat) + static_cast<int64_t>(n) * a.n_h * ROWE;
+    if constexpr (HPW == 32) {
+      const uint16_t* qh = q + (h0 + (l & 31)) * ROWE + 8 * g32;
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) qreg[s] = *reinterpret_cast<const u32x4*>(qh + 16 * s);
+    } else {
+      const uint16_t* qh = q + (h0 + (l & 15)) * ROWE + 8 * q16;
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) qreg[s] = *reinterpret_cast<const u32x4*>(qh + 32 * s);
+    }
+  }
+
+  vm_wait<0>();  // queries resident before any tile DMA is issued (keeps the loop free of waits)
+
+  // ---- tile loads: LDS chunk f = tid + 256 i of the tile receives global
+  // chunk (t, p ^ swz(t)) with (t, p) = (f / 72, f % 72)
+  constexpr int NBUF = 4;
+  int voff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int f = tid + 256 * i;
+    const int t = f / 72, p = f % 72;
+    voff[i] = 16 * (t * 72 + (p ^ swz(t)));
+  }
+  const uint8_t* gsplit =
+      static_cast<const uint8_t*>(a.cache) + (static_cast<int64_t>(b) * a.stride + lo) * ROWB;
+  // One buffer resource per tile, based at the tile's first row and sized to
+  // the tile's rows inside the split: the range check (voffset only) returns
+  // zeros for rows past the split end, so nothing past it is ever read.
+  const uint64_t gaddr = reinterpret_cast<uint64_t>(gsplit);
+  const int64_t ntiles = (hi - lo + TILE - 1) / TILE;
+  const uint32_t lds_w = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                             (__attribute__((address_space(3))) uint8_t*)smem)) +
+                         1024u * static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(w));
+  auto issue = [&](int64_t it) {
+    const uint64_t ga = gaddr + static_cast<uint64_t>(it) * TILE_BYTES;
+    const int64_t rows = min(static_cast<int64_t>(TILE), hi - lo - it * TILE);
+    const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(ga & 0xffffffffu)),
+                      __builtin_amdgcn_readfirstlane(static_cast<int>((ga >> 32) & 0xffffu)),
+                      __builtin_amdgcn_readfirstlane(static_cast<int>(rows * ROWB)), 0x00020000};
+    const uint32_t dst = lds_w + static_cast<uint32_t>((it & (NBUF - 1)) * TILE_BYTES);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) dma16(dst + 4096u * i, voff[i], rs, 0);
+  };
+
+  // ---- per-lane LDS offsets of the MFMA operands
+  int sc_off[4] = {0, 0, 0, 0};
+  int tr_off[2][4];  // [first/second transpose read][low bits of the column block]
+  if constexpr (HPW == 32) {
+    // score A: row t = l%32, element 16 s + 8 g  -> chunk 2 s + g
+    const int t = l & 31;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) sc_off[m] = t * ROWB + 16 * ((2 * m + g32) ^ swz(t));
+    // value A: rows 16u + 4g + (j16>>2) and +8, columns 32 cb + 16 hf + 4 (j16&3)
+    const int hf = (l >> 4) & 1;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int tt = 4 * g32 + (j16 >> 2) + 8 * r;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) tr_off[r][p] = tile_off(tt, 32 * (p & 1) + 16 * hf + 4 * (j16 & 3));
+    }
+  } else {
+    // score A: row t = 16 tb + l%16, element 32 s + 8 q -> chunk 4 s + q
+    const int t = l & 15;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) sc_off[m] = t * ROWB + 16 * ((4 * m + q16) ^ swz(t));
+    // value A: rows 4q + (j16>>2) and +16, columns 16 cb + 4 (j16&3)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int tt = 4 * q16 + (j16 >> 2) + 16 * r;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) tr_off[r][p] = tile_off(tt, 16 * p + 4 * (j16 & 3));
+    }
+  }
+
+  acc_t zacc[CB];
+#pragma unroll
+  for (int c = 0; c < CB; ++c)
+#pragma unroll
+    for (int r = 0; r < ZR; ++r) zacc[c][r] = 0.f;
+  float m_run = NEG_INF, l_run = 0.f;
+
+  issue(0);
+  if (ntiles > 1) issue(1);
+  if (ntiles > 2) issue(2);
+
+  for (int64_t it = 0; it < ntiles; ++it) {
+    // tile `it` must have landed: the loads of the (up to 2) later tiles may stay in flight
+    if (it + 2 < ntiles)
+      vm_wait<2 * LOADS>();
+    else if (it + 1 < ntiles)
+      vm_wait<LOADS>();
+    else
+      vm_wait<0>();
+    __syncthreads();
+    const uint8_t* buf = smem + (it & (NBUF - 1)) * TILE_BYTES;
+    const int64_t valid = hi - (lo + it * TILE);  // rows of this tile inside the split (>= 1)
+
+    // -------------------------------------------------- score S^T = rows . q
+    float x[NSC];
+    if constexpr (HPW == 32) {
+      f32x16 sacc = {0};
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(buf + sc_off[s & 3] + 128 * (s >> 2));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv),
+                                                       __builtin_bit_cast(bf16x8, qreg[s]), sacc, 0, 0, 0);
+        if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int t = 8 * (j >> 2) + 4 * g32 + (j & 3);
+        x[j] = (t < valid) ? sacc[j] * a.qscale : NEG_INF;
+      }
+    } else {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        f32x4 sacc = {0};
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) {
+          const u32x4 kv = *reinterpret_cast<const u32x4*>(buf + tb * 16 * ROWB + sc_off[s & 1] +
+                                                           128 * (s >> 1));
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
+                                                         __builtin_bit_cast(bf16x8, qreg[s]), sacc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = 16 * tb + 4 * q16 + j;
+          x[4 * tb + j] = (t < valid) ? sacc[j] * a.qscale : NEG_INF;
+        }
+      }
+    }
+
+    // -------------------------------------------------- online softmax (log2)
+    float mt = x[0];
+#pragma unroll
+    for (int j = 1; j < NSC; ++j) mt = fmaxf(mt, x[j]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    if constexpr (HPW == 16) mt = fmaxf(mt, __shfl_xor(mt, 16));
+    const bool need = mt > m_run + RESCALE_TAU;
+    if (__ballot(need)) {
+      const float m_new = need ? mt : m_run;
+      const float alpha = (m_run == NEG_INF) ? 0.f : exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int r = 0; r < ZR; ++r) {
+          float e = zacc[c][r];
+          float tmp;
+          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                       : "+a"(e), "=&v"(tmp) : "v"(alpha));
+          zacc[c][r] = e;
+        }
+      m_run = m_new;
+    }
+    float p[NSC];
+#pragma unroll
+    for (int j = 0; j < NSC; ++j) {
+      p[j] = exp2f(x[j] - m_run);
+      l_run += p[j];
+    }
+
+    // -------------------------------------------------- value Z^T += rows^T . P^T
+    if constexpr (HPW == 32) {
+      bf16x8 pb[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[u][i] = static_cast<__bf16>(p[8 * u + i]);
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const int cbg = cg * CB + c;  // 32-column block index
+        const uint8_t* base = buf + 128 * (cbg >> 1);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint8_t* bu = base + 16 * u * ROWB;
+          const bf16x8 va = cat(tr_read(bu + tr_off[0][cbg & 1]), tr_read(bu + tr_off[1][cbg & 1]));
+          zacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[u], zacc[c], 0, 0, 0);
+        }
+        if (c & 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      bf16x8 pb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(p[i]);
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const int cbg = cg * CB + c;  // 16-column block index
+        const uint8_t* base = buf + 128 * (cbg >> 2);
+        const bf16x8 va = cat(tr_read(base + tr_off[0][cbg & 3]), tr_read(base + tr_off[1][cbg & 3]));
+        zacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, zacc[c], 0, 0, 0);
+      }
+    }
+
+    // every wave passed this iteration's barrier, so buffer (it+3)&3 == (it-1)&3 is free
+    if (it + 3 < ntiles) issue(it + 3);
+  }
+
+  // ---- finalize: total over the lanes sharing a head, normalise, store
+  float lt = l_run + __shfl_xor(l_run, 32);
+  if constexpr (HPW == 16) lt += __shfl_xor(lt, 16);
+  const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+  const float lse = (lt > 0.f) ? (m_run + log2f(lt)) * LN2 : NEG_INF;
+  if constexpr (HPW == 32) {
+    const int h = h0 + (l & 31);
+    float* zh = zo + static_cast<int64_t>(h) * D_C;
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const int cbg = cg * CB + c;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 v = {zacc[c][4 * jj] * inv, zacc[c][4 * jj + 1] * inv, zacc[c][4 * jj + 2] * inv,
+                         zacc[c][4 * jj + 3] * inv};
+        *reinterpret_cast<f32x4*>(zh + 32 * cbg + 8 * jj + 4 * g32) = v;
+      }
+    }
+    if (cg == 0 && l < 32) lse_o[h] = lse;
+  } else {
+    const int h = h0 + (l & 15);
+    float* zh = zo + static_cast<int64_t>(h) * D_C;
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const int cbg = cg * CB + c;
+      const f32x4 v = {zacc[c][0] * inv, zacc[c][1] * inv, zacc[c][2] * inv, zacc[c][3] * inv};
+      *reinterpret_cast<f32x4*>(zh + 16 * cbg + 4 * q16) = v;
+    }
+    if (cg == 0 && l < 16) lse_o[h] = lse;
+  }
+}
+
+// ------------------------------------------------------------------------
+// Generic fp32 VALU path (MLA_F32 storage, or bf16 with an n_h without an MFMA
+// instance).  One workgroup per (query, split, head); 256 rows per step: one
+// thread scores one row, then every thread accumulates two latent columns.
+// ------------------------------------------------------------------------
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const float u = __shfl_xor(v, o);
+    v = is_max ? fmaxf(v, u) : v + u;
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  v = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) v = is_max ? fmaxf(v, red[i]) : v + red[i];
+  return v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void splitkv_generic_kernel(SplitArgs a) {
+  __shared__ float q[D_C + 2 * MAX_PAIRS];
+  __shared__ float pr[256];
+  __shared__ float red[4];
+  const int n = blockIdx.x, split = blockIdx.y, h = blockIdx.z;
+  const int tid = threadIdx.x;
+  int b;
+  int64_t len;
+  query_range(a, n, b, len);
+  const int64_t lo = static_cast<int64_t>(split) * a.split_rows;
+  const int64_t hi = min(lo + a.split_rows, len);
+  const int row_e = a.d_c + a.d_r;
+  float* zo = a.z_part + ((static_cast<int64_t>(n) * a.num_splits + split) * a.n_h + h) * a.d_c;
+  float* lse_o = a.lse_part + (static_cast<int64_t>(n) * a.num_splits + split) * a.n_h + h;
+  if (lo >= hi) {
+    for (int c = tid; c < a.d_c; c += 256) zo[c] = 0.f;
+    if (tid == 0) *lse_o = NEG_INF;
+    return;
+  }
+  const T* qs = static_cast<const T*>(a.q_lat) + (static_cast<int64_t>(n) * a.n_h + h) * row_e;
+  for (int e = tid; e < row_e; e += 256) q[e] = load_as_f32(qs, e);
+  __syncthreads();
+  const T* rows = static_cast<const T*>(a.cache) + static_cast<int64_t>(b) * a.stride * row_e;
+  float m = NEG_INF, lsum = 0.f, z0 = 0.f, z1 = 0.f;
+  for (int64_t base = lo; base < hi; base += 256) {
+    const int cnt = static_cast<int>(min(static_cast<int64_t>(256), hi - base));
+    float s = NEG_INF;
+    if (tid < cnt) {
+      const T* r = rows + (base + tid) * row_e;
+      float acc = 0.f;
+      for (int e = 0; e < row_e; ++e) acc = fmaf(q[e], load_as_f32(r, e), acc);
+      s = acc * a.qscale;
+    }
+    const float mt = block_reduce(s, red, true);
+    const float m_new = fmaxf(m, mt);
+    const float alpha = (m == NEG_INF) ? 0.f : exp2f(m - m_new);
+    const float p = (tid < cnt) ? exp2f(s - m_new) : 0.f;
+    pr[tid] = p;
+    const float ps = block_reduce(p, red, false);  // also orders the pr[] writes
+    lsum = lsum * alpha + ps;
+    z0 *= alpha;
+    z1 *= alpha;
+    m = m_new;
+    for (int r = 0; r < cnt; ++r) {
+      const float pv = pr[r];
+      const T* rr = rows + (base + r) * row_e;
+      if (tid < a.d_c) z0 = fmaf(pv, load_as_f32(rr, tid), z0);
+      if (tid + 256 < a.d_c) z1 = fmaf(pv, load_as_f32(rr, tid + 256), z1);
+    }
+    __syncthreads();
+  }
+  const float inv = 1.f / lsum;
+  if (tid < a.d_c) zo[tid] = z0 * inv;
+  if (tid + 256 < a.d_c) zo[tid + 256] = z1 * inv;
+  if (tid == 0) *lse_o = (m + log2f(lsum)) * LN2;
+}
+
+bool splitkv_has_fast_path(int n_h, int bf16, int d_c, int d_r) {
+  return bf16 && d_c == D_C && d_r == D_R && (n_h == 16 || n_h == 32 || n_h == 64 || n_h == 128);
+}
+
+hipError_t launch_splitkv(const SplitArgs& a, int bf16, hipStream_t st) {
+  if (a.n_q <= 0) return hipSuccess;
+  if (splitkv_has_fast_path(a.n_h, bf16, a.d_c, a.d_r)) {
+    dim3 grid(a.n_q, a.num_splits);
+    switch (a.n_h) {
+      case 16: splitkv_mfma_kernel<16, 4><<<grid, 256, 0, st>>>(a); break;
+      case 32: splitkv_mfma_kernel<32, 4><<<grid, 256, 0, st>>>(a); break;
+      case 64: splitkv_mfma_kernel<32, 2><<<grid, 256, 0, st>>>(a); break;
+      default: splitkv_mfma_kernel<32, 1><<<grid, 256, 0, st>>>(a); break;
+    }
+  } else {
+    dim3 grid(a.n_q, a.num_splits, a.n_h);
+    if (bf16)
+      splitkv_generic_kernel<uint16_t><<<grid, 256, 0, st>>>(a);
+    else
+      splitkv_generic_kernel<float><<<grid, 256, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,151 @@
+"""Device-side setup and one decode/prefill step over the C ABI.
+
+Plumbing only: torch allocates device memory and supplies the stream; every
+computation is a call into the HIP library (api.py).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import api
+from .workloads import D_C, D_R, ROW, DecodeInputs, PrefillInputs
+
+
+def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Storage array (uint16 bf16 bits or float32) -> device tensor of that dtype."""
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype == "bf16":
+        t = t.view(torch.bfloat16)
+    return t.to(device, non_blocking=False)
+
+
+def torch_dtype(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+class DecodeState:
+    """All device buffers of one decode workload, with the cache filled by A1.
+
+    cache rows: sequence b owns rows [b*stride, (b+1)*stride); rows at and past
+    len_b hold NaN so that any read past a length shows up in the output.
+    """
+
+    def __init__(self, inp: DecodeInputs, device="cuda", out_latent=False):
+        w = inp.w
+        self.inp = inp
+        self.device = device
+        self.dt = w.dtype
+        tdt = torch_dtype(w.dtype)
+        self.d = api.dims(w.n_h, rope_base=w.rope_base)
+        self.batch, self.stride = w.batch, inp.stride
+        lens = inp.seq_lens.astype(np.int64)
+        self.max_len = int(lens.max())
+        self.total_rows = int(lens.sum())
+        self.cache = torch.full((self.batch * self.stride, ROW), float("nan"), dtype=tdt, device=device)
+        self.seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(device)
+        # fill: every valid row goes through A1 (RoPE of k_raw at its position)
+        b_idx = np.repeat(np.arange(self.batch, dtype=np.int64), lens)
+        j_idx = np.concatenate([np.arange(L, dtype=np.int64) for L in lens])
+        self.fill_rows = torch.from_numpy(b_idx * self.stride + j_idx).to(device)
+        self.fill_pos = torch.from_numpy(j_idx.astype(np.int32)).to(device)
+        self.fill_c = to_device(inp.c_kv[b_idx, j_idx], w.dtype, device)
+        self.fill_k = to_device(inp.k_raw[b_idx, j_idx], w.dtype, device)
+        # the step's new token of each sequence = its last row
+        last = lens - 1
+        self.new_rows = torch.from_numpy(np.arange(self.batch) * self.stride + last).to(device)
+        self.new_pos = torch.from_numpy(last.astype(np.int32)).to(device)
+        self.new_c = to_device(inp.c_kv[np.arange(self.batch), last], w.dtype, device)
+        self.new_k = to_device(inp.k_raw[np.arange(self.batch), last], w.dtype, device)
+        self.q_c = to_device(inp.q_c, w.dtype, device)
+        self.q_r = to_device(inp.q_r, w.dtype, device)
+        self.q_pos = self.new_pos
+        self.w_uk = to_device(inp.w_uk, w.dtype, device)
+        self.w_uv = to_device(inp.w_uv, w.dtype, device)
+        self.q_lat = torch.empty((self.batch, w.n_h, ROW), dtype=tdt, device=device)
+        self.out = torch.empty((self.batch, w.n_h, 128), dtype=torch.float32, device=device)
+        self.out_latent = (torch.empty((self.batch, w.n_h, D_C), dtype=torch.float32, device=device)
+                           if out_latent else None)
+        self.splits = api.num_splits(self.d, self._api_dtype(), self.batch, self.max_len)
+        self.z_part = torch.empty((self.batch, self.splits, w.n_h, D_C), dtype=torch.float32, device=device)
+        self.lse_part = torch.empty((self.batch, self.splits, w.n_h), dtype=torch.float32, device=device)
+        self.fill_cache()
+
+    def _api_dtype(self):
+        return api.BF16 if self.dt == "bf16" else api.F32
+
+    def fill_cache(self):
+        api.append_kv(self.d, self.fill_c, self.fill_k, self.fill_pos, self.fill_rows, self.cache)
+
+    # --- the steps of one decode pass (A1, A2, A3, A4+A5)
+    def append_new(self):
+        api.append_kv(self.d, self.new_c, self.new_k, self.new_pos, self.new_rows, self.cache)
+
+    def absorb(self):
+        api.absorb_q(self.d, self.q_c, self.q_r, self.q_pos, self.w_uk, self.q_lat)
+
+    def attention(self, splits=None, z_part=None, lse_part=None):
+        S = self.splits if splits is None else splits
+        z = self.z_part if z_part is None else z_part
+        lse = self.lse_part if lse_part is None else lse_part
+        api.decode_partials(self.d, self.q_lat, self.cache, self.stride, self.seq_lens, self.max_len,
+                            S, z, lse)
+        return z, lse
+
+    def combine(self, z=None, lse=None):
+        api.combine_project(self.d, self.z_part if z is None else z, self.lse_part if lse is None else lse,
+                            self.w_uv, self.out, self.out_latent)
+
+    def step(self):
+        """One decode step of one layer: append the new rows, absorb, attend, combine."""
+        self.append_new()
+        self.absorb()
+        self.attention()
+        self.combine()
+        return self.out
+
+
+class PrefillState:
+    """One sequence: prefix rows appended first, then the chunk's rows; chunk queries."""
+
+    def __init__(self, inp: PrefillInputs, device="cuda"):
+        w = inp.w
+        self.inp = inp
+        tdt = torch_dtype(w.dtype)
+        self.d = api.dims(w.n_h, rope_base=w.rope_base)
+        self.dt = w.dtype
+        total = inp.prefix + inp.chunk
+        self.stride = total
+        self.prefix, self.chunk = inp.prefix, inp.chunk
+        self.cache = torch.full((total, ROW), float("nan"), dtype=tdt, device=device)
+        self.rows = torch.arange(total, dtype=torch.int64, device=device)
+        self.pos = torch.arange(total, dtype=torch.int32, device=device)
+        self.c_kv = to_device(inp.c_kv, w.dtype, device)
+        self.k_raw = to_device(inp.k_raw, w.dtype, device)
+        self.q_c = to_device(inp.q_c, w.dtype, device)
+        self.q_r = to_device(inp.q_r, w.dtype, device)
+        self.q_pos = torch.arange(inp.prefix, total, dtype=torch.int32, device=device)
+        self.prefix_lens = torch.tensor([inp.prefix], dtype=torch.int32, device=device)
+        self.w_uk = to_device(inp.w_uk, w.dtype, device)
+        self.w_uv = to_device(inp.w_uv, w.dtype, device)
+        self.q_lat = torch.empty((1, inp.chunk, w.n_h, ROW), dtype=tdt, device=device)
+        self.out = torch.empty((1, inp.chunk, w.n_h, 128), dtype=torch.float32, device=device)
+        dtc = api.BF16 if w.dtype == "bf16" else api.F32
+        ws = api.prefill_workspace_bytes(self.d, dtc, 1, inp.chunk, inp.prefix)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+
+    def append_all(self):
+        api.append_kv(self.d, self.c_kv, self.k_raw, self.pos, self.rows, self.cache)
+
+    def absorb(self):
+        api.absorb_q(self.d, self.q_c, self.q_r, self.q_pos, self.w_uk, self.q_lat.view(-1, self.q_lat.shape[2], ROW))
+
+    def attend(self):
+        api.prefill(self.d, self.q_lat, self.cache, self.stride, self.prefix_lens, self.prefix,
+                    self.w_uv, self.out, self.workspace)
+
+    def step(self):
+        self.append_all()
+        self.absorb()
+        self.attend()
+        return self.out

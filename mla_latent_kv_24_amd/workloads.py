@@ -277,3 +277,14 @@ def make_prefill_inputs(w: Workload) -> PrefillInputs:
     return PrefillInputs(w, prefix, chunk, to_storage(c, w.dtype), to_storage(k, w.dtype),
                          to_storage(q_c, w.dtype), to_storage(q_r, w.dtype),
                          to_storage(w_uk, w.dtype), to_storage(w_uv, w.dtype))
+
+
+def random_storage(seed, shape, dtype: str, std: float = 1.0) -> np.ndarray:
+    """Generic seeded draw N(0, std^2) rounded to the storage dtype (per-kernel test inputs)."""
+    rng = np.random.default_rng(seed)
+    return to_storage(_normal(rng, shape, std), dtype)
+
+
+def random_ints(seed, low: int, high: int, shape) -> np.ndarray:
+    """Seeded integers in [low, high) (positions, lengths, row indices of test inputs)."""
+    return np.random.default_rng(seed).integers(low, high, shape)

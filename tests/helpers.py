@@ -1,0 +1,45 @@
+"""Shared helpers of the GPU parity tests: oracle adapters and error metrics."""
+import numpy as np
+
+import oracle as O
+from mla_latent_kv_24_amd import workloads as W
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}   # max|gpu - ref| / rms(ref), per workload output
+
+
+def rel_err(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(gpu - ref)) / np.sqrt(np.mean(np.square(ref))))
+
+
+def f64(a, dtype):
+    return W.to_f64(a, dtype)
+
+
+def to_np(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.detach().cpu().numpy()
+
+
+def oracle_decode(inp, b, heads=None):
+    """Unabsorbed fp64 oracle for sequence b (selected heads): (out [h, 128], z [h, 512])."""
+    dt = inp.w.dtype
+    L = int(inp.seq_lens[b])
+    heads = np.arange(inp.w.n_h) if heads is None else np.asarray(heads)
+    c = f64(inp.c_kv[b, :L], dt)
+    k_rot = O.rope(f64(inp.k_raw[b, :L], dt), np.arange(L), inp.w.rope_base)
+    q_rot = O.rope(f64(inp.q_r[b][heads], dt), L - 1, inp.w.rope_base)
+    o, a = O.attend_unabsorbed(f64(inp.q_c[b][heads], dt), q_rot, c, k_rot,
+                               f64(inp.w_uk[heads], dt), f64(inp.w_uv[heads], dt))
+    return o, a @ c
+
+
+def oracle_prefill(pinp, queries, heads=None):
+    dt = pinp.w.dtype
+    heads = np.arange(pinp.w.n_h) if heads is None else np.asarray(heads)
+    return O.prefill(f64(pinp.q_c[:, heads], dt), f64(pinp.q_r[:, heads], dt), pinp.prefix,
+                     f64(pinp.c_kv, dt), f64(pinp.k_raw, dt), f64(pinp.w_uk[heads], dt),
+                     f64(pinp.w_uv[heads], dt), pinp.w.rope_base, query_idx=queries)

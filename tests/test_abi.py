@@ -1,0 +1,101 @@
+"""Host-only checks of the C ABI: the library loads without a GPU, exports
+every function declared in include/mla.h, and rejects bad arguments before
+launching anything (the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+api = pytest.importorskip("mla_latent_kv_24_amd.api", reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = api.raw()
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_strings():
+    lib = api.raw()
+    assert lib.mla_abi_version() == 1
+    assert lib.mla_status_string(0) == b"MLA_OK"
+    assert lib.mla_status_string(3) == b"MLA_ERR_WORKSPACE_TOO_SMALL"
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_dims_validation():
+    lib = api.raw()
+    d = api.dims(16)
+    bad = api.dims(16, d_c=256)
+    assert lib.mla_append_kv(None, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.mla_append_kv(ctypes.byref(bad), 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+    odd = api.dims(16, d_hR=63)
+    assert lib.mla_append_kv(ctypes.byref(odd), 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.mla_append_kv(ctypes.byref(d), 7, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1  # dtype
+    zero_heads = api.dims(0)
+    assert lib.mla_absorb_q(ctypes.byref(zero_heads), 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    nan_base = api.dims(16, rope_base=float("nan"))
+    assert lib.mla_append_kv(ctypes.byref(nan_base), 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert b"rope_base" in lib.mla_last_error()
+
+
+def test_null_and_size_validation():
+    lib = api.raw()
+    d = ctypes.byref(api.dims(128))
+    assert lib.mla_append_kv(d, 1, 0, None, None, None, None, None, None) == 0      # n_tok = 0: no-op
+    assert lib.mla_append_kv(d, 1, -1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.mla_append_kv(d, 1, 4, None, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.mla_absorb_q(d, 1, 2, FAKE, None, FAKE, FAKE, FAKE, None) == 1
+    # decode partials: batch, lengths, stride, splits
+    args = lambda B, st, L, S: (d, 1, B, FAKE, FAKE, st, FAKE, L, S, FAKE, FAKE, None)
+    assert lib.mla_decode_partials(*args(0, 100, 10, 1)) == 1
+    assert lib.mla_decode_partials(*args(2, 100, 0, 1)) == 1
+    assert lib.mla_decode_partials(*args(2, 9, 10, 1)) == 1      # stride < max_seq_len
+    assert lib.mla_decode_partials(*args(2, 100, 10, 0)) == 1
+    assert lib.mla_decode_partials(*args(2, 100, 10, 70000)) == 1
+    assert lib.mla_combine_project(d, 1, 0, 1, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert lib.mla_combine_project(d, 1, 4, 1, FAKE, FAKE, None, FAKE, None, None) == 1
+
+
+def test_workspace_validation():
+    lib = api.raw()
+    d = ctypes.byref(api.dims(128))
+    need = lib.mla_decode_workspace_bytes(d, 1, 64, 8192)
+    S = lib.mla_decode_num_splits(d, 1, 64, 8192)
+    assert need >= 64 * S * 128 * 512 * 4
+    st = lib.mla_decode(d, 1, 64, FAKE, FAKE, 8192, FAKE, 8192, FAKE, FAKE, None, FAKE, need - 1, None)
+    assert st == 3
+    assert b"workspace" in lib.mla_last_error()
+    pneed = lib.mla_prefill_workspace_bytes(d, 1, 1, 4096, 4096)
+    assert pneed >= 4096 * 128 * 512 * 4
+    assert lib.mla_prefill(d, 1, 1, 4096, FAKE, FAKE, 8191, FAKE, 4096, FAKE, FAKE, FAKE, pneed, None) == 1
+    assert lib.mla_prefill(d, 1, 1, 4096, FAKE, FAKE, 8192, FAKE, 4096, FAKE, FAKE, FAKE, pneed - 1, None) == 3
+
+
+def test_split_plan_covers_every_row():
+    for L in (1, 31, 32, 33, 4096, 8192, 32768, 131072):
+        for S in (1, 2, 3, 7, 64):
+            R = api.split_rows(L, S)
+            assert R % 32 == 0 and R * S >= L and (R - 32) * S < L + 32 * S
+    d = api.dims(128)
+    assert api.num_splits(d, api.BF16, 64, 8192) == 4          # 64 x 4 = 256 workgroups
+    assert api.num_splits(d, api.BF16, 4, 131072) == 64
+    assert api.num_splits(d, api.BF16, 4096, 8192) == 1
+    assert api.num_splits(api.dims(16), api.BF16, 1, 100) == 1
