@@ -87,13 +87,13 @@ mla_status mla_append_kv(const mla_dims* dims, mla_dtype dtype, int32_t n_tok,
  * query; section 3: per-head RoPE query).
  *   q_c [n_q][n_h][d_h], q_r [n_q][n_h][d_hR] (pre-RoPE), q_pos [n_q],
  *   w_uk [n_h][d_h][d_c] (U^K_i = w_uk[i], so k^C = U^K_i c)
- *   q_lat [n_q][n_h][d_c + d_hR]:
- *     q_lat[n][i][0:d_c]   = sum_d q_c[n][i][d] * w_uk[i][d][:]
+ *   q_lat [n_q][n_h][d_c + d_hR], fp32 for every storage dtype:
+ *     q_lat[n][i][0:d_c]   = sum_d q_c[n][i][d] * w_uk[i][d][:]   (fp32 sum)
  *     q_lat[n][i][d_c:]    = RoPE(q_r[n][i], q_pos[n])
- * q_lat has the storage dtype (bf16 rounding for MLA_BF16). */
+ * q_c, q_r and w_uk have the storage dtype. */
 mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q,
                         const void* q_c, const void* q_r, const int32_t* q_pos,
-                        const void* w_uk, void* q_lat, void* stream);
+                        const void* w_uk, float* q_lat, void* stream);
 
 /* Split-KV plan.  Sequence rows [0, len) are cut into `num_splits` ranges of
  * mla_split_rows(max_seq_len, num_splits) rows each (split s covers
@@ -109,7 +109,9 @@ int64_t mla_split_rows(int32_t max_seq_len, int32_t num_splits);
  *   lse_part[n][s][i]      = log sum_j exp(l_ij)                (natural log)
  *   z_part[n][s][i][0:d_c] = sum_j exp(l_ij - lse) * c_j        (fp32)
  * An empty split stores lse = -inf and z = 0.
- *   q_lat [batch][n_h][d_c + d_hR]   (output of A2)
+ *   q_lat [batch][n_h][d_c + d_hR] fp32 (output of A2).  The bf16 MFMA path
+ *   feeds it to the matrix cores as bf16 (n_h >= 32: one rounding; n_h = 16:
+ *   hi + lo parts, i.e. ~16 significant bits); the cache has the storage dtype.
  *   cache rows of sequence b start at row b * cache_seq_stride
  *   seq_lens [batch]: 1 <= len <= min(max_seq_len, cache_seq_stride)
  *   max_seq_len (host) bounds every len; it fixes the split rows.
@@ -119,7 +121,7 @@ int64_t mla_split_rows(int32_t max_seq_len, int32_t num_splits);
  * A device-side length outside [1, stride] is clamped for memory safety
  * (len < 1 behaves as an empty sequence: lse = -inf for every split). */
 mla_status mla_decode_partials(const mla_dims* dims, mla_dtype dtype, int32_t batch,
-                               const void* q_lat, const void* cache,
+                               const float* q_lat, const void* cache,
                                int64_t cache_seq_stride, const int32_t* seq_lens,
                                int32_t max_seq_len, int32_t num_splits,
                                float* z_part, float* lse_part, void* stream);
@@ -140,7 +142,7 @@ mla_status mla_combine_project(const mla_dims* dims, mla_dtype dtype, int32_t n_
 size_t mla_decode_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t batch,
                                   int32_t max_seq_len);
 mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch,
-                      const void* q_lat, const void* cache, int64_t cache_seq_stride,
+                      const float* q_lat, const void* cache, int64_t cache_seq_stride,
                       const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv,
                       float* out, float* out_latent, void* workspace,
                       size_t workspace_bytes, void* stream);
@@ -150,14 +152,14 @@ mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch,
  * sits at position prefix_lens[b] + i and attends to rows 0..prefix_lens[b]+i
  * (inclusive causal mask), with the same score, softmax and W^UV lift as
  * decode (review section 3).
- *   q_lat [batch][chunk][n_h][d_c + d_hR], prefix_lens [batch] (device,
+ *   q_lat [batch][chunk][n_h][d_c + d_hR] fp32, prefix_lens [batch] (device,
  *   0 <= prefix <= max_prefix_len), max_prefix_len (host) with
  *   max_prefix_len + chunk <= cache_seq_stride,
  *   out fp32 [batch][chunk][n_h][d_h]. */
 size_t mla_prefill_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t batch,
                                    int32_t chunk, int32_t max_prefix_len);
 mla_status mla_prefill(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk,
-                       const void* q_lat, const void* cache, int64_t cache_seq_stride,
+                       const float* q_lat, const void* cache, int64_t cache_seq_stride,
                        const int32_t* prefix_lens, int32_t max_prefix_len,
                        const void* w_uv, float* out, void* workspace,
                        size_t workspace_bytes, void* stream);

@@ -109,9 +109,9 @@ def append_kv(d: Dims, c_kv, k_r, pos, row, cache) -> None:
 
 
 def absorb_q(d: Dims, q_c, q_r, q_pos, w_uk, q_lat) -> None:
-    """A2: q_lat[n, i] = [q_c[n, i] @ w_uk[i]; RoPE(q_r[n, i], q_pos[n])]."""
-    assert q_pos.dtype == torch.int32
-    _check(_lib.mla_absorb_q(ctypes.byref(d), _dtype(q_lat), q_c.shape[0], _ptr(q_c), _ptr(q_r),
+    """A2: q_lat[n, i] = [q_c[n, i] @ w_uk[i]; RoPE(q_r[n, i], q_pos[n])] (q_lat fp32)."""
+    assert q_pos.dtype == torch.int32 and q_lat.dtype == torch.float32
+    _check(_lib.mla_absorb_q(ctypes.byref(d), _dtype(w_uk), q_c.shape[0], _ptr(q_c), _ptr(q_r),
                              _ptr(q_pos), _ptr(w_uk), _ptr(q_lat), _stream(q_lat.device)),
            "mla_absorb_q")
 

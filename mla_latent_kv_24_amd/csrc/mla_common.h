@@ -38,22 +38,22 @@ struct AppendArgs {
 };
 
 struct RopeQArgs {
-  const void* q_r;       // [n_q][n_h][d_r]
+  const void* q_r;       // [n_q][n_h][d_r] (storage dtype)
   const int32_t* q_pos;  // [n_q]
-  void* q_lat;           // [n_q][n_h][d_c + d_r]
+  float* q_lat;          // [n_q][n_h][d_c + d_r], fp32
   int32_t n_q, n_h, d_c, d_r;
   RopeTable rope;
 };
 
 struct AbsorbArgs {
-  const void* q_c;   // [n_q][n_h][d_h]
-  const void* w_uk;  // [n_h][d_h][d_c]
-  void* q_lat;       // [n_q][n_h][d_c + d_r]
+  const void* q_c;   // [n_q][n_h][d_h] (storage dtype)
+  const void* w_uk;  // [n_h][d_h][d_c] (storage dtype)
+  float* q_lat;      // [n_q][n_h][d_c + d_r], fp32
   int32_t n_q, n_h, d_c, d_h, d_r;
 };
 
 struct SplitArgs {
-  const void* q_lat;      // [n_q][n_h][d_c + d_r]
+  const float* q_lat;     // [n_q][n_h][d_c + d_r], fp32
   const void* cache;      // rows of d_c + d_r
   const int32_t* lens;    // decode: seq_lens[batch]; prefill: prefix_lens[batch]
   float* z_part;          // [n_q][num_splits][n_h][d_c]

@@ -79,6 +79,33 @@ __device__ __forceinline__ bf16x8 cat(i16x4 a, i16x4 b) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Reductions over the lanes that hold the same head (lane ^ 32, and lane ^ 16
+// for 16 heads per wave).  v_permlane32_swap / v_permlane16_swap (issued with
+// the same value in both operands) return the lane's value and its partner's,
+// so op(r[0], r[1]) is the pair result.  The empty asm pins both results in
+// their registers: without it this compiler folds r[1] into r[0].
+template <bool SWAP16>
+__device__ __forceinline__ void pair_vals(float v, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  unsigned x, y;
+  if constexpr (SWAP16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = r[0];
+    y = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    x = r[0];
+    y = r[1];
+  }
+  asm volatile("" : "+v"(x), "+v"(y));
+  a = __builtin_bit_cast(float, x);
+  b = __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float pair_max32(float v) { float a, b; pair_vals<false>(v, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float pair_max16(float v) { float a, b; pair_vals<true>(v, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float pair_sum32(float v) { float a, b; pair_vals<false>(v, a, b); return a + b; }
+__device__ __forceinline__ float pair_sum16(float v) { float a, b; pair_vals<true>(v, a, b); return a + b; }
+
 // Query n -> (sequence, attended length), the length clamped to [0, min(max_len, stride)].
 __device__ __forceinline__ void query_range(const SplitArgs& a, int n, int& b, int64_t& len) {
   b = n / a.q_per_seq;
@@ -90,7 +117,7 @@ __device__ __forceinline__ void query_range(const SplitArgs& a, int n, int& b, i
 }
 
 template <int HPW, int CG>
-__global__ __launch_bounds__(256, (HPW == 32 && CG == 1) ? 1 : 2) void splitkv_mfma_kernel(
+__global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
     SplitArgs a) {
   constexpr int NHG = 4 / CG;                    // head groups per workgroup
   constexpr int COLS = D_C / CG;                 // latent columns per wave
@@ -99,10 +126,11 @@ __global__ __launch_bounds__(256, (HPW == 32 && CG == 1) ? 1 : 2) void splitkv_m
   constexpr int NQ = (HPW == 32) ? 36 : 18;      // score k-steps: 576/16 or 576/32
   constexpr int NSC = (HPW == 32) ? 16 : 8;      // scores held per lane per tile
   constexpr int LOADS = TILE_BYTES / (16 * 256);  // 9 chunk loads per thread per tile
+  constexpr int PF = 4;                          // LDS operand prefetch depth (MFMA steps)
   static_assert(TILE_BYTES == LOADS * 16 * 256, "tile must split evenly over 256 threads");
   typedef typename std::conditional<HPW == 32, f32x16, f32x4>::type acc_t;
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_BYTES + 9 * 256 * 4];  // tile ring + DMA offset table
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int hg = w % NHG, cg = w / NHG;
@@ -127,34 +155,11 @@ __global__ __launch_bounds__(256, (HPW == 32 && CG == 1) ? 1 : 2) void splitkv_m
 
   const int g32 = l >> 5, q16 = l >> 4, j16 = l & 15;
 
-  // ---- absorbed queries of this wave's heads -> B-operand registers
-  u32x4 qreg[NQ];
-  {
-    const uint16_t* q =
-        static_cast<const uint16_t*>(a.q_lat) + static_cast<int64_t>(n) * a.n_h * ROWE;
-    if constexpr (HPW == 32) {
-      const uint16_t* qh = q + (h0 + (l & 31)) * ROWE + 8 * g32;
-#pragma unroll
-      for (int s = 0; s < NQ; ++s) qreg[s] = *reinterpret_cast<const u32x4*>(qh + 16 * s);
-    } else {
-      const uint16_t* qh = q + (h0 + (l & 15)) * ROWE + 8 * q16;
-#pragma unroll
-      for (int s = 0; s < NQ; ++s) qreg[s] = *reinterpret_cast<const u32x4*>(qh + 32 * s);
-    }
-  }
-
-  vm_wait<0>();  // queries resident before any tile DMA is issued (keeps the loop free of waits)
-
   // ---- tile loads: LDS chunk f = tid + 256 i of the tile receives global
-  // chunk (t, p ^ swz(t)) with (t, p) = (f / 72, f % 72)
+  // chunk (t, p ^ swz(t)) with (t, p) = (f / 72, f % 72).  Nothing the loop
+  // reads may be spilled: a spilled value comes back through a VMEM reload that
+  // the compiler would then fence every (asm) DMA on.
   constexpr int NBUF = 4;
-  int voff[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int f = tid + 256 * i;
-    const int t = f / 72, p = f % 72;
-    voff[i] = 16 * (t * 72 + (p ^ swz(t)));
-  }
   const uint8_t* gsplit =
       static_cast<const uint8_t*>(a.cache) + (static_cast<int64_t>(b) * a.stride + lo) * ROWB;
   // One buffer resource per tile, based at the tile's first row and sized to
@@ -165,15 +170,76 @@ __global__ __launch_bounds__(256, (HPW == 32 && CG == 1) ? 1 : 2) void splitkv_m
   const uint32_t lds_w = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
                              (__attribute__((address_space(3))) uint8_t*)smem)) +
                          1024u * static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(w));
-  auto issue = [&](int64_t it) {
+  // source byte offset (inside the tile) of the chunk that lands in LDS slot tid + 256 i
+  auto chunk_off = [&](int i, int z) {
+    const int f = tid + 256 * i + z;
+    const int t = f / 72, p = f - 72 * t;
+    return 16 * (f - p + (p ^ swz(t)));
+  };
+  auto tile_rsrc = [&](int64_t it) {
     const uint64_t ga = gaddr + static_cast<uint64_t>(it) * TILE_BYTES;
     const int64_t rows = min(static_cast<int64_t>(TILE), hi - lo - it * TILE);
     const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(ga & 0xffffffffu)),
                       __builtin_amdgcn_readfirstlane(static_cast<int>((ga >> 32) & 0xffffu)),
                       __builtin_amdgcn_readfirstlane(static_cast<int>(rows * ROWB)), 0x00020000};
+    return rs;
+  };
+  // prologue issues: offsets recomputed (registers are scarce while the queries load)
+  auto issue_direct = [&](int64_t it) {
+    const i32x4 rs = tile_rsrc(it);
     const uint32_t dst = lds_w + static_cast<uint32_t>((it & (NBUF - 1)) * TILE_BYTES);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) dma16(dst + 4096u * i, voff[i], rs, 0);
+    for (int i = 0; i < LOADS; ++i) dma16(dst + 4096u * i, chunk_off(i, 0), rs, 0);
+  };
+
+  // the first tiles stream in while the queries load
+  issue_direct(0);
+  if (ntiles > 1) issue_direct(1);
+  if (ntiles > 2) issue_direct(2);
+
+  // ---- absorbed queries (fp32 in memory) -> bf16 B-operand registers.  With
+  // 16 heads the query is kept as hi + lo bf16 parts and scored twice (the
+  // path has MFMA to spare there, and short sequences need the extra
+  // precision); with 32 heads per wave the register file holds only hi.
+  u32x4 qreg[NQ];
+  u32x4 qlo[HPW == 16 ? NQ : 1];
+  {
+    const float* q = a.q_lat + static_cast<int64_t>(n) * a.n_h * ROWE;
+    const float* qh = (HPW == 32) ? q + (h0 + (l & 31)) * ROWE + 8 * g32
+                                  : q + (h0 + (l & 15)) * ROWE + 8 * q16;
+    constexpr int QSTEP = (HPW == 32) ? 16 : 32;
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(qh + QSTEP * s);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(qh + QSTEP * s + 4);
+      bf16x8 hi8, lo8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi8[i] = static_cast<__bf16>(x0[i]);
+        hi8[4 + i] = static_cast<__bf16>(x1[i]);
+        lo8[i] = static_cast<__bf16>(x0[i] - static_cast<float>(hi8[i]));
+        lo8[4 + i] = static_cast<__bf16>(x1[i] - static_cast<float>(hi8[4 + i]));
+      }
+      qreg[s] = __builtin_bit_cast(u32x4, hi8);
+      if constexpr (HPW == 16) qlo[s] = __builtin_bit_cast(u32x4, lo8);
+    }
+  }
+  vm_wait<0>();  // queries and the first tiles resident: the loop itself carries no compiler waits
+
+  // loop issues: each thread's 9 source offsets live in a small LDS table (the
+  // loop's register budget has no room for them, and a spilled copy would come
+  // back through VMEM reloads)
+  int* voff_tab = reinterpret_cast<int*>(smem + NBUF * TILE_BYTES);
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) voff_tab[i * 256 + tid] = chunk_off(i, 0);
+  auto issue = [&](int64_t it) {
+    const i32x4 rs = tile_rsrc(it);
+    const uint32_t dst = lds_w + static_cast<uint32_t>((it & (NBUF - 1)) * TILE_BYTES);
+    int vo[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) vo[i] = voff_tab[i * 256 + tid];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) dma16(dst + 4096u * i, vo[i], rs, 0);
   };
 
   // ---- per-lane LDS offsets of the MFMA operands
@@ -213,10 +279,6 @@ __global__ __launch_bounds__(256, (HPW == 32 && CG == 1) ? 1 : 2) void splitkv_m
     for (int r = 0; r < ZR; ++r) zacc[c][r] = 0.f;
   float m_run = NEG_INF, l_run = 0.f;
 
-  issue(0);
-  if (ntiles > 1) issue(1);
-  if (ntiles > 2) issue(2);
-
   for (int64_t it = 0; it < ntiles; ++it) {
     // tile `it` must have landed: the loads of the (up to 2) later tiles may stay in flight
     if (it + 2 < ntiles)
@@ -227,53 +289,95 @@ __global__ __launch_bounds__(256, (HPW == 32 && CG == 1) ? 1 : 2) void splitkv_m
       vm_wait<0>();
     __syncthreads();
     const uint8_t* buf = smem + (it & (NBUF - 1)) * TILE_BYTES;
-    const int64_t valid = hi - (lo + it * TILE);  // rows of this tile inside the split (>= 1)
+    // rows of this tile inside the split (1..32); only a partial tile needs masking
+    const int valid = static_cast<int>(min(hi - (lo + it * TILE), static_cast<int64_t>(TILE)));
 
     // -------------------------------------------------- score S^T = rows . q
     float x[NSC];
     if constexpr (HPW == 32) {
+      // operands are read PF steps ahead of their MFMA; each (read, MFMA) pair is
+      // pinned in place so the LDS latency hides behind the previous MFMAs
       f32x16 sacc = {0};
+      u32x4 kb[PF];
+#pragma unroll
+      for (int s = 0; s < PF; ++s) kb[s] = *reinterpret_cast<const u32x4*>(buf + sc_off[s & 3] + 128 * (s >> 2));
 #pragma unroll
       for (int s = 0; s < NQ; ++s) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(buf + sc_off[s & 3] + 128 * (s >> 2));
+        const u32x4 kv = kb[s % PF];
+        if (s + PF < NQ)
+          kb[s % PF] = *reinterpret_cast<const u32x4*>(buf + sc_off[(s + PF) & 3] + 128 * ((s + PF) >> 2));
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv),
                                                        __builtin_bit_cast(bf16x8, qreg[s]), sacc, 0, 0, 0);
-        if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int t = 8 * (j >> 2) + 4 * g32 + (j & 3);
-        x[j] = (t < valid) ? sacc[j] * a.qscale : NEG_INF;
+      for (int j = 0; j < 16; ++j) x[j] = sacc[j];
+      if (valid < TILE) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (8 * (j >> 2) + 4 * g32 + (j & 3) >= valid) x[j] = NEG_INF;
       }
     } else {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         f32x4 sacc = {0};
+        u32x4 kb[PF];
+#pragma unroll
+        for (int s = 0; s < PF; ++s)
+          kb[s] = *reinterpret_cast<const u32x4*>(buf + tb * 16 * ROWB + sc_off[s & 1] + 128 * (s >> 1));
 #pragma unroll
         for (int s = 0; s < NQ; ++s) {
-          const u32x4 kv = *reinterpret_cast<const u32x4*>(buf + tb * 16 * ROWB + sc_off[s & 1] +
-                                                           128 * (s >> 1));
+          const u32x4 kv = kb[s % PF];
+          if (s + PF < NQ)
+            kb[s % PF] = *reinterpret_cast<const u32x4*>(buf + tb * 16 * ROWB + sc_off[(s + PF) & 1] +
+                                                         128 * ((s + PF) >> 1));
           sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
                                                          __builtin_bit_cast(bf16x8, qreg[s]), sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
+                                                         __builtin_bit_cast(bf16x8, qlo[s]), sacc, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = 16 * tb + 4 * q16 + j;
-          x[4 * tb + j] = (t < valid) ? sacc[j] * a.qscale : NEG_INF;
+        for (int j = 0; j < 4; ++j) x[4 * tb + j] = sacc[j];
+        if (valid < TILE) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (16 * tb + 4 * q16 + j >= valid) x[4 * tb + j] = NEG_INF;
         }
       }
     }
 
-    // -------------------------------------------------- online softmax (log2)
-    float mt = x[0];
+    // first value operands: they do not depend on P, so their LDS latency
+    // overlaps the softmax below
+    constexpr int VSTEPS = (HPW == 32) ? 2 * CB : CB;
+    auto vread = [&](int st) -> bf16x8 {
+      if constexpr (HPW == 32) {
+        const int cbg = cg * CB + (st >> 1), u = st & 1;
+        const uint8_t* bu = buf + 128 * (cbg >> 1) + 16 * u * ROWB;
+        return cat(tr_read(bu + tr_off[0][cbg & 1]), tr_read(bu + tr_off[1][cbg & 1]));
+      } else {
+        const int cbg = cg * CB + st;
+        const uint8_t* base = buf + 128 * (cbg >> 2);
+        return cat(tr_read(base + tr_off[0][cbg & 3]), tr_read(base + tr_off[1][cbg & 3]));
+      }
+    };
+    bf16x8 vb[PF];
 #pragma unroll
-    for (int j = 1; j < NSC; ++j) mt = fmaxf(mt, x[j]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    if constexpr (HPW == 16) mt = fmaxf(mt, __shfl_xor(mt, 16));
+    for (int st = 0; st < PF; ++st) vb[st] = vread(st);
+
+    // -------------------------------------------------- online softmax (log2)
+    // raw scores x; the scale is folded into one FMA per element: p = 2^(x*c - m),
+    // with c = scale*log2(e) > 0 so max(x*c) = c*max(x)
+    float mx = x[0];
+#pragma unroll
+    for (int j = 1; j < NSC; ++j) mx = fmaxf(mx, x[j]);
+    mx = pair_max32(mx);
+    if constexpr (HPW == 16) mx = pair_max16(mx);
+    const float mt = mx * a.qscale;
     const bool need = mt > m_run + RESCALE_TAU;
     if (__ballot(need)) {
       const float m_new = need ? mt : m_run;
-      const float alpha = (m_run == NEG_INF) ? 0.f : exp2f(m_run - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 when m_run = -inf
       l_run *= alpha;
 #pragma unroll
       for (int c = 0; c < CB; ++c)
@@ -287,10 +391,11 @@ __global__ __launch_bounds__(256, (HPW == 32 && CG == 1) ? 1 : 2) void splitkv_m
         }
       m_run = m_new;
     }
+    const float neg_m = -m_run;
     float p[NSC];
 #pragma unroll
     for (int j = 0; j < NSC; ++j) {
-      p[j] = exp2f(x[j] - m_run);
+      p[j] = __builtin_amdgcn_exp2f(fmaf(x[j], a.qscale, neg_m));
       l_run += p[j];
     }
 
@@ -302,27 +407,22 @@ __global__ __launch_bounds__(256, (HPW == 32 && CG == 1) ? 1 : 2) void splitkv_m
 #pragma unroll
         for (int i = 0; i < 8; ++i) pb[u][i] = static_cast<__bf16>(p[8 * u + i]);
 #pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        const int cbg = cg * CB + c;  // 32-column block index
-        const uint8_t* base = buf + 128 * (cbg >> 1);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const uint8_t* bu = base + 16 * u * ROWB;
-          const bf16x8 va = cat(tr_read(bu + tr_off[0][cbg & 1]), tr_read(bu + tr_off[1][cbg & 1]));
-          zacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[u], zacc[c], 0, 0, 0);
-        }
-        if (c & 1) __builtin_amdgcn_sched_barrier(0);
+      for (int st = 0; st < VSTEPS; ++st) {
+        const bf16x8 va = vb[st % PF];
+        if (st + PF < VSTEPS) vb[st % PF] = vread(st + PF);
+        zacc[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[st & 1], zacc[st >> 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
       bf16x8 pb;
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(p[i]);
 #pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        const int cbg = cg * CB + c;  // 16-column block index
-        const uint8_t* base = buf + 128 * (cbg >> 2);
-        const bf16x8 va = cat(tr_read(base + tr_off[0][cbg & 3]), tr_read(base + tr_off[1][cbg & 3]));
-        zacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, zacc[c], 0, 0, 0);
+      for (int st = 0; st < VSTEPS; ++st) {
+        const bf16x8 va = vb[st % PF];
+        if (st + PF < VSTEPS) vb[st % PF] = vread(st + PF);
+        zacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, zacc[st], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -330,35 +430,54 @@ __global__ __launch_bounds__(256, (HPW == 32 && CG == 1) ? 1 : 2) void splitkv_m
     if (it + 3 < ntiles) issue(it + 3);
   }
 
-  // ---- finalize: total over the lanes sharing a head, normalise, store
-  float lt = l_run + __shfl_xor(l_run, 32);
-  if constexpr (HPW == 16) lt += __shfl_xor(lt, 16);
+  // ---- finalize: total over the lanes sharing a head, normalise, store.  The
+  // normalised Z is staged row-major in the (now idle) LDS ring so that the
+  // global stores are contiguous 16-byte runs along each head's row.
+  float lt = pair_sum32(l_run);
+  if constexpr (HPW == 16) lt = pair_sum16(lt);
   const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
   const float lse = (lt > 0.f) ? (m_run + log2f(lt)) * LN2 : NEG_INF;
-  if constexpr (HPW == 32) {
-    const int h = h0 + (l & 31);
-    float* zh = zo + static_cast<int64_t>(h) * D_C;
+  if (cg == 0 && l < HPW) lse_o[h0 + l] = lse;
+
+  constexpr int WH = NHG * HPW;                                        // heads of the query (= n_h)
+  constexpr int PCOLS = (WH * (D_C * 4 + 16) <= NBUF * TILE_BYTES) ? D_C : D_C / 2;
+  constexpr int RS = PCOLS * 4 + 16;                                   // staged row stride (bytes)
+  static_assert(WH * RS <= NBUF * TILE_BYTES, "staging must fit the LDS ring");
+  float* zq = a.z_part + (static_cast<int64_t>(n) * a.num_splits + split) * a.n_h * D_C;
 #pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      const int cbg = cg * CB + c;
+  for (int pass = 0; pass < D_C / PCOLS; ++pass) {
+    const int cbase = pass * PCOLS;
+    __syncthreads();  // every wave is done with the ring (tiles, or the previous pass)
+    if constexpr (HPW == 32) {
+      uint8_t* row = smem + (h0 + (l & 31)) * RS;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const f32x4 v = {zacc[c][4 * jj] * inv, zacc[c][4 * jj + 1] * inv, zacc[c][4 * jj + 2] * inv,
-                         zacc[c][4 * jj + 3] * inv};
-        *reinterpret_cast<f32x4*>(zh + 32 * cbg + 8 * jj + 4 * g32) = v;
+      for (int c = 0; c < CB; ++c) {
+        const int cbg = cg * CB + c;
+        if (32 * cbg < cbase || 32 * cbg >= cbase + PCOLS) continue;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 v = {zacc[c][4 * jj] * inv, zacc[c][4 * jj + 1] * inv, zacc[c][4 * jj + 2] * inv,
+                           zacc[c][4 * jj + 3] * inv};
+          *reinterpret_cast<f32x4*>(row + 4 * (32 * cbg + 8 * jj + 4 * g32 - cbase)) = v;
+        }
+      }
+    } else {
+      uint8_t* row = smem + (h0 + (l & 15)) * RS;
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const int cbg = cg * CB + c;
+        if (16 * cbg < cbase || 16 * cbg >= cbase + PCOLS) continue;
+        const f32x4 v = {zacc[c][0] * inv, zacc[c][1] * inv, zacc[c][2] * inv, zacc[c][3] * inv};
+        *reinterpret_cast<f32x4*>(row + 4 * (16 * cbg + 4 * q16 - cbase)) = v;
       }
     }
-    if (cg == 0 && l < 32) lse_o[h] = lse;
-  } else {
-    const int h = h0 + (l & 15);
-    float* zh = zo + static_cast<int64_t>(h) * D_C;
-#pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      const int cbg = cg * CB + c;
-      const f32x4 v = {zacc[c][0] * inv, zacc[c][1] * inv, zacc[c][2] * inv, zacc[c][3] * inv};
-      *reinterpret_cast<f32x4*>(zh + 16 * cbg + 4 * q16) = v;
+    __syncthreads();
+    constexpr int CH = PCOLS / 4;  // 16-byte chunks per staged row
+    for (int idx = tid; idx < WH * CH; idx += 256) {
+      const int r = idx / CH, k = idx % CH;
+      *reinterpret_cast<f32x4*>(zq + static_cast<int64_t>(r) * D_C + cbase + 4 * k) =
+          *reinterpret_cast<const f32x4*>(smem + r * RS + 16 * k);
     }
-    if (cg == 0 && l < 16) lse_o[h] = lse;
   }
 }
 
@@ -401,8 +520,8 @@ __global__ __launch_bounds__(256) void splitkv_generic_kernel(SplitArgs a) {
     if (tid == 0) *lse_o = NEG_INF;
     return;
   }
-  const T* qs = static_cast<const T*>(a.q_lat) + (static_cast<int64_t>(n) * a.n_h + h) * row_e;
-  for (int e = tid; e < row_e; e += 256) q[e] = load_as_f32(qs, e);
+  const float* qs = a.q_lat + (static_cast<int64_t>(n) * a.n_h + h) * row_e;
+  for (int e = tid; e < row_e; e += 256) q[e] = qs[e];
   __syncthreads();
   const T* rows = static_cast<const T*>(a.cache) + static_cast<int64_t>(b) * a.stride * row_e;
   float m = NEG_INF, lsum = 0.f, z0 = 0.f, z1 = 0.f;

@@ -62,7 +62,7 @@ class DecodeState:
         self.q_pos = self.new_pos
         self.w_uk = to_device(inp.w_uk, w.dtype, device)
         self.w_uv = to_device(inp.w_uv, w.dtype, device)
-        self.q_lat = torch.empty((self.batch, w.n_h, ROW), dtype=tdt, device=device)
+        self.q_lat = torch.empty((self.batch, w.n_h, ROW), dtype=torch.float32, device=device)
         self.out = torch.empty((self.batch, w.n_h, 128), dtype=torch.float32, device=device)
         self.out_latent = (torch.empty((self.batch, w.n_h, D_C), dtype=torch.float32, device=device)
                            if out_latent else None)
@@ -128,7 +128,7 @@ class PrefillState:
         self.prefix_lens = torch.tensor([inp.prefix], dtype=torch.int32, device=device)
         self.w_uk = to_device(inp.w_uk, w.dtype, device)
         self.w_uv = to_device(inp.w_uv, w.dtype, device)
-        self.q_lat = torch.empty((1, inp.chunk, w.n_h, ROW), dtype=tdt, device=device)
+        self.q_lat = torch.empty((1, inp.chunk, w.n_h, ROW), dtype=torch.float32, device=device)
         self.out = torch.empty((1, inp.chunk, w.n_h, 128), dtype=torch.float32, device=device)
         dtc = api.BF16 if w.dtype == "bf16" else api.F32
         ws = api.prefill_workspace_bytes(self.d, dtc, 1, inp.chunk, inp.prefix)
