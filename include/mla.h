@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 typedef enum {
   MLA_OK = 0,
@@ -87,13 +87,20 @@ mla_status mla_append_kv(const mla_dims* dims, mla_dtype dtype, int32_t n_tok,
  * query; section 3: per-head RoPE query).
  *   q_c [n_q][n_h][d_h], q_r [n_q][n_h][d_hR] (pre-RoPE), q_pos [n_q],
  *   w_uk [n_h][d_h][d_c] (U^K_i = w_uk[i], so k^C = U^K_i c)
- *   q_lat [n_q][n_h][d_c + d_hR], fp32 for every storage dtype:
- *     q_lat[n][i][0:d_c]   = sum_d q_c[n][i][d] * w_uk[i][d][:]   (fp32 sum)
- *     q_lat[n][i][d_c:]    = RoPE(q_r[n][i], q_pos[n])
- * q_c, q_r and w_uk have the storage dtype. */
+ * Each absorbed query row v (d_c + d_hR values) is formed in fp32:
+ *     v[0:d_c] = sum_d q_c[n][i][d] * w_uk[i][d][:]   (fp32 sum)
+ *     v[d_c:]  = RoPE(q_r[n][i], q_pos[n])
+ * and written to q_lat in the "absorbed query layout" of the storage dtype:
+ *   MLA_F32:  float    [n_q][n_h][d_c + d_hR]      q_lat[n][i][e] = v[e]
+ *   MLA_BF16: bfloat16 [n_q][n_h][2][d_c + d_hR]   part 0 = hi = bf16(v),
+ *             part 1 = lo = bf16(v - hi), both rounded to nearest even, so
+ *             hi + lo carries v to ~2^-17 relative.  hi is the matrix-core
+ *             operand; lo refines it where a path needs more precision.
+ * Both layouts take (d_c + d_hR) * 4 bytes per head.  q_c, q_r and w_uk have
+ * the storage dtype. */
 mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q,
                         const void* q_c, const void* q_r, const int32_t* q_pos,
-                        const void* w_uk, float* q_lat, void* stream);
+                        const void* w_uk, void* q_lat, void* stream);
 
 /* Split-KV plan.  Sequence rows [0, len) are cut into `num_splits` ranges of
  * mla_split_rows(max_seq_len, num_splits) rows each (split s covers
@@ -109,9 +116,9 @@ int64_t mla_split_rows(int32_t max_seq_len, int32_t num_splits);
  *   lse_part[n][s][i]      = log sum_j exp(l_ij)                (natural log)
  *   z_part[n][s][i][0:d_c] = sum_j exp(l_ij - lse) * c_j        (fp32)
  * An empty split stores lse = -inf and z = 0.
- *   q_lat [batch][n_h][d_c + d_hR] fp32 (output of A2).  The bf16 MFMA path
- *   feeds it to the matrix cores as bf16 (n_h >= 32: one rounding; n_h = 16:
- *   hi + lo parts, i.e. ~16 significant bits); the cache has the storage dtype.
+ *   q_lat: batch queries in the absorbed query layout of `dtype` (output of
+ *   A2).  The bf16 MFMA kernels use hi alone for n_h >= 32 and hi + lo for
+ *   n_h = 16; every other path uses hi + lo.  The cache has the storage dtype.
  *   cache rows of sequence b start at row b * cache_seq_stride
  *   seq_lens [batch]: 1 <= len <= min(max_seq_len, cache_seq_stride)
  *   max_seq_len (host) bounds every len; it fixes the split rows.
@@ -121,7 +128,7 @@ int64_t mla_split_rows(int32_t max_seq_len, int32_t num_splits);
  * A device-side length outside [1, stride] is clamped for memory safety
  * (len < 1 behaves as an empty sequence: lse = -inf for every split). */
 mla_status mla_decode_partials(const mla_dims* dims, mla_dtype dtype, int32_t batch,
-                               const float* q_lat, const void* cache,
+                               const void* q_lat, const void* cache,
                                int64_t cache_seq_stride, const int32_t* seq_lens,
                                int32_t max_seq_len, int32_t num_splits,
                                float* z_part, float* lse_part, void* stream);
@@ -142,7 +149,7 @@ mla_status mla_combine_project(const mla_dims* dims, mla_dtype dtype, int32_t n_
 size_t mla_decode_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t batch,
                                   int32_t max_seq_len);
 mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch,
-                      const float* q_lat, const void* cache, int64_t cache_seq_stride,
+                      const void* q_lat, const void* cache, int64_t cache_seq_stride,
                       const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv,
                       float* out, float* out_latent, void* workspace,
                       size_t workspace_bytes, void* stream);
@@ -152,14 +159,15 @@ mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch,
  * sits at position prefix_lens[b] + i and attends to rows 0..prefix_lens[b]+i
  * (inclusive causal mask), with the same score, softmax and W^UV lift as
  * decode (review section 3).
- *   q_lat [batch][chunk][n_h][d_c + d_hR] fp32, prefix_lens [batch] (device,
+ *   q_lat: batch * chunk queries in the absorbed query layout (query index
+ *   b * chunk + i), prefix_lens [batch] (device,
  *   0 <= prefix <= max_prefix_len), max_prefix_len (host) with
  *   max_prefix_len + chunk <= cache_seq_stride,
  *   out fp32 [batch][chunk][n_h][d_h]. */
 size_t mla_prefill_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t batch,
                                    int32_t chunk, int32_t max_prefix_len);
 mla_status mla_prefill(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk,
-                       const float* q_lat, const void* cache, int64_t cache_seq_stride,
+                       const void* q_lat, const void* cache, int64_t cache_seq_stride,
                        const int32_t* prefix_lens, int32_t max_prefix_len,
                        const void* w_uv, float* out, void* workspace,
                        size_t workspace_bytes, void* stream);

@@ -108,9 +108,28 @@ def append_kv(d: Dims, c_kv, k_r, pos, row, cache) -> None:
                               _ptr(row), _ptr(cache), _stream(cache.device)), "mla_append_kv")
 
 
+def q_lat_empty(d: Dims, storage: torch.dtype, *lead: int, device="cuda") -> torch.Tensor:
+    """Absorbed query buffer in the layout of `storage`: fp32 [*lead, n_h, 576], or
+    for bf16 the hi/lo pair [*lead, n_h, 2, 576]."""
+    row = d.d_c + d.d_hR
+    if storage == torch.bfloat16:
+        return torch.empty((*lead, d.n_h, 2, row), dtype=torch.bfloat16, device=device)
+    if storage == torch.float32:
+        return torch.empty((*lead, d.n_h, row), dtype=torch.float32, device=device)
+    raise TypeError(f"storage dtype must be bfloat16 or float32, got {storage}")
+
+
+def q_lat_value(q_lat: torch.Tensor) -> torch.Tensor:
+    """fp32 value of an absorbed query buffer (hi + lo for the bf16 layout)."""
+    if q_lat.dtype == torch.bfloat16:
+        return q_lat[..., 0, :].float() + q_lat[..., 1, :].float()
+    return q_lat.float()
+
+
 def absorb_q(d: Dims, q_c, q_r, q_pos, w_uk, q_lat) -> None:
-    """A2: q_lat[n, i] = [q_c[n, i] @ w_uk[i]; RoPE(q_r[n, i], q_pos[n])] (q_lat fp32)."""
-    assert q_pos.dtype == torch.int32 and q_lat.dtype == torch.float32
+    """A2: q_lat[n, i] = [q_c[n, i] @ w_uk[i]; RoPE(q_r[n, i], q_pos[n])] in the
+    absorbed query layout of the storage dtype (see q_lat_empty)."""
+    assert q_pos.dtype == torch.int32 and q_lat.dtype == w_uk.dtype
     _check(_lib.mla_absorb_q(ctypes.byref(d), _dtype(w_uk), q_c.shape[0], _ptr(q_c), _ptr(q_r),
                              _ptr(q_pos), _ptr(w_uk), _ptr(q_lat), _stream(q_lat.device)),
            "mla_absorb_q")
@@ -127,7 +146,7 @@ def split_rows(max_seq_len: int, splits: int) -> int:
 def decode_partials(d: Dims, q_lat, cache, stride: int, seq_lens, max_seq_len: int, splits: int,
                     z_part, lse_part) -> None:
     """A3: split-KV partials (z_part [B, S, n_h, d_c] fp32, lse_part [B, S, n_h] fp32)."""
-    assert seq_lens.dtype == torch.int32
+    assert seq_lens.dtype == torch.int32 and q_lat.dtype == cache.dtype
     _check(_lib.mla_decode_partials(ctypes.byref(d), _dtype(cache), q_lat.shape[0], _ptr(q_lat),
                                     _ptr(cache), stride, _ptr(seq_lens), max_seq_len, splits,
                                     _ptr(z_part), _ptr(lse_part), _stream(cache.device)),
@@ -149,7 +168,7 @@ def decode_workspace_bytes(d: Dims, dtype: int, batch: int, max_seq_len: int) ->
 def decode(d: Dims, q_lat, cache, stride: int, seq_lens, max_seq_len: int, w_uv, out,
            out_latent=None, workspace=None) -> None:
     """A3 + A4 + A5 with the automatic split plan."""
-    assert seq_lens.dtype == torch.int32
+    assert seq_lens.dtype == torch.int32 and q_lat.dtype == cache.dtype
     dt = _dtype(cache)
     need = decode_workspace_bytes(d, dt, q_lat.shape[0], max_seq_len)
     if workspace is None:
@@ -165,8 +184,8 @@ def prefill_workspace_bytes(d: Dims, dtype: int, batch: int, chunk: int, max_pre
 
 def prefill(d: Dims, q_lat, cache, stride: int, prefix_lens, max_prefix_len: int, w_uv, out,
             workspace=None) -> None:
-    """A6: causal prefill; q_lat [B, chunk, n_h, d_c + d_hR], out [B, chunk, n_h, d_h]."""
-    assert prefix_lens.dtype == torch.int32
+    """A6: causal prefill; q_lat [B, chunk, n_h, ...] (absorbed query layout), out [B, chunk, n_h, d_h]."""
+    assert prefix_lens.dtype == torch.int32 and q_lat.dtype == cache.dtype
     dt = _dtype(cache)
     B, chunk = q_lat.shape[0], q_lat.shape[1]
     need = prefill_workspace_bytes(d, dt, B, chunk, max_prefix_len)

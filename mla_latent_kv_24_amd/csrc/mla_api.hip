@@ -123,7 +123,7 @@ mla_status mla_append_kv(const mla_dims* dims, mla_dtype dtype, int32_t n_tok, c
 }
 
 mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q, const void* q_c,
-                        const void* q_r, const int32_t* q_pos, const void* w_uk, float* q_lat,
+                        const void* q_r, const int32_t* q_pos, const void* w_uk, void* q_lat,
                         void* stream) {
   mla_status st = check_dims(dims, dtype);
   if (st != MLA_OK) return st;
@@ -155,7 +155,7 @@ int32_t mla_decode_num_splits(const mla_dims* dims, mla_dtype dtype, int32_t bat
 
 int64_t mla_split_rows(int32_t max_seq_len, int32_t num_splits) { return split_rows(max_seq_len, num_splits); }
 
-static mla_status run_partials(const mla_dims* dims, mla_dtype dtype, int64_t n_q, const float* q_lat,
+static mla_status run_partials(const mla_dims* dims, mla_dtype dtype, int64_t n_q, const void* q_lat,
                                const void* cache, int64_t stride, const int32_t* lens, int32_t max_len,
                                int32_t q_per_seq, int prefill, int32_t num_splits, float* z_part,
                                float* lse_part, hipStream_t s, const char* who) {
@@ -179,7 +179,7 @@ static mla_status run_partials(const mla_dims* dims, mla_dtype dtype, int64_t n_
   return hip_status(mla::launch_splitkv(a, dtype == MLA_BF16, s), who);
 }
 
-mla_status mla_decode_partials(const mla_dims* dims, mla_dtype dtype, int32_t batch, const float* q_lat,
+mla_status mla_decode_partials(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat,
                                const void* cache, int64_t cache_seq_stride, const int32_t* seq_lens,
                                int32_t max_seq_len, int32_t num_splits, float* z_part, float* lse_part,
                                void* stream) {
@@ -214,7 +214,7 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t
   return partial_bytes(dims, batch, plan_splits(dims, dtype, batch, max_seq_len));
 }
 
-mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch, const float* q_lat, const void* cache,
+mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat, const void* cache,
                       int64_t cache_seq_stride, const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv,
                       float* out, float* out_latent, void* workspace, size_t workspace_bytes, void* stream) {
   mla_status st = check_dims(dims, dtype);
@@ -248,7 +248,7 @@ size_t mla_prefill_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_
   return partial_bytes(dims, n_q, plan_splits(dims, dtype, n_q, max_len));
 }
 
-mla_status mla_prefill(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk, const float* q_lat,
+mla_status mla_prefill(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk, const void* q_lat,
                        const void* cache, int64_t cache_seq_stride, const int32_t* prefix_lens,
                        int32_t max_prefix_len, const void* w_uv, float* out, void* workspace,
                        size_t workspace_bytes, void* stream) {

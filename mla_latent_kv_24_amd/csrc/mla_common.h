@@ -37,10 +37,13 @@ struct AppendArgs {
   RopeTable rope;
 };
 
+// Absorbed query layout (q_lat): fp32 [n_q][n_h][d_c + d_r] for fp32 storage;
+// for bf16 storage [n_q][n_h][2][d_c + d_r] bf16, the fp32 value v split as
+// hi = bf16(v) (part 0) and lo = bf16(v - hi) (part 1).
 struct RopeQArgs {
   const void* q_r;       // [n_q][n_h][d_r] (storage dtype)
   const int32_t* q_pos;  // [n_q]
-  float* q_lat;          // [n_q][n_h][d_c + d_r], fp32
+  void* q_lat;           // absorbed query layout above
   int32_t n_q, n_h, d_c, d_r;
   RopeTable rope;
 };
@@ -48,12 +51,12 @@ struct RopeQArgs {
 struct AbsorbArgs {
   const void* q_c;   // [n_q][n_h][d_h] (storage dtype)
   const void* w_uk;  // [n_h][d_h][d_c] (storage dtype)
-  float* q_lat;      // [n_q][n_h][d_c + d_r], fp32
+  void* q_lat;       // absorbed query layout above
   int32_t n_q, n_h, d_c, d_h, d_r;
 };
 
 struct SplitArgs {
-  const float* q_lat;     // [n_q][n_h][d_c + d_r], fp32
+  const void* q_lat;      // absorbed query layout above
   const void* cache;      // rows of d_c + d_r
   const int32_t* lens;    // decode: seq_lens[batch]; prefill: prefix_lens[batch]
   float* z_part;          // [n_q][num_splits][n_h][d_c]
@@ -101,6 +104,32 @@ template <>
 __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, int64_t i) {
   return bf16_to_f32(p[i]);
 }
+// element e of (query n, head h) in the absorbed query layout
+template <typename T>
+__device__ __forceinline__ void store_q(void* q_lat, int64_t nh, int row_e, int e, float v);
+template <>
+__device__ __forceinline__ void store_q<float>(void* q_lat, int64_t nh, int row_e, int e, float v) {
+  static_cast<float*>(q_lat)[nh * row_e + e] = v;
+}
+template <>
+__device__ __forceinline__ void store_q<uint16_t>(void* q_lat, int64_t nh, int row_e, int e, float v) {
+  uint16_t* q = static_cast<uint16_t*>(q_lat) + nh * 2 * row_e;
+  const uint16_t hi = f32_to_bf16(v);
+  q[e] = hi;
+  q[row_e + e] = f32_to_bf16(v - bf16_to_f32(hi));
+}
+template <typename T>
+__device__ __forceinline__ float load_q(const void* q_lat, int64_t nh, int row_e, int e);
+template <>
+__device__ __forceinline__ float load_q<float>(const void* q_lat, int64_t nh, int row_e, int e) {
+  return static_cast<const float*>(q_lat)[nh * row_e + e];
+}
+template <>
+__device__ __forceinline__ float load_q<uint16_t>(const void* q_lat, int64_t nh, int row_e, int e) {
+  const uint16_t* q = static_cast<const uint16_t*>(q_lat) + nh * 2 * row_e;
+  return bf16_to_f32(q[e]) + bf16_to_f32(q[row_e + e]);
+}
+
 template <typename T>
 __device__ __forceinline__ T store_from_f32(float v);
 template <>

@@ -5,6 +5,8 @@
 // on xyznot.com, Metode 1: only c^KV and k^R are cached).
 // A2 folds U^K_i into the query, q~_i = (U^K_i)^T q^C_i (review section 2), and
 // rotates the per-head RoPE query by the token position (review section 3).
+// Both are formed in fp32 and written in the absorbed query layout: fp32 for
+// fp32 storage, a bf16 hi/lo pair (the matrix-core operand format) for bf16.
 #include "mla_common.h"
 
 namespace mla {
@@ -59,14 +61,14 @@ __global__ __launch_bounds__(256) void rope_q_kernel(RopeQArgs a) {
   }
   __syncthreads();
   const T* src = static_cast<const T*>(a.q_r) + static_cast<int64_t>(n) * a.n_h * a.d_r;
-  float* dst = a.q_lat + static_cast<int64_t>(n) * a.n_h * (a.d_c + a.d_r);
+  const int row_e = a.d_c + a.d_r;
   for (int idx = threadIdx.x; idx < a.n_h * pairs; idx += blockDim.x) {
     const int h = idx / pairs, k = idx % pairs;
     const float x0 = load_as_f32(src, h * a.d_r + 2 * k);
     const float x1 = load_as_f32(src, h * a.d_r + 2 * k + 1);
-    float* o = dst + static_cast<int64_t>(h) * (a.d_c + a.d_r) + a.d_c + 2 * k;
-    o[0] = x0 * cs[k] - x1 * sn[k];
-    o[1] = x0 * sn[k] + x1 * cs[k];
+    const int64_t nh = static_cast<int64_t>(n) * a.n_h + h;
+    store_q<T>(a.q_lat, nh, row_e, a.d_c + 2 * k, x0 * cs[k] - x1 * sn[k]);
+    store_q<T>(a.q_lat, nh, row_e, a.d_c + 2 * k + 1, x0 * sn[k] + x1 * cs[k]);
   }
 }
 
@@ -80,11 +82,11 @@ __global__ __launch_bounds__(256) void absorb_generic_kernel(AbsorbArgs a) {
   for (int d = threadIdx.x; d < a.d_h; d += blockDim.x) q[d] = load_as_f32(qc, d);
   __syncthreads();
   const T* w = static_cast<const T*>(a.w_uk) + static_cast<int64_t>(h) * a.d_h * a.d_c;
-  float* dst = a.q_lat + (static_cast<int64_t>(n) * a.n_h + h) * (a.d_c + a.d_r);
+  const int64_t nh = static_cast<int64_t>(n) * a.n_h + h;
   for (int c = threadIdx.x; c < a.d_c; c += blockDim.x) {
     float acc = 0.f;
     for (int d = 0; d < a.d_h; ++d) acc = fmaf(q[d], load_as_f32(w, static_cast<int64_t>(d) * a.d_c + c), acc);
-    dst[c] = acc;
+    store_q<T>(a.q_lat, nh, a.d_c + a.d_r, c, acc);
   }
 }
 
@@ -118,7 +120,6 @@ __global__ __launch_bounds__(256, 2) void absorb_mfma_kernel(AbsorbArgs a) {
   const int tr_row = 8 * g + (j16 >> 2);
   const int tr_col_b = 2 * (16 * hf + 4 * (j16 & 3));
   const uint16_t* qc = static_cast<const uint16_t*>(a.q_c);
-  float* out = a.q_lat;
   const int row_e = a.d_c + a.d_r;
 
   for (int n0 = n_begin; n0 < min(n_begin + ABS_QCHUNK, a.n_q); n0 += 32) {
@@ -149,8 +150,7 @@ __global__ __launch_bounds__(256, 2) void absorb_mfma_kernel(AbsorbArgs a) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int nn = n0 + 8 * (j >> 2) + 4 * g + (j & 3);
-        if (nn < a.n_q)
-          out[(static_cast<int64_t>(nn) * a.n_h + h) * row_e + c] = acc[j];
+        if (nn < a.n_q) store_q<uint16_t>(a.q_lat, static_cast<int64_t>(nn) * a.n_h + h, row_e, c, acc[j]);
       }
     }
   }

@@ -197,31 +197,21 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
   if (ntiles > 1) issue_direct(1);
   if (ntiles > 2) issue_direct(2);
 
-  // ---- absorbed queries (fp32 in memory) -> bf16 B-operand registers.  With
-  // 16 heads the query is kept as hi + lo bf16 parts and scored twice (the
-  // path has MFMA to spare there, and short sequences need the extra
-  // precision); with 32 heads per wave the register file holds only hi.
+  // ---- absorbed queries -> B-operand registers, straight from their bf16
+  // hi/lo layout.  With 16 heads both parts are scored (the path has MFMA to
+  // spare there, and short sequences need the extra precision); with 32 heads
+  // per wave the register file holds only hi.
   u32x4 qreg[NQ];
   u32x4 qlo[HPW == 16 ? NQ : 1];
   {
-    const float* q = a.q_lat + static_cast<int64_t>(n) * a.n_h * ROWE;
-    const float* qh = (HPW == 32) ? q + (h0 + (l & 31)) * ROWE + 8 * g32
-                                  : q + (h0 + (l & 15)) * ROWE + 8 * q16;
+    const uint16_t* q = static_cast<const uint16_t*>(a.q_lat) + static_cast<int64_t>(n) * a.n_h * 2 * ROWE;
+    const uint16_t* qh = (HPW == 32) ? q + (h0 + (l & 31)) * 2 * ROWE + 8 * g32
+                                     : q + (h0 + (l & 15)) * 2 * ROWE + 8 * q16;
     constexpr int QSTEP = (HPW == 32) ? 16 : 32;
 #pragma unroll
     for (int s = 0; s < NQ; ++s) {
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(qh + QSTEP * s);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(qh + QSTEP * s + 4);
-      bf16x8 hi8, lo8;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hi8[i] = static_cast<__bf16>(x0[i]);
-        hi8[4 + i] = static_cast<__bf16>(x1[i]);
-        lo8[i] = static_cast<__bf16>(x0[i] - static_cast<float>(hi8[i]));
-        lo8[4 + i] = static_cast<__bf16>(x1[i] - static_cast<float>(hi8[4 + i]));
-      }
-      qreg[s] = __builtin_bit_cast(u32x4, hi8);
-      if constexpr (HPW == 16) qlo[s] = __builtin_bit_cast(u32x4, lo8);
+      qreg[s] = *reinterpret_cast<const u32x4*>(qh + QSTEP * s);
+      if constexpr (HPW == 16) qlo[s] = *reinterpret_cast<const u32x4*>(qh + ROWE + QSTEP * s);
     }
   }
   vm_wait<0>();  // queries and the first tiles resident: the loop itself carries no compiler waits
@@ -482,6 +472,351 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
 }
 
 // ------------------------------------------------------------------------
+// n_h = 128 (the V2 shape): one workgroup streams its split once for all 128
+// heads, and the work is cut two ways.
+//   * score: wave w owns heads 32w..32w+31; their absorbed queries stay in
+//     VGPRs as the B operand.
+//   * value: wave w owns latent columns 128w..128w+127 of every head.  The
+//     probabilities of all four head groups reach it through an 8 KB LDS slot,
+//     so each wave transposes only its quarter of the tile's columns (a
+//     quarter of the LDS reads of a head split).
+//   * software pipeline: while the matrix cores score tile t+1, the same wave
+//     runs the softmax of tile t (max, exp, sums), so that VALU work issues in
+//     the shadow of the MFMAs; after a barrier the value MFMAs of tile t run.
+// The score accumulator is kept in VGPRs by issuing those MFMAs from asm; the
+// 256 AGPRs hold the Z accumulators (16 blocks of 32 columns x 32 heads).
+// ------------------------------------------------------------------------
+__device__ __forceinline__ void mfma_v0(f32x16& acc, const u32x4& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16& acc, const u32x4& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// bf16 pair (round to nearest even), lo in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+// A VALU read of an asm-issued MFMA result must wait for its write-back; 24
+// idle cycles cover the 32x32x16 latency with margin.
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+__global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
+  constexpr int NQ = 36;                           // score k-steps (576 / 16)
+  constexpr int NBUF = 4;                          // LDS tile ring
+  constexpr int LOADS = TILE_BYTES / (16 * 256);   // 9 DMA chunks per thread per tile
+  constexpr int PF = 4;                            // score operand prefetch depth
+  constexpr int P_OFF = NBUF * TILE_BYTES;         // P^T slots: [head group][row half][lane] x 16 B
+  constexpr int A_OFF = P_OFF + 4 * 2 * 64 * 16;   // rescale factors: [head % 32][head group] floats
+  constexpr int I_OFF = A_OFF + 128 * 4;           // 1 / l per head (128 floats)
+  constexpr int T_OFF = I_OFF + 128 * 4;           // per-thread DMA source chunk indices, u16 [LOADS][256]
+  __shared__ __attribute__((aligned(16))) uint8_t smem[T_OFF + LOADS * 256 * 2];
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int g32 = l >> 5, j16 = l & 15, l32 = l & 31;
+  const int n = blockIdx.x, split = blockIdx.y;
+  int b;
+  int64_t len;
+  query_range(a, n, b, len);
+  const int64_t lo = static_cast<int64_t>(split) * a.split_rows;
+  const int64_t hi = min(lo + a.split_rows, len);
+  float* zo = a.z_part + (static_cast<int64_t>(n) * a.num_splits + split) * 128 * D_C;
+  float* lse_o = a.lse_part + (static_cast<int64_t>(n) * a.num_splits + split) * 128;
+
+  if (lo >= hi) {  // empty split (uniform over the workgroup)
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    for (int idx = tid; idx < 128 * D_C / 4; idx += 256) reinterpret_cast<f32x4*>(zo)[idx] = zero;
+    if (tid < 128) lse_o[tid] = NEG_INF;
+    return;
+  }
+
+  // ---- tile DMA: LDS chunk f = tid + 256 i of a tile receives global chunk
+  // (t, p ^ swz(t)) with (t, p) = (f / 72, f % 72).  Each thread keeps its nine
+  // source chunk indices in its own LDS slots (live in registers across the
+  // loop they would be spilled, and a spill reload is a VMEM access that fences
+  // the DMAs); only the thread itself reads them, so no barrier is needed.
+  const uint8_t* gsplit =
+      static_cast<const uint8_t*>(a.cache) + (static_cast<int64_t>(b) * a.stride + lo) * ROWB;
+  const uint64_t gaddr = reinterpret_cast<uint64_t>(gsplit);
+  const int64_t ntiles = (hi - lo + TILE - 1) / TILE;
+  const uint32_t lds_w = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                             (__attribute__((address_space(3))) uint8_t*)smem)) +
+                         1024u * static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(w));
+  uint16_t* otab = reinterpret_cast<uint16_t*>(smem + T_OFF);
+  // A tile's buffer resource: based at the tile, sized to its rows inside the
+  // split (0 past the last tile: such loads only zero-fill a free buffer, which
+  // keeps the issue pattern and the vmcnt bookkeeping uniform).
+  auto tile_rsrc = [&](int64_t it) {
+    const uint64_t ga = gaddr + static_cast<uint64_t>(it) * TILE_BYTES;
+    const int64_t rows = max(min(static_cast<int64_t>(TILE), hi - lo - it * TILE), static_cast<int64_t>(0));
+    const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(ga & 0xffffffffu)),
+                      __builtin_amdgcn_readfirstlane(static_cast<int>((ga >> 32) & 0xffffu)),
+                      __builtin_amdgcn_readfirstlane(static_cast<int>(rows * ROWB)), 0x00020000};
+    return rs;
+  };
+  auto dma = [&](int64_t it, const i32x4& rs, int i, uint32_t chunk) {
+    dma16(lds_w + static_cast<uint32_t>((it & (NBUF - 1)) * TILE_BYTES) + 4096u * i,
+          static_cast<int>(chunk << 4), rs, 0);
+  };
+  {
+    uint32_t ch[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int f = tid + 256 * i;
+      const int t = f / 72, p = f - 72 * t;
+      ch[i] = static_cast<uint32_t>(72 * t + (p ^ swz(t)));
+      otab[i * 256 + tid] = static_cast<uint16_t>(ch[i]);
+    }
+#pragma unroll
+    for (int it = 0; it < 3; ++it) {
+      const i32x4 rs = tile_rsrc(it);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) dma(it, rs, i, ch[i]);
+    }
+  }
+
+  // ---- this wave's 32 absorbed queries: the hi parts are the B operands
+  u32x4 qreg[NQ];
+  {
+    const uint16_t* qh = static_cast<const uint16_t*>(a.q_lat) +
+                         (static_cast<int64_t>(n) * 128 + 32 * w + l32) * 2 * ROWE + 8 * g32;
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) qreg[s] = *reinterpret_cast<const u32x4*>(qh + 16 * s);
+  }
+
+  // ---- per-lane LDS operand offsets
+  // score A: tile row l%32, elements 16 s + 8 g (chunk 2 s + g)
+  int sc_off[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) sc_off[m] = l32 * ROWB + 16 * ((2 * m + g32) ^ swz(l32));
+  // value A (transpose reads): rows 4g + (j16>>2) [+8], columns 16 hf + 4 (j16&3) of a 32-block
+  int tr_off[2][2];
+  {
+    const int hf = (l >> 4) & 1;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        tr_off[r][p] = tile_off(4 * g32 + (j16 >> 2) + 8 * r, 32 * p + 16 * hf + 4 * (j16 & 3));
+  }
+  auto vread = [&](const uint8_t* buf, int cbg, int u) -> bf16x8 {
+    const uint8_t* bu = buf + 128 * (cbg >> 1) + 16 * u * ROWB;
+    return cat(tr_read(bu + tr_off[0][cbg & 1]), tr_read(bu + tr_off[1][cbg & 1]));
+  };
+  auto kread = [&](const uint8_t* buf, int s) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(buf + sc_off[s & 3] + 128 * (s >> 2));
+  };
+
+  vm_wait<0>();  // queries and the first tiles resident
+  __syncthreads();
+
+  // Two score accumulators alternate between "being scored" and "in softmax",
+  // so no register copies sit between the asm MFMAs and their readers.
+  f32x16 sA, sB;
+  {
+    u32x4 kb[PF];
+#pragma unroll
+    for (int s = 0; s < PF; ++s) kb[s] = kread(smem, s);
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      const u32x4 kv = kb[s % PF];
+      if (s + PF < NQ) kb[s % PF] = kread(smem, s + PF);
+      if (s == 0)
+        mfma_v0(sA, kv, qreg[0]);
+      else
+        mfma_v(sA, kv, qreg[s]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfma_drain();
+  }
+
+  f32x16 zacc[16];  // [c-block cb][head group hb] at 4 cb + hb
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) zacc[c][r] = 0.f;
+  float m_run = NEG_INF, l_run = 0.f;
+  const float qscale = a.qscale;
+
+  // One tile step: softmax + value of tile t (scores in sx), score of tile t+1
+  // into sn (a stale buffer on the last tile; that result is never used).
+  auto step = [&](int64_t t, f32x16& sx, f32x16& sn) {
+    // tile t+1 must have landed (only the nine loads of tile t+2 may still be
+    // in flight); every wave is done with tile t-1, whose buffer takes tile t+3
+    vm_wait<LOADS>();
+    __syncthreads();
+    const i32x4 rs3 = tile_rsrc(t + 3);
+    const int valid = static_cast<int>(min(hi - lo - t * TILE, static_cast<int64_t>(TILE)));
+    if (valid < TILE) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (8 * (j >> 2) + 4 * g32 + (j & 3) >= valid) sx[j] = NEG_INF;
+    }
+    const uint8_t* nb = smem + ((t + 1) & (NBUF - 1)) * TILE_BYTES;
+    const uint8_t* cbuf = smem + (t & (NBUF - 1)) * TILE_BYTES;
+
+    // ---- phase 1: 36 score MFMAs; between them, in small groups of
+    // independent instructions so that no group outlasts an MFMA: the max
+    // tree, the reference update, the exp pipeline, the P^T export, the DMA
+    // issues of tile t+3 and the first value operands of tile t.
+    bf16x8 va0, va1;
+    {
+      u32x4 kb[PF];
+#pragma unroll
+      for (int s = 0; s < PF; ++s) kb[s] = kread(nb, s);
+      float ma = 0.f, mb = 0.f, mc = 0.f, md = 0.f, me = 0.f, thr = 0.f, m_new = 0.f, dd = 0.f;
+      float neg_m = 0.f, alpha = 1.f, ls0 = 0.f, ls1 = 0.f;
+      float y[16], p[16];
+      uint32_t pw[8];          // P^T of the lane's 16 rows as packed bf16 pairs
+      uint32_t ch[LOADS];      // DMA source chunk index, read two MFMAs ahead of its issue
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) {
+        const u32x4 kv = kb[s % PF];
+        if (s + PF < NQ) kb[s % PF] = kread(nb, s + PF);
+        if (s == 0)
+          mfma_v0(sn, kv, qreg[0]);
+        else
+          mfma_v(sn, kv, qreg[s]);
+        // max over the lane's 16 rows (a 3-level tree)
+        if (s == 0) {
+          ma = fmaxf(fmaxf(sx[0], sx[1]), sx[2]);
+          mb = fmaxf(fmaxf(sx[3], sx[4]), sx[5]);
+          mc = fmaxf(fmaxf(sx[6], sx[7]), sx[8]);
+        } else if (s == 1) {
+          md = fmaxf(fmaxf(sx[9], sx[10]), sx[11]);
+          me = fmaxf(fmaxf(sx[12], sx[13]), sx[14]);
+          ma = fmaxf(ma, sx[15]);
+        } else if (s == 2) {
+          ma = fmaxf(fmaxf(ma, mb), mc);
+          md = fmaxf(md, me);
+          thr = m_run + RESCALE_TAU;
+        } else if (s == 3) {
+          ma = fmaxf(ma, md);
+        } else if (s == 4) {
+          pair_vals<false>(ma, mb, mc);  // this lane's and its partner's (lane ^ 32) max
+        } else if (s == 5) {
+          ma = fmaxf(mb, mc);
+        } else if (s == 6) {
+          ma *= qscale;  // scale > 0 commutes with max
+        } else if (s == 7) {
+          m_new = (ma > thr) ? ma : m_run;  // move the reference only by more than tau
+        } else if (s == 8) {
+          dd = m_run - m_new;
+          neg_m = -m_new;
+        } else if (s == 9) {
+          alpha = __builtin_amdgcn_exp2f(dd);  // exactly 1 if unchanged, 0 from -inf
+          y[0] = fmaf(sx[0], qscale, neg_m);
+        } else if (s == 10) {
+          l_run *= alpha;
+          m_run = m_new;
+          *reinterpret_cast<float*>(smem + A_OFF + 16 * l32 + 4 * w) = alpha;
+          p[0] = __builtin_amdgcn_exp2f(y[0]);
+          y[1] = fmaf(sx[1], qscale, neg_m);
+        } else if (s >= 11 && s <= 25) {
+          const int k = s - 10;
+          p[k] = __builtin_amdgcn_exp2f(y[k]);
+          if (k + 1 < 16) y[k + 1] = fmaf(sx[k + 1], qscale, neg_m);
+          if ((k & 1) == 0) {
+            ls0 += p[k - 1];
+            ls1 += p[k - 2];
+            pw[(k - 2) >> 1] = pack_bf16x2(p[k - 2], p[k - 1]);
+          }
+        } else if (s == 26) {
+          ls0 += p[15];
+          ls1 += p[14];
+          pw[7] = pack_bf16x2(p[14], p[15]);
+        } else if (s == 27 || s == 28) {
+          const int o = 4 * (s - 27);
+          const u32x4 pb = {pw[o], pw[o + 1], pw[o + 2], pw[o + 3]};
+          *reinterpret_cast<u32x4*>(smem + P_OFF + 2048 * w + 1024 * (s - 27) + 16 * l) = pb;
+        } else if (s == 29) {
+          l_run += ls0 + ls1;
+        } else if (s == 33) {
+          va0 = vread(cbuf, 4 * w, 0);
+        } else if (s == 34) {
+          va1 = vread(cbuf, 4 * w, 1);
+        }
+        // DMA of tile t+3: source chunk indices read 2 MFMAs ahead of each issue
+        if (s >= 10 && s <= 10 + 2 * (LOADS - 1) && (s & 1) == 0) ch[(s - 10) >> 1] = otab[((s - 10) >> 1) * 256 + tid];
+        if (s >= 12 && s <= 12 + 2 * (LOADS - 1) && (s & 1) == 0) dma(t + 3, rs3, (s - 12) >> 1, ch[(s - 12) >> 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();  // P^T and rescale factors of every head group visible
+
+    // ---- phase 2: Z^T[c][i] += rows^T P^T over this wave's 128 columns
+    {
+      const f32x4 al4 = *reinterpret_cast<const f32x4*>(smem + A_OFF + 16 * l32);
+      u32x4 pv[8];  // [hb][u] at 2 hb + u
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pv[i] = *reinterpret_cast<const u32x4*>(smem + P_OFF + 1024 * i + 16 * l);
+      // a head group whose reference max moved has a factor != 1 in some lane
+      // (exactly 1 otherwise); Z is still zero on the first tile
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) {
+        if (t > 0 && __ballot(al4[hb] != 1.f)) {
+          const float al = al4[hb];
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              float e = zacc[4 * cb + hb][r];
+              float tmp;
+              asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                           : "+a"(e), "=&v"(tmp) : "v"(al));
+              zacc[4 * cb + hb][r] = e;
+            }
+        }
+      }
+      bf16x8 va[2][2];
+      va[0][0] = va0;
+      va[0][1] = va1;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        if (cb + 1 < 4) {
+          va[(cb + 1) & 1][0] = vread(cbuf, 4 * w + cb + 1, 0);
+          va[(cb + 1) & 1][1] = vread(cbuf, 4 * w + cb + 1, 1);
+        }
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            zacc[4 * cb + hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                va[cb & 1][u], __builtin_bit_cast(bf16x8, pv[2 * hb + u]), zacc[4 * cb + hb], 0, 0, 0);
+      }
+    }
+  };
+
+  for (int64_t t = 0; t < ntiles; t += 2) {
+    step(t, sA, sB);
+    if (t + 1 >= ntiles) break;
+    step(t + 1, sB, sA);
+  }
+
+  // ---- finalize: lse per head from its score wave; Z normalised by every
+  // column wave with the head's 1/l taken from LDS.  The zero-fill loads
+  // issued past the last tile are drained before the workgroup may exit.
+  vm_wait<0>();
+  const float lt = pair_sum32(l_run);
+  const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+  if (l < 32) lse_o[32 * w + l] = (lt > 0.f) ? (m_run + log2f(lt)) * LN2 : NEG_INF;
+  *reinterpret_cast<float*>(smem + I_OFF + 4 * (32 * w + l32)) = inv;
+  __syncthreads();
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const float ih = *reinterpret_cast<const float*>(smem + I_OFF + 4 * (32 * hb + l32));
+    float* zrow = zo + static_cast<int64_t>(32 * hb + l32) * D_C + 128 * w + 4 * g32;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x16& zz = zacc[4 * cb + hb];
+        const f32x4 v = {zz[4 * jj] * ih, zz[4 * jj + 1] * ih, zz[4 * jj + 2] * ih, zz[4 * jj + 3] * ih};
+        *reinterpret_cast<f32x4*>(zrow + 32 * cb + 8 * jj) = v;
+      }
+  }
+}
+
+// ------------------------------------------------------------------------
 // Generic fp32 VALU path (MLA_F32 storage, or bf16 with an n_h without an MFMA
 // instance).  One workgroup per (query, split, head); 256 rows per step: one
 // thread scores one row, then every thread accumulates two latent columns.
@@ -520,8 +855,7 @@ __global__ __launch_bounds__(256) void splitkv_generic_kernel(SplitArgs a) {
     if (tid == 0) *lse_o = NEG_INF;
     return;
   }
-  const float* qs = a.q_lat + (static_cast<int64_t>(n) * a.n_h + h) * row_e;
-  for (int e = tid; e < row_e; e += 256) q[e] = qs[e];
+  for (int e = tid; e < row_e; e += 256) q[e] = load_q<T>(a.q_lat, static_cast<int64_t>(n) * a.n_h + h, row_e, e);
   __syncthreads();
   const T* rows = static_cast<const T*>(a.cache) + static_cast<int64_t>(b) * a.stride * row_e;
   float m = NEG_INF, lsum = 0.f, z0 = 0.f, z1 = 0.f;
@@ -570,7 +904,7 @@ hipError_t launch_splitkv(const SplitArgs& a, int bf16, hipStream_t st) {
       case 16: splitkv_mfma_kernel<16, 4><<<grid, 256, 0, st>>>(a); break;
       case 32: splitkv_mfma_kernel<32, 4><<<grid, 256, 0, st>>>(a); break;
       case 64: splitkv_mfma_kernel<32, 2><<<grid, 256, 0, st>>>(a); break;
-      default: splitkv_mfma_kernel<32, 1><<<grid, 256, 0, st>>>(a); break;
+      default: splitkv_wide_kernel<<<grid, 256, 0, st>>>(a); break;
     }
   } else {
     dim3 grid(a.n_q, a.num_splits, a.n_h);

@@ -62,7 +62,7 @@ class DecodeState:
         self.q_pos = self.new_pos
         self.w_uk = to_device(inp.w_uk, w.dtype, device)
         self.w_uv = to_device(inp.w_uv, w.dtype, device)
-        self.q_lat = torch.empty((self.batch, w.n_h, ROW), dtype=torch.float32, device=device)
+        self.q_lat = api.q_lat_empty(self.d, tdt, self.batch, device=device)
         self.out = torch.empty((self.batch, w.n_h, 128), dtype=torch.float32, device=device)
         self.out_latent = (torch.empty((self.batch, w.n_h, D_C), dtype=torch.float32, device=device)
                            if out_latent else None)
@@ -128,7 +128,7 @@ class PrefillState:
         self.prefix_lens = torch.tensor([inp.prefix], dtype=torch.int32, device=device)
         self.w_uk = to_device(inp.w_uk, w.dtype, device)
         self.w_uv = to_device(inp.w_uv, w.dtype, device)
-        self.q_lat = torch.empty((1, inp.chunk, w.n_h, ROW), dtype=torch.float32, device=device)
+        self.q_lat = api.q_lat_empty(self.d, tdt, 1, inp.chunk, device=device)
         self.out = torch.empty((1, inp.chunk, w.n_h, 128), dtype=torch.float32, device=device)
         dtc = api.BF16 if w.dtype == "bf16" else api.F32
         ws = api.prefill_workspace_bytes(self.d, dtc, 1, inp.chunk, inp.prefix)
@@ -138,7 +138,7 @@ class PrefillState:
         api.append_kv(self.d, self.c_kv, self.k_raw, self.pos, self.rows, self.cache)
 
     def absorb(self):
-        api.absorb_q(self.d, self.q_c, self.q_r, self.q_pos, self.w_uk, self.q_lat.view(-1, self.q_lat.shape[2], ROW))
+        api.absorb_q(self.d, self.q_c, self.q_r, self.q_pos, self.w_uk, self.q_lat.view(-1, *self.q_lat.shape[2:]))
 
     def attend(self):
         api.prefill(self.d, self.q_lat, self.cache, self.stride, self.prefix_lens, self.prefix,

@@ -43,3 +43,17 @@ def oracle_prefill(pinp, queries, heads=None):
     return O.prefill(f64(pinp.q_c[:, heads], dt), f64(pinp.q_r[:, heads], dt), pinp.prefix,
                      f64(pinp.c_kv, dt), f64(pinp.k_raw, dt), f64(pinp.w_uk[heads], dt),
                      f64(pinp.w_uv[heads], dt), pinp.w.rope_base, query_idx=queries)
+
+
+def absorbed_layout(q32, dtype):
+    """Absorbed query input for the device: fp32 as is, or for bf16 storage the
+    hi/lo pair (hi = bf16(q), lo = bf16(q - hi)) on a new axis -2.  Returns the
+    storage array and the fp64 value it carries (what the oracle is given)."""
+    q32 = np.asarray(q32, dtype=np.float32)
+    if dtype != "bf16":
+        return q32, q32.astype(np.float64)
+    hi = W.f32_to_bf16_bits(q32)
+    lo = W.f32_to_bf16_bits(q32 - W.bf16_bits_to_f32(hi))
+    pair = np.stack([hi, lo], axis=-2)
+    value = W.bf16_bits_to_f32(hi).astype(np.float64) + W.bf16_bits_to_f32(lo).astype(np.float64)
+    return pair, value
