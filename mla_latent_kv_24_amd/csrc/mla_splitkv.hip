@@ -609,8 +609,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
   vm_wait<0>();  // queries and the first tiles resident
   __syncthreads();
 
-  // Two score accumulators alternate between "being scored" and "in softmax",
-  // so no register copies sit between the asm MFMAs and their readers.
+  // sA: scores in softmax; sB: scores being accumulated by the asm MFMAs.
   f32x16 sA, sB;
   {
     u32x4 kb[PF];
@@ -637,37 +636,85 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
   float m_run = NEG_INF, l_run = 0.f;
   const float qscale = a.qscale;
 
-  // One tile step: softmax + value of tile t (scores in sx), score of tile t+1
-  // into sn (a stale buffer on the last tile; that result is never used).
+  // Rows of tile t inside the split: <= 0 past the last tile (every row masked).
+  auto tile_valid = [&](int64_t t) {
+    return static_cast<int>(max(min(hi - lo - t * TILE, static_cast<int64_t>(TILE)), static_cast<int64_t>(-1)));
+  };
+  // Reference update for a freshly scored tile (scores sc, masked in place):
+  // the max over the head's 32 rows (lanes l and l^32), moved only when it
+  // exceeds the reference by more than tau; returns the factor 2^(m_old - m_new)
+  // (exactly 1 when unchanged, 0 from -inf) and rescales l_run.  A fully
+  // masked tile leaves everything unchanged.  Spread over several calls with
+  // `part` so that each piece fits between two MFMAs.
+  float ma = 0.f, mb = 0.f, mc = 0.f, md = 0.f, me = 0.f, m_new = 0.f, alpha = 1.f;
+  auto ref_update = [&](f32x16& sc, int part, int valid) {
+    if (part == 0) {
+      if (valid < TILE) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (8 * (j >> 2) + 4 * g32 + (j & 3) >= valid) sc[j] = NEG_INF;
+      }
+    } else if (part == 1) {
+      ma = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+      mb = fmaxf(fmaxf(sc[3], sc[4]), sc[5]);
+      mc = fmaxf(fmaxf(sc[6], sc[7]), sc[8]);
+    } else if (part == 2) {
+      md = fmaxf(fmaxf(sc[9], sc[10]), sc[11]);
+      me = fmaxf(fmaxf(sc[12], sc[13]), sc[14]);
+      ma = fmaxf(ma, sc[15]);
+    } else if (part == 3) {
+      ma = fmaxf(fmaxf(ma, mb), mc);
+      md = fmaxf(md, me);
+    } else if (part == 4) {
+      ma = fmaxf(ma, md);
+    } else if (part == 5) {
+      pair_vals<false>(ma, mb, mc);
+    } else if (part == 6) {
+      ma = fmaxf(mb, mc) * qscale;  // scale > 0 commutes with max
+    } else if (part == 7) {
+      m_new = (ma > m_run + RESCALE_TAU) ? ma : m_run;
+    } else if (part == 8) {
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    } else if (part == 9) {
+      l_run *= alpha;
+      m_run = m_new;
+    }
+  };
+  // tile 0's reference (Z and l are still zero: no factor is needed)
+#pragma unroll
+  for (int part = 0; part < 10; ++part) ref_update(sA, part, tile_valid(0));
+
+  // One tile step.  Entering step t: sx holds tile t's masked scores and
+  // m_run / l_run already include tile t's reference update, whose factor
+  // every head group published in LDS.
+  //   phase 1: 36 score MFMAs of tile t+1 (into sn) with the exp pipeline of
+  //            tile t and its P^T export woven in;
+  //   phase 2: 32 value MFMAs of tile t with the reference update of tile t+1
+  //            woven in (its factor is read by every wave in the next phase 1).
+  // The DMA of tile t+3 is issued between MFMAs of phase MLA_DMA_PHASE.
+#ifndef MLA_DMA_PHASE
+#define MLA_DMA_PHASE 1
+#endif
   auto step = [&](int64_t t, f32x16& sx, f32x16& sn) {
     // tile t+1 must have landed (only the nine loads of tile t+2 may still be
     // in flight); every wave is done with tile t-1, whose buffer takes tile t+3
     vm_wait<LOADS>();
     __syncthreads();
     const i32x4 rs3 = tile_rsrc(t + 3);
-    const int valid = static_cast<int>(min(hi - lo - t * TILE, static_cast<int64_t>(TILE)));
-    if (valid < TILE) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (8 * (j >> 2) + 4 * g32 + (j & 3) >= valid) sx[j] = NEG_INF;
-    }
     const uint8_t* nb = smem + ((t + 1) & (NBUF - 1)) * TILE_BYTES;
     const uint8_t* cbuf = smem + (t & (NBUF - 1)) * TILE_BYTES;
+    uint32_t ch[LOADS];  // DMA source chunk index, read two MFMAs ahead of its issue
 
-    // ---- phase 1: 36 score MFMAs; between them, in small groups of
-    // independent instructions so that no group outlasts an MFMA: the max
-    // tree, the reference update, the exp pipeline, the P^T export, the DMA
-    // issues of tile t+3 and the first value operands of tile t.
+    // ---- phase 1
     bf16x8 va0, va1;
+    f32x4 al4;
     {
       u32x4 kb[PF];
 #pragma unroll
       for (int s = 0; s < PF; ++s) kb[s] = kread(nb, s);
-      float ma = 0.f, mb = 0.f, mc = 0.f, md = 0.f, me = 0.f, thr = 0.f, m_new = 0.f, dd = 0.f;
-      float neg_m = 0.f, alpha = 1.f, ls0 = 0.f, ls1 = 0.f;
-      float y[16], p[16];
-      uint32_t pw[8];          // P^T of the lane's 16 rows as packed bf16 pairs
-      uint32_t ch[LOADS];      // DMA source chunk index, read two MFMAs ahead of its issue
+      const float neg_m = -m_run;
+      float y[16], p[16], ls0 = 0.f, ls1 = 0.f;
+      uint32_t pw[8];  // P^T of the lane's 16 rows as packed bf16 pairs
 #pragma unroll
       for (int s = 0; s < NQ; ++s) {
         const u32x4 kv = kb[s % PF];
@@ -676,81 +723,37 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
           mfma_v0(sn, kv, qreg[0]);
         else
           mfma_v(sn, kv, qreg[s]);
-        // max over the lane's 16 rows (a 3-level tree)
-        if (s == 0) {
-          ma = fmaxf(fmaxf(sx[0], sx[1]), sx[2]);
-          mb = fmaxf(fmaxf(sx[3], sx[4]), sx[5]);
-          mc = fmaxf(fmaxf(sx[6], sx[7]), sx[8]);
-        } else if (s == 1) {
-          md = fmaxf(fmaxf(sx[9], sx[10]), sx[11]);
-          me = fmaxf(fmaxf(sx[12], sx[13]), sx[14]);
-          ma = fmaxf(ma, sx[15]);
-        } else if (s == 2) {
-          ma = fmaxf(fmaxf(ma, mb), mc);
-          md = fmaxf(md, me);
-          thr = m_run + RESCALE_TAU;
-        } else if (s == 3) {
-          ma = fmaxf(ma, md);
-        } else if (s == 4) {
-          pair_vals<false>(ma, mb, mc);  // this lane's and its partner's (lane ^ 32) max
-        } else if (s == 5) {
-          ma = fmaxf(mb, mc);
-        } else if (s == 6) {
-          ma *= qscale;  // scale > 0 commutes with max
-        } else if (s == 7) {
-          m_new = (ma > thr) ? ma : m_run;  // move the reference only by more than tau
-        } else if (s == 8) {
-          dd = m_run - m_new;
-          neg_m = -m_new;
-        } else if (s == 9) {
-          alpha = __builtin_amdgcn_exp2f(dd);  // exactly 1 if unchanged, 0 from -inf
-          y[0] = fmaf(sx[0], qscale, neg_m);
-        } else if (s == 10) {
-          l_run *= alpha;
-          m_run = m_new;
-          *reinterpret_cast<float*>(smem + A_OFF + 16 * l32 + 4 * w) = alpha;
-          p[0] = __builtin_amdgcn_exp2f(y[0]);
-          y[1] = fmaf(sx[1], qscale, neg_m);
-        } else if (s >= 11 && s <= 25) {
-          const int k = s - 10;
-          p[k] = __builtin_amdgcn_exp2f(y[k]);
-          if (k + 1 < 16) y[k + 1] = fmaf(sx[k + 1], qscale, neg_m);
-          if ((k & 1) == 0) {
-            ls0 += p[k - 1];
-            ls1 += p[k - 2];
-            pw[(k - 2) >> 1] = pack_bf16x2(p[k - 2], p[k - 1]);
-          }
-        } else if (s == 26) {
-          ls0 += p[15];
-          ls1 += p[14];
-          pw[7] = pack_bf16x2(p[14], p[15]);
-        } else if (s == 27 || s == 28) {
-          const int o = 4 * (s - 27);
-          const u32x4 pb = {pw[o], pw[o + 1], pw[o + 2], pw[o + 3]};
-          *reinterpret_cast<u32x4*>(smem + P_OFF + 2048 * w + 1024 * (s - 27) + 16 * l) = pb;
-        } else if (s == 29) {
-          l_run += ls0 + ls1;
-        } else if (s == 33) {
-          va0 = vread(cbuf, 4 * w, 0);
-        } else if (s == 34) {
-          va1 = vread(cbuf, 4 * w, 1);
+        if (s == 0) al4 = *reinterpret_cast<const f32x4*>(smem + A_OFF + 16 * l32);  // tile t's factors
+        // exp pipeline: fma in slot j, exp in slot j+1, sums and packing after
+        if (s < 16) y[s] = fmaf(sx[s], qscale, neg_m);
+        if (s >= 1 && s <= 16) p[s - 1] = __builtin_amdgcn_exp2f(y[s - 1]);
+        if (s >= 3 && s <= 17 && (s & 1) == 1) {
+          const int k = s - 3;  // p[k], p[k+1] ready
+          ls0 += p[k];
+          ls1 += p[k + 1];
+          pw[k >> 1] = pack_bf16x2(p[k], p[k + 1]);
         }
-        // DMA of tile t+3: source chunk indices read 2 MFMAs ahead of each issue
+        if (s == 18 || s == 19) {
+          const int o = 4 * (s - 18);
+          const u32x4 pb = {pw[o], pw[o + 1], pw[o + 2], pw[o + 3]};
+          *reinterpret_cast<u32x4*>(smem + P_OFF + 2048 * w + 1024 * (s - 18) + 16 * l) = pb;
+        }
+        if (s == 20) l_run += ls0 + ls1;
+        if (s == 33) va0 = vread(cbuf, 4 * w, 0);
+        if (s == 34) va1 = vread(cbuf, 4 * w, 1);
+#if MLA_DMA_PHASE == 1
         if (s >= 10 && s <= 10 + 2 * (LOADS - 1) && (s & 1) == 0) ch[(s - 10) >> 1] = otab[((s - 10) >> 1) * 256 + tid];
         if (s >= 12 && s <= 12 + 2 * (LOADS - 1) && (s & 1) == 0) dma(t + 3, rs3, (s - 12) >> 1, ch[(s - 12) >> 1]);
+#endif
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();  // P^T and rescale factors of every head group visible
+    __syncthreads();  // P^T of every head group visible
 
-    // ---- phase 2: Z^T[c][i] += rows^T P^T over this wave's 128 columns
+    // ---- phase 2
     {
-      const f32x4 al4 = *reinterpret_cast<const f32x4*>(smem + A_OFF + 16 * l32);
-      u32x4 pv[8];  // [hb][u] at 2 hb + u
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pv[i] = *reinterpret_cast<const u32x4*>(smem + P_OFF + 1024 * i + 16 * l);
-      // a head group whose reference max moved has a factor != 1 in some lane
-      // (exactly 1 otherwise); Z is still zero on the first tile
+      // tile t's rescale (rare): a head group whose reference moved has a
+      // factor != 1 in some lane; Z is still zero on the first tile
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) {
         if (t > 0 && __ballot(al4[hb] != 1.f)) {
@@ -767,29 +770,38 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
             }
         }
       }
+      u32x4 pv[8];  // [hb][u] at 2 hb + u
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pv[i] = *reinterpret_cast<const u32x4*>(smem + P_OFF + 1024 * i + 16 * l);
+      const int valid1 = tile_valid(t + 1);
       bf16x8 va[2][2];
       va[0][0] = va0;
       va[0][1] = va1;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        if (cb + 1 < 4) {
-          va[(cb + 1) & 1][0] = vread(cbuf, 4 * w + cb + 1, 0);
-          va[(cb + 1) & 1][1] = vread(cbuf, 4 * w + cb + 1, 1);
-        }
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-            zacc[4 * cb + hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                va[cb & 1][u], __builtin_bit_cast(bf16x8, pv[2 * hb + u]), zacc[4 * cb + hb], 0, 0, 0);
+      for (int v = 0; v < 32; ++v) {
+        const int cb = v >> 3, hb = (v >> 1) & 3, u = v & 1;
+        zacc[4 * cb + hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            va[cb & 1][u], __builtin_bit_cast(bf16x8, pv[2 * hb + u]), zacc[4 * cb + hb], 0, 0, 0);
+        if (cb + 1 < 4 && (v & 7) == 1) va[(cb + 1) & 1][0] = vread(cbuf, 4 * w + cb + 1, 0);
+        if (cb + 1 < 4 && (v & 7) == 2) va[(cb + 1) & 1][1] = vread(cbuf, 4 * w + cb + 1, 1);
+        // tile t+1's reference update; sn's last MFMA is far behind by now
+        if (v >= 8 && v < 18) ref_update(sn, v - 8, valid1);
+        if (v == 18) *reinterpret_cast<float*>(smem + A_OFF + 16 * l32 + 4 * w) = alpha;
+#if MLA_DMA_PHASE == 2
+        if (v >= 12 && v <= 12 + 2 * (LOADS - 1) && (v & 1) == 0) ch[(v - 12) >> 1] = otab[((v - 12) >> 1) * 256 + tid];
+        if (v >= 14 && v <= 14 + 2 * (LOADS - 1) && (v & 1) == 0) dma(t + 3, rs3, (v - 14) >> 1, ch[(v - 14) >> 1]);
+#endif
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
 
-  for (int64_t t = 0; t < ntiles; t += 2) {
+  // The scores of tile t+1 move into sA at the end of each step with asm
+  // copies: their position stays after phase 2, far behind sB's last MFMA.
+  for (int64_t t = 0; t < ntiles; ++t) {
     step(t, sA, sB);
-    if (t + 1 >= ntiles) break;
-    step(t + 1, sB, sA);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) asm volatile("v_mov_b32 %0, %1" : "=v"(sA[j]) : "v"(sB[j]));
   }
 
   // ---- finalize: lse per head from its score wave; Z normalised by every
