@@ -111,37 +111,41 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copy probe: 1 GiB device-to-device copy done")
 
+    # The step runs as one HIP graph (append, absorb, attention, combine): no
+    # host work between its kernels, as a serving loop would run it.
+    graph = st.capture()
     for _ in range(args.warmup):
-        st.step()
+        graph.replay()
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        st.append_new()
-        st.absorb()
-        ev[i][0].record()
-        st.attention()
-        ev[i][1].record()
-        st.combine()
+    for _ in range(args.steps):
+        graph.replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
-    # per-step breakdown (separate, not part of the headline timing)
+    # Per-kernel durations: each stage captured as REPS back-to-back launches,
+    # bracketed by HIP events on the stream the graph runs on (so no host gap
+    # enters a launch), averaged over the launches.
+    REPS = 10
+    stages = (("append_kv", st.append_new), ("absorb_q", st.absorb),
+              ("splitkv_attention", st.attention), ("combine_project", st.combine))
     parts = {}
-    for nm, fn in (("append_kv", st.append_new), ("absorb_q", st.absorb), ("splitkv_attention", st.attention),
-                   ("combine_project", st.combine)):
+    for nm, fn in stages:
+        g = st.capture(fn, repeat=REPS)
+        g.replay()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        rounds = max(1, args.steps // REPS)
         e0.record()
-        for _ in range(10):
-            fn()
+        for _ in range(rounds):
+            g.replay()
         e1.record()
         torch.cuda.synchronize()
-        parts[nm] = round(e0.elapsed_time(e1) / 10 * 1e3, 2)   # microseconds
+        parts[nm] = round(e0.elapsed_time(e1) / (rounds * REPS) * 1e3, 2)   # microseconds
+    attn_ms = parts["splitkv_attention"] * 1e-3
 
     ms_per_step = elapsed / args.steps * 1e3
     value = tokens * args.steps / elapsed
@@ -168,7 +172,7 @@ def main():
                    "d_hR": 64, "d_h": 128, "latent_rows": tokens, "splits": st.splits},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "splitkv_mfma_kernel",
+                     "traffic": traffic, "kernel": "splitkv_wide_kernel",
                      "kernel_us": round(attn_ms * 1e3, 2),
                      "mfma_tflops": round(tflops, 1),
                      "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},

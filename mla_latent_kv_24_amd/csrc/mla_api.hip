@@ -133,9 +133,20 @@ mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q, cons
   if (!q_c || !q_r || !q_pos || !w_uk || !q_lat) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
   const int bf = dtype == MLA_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  mla::AbsorbArgs a{q_c, w_uk, q_lat, n_q, dims->n_h, dims->d_c, dims->d_h, dims->d_hR};
+  mla::AbsorbArgs a{};
+  a.q_c = q_c;
+  a.w_uk = w_uk;
+  a.q_lat = q_lat;
+  a.n_q = n_q;
+  a.n_h = dims->n_h;
+  a.d_c = dims->d_c;
+  a.d_h = dims->d_h;
+  a.d_r = dims->d_hR;
+  a.q_r = q_r;
+  a.q_pos = q_pos;
+  fill_rope(dims, a.rope);
   mla_status r = hip_status(mla::launch_absorb(a, bf, s), "mla_absorb_q (latent)");
-  if (r != MLA_OK) return r;
+  if (r != MLA_OK || mla::absorb_fuses_rope(bf, dims->d_c, dims->d_h, dims->d_hR)) return r;
   mla::RopeQArgs ra{};
   ra.q_r = q_r;
   ra.q_pos = q_pos;

@@ -21,20 +21,41 @@ constexpr int ZSTRIDE = 1040;        // bytes per staged z row (512 bf16 + 16 B 
 // the 32x32x16 MFMA lift keeps fp32-level accuracy:
 //   out[n][d] = sum_c (hi[n][c] + lo[n][c]) * w_uv[h][d][c]
 // A = z rows from LDS (c contiguous), B = w_uv rows from global (c contiguous).
+// The kernel is a stream of the partials (256 KB per workgroup) and of W^UV:
+// split s+1's loads are in flight while split s accumulates, split 0's before
+// the weights are known, and the first W^UV operands before all of it.
 // ------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void combine_mfma_kernel(CombineArgs a) {
+__global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a) {
   __shared__ float wts[32][CMB_MAX_SPLITS];
   __shared__ __attribute__((aligned(16))) uint8_t zhi[32 * ZSTRIDE];
   __shared__ __attribute__((aligned(16))) uint8_t zlo[32 * ZSTRIDE];
+  constexpr int PFW = 8;  // W^UV operand prefetch depth (MFMA k-steps)
   const int h = blockIdx.x, n0 = blockIdx.y * 32;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int S = a.num_splits;
 
+  // B operands of the lift: this lane's W^UV row d, 16 columns per k-step
+  const int g = l >> 5;
+  const int d = 32 * w + (l & 31);
+  const uint16_t* wrow = static_cast<const uint16_t*>(a.w_uv) + (static_cast<int64_t>(h) * D_H + d) * D_C + 8 * g;
+  u32x4 bw[PFW];
+#pragma unroll
+  for (int s = 0; s < PFW; ++s) bw[s] = *reinterpret_cast<const u32x4*>(wrow + 16 * s);
+
+  // this thread's slice of the combined latent: query row r, columns 4 cg + 32 i
+  const int r = tid >> 3, cg = tid & 7;
+  const int n = n0 + r;
+  const float* zp = a.z_part + (static_cast<int64_t>(min(n, a.n_q - 1)) * S * a.n_h + h) * D_C + 4 * cg;
+  const int64_t zs = static_cast<int64_t>(a.n_h) * D_C;  // split stride (floats)
+  f32x4 cur[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) cur[i] = *reinterpret_cast<const f32x4*>(zp + 32 * i);
+
   // split weights: one thread per query
   if (tid < 32) {
-    const int n = n0 + tid;
-    if (n < a.n_q) {
-      const float* ls = a.lse_part + static_cast<int64_t>(n) * S * a.n_h + h;
+    const int nq = n0 + tid;
+    if (nq < a.n_q) {
+      const float* ls = a.lse_part + static_cast<int64_t>(nq) * S * a.n_h + h;
       float m = CNEG_INF;
       for (int s = 0; s < S; ++s) m = fmaxf(m, ls[static_cast<int64_t>(s) * a.n_h]);
       float tot = 0.f;
@@ -51,57 +72,58 @@ __global__ __launch_bounds__(256) void combine_mfma_kernel(CombineArgs a) {
   }
   __syncthreads();
 
-  // combined latent: thread -> (query row, 4-column group), 128 groups per row
-  for (int idx = tid; idx < 32 * 128; idx += 256) {
-    const int r = idx >> 7, c4 = (idx & 127) * 4;
-    const int n = n0 + r;
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    if (n < a.n_q) {
-      const float* zp = a.z_part + (static_cast<int64_t>(n) * S * a.n_h + h) * D_C + c4;
-      for (int s = 0; s < S; ++s) {
-        const float wv = wts[r][s];
-        if (wv != 0.f) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(zp + static_cast<int64_t>(s) * a.n_h * D_C);
-          z += wv * v;
-        }
-      }
-      if (a.out_latent)
-        *reinterpret_cast<f32x4*>(a.out_latent + (static_cast<int64_t>(n) * a.n_h + h) * D_C + c4) = z;
+  f32x4 z[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    f32x4 nxt[16];
+    if (s + 1 < S) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) nxt[i] = *reinterpret_cast<const f32x4*>(zp + (s + 1) * zs + 32 * i);
     }
+    const float wv = wts[r][s];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] += wv * cur[i];
+    if (s + 1 < S) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cur[i] = nxt[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c4 = 4 * cg + 32 * i;
+    if (a.out_latent && n < a.n_q)
+      *reinterpret_cast<f32x4*>(a.out_latent + (static_cast<int64_t>(n) * a.n_h + h) * D_C + c4) = z[i];
     uint16_t hi4[4], lo4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      hi4[i] = f32_to_bf16(z[i]);
-      lo4[i] = f32_to_bf16(z[i] - bf16_to_f32(hi4[i]));
+    for (int e = 0; e < 4; ++e) {
+      hi4[e] = f32_to_bf16(z[i][e]);
+      lo4[e] = f32_to_bf16(z[i][e] - bf16_to_f32(hi4[e]));
     }
-    uint2 hv = make_uint2(hi4[0] | (static_cast<uint32_t>(hi4[1]) << 16),
-                          hi4[2] | (static_cast<uint32_t>(hi4[3]) << 16));
-    uint2 lv = make_uint2(lo4[0] | (static_cast<uint32_t>(lo4[1]) << 16),
-                          lo4[2] | (static_cast<uint32_t>(lo4[3]) << 16));
-    *reinterpret_cast<uint2*>(zhi + r * ZSTRIDE + 2 * c4) = hv;
-    *reinterpret_cast<uint2*>(zlo + r * ZSTRIDE + 2 * c4) = lv;
+    *reinterpret_cast<uint2*>(zhi + r * ZSTRIDE + 2 * c4) =
+        make_uint2(hi4[0] | (static_cast<uint32_t>(hi4[1]) << 16), hi4[2] | (static_cast<uint32_t>(hi4[3]) << 16));
+    *reinterpret_cast<uint2*>(zlo + r * ZSTRIDE + 2 * c4) =
+        make_uint2(lo4[0] | (static_cast<uint32_t>(lo4[1]) << 16), lo4[2] | (static_cast<uint32_t>(lo4[3]) << 16));
   }
   __syncthreads();
 
-  const int g = l >> 5;
-  const int d = 32 * w + (l & 31);
-  const uint16_t* wrow = static_cast<const uint16_t*>(a.w_uv) + (static_cast<int64_t>(h) * D_H + d) * D_C;
   const int arow = (l & 31) * ZSTRIDE + 16 * g;
   f32x16 acc = {0};
-#pragma unroll 4
+#pragma unroll
   for (int s = 0; s < D_C / 16; ++s) {
-    const u32x4 bw = *reinterpret_cast<const u32x4*>(wrow + 16 * s + 8 * g);
+    const u32x4 b = bw[s % PFW];
+    if (s + PFW < D_C / 16) bw[s % PFW] = *reinterpret_cast<const u32x4*>(wrow + 16 * (s + PFW));
     const u32x4 ah = *reinterpret_cast<const u32x4*>(zhi + arow + 32 * s);
     const u32x4 al = *reinterpret_cast<const u32x4*>(zlo + arow + 32 * s);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah),
-                                                  __builtin_bit_cast(bf16x8, bw), acc, 0, 0, 0);
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, al),
-                                                  __builtin_bit_cast(bf16x8, bw), acc, 0, 0, 0);
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int n = n0 + 8 * (j >> 2) + 4 * g + (j & 3);
-    if (n < a.n_q) a.out[(static_cast<int64_t>(n) * a.n_h + h) * D_H + d] = acc[j];
+    const int nn = n0 + 8 * (j >> 2) + 4 * g + (j & 3);
+    if (nn < a.n_q) a.out[(static_cast<int64_t>(nn) * a.n_h + h) * D_H + d] = acc[j];
   }
 }
 

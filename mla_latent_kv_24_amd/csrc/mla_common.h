@@ -53,7 +53,12 @@ struct AbsorbArgs {
   const void* w_uk;  // [n_h][d_h][d_c] (storage dtype)
   void* q_lat;       // absorbed query layout above
   int32_t n_q, n_h, d_c, d_h, d_r;
+  const void* q_r;       // [n_q][n_h][d_r] (storage dtype); used by the fused bf16 kernel
+  const int32_t* q_pos;  // [n_q]
+  RopeTable rope;
 };
+// true when launch_absorb also writes the RoPE part (no launch_rope_q needed)
+bool absorb_fuses_rope(int bf16, int d_c, int d_h, int d_r);
 
 struct SplitArgs {
   const void* q_lat;      // absorbed query layout above

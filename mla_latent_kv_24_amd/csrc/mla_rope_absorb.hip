@@ -90,47 +90,105 @@ __global__ __launch_bounds__(256) void absorb_generic_kernel(AbsorbArgs a) {
   }
 }
 
-// ------------------------------------------- A2, latent part, bf16 MFMA path
-// Per head i: q_lat[n, i, :] = q_c[n, i, :] @ w_uk[i]  ([n x 128] @ [128 x 512]).
-// Grid (head, column half, query chunk of 256).  The workgroup stages its
-// [128 d][256 c] slab of W^UK in LDS once (row stride 576 B keeps the four rows
-// of a transpose read in distinct banks), then runs 32-query blocks through
-// v_mfma_f32_32x32x16_bf16: A = q_c rows straight from global memory (d is
-// contiguous), B = W^UK columns via ds_read_b64_tr_b16 (d is the LDS row index).
+// ---------------------------------------------- A2, bf16 MFMA path (fused)
+// Per head i: q_lat[n, i, 0:512] = q_c[n, i, :] @ w_uk[i]  ([n x 128] @ [128 x 512])
+// and q_lat[n, i, 512:] = RoPE(q_r[n, i], q_pos[n]), in one launch.
+// Grid (head, column half, query chunk of 256).  The workgroup issues the loads
+// of its [128 d][256 c] slab of W^UK, of its first query block and of its half
+// of the head's RoPE pairs, stages the slab in LDS (row stride 576 B keeps the
+// four rows of a transpose read in distinct banks), rotates its RoPE pairs,
+// and runs 32-query blocks through v_mfma_f32_32x32x16_bf16: A = q_c rows from
+// global memory (d contiguous), B = W^UK columns via ds_read_b64_tr_b16.
+// Results are staged in LDS so the hi/lo bf16 pairs leave as 16-byte stores.
 constexpr int ABS_QCHUNK = 256;
-constexpr int ABS_WSTRIDE = 576;  // bytes per staged W row (256 bf16 + 64 B pad)
+constexpr int ABS_WSTRIDE = 576;         // bytes per staged W row (256 bf16 + 64 B pad)
+constexpr int ABS_SSTRIDE = 256 * 4 + 16;  // bytes per staged fp32 output row
 
-__global__ __launch_bounds__(256, 2) void absorb_mfma_kernel(AbsorbArgs a) {
+__device__ __forceinline__ uint32_t bf16_pair(float lo_elem, float hi_elem) {
+  return static_cast<uint32_t>(f32_to_bf16(lo_elem)) | (static_cast<uint32_t>(f32_to_bf16(hi_elem)) << 16);
+}
+
+__global__ __launch_bounds__(256, 1) void absorb_mfma_kernel(AbsorbArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t wlds[D_H * ABS_WSTRIDE];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[32 * ABS_SSTRIDE];
   const int h = blockIdx.x, half_c = blockIdx.y;
   const int n_begin = blockIdx.z * ABS_QCHUNK;
+  const int n_end = min(n_begin + ABS_QCHUNK, a.n_q);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const uint16_t* wsrc = static_cast<const uint16_t*>(a.w_uk) +
-                         static_cast<int64_t>(h) * D_H * D_C + half_c * 256;
-  for (int f = tid; f < D_H * 32; f += 256) {  // 32 chunks of 16 B per row
-    const int d = f >> 5, k = f & 31;
-    *reinterpret_cast<uint4*>(wlds + d * ABS_WSTRIDE + 16 * k) =
-        *reinterpret_cast<const uint4*>(wsrc + static_cast<int64_t>(d) * D_C + 8 * k);
+  const int g = l >> 5;  // k-half of the 32x32x16 operand
+  const uint16_t* qc = static_cast<const uint16_t*>(a.q_c);
+  uint16_t* qout = static_cast<uint16_t*>(a.q_lat);
+  const int64_t rec = 2 * ROWE;  // bf16 elements per (query, head) record: hi row, lo row
+
+  // ---- issue: W^UK slab (16 chunks of 16 B per thread) and the first query block
+  const uint16_t* wsrc = static_cast<const uint16_t*>(a.w_uk) + static_cast<int64_t>(h) * D_H * D_C + half_c * 256;
+  uint4 wv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int f = tid + 256 * i, d = f >> 5, k = f & 31;
+    wv[i] = *reinterpret_cast<const uint4*>(wsrc + static_cast<int64_t>(d) * D_C + 8 * k);
+  }
+  auto load_q = [&](int n0, uint4 (&qa)[8]) {
+    const int n = n0 + (l & 31);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qa[s] = (n < n_end) ? *reinterpret_cast<const uint4*>(qc + (static_cast<int64_t>(n) * a.n_h + h) * D_H + 16 * s + 8 * g)
+                          : make_uint4(0, 0, 0, 0);
+  };
+  uint4 qa[8];
+  load_q(n_begin, qa);
+
+  // RoPE inputs of this workgroup's share of the pairs: column-half hc rotates
+  // pairs 16 hc .. 16 hc + 15 of its head for every query of the chunk
+  constexpr int RITEMS = ABS_QCHUNK * (D_R / 4) / 256;  // (query, pair) items per thread
+  const uint16_t* qr = static_cast<const uint16_t*>(a.q_r);
+  uint32_t xr[RITEMS];
+  int32_t rpos[RITEMS];
+#pragma unroll
+  for (int it = 0; it < RITEMS; ++it) {
+    const int idx = tid + 256 * it, n = n_begin + (idx >> 4), k = 16 * half_c + (idx & 15);
+    xr[it] = 0u;
+    rpos[it] = 0;
+    if (n < n_end) {
+      xr[it] = *reinterpret_cast<const uint32_t*>(qr + (static_cast<int64_t>(n) * a.n_h + h) * D_R + 2 * k);
+      rpos[it] = a.q_pos[n];
+    }
+  }
+
+  // the slab into LDS (its registers are free before the fp64 RoPE math)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int f = tid + 256 * i, d = f >> 5, k = f & 31;
+    *reinterpret_cast<uint4*>(wlds + d * ABS_WSTRIDE + 16 * k) = wv[i];
+  }
+
+  // angle and sine/cosine in fp64, rotation in fp32
+#pragma unroll
+  for (int it = 0; it < RITEMS; ++it) {
+    const int idx = tid + 256 * it, n = n_begin + (idx >> 4), k = 16 * half_c + (idx & 15);
+    if (n < n_end) {
+      double sd, cd;
+      sincos(static_cast<double>(rpos[it]) * a.rope.theta[k], &sd, &cd);
+      const float cf = static_cast<float>(cd), sf = static_cast<float>(sd);
+      const float x0 = bf16_to_f32(static_cast<uint16_t>(xr[it] & 0xffffu));
+      const float x1 = bf16_to_f32(static_cast<uint16_t>(xr[it] >> 16));
+      const float y0 = x0 * cf - x1 * sf, y1 = x0 * sf + x1 * cf;
+      const float h0 = bf16_to_f32(f32_to_bf16(y0)), h1 = bf16_to_f32(f32_to_bf16(y1));
+      uint16_t* o = qout + (static_cast<int64_t>(n) * a.n_h + h) * rec + D_C + 2 * k;
+      *reinterpret_cast<uint32_t*>(o) = bf16_pair(y0, y1);
+      *reinterpret_cast<uint32_t*>(o + ROWE) = bf16_pair(y0 - h0, y1 - h1);
+    }
   }
   __syncthreads();
 
-  const int g = l >> 5;            // k-half of the 32x32x16 operand
   const int j16 = l & 15, hf = (l >> 4) & 1;
   // transpose-read address pieces: row d = 16s + 8g + (j16>>2) [+4], column 32cb + 16hf + 4(j16&3)
   const int tr_row = 8 * g + (j16 >> 2);
   const int tr_col_b = 2 * (16 * hf + 4 * (j16 & 3));
-  const uint16_t* qc = static_cast<const uint16_t*>(a.q_c);
-  const int row_e = a.d_c + a.d_r;
 
-  for (int n0 = n_begin; n0 < min(n_begin + ABS_QCHUNK, a.n_q); n0 += 32) {
-    const int n = n0 + (l & 31);
-    uint4 qa[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      qa[s] = (n < a.n_q) ? *reinterpret_cast<const uint4*>(
-                                qc + (static_cast<int64_t>(n) * a.n_h + h) * D_H + 16 * s + 8 * g)
-                          : make_uint4(0, 0, 0, 0);
-    }
+  for (int n0 = n_begin; n0 < n_end; n0 += 32) {
+    uint4 qn[8];
+    if (n0 + 32 < n_end) load_q(n0 + 32, qn);  // next block in flight during this one
 #pragma unroll
     for (int cbl = 0; cbl < 2; ++cbl) {
       const int cb = 2 * w + cbl;  // 32-column block inside this half
@@ -138,20 +196,45 @@ __global__ __launch_bounds__(256, 2) void absorb_mfma_kernel(AbsorbArgs a) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const uint8_t* p0 = wlds + (16 * s + tr_row) * ABS_WSTRIDE + 64 * cb + tr_col_b;
-        i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(p0));
+        i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0));
         i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(p0 + 4 * ABS_WSTRIDE));
         struct { i16x4 lo, hi; } pr = {v0, v1};
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa[s]),
                                                       __builtin_bit_cast(bf16x8, pr), acc, 0, 0, 0);
       }
-      const int c = half_c * 256 + 32 * cb + (l & 31);
+      // C layout: lane l holds column 32cb + l%32 of rows 8(j/4) + 4g + j%4
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int nn = n0 + 8 * (j >> 2) + 4 * g + (j & 3);
-        if (nn < a.n_q) store_q<uint16_t>(a.q_lat, static_cast<int64_t>(nn) * a.n_h + h, row_e, c, acc[j]);
+      for (int j = 0; j < 16; ++j)
+        *reinterpret_cast<float*>(stage + (8 * (j >> 2) + 4 * g + (j & 3)) * ABS_SSTRIDE + 4 * (32 * cb + (l & 31))) = acc[j];
+    }
+    __syncthreads();
+    // 32 rows x 32 runs of 8 columns: hi and lo as 16-byte stores
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = tid + 256 * it, r = idx >> 5, k = idx & 31;
+      const int n = n0 + r;
+      if (n < n_end) {
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(stage + r * ABS_SSTRIDE + 32 * k);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(stage + r * ABS_SSTRIDE + 32 * k + 16);
+        const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hw[e] = bf16_pair(v[2 * e], v[2 * e + 1]);
+          const float h0 = bf16_to_f32(static_cast<uint16_t>(hw[e] & 0xffffu));
+          const float h1 = bf16_to_f32(static_cast<uint16_t>(hw[e] >> 16));
+          lw[e] = bf16_pair(v[2 * e] - h0, v[2 * e + 1] - h1);
+        }
+        uint16_t* o = qout + (static_cast<int64_t>(n) * a.n_h + h) * rec + half_c * 256 + 8 * k;
+        *reinterpret_cast<uint4*>(o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(o + ROWE) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       }
+    }
+    __syncthreads();  // stage reused by the next block
+    if (n0 + 32 < n_end) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qa[s] = qn[s];
     }
   }
 }
@@ -175,9 +258,13 @@ hipError_t launch_rope_q(const RopeQArgs& a, int bf16, hipStream_t st) {
   return hipGetLastError();
 }
 
+bool absorb_fuses_rope(int bf16, int d_c, int d_h, int d_r) {
+  return bf16 && d_c == D_C && d_h == D_H && d_r == D_R;
+}
+
 hipError_t launch_absorb(const AbsorbArgs& a, int bf16, hipStream_t st) {
   if (a.n_q <= 0) return hipSuccess;
-  if (bf16 && a.d_c == D_C && a.d_h == D_H) {
+  if (absorb_fuses_rope(bf16, a.d_c, a.d_h, a.d_r)) {
     dim3 grid(a.n_h, 2, (a.n_q + ABS_QCHUNK - 1) / ABS_QCHUNK);
     absorb_mfma_kernel<<<grid, 256, 0, st>>>(a);
   } else if (bf16) {

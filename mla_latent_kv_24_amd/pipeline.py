@@ -104,6 +104,19 @@ class DecodeState:
         self.combine()
         return self.out
 
+    def capture(self, fn=None, repeat=1):
+        """Capture `repeat` calls of fn (default: step) into a HIP graph.
+
+        Every launch goes to torch's current stream, which torch.cuda.graph
+        makes its capture stream, so replaying the graph reruns the same kernels
+        on the same buffers with no host work in between."""
+        fn = fn or self.step
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(repeat):
+                fn()
+        return g
+
 
 class PrefillState:
     """One sequence: prefix rows appended first, then the chunk's rows; chunk queries."""

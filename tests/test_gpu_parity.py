@@ -208,6 +208,26 @@ def test_decode_is_deterministic_and_split_invariant(pipeline):
         assert rel_err(o, outs[0]) < 1e-2
 
 
+@pytest.mark.parametrize("name", ["v2_decode", "lite_decode"])
+def test_step_graph_replay(pipeline, name):
+    """The decode step captured as a HIP graph reproduces the eager step bitwise
+    on every replay, with eager kernels and synchronisations between replays."""
+    w = W.scaled(W.WORKLOADS[name], batch=3, seq_len=700)
+    st = pipeline.DecodeState(W.make_decode_inputs(w), out_latent=True)
+    st.step()
+    torch.cuda.synchronize()
+    ref, ref_lat = st.out.clone(), st.out_latent.clone()
+    g = st.capture()
+    for _ in range(3):
+        st.out.zero_()
+        st.out_latent.zero_()
+        st.absorb()                      # eager work of the program between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.out, ref) and torch.equal(st.out_latent, ref_lat)
+
+
 @pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 63, 64, 65, 97, 4097])
 def test_decode_tile_edges(pipeline, T):
     w = W.scaled(W.WORKLOADS["v2_decode"], batch=1, seq_len=T)
