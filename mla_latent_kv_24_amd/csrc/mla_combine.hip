@@ -15,22 +15,27 @@ constexpr int CMB_MAX_SPLITS = 128;   // weights staged in LDS for the MFMA path
 constexpr int ZSTRIDE = 1040;        // bytes per staged z row (512 bf16 + 16 B pad)
 
 // ------------------------------------------------------------------------
-// bf16 MFMA path.  Grid (head, block of 32 queries); 4 waves, wave w owns the
-// 32 output dims d = 32w..32w+31.  z is combined in fp32, optionally written
-// out, then split into bf16 hi + lo parts (z = hi + lo to ~2^-16 relative) so
-// the 32x32x16 MFMA lift keeps fp32-level accuracy:
+// bf16 MFMA path.  Grid (head, block of qb <= 32 queries); 4 waves, wave w owns
+// the 32 output dims d = 32w..32w+31.  z is combined in fp32, optionally
+// written out, then split into bf16 hi + lo parts (z = hi + lo to ~2^-16
+// relative) so the 32x32x16 MFMA lift keeps fp32-level accuracy:
 //   out[n][d] = sum_c (hi[n][c] + lo[n][c]) * w_uv[h][d][c]
-// A = z rows from LDS (c contiguous), B = w_uv rows from global (c contiguous).
-// The kernel is a stream of the partials (256 KB per workgroup) and of W^UV:
-// split s+1's loads are in flight while split s accumulates, split 0's before
-// the weights are known, and the first W^UV operands before all of it.
+// A = z rows from LDS (c contiguous; rows past the block's queries are never
+// stored), B = w_uv rows from global (c contiguous).
+// The kernel is a stream of the partials and of W^UV: the split weights are
+// formed by all threads (8 per query row), the partial loads of G splits x
+// 32 / G row chunks are in flight together (G = 4 for few splits, 16 for
+// many), and the first W^UV operands are requested before all of it.
 // ------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a) {
+template <int G>
+__global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int qb) {
   __shared__ float wts[32][CMB_MAX_SPLITS];
   __shared__ __attribute__((aligned(16))) uint8_t zhi[32 * ZSTRIDE];
   __shared__ __attribute__((aligned(16))) uint8_t zlo[32 * ZSTRIDE];
-  constexpr int PFW = 8;  // W^UV operand prefetch depth (MFMA k-steps)
-  const int h = blockIdx.x, n0 = blockIdx.y * 32;
+  constexpr int PFW = 8;       // W^UV operand prefetch depth (MFMA k-steps)
+  constexpr int UB = 32 / G;   // row chunks per batch
+  const int h = blockIdx.x, n0 = blockIdx.y * qb;
+  const int rows = min(qb, a.n_q - n0);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int S = a.num_splits;
 
@@ -42,68 +47,77 @@ __global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a) {
 #pragma unroll
   for (int s = 0; s < PFW; ++s) bw[s] = *reinterpret_cast<const u32x4*>(wrow + 16 * s);
 
-  // this thread's slice of the combined latent: query row r, columns 4 cg + 32 i
-  const int r = tid >> 3, cg = tid & 7;
-  const int n = n0 + r;
-  const float* zp = a.z_part + (static_cast<int64_t>(min(n, a.n_q - 1)) * S * a.n_h + h) * D_C + 4 * cg;
-  const int64_t zs = static_cast<int64_t>(a.n_h) * D_C;  // split stride (floats)
-  f32x4 cur[16];
+  // ---- split weights exp(lse_s - LSE): thread (row r, phase p) covers splits
+  // p, p+8, ...; max and sum are reduced over the row's 8 adjacent lanes
+  {
+    const int r = tid >> 3, p = tid & 7;
+    const bool rv = r < rows;
+    const float* ls = a.lse_part + static_cast<int64_t>(n0 + (rv ? r : 0)) * S * a.n_h + h;
+    float m = CNEG_INF;
+    if (rv)
+      for (int s = p; s < S; s += 8) m = fmaxf(m, ls[static_cast<int64_t>(s) * a.n_h]);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) cur[i] = *reinterpret_cast<const f32x4*>(zp + 32 * i);
-
-  // split weights: one thread per query
-  if (tid < 32) {
-    const int nq = n0 + tid;
-    if (nq < a.n_q) {
-      const float* ls = a.lse_part + static_cast<int64_t>(nq) * S * a.n_h + h;
-      float m = CNEG_INF;
-      for (int s = 0; s < S; ++s) m = fmaxf(m, ls[static_cast<int64_t>(s) * a.n_h]);
-      float tot = 0.f;
-      for (int s = 0; s < S; ++s) {
+    for (int o = 1; o < 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float tot = 0.f;
+    if (rv)
+      for (int s = p; s < S; s += 8) {
         const float e = (m == CNEG_INF) ? 0.f : expf(ls[static_cast<int64_t>(s) * a.n_h] - m);
-        wts[tid][s] = e;
+        wts[r][s] = e;
         tot += e;
       }
-      const float inv = (tot > 0.f) ? 1.f / tot : 0.f;
-      for (int s = 0; s < S; ++s) wts[tid][s] *= inv;
-    } else {
-      for (int s = 0; s < S; ++s) wts[tid][s] = 0.f;
-    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) tot += __shfl_xor(tot, o);
+    const float inv = (tot > 0.f) ? 1.f / tot : 0.f;
+    for (int s = p; s < S; s += 8) wts[r][s] = rv ? wts[r][s] * inv : 0.f;
   }
   __syncthreads();
 
-  f32x4 z[16];
+  // ---- combined latent: unit u = (row u / 128, 4-column chunk u % 128), thread
+  // tid takes units tid + 256 j; consecutive lanes read consecutive 16 B
+  const int units = rows * (D_C / 4);
+  const int64_t zs = static_cast<int64_t>(a.n_h) * D_C;  // split stride (floats)
+  for (int j0 = 0; j0 < 16; j0 += UB) {
+    if (tid + 256 * j0 >= units) break;
+    f32x4 acc[UB];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) z[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) {
-    f32x4 nxt[16];
-    if (s + 1 < S) {
+    for (int i = 0; i < UB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += G) {
+      f32x4 v[UB][G];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) nxt[i] = *reinterpret_cast<const f32x4*>(zp + (s + 1) * zs + 32 * i);
+      for (int i = 0; i < UB; ++i) {
+        const int u = tid + 256 * (j0 + i);
+        const float* zp = a.z_part + ((static_cast<int64_t>(n0 + (u >> 7)) * S + s0) * a.n_h + h) * D_C + 4 * (u & 127);
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg)
+          v[i][gg] = (u < units && s0 + gg < S) ? *reinterpret_cast<const f32x4*>(zp + gg * zs)
+                                                : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int i = 0; i < UB; ++i) {
+        const int r = (tid + 256 * (j0 + i)) >> 7;
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg)
+          if (s0 + gg < S) acc[i] += wts[r & 31][s0 + gg] * v[i][gg];
+      }
     }
-    const float wv = wts[r][s];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) z[i] += wv * cur[i];
-    if (s + 1 < S) {
+    for (int i = 0; i < UB; ++i) {
+      const int u = tid + 256 * (j0 + i);
+      if (u >= units) continue;
+      const int r = u >> 7, c4 = 4 * (u & 127);
+      if (a.out_latent)
+        *reinterpret_cast<f32x4*>(a.out_latent + (static_cast<int64_t>(n0 + r) * a.n_h + h) * D_C + c4) = acc[i];
+      uint16_t hi4[4], lo4[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) cur[i] = nxt[i];
+      for (int e = 0; e < 4; ++e) {
+        hi4[e] = f32_to_bf16(acc[i][e]);
+        lo4[e] = f32_to_bf16(acc[i][e] - bf16_to_f32(hi4[e]));
+      }
+      *reinterpret_cast<uint2*>(zhi + r * ZSTRIDE + 2 * c4) =
+          make_uint2(hi4[0] | (static_cast<uint32_t>(hi4[1]) << 16), hi4[2] | (static_cast<uint32_t>(hi4[3]) << 16));
+      *reinterpret_cast<uint2*>(zlo + r * ZSTRIDE + 2 * c4) =
+          make_uint2(lo4[0] | (static_cast<uint32_t>(lo4[1]) << 16), lo4[2] | (static_cast<uint32_t>(lo4[3]) << 16));
     }
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int c4 = 4 * cg + 32 * i;
-    if (a.out_latent && n < a.n_q)
-      *reinterpret_cast<f32x4*>(a.out_latent + (static_cast<int64_t>(n) * a.n_h + h) * D_C + c4) = z[i];
-    uint16_t hi4[4], lo4[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      hi4[e] = f32_to_bf16(z[i][e]);
-      lo4[e] = f32_to_bf16(z[i][e] - bf16_to_f32(hi4[e]));
-    }
-    *reinterpret_cast<uint2*>(zhi + r * ZSTRIDE + 2 * c4) =
-        make_uint2(hi4[0] | (static_cast<uint32_t>(hi4[1]) << 16), hi4[2] | (static_cast<uint32_t>(hi4[3]) << 16));
-    *reinterpret_cast<uint2*>(zlo + r * ZSTRIDE + 2 * c4) =
-        make_uint2(lo4[0] | (static_cast<uint32_t>(lo4[1]) << 16), lo4[2] | (static_cast<uint32_t>(lo4[3]) << 16));
   }
   __syncthreads();
 
@@ -122,8 +136,8 @@ __global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int nn = n0 + 8 * (j >> 2) + 4 * g + (j & 3);
-    if (nn < a.n_q) a.out[(static_cast<int64_t>(nn) * a.n_h + h) * D_H + d] = acc[j];
+    const int r = 8 * (j >> 2) + 4 * g + (j & 3);
+    if (r < rows) a.out[(static_cast<int64_t>(n0 + r) * a.n_h + h) * D_H + d] = acc[j];
   }
 }
 
@@ -169,7 +183,15 @@ __global__ __launch_bounds__(256) void combine_generic_kernel(CombineArgs a) {
 hipError_t launch_combine(const CombineArgs& a, int bf16, hipStream_t st) {
   if (a.n_q <= 0) return hipSuccess;
   if (bf16 && a.d_c == D_C && a.d_h == D_H && a.num_splits <= CMB_MAX_SPLITS) {
-    combine_mfma_kernel<<<dim3(a.n_h, (a.n_q + 31) / 32), 256, 0, st>>>(a);
+    // query block: the largest of 32, 16, 8, 4 that still gives >= 256
+    // workgroups (W^UV is read once per block, the partials once in all)
+    int qb = 32;
+    while (qb > 4 && static_cast<int64_t>(a.n_h) * ((a.n_q + qb - 1) / qb) < 256) qb >>= 1;
+    const dim3 grid(a.n_h, (a.n_q + qb - 1) / qb);
+    if (a.num_splits <= 4)
+      combine_mfma_kernel<4><<<grid, 256, 0, st>>>(a, qb);
+    else
+      combine_mfma_kernel<16><<<grid, 256, 0, st>>>(a, qb);
   } else if (bf16) {
     combine_generic_kernel<uint16_t><<<dim3(a.n_q, a.n_h), 256, 0, st>>>(a);
   } else {

@@ -139,9 +139,10 @@ def test_splitkv_partials_f32(api):
 
 
 # ------------------------------------------------------ A4 + A5 combine/lift
-@pytest.mark.parametrize("dtype,n_h,S", [("bf16", 128, 4), ("bf16", 16, 1), ("bf16", 16, 64), ("f32", 16, 3)])
-def test_combine_project(api, dtype, n_h, S):
-    n_q = 45
+@pytest.mark.parametrize("dtype,n_h,S,n_q", [("bf16", 128, 4, 45), ("bf16", 16, 1, 45), ("bf16", 16, 64, 45),
+                                             ("f32", 16, 3, 45), ("bf16", 128, 64, 4), ("bf16", 128, 5, 45),
+                                             ("bf16", 128, 17, 33), ("bf16", 16, 16, 32)])
+def test_combine_project(api, dtype, n_h, S, n_q):
     Z = np.random.default_rng(40).standard_normal((n_q, S, n_h, 512)).astype(np.float32)
     lse = (np.random.default_rng(41).standard_normal((n_q, S, n_h)) * 3).astype(np.float32)
     if S > 1:
