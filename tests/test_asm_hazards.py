@@ -1,0 +1,132 @@
+"""Static checks of the split-KV kernels' gfx950 ISA (no GPU needed).
+
+The 128-head kernel issues its score MFMAs from inline asm with VGPR
+accumulators, which the compiler's hazard recognizer does not see.  These
+tests compile mla_splitkv.hip to assembly with the library's own flags and
+check:
+  * no instruction reads a VGPR written by such an MFMA within 18 wait states
+    (an XDL result needs ~11-12 on gfx950; 18 leaves margin), except the next
+    MFMA of the same accumulate chain;
+  * the 128-head kernel has no scratch reload between its first and last
+    MFMA: a spill reload is a VMEM access, and the loop's explicit vmcnt
+    bookkeeping of its LDS DMAs assumes none.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+from mla_latent_kv_24_amd import build as B
+
+NEED_WAIT_STATES = 18
+WIDE = "_ZN3mla19splitkv_wide_kernelENS_9SplitArgsE"
+MFMA_V = re.compile(r"^\s*v_mfma\S*\s+v\[(\d+):(\d+)\],\s*(\S+),\s*(\S+),\s*(\S+)")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    try:
+        cc = B.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "mla_splitkv.s"
+    cmd = [cc, *B.common_flags(), "--cuda-device-only", "-S",
+           os.path.join(B.CSRC, "mla_splitkv.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def _regs(tok):
+    m = re.match(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _operand_regs(line):
+    parts = line.split(None, 1)
+    body = parts[1] if len(parts) > 1 else ""
+    found = set()
+    for t in re.findall(r"v\[\d+:\d+\]|\bv\d+\b", body):
+        found |= _regs(t)
+    return found
+
+
+def _instructions(text):
+    out = []
+    for raw in text.splitlines():
+        s = raw.strip()
+        if not s or s.startswith((";", ".")) or s.endswith(":"):
+            continue
+        out.append(s.split(";")[0].strip())
+    return out
+
+
+def _function(text, name):
+    start = text.index(f"{name}:")
+    end = text.index(".Lfunc_end", start)
+    return text[start:end]
+
+
+def vgpr_mfma_hazards(instrs, need=NEED_WAIT_STATES):
+    """(mfma, reader, wait states) for every read of a VGPR-accumulator MFMA
+    result that comes too early."""
+    bad = []
+    for i, ins in enumerate(instrs):
+        m = MFMA_V.match(ins)
+        if not m:
+            continue
+        dst = set(range(int(m.group(1)), int(m.group(2)) + 1))
+        ws = 0
+        for nxt in instrs[i + 1:i + 60]:
+            if nxt.startswith("s_nop"):
+                ws += int(nxt.split()[1]) + 1
+                continue
+            if ws >= need:
+                break
+            m2 = MFMA_V.match(nxt)
+            if m2:
+                if (_regs(m2.group(3)) | _regs(m2.group(4))) & dst:
+                    bad.append((ins, nxt, ws))
+                src_c = _regs(m2.group(5))
+                d2 = set(range(int(m2.group(1)), int(m2.group(2)) + 1))
+                if src_c & dst and src_c != dst:
+                    bad.append((ins, nxt, ws))
+                if d2 == dst and src_c == dst:
+                    break          # the accumulate chain continues in this MFMA
+                ws += 1
+                continue
+            if _operand_regs(nxt) & dst:
+                bad.append((ins, nxt, ws))
+            ws += 1
+    return bad
+
+
+def test_checker_flags_an_early_read():
+    early = ["v_mfma_f32_32x32x16_bf16 v[18:33], v[2:5], v[6:9], v[18:33]", "s_nop 0",
+             "v_mov_b64_e32 v[40:41], v[18:19]"]
+    late = early[:1] + ["s_nop 7", "s_nop 7", "s_nop 7"] + early[2:]
+    chain = early[:1] + ["v_mfma_f32_32x32x16_bf16 v[18:33], v[2:5], v[6:9], v[18:33]"]
+    assert len(vgpr_mfma_hazards(early)) == 1
+    assert vgpr_mfma_hazards(late) == []
+    assert vgpr_mfma_hazards(chain) == []
+
+
+def test_no_early_reads_of_vgpr_mfma_results(asm):
+    bad = vgpr_mfma_hazards(_instructions(asm))
+    assert not bad, bad[:5]
+
+
+def test_wide_kernel_has_vgpr_score_mfmas(asm):
+    body = _instructions(_function(asm, WIDE))
+    assert sum(1 for s in body if MFMA_V.match(s)) >= 72      # prologue + one step's 36
+    assert sum(1 for s in body if re.match(r"v_mfma\S*\s+a\[", s)) >= 32
+
+
+def test_wide_kernel_loop_has_no_scratch_reloads(asm):
+    body = _instructions(_function(asm, WIDE))
+    idx = [i for i, s in enumerate(body) if s.startswith("v_mfma")]
+    inside = body[idx[0]:idx[-1]]
+    assert not [s for s in inside if s.startswith("scratch_load")]
