@@ -209,6 +209,55 @@ def test_decode_is_deterministic_and_split_invariant(pipeline):
         assert rel_err(o, outs[0]) < 1e-2
 
 
+@pytest.mark.parametrize("name", ["v2_decode", "lite_ragged"])
+def test_fused_decode_equals_partials_then_combine(api, pipeline, name):
+    """mla_decode (A3 + A4 + A5 in one call, partials in the caller's workspace)
+    gives bitwise the result of the separate calls under the same split plan."""
+    w = W.scaled(W.WORKLOADS[name], batch=5, seq_len=1500)
+    st = pipeline.DecodeState(W.make_decode_inputs(w), out_latent=True)
+    st.absorb()
+    st.attention()
+    st.combine()
+    torch.cuda.synchronize()
+    out = torch.empty_like(st.out)
+    lat = torch.empty_like(st.out_latent)
+    api.decode(st.d, st.q_lat, st.cache, st.stride, st.seq_lens, st.max_len, st.w_uv, out, lat)
+    torch.cuda.synchronize()
+    assert torch.equal(out, st.out) and torch.equal(lat, st.out_latent)
+
+
+def test_prefill_two_sequences(api, pipeline):
+    """One mla_prefill call over two sequences with different prefix lengths
+    (sequence slots of a shared cache), each against the oracle."""
+    C, prefixes, n_h, dtype = 40, (70, 5), 128, "bf16"
+    pinps = [W.make_prefill_inputs(W.scaled(W.WORKLOADS["v2_prefill"], seq_len=p + C, prefill_chunk=C,
+                                            seed=7 + b)) for b, p in enumerate(prefixes)]
+    w_uk, w_uv = pinps[0].w_uk, pinps[0].w_uv          # one layer: shared weights
+    stride = max(prefixes) + C + 3
+    d = api.dims(n_h)
+    cache = torch.full((2 * stride, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
+    for b, pi in enumerate(pinps):
+        tot = pi.prefix + pi.chunk
+        api.append_kv(d, dev(pi.c_kv, dtype), dev(pi.k_raw, dtype),
+                      torch.arange(tot, dtype=torch.int32, device="cuda"),
+                      torch.arange(tot, dtype=torch.int64, device="cuda") + b * stride, cache)
+    q_c = np.concatenate([pi.q_c for pi in pinps])
+    q_r = np.concatenate([pi.q_r for pi in pinps])
+    q_pos = np.concatenate([np.arange(p, p + C) for p in prefixes]).astype(np.int32)
+    q_lat = api.q_lat_empty(d, torch.bfloat16, 2, C)
+    api.absorb_q(d, dev(q_c, dtype), dev(q_r, dtype), torch.from_numpy(q_pos).cuda(), dev(w_uk, dtype),
+                 q_lat.view(2 * C, n_h, 2, 576))
+    out = torch.empty((2, C, n_h, 128), dtype=torch.float32, device="cuda")
+    plen = torch.tensor(prefixes, dtype=torch.int32, device="cuda")
+    api.prefill(d, q_lat, cache, stride, plen, max(prefixes), dev(w_uv, dtype), out)
+    got = out.cpu().numpy()
+    for b, pi in enumerate(pinps):
+        ref = O.prefill(f64(pi.q_c, dtype), f64(pi.q_r, dtype), pi.prefix, f64(pi.c_kv, dtype),
+                        f64(pi.k_raw, dtype), f64(w_uk, dtype), f64(w_uv, dtype), pi.w.rope_base)
+        assert np.all(np.isfinite(got[b]))
+        assert rel_err(got[b], ref) < SHORT_CONTEXT_TOL
+
+
 @pytest.mark.parametrize("name", ["v2_decode", "lite_decode"])
 def test_step_graph_replay(pipeline, name):
     """The decode step captured as a HIP graph reproduces the eager step bitwise
