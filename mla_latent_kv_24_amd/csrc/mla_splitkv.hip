@@ -691,10 +691,8 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
   //            tile t and its P^T export woven in;
   //   phase 2: 32 value MFMAs of tile t with the reference update of tile t+1
   //            woven in (its factor is read by every wave in the next phase 1).
-  // The DMA of tile t+3 is issued between MFMAs of phase MLA_DMA_PHASE.
-#ifndef MLA_DMA_PHASE
-#define MLA_DMA_PHASE 1
-#endif
+  // The DMA of tile t+3 is issued between score MFMAs (measured faster than
+  // between value MFMAs).
   auto step = [&](int64_t t, f32x16& sx, f32x16& sn) {
     // tile t+1 must have landed (only the nine loads of tile t+2 may still be
     // in flight); every wave is done with tile t-1, whose buffer takes tile t+3
@@ -741,10 +739,8 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
         if (s == 20) l_run += ls0 + ls1;
         if (s == 33) va0 = vread(cbuf, 4 * w, 0);
         if (s == 34) va1 = vread(cbuf, 4 * w, 1);
-#if MLA_DMA_PHASE == 1
         if (s >= 10 && s <= 10 + 2 * (LOADS - 1) && (s & 1) == 0) ch[(s - 10) >> 1] = otab[((s - 10) >> 1) * 256 + tid];
         if (s >= 12 && s <= 12 + 2 * (LOADS - 1) && (s & 1) == 0) dma(t + 3, rs3, (s - 12) >> 1, ch[(s - 12) >> 1]);
-#endif
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -787,10 +783,6 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
         // tile t+1's reference update; sn's last MFMA is far behind by now
         if (v >= 8 && v < 18) ref_update(sn, v - 8, valid1);
         if (v == 18) *reinterpret_cast<float*>(smem + A_OFF + 16 * l32 + 4 * w) = alpha;
-#if MLA_DMA_PHASE == 2
-        if (v >= 12 && v <= 12 + 2 * (LOADS - 1) && (v & 1) == 0) ch[(v - 12) >> 1] = otab[((v - 12) >> 1) * 256 + tid];
-        if (v >= 14 && v <= 14 + 2 * (LOADS - 1) && (v & 1) == 0) dma(t + 3, rs3, (v - 14) >> 1, ch[(v - 14) >> 1]);
-#endif
         __builtin_amdgcn_sched_barrier(0);
       }
     }
