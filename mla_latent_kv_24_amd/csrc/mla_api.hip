@@ -32,6 +32,7 @@ mla_status hip_status(hipError_t e, const char* where) {
 
 constexpr int kNumCUs = 256;     // MI355X compute units (the plan is device independent)
 constexpr int kMinSplitRows = 256;
+constexpr int kMaxSplitRows = 4096;  // rows per split at most (MFMA paths)
 constexpr int kMaxSplits = 65535;
 
 mla_status check_dims(const mla_dims* d, mla_dtype dt) {
@@ -65,11 +66,17 @@ int64_t split_rows(int32_t max_seq_len, int32_t num_splits) {
   return (r + mla::TILE - 1) / mla::TILE * mla::TILE;
 }
 
+// Split plan.  The MFMA kernels hold one workgroup per CU (their LDS ring),
+// so the plan aims at one round of kNumCUs workgroups and caps a split at
+// kMaxSplitRows rows, which keeps ragged batches balanced (a long sequence is
+// cut into several workgroups; splits past a short one's length exit at once).
+// The generic kernels run several workgroups per CU and aim at two rounds.
 int32_t plan_splits(const mla_dims* d, mla_dtype dt, int64_t n_q, int64_t max_len) {
   if (n_q <= 0 || max_len <= 0) return 1;
-  const bool wide = mla::splitkv_has_fast_path(d->n_h, dt == MLA_BF16, d->d_c, d->d_hR) && d->n_h >= 32;
-  const int64_t target = static_cast<int64_t>(kNumCUs) * (wide ? 1 : 2);
+  const bool fast = mla::splitkv_has_fast_path(d->n_h, dt == MLA_BF16, d->d_c, d->d_hR);
+  const int64_t target = static_cast<int64_t>(kNumCUs) * (fast ? 1 : 2);
   int64_t s = (target + n_q - 1) / n_q;
+  if (fast) s = std::max<int64_t>(s, (max_len + kMaxSplitRows - 1) / kMaxSplitRows);
   const int64_t max_s = std::max<int64_t>(1, (max_len + kMinSplitRows - 1) / kMinSplitRows);
   s = std::min(std::max<int64_t>(s, 1), max_s);
   return static_cast<int32_t>(std::min<int64_t>(s, kMaxSplits));
