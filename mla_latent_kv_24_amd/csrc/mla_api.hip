@@ -67,16 +67,20 @@ int64_t split_rows(int32_t max_seq_len, int32_t num_splits) {
 }
 
 // Split plan.  The MFMA kernels hold one workgroup per CU (their LDS ring),
-// so the plan aims at one round of kNumCUs workgroups and caps a split at
-// kMaxSplitRows rows, which keeps ragged batches balanced (a long sequence is
-// cut into several workgroups; splits past a short one's length exit at once).
+// so the plan aims at one round of kNumCUs workgroups and, for batches of
+// fewer than four rounds of queries, caps a split at kMaxSplitRows rows, which
+// keeps ragged batches balanced (a long sequence is cut into several
+// workgroups; splits past a short one's length exit at once).
 // The generic kernels run several workgroups per CU and aim at two rounds.
 int32_t plan_splits(const mla_dims* d, mla_dtype dt, int64_t n_q, int64_t max_len) {
   if (n_q <= 0 || max_len <= 0) return 1;
   const bool fast = mla::splitkv_has_fast_path(d->n_h, dt == MLA_BF16, d->d_c, d->d_hR);
   const int64_t target = static_cast<int64_t>(kNumCUs) * (fast ? 1 : 2);
   int64_t s = (target + n_q - 1) / n_q;
-  if (fast) s = std::max<int64_t>(s, (max_len + kMaxSplitRows - 1) / kMaxSplitRows);
+  // (with four or more rounds of queries, e.g. a prefill chunk, the hardware
+  // scheduler already balances whole queries and splitting only adds partials)
+  if (fast && n_q < 4 * static_cast<int64_t>(kNumCUs))
+    s = std::max<int64_t>(s, (max_len + kMaxSplitRows - 1) / kMaxSplitRows);
   const int64_t max_s = std::max<int64_t>(1, (max_len + kMinSplitRows - 1) / kMinSplitRows);
   s = std::min(std::max<int64_t>(s, 1), max_s);
   return static_cast<int32_t>(std::min<int64_t>(s, kMaxSplits));
