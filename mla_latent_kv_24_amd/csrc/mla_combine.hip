@@ -22,18 +22,19 @@ constexpr int ZSTRIDE = 1040;        // bytes per staged z row (512 bf16 + 16 B 
 //   out[n][d] = sum_c (hi[n][c] + lo[n][c]) * w_uv[h][d][c]
 // A = z rows from LDS (c contiguous; rows past the block's queries are never
 // stored), B = w_uv rows from global (c contiguous).
-// The kernel is a stream of the partials and of W^UV: the split weights are
-// formed by all threads (8 per query row), the partial loads of G splits x
-// 32 / G row chunks are in flight together (G = 4 for few splits, 16 for
-// many), and the first W^UV operands are requested before all of it.
+// The kernel is a stream of the partials and of W^UV: the wave's whole W^UV
+// slice (32 rows x 512 columns, 128 VGPRs) is requested first, so that it
+// arrives while the partials are combined; the split weights are formed by all
+// threads (8 per query row); the partial loads of G splits x 16 / G row chunks
+// are in flight together (G = 4 for few splits, 16 for many).
 // ------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int qb) {
   __shared__ float wts[32][CMB_MAX_SPLITS];
   __shared__ __attribute__((aligned(16))) uint8_t zhi[32 * ZSTRIDE];
   __shared__ __attribute__((aligned(16))) uint8_t zlo[32 * ZSTRIDE];
-  constexpr int PFW = 8;       // W^UV operand prefetch depth (MFMA k-steps)
-  constexpr int UB = 32 / G;   // row chunks per batch
+  constexpr int KS = D_C / 16;  // MFMA k-steps of the lift
+  constexpr int UB = 16 / G;    // row chunks per batch
   const int h = blockIdx.x, n0 = blockIdx.y * qb;
   const int rows = min(qb, a.n_q - n0);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -43,9 +44,9 @@ __global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int
   const int g = l >> 5;
   const int d = 32 * w + (l & 31);
   const uint16_t* wrow = static_cast<const uint16_t*>(a.w_uv) + (static_cast<int64_t>(h) * D_H + d) * D_C + 8 * g;
-  u32x4 bw[PFW];
+  u32x4 bw[KS];
 #pragma unroll
-  for (int s = 0; s < PFW; ++s) bw[s] = *reinterpret_cast<const u32x4*>(wrow + 16 * s);
+  for (int s = 0; s < KS; ++s) bw[s] = *reinterpret_cast<const u32x4*>(wrow + 16 * s);
 
   // ---- split weights exp(lse_s - LSE): thread (row r, phase p) covers splits
   // p, p+8, ...; max and sum are reduced over the row's 8 adjacent lanes
@@ -124,9 +125,8 @@ __global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int
   const int arow = (l & 31) * ZSTRIDE + 16 * g;
   f32x16 acc = {0};
 #pragma unroll
-  for (int s = 0; s < D_C / 16; ++s) {
-    const u32x4 b = bw[s % PFW];
-    if (s + PFW < D_C / 16) bw[s % PFW] = *reinterpret_cast<const u32x4*>(wrow + 16 * (s + PFW));
+  for (int s = 0; s < KS; ++s) {
+    const u32x4 b = bw[s];
     const u32x4 ah = *reinterpret_cast<const u32x4*>(zhi + arow + 32 * s);
     const u32x4 al = *reinterpret_cast<const u32x4*>(zlo + arow + 32 * s);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah),

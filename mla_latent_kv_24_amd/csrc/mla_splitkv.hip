@@ -404,14 +404,22 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      bf16x8 pb;
+      // P as bf16 hi + lo (p = hi + lo to ~2^-16): with 16 heads the matrix
+      // cores have room for the second product, and a batch that mixes very
+      // short sequences (few rows, large outputs) with long ones needs the
+      // precision
+      bf16x8 pb, pl;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(p[i]);
+      for (int i = 0; i < 8; ++i) {
+        pb[i] = static_cast<__bf16>(p[i]);
+        pl[i] = static_cast<__bf16>(p[i] - static_cast<float>(pb[i]));
+      }
 #pragma unroll
       for (int st = 0; st < VSTEPS; ++st) {
         const bf16x8 va = vb[st % PF];
         if (st + PF < VSTEPS) vb[st % PF] = vread(st + PF);
         zacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, zacc[st], 0, 0, 0);
+        zacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, zacc[st], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
