@@ -34,6 +34,11 @@ no body, and no page defines RoPE itself):
   * Prefill: query i of a chunk sits at position prefix+i and attends to rows
     0..prefix+i (inclusive causal mask).
   * W^UK and W^UV are stored per head as [n_h][d_h][d_c]; U^K_i = w_uk[i].
+  * The cache is a tensor of the storage dtype ([V3]: c^KV and k^R are what is
+    cached; [R4]: d_c + d_h^R elements per token), so the RoPE key that the
+    attention reads is RoPE(k_raw) rounded to that dtype (`store=` below;
+    round to nearest even, float64 -> float32 -> bfloat16).  c^KV needs no
+    rounding: it is stored as given.
 
 Parity: every function below is pinned by tests that do not re-type its
 formula (closed forms, brute force, a library attention routine, identities,
@@ -69,6 +74,32 @@ def rope(x: np.ndarray, pos, base: float = ROPE_BASE) -> np.ndarray:
     out[..., 0::2] = xe * cos - xo * sin
     out[..., 1::2] = xe * sin + xo * cos
     return out
+
+
+def round_to_storage(x, store: str) -> np.ndarray:
+    """Values of x as a tensor of storage dtype `store` holds them, as float64.
+
+    "f32": round to nearest even float32.  "bf16": float32 first, then round to
+    nearest even on the upper 16 bits (bfloat16 keeps float32's sign and
+    exponent and the top 7 mantissa bits); NaN stays NaN.
+    """
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if store == "f32":
+        return x32.astype(np.float64)
+    if store != "bf16":
+        raise ValueError(f"unknown storage dtype {store!r}")
+    u = x32.view(np.uint32).astype(np.uint64)
+    kept_lsb = (u >> 16) & 1
+    r = (((u + 0x7FFF + kept_lsb) >> 16) << 16) & 0xFFFFFFFF
+    out = r.astype(np.uint32).view(np.float32)
+    return np.where(np.isnan(x32), np.float32(np.nan), out).astype(np.float64)
+
+
+def cached_rope_key(k_raw, pos, base: float = ROPE_BASE, store=None) -> np.ndarray:
+    """k^R_j = RoPE(k_raw_j, pos_j) ([V3]) as the cache holds it: exact float64
+    when store is None, else rounded to the storage dtype."""
+    k = rope(k_raw, pos, base)
+    return k if store is None else round_to_storage(k, store)
 
 
 def softmax(logits: np.ndarray, axis: int = -1) -> np.ndarray:
@@ -176,10 +207,10 @@ def attend_absorbed(q_c, q_r_rot, c, k_r_rot, w_uk, w_uv, scale=None):
 
 
 # ---------------------------------------------------------------------------
-# Decode over a batch (the spec step) and causal prefill
+# Decode over a batch and causal prefill
 # ---------------------------------------------------------------------------
 def decode(q_c, q_r, seq_lens, c_kv, k_raw, w_uk, w_uv, base=ROPE_BASE, scale=None,
-           batch_idx=None, absorbed=False):
+           batch_idx=None, absorbed=False, store=None):
     """Decode one token per sequence.
 
     q_c [B, n_h, d_h], q_r [B, n_h, d_r] (pre-RoPE), seq_lens [B],
@@ -187,13 +218,15 @@ def decode(q_c, q_r, seq_lens, c_kv, k_raw, w_uk, w_uv, base=ROPE_BASE, scale=No
     The query of sequence b sits at position len_b - 1 and attends rows
     0..len_b-1.  Returns (out [B', n_h, d_h], z [B', n_h, d_c]) for the
     sequences in `batch_idx` (all by default).  z is sum_j a_ij c_j.
+    store: storage dtype of the cache ("bf16", "f32"), whose rounding of the
+    RoPE key the attention reads; None keeps the exact key.
     """
     idx = range(len(seq_lens)) if batch_idx is None else list(batch_idx)
     outs, zs = [], []
     for b in idx:
         T = int(seq_lens[b])
         c = np.asarray(c_kv[b, :T], dtype=np.float64)
-        k_rot = rope(k_raw[b, :T], np.arange(T), base)
+        k_rot = cached_rope_key(k_raw[b, :T], np.arange(T), base, store)
         q_rot = rope(q_r[b], T - 1, base)
         if absorbed:
             o, z, _ = attend_absorbed(q_c[b], q_rot, c, k_rot, w_uk, w_uv, scale)
@@ -206,19 +239,19 @@ def decode(q_c, q_r, seq_lens, c_kv, k_raw, w_uk, w_uv, base=ROPE_BASE, scale=No
 
 
 def prefill(q_c, q_r, prefix, c_kv, k_raw, w_uk, w_uv, base=ROPE_BASE, scale=None,
-            query_idx=None):
+            query_idx=None, store=None):
     """Causal prefill of one sequence.
 
     Rows 0..prefix+chunk-1 of (c_kv, k_raw) are cached (row j at position j).
     Query i (q_c [chunk, n_h, d_h], q_r pre-RoPE) sits at position prefix+i and
     attends rows 0..prefix+i.  Returns out [n, n_h, d_h] for the queries in
-    `query_idx` (all by default), computed unabsorbed.
+    `query_idx` (all by default), computed unabsorbed.  store: as in decode.
     """
     chunk = q_c.shape[0]
     idx = range(chunk) if query_idx is None else list(query_idx)
     total = prefix + chunk
     c = np.asarray(c_kv[:total], dtype=np.float64)
-    k_rot = rope(k_raw[:total], np.arange(total), base)
+    k_rot = cached_rope_key(k_raw[:total], np.arange(total), base, store)
     n_h, d_h = q_c.shape[1], q_c.shape[2]
     d_r = q_r.shape[2]
     if scale is None:

@@ -24,16 +24,23 @@ def to_np(t):
     return t.detach().cpu().numpy()
 
 
-def oracle_decode(inp, b, heads=None):
-    """Unabsorbed fp64 oracle for sequence b (selected heads): (out [h, 128], z [h, 512])."""
+def oracle_decode(inp, b, heads=None, absorbed=False):
+    """fp64 oracle for sequence b (selected heads): (out [h, 128], z [h, 512]),
+    over the cache as stored (RoPE key rounded to the workload's dtype).
+    Unabsorbed by default; absorbed=True takes the oracle's absorbed form
+    (pinned equal to the unabsorbed one to 1e-10), which is cheap enough to run
+    over every sequence of a large batch."""
     dt = inp.w.dtype
     L = int(inp.seq_lens[b])
     heads = np.arange(inp.w.n_h) if heads is None else np.asarray(heads)
     c = f64(inp.c_kv[b, :L], dt)
-    k_rot = O.rope(f64(inp.k_raw[b, :L], dt), np.arange(L), inp.w.rope_base)
+    k_rot = O.cached_rope_key(f64(inp.k_raw[b, :L], dt), np.arange(L), inp.w.rope_base, store=dt)
     q_rot = O.rope(f64(inp.q_r[b][heads], dt), L - 1, inp.w.rope_base)
-    o, a = O.attend_unabsorbed(f64(inp.q_c[b][heads], dt), q_rot, c, k_rot,
-                               f64(inp.w_uk[heads], dt), f64(inp.w_uv[heads], dt))
+    args = (f64(inp.q_c[b][heads], dt), q_rot, c, k_rot, f64(inp.w_uk[heads], dt), f64(inp.w_uv[heads], dt))
+    if absorbed:
+        o, z, _ = O.attend_absorbed(*args)
+        return o, z
+    o, a = O.attend_unabsorbed(*args)
     return o, a @ c
 
 
@@ -42,7 +49,7 @@ def oracle_prefill(pinp, queries, heads=None):
     heads = np.arange(pinp.w.n_h) if heads is None else np.asarray(heads)
     return O.prefill(f64(pinp.q_c[:, heads], dt), f64(pinp.q_r[:, heads], dt), pinp.prefix,
                      f64(pinp.c_kv, dt), f64(pinp.k_raw, dt), f64(pinp.w_uk[heads], dt),
-                     f64(pinp.w_uv[heads], dt), pinp.w.rope_base, query_idx=queries)
+                     f64(pinp.w_uv[heads], dt), pinp.w.rope_base, query_idx=queries, store=dt)
 
 
 def absorbed_layout(q32, dtype):

@@ -11,11 +11,15 @@ from helpers import TOL, oracle_decode, oracle_prefill, rel_err
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
-# (workload, sampled sequences (None = all), sampled heads (None = all))
+# (workload, sampled sequences (None = all), sampled heads (None = all)).
+# The ragged batch mixes outputs of very different sizes (a 24-row sequence's
+# output is ~6x the batch rms), so its metric takes the rms of the whole output
+# tensor: every sequence is checked against the oracle's absorbed form, and the
+# extremes of the length distribution also against the unabsorbed form.
 DECODE = [
     ("tiny_f32", None, None),
     ("lite_decode", [0, 7, 31], None),
-    ("lite_ragged", "extremes", None),
+    ("lite_ragged", "whole", None),
     ("v2_decode", [0, 21, 63], [0, 1, 37, 64, 100, 127]),
     ("v2_long", [0, 3], [0, 77, 127]),
 ]
@@ -30,9 +34,17 @@ def test_decode_full_size(name, seqs, heads):
     st = DecodeState(inp)
     out = st.step().cpu().numpy()          # append + absorb + attend + combine, as benchmarked
     assert np.all(np.isfinite(out))
-    if seqs == "extremes":
+    if seqs == "whole":
+        ref_all = np.stack([oracle_decode(inp, b, absorbed=True)[0] for b in range(w.batch)])
+        err = rel_err(out, ref_all)
+        rms = float(np.sqrt(np.mean(np.square(ref_all))))
         order = np.argsort(inp.seq_lens)
-        seqs = sorted({int(order[0]), int(order[1]), int(order[len(order) // 2]), int(order[-1])})
+        ext = sorted({int(order[0]), int(order[1]), int(order[len(order) // 2]), int(order[-1])})
+        worst = max(float(np.max(np.abs(out[b] - oracle_decode(inp, b)[0]))) for b in ext)
+        print(f"[{name}] splits={st.splits} whole-tensor max|err|/rms = {err:.3e}, "
+              f"unabsorbed on {ext}: {worst / rms:.3e}", flush=True)
+        assert err < TOL[w.dtype] and worst / rms < TOL[w.dtype]
+        return
     seqs = range(w.batch) if seqs is None else seqs
     hs = np.arange(w.n_h) if heads is None else np.asarray(heads)
     got, ref = [], []

@@ -253,7 +253,8 @@ def test_prefill_two_sequences(api, pipeline):
     got = out.cpu().numpy()
     for b, pi in enumerate(pinps):
         ref = O.prefill(f64(pi.q_c, dtype), f64(pi.q_r, dtype), pi.prefix, f64(pi.c_kv, dtype),
-                        f64(pi.k_raw, dtype), f64(w_uk, dtype), f64(w_uv, dtype), pi.w.rope_base)
+                        f64(pi.k_raw, dtype), f64(w_uk, dtype), f64(w_uv, dtype), pi.w.rope_base,
+                        store=dtype)
         assert np.all(np.isfinite(got[b]))
         assert rel_err(got[b], ref) < SHORT_CONTEXT_TOL
 

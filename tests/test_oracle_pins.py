@@ -337,6 +337,39 @@ def test_cache_accounting_matches_pages():
     assert round(O.cache_elements("mla", 60) / 1000, 1) == g["table9_large_mla_elements_k"]["value"]
 
 
+# ----------------------------------------------------- cache storage rounding
+def test_round_to_storage_matches_library_bf16():
+    """The oracle's storage rounding against torch's own float32 -> bfloat16
+    conversion (round to nearest even), over magnitudes from subnormal to
+    near overflow, and the textbook tie cases."""
+    torch = pytest.importorskip("torch")
+    r = _rng(7)
+    x = np.concatenate([r.standard_normal(20000) * 10.0 ** r.integers(-40, 38, 20000),
+                        [0.0, -0.0, 1.0, -2.5, np.inf, -np.inf]])
+    lib = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    ours = O.round_to_storage(x, "bf16")
+    assert np.array_equal(ours, lib)
+    ties = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8)])
+    assert list(O.round_to_storage(ties, "bf16")) == [1.0, 1.0 + 2.0 ** -6, -1.0]
+    assert np.isnan(O.round_to_storage(np.array([np.nan]), "bf16")[0])
+    assert np.array_equal(O.round_to_storage(ours, "bf16"), ours)          # idempotent
+    assert np.array_equal(O.round_to_storage(x, "f32"), x.astype(np.float32).astype(np.float64))
+
+
+def test_cached_rope_key_is_rope_then_storage():
+    k = _rng(8).standard_normal((50, 64))
+    pos = np.arange(50) * 977
+    assert np.array_equal(O.cached_rope_key(k, pos), O.rope(k, pos))
+    kb = O.cached_rope_key(k, pos, store="bf16")
+    exact = O.rope(k, pos)
+    # within half a bf16 ulp of the exact key (float32 first: 2^-24 more at most)
+    half_ulp = np.exp2(np.floor(np.log2(np.abs(exact))) - 8)
+    assert np.all(np.abs(kb - exact) <= half_ulp * (1 + 2.0 ** -15))
+    # position 0 leaves a bf16-representable key unchanged
+    k16 = O.round_to_storage(k, "bf16")
+    assert np.array_equal(O.cached_rope_key(k16, np.zeros(50), store="bf16"), k16)
+
+
 # -------------------------------------------------------------- generators
 def test_bf16_rounding_is_rne():
     vals = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, 1.0 + 2**-8 + 2**-20, -2.5,
