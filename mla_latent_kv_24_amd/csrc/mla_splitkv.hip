@@ -11,11 +11,11 @@
 //   S^T[t][i] = sum_e row[t][e] q_lat[i][e]    (e over d_c + d_hR = 576)
 //   Z^T[c][i] += sum_t row[t][c] P^T[t][i]    (t over the tile's rows)
 //
-// MFMA fast path (bf16, d_c=512, d_hR=64, n_h in {16,32,64,128}):
-//   * 4 waves; a wave owns HPW heads (32, or 16 when n_h=16) and a slice of the
-//     512 latent columns.  n_h=128: 4 head groups x all columns.  n_h=16:
-//     1 head group x 4 column quarters (the score is recomputed per wave; it
-//     is cheap next to the HBM stream at 16 heads).
+// MFMA fast paths (bf16, d_c=512, d_hR=64, n_h in {16,32,64,128}): n_h = 128
+// and n_h = 16 have kernels of their own below; n_h = 32 and 64 run
+// splitkv_mfma_kernel:
+//   * 4 waves; a wave owns 32 heads and a slice of the 512 latent columns
+//     (n_h = 32: 1 head group x 4 column quarters; 64: 2 x 2).
 //   * Tiles of 32 rows (36,864 B) stream into a ring of 4 LDS buffers by
 //     buffer_load ... lds (global -> LDS DMA, no staging registers), three tiles
 //     in flight while one is computed.  Rows keep their natural 1152-B stride;
@@ -32,14 +32,13 @@
 //   * Online softmax in the log2 domain with a lazy rescale: the reference max
 //     only moves when a tile max exceeds it by more than 8 (so p <= 2^8), and
 //     the Z accumulators are rescaled only then.  Exact up to rounding.
-#include <type_traits>
-
 #include "mla_common.h"
 
 namespace mla {
 
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr float RESCALE_TAU = 8.0f;
+constexpr int NQ16 = (D_C + D_R) / 32;  // 16-head score k-steps of 32 elements
 
 // 16-byte chunk swizzle of tile row t: chunk k of the row lives at k ^ swz(t).
 __device__ __forceinline__ int swz(int t) {
@@ -116,19 +115,18 @@ __device__ __forceinline__ void query_range(const SplitArgs& a, int n, int& b, i
   len = max(L, static_cast<int64_t>(0));
 }
 
-template <int HPW, int CG>
+template <int CG>
 __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
     SplitArgs a) {
+  constexpr int HPW = 32;                        // heads per wave
   constexpr int NHG = 4 / CG;                    // head groups per workgroup
   constexpr int COLS = D_C / CG;                 // latent columns per wave
   constexpr int CB = COLS / HPW;                 // value c-blocks per wave
-  constexpr int ZR = (HPW == 32) ? 16 : 4;       // accumulator registers per c-block
-  constexpr int NQ = (HPW == 32) ? 36 : 18;      // score k-steps: 576/16 or 576/32
-  constexpr int NSC = (HPW == 32) ? 16 : 8;      // scores held per lane per tile
+  constexpr int NQ = 36;                         // score k-steps (576 / 16)
+  constexpr int NSC = 16;                        // scores held per lane per tile
   constexpr int LOADS = TILE_BYTES / (16 * 256);  // 9 chunk loads per thread per tile
   constexpr int PF = 4;                          // LDS operand prefetch depth (MFMA steps)
   static_assert(TILE_BYTES == LOADS * 16 * 256, "tile must split evenly over 256 threads");
-  typedef typename std::conditional<HPW == 32, f32x16, f32x4>::type acc_t;
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_BYTES + 9 * 256 * 4];  // tile ring + DMA offset table
 
@@ -153,7 +151,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
     return;
   }
 
-  const int g32 = l >> 5, q16 = l >> 4, j16 = l & 15;
+  const int g32 = l >> 5, j16 = l & 15;
 
   // ---- tile loads: LDS chunk f = tid + 256 i of the tile receives global
   // chunk (t, p ^ swz(t)) with (t, p) = (f / 72, f % 72).  Nothing the loop
@@ -197,22 +195,14 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
   if (ntiles > 1) issue_direct(1);
   if (ntiles > 2) issue_direct(2);
 
-  // ---- absorbed queries -> B-operand registers, straight from their bf16
-  // hi/lo layout.  With 16 heads both parts are scored (the path has MFMA to
-  // spare there, and short sequences need the extra precision); with 32 heads
-  // per wave the register file holds only hi.
+  // ---- absorbed queries -> B-operand registers: the hi part of the bf16
+  // hi/lo layout (the register file has no room for lo at 32 heads per wave)
   u32x4 qreg[NQ];
-  u32x4 qlo[HPW == 16 ? NQ : 1];
   {
     const uint16_t* q = static_cast<const uint16_t*>(a.q_lat) + static_cast<int64_t>(n) * a.n_h * 2 * ROWE;
-    const uint16_t* qh = (HPW == 32) ? q + (h0 + (l & 31)) * 2 * ROWE + 8 * g32
-                                     : q + (h0 + (l & 15)) * 2 * ROWE + 8 * q16;
-    constexpr int QSTEP = (HPW == 32) ? 16 : 32;
+    const uint16_t* qh = q + (h0 + (l & 31)) * 2 * ROWE + 8 * g32;
 #pragma unroll
-    for (int s = 0; s < NQ; ++s) {
-      qreg[s] = *reinterpret_cast<const u32x4*>(qh + QSTEP * s);
-      if constexpr (HPW == 16) qlo[s] = *reinterpret_cast<const u32x4*>(qh + ROWE + QSTEP * s);
-    }
+    for (int s = 0; s < NQ; ++s) qreg[s] = *reinterpret_cast<const u32x4*>(qh + 16 * s);
   }
   vm_wait<0>();  // queries and the first tiles resident: the loop itself carries no compiler waits
 
@@ -233,40 +223,30 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
   };
 
   // ---- per-lane LDS offsets of the MFMA operands
-  int sc_off[4] = {0, 0, 0, 0};
-  int tr_off[2][4];  // [first/second transpose read][low bits of the column block]
-  if constexpr (HPW == 32) {
-    // score A: row t = l%32, element 16 s + 8 g  -> chunk 2 s + g
+  // score A: row t = l%32, element 16 s + 8 g  -> chunk 2 s + g
+  int sc_off[4];
+  {
     const int t = l & 31;
 #pragma unroll
     for (int m = 0; m < 4; ++m) sc_off[m] = t * ROWB + 16 * ((2 * m + g32) ^ swz(t));
-    // value A: rows 16u + 4g + (j16>>2) and +8, columns 32 cb + 16 hf + 4 (j16&3)
+  }
+  // value A: rows 16u + 4g + (j16>>2) and +8, columns 32 cb + 16 hf + 4 (j16&3)
+  int tr_off[2][2];  // [first/second transpose read][odd/even 32-column block]
+  {
     const int hf = (l >> 4) & 1;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int tt = 4 * g32 + (j16 >> 2) + 8 * r;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) tr_off[r][p] = tile_off(tt, 32 * (p & 1) + 16 * hf + 4 * (j16 & 3));
-    }
-  } else {
-    // score A: row t = 16 tb + l%16, element 32 s + 8 q -> chunk 4 s + q
-    const int t = l & 15;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) sc_off[m] = t * ROWB + 16 * ((4 * m + q16) ^ swz(t));
-    // value A: rows 4q + (j16>>2) and +16, columns 16 cb + 4 (j16&3)
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int tt = 4 * q16 + (j16 >> 2) + 16 * r;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) tr_off[r][p] = tile_off(tt, 16 * p + 4 * (j16 & 3));
+      for (int p = 0; p < 2; ++p) tr_off[r][p] = tile_off(tt, 32 * p + 16 * hf + 4 * (j16 & 3));
     }
   }
 
-  acc_t zacc[CB];
+  f32x16 zacc[CB];
 #pragma unroll
   for (int c = 0; c < CB; ++c)
 #pragma unroll
-    for (int r = 0; r < ZR; ++r) zacc[c][r] = 0.f;
+    for (int r = 0; r < 16; ++r) zacc[c][r] = 0.f;
   float m_run = NEG_INF, l_run = 0.f;
 
   for (int64_t it = 0; it < ntiles; ++it) {
@@ -284,7 +264,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
 
     // -------------------------------------------------- score S^T = rows . q
     float x[NSC];
-    if constexpr (HPW == 32) {
+    {
       // operands are read PF steps ahead of their MFMA; each (read, MFMA) pair is
       // pinned in place so the LDS latency hides behind the previous MFMAs
       f32x16 sacc = {0};
@@ -307,49 +287,15 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
         for (int j = 0; j < 16; ++j)
           if (8 * (j >> 2) + 4 * g32 + (j & 3) >= valid) x[j] = NEG_INF;
       }
-    } else {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        f32x4 sacc = {0};
-        u32x4 kb[PF];
-#pragma unroll
-        for (int s = 0; s < PF; ++s)
-          kb[s] = *reinterpret_cast<const u32x4*>(buf + tb * 16 * ROWB + sc_off[s & 1] + 128 * (s >> 1));
-#pragma unroll
-        for (int s = 0; s < NQ; ++s) {
-          const u32x4 kv = kb[s % PF];
-          if (s + PF < NQ)
-            kb[s % PF] = *reinterpret_cast<const u32x4*>(buf + tb * 16 * ROWB + sc_off[(s + PF) & 1] +
-                                                         128 * ((s + PF) >> 1));
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
-                                                         __builtin_bit_cast(bf16x8, qreg[s]), sacc, 0, 0, 0);
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
-                                                         __builtin_bit_cast(bf16x8, qlo[s]), sacc, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[4 * tb + j] = sacc[j];
-        if (valid < TILE) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (16 * tb + 4 * q16 + j >= valid) x[4 * tb + j] = NEG_INF;
-        }
-      }
     }
 
     // first value operands: they do not depend on P, so their LDS latency
     // overlaps the softmax below
-    constexpr int VSTEPS = (HPW == 32) ? 2 * CB : CB;
+    constexpr int VSTEPS = 2 * CB;
     auto vread = [&](int st) -> bf16x8 {
-      if constexpr (HPW == 32) {
-        const int cbg = cg * CB + (st >> 1), u = st & 1;
-        const uint8_t* bu = buf + 128 * (cbg >> 1) + 16 * u * ROWB;
-        return cat(tr_read(bu + tr_off[0][cbg & 1]), tr_read(bu + tr_off[1][cbg & 1]));
-      } else {
-        const int cbg = cg * CB + st;
-        const uint8_t* base = buf + 128 * (cbg >> 2);
-        return cat(tr_read(base + tr_off[0][cbg & 3]), tr_read(base + tr_off[1][cbg & 3]));
-      }
+      const int cbg = cg * CB + (st >> 1), u = st & 1;
+      const uint8_t* bu = buf + 128 * (cbg >> 1) + 16 * u * ROWB;
+      return cat(tr_read(bu + tr_off[0][cbg & 1]), tr_read(bu + tr_off[1][cbg & 1]));
     };
     bf16x8 vb[PF];
 #pragma unroll
@@ -362,7 +308,6 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
 #pragma unroll
     for (int j = 1; j < NSC; ++j) mx = fmaxf(mx, x[j]);
     mx = pair_max32(mx);
-    if constexpr (HPW == 16) mx = pair_max16(mx);
     const float mt = mx * a.qscale;
     const bool need = mt > m_run + RESCALE_TAU;
     if (__ballot(need)) {
@@ -372,7 +317,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
 #pragma unroll
       for (int c = 0; c < CB; ++c)
 #pragma unroll
-        for (int r = 0; r < ZR; ++r) {
+        for (int r = 0; r < 16; ++r) {
           float e = zacc[c][r];
           float tmp;
           asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
@@ -390,38 +335,17 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
     }
 
     // -------------------------------------------------- value Z^T += rows^T . P^T
-    if constexpr (HPW == 32) {
-      bf16x8 pb[2];
+    bf16x8 pb[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pb[u][i] = static_cast<__bf16>(p[8 * u + i]);
+      for (int i = 0; i < 8; ++i) pb[u][i] = static_cast<__bf16>(p[8 * u + i]);
 #pragma unroll
-      for (int st = 0; st < VSTEPS; ++st) {
-        const bf16x8 va = vb[st % PF];
-        if (st + PF < VSTEPS) vb[st % PF] = vread(st + PF);
-        zacc[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[st & 1], zacc[st >> 1], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      // P as bf16 hi + lo (p = hi + lo to ~2^-16): with 16 heads the matrix
-      // cores have room for the second product, and a batch that mixes very
-      // short sequences (few rows, large outputs) with long ones needs the
-      // precision
-      bf16x8 pb, pl;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pb[i] = static_cast<__bf16>(p[i]);
-        pl[i] = static_cast<__bf16>(p[i] - static_cast<float>(pb[i]));
-      }
-#pragma unroll
-      for (int st = 0; st < VSTEPS; ++st) {
-        const bf16x8 va = vb[st % PF];
-        if (st + PF < VSTEPS) vb[st % PF] = vread(st + PF);
-        zacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, zacc[st], 0, 0, 0);
-        zacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, zacc[st], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int st = 0; st < VSTEPS; ++st) {
+      const bf16x8 va = vb[st % PF];
+      if (st + PF < VSTEPS) vb[st % PF] = vread(st + PF);
+      zacc[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[st & 1], zacc[st >> 1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // every wave passed this iteration's barrier, so buffer (it+3)&3 == (it-1)&3 is free
@@ -431,8 +355,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
   // ---- finalize: total over the lanes sharing a head, normalise, store.  The
   // normalised Z is staged row-major in the (now idle) LDS ring so that the
   // global stores are contiguous 16-byte runs along each head's row.
-  float lt = pair_sum32(l_run);
-  if constexpr (HPW == 16) lt = pair_sum16(lt);
+  const float lt = pair_sum32(l_run);
   const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
   const float lse = (lt > 0.f) ? (m_run + log2f(lt)) * LN2 : NEG_INF;
   if (cg == 0 && l < HPW) lse_o[h0 + l] = lse;
@@ -446,27 +369,16 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
   for (int pass = 0; pass < D_C / PCOLS; ++pass) {
     const int cbase = pass * PCOLS;
     __syncthreads();  // every wave is done with the ring (tiles, or the previous pass)
-    if constexpr (HPW == 32) {
-      uint8_t* row = smem + (h0 + (l & 31)) * RS;
+    uint8_t* row = smem + (h0 + (l & 31)) * RS;
 #pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        const int cbg = cg * CB + c;
-        if (32 * cbg < cbase || 32 * cbg >= cbase + PCOLS) continue;
+    for (int c = 0; c < CB; ++c) {
+      const int cbg = cg * CB + c;
+      if (32 * cbg < cbase || 32 * cbg >= cbase + PCOLS) continue;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const f32x4 v = {zacc[c][4 * jj] * inv, zacc[c][4 * jj + 1] * inv, zacc[c][4 * jj + 2] * inv,
-                           zacc[c][4 * jj + 3] * inv};
-          *reinterpret_cast<f32x4*>(row + 4 * (32 * cbg + 8 * jj + 4 * g32 - cbase)) = v;
-        }
-      }
-    } else {
-      uint8_t* row = smem + (h0 + (l & 15)) * RS;
-#pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        const int cbg = cg * CB + c;
-        if (16 * cbg < cbase || 16 * cbg >= cbase + PCOLS) continue;
-        const f32x4 v = {zacc[c][0] * inv, zacc[c][1] * inv, zacc[c][2] * inv, zacc[c][3] * inv};
-        *reinterpret_cast<f32x4*>(row + 4 * (16 * cbg + 4 * q16 - cbase)) = v;
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 v = {zacc[c][4 * jj] * inv, zacc[c][4 * jj + 1] * inv, zacc[c][4 * jj + 2] * inv,
+                         zacc[c][4 * jj + 3] * inv};
+        *reinterpret_cast<f32x4*>(row + 4 * (32 * cbg + 8 * jj + 4 * g32 - cbase)) = v;
       }
     }
     __syncthreads();
@@ -829,6 +741,235 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
 }
 
 // ------------------------------------------------------------------------
+// n_h = 16 (the V2-Lite shape).  Per cache row the matrix work is an eighth of
+// the 128-head case, so this kernel is a stream of the cache: what counts is
+// bytes in flight and little LDS traffic.  Each wave owns every fourth 16-row
+// tile of the split (tiles w, w+4, ...) with its own online softmax and its
+// own Z for all 16 heads x 512 columns (128 AGPRs), and two LDS buffers that
+// its own DMAs fill (one tile scored while the next lands), so the loop has
+// no workgroup barrier.  The four waves' (m, l, Z) merge through LDS at the
+// end.
+//   score: v_mfma_f32_16x16x32_bf16, A = tile rows, B = absorbed queries (hi,
+//          then lo: the two products sum to the fp32 query to ~2^-16);
+//   value: v_mfma_f32_16x16x32_bf16, A = tile columns by transpose reads
+//          (each read twice along K), B = P^T straight from the score
+//          accumulator (lane l holds rows 4(l/16)+i of head l%16 in both),
+//          hi in the first half of K and lo in the second.
+// ------------------------------------------------------------------------
+constexpr int T16 = 16;                          // rows per tile
+constexpr int T16_BYTES = T16 * ROWB;            // 18,432 B
+constexpr int T16_LOADS = T16_BYTES / (16 * 64);  // 18 DMA chunks per lane per tile
+constexpr int ZPAD = D_C * 4 + 16;               // merge: bytes per staged head row
+
+__global__ __launch_bounds__(256, 1) void splitkv_h16_kernel(SplitArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[8 * T16_BYTES];
+  static_assert(4 * 16 * ZPAD + 2 * 4 * 16 * 4 <= 8 * T16_BYTES, "merge staging must fit the buffers");
+  static_assert(T16_BYTES == T16_LOADS * 16 * 64, "tile must split evenly over 64 lanes");
+
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: DMA addresses go to SGPRs
+  const int q4 = l >> 4, j16 = l & 15;
+  const int n = blockIdx.x, split = blockIdx.y;
+  int b;
+  int64_t len;
+  query_range(a, n, b, len);
+  const int64_t lo = static_cast<int64_t>(split) * a.split_rows;
+  const int64_t hi = min(lo + a.split_rows, len);
+  float* zo = a.z_part + (static_cast<int64_t>(n) * a.num_splits + split) * 16 * D_C;
+  float* lse_o = a.lse_part + (static_cast<int64_t>(n) * a.num_splits + split) * 16;
+
+  if (lo >= hi) {  // empty split (uniform over the workgroup)
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    for (int idx = tid; idx < 16 * D_C / 4; idx += 256) reinterpret_cast<f32x4*>(zo)[idx] = zero;
+    if (tid < 16) lse_o[tid] = NEG_INF;
+    return;
+  }
+  const int64_t ntiles = (hi - lo + T16 - 1) / T16;
+  const int my_tiles = static_cast<int>((ntiles > w) ? (ntiles - w + 3) / 4 : 0);  // wave-uniform
+
+  // ---- absorbed queries (B operands): head j16, elements 32 s + 8 q4 .. +7
+  u32x4 qh[NQ16], ql[NQ16];
+  {
+    const uint16_t* q = static_cast<const uint16_t*>(a.q_lat) + (static_cast<int64_t>(n) * 16 + j16) * 2 * ROWE + 8 * q4;
+#pragma unroll
+    for (int s = 0; s < NQ16; ++s) {
+      qh[s] = *reinterpret_cast<const u32x4*>(q + 32 * s);
+      ql[s] = *reinterpret_cast<const u32x4*>(q + ROWE + 32 * s);
+    }
+  }
+
+  // ---- this wave's tile DMAs: its k-th tile (split tile w + 4k) goes to
+  // buffer 2w + (k & 1).  LDS chunk f = 64 i + l of a buffer receives global
+  // chunk (t, p ^ swz(t)) with (t, p) = (f / 72, f % 72).  The buffer resource
+  // spans the tile's rows inside the split, so rows past its end arrive as zeros.
+  const uint8_t* gsplit =
+      static_cast<const uint8_t*>(a.cache) + (static_cast<int64_t>(b) * a.stride + lo) * ROWB;
+  const uint64_t gaddr = reinterpret_cast<uint64_t>(gsplit);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint8_t*)smem));
+  auto issue = [&](int k) {
+    const int64_t it = w + 4 * static_cast<int64_t>(k);
+    const uint64_t ga = gaddr + static_cast<uint64_t>(it) * T16_BYTES;
+    const int64_t rows = min(static_cast<int64_t>(T16), hi - lo - it * T16);
+    const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(ga & 0xffffffffu)),
+                      __builtin_amdgcn_readfirstlane(static_cast<int>((ga >> 32) & 0xffffu)),
+                      __builtin_amdgcn_readfirstlane(static_cast<int>(rows * ROWB)), 0x00020000};
+    const uint32_t dst = lds0 + static_cast<uint32_t>((2 * w + (k & 1)) * T16_BYTES);
+    // the lane index passes through an empty asm so that the 18 source offsets
+    // are formed here, not hoisted out of the loop into 18 live registers
+    int lx = l;
+    asm volatile("" : "+v"(lx));
+#pragma unroll
+    for (int i = 0; i < T16_LOADS; ++i) {
+      const int f = 64 * i + lx;
+      const int t = f / 72, p = f - 72 * t;
+      dma16(dst + 1024u * i, 16 * (72 * t + (p ^ swz(t))), rs, 0);
+    }
+  };
+  if (my_tiles > 0) issue(0);
+  if (my_tiles > 1) issue(1);
+  // queries and the first two tiles resident: after this the compiler has no
+  // load of its own in flight, so the loop carries no waits but the explicit ones
+  vm_wait<0>();
+
+  // ---- per-lane LDS operand offsets
+  // score A: row j16, elements 32 s + 8 q4 .. +7 -> chunk 4 s + q4
+  int sc_off[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) sc_off[m] = j16 * ROWB + 16 * ((4 * m + q4) ^ swz(j16));
+  // value A (transpose reads): rows 4 q4 + (j16 >> 2), columns 16 cb + 4 (j16 & 3)
+  int tr_off[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) tr_off[p] = tile_off(4 * q4 + (j16 >> 2), 16 * p + 4 * (j16 & 3));
+
+  f32x4 zacc[32];  // Z^T of c-block cb: columns 16 cb + 4 q4 + i of head j16
+#pragma unroll
+  for (int c = 0; c < 32; ++c) zacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = NEG_INF, l_run = 0.f;
+  const float qscale = a.qscale;
+
+  for (int k = 0; k < my_tiles; ++k) {
+    // this tile has landed (the next one's loads may stay in flight)
+    if (k + 1 < my_tiles)
+      vm_wait<T16_LOADS>();
+    else
+      vm_wait<0>();
+    const uint8_t* buf = smem + (2 * w + (k & 1)) * T16_BYTES;
+    const int64_t it = w + 4 * static_cast<int64_t>(k);
+    const int valid = static_cast<int>(min(hi - lo - it * T16, static_cast<int64_t>(T16)));
+
+    // -------------------------------------------------- score S^T = rows . q
+    constexpr int PF = 4;
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    {
+      u32x4 kb[PF];
+#pragma unroll
+      for (int s = 0; s < PF; ++s) kb[s] = *reinterpret_cast<const u32x4*>(buf + sc_off[s & 1] + 128 * (s >> 1));
+#pragma unroll
+      for (int s = 0; s < NQ16; ++s) {
+        const u32x4 kv = kb[s % PF];
+        if (s + PF < NQ16)
+          kb[s % PF] = *reinterpret_cast<const u32x4*>(buf + sc_off[(s + PF) & 1] + 128 * ((s + PF) >> 1));
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
+                                                       __builtin_bit_cast(bf16x8, qh[s]), sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
+                                                       __builtin_bit_cast(bf16x8, ql[s]), sacc, 0, 0, 0);
+      }
+    }
+    // first value operands: independent of P, so their latency overlaps the softmax
+    constexpr int VPF = 4;
+    i16x4 vb[VPF];
+#pragma unroll
+    for (int c = 0; c < VPF; ++c) vb[c] = tr_read(buf + 128 * (c >> 2) + tr_off[c & 3]);
+
+    // -------------------------------------------------- online softmax (log2)
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (4 * q4 + i < valid) ? sacc[i] : NEG_INF;
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = pair_max32(mx);
+    mx = pair_max16(mx);
+    const float mt = mx * qscale;  // scale > 0 commutes with max
+    const bool need = mt > m_run + RESCALE_TAU;
+    if (__ballot(need)) {
+      const float m_new = need ? mt : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) zacc[c] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = -m_run;
+    i16x4 ph, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(x[i], qscale, neg_m));
+      l_run += pv;
+      const uint16_t h16 = f32_to_bf16(pv);
+      ph[i] = static_cast<short>(h16);
+      pl[i] = static_cast<short>(f32_to_bf16(pv - bf16_to_f32(h16)));
+    }
+    // one K = 32 product covers both parts: k < 4 pairs the tile rows with
+    // P hi, k >= 4 pairs the same rows with P lo
+    const bf16x8 pp = cat(ph, pl);
+
+    // -------------------------------------------------- value Z^T += rows^T . P^T
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      const i16x4 va = vb[c % VPF];
+      if (c + VPF < 32) vb[c % VPF] = tr_read(buf + 128 * ((c + VPF) >> 2) + tr_off[(c + VPF) & 3]);
+      zacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat(va, va), pp, zacc[c], 0, 0, 0);
+    }
+
+    // the buffer is free once this wave's reads of it returned: refill it
+    if (k + 2 < my_tiles) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+      issue(k + 2);
+    }
+  }
+
+  // ---- merge the four waves: M = max m_w, L = sum_w 2^(m_w - M) l_w,
+  // z = sum_w 2^(m_w - M) Z_w / L.  A wave without tiles has m = -inf, l = 0.
+  float lt = pair_sum32(l_run);
+  lt = pair_sum16(lt);
+  __syncthreads();  // every wave is done with its buffers
+  float* mst = reinterpret_cast<float*>(smem + 4 * 16 * ZPAD);
+  float* lst = mst + 64;
+  if (q4 == 0) {
+    mst[16 * w + j16] = m_run;
+    lst[16 * w + j16] = lt;
+  }
+  __syncthreads();
+  float M = NEG_INF;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) M = fmaxf(M, mst[16 * v + j16]);
+  float L = 0.f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float mv = mst[16 * v + j16];
+    if (mv != NEG_INF) L += lst[16 * v + j16] * __builtin_amdgcn_exp2f(mv - M);
+  }
+  const float f = (m_run != NEG_INF && L > 0.f) ? __builtin_amdgcn_exp2f(m_run - M) / L : 0.f;
+  {
+    uint8_t* row = smem + w * 16 * ZPAD + j16 * ZPAD + 16 * q4;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      const f32x4 v = {zacc[c][0] * f, zacc[c][1] * f, zacc[c][2] * f, zacc[c][3] * f};
+      *reinterpret_cast<f32x4*>(row + 64 * c) = v;
+    }
+  }
+  if (w == 0 && q4 == 0) lse_o[j16] = (L > 0.f) ? (M + log2f(L)) * LN2 : NEG_INF;
+  __syncthreads();
+  for (int idx = tid; idx < 16 * (D_C / 4); idx += 256) {
+    const int h = idx >> 7, c4 = idx & 127;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(smem + h * ZPAD + 16 * c4);
+#pragma unroll
+    for (int v = 1; v < 4; ++v) acc += *reinterpret_cast<const f32x4*>(smem + v * 16 * ZPAD + h * ZPAD + 16 * c4);
+    *reinterpret_cast<f32x4*>(zo + h * D_C + 4 * c4) = acc;
+  }
+}
+
+// ------------------------------------------------------------------------
 // Generic fp32 VALU path (MLA_F32 storage, or bf16 with an n_h without an MFMA
 // instance).  One workgroup per (query, split, head); 256 rows per step: one
 // thread scores one row, then every thread accumulates two latent columns.
@@ -913,9 +1054,9 @@ hipError_t launch_splitkv(const SplitArgs& a, int bf16, hipStream_t st) {
   if (splitkv_has_fast_path(a.n_h, bf16, a.d_c, a.d_r)) {
     dim3 grid(a.n_q, a.num_splits);
     switch (a.n_h) {
-      case 16: splitkv_mfma_kernel<16, 4><<<grid, 256, 0, st>>>(a); break;
-      case 32: splitkv_mfma_kernel<32, 4><<<grid, 256, 0, st>>>(a); break;
-      case 64: splitkv_mfma_kernel<32, 2><<<grid, 256, 0, st>>>(a); break;
+      case 16: splitkv_h16_kernel<<<grid, 256, 0, st>>>(a); break;
+      case 32: splitkv_mfma_kernel<4><<<grid, 256, 0, st>>>(a); break;
+      case 64: splitkv_mfma_kernel<2><<<grid, 256, 0, st>>>(a); break;
       default: splitkv_wide_kernel<<<grid, 256, 0, st>>>(a); break;
     }
   } else {
