@@ -114,23 +114,21 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copy probe: 1 GiB device-to-device copy done")
 
-    # The step: (append, absorb) as one HIP graph, the attention kernel
-    # launched between the two HIP events that time it inside the timed region
-    # (events cannot be recorded inside a captured graph here), then the
-    # combine as a graph.  All on torch's current stream.
-    def pre():
+    # The step: append, absorb, the attention kernel between the two HIP
+    # events that time it inside the timed region, then the combine; each a
+    # plain launch on torch's current stream.  (Events cannot be recorded
+    # inside a captured HIP graph here, and replaying the other stages as
+    # graphs around the eager attention launch measured ~7 us slower per
+    # graph than plain launches: the host enqueues far ahead of the GPU.)
+    def run_step(e0=None, e1=None):
         st.append_new()
         st.absorb()
-    g_pre, g_post = st.capture(pre), st.capture(st.combine)
-
-    def run_step(e0=None, e1=None):
-        g_pre.replay()
         if e0 is not None:
             e0.record()
         st.attention()
         if e1 is not None:
             e1.record()
-        g_post.replay()
+        st.combine()
 
     # Settle: at its 1400 W limit the board's clock needs about a second of
     # this load to reach its sustained value; the first ~10 ms run at a
