@@ -25,7 +25,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 ROW_BYTES = 1152               # one bf16 cache row [c_kv 512 ; k_R 64]
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_splitkv_v2_decode.json")
-KERNEL_SRC = os.path.join(ROOT, "mla_latent_kv_24_amd", "csrc", "mla_splitkv.hip")
+# the attention kernel's sources: the counters are valid only for exactly these
+KERNEL_SRCS = [os.path.join(ROOT, "mla_latent_kv_24_amd", "csrc", f)
+               for f in ("mla_splitkv.hip", "mla_tile.h", "mla_common.h")]
 
 
 def log(msg):
@@ -33,7 +35,10 @@ def log(msg):
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def pmc_traffic(per_launch_units):

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3
 
 typedef enum {
   MLA_OK = 0,
@@ -171,6 +171,34 @@ mla_status mla_prefill(const mla_dims* dims, mla_dtype dtype, int32_t batch, int
                        const int32_t* prefix_lens, int32_t max_prefix_len,
                        const void* w_uv, float* out, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* A6, unabsorbed form -- the causal prefill of mla_prefill computed from
+ * per-head keys and values made explicit (review section 2: k^C_{j,i} =
+ * U^K_i c_j, v^C_{j,i} = U^V_i c_j; section 3: k_{j,i} = [k^C_{j,i}; k^R_j],
+ * l_ij = [q^C_i; RoPE(q^R_i)] . k_{j,i} / sqrt(d_h + d_hR),
+ * o_i = sum_j softmax_j(l_ij) v^C_{j,i}).  Per (key, query, head) this is
+ * 640 multiply-adds against the absorbed form's 1,088, at the price of one
+ * pass that writes the explicit keys and values into the workspace.
+ *   q_c [batch][chunk][n_h][d_h] and q_r [batch][chunk][n_h][d_hR] (before
+ *   RoPE; query i of sequence b sits at position prefix_lens[b] + i and is
+ *   rotated there), bf16.
+ *   cache, cache_seq_stride, prefix_lens, max_prefix_len: as mla_prefill.
+ *   w_uk, w_uv [n_h][d_h][d_c] bf16; out fp32 [batch][chunk][n_h][d_h].
+ *   workspace: at least mla_prefill_unabsorbed_workspace_bytes() (device;
+ *   batch * n_h * round_up(max_prefix_len + chunk, 128) rows of 1,152 B).
+ * bf16 storage and n_h a multiple of 8 only (else MLA_ERR_UNSUPPORTED).
+ * Precision: queries that see few keys (a workgroup of 256 queries whose
+ * first one sees fewer than 2,048) take every operand as a bf16 hi + lo pair;
+ * longer ones round k^C, v^C, RoPE(q^R) and the softmax weights to bf16 once. */
+size_t mla_prefill_unabsorbed_workspace_bytes(const mla_dims* dims, mla_dtype dtype,
+                                              int32_t batch, int32_t chunk,
+                                              int32_t max_prefix_len);
+mla_status mla_prefill_unabsorbed(const mla_dims* dims, mla_dtype dtype, int32_t batch,
+                                  int32_t chunk, const void* q_c, const void* q_r,
+                                  const void* cache, int64_t cache_seq_stride,
+                                  const int32_t* prefix_lens, int32_t max_prefix_len,
+                                  const void* w_uk, const void* w_uv, float* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -59,6 +59,9 @@ _SIGS = {
     "mla_decode": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp,
                                   _vp, _sz, _vp]),
     "mla_prefill_workspace_bytes": (_sz, [_P, ctypes.c_int, _i32, _i32, _i32]),
+    "mla_prefill_unabsorbed_workspace_bytes": (_sz, [_P, ctypes.c_int, _i32, _i32, _i32]),
+    "mla_prefill_unabsorbed": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i32,
+                                              _vp, _vp, _vp, _vp, _sz, _vp]),
     "mla_prefill": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _i64, _vp, _i32, _vp, _vp,
                                    _vp, _sz, _vp]),
 }
@@ -195,3 +198,23 @@ def prefill(d: Dims, q_lat, cache, stride: int, prefix_lens, max_prefix_len: int
                             _ptr(prefix_lens), max_prefix_len, _ptr(w_uv), _ptr(out),
                             _ptr(workspace), workspace.numel(), _stream(cache.device)),
            "mla_prefill")
+
+
+def prefill_unabsorbed_workspace_bytes(d: Dims, dtype: int, batch: int, chunk: int, max_prefix_len: int) -> int:
+    return _lib.mla_prefill_unabsorbed_workspace_bytes(ctypes.byref(d), dtype, batch, chunk, max_prefix_len)
+
+
+def prefill_unabsorbed(d: Dims, q_c, q_r, cache, stride: int, prefix_lens, max_prefix_len: int, w_uk, w_uv,
+                       out, workspace=None) -> None:
+    """A6 in the unabsorbed form: q_c [B, chunk, n_h, d_h], q_r [B, chunk, n_h, d_hR] (before RoPE),
+    out [B, chunk, n_h, d_h] fp32."""
+    assert prefix_lens.dtype == torch.int32 and q_c.dtype == cache.dtype == q_r.dtype == w_uk.dtype
+    dt = _dtype(cache)
+    B, chunk = q_c.shape[0], q_c.shape[1]
+    need = prefill_unabsorbed_workspace_bytes(d, dt, B, chunk, max_prefix_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=cache.device)
+    _check(_lib.mla_prefill_unabsorbed(ctypes.byref(d), dt, B, chunk, _ptr(q_c), _ptr(q_r), _ptr(cache), stride,
+                                       _ptr(prefix_lens), max_prefix_len, _ptr(w_uk), _ptr(w_uv), _ptr(out),
+                                       _ptr(workspace), workspace.numel(), _stream(cache.device)),
+           "mla_prefill_unabsorbed")

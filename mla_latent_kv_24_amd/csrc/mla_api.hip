@@ -34,6 +34,9 @@ constexpr int kNumCUs = 256;     // MI355X compute units (the plan is device ind
 constexpr int kMinSplitRows = 256;
 constexpr int kMaxSplitRows = 4096;  // rows per split at most (MFMA paths)
 constexpr int kMaxSplits = 65535;
+// unabsorbed prefill: a workgroup whose first query sees fewer keys than this
+// takes the hi + lo products
+constexpr int kPreciseBelow = 2048;
 
 mla_status check_dims(const mla_dims* d, mla_dtype dt) {
   if (!d) return fail(MLA_ERR_INVALID_ARGUMENT, "dims is NULL");
@@ -302,4 +305,65 @@ mla_status mla_prefill(const mla_dims* dims, mla_dtype dtype, int32_t batch, int
   return hip_status(mla::launch_combine(a, dtype == MLA_BF16, s), "mla_prefill (combine)");
 }
 
+
+size_t mla_prefill_unabsorbed_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t batch,
+                                              int32_t chunk, int32_t max_prefix_len) {
+  if (check_dims(dims, dtype) != MLA_OK || dtype != MLA_BF16 || batch < 1 || chunk < 1 || max_prefix_len < 0)
+    return 0;
+  const int64_t rows = static_cast<int64_t>(max_prefix_len) + chunk;
+  const int64_t rows_cap = (rows + mla::XROWS_ALIGN - 1) / mla::XROWS_ALIGN * mla::XROWS_ALIGN;
+  return static_cast<size_t>(batch) * dims->n_h * rows_cap * mla::ROWB;
+}
+
+mla_status mla_prefill_unabsorbed(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk,
+                                  const void* q_c, const void* q_r, const void* cache, int64_t cache_seq_stride,
+                                  const int32_t* prefix_lens, int32_t max_prefix_len, const void* w_uk,
+                                  const void* w_uv, float* out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  if (dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_unabsorbed: bf16 storage only");
+  if (dims->n_h % 8) return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_unabsorbed: n_h=%d must be a multiple of 8", dims->n_h);
+  if (batch < 1 || chunk < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d, chunk=%d must be >= 1", batch, chunk);
+  if (batch > 65535) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d > 65535", batch);
+  if (max_prefix_len < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "max_prefix_len=%d < 0", max_prefix_len);
+  const int64_t max_len = static_cast<int64_t>(max_prefix_len) + chunk;
+  if (max_len > cache_seq_stride)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "max_prefix_len + chunk = %lld > cache_seq_stride=%lld",
+                (long long)max_len, (long long)cache_seq_stride);
+  if (max_len > 0x7fffffff - mla::XROWS_ALIGN) return fail(MLA_ERR_INVALID_ARGUMENT, "prefix + chunk too large");
+  if (!q_c || !q_r || !cache || !prefix_lens || !w_uk || !w_uv || !out || !workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const size_t need = mla_prefill_unabsorbed_workspace_bytes(dims, dtype, batch, chunk, max_prefix_len);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", workspace_bytes, need);
+  const int64_t rows_cap = (max_len + mla::XROWS_ALIGN - 1) / mla::XROWS_ALIGN * mla::XROWS_ALIGN;
+  mla::ExpandArgs e{};
+  e.cache = cache;
+  e.prefix_lens = prefix_lens;
+  e.w_uk = w_uk;
+  e.w_uv = w_uv;
+  e.x = workspace;
+  e.stride = cache_seq_stride;
+  e.rows_cap = rows_cap;
+  e.batch = batch;
+  e.n_h = dims->n_h;
+  e.chunk = chunk;
+  e.max_len = static_cast<int32_t>(max_len);
+  mla::PrefillArgs p{};
+  p.q_c = q_c;
+  p.q_r = q_r;
+  p.x = workspace;
+  p.prefix_lens = prefix_lens;
+  p.out = out;
+  p.rows_cap = rows_cap;
+  p.batch = batch;
+  p.n_h = dims->n_h;
+  p.chunk = chunk;
+  p.max_len = static_cast<int32_t>(max_len);
+  p.precise_below = kPreciseBelow;
+  p.qscale = static_cast<float>(scale_of(dims) * 1.4426950408889634);
+  fill_rope(dims, p.rope);
+  return hip_status(mla::launch_prefill_unabsorbed(e, p, static_cast<hipStream_t>(stream)), "mla_prefill_unabsorbed");
+}
 }  // extern "C"

@@ -85,12 +85,41 @@ struct CombineArgs {
   int32_t n_q, n_h, d_c, d_h, num_splits;
 };
 
+// Unabsorbed prefill.  Expanded rows x[b][h][row][576] (bf16) keep the cache
+// row geometry: [k^C hi | v^C hi | k^C lo | v^C lo] (4 x 128) then k^R (64),
+// with k^C = U^K_h c_row, v^C = U^V_h c_row formed in fp32 and split as
+// hi = bf16(v), lo = bf16(v - hi).
+constexpr int XROWS_ALIGN = 128;   // rows_cap is a multiple of this
+struct ExpandArgs {
+  const void* cache;            // bf16 rows of d_c + d_r
+  const int32_t* prefix_lens;   // [batch]
+  const void* w_uk;             // [n_h][d_h][d_c] bf16
+  const void* w_uv;             // [n_h][d_h][d_c] bf16
+  void* x;                      // [batch][n_h][rows_cap][576] bf16
+  int64_t stride;               // cache rows per sequence slot
+  int64_t rows_cap;             // expanded rows per (sequence, head)
+  int32_t batch, n_h, chunk, max_len;  // max_len: host bound on prefix + chunk
+};
+struct PrefillArgs {
+  const void* q_c;              // [batch][chunk][n_h][d_h] bf16
+  const void* q_r;              // [batch][chunk][n_h][d_r] bf16, before RoPE
+  const void* x;                // expanded rows (ExpandArgs::x)
+  const int32_t* prefix_lens;   // [batch]
+  float* out;                   // [batch][chunk][n_h][d_h] fp32
+  int64_t rows_cap;
+  int32_t batch, n_h, chunk, max_len;
+  int32_t precise_below;        // workgroups whose first query sees fewer keys take hi + lo products
+  float qscale;                 // softmax_scale * log2(e)
+  RopeTable rope;
+};
+
 // host launchers (defined in the .hip files); return hipGetLastError() after launch
 hipError_t launch_append(const AppendArgs& a, int bf16, hipStream_t st);
 hipError_t launch_rope_q(const RopeQArgs& a, int bf16, hipStream_t st);
 hipError_t launch_absorb(const AbsorbArgs& a, int bf16, hipStream_t st);
 hipError_t launch_splitkv(const SplitArgs& a, int bf16, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, int bf16, hipStream_t st);
+hipError_t launch_prefill_unabsorbed(const ExpandArgs& e, const PrefillArgs& p, hipStream_t st);
 bool splitkv_has_fast_path(int n_h, int bf16, int d_c, int d_r);
 
 // ---------------------------------------------------------------- device helpers
@@ -100,6 +129,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {  // round to nearest even
   __bf16 h = static_cast<__bf16>(f);
   return __builtin_bit_cast(uint16_t, h);
+}
+// bf16 pair (round to nearest even), lo in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 template <typename T>
 __device__ __forceinline__ float load_as_f32(const T* p, int64_t i);
@@ -133,6 +166,17 @@ template <>
 __device__ __forceinline__ float load_q<uint16_t>(const void* q_lat, int64_t nh, int row_e, int e) {
   const uint16_t* q = static_cast<const uint16_t*>(q_lat) + nh * 2 * row_e;
   return bf16_to_f32(q[e]) + bf16_to_f32(q[row_e + e]);
+}
+
+// RoPE of the interleaved pair (x0, x1) by angle pos * theta: the angle and
+// its sine/cosine in fp64, the rotation itself in fp32.
+__device__ __forceinline__ void rope_pair(float x0, float x1, int64_t pos, double theta,
+                                          float& y0, float& y1) {
+  double s, c;
+  sincos(static_cast<double>(pos) * theta, &s, &c);
+  const float cf = static_cast<float>(c), sf = static_cast<float>(s);
+  y0 = x0 * cf - x1 * sf;
+  y1 = x0 * sf + x1 * cf;
 }
 
 template <typename T>

@@ -11,18 +11,6 @@
 
 namespace mla {
 
-// ----------------------------------------------------------------- RoPE pair
-// Interleaved pair (x0, x1) rotated by angle pos * theta: the angle and its
-// sine/cosine in fp64, the rotation itself in fp32.
-__device__ __forceinline__ void rope_pair(float x0, float x1, int32_t pos, double theta,
-                                          float& y0, float& y1) {
-  double s, c;
-  sincos(static_cast<double>(pos) * theta, &s, &c);
-  const float cf = static_cast<float>(c), sf = static_cast<float>(s);
-  y0 = x0 * cf - x1 * sf;
-  y1 = x0 * sf + x1 * cf;
-}
-
 // ------------------------------------------------------------- A1: append
 // One workgroup of 64 threads per token.  Threads copy the latent in 16-byte
 // pieces; the first d_r/2 threads rotate one RoPE pair each.

@@ -146,6 +146,7 @@ class PrefillState:
         dtc = api.BF16 if w.dtype == "bf16" else api.F32
         ws = api.prefill_workspace_bytes(self.d, dtc, 1, inp.chunk, inp.prefix)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        self.workspace_x = None            # expanded rows of the unabsorbed form, on first use
 
     def append_all(self):
         api.append_kv(self.d, self.c_kv, self.k_raw, self.pos, self.rows, self.cache)
@@ -156,6 +157,15 @@ class PrefillState:
     def attend(self):
         api.prefill(self.d, self.q_lat, self.cache, self.stride, self.prefix_lens, self.prefix,
                     self.w_uv, self.out, self.workspace)
+
+    def attend_unabsorbed(self, out=None):
+        """A6 in the unabsorbed form (explicit per-head keys and values), into `out` (default self.out)."""
+        if self.workspace_x is None:
+            n = api.prefill_unabsorbed_workspace_bytes(self.d, api.BF16, 1, self.chunk, self.prefix)
+            self.workspace_x = torch.empty(n, dtype=torch.uint8, device=self.cache.device)
+        api.prefill_unabsorbed(self.d, self.q_c.view(1, *self.q_c.shape), self.q_r.view(1, *self.q_r.shape),
+                               self.cache, self.stride, self.prefix_lens, self.prefix, self.w_uk, self.w_uv,
+                               self.out if out is None else out, self.workspace_x)
 
     def step(self):
         self.append_all()

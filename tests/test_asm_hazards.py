@@ -1,15 +1,15 @@
-"""Static checks of the split-KV kernels' gfx950 ISA (no GPU needed).
+"""Static checks of the attention kernels' gfx950 ISA (no GPU needed).
 
-The 128-head kernel issues its score MFMAs from inline asm with VGPR
-accumulators, which the compiler's hazard recognizer does not see.  These
-tests compile mla_splitkv.hip to assembly with the library's own flags and
-check:
+The 128-head decode kernel and the prefill attention kernel issue MFMAs from
+inline asm with VGPR accumulators, which the compiler's hazard recognizer
+does not see.  These tests compile mla_splitkv.hip and mla_prefill.hip to
+assembly with the library's own flags and check:
   * no instruction reads a VGPR written by such an MFMA within 18 wait states
     (an XDL result needs ~11-12 on gfx950; 18 leaves margin), except the next
     MFMA of the same accumulate chain;
-  * the 128-head kernel has no scratch reload between its first and last
-    MFMA: a spill reload is a VMEM access, and the loop's explicit vmcnt
-    bookkeeping of its LDS DMAs assumes none.
+  * the kernels that stream tiles by LDS DMA have no scratch reload between
+    their first and last MFMA: a spill reload is a VMEM access, and the
+    loops' explicit vmcnt bookkeeping of their DMAs assumes none.
 """
 import os
 import re
@@ -24,17 +24,25 @@ WIDE = "_ZN3mla19splitkv_wide_kernelENS_9SplitArgsE"
 MFMA_V = re.compile(r"^\s*v_mfma\S*\s+v\[(\d+):(\d+)\],\s*(\S+),\s*(\S+),\s*(\S+)")
 
 
-@pytest.fixture(scope="module")
-def asm(tmp_path_factory):
+def _compile(tmp_path_factory, src):
     try:
         cc = B.hipcc()
     except RuntimeError:
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "mla_splitkv.s"
-    cmd = [cc, *B.common_flags(), "--cuda-device-only", "-S",
-           os.path.join(B.CSRC, "mla_splitkv.hip"), "-o", str(out)]
+    out = tmp_path_factory.mktemp("asm") / src.replace(".hip", ".s")
+    cmd = [cc, *B.common_flags(), "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     return out.read_text()
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    return _compile(tmp_path_factory, "mla_splitkv.hip")
+
+
+@pytest.fixture(scope="module")
+def asm_prefill(tmp_path_factory):
+    return _compile(tmp_path_factory, "mla_prefill.hip")
 
 
 def _regs(tok):
@@ -130,3 +138,35 @@ def test_wide_kernel_loop_has_no_scratch_reloads(asm):
     idx = [i for i, s in enumerate(body) if s.startswith("v_mfma")]
     inside = body[idx[0]:idx[-1]]
     assert not [s for s in inside if s.startswith("scratch_load")]
+
+
+PREFILL = ["_ZN3mla19prefill_attn_kernelILb1EEEvNS_11PrefillArgsE",
+           "_ZN3mla19prefill_attn_kernelILb0EEEvNS_11PrefillArgsE"]
+
+
+def test_prefill_no_early_reads_of_vgpr_mfma_results(asm_prefill):
+    body = _instructions(asm_prefill)
+    assert sum(1 for x in body if MFMA_V.match(x)) >= 64      # both instances issue VGPR-accumulator MFMAs
+    bad = vgpr_mfma_hazards(body)
+    assert not bad, bad[:5]
+
+
+@pytest.mark.parametrize("name", PREFILL)
+def test_prefill_attention_loop_has_no_scratch_reloads(asm_prefill, name):
+    body = _instructions(_function(asm_prefill, name))
+    idx = [i for i, x in enumerate(body) if x.startswith("v_mfma")]
+    inside = body[idx[0]:idx[-1]]
+    assert not [x for x in inside if x.startswith("scratch_load")]
+
+
+def test_prefill_asm_mfmas_wait_after_valu_writes(asm_prefill):
+    """The prefill kernel's asm MFMAs read sources that VALU code writes just
+    before (P, copies of the queries, rescaled accumulators); an MFMA needs 2
+    wait states after such a write, and the compiler inserts none for asm:
+    each of these MFMAs is emitted right after an s_nop of at least 1."""
+    for name in PREFILL:
+        body = _instructions(_function(asm_prefill, name))
+        for i, ins in enumerate(body):
+            if MFMA_V.match(ins):
+                assert body[i - 1].startswith("s_nop") and int(body[i - 1].split()[1]) >= 1, (name, i, body[i - 1])
+

@@ -71,3 +71,23 @@ def test_prefill_full_size():
     err = rel_err(got, ref)
     print(f"[v2_prefill] max|err|/rms = {err:.3e}", flush=True)
     assert err < TOL["bf16"]
+
+
+def test_prefill_unabsorbed_full_size():
+    """The 4,096-query chunk after a 4,096-row prefix through the unabsorbed
+    entry point, sampled queries and heads against the oracle."""
+    from mla_latent_kv_24_amd.pipeline import PrefillState
+    w = W.WORKLOADS["v2_prefill"]
+    pinp = W.make_prefill_inputs(w)
+    st = PrefillState(pinp)
+    st.append_all()
+    st.attend_unabsorbed()
+    out = st.out.cpu().numpy()[0]
+    assert np.all(np.isfinite(out))
+    queries = [0, 1, 31, 32, 255, 256, 1000, 2047, 4000, 4095]
+    heads = [0, 5, 64, 127]
+    ref = oracle_prefill(pinp, queries, heads)
+    err = rel_err(out[queries][:, heads], ref)
+    print(f"[v2_prefill unabsorbed] max|err|/rms = {err:.3e}", flush=True)
+    assert err < TOL["bf16"]
+

@@ -357,3 +357,55 @@ def test_prefill_causal_rows(pipeline):
     for i in range(96):
         same = torch.equal(before[0, i], after[0, i])
         assert same == (64 + i < j), i
+
+
+# ------------------------------------------------- prefill, unabsorbed form
+# Shapes cover: both precisions (a workgroup of 256 queries takes hi + lo
+# products when its first query sees fewer than 2,048 keys), a chunk whose
+# query blocks straddle that threshold, ragged last tiles and query blocks,
+# and 16 heads.  The bar is the plain 2e-2 at every length.
+@pytest.mark.parametrize("n_h,prefix,chunk", [(128, 0, 33), (128, 100, 65), (128, 2000, 65), (128, 2100, 300),
+                                              (128, 1900, 600), (16, 40, 70), (16, 3000, 257)])
+def test_prefill_unabsorbed(pipeline, n_h, prefix, chunk):
+    base = W.WORKLOADS["v2_prefill"] if n_h == 128 else W.scaled(W.WORKLOADS["lite_decode"], batch=1)
+    w = W.scaled(base, seq_len=prefix + chunk, prefill_chunk=chunk, batch=1)
+    pinp = W.make_prefill_inputs(w)
+    st = pipeline.PrefillState(pinp)
+    st.append_all()
+    st.attend_unabsorbed()
+    got = st.out.cpu().numpy()[0]
+    queries = range(chunk) if chunk <= 80 else sorted({0, 1, 31, 32, 63, 64, 255, 256, chunk // 2, chunk - 1})
+    heads = None if n_h == 16 else [0, 1, 37, 64, 127]
+    ref = oracle_prefill(pinp, list(queries), heads)
+    g = got[list(queries)] if heads is None else got[list(queries)][:, heads]
+    assert np.all(np.isfinite(got))
+    assert rel_err(g, ref) < TOL["bf16"], (n_h, prefix, chunk, rel_err(g, ref))
+
+
+def test_prefill_unabsorbed_two_sequences(api):
+    """One call over two sequences with different prefixes (slots of a shared
+    cache, shared weights), each against the oracle at the plain bar."""
+    C, prefixes, n_h, dtype = 40, (70, 5), 128, "bf16"
+    pinps = [W.make_prefill_inputs(W.scaled(W.WORKLOADS["v2_prefill"], seq_len=p + C, prefill_chunk=C,
+                                            seed=7 + b)) for b, p in enumerate(prefixes)]
+    w_uk, w_uv = pinps[0].w_uk, pinps[0].w_uv
+    stride = max(prefixes) + C + 3
+    d = api.dims(n_h)
+    cache = torch.full((2 * stride, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
+    for b, pi in enumerate(pinps):
+        tot = pi.prefix + pi.chunk
+        api.append_kv(d, dev(pi.c_kv, dtype), dev(pi.k_raw, dtype),
+                      torch.arange(tot, dtype=torch.int32, device="cuda"),
+                      torch.arange(tot, dtype=torch.int64, device="cuda") + b * stride, cache)
+    q_c = dev(np.stack([pi.q_c for pi in pinps]), dtype)
+    q_r = dev(np.stack([pi.q_r for pi in pinps]), dtype)
+    out = torch.empty((2, C, n_h, 128), dtype=torch.float32, device="cuda")
+    plen = torch.tensor(prefixes, dtype=torch.int32, device="cuda")
+    api.prefill_unabsorbed(d, q_c, q_r, cache, stride, plen, max(prefixes), dev(w_uk, dtype), dev(w_uv, dtype), out)
+    got = out.cpu().numpy()
+    for b, pi in enumerate(pinps):
+        ref = O.prefill(f64(pi.q_c, dtype), f64(pi.q_r, dtype), pi.prefix, f64(pi.c_kv, dtype),
+                        f64(pi.k_raw, dtype), f64(w_uk, dtype), f64(w_uv, dtype), pi.w.rope_base,
+                        store=dtype)
+        assert np.all(np.isfinite(got[b]))
+        assert rel_err(got[b], ref) < TOL["bf16"]
