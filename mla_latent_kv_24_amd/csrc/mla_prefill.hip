@@ -48,7 +48,9 @@ __device__ __forceinline__ void pf_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\
 constexpr int XB_ROWS = 128;  // rows per expansion workgroup
 constexpr int XB_HEADS = 8;   // heads per expansion workgroup
 constexpr int XPF = 8;        // expansion: W operand prefetch depth (k-steps)
-constexpr int PQ = 256;       // queries per attention workgroup (4 waves x 2 blocks of 32)
+constexpr int PF_WAVES = 8;   // attention waves per workgroup (two per SIMD)
+constexpr int PF_QBW = 1;     // query blocks of 32 per attention wave
+constexpr int PQ = 32 * PF_QBW * PF_WAVES;  // queries per attention workgroup (256)
 static_assert(XB_ROWS == XROWS_ALIGN, "expanded rows come in whole expansion blocks");
 
 // ------------------------------------------------------------------------
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
 // the workgroup streams up to its last query's keys.
 // ------------------------------------------------------------------------
 template <bool PRECISE>
-__global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillArgs a) {
   constexpr int NBUF = 4;
   constexpr int LOADS = TILE_BYTES / (16 * 256);  // 9 DMA chunks per thread per tile
   constexpr int T_OFF = NBUF * TILE_BYTES;        // per-thread DMA source chunk indices, u16 [LOADS][256]
@@ -199,8 +201,9 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   const int q0 = qb * PQ;
   const int64_t kend = prefix + min(q0 + PQ, a.chunk);  // keys of the workgroup: [0, kend)
   const int64_t ntiles = (kend + TILE - 1) / TILE;
-  const int qw = q0 + 64 * w;                           // this wave's first query
-  const int64_t my_tiles = (qw < a.chunk) ? (prefix + min(qw + 64, a.chunk) + TILE - 1) / TILE : 0;
+  const int qw = q0 + 32 * PF_QBW * w;                  // this wave's first query
+  const int64_t my_tiles = (qw < a.chunk) ? (prefix + min(qw + 32 * PF_QBW, a.chunk) + TILE - 1) / TILE : 0;
+  const bool dma_wave = w < 4;                          // waves 0..3 move the tiles
   // both instances are launched over the same grid; each workgroup runs in
   // the one that matches its first query's key count (uniform)
   if ((prefix + q0 + 1 < a.precise_below) != PRECISE) return;
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
       dma16(dst + 4096u * i, off, rs, 0);
     }
   };
-  {
+  if (dma_wave) {
     uint32_t ch[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -251,9 +254,9 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
 
   // ---- score B operands per query block k: q^C (8 k-steps), RoPE(q^R) hi and
   // lo (4 k-steps).  Lanes past the chunk take its last query (never stored).
-  u32x4 qc[2][8], qrh[2][4], qrl[2][PRECISE ? 4 : 1];
+  u32x4 qc[PF_QBW][8], qrh[PF_QBW][4], qrl[PF_QBW][PRECISE ? 4 : 1];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < PF_QBW; ++k) {
     const int q = min(qw + 32 * k + l32, a.chunk - 1);
     const int64_t nq = (static_cast<int64_t>(b) * a.chunk + q) * a.n_h + h;
     const uint16_t* qcp = static_cast<const uint16_t*>(a.q_c) + nq * D_H + 8 * g32;
@@ -292,14 +295,19 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
       for (int p = 0; p < 2; ++p) tr_off[r][p] = tile_off(4 * g32 + (j16 >> 2) + 8 * r, 32 * p + 16 * hf + 4 * (j16 & 3));
   }
 
-  f32x16 oacc[2][4];  // O^T of query block k, dims 32 db .. +31
+  f32x16 oacc[PF_QBW][4];  // O^T of query block k, dims 32 db .. +31
 #pragma unroll
-  for (int k = 0; k < 2; ++k)
+  for (int k = 0; k < PF_QBW; ++k)
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[k][db][r] = 0.f;
-  float m_run[2] = {NEG_INF, NEG_INF}, l_run[2] = {0.f, 0.f};
+  float m_run[PF_QBW], l_run[PF_QBW];
+#pragma unroll
+  for (int k = 0; k < PF_QBW; ++k) {
+    m_run[k] = NEG_INF;
+    l_run[k] = 0.f;
+  }
   const float qscale = a.qscale;
 
   // One tile for this wave's two query blocks; PRECISE adds the lo products.
@@ -314,12 +322,12 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
     };
     // ---- score: elements 0..127 (k^C hi: k-steps 0..7), 256..383 (k^C lo:
     // 16..23), 512..575 (k^R: 32..35)
-    f32x16 sacc[2];
+    f32x16 sacc[PF_QBW];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const bf16x8 kv = kread(s);
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < PF_QBW; ++k) {
         if (s == 0)
           pf_mfma0(sacc[k], kv, qc[k][0]);
         else
@@ -328,23 +336,23 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
       if constexpr (PRECISE) {
         const bf16x8 kl = kread(16 + s);
 #pragma unroll
-        for (int k = 0; k < 2; ++k) pf_mfma_qa(sacc[k], kl, qc[k][s]);
+        for (int k = 0; k < PF_QBW; ++k) pf_mfma_qa(sacc[k], kl, qc[k][s]);
       }
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 kv = kread(32 + s);
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < PF_QBW; ++k) {
         pf_mfma_qa(sacc[k], kv, qrh[k][s]);
         if constexpr (PRECISE) pf_mfma_qa(sacc[k], kv, qrl[k][s]);
       }
     }
     pf_drain();
     // ---- causal mask, online softmax (log2, lazy rescale) and P^T
-    bf16x8 ph[2][2], pl[2][PRECISE ? 2 : 1];
+    bf16x8 ph[PF_QBW][2], pl[PF_QBW][PRECISE ? 2 : 1];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < PF_QBW; ++k) {
       f32x16& x = sacc[k];
       // positions fit in 32 bits (prefix + chunk <= max_len < 2^31)
       const int pos = prefix32 + min(qw + 32 * k + l32, a.chunk - 1);
@@ -387,14 +395,14 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
       for (int u = 0; u < 2; ++u) {
         const bf16x8 vh = vread(4 + db, u);
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < PF_QBW; ++k) {
           pf_mfma_vv(oacc[k][db], vh, ph[k][u]);
           if constexpr (PRECISE) pf_mfma_vv(oacc[k][db], vh, pl[k][u]);
         }
         if constexpr (PRECISE) {
           const bf16x8 vl = vread(12 + db, u);
 #pragma unroll
-          for (int k = 0; k < 2; ++k) pf_mfma_vv(oacc[k][db], vl, ph[k][u]);
+          for (int k = 0; k < PF_QBW; ++k) pf_mfma_vv(oacc[k][db], vl, ph[k][u]);
         }
       }
   };
@@ -410,7 +418,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
     __syncthreads();
     // every wave passed this barrier, so buffer (it+3)&3 == (it-1)&3 is free:
     // its refill starts before this tile's products
-    if (it + 3 < ntiles) {
+    if (dma_wave && it + 3 < ntiles) {
       uint32_t ch[LOADS];
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) ch[i] = otab[i * 256 + tid];
@@ -426,7 +434,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   // of query qw + 32 k + l32
   if (qw < a.chunk) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < PF_QBW; ++k) {
       const int q = qw + 32 * k + l32;
       const float lt = pair_sum32(l_run[k]);
       const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
@@ -452,10 +460,10 @@ hipError_t launch_prefill_unabsorbed(const ExpandArgs& e, const PrefillArgs& p, 
   const hipError_t r = hipGetLastError();
   if (r != hipSuccess) return r;
   const dim3 g2((p.chunk + PQ - 1) / PQ, p.n_h, p.batch);
-  prefill_attn_kernel<true><<<g2, 256, 0, st>>>(p);
+  prefill_attn_kernel<true><<<g2, 64 * PF_WAVES, 0, st>>>(p);
   const hipError_t r2 = hipGetLastError();
   if (r2 != hipSuccess) return r2;
-  prefill_attn_kernel<false><<<g2, 256, 0, st>>>(p);
+  prefill_attn_kernel<false><<<g2, 64 * PF_WAVES, 0, st>>>(p);
   return hipGetLastError();
 }
 
