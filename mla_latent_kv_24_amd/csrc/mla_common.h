@@ -99,6 +99,7 @@ struct ExpandArgs {
   int64_t stride;               // cache rows per sequence slot
   int64_t rows_cap;             // expanded rows per (sequence, head)
   int32_t batch, n_h, chunk, max_len;  // max_len: host bound on prefix + chunk
+  int32_t lo_rows;              // lo parts are written for rows below this only
 };
 struct PrefillArgs {
   const void* q_c;              // [batch][chunk][n_h][d_h] bf16

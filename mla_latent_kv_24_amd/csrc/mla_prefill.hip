@@ -145,7 +145,9 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
       }
     }
     // lane l holds dims 8 jq + 4 g + (0..3) of block (db) for row 32 rb + l32:
-    // hi at element d, lo at element 256 + d of the expanded row
+    // hi at element d, lo at element 256 + d of the expanded row.  Only the
+    // hi + lo attention workgroups read lo, and their keys all lie below
+    // lo_rows; past it the lo parts are left unwritten.
     uint16_t* xh = static_cast<uint16_t*>(a.x) + (static_cast<int64_t>(b) * a.n_h + h) * a.rows_cap * ROWE;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
           const uint32_t l01 = pack_bf16x2(x0 - __uint_as_float(h01 << 16), x1 - __uint_as_float(h01 & 0xffff0000u));
           const uint32_t l23 = pack_bf16x2(x2 - __uint_as_float(h23 << 16), x3 - __uint_as_float(h23 & 0xffff0000u));
           *reinterpret_cast<uint2*>(xr + d) = make_uint2(h01, h23);
-          *reinterpret_cast<uint2*>(xr + 2 * D_H + d) = make_uint2(l01, l23);
+          if (row0 + r < a.lo_rows) *reinterpret_cast<uint2*>(xr + 2 * D_H + d) = make_uint2(l01, l23);
         }
     }
   }
@@ -453,8 +455,12 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
   }
 }
 
-hipError_t launch_prefill_unabsorbed(const ExpandArgs& e, const PrefillArgs& p, hipStream_t st) {
+hipError_t launch_prefill_unabsorbed(const ExpandArgs& e_in, const PrefillArgs& p, hipStream_t st) {
   if (p.chunk <= 0 || p.batch <= 0) return hipSuccess;
+  ExpandArgs e = e_in;
+  // a hi + lo workgroup's first query sees < precise_below keys, so all its
+  // keys lie below precise_below + PQ - 1
+  e.lo_rows = p.precise_below + PQ;
   const dim3 g1(static_cast<unsigned>(e.rows_cap / XB_ROWS), e.n_h / XB_HEADS, e.batch);
   expand_kv_kernel<<<g1, 256, 0, st>>>(e);
   const hipError_t r = hipGetLastError();
