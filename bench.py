@@ -80,6 +80,55 @@ def cpu_baseline(inp, budget_s=12.0):
                       f"unabsorbed fp64 numpy, {dt:.1f} s"}
 
 
+def bench_prefill(args):
+    """A6 on the v2_prefill workload: one 4,096-query chunk after a 4,096-row
+    prefix, 128 heads.  Times mla_prefill (absorbed queries in; A2 is not
+    timed) and mla_prefill_unabsorbed (raw queries in), each over K calls
+    after W, and reports FLOP rates against the absorbed form's count
+    (pairs x n_h x 2,176) and the unabsorbed form's own (pairs x n_h x 640
+    plus the expansion's rows x n_h x 2 x 2 x 128 x 512)."""
+    import torch
+    from mla_latent_kv_24_amd import workloads as W
+    from mla_latent_kv_24_amd.pipeline import PrefillState
+    w = W.WORKLOADS["v2_prefill"]
+    log(f"[bench] generating {w.name} ...")
+    st = PrefillState(W.make_prefill_inputs(w))
+    st.append_all()
+    st.absorb()
+    torch.cuda.synchronize()
+    steps, warm = max(1, min(args.steps, 20)), max(1, min(args.warmup, 3))
+    res = {}
+    for name, fn in (("absorbed", st.attend), ("unabsorbed", st.attend_unabsorbed)):
+        t = time.perf_counter()
+        while (time.perf_counter() - t) * 1e3 < min(args.settle_ms, 1500.0):
+            fn()
+            torch.cuda.synchronize()
+        for _ in range(warm):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    pairs = sum(st.prefix + i + 1 for i in range(st.chunk))
+    flop_abs = pairs * w.n_h * 2176
+    rows = st.prefix + st.chunk
+    flop_unabs = pairs * w.n_h * 640 + rows * w.n_h * 4 * 128 * 512
+    line = {"metric": "MLA causal prefill time (v2_prefill: 4,096 queries after a 4,096-row prefix, 128 heads)",
+            "unit": "ms", "higher_is_better": False, "steps": steps, "warmup": warm, "dtype": "bf16",
+            "data": "synthetic", "pairs": pairs,
+            "absorbed_ms": round(res["absorbed"], 3),
+            "absorbed_tflops": round(flop_abs / (res["absorbed"] * 1e-3) / 1e12, 1),
+            "unabsorbed_ms": round(res["unabsorbed"], 3),
+            "unabsorbed_tflops_own_count": round(flop_unabs / (res["unabsorbed"] * 1e-3) / 1e12, 1),
+            "unabsorbed_tflops_absorbed_count": round(flop_abs / (res["unabsorbed"] * 1e-3) / 1e12, 1),
+            "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -92,6 +141,9 @@ def main():
                          "management reaches its sustained state (0 to skip)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (rocprofv3 --pmc calibration)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="instead of the decode step, time the causal prefill of the v2_prefill "
+                         "workload in both forms (absorbed, unabsorbed); one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -104,6 +156,8 @@ def main():
     from mla_latent_kv_24_amd.pipeline import DecodeState
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.prefill:
+        return bench_prefill(args)
     w = W.WORKLOADS[args.workload]
     log(f"[bench] generating {w.name} ...")
     inp = W.make_decode_inputs(w)
