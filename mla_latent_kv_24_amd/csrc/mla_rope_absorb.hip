@@ -81,22 +81,27 @@ __global__ __launch_bounds__(256) void absorb_generic_kernel(AbsorbArgs a) {
 // ---------------------------------------------- A2, bf16 MFMA path (fused)
 // Per head i: q_lat[n, i, 0:512] = q_c[n, i, :] @ w_uk[i]  ([n x 128] @ [128 x 512])
 // and q_lat[n, i, 512:] = RoPE(q_r[n, i], q_pos[n]), in one launch.
-// Grid (head, column half, query chunk of 256).  The workgroup issues the loads
-// of its [128 d][256 c] slab of W^UK, of its first query block and of its half
-// of the head's RoPE pairs, stages the slab in LDS (row stride 576 B keeps the
-// four rows of a transpose read in distinct banks), rotates its RoPE pairs,
+// Grid (head, column quarter, query chunk of 256), two workgroups per CU so
+// that one's loads overlap the other's products and stores.  The workgroup
+// issues the loads of its [128 d][128 c] slab of W^UK, of its first query
+// block and of its quarter of the head's RoPE pairs, stages the slab in LDS
+// (a row stride of 64 B past a multiple of 128 B keeps the four rows of a
+// transpose read in distinct banks), rotates its RoPE pairs,
 // and runs 32-query blocks through v_mfma_f32_32x32x16_bf16: A = q_c rows from
 // global memory (d contiguous), B = W^UK columns via ds_read_b64_tr_b16.
 // Results are staged in LDS so the hi/lo bf16 pairs leave as 16-byte stores.
 constexpr int ABS_QCHUNK = 256;
-constexpr int ABS_WSTRIDE = 576;         // bytes per staged W row (256 bf16 + 64 B pad)
-constexpr int ABS_SSTRIDE = 256 * 4 + 16;  // bytes per staged fp32 output row
+constexpr int ABS_COLS = 128;                      // latent columns per workgroup (a quarter of d_c)
+constexpr int ABS_PARTS = D_C / ABS_COLS;          // workgroups per head
+constexpr int ABS_WSTRIDE = ABS_COLS * 2 + 64;     // bytes per staged W row (bf16 + 64 B pad)
+constexpr int ABS_SSTRIDE = ABS_COLS * 4 + 16;     // bytes per staged fp32 output row
+constexpr int ABS_PAIRS = D_R / 2 / ABS_PARTS;     // RoPE pairs rotated per workgroup
 
 __device__ __forceinline__ uint32_t bf16_pair(float lo_elem, float hi_elem) {
   return static_cast<uint32_t>(f32_to_bf16(lo_elem)) | (static_cast<uint32_t>(f32_to_bf16(hi_elem)) << 16);
 }
 
-__global__ __launch_bounds__(256, 1) void absorb_mfma_kernel(AbsorbArgs a) {
+__global__ __launch_bounds__(256, 2) void absorb_mfma_kernel(AbsorbArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t wlds[D_H * ABS_WSTRIDE];
   __shared__ __attribute__((aligned(16))) uint8_t stage[32 * ABS_SSTRIDE];
   const int h = blockIdx.x, half_c = blockIdx.y;
@@ -109,11 +114,13 @@ __global__ __launch_bounds__(256, 1) void absorb_mfma_kernel(AbsorbArgs a) {
   const int64_t rec = 2 * ROWE;  // bf16 elements per (query, head) record: hi row, lo row
 
   // ---- issue: W^UK slab (16 chunks of 16 B per thread) and the first query block
-  const uint16_t* wsrc = static_cast<const uint16_t*>(a.w_uk) + static_cast<int64_t>(h) * D_H * D_C + half_c * 256;
-  uint4 wv[16];
+  constexpr int WCH = ABS_COLS / 8;             // 16-B chunks per W row of the slab
+  constexpr int WLOADS = D_H * WCH / 256;         // chunks per thread
+  const uint16_t* wsrc = static_cast<const uint16_t*>(a.w_uk) + static_cast<int64_t>(h) * D_H * D_C + half_c * ABS_COLS;
+  uint4 wv[WLOADS];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int f = tid + 256 * i, d = f >> 5, k = f & 31;
+  for (int i = 0; i < WLOADS; ++i) {
+    const int f = tid + 256 * i, d = f / WCH, k = f % WCH;
     wv[i] = *reinterpret_cast<const uint4*>(wsrc + static_cast<int64_t>(d) * D_C + 8 * k);
   }
   auto load_q = [&](int n0, uint4 (&qa)[8]) {
@@ -126,15 +133,15 @@ __global__ __launch_bounds__(256, 1) void absorb_mfma_kernel(AbsorbArgs a) {
   uint4 qa[8];
   load_q(n_begin, qa);
 
-  // RoPE inputs of this workgroup's share of the pairs: column-half hc rotates
-  // pairs 16 hc .. 16 hc + 15 of its head for every query of the chunk
-  constexpr int RITEMS = ABS_QCHUNK * (D_R / 4) / 256;  // (query, pair) items per thread
+  // RoPE inputs of this workgroup's share of the pairs: column part pc rotates
+  // pairs ABS_PAIRS pc .. +ABS_PAIRS-1 of its head for every query of the chunk
+  constexpr int RITEMS = ABS_QCHUNK * ABS_PAIRS / 256;  // (query, pair) items per thread
   const uint16_t* qr = static_cast<const uint16_t*>(a.q_r);
   uint32_t xr[RITEMS];
   int32_t rpos[RITEMS];
 #pragma unroll
   for (int it = 0; it < RITEMS; ++it) {
-    const int idx = tid + 256 * it, n = n_begin + (idx >> 4), k = 16 * half_c + (idx & 15);
+    const int idx = tid + 256 * it, n = n_begin + idx / ABS_PAIRS, k = ABS_PAIRS * half_c + idx % ABS_PAIRS;
     xr[it] = 0u;
     rpos[it] = 0;
     if (n < n_end) {
@@ -145,15 +152,15 @@ __global__ __launch_bounds__(256, 1) void absorb_mfma_kernel(AbsorbArgs a) {
 
   // the slab into LDS (its registers are free before the fp64 RoPE math)
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int f = tid + 256 * i, d = f >> 5, k = f & 31;
+  for (int i = 0; i < WLOADS; ++i) {
+    const int f = tid + 256 * i, d = f / WCH, k = f % WCH;
     *reinterpret_cast<uint4*>(wlds + d * ABS_WSTRIDE + 16 * k) = wv[i];
   }
 
   // angle and sine/cosine in fp64, rotation in fp32
 #pragma unroll
   for (int it = 0; it < RITEMS; ++it) {
-    const int idx = tid + 256 * it, n = n_begin + (idx >> 4), k = 16 * half_c + (idx & 15);
+    const int idx = tid + 256 * it, n = n_begin + idx / ABS_PAIRS, k = ABS_PAIRS * half_c + idx % ABS_PAIRS;
     if (n < n_end) {
       double sd, cd;
       sincos(static_cast<double>(rpos[it]) * a.rope.theta[k], &sd, &cd);
@@ -178,8 +185,8 @@ __global__ __launch_bounds__(256, 1) void absorb_mfma_kernel(AbsorbArgs a) {
     uint4 qn[8];
     if (n0 + 32 < n_end) load_q(n0 + 32, qn);  // next block in flight during this one
 #pragma unroll
-    for (int cbl = 0; cbl < 2; ++cbl) {
-      const int cb = 2 * w + cbl;  // 32-column block inside this half
+    for (int cbl = 0; cbl < ABS_COLS / 128; ++cbl) {
+      const int cb = (ABS_COLS / 128) * w + cbl;  // 32-column block inside this part
       f32x16 acc = {0};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
@@ -197,10 +204,10 @@ __global__ __launch_bounds__(256, 1) void absorb_mfma_kernel(AbsorbArgs a) {
         *reinterpret_cast<float*>(stage + (8 * (j >> 2) + 4 * g + (j & 3)) * ABS_SSTRIDE + 4 * (32 * cb + (l & 31))) = acc[j];
     }
     __syncthreads();
-    // 32 rows x 32 runs of 8 columns: hi and lo as 16-byte stores
+    // 32 rows x (ABS_COLS / 8) runs of 8 columns: hi and lo as 16-byte stores
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = tid + 256 * it, r = idx >> 5, k = idx & 31;
+    for (int it = 0; it < 32 * (ABS_COLS / 8) / 256; ++it) {
+      const int idx = tid + 256 * it, r = idx / (ABS_COLS / 8), k = idx % (ABS_COLS / 8);
       const int n = n0 + r;
       if (n < n_end) {
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(stage + r * ABS_SSTRIDE + 32 * k);
@@ -214,7 +221,7 @@ __global__ __launch_bounds__(256, 1) void absorb_mfma_kernel(AbsorbArgs a) {
           const float h1 = bf16_to_f32(static_cast<uint16_t>(hw[e] >> 16));
           lw[e] = bf16_pair(v[2 * e] - h0, v[2 * e + 1] - h1);
         }
-        uint16_t* o = qout + (static_cast<int64_t>(n) * a.n_h + h) * rec + half_c * 256 + 8 * k;
+        uint16_t* o = qout + (static_cast<int64_t>(n) * a.n_h + h) * rec + half_c * ABS_COLS + 8 * k;
         *reinterpret_cast<uint4*>(o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         *reinterpret_cast<uint4*>(o + ROWE) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       }
@@ -253,7 +260,7 @@ bool absorb_fuses_rope(int bf16, int d_c, int d_h, int d_r) {
 hipError_t launch_absorb(const AbsorbArgs& a, int bf16, hipStream_t st) {
   if (a.n_q <= 0) return hipSuccess;
   if (absorb_fuses_rope(bf16, a.d_c, a.d_h, a.d_r)) {
-    dim3 grid(a.n_h, 2, (a.n_q + ABS_QCHUNK - 1) / ABS_QCHUNK);
+    dim3 grid(a.n_h, ABS_PARTS, (a.n_q + ABS_QCHUNK - 1) / ABS_QCHUNK);
     absorb_mfma_kernel<<<grid, 256, 0, st>>>(a);
   } else if (bf16) {
     absorb_generic_kernel<uint16_t><<<dim3(a.n_q, a.n_h), 256, 0, st>>>(a);
