@@ -144,6 +144,9 @@ def main():
     ap.add_argument("--prefill", action="store_true",
                     help="instead of the decode step, time the causal prefill of the v2_prefill "
                          "workload in both forms (absorbed, unabsorbed); one JSON line")
+    ap.add_argument("--page-rows", type=int, default=0,
+                    help="run the decode step over a paged cache of pages of this many rows, "
+                         "handed out in a seeded random order (0: contiguous sequence slots)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -161,10 +164,11 @@ def main():
     w = W.WORKLOADS[args.workload]
     log(f"[bench] generating {w.name} ...")
     inp = W.make_decode_inputs(w)
-    st = DecodeState(inp)
+    st = DecodeState(inp, page_rows=args.page_rows or None)
     torch.cuda.synchronize()
     tokens = int(inp.seq_lens.sum())
-    log(f"[bench] {w.name}: batch={w.batch} rows={tokens} n_h={w.n_h} splits={st.splits}")
+    layout = f"paged ({args.page_rows}-row pages)" if args.page_rows else "contiguous"
+    log(f"[bench] {w.name}: batch={w.batch} rows={tokens} n_h={w.n_h} splits={st.splits} cache={layout}")
 
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -241,7 +245,8 @@ def main():
     alg_flop = tokens * 2176 * n_h                                     # (2*576 + 2*512) per row per head
     achieved_gbs = alg_bytes / (attn_ms * 1e-3) / 1e9
     tflops = alg_flop / (attn_ms * 1e-3) / 1e12
-    traffic = pmc_traffic(tokens)
+    # the committed counter summary covers the contiguous kernel instance only
+    traffic = None if args.page_rows else pmc_traffic(tokens)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -256,7 +261,9 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) latent cache and RoPE keys; V2 query path from random hidden states)",
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "n_h": n_h, "d_c": 512,
-                   "d_hR": 64, "d_h": 128, "latent_rows": tokens, "splits": st.splits},
+                   "d_hR": 64, "d_h": 128, "latent_rows": tokens, "splits": st.splits,
+                   "cache_layout": "paged" if args.page_rows else "contiguous",
+                   **({"page_rows": args.page_rows} if args.page_rows else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "splitkv_wide_kernel",

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 3
+#define MLA_ABI_VERSION 4
 
 typedef enum {
   MLA_OK = 0,
@@ -199,6 +199,68 @@ mla_status mla_prefill_unabsorbed(const mla_dims* dims, mla_dtype dtype, int32_t
                                   const int32_t* prefix_lens, int32_t max_prefix_len,
                                   const void* w_uk, const void* w_uv, float* out,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Paged latent cache.  The pages serve the model through a dedicated vLLM
+ * stack (axforge.ai DeepSeek-Lite page, section 3); what such a server needs
+ * from the attention is a cache it can grow by fixed-size pages, so the
+ * entry points below run the same computation as their contiguous
+ * counterparts (review section 3) over this layout:
+ *   pool [num_pages][page_rows][d_c + d_hR] in the storage dtype; row r of
+ *   sequence b is row (r mod page_rows) of page block_table[b][r / page_rows];
+ *   block_table [batch][max_pages] int32 (device).
+ *   page_rows: a power of two in [32, 65536]; max_pages >= 1, num_pages >= 1.
+ * Rows are written with mla_append_kv, whose `row` argument is then the pool
+ * row page * page_rows + offset.  Only the table entries of pages that hold
+ * attended rows are read.  An entry outside [0, num_pages) is never
+ * dereferenced: its rows are not read, and the output of every query that
+ * attends one of them is NaN (in the unabsorbed prefill, other queries of the
+ * same sequence may be NaN too).
+ * The partial sums follow the same split plan as the contiguous entry point
+ * with the same batch and length bound, so a paged call returns bitwise the
+ * output of the contiguous call on the same rows. */
+typedef struct {
+  const void* pool;
+  const int32_t* block_table;
+  int64_t num_pages;
+  int32_t page_rows;
+  int32_t max_pages;
+} mla_paged_cache;
+
+/* mla_decode_partials over a paged cache (max_seq_len <= max_pages *
+ * page_rows); the split plan and the partials' layout are unchanged. */
+mla_status mla_decode_partials_paged(const mla_dims* dims, mla_dtype dtype, int32_t batch,
+                                     const void* q_lat, const mla_paged_cache* cache,
+                                     const int32_t* seq_lens, int32_t max_seq_len,
+                                     int32_t num_splits, float* z_part, float* lse_part,
+                                     void* stream);
+
+/* mla_decode over a paged cache.  max_seq_len <= max_pages * page_rows takes
+ * the place of cache_seq_stride; the workspace is mla_decode_workspace_bytes()
+ * for the same dims, dtype, batch and max_seq_len. */
+mla_status mla_decode_paged(const mla_dims* dims, mla_dtype dtype, int32_t batch,
+                            const void* q_lat, const mla_paged_cache* cache,
+                            const int32_t* seq_lens, int32_t max_seq_len,
+                            const void* w_uv, float* out, float* out_latent,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* mla_prefill over a paged cache (max_prefix_len + chunk <= max_pages *
+ * page_rows); the workspace is mla_prefill_workspace_bytes(). */
+mla_status mla_prefill_paged(const mla_dims* dims, mla_dtype dtype, int32_t batch,
+                             int32_t chunk, const void* q_lat,
+                             const mla_paged_cache* cache, const int32_t* prefix_lens,
+                             int32_t max_prefix_len, const void* w_uv, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* mla_prefill_unabsorbed over a paged cache (bf16, n_h a multiple of 8;
+ * max_prefix_len + chunk <= max_pages * page_rows); the workspace is
+ * mla_prefill_unabsorbed_workspace_bytes(). */
+mla_status mla_prefill_unabsorbed_paged(const mla_dims* dims, mla_dtype dtype, int32_t batch,
+                                        int32_t chunk, const void* q_c, const void* q_r,
+                                        const mla_paged_cache* cache,
+                                        const int32_t* prefix_lens, int32_t max_prefix_len,
+                                        const void* w_uk, const void* w_uv, float* out,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
 
 #ifdef __cplusplus
 }

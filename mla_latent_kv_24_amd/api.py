@@ -44,6 +44,15 @@ class MLAError(RuntimeError):
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _P = ctypes.POINTER(Dims)
+
+
+class PagedCache(ctypes.Structure):
+    """mla_paged_cache: pool [num_pages][page_rows][d_c + d_hR], block_table [batch][max_pages] int32."""
+    _fields_ = [("pool", _vp), ("block_table", _vp), ("num_pages", _i64), ("page_rows", _i32),
+                ("max_pages", _i32)]
+
+
+_PC = ctypes.POINTER(PagedCache)
 _SIGS = {
     "mla_abi_version": (_i32, []),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -64,6 +73,14 @@ _SIGS = {
                                               _vp, _vp, _vp, _vp, _sz, _vp]),
     "mla_prefill": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _i64, _vp, _i32, _vp, _vp,
                                    _vp, _sz, _vp]),
+    "mla_decode_partials_paged": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _PC, _vp, _i32, _i32, _vp, _vp,
+                                                 _vp]),
+    "mla_decode_paged": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _PC, _vp, _i32, _vp, _vp, _vp, _vp,
+                                        _sz, _vp]),
+    "mla_prefill_paged": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _PC, _vp, _i32, _vp, _vp, _vp,
+                                         _sz, _vp]),
+    "mla_prefill_unabsorbed_paged": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _PC, _vp, _i32,
+                                                    _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -218,3 +235,66 @@ def prefill_unabsorbed(d: Dims, q_c, q_r, cache, stride: int, prefix_lens, max_p
                                        _ptr(prefix_lens), max_prefix_len, _ptr(w_uk), _ptr(w_uv), _ptr(out),
                                        _ptr(workspace), workspace.numel(), _stream(cache.device)),
            "mla_prefill_unabsorbed")
+
+
+def paged_cache(pool, block_table) -> PagedCache:
+    """Descriptor of a paged latent cache: pool [num_pages, page_rows, d_c + d_hR] (storage dtype),
+    block_table [batch, max_pages] int32; row r of sequence b is pool[block_table[b, r // page_rows],
+    r % page_rows].  The tensors must outlive every call that uses the descriptor."""
+    assert pool.dim() == 3 and block_table.dim() == 2 and block_table.dtype == torch.int32
+    return PagedCache(_ptr(pool), _ptr(block_table), pool.shape[0], pool.shape[1], block_table.shape[1])
+
+
+def decode_partials_paged(d: Dims, q_lat, pool, block_table, seq_lens, max_seq_len: int, splits: int,
+                          z_part, lse_part) -> None:
+    """decode_partials() over a paged cache (see paged_cache)."""
+    assert seq_lens.dtype == torch.int32 and q_lat.dtype == pool.dtype
+    pc = paged_cache(pool, block_table)
+    _check(_lib.mla_decode_partials_paged(ctypes.byref(d), _dtype(pool), q_lat.shape[0], _ptr(q_lat),
+                                          ctypes.byref(pc), _ptr(seq_lens), max_seq_len, splits, _ptr(z_part),
+                                          _ptr(lse_part), _stream(pool.device)), "mla_decode_partials_paged")
+
+
+def decode_paged(d: Dims, q_lat, pool, block_table, seq_lens, max_seq_len: int, w_uv, out,
+                 out_latent=None, workspace=None) -> None:
+    """decode() over a paged cache (see paged_cache)."""
+    assert seq_lens.dtype == torch.int32 and q_lat.dtype == pool.dtype
+    dt = _dtype(pool)
+    need = decode_workspace_bytes(d, dt, q_lat.shape[0], max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=pool.device)
+    pc = paged_cache(pool, block_table)
+    _check(_lib.mla_decode_paged(ctypes.byref(d), dt, q_lat.shape[0], _ptr(q_lat), ctypes.byref(pc),
+                                 _ptr(seq_lens), max_seq_len, _ptr(w_uv), _ptr(out), _ptr(out_latent),
+                                 _ptr(workspace), workspace.numel(), _stream(pool.device)), "mla_decode_paged")
+
+
+def prefill_paged(d: Dims, q_lat, pool, block_table, prefix_lens, max_prefix_len: int, w_uv, out,
+                  workspace=None) -> None:
+    """prefill() over a paged cache (see paged_cache)."""
+    assert prefix_lens.dtype == torch.int32 and q_lat.dtype == pool.dtype
+    dt = _dtype(pool)
+    B, chunk = q_lat.shape[0], q_lat.shape[1]
+    need = prefill_workspace_bytes(d, dt, B, chunk, max_prefix_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=pool.device)
+    pc = paged_cache(pool, block_table)
+    _check(_lib.mla_prefill_paged(ctypes.byref(d), dt, B, chunk, _ptr(q_lat), ctypes.byref(pc),
+                                  _ptr(prefix_lens), max_prefix_len, _ptr(w_uv), _ptr(out),
+                                  _ptr(workspace), workspace.numel(), _stream(pool.device)), "mla_prefill_paged")
+
+
+def prefill_unabsorbed_paged(d: Dims, q_c, q_r, pool, block_table, prefix_lens, max_prefix_len: int, w_uk,
+                             w_uv, out, workspace=None) -> None:
+    """prefill_unabsorbed() over a paged cache (see paged_cache)."""
+    assert prefix_lens.dtype == torch.int32 and q_c.dtype == pool.dtype == q_r.dtype == w_uk.dtype
+    dt = _dtype(pool)
+    B, chunk = q_c.shape[0], q_c.shape[1]
+    need = prefill_unabsorbed_workspace_bytes(d, dt, B, chunk, max_prefix_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=pool.device)
+    pc = paged_cache(pool, block_table)
+    _check(_lib.mla_prefill_unabsorbed_paged(ctypes.byref(d), dt, B, chunk, _ptr(q_c), _ptr(q_r),
+                                             ctypes.byref(pc), _ptr(prefix_lens), max_prefix_len, _ptr(w_uk),
+                                             _ptr(w_uv), _ptr(out), _ptr(workspace), workspace.numel(),
+                                             _stream(pool.device)), "mla_prefill_unabsorbed_paged")

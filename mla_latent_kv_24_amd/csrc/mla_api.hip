@@ -91,6 +91,31 @@ int32_t plan_splits(const mla_dims* d, mla_dtype dt, int64_t n_q, int64_t max_le
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+int32_t page_shift_of(int32_t page_rows) {
+  int32_t k = 0;
+  while ((int64_t{1} << k) < page_rows) ++k;
+  return k;
+}
+
+// Paged-cache descriptor: pool and table present, page_rows a power of two in
+// [32, 65536], and room in the table for `max_len` rows.  Returns the row
+// capacity per sequence (the stride the kernels clamp lengths to).
+mla_status check_paged(const mla_paged_cache* c, int64_t max_len, int64_t& cap) {
+  if (!c) return fail(MLA_ERR_INVALID_ARGUMENT, "paged cache descriptor is NULL");
+  if (!c->pool || !c->block_table) return fail(MLA_ERR_INVALID_ARGUMENT, "paged cache: NULL pool or block_table");
+  if (c->page_rows < 32 || c->page_rows > 65536 || (c->page_rows & (c->page_rows - 1)))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "page_rows=%d must be a power of two in [32, 65536]", c->page_rows);
+  if (c->max_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "max_pages=%d < 1", c->max_pages);
+  if (c->num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages=%lld < 1", (long long)c->num_pages);
+  if (c->num_pages > (int64_t{1} << 31) - 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages=%lld exceeds the int32 page index", (long long)c->num_pages);
+  cap = static_cast<int64_t>(c->max_pages) * c->page_rows;
+  if (max_len > cap)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "attended length bound %lld > max_pages * page_rows = %lld",
+                (long long)max_len, (long long)cap);
+  return MLA_OK;
+}
+
 size_t partial_bytes(const mla_dims* d, int64_t n_q, int32_t S) {
   return align256(static_cast<size_t>(n_q) * S * d->n_h * d->d_c * sizeof(float)) +
          align256(static_cast<size_t>(n_q) * S * d->n_h * sizeof(float));
@@ -183,8 +208,15 @@ int64_t mla_split_rows(int32_t max_seq_len, int32_t num_splits) { return split_r
 static mla_status run_partials(const mla_dims* dims, mla_dtype dtype, int64_t n_q, const void* q_lat,
                                const void* cache, int64_t stride, const int32_t* lens, int32_t max_len,
                                int32_t q_per_seq, int prefill, int32_t num_splits, float* z_part,
-                               float* lse_part, hipStream_t s, const char* who) {
+                               float* lse_part, hipStream_t s, const char* who,
+                               const mla_paged_cache* paged = nullptr) {
   mla::SplitArgs a{};
+  if (paged) {
+    a.block_table = paged->block_table;
+    a.num_pages = paged->num_pages;
+    a.bt_stride = paged->max_pages;
+    a.page_shift = page_shift_of(paged->page_rows);
+  }
   a.q_lat = q_lat;
   a.cache = cache;
   a.lens = lens;
@@ -221,6 +253,23 @@ mla_status mla_decode_partials(const mla_dims* dims, mla_dtype dtype, int32_t ba
                       num_splits, z_part, lse_part, static_cast<hipStream_t>(stream), "mla_decode_partials");
 }
 
+mla_status mla_decode_partials_paged(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat,
+                                     const mla_paged_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
+                                     int32_t num_splits, float* z_part, float* lse_part, void* stream) {
+  mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  if (batch < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d < 1", batch);
+  if (max_seq_len < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "max_seq_len=%d < 1", max_seq_len);
+  int64_t cap = 0;
+  st = check_paged(cache, max_seq_len, cap);
+  if (st != MLA_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "num_splits=%d out of range [1,%d]", num_splits, kMaxSplits);
+  if (!q_lat || !seq_lens || !z_part || !lse_part) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  return run_partials(dims, dtype, batch, q_lat, cache->pool, cap, seq_lens, max_seq_len, 1, 0, num_splits, z_part,
+                      lse_part, static_cast<hipStream_t>(stream), "mla_decode_partials_paged", cache);
+}
+
 mla_status mla_combine_project(const mla_dims* dims, mla_dtype dtype, int32_t n_q, int32_t num_splits,
                                const float* z_part, const float* lse_part, const void* w_uv, float* out,
                                float* out_latent, void* stream) {
@@ -239,13 +288,19 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t
   return partial_bytes(dims, batch, plan_splits(dims, dtype, batch, max_seq_len));
 }
 
-mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat, const void* cache,
-                      int64_t cache_seq_stride, const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv,
-                      float* out, float* out_latent, void* workspace, size_t workspace_bytes, void* stream) {
+static mla_status decode_impl(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat,
+                              const void* cache, int64_t cache_seq_stride, const mla_paged_cache* paged,
+                              const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv, float* out,
+                              float* out_latent, void* workspace, size_t workspace_bytes, void* stream) {
   mla_status st = check_dims(dims, dtype);
   if (st != MLA_OK) return st;
   if (batch < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d < 1", batch);
   if (max_seq_len < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "max_seq_len=%d < 1", max_seq_len);
+  if (paged) {
+    st = check_paged(paged, max_seq_len, cache_seq_stride);
+    if (st != MLA_OK) return st;
+    cache = paged->pool;
+  }
   if (cache_seq_stride < max_seq_len)
     return fail(MLA_ERR_INVALID_ARGUMENT, "cache_seq_stride=%lld < max_seq_len=%d", (long long)cache_seq_stride, max_seq_len);
   if (!q_lat || !cache || !seq_lens || !w_uv || !out || !workspace)
@@ -259,10 +314,26 @@ mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch, cons
                                         align256(static_cast<size_t>(batch) * S * dims->n_h * dims->d_c * sizeof(float)));
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = run_partials(dims, dtype, batch, q_lat, cache, cache_seq_stride, seq_lens, max_seq_len, 1, 0, S, z, lse, s,
-                    "mla_decode (partials)");
+                    "mla_decode (partials)", paged);
   if (st != MLA_OK) return st;
   mla::CombineArgs a{z, lse, w_uv, out, out_latent, batch, dims->n_h, dims->d_c, dims->d_h, S};
   return hip_status(mla::launch_combine(a, dtype == MLA_BF16, s), "mla_decode (combine)");
+}
+
+mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat, const void* cache,
+                      int64_t cache_seq_stride, const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv,
+                      float* out, float* out_latent, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(dims, dtype, batch, q_lat, cache, cache_seq_stride, nullptr, seq_lens, max_seq_len, w_uv, out,
+                     out_latent, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_decode_paged(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat,
+                            const mla_paged_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
+                            const void* w_uv, float* out, float* out_latent, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!cache) return fail(MLA_ERR_INVALID_ARGUMENT, "paged cache descriptor is NULL");
+  return decode_impl(dims, dtype, batch, q_lat, nullptr, 0, cache, seq_lens, max_seq_len, w_uv, out, out_latent,
+                     workspace, workspace_bytes, stream);
 }
 
 size_t mla_prefill_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk,
@@ -273,15 +344,21 @@ size_t mla_prefill_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_
   return partial_bytes(dims, n_q, plan_splits(dims, dtype, n_q, max_len));
 }
 
-mla_status mla_prefill(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk, const void* q_lat,
-                       const void* cache, int64_t cache_seq_stride, const int32_t* prefix_lens,
-                       int32_t max_prefix_len, const void* w_uv, float* out, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+static mla_status prefill_impl(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk,
+                               const void* q_lat, const void* cache, int64_t cache_seq_stride,
+                               const mla_paged_cache* paged, const int32_t* prefix_lens, int32_t max_prefix_len,
+                               const void* w_uv, float* out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
   mla_status st = check_dims(dims, dtype);
   if (st != MLA_OK) return st;
   if (batch < 1 || chunk < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d, chunk=%d must be >= 1", batch, chunk);
   if (max_prefix_len < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "max_prefix_len=%d < 0", max_prefix_len);
   const int64_t max_len = static_cast<int64_t>(max_prefix_len) + chunk;
+  if (paged) {
+    st = check_paged(paged, max_len, cache_seq_stride);
+    if (st != MLA_OK) return st;
+    cache = paged->pool;
+  }
   if (max_len > cache_seq_stride)
     return fail(MLA_ERR_INVALID_ARGUMENT, "max_prefix_len + chunk = %lld > cache_seq_stride=%lld",
                 (long long)max_len, (long long)cache_seq_stride);
@@ -299,10 +376,26 @@ mla_status mla_prefill(const mla_dims* dims, mla_dtype dtype, int32_t batch, int
                                         align256(static_cast<size_t>(n_q) * S * dims->n_h * dims->d_c * sizeof(float)));
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = run_partials(dims, dtype, n_q, q_lat, cache, cache_seq_stride, prefix_lens, static_cast<int32_t>(max_len),
-                    chunk, 1, S, z, lse, s, "mla_prefill (partials)");
+                    chunk, 1, S, z, lse, s, "mla_prefill (partials)", paged);
   if (st != MLA_OK) return st;
   mla::CombineArgs a{z, lse, w_uv, out, nullptr, static_cast<int32_t>(n_q), dims->n_h, dims->d_c, dims->d_h, S};
   return hip_status(mla::launch_combine(a, dtype == MLA_BF16, s), "mla_prefill (combine)");
+}
+
+mla_status mla_prefill(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk, const void* q_lat,
+                       const void* cache, int64_t cache_seq_stride, const int32_t* prefix_lens,
+                       int32_t max_prefix_len, const void* w_uv, float* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return prefill_impl(dims, dtype, batch, chunk, q_lat, cache, cache_seq_stride, nullptr, prefix_lens, max_prefix_len,
+                      w_uv, out, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_prefill_paged(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk, const void* q_lat,
+                             const mla_paged_cache* cache, const int32_t* prefix_lens, int32_t max_prefix_len,
+                             const void* w_uv, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cache) return fail(MLA_ERR_INVALID_ARGUMENT, "paged cache descriptor is NULL");
+  return prefill_impl(dims, dtype, batch, chunk, q_lat, nullptr, 0, cache, prefix_lens, max_prefix_len, w_uv, out,
+                      workspace, workspace_bytes, stream);
 }
 
 
@@ -315,11 +408,12 @@ size_t mla_prefill_unabsorbed_workspace_bytes(const mla_dims* dims, mla_dtype dt
   return static_cast<size_t>(batch) * dims->n_h * rows_cap * mla::ROWB;
 }
 
-mla_status mla_prefill_unabsorbed(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk,
-                                  const void* q_c, const void* q_r, const void* cache, int64_t cache_seq_stride,
-                                  const int32_t* prefix_lens, int32_t max_prefix_len, const void* w_uk,
-                                  const void* w_uv, float* out, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+static mla_status prefill_unabsorbed_impl(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk,
+                                          const void* q_c, const void* q_r, const void* cache,
+                                          int64_t cache_seq_stride, const mla_paged_cache* paged,
+                                          const int32_t* prefix_lens, int32_t max_prefix_len, const void* w_uk,
+                                          const void* w_uv, float* out, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
   mla_status st = check_dims(dims, dtype);
   if (st != MLA_OK) return st;
   if (dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_unabsorbed: bf16 storage only");
@@ -328,6 +422,11 @@ mla_status mla_prefill_unabsorbed(const mla_dims* dims, mla_dtype dtype, int32_t
   if (batch > 65535) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d > 65535", batch);
   if (max_prefix_len < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "max_prefix_len=%d < 0", max_prefix_len);
   const int64_t max_len = static_cast<int64_t>(max_prefix_len) + chunk;
+  if (paged) {
+    st = check_paged(paged, max_len, cache_seq_stride);
+    if (st != MLA_OK) return st;
+    cache = paged->pool;
+  }
   if (max_len > cache_seq_stride)
     return fail(MLA_ERR_INVALID_ARGUMENT, "max_prefix_len + chunk = %lld > cache_seq_stride=%lld",
                 (long long)max_len, (long long)cache_seq_stride);
@@ -350,6 +449,12 @@ mla_status mla_prefill_unabsorbed(const mla_dims* dims, mla_dtype dtype, int32_t
   e.n_h = dims->n_h;
   e.chunk = chunk;
   e.max_len = static_cast<int32_t>(max_len);
+  if (paged) {
+    e.block_table = paged->block_table;
+    e.num_pages = paged->num_pages;
+    e.bt_stride = paged->max_pages;
+    e.page_shift = page_shift_of(paged->page_rows);
+  }
   mla::PrefillArgs p{};
   p.q_c = q_c;
   p.q_r = q_r;
@@ -365,5 +470,24 @@ mla_status mla_prefill_unabsorbed(const mla_dims* dims, mla_dtype dtype, int32_t
   p.qscale = static_cast<float>(scale_of(dims) * 1.4426950408889634);
   fill_rope(dims, p.rope);
   return hip_status(mla::launch_prefill_unabsorbed(e, p, static_cast<hipStream_t>(stream)), "mla_prefill_unabsorbed");
+}
+
+mla_status mla_prefill_unabsorbed(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk,
+                                  const void* q_c, const void* q_r, const void* cache, int64_t cache_seq_stride,
+                                  const int32_t* prefix_lens, int32_t max_prefix_len, const void* w_uk,
+                                  const void* w_uv, float* out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return prefill_unabsorbed_impl(dims, dtype, batch, chunk, q_c, q_r, cache, cache_seq_stride, nullptr, prefix_lens,
+                                 max_prefix_len, w_uk, w_uv, out, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_prefill_unabsorbed_paged(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk,
+                                        const void* q_c, const void* q_r, const mla_paged_cache* cache,
+                                        const int32_t* prefix_lens, int32_t max_prefix_len, const void* w_uk,
+                                        const void* w_uv, float* out, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  if (!cache) return fail(MLA_ERR_INVALID_ARGUMENT, "paged cache descriptor is NULL");
+  return prefill_unabsorbed_impl(dims, dtype, batch, chunk, q_c, q_r, nullptr, 0, cache, prefix_lens, max_prefix_len,
+                                 w_uk, w_uv, out, workspace, workspace_bytes, stream);
 }
 }  // extern "C"

@@ -74,6 +74,13 @@ struct SplitArgs {
   int32_t q_per_seq;      // 1 for decode, chunk for prefill
   int32_t prefill;        // 0 decode, 1 causal prefill
   float qscale;           // softmax_scale * log2(e)
+  // paged cache (block_table != NULL): `cache` is the page pool, row r of
+  // sequence b is row r & (2^page_shift - 1) of page block_table[b][r >> page_shift],
+  // and stride = bt_stride << page_shift bounds the attended length
+  const int32_t* block_table;  // [batch][bt_stride]
+  int64_t num_pages;
+  int32_t bt_stride;
+  int32_t page_shift;          // >= 5: a page holds whole 32-row tiles
 };
 
 struct CombineArgs {
@@ -100,6 +107,11 @@ struct ExpandArgs {
   int64_t rows_cap;             // expanded rows per (sequence, head)
   int32_t batch, n_h, chunk, max_len;  // max_len: host bound on prefix + chunk
   int32_t lo_rows;              // lo parts are written for rows below this only
+  // paged cache, as SplitArgs (block_table != NULL)
+  const int32_t* block_table;
+  int64_t num_pages;
+  int32_t bt_stride;
+  int32_t page_shift;
 };
 struct PrefillArgs {
   const void* q_c;              // [batch][chunk][n_h][d_h] bf16

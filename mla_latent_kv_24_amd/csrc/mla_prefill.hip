@@ -58,6 +58,7 @@ static_assert(XB_ROWS == XROWS_ALIGN, "expanded rows come in whole expansion blo
 // (256 dims) for all 128 rows: A = W rows (U^K or U^V, d_c contiguous, from
 // global), B = c^T (rows from LDS), 2 x 4 blocks of 32 x 32 accumulators.
 // ------------------------------------------------------------------------
+template <bool PAGED>
 __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[XB_ROWS * D_C * 2];  // c rows, 1024 B each
   const int tid = threadIdx.x, l = tid & 63;
@@ -71,24 +72,37 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
   L = min(L, a.stride);
   if (row0 >= L) return;  // uniform over the workgroup
   const int nrows = static_cast<int>(min(static_cast<int64_t>(XB_ROWS), L - row0));
-  const uint8_t* gsrc = static_cast<const uint8_t*>(a.cache) + (static_cast<int64_t>(b) * a.stride + row0) * ROWB;
+  auto row_at = [&](int64_t r, bool& ok) {
+    return cache_row_addr<PAGED>(a.cache, a.block_table, a.num_pages, a.bt_stride, a.page_shift, a.stride, b, r,
+                                 ROWB, ok);
+  };
 
   // ---- c rows -> LDS.  LDS chunk f = 256 i + tid is row 4 i + w, slot l, and
   // holds the row's global chunk l ^ (row & 7): the swizzle spreads the eight
-  // rows that one operand read touches over distinct banks.  Rows past the
-  // sequence arrive as zeros (the buffer resource spans the valid rows).
+  // rows that one operand read touches over distinct banks.  The block's rows
+  // come as four 32-row runs (one page each when paged), each through a buffer
+  // resource that spans the run's valid rows, so rows past the sequence (and
+  // the rows of a page outside the pool) arrive as zeros.  bad_runs marks the
+  // runs of such pages; their expanded rows are written as NaN.
+  uint32_t bad_runs = 0;  // uniform
   {
-    const uint64_t ga = reinterpret_cast<uint64_t>(gsrc);
-    const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(ga & 0xffffffffu)),
-                      __builtin_amdgcn_readfirstlane(static_cast<int>((ga >> 32) & 0xffffu)),
-                      __builtin_amdgcn_readfirstlane(nrows * ROWB), 0x00020000};
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
                               (__attribute__((address_space(3))) uint8_t*)smem)) +
                           1024u * static_cast<uint32_t>(w);
 #pragma unroll
-    for (int i = 0; i < XB_ROWS / 4; ++i) {
-      const int r = 4 * i + w;
-      dma16(lds0 + 4096u * i, r * ROWB + 16 * (l ^ (r & 7)), rs, 0);
+    for (int k = 0; k < XB_ROWS / 32; ++k) {
+      const int rows = max(min(nrows - 32 * k, 32), 0);
+      bool ok = true;
+      const uint64_t ga = rows > 0 ? row_at(row0 + 32 * k, ok) : reinterpret_cast<uint64_t>(a.cache);
+      if (!ok) bad_runs |= 1u << k;
+      const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(ga & 0xffffffffu)),
+                        __builtin_amdgcn_readfirstlane(static_cast<int>((ga >> 32) & 0xffffu)),
+                        __builtin_amdgcn_readfirstlane(ok ? rows * ROWB : 0), 0x00020000};
+#pragma unroll
+      for (int i = 8 * k; i < 8 * k + 8; ++i) {
+        const int r = 4 * i + w;  // row of the block; 32 k <= r < 32 k + 32
+        dma16(lds0 + 4096u * i, (r - 32 * k) * ROWB + 16 * (l ^ (r & 7)), rs, 0);
+      }
     }
   }
 
@@ -97,7 +111,10 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
   for (int idx = tid; idx < XB_ROWS * 8; idx += 256) {
     const int r = idx >> 3, c = idx & 7;
     if (r < nrows) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(gsrc + r * ROWB + 2 * D_C + 16 * c);
+      bool ok;
+      const uint64_t ga = row_at(row0 + r, ok);
+      const u32x4 nan8 = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+      const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(ga + 2 * D_C + 16 * c) : nan8;
 #pragma unroll
       for (int hh = 0; hh < XB_HEADS; ++hh)
         *reinterpret_cast<u32x4*>(xb + (hh * a.rows_cap + row0 + r) * ROWE + D_C + 8 * c) = v;
@@ -154,13 +171,16 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
       const int r = 32 * rb + l32;
       if (r >= nrows) continue;
       uint16_t* xr = xh + (row0 + r) * ROWE;
+      const bool pz = (bad_runs >> rb) & 1;  // row of a page outside the pool
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
           const int d = 64 * w + 32 * db + 8 * jq + 4 * g;
           const f32x16& v = acc[db][rb];
-          const float x0 = v[4 * jq], x1 = v[4 * jq + 1], x2 = v[4 * jq + 2], x3 = v[4 * jq + 3];
+          const float nan = __builtin_nanf("");
+          const float x0 = pz ? nan : v[4 * jq], x1 = pz ? nan : v[4 * jq + 1], x2 = pz ? nan : v[4 * jq + 2],
+                      x3 = pz ? nan : v[4 * jq + 3];
           const uint32_t h01 = pack_bf16x2(x0, x1), h23 = pack_bf16x2(x2, x3);
           const uint32_t l01 = pack_bf16x2(x0 - __uint_as_float(h01 << 16), x1 - __uint_as_float(h01 & 0xffff0000u));
           const uint32_t l23 = pack_bf16x2(x2 - __uint_as_float(h23 << 16), x3 - __uint_as_float(h23 & 0xffff0000u));
@@ -462,7 +482,10 @@ hipError_t launch_prefill_unabsorbed(const ExpandArgs& e_in, const PrefillArgs& 
   // keys lie below precise_below + PQ - 1
   e.lo_rows = p.precise_below + PQ;
   const dim3 g1(static_cast<unsigned>(e.rows_cap / XB_ROWS), e.n_h / XB_HEADS, e.batch);
-  expand_kv_kernel<<<g1, 256, 0, st>>>(e);
+  if (e.block_table)
+    expand_kv_kernel<true><<<g1, 256, 0, st>>>(e);
+  else
+    expand_kv_kernel<false><<<g1, 256, 0, st>>>(e);
   const hipError_t r = hipGetLastError();
   if (r != hipSuccess) return r;
   const dim3 g2((p.chunk + PQ - 1) / PQ, p.n_h, p.batch);

@@ -49,7 +49,17 @@ __device__ __forceinline__ void query_range(const SplitArgs& a, int n, int& b, i
   len = max(L, static_cast<int64_t>(0));
 }
 
-template <int CG>
+template <bool PAGED>
+__device__ __forceinline__ uint64_t row_addr(const SplitArgs& a, int b, int64_t r, int64_t row_bytes, bool& ok) {
+  return cache_row_addr<PAGED>(a.cache, a.block_table, a.num_pages, a.bt_stride, a.page_shift, a.stride, b, r,
+                               row_bytes, ok);
+}
+
+// A split whose rows include one of a bad page reports lse = +inf and z = NaN:
+// the combine then turns every output of the query into NaN.
+constexpr float POS_INF = __builtin_huge_valf();
+
+template <int CG, bool PAGED>
 __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
     SplitArgs a) {
   constexpr int HPW = 32;                        // heads per wave
@@ -108,9 +118,18 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
     const int t = f / 72, p = f - 72 * t;
     return 16 * (f - p + (p ^ swz(t)));
   };
+  bool bad = false;  // a tile of this split sits in a page outside the pool (uniform)
   auto tile_rsrc = [&](int64_t it) {
-    const uint64_t ga = gaddr + static_cast<uint64_t>(it) * TILE_BYTES;
-    const int64_t rows = min(static_cast<int64_t>(TILE), hi - lo - it * TILE);
+    uint64_t ga = gaddr + static_cast<uint64_t>(it) * TILE_BYTES;
+    int64_t rows = min(static_cast<int64_t>(TILE), hi - lo - it * TILE);
+    if constexpr (PAGED) {
+      bool ok = true;
+      if (rows > 0) ga = row_addr<true>(a, b, lo + it * TILE, ROWB, ok);
+      if (!ok) {
+        rows = 0;
+        bad = true;
+      }
+    }
     const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(ga & 0xffffffffu)),
                       __builtin_amdgcn_readfirstlane(static_cast<int>((ga >> 32) & 0xffffu)),
                       __builtin_amdgcn_readfirstlane(static_cast<int>(rows * ROWB)), 0x00020000};
@@ -290,8 +309,12 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
   // normalised Z is staged row-major in the (now idle) LDS ring so that the
   // global stores are contiguous 16-byte runs along each head's row.
   const float lt = pair_sum32(l_run);
-  const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-  const float lse = (lt > 0.f) ? (m_run + log2f(lt)) * LN2 : NEG_INF;
+  float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+  float lse = (lt > 0.f) ? (m_run + log2f(lt)) * LN2 : NEG_INF;
+  if (PAGED && bad) {
+    inv = __builtin_nanf("");
+    lse = POS_INF;
+  }
   if (cg == 0 && l < HPW) lse_o[h0 + l] = lse;
 
   constexpr int WH = NHG * HPW;                                        // heads of the query (= n_h)
@@ -350,6 +373,7 @@ __device__ __forceinline__ void mfma_v(f32x16& acc, const u32x4& a, const u32x4&
 // idle cycles cover the 32x32x16 latency with margin.
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
+template <bool PAGED>
 __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
   constexpr int NQ = 36;                           // score k-steps (576 / 16)
   constexpr int NBUF = 4;                          // LDS tile ring
@@ -395,9 +419,18 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
   // A tile's buffer resource: based at the tile, sized to its rows inside the
   // split (0 past the last tile: such loads only zero-fill a free buffer, which
   // keeps the issue pattern and the vmcnt bookkeeping uniform).
+  bool bad = false;  // a tile of this split sits in a page outside the pool (uniform)
   auto tile_rsrc = [&](int64_t it) {
-    const uint64_t ga = gaddr + static_cast<uint64_t>(it) * TILE_BYTES;
-    const int64_t rows = max(min(static_cast<int64_t>(TILE), hi - lo - it * TILE), static_cast<int64_t>(0));
+    uint64_t ga = gaddr + static_cast<uint64_t>(it) * TILE_BYTES;
+    int64_t rows = max(min(static_cast<int64_t>(TILE), hi - lo - it * TILE), static_cast<int64_t>(0));
+    if constexpr (PAGED) {
+      bool ok = true;
+      if (rows > 0) ga = row_addr<true>(a, b, lo + it * TILE, ROWB, ok);
+      if (!ok) {
+        rows = 0;
+        bad = true;
+      }
+    }
     const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(ga & 0xffffffffu)),
                       __builtin_amdgcn_readfirstlane(static_cast<int>((ga >> 32) & 0xffffu)),
                       __builtin_amdgcn_readfirstlane(static_cast<int>(rows * ROWB)), 0x00020000};
@@ -651,8 +684,13 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
   // issued past the last tile are drained before the workgroup may exit.
   vm_wait<0>();
   const float lt = pair_sum32(l_run);
-  const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-  if (l < 32) lse_o[32 * w + l] = (lt > 0.f) ? (m_run + log2f(lt)) * LN2 : NEG_INF;
+  float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+  float lse = (lt > 0.f) ? (m_run + log2f(lt)) * LN2 : NEG_INF;
+  if (PAGED && bad) {
+    inv = __builtin_nanf("");
+    lse = POS_INF;
+  }
+  if (l < 32) lse_o[32 * w + l] = lse;
   *reinterpret_cast<float*>(smem + I_OFF + 4 * (32 * w + l32)) = inv;
   __syncthreads();
 #pragma unroll
@@ -691,6 +729,7 @@ constexpr int T16_BYTES = T16 * ROWB;            // 18,432 B
 constexpr int T16_LOADS = T16_BYTES / (16 * 64);  // 18 DMA chunks per lane per tile
 constexpr int ZPAD = D_C * 4 + 16;               // merge: bytes per staged head row
 
+template <bool PAGED>
 __global__ __launch_bounds__(256, 1) void splitkv_h16_kernel(SplitArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[8 * T16_BYTES];
   static_assert(4 * 16 * ZPAD + 2 * 4 * 16 * 4 <= 8 * T16_BYTES, "merge staging must fit the buffers");
@@ -737,10 +776,19 @@ __global__ __launch_bounds__(256, 1) void splitkv_h16_kernel(SplitArgs a) {
   const uint64_t gaddr = reinterpret_cast<uint64_t>(gsplit);
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) uint8_t*)smem));
+  bool bad = false;  // one of this wave's tiles sits in a page outside the pool (wave-uniform)
   auto issue = [&](int k) {
     const int64_t it = w + 4 * static_cast<int64_t>(k);
-    const uint64_t ga = gaddr + static_cast<uint64_t>(it) * T16_BYTES;
-    const int64_t rows = min(static_cast<int64_t>(T16), hi - lo - it * T16);
+    uint64_t ga = gaddr + static_cast<uint64_t>(it) * T16_BYTES;
+    int64_t rows = min(static_cast<int64_t>(T16), hi - lo - it * T16);
+    if constexpr (PAGED) {
+      bool ok = true;
+      if (rows > 0) ga = row_addr<true>(a, b, lo + it * T16, ROWB, ok);
+      if (!ok) {
+        rows = 0;
+        bad = true;
+      }
+    }
     const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(ga & 0xffffffffu)),
                       __builtin_amdgcn_readfirstlane(static_cast<int>((ga >> 32) & 0xffffu)),
                       __builtin_amdgcn_readfirstlane(static_cast<int>(rows * ROWB)), 0x00020000};
@@ -862,6 +910,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_h16_kernel(SplitArgs a) {
   // z = sum_w 2^(m_w - M) Z_w / L.  A wave without tiles has m = -inf, l = 0.
   float lt = pair_sum32(l_run);
   lt = pair_sum16(lt);
+  if (PAGED && bad) lt = __builtin_nanf("");  // carried into L by the merge
   __syncthreads();  // every wave is done with its buffers
   float* mst = reinterpret_cast<float*>(smem + 4 * 16 * ZPAD);
   float* lst = mst + 64;
@@ -879,7 +928,12 @@ __global__ __launch_bounds__(256, 1) void splitkv_h16_kernel(SplitArgs a) {
     const float mv = mst[16 * v + j16];
     if (mv != NEG_INF) L += lst[16 * v + j16] * __builtin_amdgcn_exp2f(mv - M);
   }
-  const float f = (m_run != NEG_INF && L > 0.f) ? __builtin_amdgcn_exp2f(m_run - M) / L : 0.f;
+  float f = (m_run != NEG_INF && L > 0.f) ? __builtin_amdgcn_exp2f(m_run - M) / L : 0.f;
+  float lse = (L > 0.f) ? (M + log2f(L)) * LN2 : NEG_INF;
+  if (PAGED && L != L) {
+    f = __builtin_nanf("");
+    lse = POS_INF;
+  }
   {
     uint8_t* row = smem + w * 16 * ZPAD + j16 * ZPAD + 16 * q4;
 #pragma unroll
@@ -888,7 +942,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_h16_kernel(SplitArgs a) {
       *reinterpret_cast<f32x4*>(row + 64 * c) = v;
     }
   }
-  if (w == 0 && q4 == 0) lse_o[j16] = (L > 0.f) ? (M + log2f(L)) * LN2 : NEG_INF;
+  if (w == 0 && q4 == 0) lse_o[j16] = lse;
   __syncthreads();
   for (int idx = tid; idx < 16 * (D_C / 4); idx += 256) {
     const int h = idx >> 7, c4 = idx & 127;
@@ -918,7 +972,7 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
   return v;
 }
 
-template <typename T>
+template <typename T, bool PAGED>
 __global__ __launch_bounds__(256) void splitkv_generic_kernel(SplitArgs a) {
   __shared__ float q[D_C + 2 * MAX_PAIRS];
   __shared__ float pr[256];
@@ -940,15 +994,23 @@ __global__ __launch_bounds__(256) void splitkv_generic_kernel(SplitArgs a) {
   }
   for (int e = tid; e < row_e; e += 256) q[e] = load_q<T>(a.q_lat, static_cast<int64_t>(n) * a.n_h + h, row_e, e);
   __syncthreads();
-  const T* rows = static_cast<const T*>(a.cache) + static_cast<int64_t>(b) * a.stride * row_e;
+  // a row of a bad page reads as zeros (as in the MFMA kernels) and poisons the split
+  bool bad = false;
+  auto row_ptr = [&](int64_t r, bool& ok) {
+    return reinterpret_cast<const T*>(row_addr<PAGED>(a, b, r, static_cast<int64_t>(row_e) * sizeof(T), ok));
+  };
   float m = NEG_INF, lsum = 0.f, z0 = 0.f, z1 = 0.f;
   for (int64_t base = lo; base < hi; base += 256) {
     const int cnt = static_cast<int>(min(static_cast<int64_t>(256), hi - base));
     float s = NEG_INF;
     if (tid < cnt) {
-      const T* r = rows + (base + tid) * row_e;
+      bool ok;
+      const T* r = row_ptr(base + tid, ok);
       float acc = 0.f;
-      for (int e = 0; e < row_e; ++e) acc = fmaf(q[e], load_as_f32(r, e), acc);
+      if (ok)
+        for (int e = 0; e < row_e; ++e) acc = fmaf(q[e], load_as_f32(r, e), acc);
+      else
+        bad = true;
       s = acc * a.qscale;
     }
     const float mt = block_reduce(s, red, true);
@@ -963,39 +1025,54 @@ __global__ __launch_bounds__(256) void splitkv_generic_kernel(SplitArgs a) {
     m = m_new;
     for (int r = 0; r < cnt; ++r) {
       const float pv = pr[r];
-      const T* rr = rows + (base + r) * row_e;
+      bool ok;
+      const T* rr = row_ptr(base + r, ok);
+      if (!ok) continue;
       if (tid < a.d_c) z0 = fmaf(pv, load_as_f32(rr, tid), z0);
       if (tid + 256 < a.d_c) z1 = fmaf(pv, load_as_f32(rr, tid + 256), z1);
     }
     __syncthreads();
   }
-  const float inv = 1.f / lsum;
+  float inv = 1.f / lsum;
+  float lse = (m + log2f(lsum)) * LN2;
+  if (PAGED && __syncthreads_or(bad)) {
+    inv = __builtin_nanf("");
+    lse = POS_INF;
+  }
   if (tid < a.d_c) zo[tid] = z0 * inv;
   if (tid + 256 < a.d_c) zo[tid + 256] = z1 * inv;
-  if (tid == 0) *lse_o = (m + log2f(lsum)) * LN2;
+  if (tid == 0) *lse_o = lse;
 }
 
 bool splitkv_has_fast_path(int n_h, int bf16, int d_c, int d_r) {
   return bf16 && d_c == D_C && d_r == D_R && (n_h == 16 || n_h == 32 || n_h == 64 || n_h == 128);
 }
 
-hipError_t launch_splitkv(const SplitArgs& a, int bf16, hipStream_t st) {
-  if (a.n_q <= 0) return hipSuccess;
+template <bool PAGED>
+static void launch_splitkv_as(const SplitArgs& a, int bf16, hipStream_t st) {
   if (splitkv_has_fast_path(a.n_h, bf16, a.d_c, a.d_r)) {
     dim3 grid(a.n_q, a.num_splits);
     switch (a.n_h) {
-      case 16: splitkv_h16_kernel<<<grid, 256, 0, st>>>(a); break;
-      case 32: splitkv_mfma_kernel<4><<<grid, 256, 0, st>>>(a); break;
-      case 64: splitkv_mfma_kernel<2><<<grid, 256, 0, st>>>(a); break;
-      default: splitkv_wide_kernel<<<grid, 256, 0, st>>>(a); break;
+      case 16: splitkv_h16_kernel<PAGED><<<grid, 256, 0, st>>>(a); break;
+      case 32: splitkv_mfma_kernel<4, PAGED><<<grid, 256, 0, st>>>(a); break;
+      case 64: splitkv_mfma_kernel<2, PAGED><<<grid, 256, 0, st>>>(a); break;
+      default: splitkv_wide_kernel<PAGED><<<grid, 256, 0, st>>>(a); break;
     }
   } else {
     dim3 grid(a.n_q, a.num_splits, a.n_h);
     if (bf16)
-      splitkv_generic_kernel<uint16_t><<<grid, 256, 0, st>>>(a);
+      splitkv_generic_kernel<uint16_t, PAGED><<<grid, 256, 0, st>>>(a);
     else
-      splitkv_generic_kernel<float><<<grid, 256, 0, st>>>(a);
+      splitkv_generic_kernel<float, PAGED><<<grid, 256, 0, st>>>(a);
   }
+}
+
+hipError_t launch_splitkv(const SplitArgs& a, int bf16, hipStream_t st) {
+  if (a.n_q <= 0) return hipSuccess;
+  if (a.block_table)
+    launch_splitkv_as<true>(a, bf16, st);
+  else
+    launch_splitkv_as<false>(a, bf16, st);
   return hipGetLastError();
 }
 

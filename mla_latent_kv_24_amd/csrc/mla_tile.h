@@ -1,6 +1,7 @@
 // Device helpers shared by the attention kernels (internal): the LDS tile
-// geometry of 1152-B rows, the global -> LDS DMA, the LDS transpose read, and
-// the lane-pair reductions of the 32x32 MFMA layouts.
+// geometry of 1152-B rows, the global -> LDS DMA, the LDS transpose read, the
+// lane-pair reductions of the 32x32 MFMA layouts, and cache-row addressing
+// (contiguous or paged).
 #pragma once
 #include "mla_common.h"
 
@@ -73,5 +74,29 @@ __device__ __forceinline__ float pair_max32(float v) { float a, b; pair_vals<fal
 __device__ __forceinline__ float pair_max16(float v) { float a, b; pair_vals<true>(v, a, b); return fmaxf(a, b); }
 __device__ __forceinline__ float pair_sum32(float v) { float a, b; pair_vals<false>(v, a, b); return a + b; }
 __device__ __forceinline__ float pair_sum16(float v) { float a, b; pair_vals<true>(v, a, b); return a + b; }
+
+// Address of cache row r of sequence b.  Contiguous: slot b of `stride` rows.
+// Paged: row r & (2^page_shift - 1) of pool page block_table[b][r >> page_shift];
+// with pages of 32 rows or more, a run of rows that starts at a multiple of 16
+// and ends inside the same 32-row tile stays in one page.  The table is
+// read-only for the kernels, so an entry at a uniform index comes through a
+// scalar load.  An entry outside [0, num_pages) sets ok = false and yields the
+// pool base, which the caller must not read.
+template <bool PAGED>
+__device__ __forceinline__ uint64_t cache_row_addr(const void* cache, const int32_t* block_table, int64_t num_pages,
+                                                   int32_t bt_stride, int32_t page_shift, int64_t stride, int b,
+                                                   int64_t r, int64_t row_bytes, bool& ok) {
+  const uint64_t base = reinterpret_cast<uint64_t>(cache);
+  if constexpr (!PAGED) {
+    ok = true;
+    return base + static_cast<uint64_t>((static_cast<int64_t>(b) * stride + r) * row_bytes);
+  } else {
+    const auto* bt = (const __attribute__((address_space(4))) int32_t*)(block_table);
+    const int32_t pg = bt[static_cast<int64_t>(b) * bt_stride + (r >> page_shift)];
+    ok = pg >= 0 && pg < num_pages;
+    const int64_t prow = (static_cast<int64_t>(ok ? pg : 0) << page_shift) + (r & ((int64_t{1} << page_shift) - 1));
+    return base + static_cast<uint64_t>(prow * row_bytes);
+  }
+}
 
 }  // namespace mla

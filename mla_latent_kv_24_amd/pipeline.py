@@ -9,7 +9,7 @@ import numpy as np
 import torch
 
 from . import api
-from .workloads import D_C, D_R, ROW, DecodeInputs, PrefillInputs
+from .workloads import D_C, D_R, ROW, DecodeInputs, PrefillInputs, paged_block_table, paged_rows
 
 
 def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -29,9 +29,13 @@ class DecodeState:
 
     cache rows: sequence b owns rows [b*stride, (b+1)*stride); rows at and past
     len_b hold NaN so that any read past a length shows up in the output.
+    With page_rows set, the cache is a pool of pages of that many rows instead,
+    handed out by a seeded block table (workloads.paged_block_table); unused
+    pool rows hold NaN likewise.
     """
 
-    def __init__(self, inp: DecodeInputs, device="cuda", out_latent=False):
+    def __init__(self, inp: DecodeInputs, device="cuda", out_latent=False, page_rows=None,
+                 spare_pages=0, table_seed=0):
         w = inp.w
         self.inp = inp
         self.device = device
@@ -42,18 +46,27 @@ class DecodeState:
         lens = inp.seq_lens.astype(np.int64)
         self.max_len = int(lens.max())
         self.total_rows = int(lens.sum())
-        self.cache = torch.full((self.batch * self.stride, ROW), float("nan"), dtype=tdt, device=device)
+        self.page_rows = page_rows
+        if page_rows is None:
+            self.cache = torch.full((self.batch * self.stride, ROW), float("nan"), dtype=tdt, device=device)
+            self.block_table = None
+            row_of = lambda b, j: np.asarray(b, dtype=np.int64) * self.stride + np.asarray(j, dtype=np.int64)
+        else:
+            table, num_pages = paged_block_table(lens, page_rows, table_seed, spare_pages)
+            self.cache = torch.full((num_pages, page_rows, ROW), float("nan"), dtype=tdt, device=device)
+            self.block_table = torch.from_numpy(table).to(device)
+            row_of = lambda b, j: paged_rows(table, page_rows, b, j)
         self.seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(device)
         # fill: every valid row goes through A1 (RoPE of k_raw at its position)
         b_idx = np.repeat(np.arange(self.batch, dtype=np.int64), lens)
         j_idx = np.concatenate([np.arange(L, dtype=np.int64) for L in lens])
-        self.fill_rows = torch.from_numpy(b_idx * self.stride + j_idx).to(device)
+        self.fill_rows = torch.from_numpy(row_of(b_idx, j_idx)).to(device)
         self.fill_pos = torch.from_numpy(j_idx.astype(np.int32)).to(device)
         self.fill_c = to_device(inp.c_kv[b_idx, j_idx], w.dtype, device)
         self.fill_k = to_device(inp.k_raw[b_idx, j_idx], w.dtype, device)
         # the step's new token of each sequence = its last row
         last = lens - 1
-        self.new_rows = torch.from_numpy(np.arange(self.batch) * self.stride + last).to(device)
+        self.new_rows = torch.from_numpy(row_of(np.arange(self.batch), last)).to(device)
         self.new_pos = torch.from_numpy(last.astype(np.int32)).to(device)
         self.new_c = to_device(inp.c_kv[np.arange(self.batch), last], w.dtype, device)
         self.new_k = to_device(inp.k_raw[np.arange(self.batch), last], w.dtype, device)
@@ -88,8 +101,12 @@ class DecodeState:
         S = self.splits if splits is None else splits
         z = self.z_part if z_part is None else z_part
         lse = self.lse_part if lse_part is None else lse_part
-        api.decode_partials(self.d, self.q_lat, self.cache, self.stride, self.seq_lens, self.max_len,
-                            S, z, lse)
+        if self.block_table is None:
+            api.decode_partials(self.d, self.q_lat, self.cache, self.stride, self.seq_lens, self.max_len,
+                                S, z, lse)
+        else:
+            api.decode_partials_paged(self.d, self.q_lat, self.cache, self.block_table, self.seq_lens,
+                                      self.max_len, S, z, lse)
         return z, lse
 
     def combine(self, z=None, lse=None):

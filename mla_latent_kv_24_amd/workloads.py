@@ -288,3 +288,32 @@ def random_storage(seed, shape, dtype: str, std: float = 1.0) -> np.ndarray:
 def random_ints(seed, low: int, high: int, shape) -> np.ndarray:
     """Seeded integers in [low, high) (positions, lengths, row indices of test inputs)."""
     return np.random.default_rng(seed).integers(low, high, shape)
+
+
+def paged_block_table(lens, page_rows: int, seed: int = 0, spare_pages: int = 0):
+    """Block table of a paged cache for sequences of the given lengths.
+
+    Sequence b needs ceil(len_b / page_rows) pages; all pages of the batch
+    (plus `spare_pages` that no sequence uses) are handed out in a seeded
+    random order, so a sequence's consecutive pages sit far apart in the pool,
+    as in a server whose pages were freed and reused.  Returns
+    (table [B, max_pages] int32, num_pages); entries past a sequence's pages
+    are -1 (never read for lengths within the table)."""
+    lens = np.asarray(lens, dtype=np.int64)
+    need = (lens + page_rows - 1) // page_rows
+    max_pages = max(int(need.max()), 1)
+    num_pages = int(need.sum()) + int(spare_pages)
+    order = np.random.default_rng(seed).permutation(num_pages).astype(np.int32)
+    table = np.full((len(lens), max_pages), -1, dtype=np.int32)
+    k = 0
+    for b, n in enumerate(need):
+        table[b, :n] = order[k:k + n]
+        k += int(n)
+    return table, num_pages
+
+
+def paged_rows(table: np.ndarray, page_rows: int, b_idx, j_idx) -> np.ndarray:
+    """Pool row of logical row j of sequence b under `table` (int64)."""
+    b_idx = np.asarray(b_idx, dtype=np.int64)
+    j_idx = np.asarray(j_idx, dtype=np.int64)
+    return table[b_idx, j_idx // page_rows].astype(np.int64) * page_rows + j_idx % page_rows

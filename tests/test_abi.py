@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -21,7 +22,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = api.raw()
     names = declared_functions()
-    assert len(names) >= 13
+    assert len(names) >= 17
     for n in names:
         assert hasattr(lib, n), n
 
@@ -105,3 +106,50 @@ def test_split_plan_covers_every_row():
     for B, L in ((1, 100), (3, 5000), (64, 8192), (128, 32768), (4, 131072), (4096, 8192)):
         S = api.num_splits(d, api.BF16, B, L)
         assert api.split_rows(L, S) <= 4096 or B >= 1024
+
+
+def test_paged_validation():
+    """Paged entry points reject bad descriptors on the host (nothing launches)."""
+    lib = api.raw()
+    d = ctypes.byref(api.dims(128))
+
+    def pc(page_rows=64, max_pages=4, num_pages=10, pool=FAKE, table=FAKE):
+        return api.PagedCache(pool, table, num_pages, page_rows, max_pages)
+
+    def dec(c, max_len=200):
+        return lib.mla_decode_paged(d, 1, 2, FAKE, ctypes.byref(c) if c is not None else None, FAKE, max_len,
+                                    FAKE, FAKE, None, FAKE, 1 << 30, None)
+
+    assert dec(None) == 1
+    for bad in (pc(page_rows=48), pc(page_rows=16), pc(page_rows=1 << 17), pc(max_pages=0), pc(num_pages=0),
+                pc(num_pages=1 << 31), pc(pool=None), pc(table=None)):
+        assert dec(bad) == 1
+    assert dec(pc(page_rows=64, max_pages=3), max_len=193) == 1      # 193 rows need 4 pages of 64
+    assert b"max_pages" in lib.mla_last_error()
+    assert lib.mla_decode_partials_paged(d, 1, 2, FAKE, ctypes.byref(pc()), FAKE, 200, 0, FAKE, FAKE, None) == 1
+    assert lib.mla_prefill_paged(d, 1, 1, 100, FAKE, ctypes.byref(pc(page_rows=32, max_pages=4)), FAKE, 29,
+                                 FAKE, FAKE, FAKE, 1 << 30, None) == 1   # 29 + 100 > 128
+    assert lib.mla_prefill_unabsorbed_paged(ctypes.byref(api.dims(12)), 1, 1, 8, FAKE, FAKE, ctypes.byref(pc()),
+                                            FAKE, 0, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 2   # n_h % 8
+    # a workspace too small is still caught after the descriptor passes
+    need = lib.mla_decode_workspace_bytes(d, 1, 2, 200)
+    assert lib.mla_decode_paged(d, 1, 2, FAKE, ctypes.byref(pc()), FAKE, 200, FAKE, FAKE, None, FAKE,
+                                need - 1, None) == 3
+
+
+def test_paged_block_table_recipe():
+    """The seeded block table hands every sequence distinct pages of the pool."""
+    from mla_latent_kv_24_amd import workloads as W
+    lens = [1, 31, 32, 33, 700, 4096]
+    for P in (32, 64, 256):
+        table, num_pages = W.paged_block_table(lens, P, seed=5, spare_pages=7)
+        used = []
+        for b, L in enumerate(lens):
+            n = -(-L // P)
+            assert np.all(table[b, :n] >= 0) and np.all(table[b, :n] < num_pages)
+            assert np.all(table[b, n:] == -1)
+            used.extend(table[b, :n].tolist())
+        assert len(set(used)) == len(used) == num_pages - 7
+        rows = W.paged_rows(table, P, np.repeat(np.arange(len(lens)), lens),
+                            np.concatenate([np.arange(L) for L in lens]))
+        assert len(np.unique(rows)) == sum(lens) and rows.max() < num_pages * P

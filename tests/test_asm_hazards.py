@@ -20,7 +20,12 @@ import pytest
 from mla_latent_kv_24_amd import build as B
 
 NEED_WAIT_STATES = 18
-WIDE = "_ZN3mla19splitkv_wide_kernelENS_9SplitArgsE"
+# the 128-head kernel over a contiguous and over a paged cache
+WIDE = ["_ZN3mla19splitkv_wide_kernelILb0EEEvNS_9SplitArgsE",
+        "_ZN3mla19splitkv_wide_kernelILb1EEEvNS_9SplitArgsE"]
+# every tile-streaming decode kernel, both cache layouts
+STREAMING = WIDE + [f"_ZN3mla{k}ILb{p}EEEvNS_9SplitArgsE" for k in ("18splitkv_h16_kernel",) for p in (0, 1)] + \
+    [f"_ZN3mla19splitkv_mfma_kernelILi{c}ELb{p}EEEvNS_9SplitArgsE" for c in (2, 4) for p in (0, 1)]
 MFMA_V = re.compile(r"^\s*v_mfma\S*\s+v\[(\d+):(\d+)\],\s*(\S+),\s*(\S+),\s*(\S+)")
 
 
@@ -127,14 +132,16 @@ def test_no_early_reads_of_vgpr_mfma_results(asm):
     assert not bad, bad[:5]
 
 
-def test_wide_kernel_has_vgpr_score_mfmas(asm):
-    body = _instructions(_function(asm, WIDE))
+@pytest.mark.parametrize("name", WIDE)
+def test_wide_kernel_has_vgpr_score_mfmas(asm, name):
+    body = _instructions(_function(asm, name))
     assert sum(1 for s in body if MFMA_V.match(s)) >= 72      # prologue + one step's 36
     assert sum(1 for s in body if re.match(r"v_mfma\S*\s+a\[", s)) >= 32
 
 
-def test_wide_kernel_loop_has_no_scratch_reloads(asm):
-    body = _instructions(_function(asm, WIDE))
+@pytest.mark.parametrize("name", STREAMING)
+def test_streaming_kernel_loop_has_no_scratch_reloads(asm, name):
+    body = _instructions(_function(asm, name))
     idx = [i for i, s in enumerate(body) if s.startswith("v_mfma")]
     inside = body[idx[0]:idx[-1]]
     assert not [s for s in inside if s.startswith("scratch_load")]

@@ -1,0 +1,200 @@
+"""GPU tests of the paged latent cache: the same rows laid out in pages of a
+shuffled pool must give bitwise the output of the contiguous layout (same
+split plan, same arithmetic), and that output meets the oracle's bar.  An
+out-of-range page entry is never read and turns the outputs that attend it
+into NaN."""
+import numpy as np
+import pytest
+
+import oracle as O
+from mla_latent_kv_24_amd import workloads as W
+from helpers import TOL, f64, oracle_decode, rel_err
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def api():
+    from mla_latent_kv_24_amd import api as A
+    return A
+
+
+@pytest.fixture(scope="module")
+def pipeline():
+    from mla_latent_kv_24_amd import pipeline as P
+    return P
+
+
+def dev(a, dtype):
+    from mla_latent_kv_24_amd.pipeline import to_device
+    return to_device(a, dtype)
+
+
+def _run(st):
+    st.absorb()
+    st.attention()
+    st.combine()
+    torch.cuda.synchronize()
+    return st.out.clone(), st.out_latent.clone()
+
+
+# one case per attention kernel: 128 heads (wide), 16 (h16), 32 and 64
+# (mfma<CG>), fp32 storage and 8 heads (generic)
+CASES = [
+    ("v2_decode", dict(batch=3, seq_len=1000), 64),
+    ("v2_decode", dict(batch=2, seq_len=4099), 32),
+    ("lite_ragged", dict(batch=6, seq_len=3000), 32),
+    ("lite_decode", dict(batch=3, seq_len=777), 256),
+    ("v2_decode", dict(batch=3, seq_len=900, n_h=32), 64),
+    ("v2_decode", dict(batch=3, seq_len=900, n_h=64), 128),
+    ("tiny_f32", dict(batch=2, seq_len=300), 32),
+    ("lite_decode", dict(batch=2, seq_len=500, n_h=8), 64),
+]
+
+
+@pytest.mark.parametrize("name,changes,page_rows", CASES,
+                         ids=[f"{c[0]}-{c[1].get('n_h', 'h')}-{c[2]}" for c in CASES])
+def test_decode_paged_equals_contiguous(pipeline, name, changes, page_rows):
+    w = W.scaled(W.WORKLOADS[name], **changes)
+    inp = W.make_decode_inputs(w)
+    print(f"paged decode {name} {changes} page_rows={page_rows}", flush=True)
+    ref_out, ref_lat = _run(pipeline.DecodeState(inp, out_latent=True))
+    st = pipeline.DecodeState(inp, out_latent=True, page_rows=page_rows, spare_pages=5, table_seed=3)
+    out, lat = _run(st)
+    assert torch.equal(out, ref_out) and torch.equal(lat, ref_lat)
+    # and the paged output against the oracle directly
+    o_ref = np.stack([oracle_decode(inp, b, absorbed=True)[0] for b in range(w.batch)])
+    assert rel_err(out.cpu().numpy(), o_ref) < TOL[w.dtype]
+
+
+def test_decode_paged_fused_entry_point(api, pipeline):
+    """mla_decode_paged (partials + combine in one call) equals the separate calls, bit for bit."""
+    w = W.scaled(W.WORKLOADS["v2_decode"], batch=4, seq_len=2500)
+    st = pipeline.DecodeState(W.make_decode_inputs(w), out_latent=True, page_rows=64, table_seed=9)
+    out, lat = _run(st)
+    out2 = torch.empty_like(out)
+    lat2 = torch.empty_like(lat)
+    api.decode_paged(st.d, st.q_lat, st.cache, st.block_table, st.seq_lens, st.max_len, st.w_uv, out2, lat2)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out) and torch.equal(lat2, lat)
+
+
+@pytest.mark.parametrize("name,n_h", [("v2_decode", 128), ("lite_ragged", 16), ("v2_decode", 64),
+                                      ("tiny_f32", 16)])
+def test_decode_bad_page_is_not_read(pipeline, name, n_h):
+    """A block-table entry outside the pool: its sequence's output is NaN, the
+    other sequences' outputs are unchanged bit for bit."""
+    w = W.scaled(W.WORKLOADS[name], batch=3, seq_len=700, n_h=n_h)
+    st = pipeline.DecodeState(W.make_decode_inputs(w), out_latent=True, page_rows=64, table_seed=1)
+    good, _ = _run(st)
+    num_pages = st.cache.shape[0]
+    page = min(2, (int(st.seq_lens[1]) - 1) // 64)   # a page that sequence 1 attends
+    orig = int(st.block_table[1, page])
+    for bad in (num_pages, -7, 2 ** 31 - 1):
+        st.block_table[1, page] = bad
+        print(f"bad page {name} n_h={n_h} entry={bad}", flush=True)
+        out, _ = _run(st)
+        assert torch.isnan(out[1]).all()
+        assert torch.equal(out[0], good[0]) and torch.equal(out[2], good[2])
+    st.block_table[1, page] = orig
+    out, _ = _run(st)
+    assert torch.equal(out, good)
+
+
+def _paged_prefill_setup(api, prefixes, C, page_rows, n_h=128, seed=7):
+    dtype = "bf16"
+    pinps = [W.make_prefill_inputs(W.scaled(W.WORKLOADS["v2_prefill"], seq_len=p + C, prefill_chunk=C,
+                                            seed=seed + b, n_h=n_h)) for b, p in enumerate(prefixes)]
+    w_uk, w_uv = pinps[0].w_uk, pinps[0].w_uv
+    d = api.dims(n_h)
+    lens = [p + C for p in prefixes]
+    stride = max(lens) + 3
+    table, num_pages = W.paged_block_table(lens, page_rows, seed, spare_pages=3)
+    cache = torch.full((2 * stride, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pool = torch.full((num_pages, page_rows, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
+    for b, pi in enumerate(pinps):
+        tot = pi.prefix + pi.chunk
+        pos = torch.arange(tot, dtype=torch.int32, device="cuda")
+        c, k = dev(pi.c_kv, dtype), dev(pi.k_raw, dtype)
+        api.append_kv(d, c, k, pos, torch.arange(tot, dtype=torch.int64, device="cuda") + b * stride, cache)
+        prow = torch.from_numpy(W.paged_rows(table, page_rows, np.full(tot, b), np.arange(tot))).cuda()
+        api.append_kv(d, c, k, pos, prow, pool)
+    return pinps, d, cache, stride, pool, torch.from_numpy(table).cuda(), w_uk, w_uv
+
+
+@pytest.mark.parametrize("page_rows", [32, 128])
+def test_prefill_paged_equals_contiguous(api, page_rows):
+    """Absorbed and unabsorbed prefill over two sequences (prefixes 70 and 5,
+    chunk 40): paged equals contiguous bit for bit, and meets the oracle."""
+    C, prefixes, n_h, dtype = 40, (70, 5), 128, "bf16"
+    pinps, d, cache, stride, pool, table, w_uk, w_uv = _paged_prefill_setup(api, prefixes, C, page_rows)
+    plen = torch.tensor(prefixes, dtype=torch.int32, device="cuda")
+    q_c = dev(np.stack([pi.q_c for pi in pinps]), dtype)
+    q_r = dev(np.stack([pi.q_r for pi in pinps]), dtype)
+    q_pos = np.concatenate([np.arange(p, p + C) for p in prefixes]).astype(np.int32)
+    q_lat = api.q_lat_empty(d, torch.bfloat16, 2, C)
+    api.absorb_q(d, q_c.view(2 * C, n_h, 128), q_r.view(2 * C, n_h, 64), torch.from_numpy(q_pos).cuda(),
+                 dev(w_uk, dtype), q_lat.view(2 * C, n_h, 2, 576))
+    outs = {}
+    for form in ("absorbed", "unabsorbed"):
+        for layout in ("contiguous", "paged"):
+            out = torch.empty((2, C, n_h, 128), dtype=torch.float32, device="cuda")
+            print(f"prefill {form} {layout} page_rows={page_rows}", flush=True)
+            if form == "absorbed" and layout == "contiguous":
+                api.prefill(d, q_lat, cache, stride, plen, max(prefixes), dev(w_uv, dtype), out)
+            elif form == "absorbed":
+                api.prefill_paged(d, q_lat, pool, table, plen, max(prefixes), dev(w_uv, dtype), out)
+            elif layout == "contiguous":
+                api.prefill_unabsorbed(d, q_c, q_r, cache, stride, plen, max(prefixes), dev(w_uk, dtype),
+                                       dev(w_uv, dtype), out)
+            else:
+                api.prefill_unabsorbed_paged(d, q_c, q_r, pool, table, plen, max(prefixes), dev(w_uk, dtype),
+                                             dev(w_uv, dtype), out)
+            torch.cuda.synchronize()
+            outs[form, layout] = out
+    for form in ("absorbed", "unabsorbed"):
+        assert torch.equal(outs[form, "paged"], outs[form, "contiguous"]), form
+    got = outs["unabsorbed", "paged"].cpu().numpy()
+    for b, pi in enumerate(pinps):
+        ref = O.prefill(f64(pi.q_c, dtype), f64(pi.q_r, dtype), pi.prefix, f64(pi.c_kv, dtype),
+                        f64(pi.k_raw, dtype), f64(w_uk, dtype), f64(w_uv, dtype), pi.w.rope_base, store=dtype)
+        assert rel_err(got[b], ref) < TOL["bf16"]
+
+
+def test_prefill_paged_bad_page(api):
+    """Sequence 0 (prefix 70, chunk 40, pages of 32 rows) loses page 2 (rows
+    64..95): queries at positions >= 64 attend it and come out NaN; in the
+    absorbed form the earlier ones are unchanged and sequence 1 is untouched."""
+    C, prefixes, n_h, dtype = 40, (70, 5), 128, "bf16"
+    pinps, d, cache, stride, pool, table, w_uk, w_uv = _paged_prefill_setup(api, prefixes, C, 32)
+    plen = torch.tensor(prefixes, dtype=torch.int32, device="cuda")
+    q_c = dev(np.stack([pi.q_c for pi in pinps]), dtype)
+    q_r = dev(np.stack([pi.q_r for pi in pinps]), dtype)
+    q_pos = np.concatenate([np.arange(p, p + C) for p in prefixes]).astype(np.int32)
+    q_lat = api.q_lat_empty(d, torch.bfloat16, 2, C)
+    api.absorb_q(d, q_c.view(2 * C, n_h, 128), q_r.view(2 * C, n_h, 64), torch.from_numpy(q_pos).cuda(),
+                 dev(w_uk, dtype), q_lat.view(2 * C, n_h, 2, 576))
+    good = torch.empty((2, C, n_h, 128), dtype=torch.float32, device="cuda")
+    api.prefill_paged(d, q_lat, pool, table, plen, max(prefixes), dev(w_uv, dtype), good)
+    orig = int(table[0, 2])
+    table[0, 2] = pool.shape[0] + 11
+    out = torch.empty_like(good)
+    api.prefill_paged(d, q_lat, pool, table, plen, max(prefixes), dev(w_uv, dtype), out)
+    out_u = torch.empty_like(good)
+    api.prefill_unabsorbed_paged(d, q_c, q_r, pool, table, plen, max(prefixes), dev(w_uk, dtype),
+                                 dev(w_uv, dtype), out_u)
+    torch.cuda.synchronize()
+    first_bad = 64 - prefixes[0]   # query i sits at position 70 + i >= 64: every query of the chunk
+    assert first_bad <= 0
+    assert torch.isnan(out[0]).all() and torch.isnan(out_u[0]).all()
+    assert torch.equal(out[1], good[1])
+    table[0, 2] = orig
+    table[0, 3] = -1                # rows 96..127: read by the queries at positions 96..109 only
+    out2 = torch.empty_like(good)
+    api.prefill_paged(d, q_lat, pool, table, plen, max(prefixes), dev(w_uv, dtype), out2)
+    torch.cuda.synchronize()
+    # queries at positions 70..95 see rows < 96 only: unchanged; 96.. attend page 3: NaN
+    assert torch.equal(out2[0, :96 - 70], good[0, :96 - 70])
+    assert torch.isnan(out2[0, 96 - 70:]).all()
