@@ -39,6 +39,15 @@ no body, and no page defines RoPE itself):
     attention reads is RoPE(k_raw) rounded to that dtype (`store=` below;
     round to nearest even, float64 -> float32 -> bfloat16).  c^KV needs no
     rounding: it is stored as given.
+  * Rows made from hidden states ([L1], [V3]: c^KV = W^DKV h, k^R =
+    RoPE(W^KR h); [R2]: the model normalises the compressed latent with an
+    RMSNorm): c^KV = RMSNorm(W^DKV h) * weight, over the d_c latent channels
+    only, with eps 1e-6 unless given (the pages give no value) and a
+    per-channel weight supplied by the caller (1 if absent); the width
+    bottleneck scaling that [R2] mentions has no value on the pages and is
+    taken as folded into that weight.  The cache holds the normalised latent
+    (the one W^UK and W^UV consume); k^R is not normalised.  Both halves of
+    the row are rounded to the storage dtype once, from their exact values.
 
 Parity: every function below is pinned by tests that do not re-type its
 formula (closed forms, brute force, a library attention routine, identities,
@@ -122,6 +131,37 @@ def append_rows(c_kv: np.ndarray, k_raw: np.ndarray, pos, base: float = ROPE_BAS
     """Cache rows [c^KV_t ; RoPE(k_raw_t, pos_t)] -> [N, d_c + d_h^R]."""
     c_kv = np.asarray(c_kv, dtype=np.float64)
     return np.concatenate([c_kv, rope(k_raw, pos, base)], axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# A1 from hidden states ([L1] / [V3] c^KV = W^DKV h, k^R = RoPE(W^KR h);
+# [R2] RMSNorm after the compressed latent)
+# ---------------------------------------------------------------------------
+def rms_norm(x, weight=None, eps: float = 1e-6) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) over the last axis, times a per-channel weight."""
+    x = np.asarray(x, dtype=np.float64)
+    inv = 1.0 / np.sqrt(np.mean(np.square(x), axis=-1, keepdims=True) + eps)
+    out = x * inv
+    return out if weight is None else out * np.asarray(weight, dtype=np.float64)
+
+
+def kv_from_hidden(h, w_dkv, w_kr, norm_weight=None, eps: float = 1e-6):
+    """(c^KV, k_raw) of tokens with hidden states h [N, d_model]:
+    c^KV = RMSNorm(W^DKV h) * norm_weight  [N, d_c]   (w_dkv [d_c, d_model])
+    k_raw = W^KR h                        [N, d_h^R] (w_kr [d_h^R, d_model]; RoPE comes at append)."""
+    h = np.asarray(h, dtype=np.float64)
+    latent = h @ np.asarray(w_dkv, dtype=np.float64).T
+    k_raw = h @ np.asarray(w_kr, dtype=np.float64).T
+    return rms_norm(latent, norm_weight, eps), k_raw
+
+
+def append_rows_from_hidden(h, w_dkv, w_kr, pos, norm_weight=None, eps: float = 1e-6,
+                            base: float = ROPE_BASE, store=None) -> np.ndarray:
+    """Cache rows [c^KV_t ; RoPE(W^KR h_t, pos_t)] made from hidden states, each
+    half rounded once to the storage dtype when `store` is given."""
+    c, k_raw = kv_from_hidden(h, w_dkv, w_kr, norm_weight, eps)
+    rows = append_rows(c, k_raw, pos, base)
+    return rows if store is None else round_to_storage(rows, store)
 
 
 # ---------------------------------------------------------------------------

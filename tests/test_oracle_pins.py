@@ -408,3 +408,72 @@ def test_query_scale_keeps_logits_order_one():
     rows = O.append_rows(f(inp.c_kv[0]), f(inp.k_raw[0]), np.arange(256))
     logits = lat[0] @ rows.T / math.sqrt(192.0)
     assert 0.3 < np.std(logits) < 3.0
+
+
+# ------------------------------------------- rows from hidden states ([L1], [V3], [R2])
+def test_rms_norm_matches_torch_library_routine():
+    """The oracle's RMSNorm against torch.nn.functional.rms_norm in float64
+    (library routine; weight per channel, eps inside the square root)."""
+    torch = pytest.importorskip("torch")
+    r = _rng(41)
+    for shape, eps in (((5, 512), 1e-6), ((3, 7), 0.5), ((1, 64), 0.0)):
+        x = r.standard_normal(shape) * r.uniform(0.01, 30.0)
+        wgt = r.uniform(0.5, 1.5, shape[-1])
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (shape[-1],), torch.from_numpy(wgt),
+                                           eps).numpy()
+        assert np.max(np.abs(O.rms_norm(x, wgt, eps) - ref)) < 1e-13 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_rms_norm_invariants():
+    """Unit weight, eps = 0: the output has mean square exactly 1, is unchanged
+    by a positive scale of x and flips with its sign; eps > 0 leaves mean
+    square ms / (ms + eps)."""
+    x = _rng(42).standard_normal((6, 512)) * 3.0
+    y = O.rms_norm(x, None, 0.0)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-14)
+    assert np.allclose(O.rms_norm(7.5 * x, None, 0.0), y, rtol=1e-13, atol=0)
+    assert np.allclose(O.rms_norm(-x, None, 0.0), -y, rtol=0, atol=0)
+    ms = np.mean(x * x, axis=-1)
+    ye = O.rms_norm(x, None, 0.25)
+    assert np.allclose(np.mean(ye * ye, axis=-1), ms / (ms + 0.25), rtol=1e-13)
+
+
+def test_kv_from_hidden_bruteforce():
+    """Tiny case against pure-Python loops: latent_o = sum_k W^DKV[o][k] h[k],
+    c = latent / sqrt(mean(latent^2) + eps) * weight, k_raw_r = sum_k W^KR[r][k] h[k]."""
+    r = _rng(43)
+    N, D, C, R, eps = 3, 6, 4, 2, 1e-3
+    h = r.standard_normal((N, D))
+    w_dkv = r.standard_normal((C, D))
+    w_kr = r.standard_normal((R, D))
+    wgt = r.uniform(0.5, 1.5, C)
+    c, k = O.kv_from_hidden(h, w_dkv, w_kr, wgt, eps)
+    for t in range(N):
+        lat = [sum(w_dkv[o][j] * h[t][j] for j in range(D)) for o in range(C)]
+        ms = sum(v * v for v in lat) / C
+        for o in range(C):
+            assert abs(c[t][o] - lat[o] / math.sqrt(ms + eps) * wgt[o]) < 1e-12
+        for o in range(R):
+            assert abs(k[t][o] - sum(w_kr[o][j] * h[t][j] for j in range(D))) < 1e-12
+
+
+def test_rows_from_hidden_compose_and_scale():
+    """k_raw is linear in h while the normalised latent ignores h's scale
+    (eps = 0); the row is [c ; RoPE(k_raw)] with RoPE at the row's position,
+    and with store given each half is the storage rounding of the exact one."""
+    r = _rng(44)
+    h = r.standard_normal((4, 64))
+    w_dkv = r.standard_normal((16, 64)) / 8.0
+    w_kr = r.standard_normal((8, 64)) / 8.0
+    c1, k1 = O.kv_from_hidden(h, w_dkv, w_kr, None, 0.0)
+    c3, k3 = O.kv_from_hidden(3.0 * h, w_dkv, w_kr, None, 0.0)
+    assert np.allclose(c3, c1, rtol=1e-13, atol=0) and np.allclose(k3, 3.0 * k1, rtol=1e-13, atol=0)
+    pos = np.array([0, 5, 4095, 131071])
+    rows = O.append_rows_from_hidden(h, w_dkv, w_kr, pos, None, 0.0)
+    assert np.array_equal(rows[:, :16], c1)
+    assert np.array_equal(rows[0, 16:], k1[0])                       # RoPE at position 0 is the identity
+    assert np.allclose(np.linalg.norm(rows[:, 16:], axis=-1), np.linalg.norm(k1, axis=-1), rtol=1e-13)
+    stored = O.append_rows_from_hidden(h, w_dkv, w_kr, pos, None, 0.0, store="bf16")
+    ulp = np.exp2(np.floor(np.log2(np.abs(rows))) - 7)
+    assert np.all(np.abs(stored - rows) <= 0.5 * ulp * (1 + 1e-9))
+    assert np.all(W.to_f64(W.f32_to_bf16_bits(stored.astype(np.float32)), "bf16") == stored)
