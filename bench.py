@@ -129,6 +129,56 @@ def bench_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_kv_proj(args):
+    """A1 from hidden states (mla_append_kv_from_hidden) at the V2 shapes:
+    d_model 5120 -> [c^KV (512, RMSNorm) ; k^R (64, RoPE)] rows, for the 64
+    tokens of a v2_decode step and a 4,096-token prefill chunk.  Reports the
+    time per call and its rate against the bytes the call must move (the
+    weights once, the hidden states once, the rows written) and its FLOP."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_24_amd import api, workloads as W
+    from mla_latent_kv_24_amd.pipeline import to_device
+    d_model, res = 5120, {}
+    d = api.dims(128)
+    w_dkv = to_device(W.random_storage(1, (512, d_model), "bf16", d_model ** -0.5), "bf16")
+    w_kr = to_device(W.random_storage(2, (64, d_model), "bf16", d_model ** -0.5), "bf16")
+    gamma = to_device(W.to_storage(np.ones(512, np.float32), "bf16"), "bf16")
+    steps, warm = max(1, min(args.steps, 200)), max(1, args.warmup)
+    for name, n_tok in (("decode_step", 64), ("prefill_chunk", 4096)):
+        h = to_device(W.random_storage(3, (n_tok, d_model), "bf16"), "bf16")
+        pos = torch.arange(n_tok, dtype=torch.int32, device="cuda")
+        row = torch.arange(n_tok, dtype=torch.int64, device="cuda")
+        cache = torch.empty((n_tok, 576), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(api.append_kv_from_hidden_workspace_bytes(d, api.BF16, n_tok, d_model),
+                         dtype=torch.uint8, device="cuda")
+        fn = lambda: api.append_kv_from_hidden(d, h, w_dkv, w_kr, gamma, 1e-6, pos, row, cache, ws)
+        t = time.perf_counter()
+        while (time.perf_counter() - t) * 1e3 < min(args.settle_ms, 1000.0):
+            for _ in range(20):
+                fn()
+            torch.cuda.synchronize()
+        for _ in range(warm):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        alg_bytes = 576 * d_model * 2 + n_tok * d_model * 2 + n_tok * 576 * 2
+        flop = 2 * n_tok * d_model * 576
+        res[name] = {"n_tok": n_tok, "us": round(us, 2), "alg_bytes": alg_bytes,
+                     "gbs": round(alg_bytes / (us * 1e-6) / 1e9, 1),
+                     "tflops": round(flop / (us * 1e-6) / 1e12, 1)}
+    line = {"metric": "cache rows from hidden states (W^DKV, RMSNorm, W^KR, RoPE; d_model 5120)",
+            "unit": "us", "higher_is_better": False, "steps": steps, "warmup": warm, "dtype": "bf16",
+            "data": "synthetic", **res, "hbm_peak_gbs": HBM_PEAK_GBS, "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +194,9 @@ def main():
     ap.add_argument("--prefill", action="store_true",
                     help="instead of the decode step, time the causal prefill of the v2_prefill "
                          "workload in both forms (absorbed, unabsorbed); one JSON line")
+    ap.add_argument("--kv-proj", action="store_true",
+                    help="instead of the decode step, time the cache rows made from hidden states "
+                         "(KV down-projection + RMSNorm + RoPE) at a decode step and a prefill chunk")
     ap.add_argument("--page-rows", type=int, default=0,
                     help="run the decode step over a paged cache of pages of this many rows, "
                          "handed out in a seeded random order (0: contiguous sequence slots)")
@@ -161,6 +214,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.prefill:
         return bench_prefill(args)
+    if args.kv_proj:
+        return bench_kv_proj(args)
     w = W.WORKLOADS[args.workload]
     log(f"[bench] generating {w.name} ...")
     inp = W.make_decode_inputs(w)

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 4
+#define MLA_ABI_VERSION 5
 
 typedef enum {
   MLA_OK = 0,
@@ -82,6 +82,30 @@ const char* mla_last_error(void);
 mla_status mla_append_kv(const mla_dims* dims, mla_dtype dtype, int32_t n_tok,
                          const void* c_kv, const void* k_r, const int32_t* pos,
                          const int64_t* row, void* cache, void* stream);
+
+/* A1 from hidden states -- the cache rows of new tokens made from their
+ * hidden states (irregular6612 notes, section 2.1.2, and DeepSeek-V3 report,
+ * Metode 1: c^KV_t = W^DKV h_t, k^R_t = RoPE(W^KR h_t); review section 2: the
+ * model normalises the compressed latent with an RMSNorm):
+ *   x = W^DKV h_t (d_c), k = W^KR h_t (d_hR), fp32 sums;
+ *   row[t] <- [ x / sqrt(mean(x^2) + eps) * norm_weight ; RoPE(k, pos[t]) ]
+ * each half rounded once to the storage dtype (RoPE as mla_append_kv).
+ *   h [n_tok][d_model], w_dkv [d_c][d_model], w_kr [d_hR][d_model] (row-major,
+ *   one row per output), norm_weight [d_c] or NULL (weight 1; a model's extra
+ *   latent scaling factor folds into it), eps >= 0 (1e-6 is the usual value),
+ *   pos, row, cache: as mla_append_kv (rows must be distinct).
+ *   workspace: at least mla_append_kv_from_hidden_workspace_bytes() (fp32
+ *   partial sums; device).
+ * n_tok in [0, 65535] (0 is a no-op); d_model in [1, 2^20].  The bf16 matrix-core
+ * kernel needs d_model to be a multiple of 128; other shapes and MLA_F32 run
+ * a generic fp32 kernel. */
+size_t mla_append_kv_from_hidden_workspace_bytes(const mla_dims* dims, mla_dtype dtype,
+                                                 int32_t n_tok, int32_t d_model);
+mla_status mla_append_kv_from_hidden(const mla_dims* dims, mla_dtype dtype, int32_t n_tok,
+                                     int32_t d_model, const void* h, const void* w_dkv,
+                                     const void* w_kr, const void* norm_weight, double eps,
+                                     const int32_t* pos, const int64_t* row, void* cache,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* A2 -- absorbed query (review section 2: (U^K_i)^T q^C folded into the
  * query; section 3: per-head RoPE query).

@@ -58,6 +58,9 @@ _SIGS = {
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_last_error": (ctypes.c_char_p, []),
     "mla_append_kv": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mla_append_kv_from_hidden_workspace_bytes": (_sz, [_P, ctypes.c_int, _i32, _i32]),
+    "mla_append_kv_from_hidden": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _vp,
+                                                 ctypes.c_double, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mla_absorb_q": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mla_decode_num_splits": (_i32, [_P, ctypes.c_int, _i32, _i32]),
     "mla_split_rows": (_i64, [_i32, _i32]),
@@ -126,6 +129,27 @@ def append_kv(d: Dims, c_kv, k_r, pos, row, cache) -> None:
     assert pos.dtype == torch.int32 and row.dtype == torch.int64
     _check(_lib.mla_append_kv(ctypes.byref(d), _dtype(cache), n, _ptr(c_kv), _ptr(k_r), _ptr(pos),
                               _ptr(row), _ptr(cache), _stream(cache.device)), "mla_append_kv")
+
+
+def append_kv_from_hidden_workspace_bytes(d: Dims, dtype: int, n_tok: int, d_model: int) -> int:
+    return _lib.mla_append_kv_from_hidden_workspace_bytes(ctypes.byref(d), dtype, n_tok, d_model)
+
+
+def append_kv_from_hidden(d: Dims, h, w_dkv, w_kr, norm_weight, eps: float, pos, row, cache,
+                          workspace=None) -> None:
+    """A1 from hidden states: cache[row[t]] = [RMSNorm(w_dkv @ h[t]) * norm_weight;
+    RoPE(w_kr @ h[t], pos[t])]; h [n_tok, d_model], w_dkv [d_c, d_model], w_kr [d_hR, d_model],
+    norm_weight [d_c] or None."""
+    assert pos.dtype == torch.int32 and row.dtype == torch.int64
+    n, dm = h.shape
+    dt = _dtype(cache)
+    if workspace is None:
+        need = append_kv_from_hidden_workspace_bytes(d, dt, n, dm)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=cache.device)
+    _check(_lib.mla_append_kv_from_hidden(ctypes.byref(d), dt, n, dm, _ptr(h), _ptr(w_dkv), _ptr(w_kr),
+                                          _ptr(norm_weight), float(eps), _ptr(pos), _ptr(row), _ptr(cache),
+                                          _ptr(workspace), workspace.numel(), _stream(cache.device)),
+           "mla_append_kv_from_hidden")
 
 
 def q_lat_empty(d: Dims, storage: torch.dtype, *lead: int, device="cuda") -> torch.Tensor:

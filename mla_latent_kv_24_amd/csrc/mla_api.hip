@@ -161,6 +161,48 @@ mla_status mla_append_kv(const mla_dims* dims, mla_dtype dtype, int32_t n_tok, c
   return hip_status(mla::launch_append(a, dtype == MLA_BF16, static_cast<hipStream_t>(stream)), "mla_append_kv");
 }
 
+size_t mla_append_kv_from_hidden_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t n_tok,
+                                                 int32_t d_model) {
+  if (check_dims(dims, dtype) != MLA_OK || n_tok < 1 || d_model < 1) return 0;
+  int32_t slices = 1, kr = 0;
+  mla::kv_project_plan(n_tok, d_model, slices, kr);
+  return static_cast<size_t>(slices) * n_tok * mla::ROWE * sizeof(float);
+}
+
+mla_status mla_append_kv_from_hidden(const mla_dims* dims, mla_dtype dtype, int32_t n_tok, int32_t d_model,
+                                     const void* h, const void* w_dkv, const void* w_kr, const void* norm_weight,
+                                     double eps, const int32_t* pos, const int64_t* row, void* cache,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  if (n_tok < 0 || n_tok > 65535) return fail(MLA_ERR_INVALID_ARGUMENT, "n_tok=%d out of range [0,65535]", n_tok);
+  if (n_tok == 0) return MLA_OK;
+  if (d_model < 1 || d_model > (1 << 20))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "d_model=%d out of range [1,%d]", d_model, 1 << 20);
+  if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(MLA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (!h || !w_dkv || !w_kr || !pos || !row || !cache || !workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const size_t need = mla_append_kv_from_hidden_workspace_bytes(dims, dtype, n_tok, d_model);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", workspace_bytes, need);
+  mla::KvProjArgs a{};
+  a.h = h;
+  a.w_dkv = w_dkv;
+  a.w_kr = w_kr;
+  a.norm_w = norm_weight;
+  a.pos = pos;
+  a.row = row;
+  a.cache = cache;
+  a.part = static_cast<float*>(workspace);
+  a.n_tok = n_tok;
+  a.d_model = d_model;
+  mla::kv_project_plan(n_tok, d_model, a.k_slices, a.k_per_slice);
+  a.eps = static_cast<float>(eps);
+  fill_rope(dims, a.rope);
+  return hip_status(mla::launch_kv_project_append(a, dtype == MLA_BF16, static_cast<hipStream_t>(stream)),
+                    "mla_append_kv_from_hidden");
+}
+
 mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q, const void* q_c,
                         const void* q_r, const int32_t* q_pos, const void* w_uk, void* q_lat,
                         void* stream) {

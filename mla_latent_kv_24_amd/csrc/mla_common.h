@@ -126,6 +126,22 @@ struct PrefillArgs {
   RopeTable rope;
 };
 
+// Cache rows from hidden states: split-K partial sums of [W^DKV; W^KR] h, then
+// per token the sum over slices, the latent RMSNorm, RoPE and the row store.
+struct KvProjArgs {
+  const void* h;                // [n_tok][d_model]
+  const void* w_dkv;            // [d_c][d_model]
+  const void* w_kr;             // [d_r][d_model]
+  const void* norm_w;           // [d_c] or NULL (weight 1)
+  const int32_t* pos;           // [n_tok]
+  const int64_t* row;           // [n_tok] destination cache rows
+  void* cache;
+  float* part;                  // [k_slices][n_tok][d_c + d_r] fp32
+  int32_t n_tok, d_model, k_slices, k_per_slice;
+  float eps;
+  RopeTable rope;
+};
+
 // host launchers (defined in the .hip files); return hipGetLastError() after launch
 hipError_t launch_append(const AppendArgs& a, int bf16, hipStream_t st);
 hipError_t launch_rope_q(const RopeQArgs& a, int bf16, hipStream_t st);
@@ -133,6 +149,9 @@ hipError_t launch_absorb(const AbsorbArgs& a, int bf16, hipStream_t st);
 hipError_t launch_splitkv(const SplitArgs& a, int bf16, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, int bf16, hipStream_t st);
 hipError_t launch_prefill_unabsorbed(const ExpandArgs& e, const PrefillArgs& p, hipStream_t st);
+hipError_t launch_kv_project_append(const KvProjArgs& a, int bf16, hipStream_t st);
+// split-K plan of launch_kv_project_append: slices and k per slice (a multiple of 64)
+void kv_project_plan(int32_t n_tok, int32_t d_model, int32_t& k_slices, int32_t& k_per_slice);
 bool splitkv_has_fast_path(int n_h, int bf16, int d_c, int d_r);
 
 // ---------------------------------------------------------------- device helpers

@@ -153,3 +153,24 @@ def test_paged_block_table_recipe():
         rows = W.paged_rows(table, P, np.repeat(np.arange(len(lens)), lens),
                             np.concatenate([np.arange(L) for L in lens]))
         assert len(np.unique(rows)) == sum(lens) and rows.max() < num_pages * P
+
+
+def test_append_kv_from_hidden_validation():
+    lib = api.raw()
+    d = ctypes.byref(api.dims(16))
+    need = lib.mla_append_kv_from_hidden_workspace_bytes(d, 1, 64, 5120)
+    assert need >= 64 * 576 * 4
+
+    def call(n_tok=64, dm=5120, eps=1e-6, h=FAKE, ws=need):
+        return lib.mla_append_kv_from_hidden(d, 1, n_tok, dm, h, FAKE, FAKE, None, eps, FAKE, FAKE, FAKE, FAKE, ws,
+                                             None)
+
+    assert lib.mla_append_kv_from_hidden(d, 1, 0, 5120, None, None, None, None, 1e-6, None, None, None, None, 0,
+                                         None) == 0          # n_tok = 0: no-op
+    assert call(n_tok=-1) == 1
+    assert call(n_tok=70000) == 1
+    assert call(dm=0) == 1
+    assert call(eps=float("nan")) == 1
+    assert call(eps=-1.0) == 1
+    assert call(h=None) == 1
+    assert call(ws=need - 1) == 3
