@@ -49,6 +49,16 @@ no body, and no page defines RoPE itself):
     (the one W^UK and W^UV consume); k^R is not normalised.  Both halves of
     the row are rounded to the storage dtype once, from their exact values.
 
+  * Quantised latent cache (the pages report a cache of about 6 bits per
+    element for the served model -- review section 4 -- without giving a
+    format): c^KV is stored as FP8 E4M3 (the OCP 8-bit float: 1 sign, 4
+    exponent bits of bias 7, 3 mantissa bits, no infinities, 448 the largest
+    finite value) with one float32 scale per row, s = amax|c| / 448, and the
+    code of each element the round-to-nearest-even of c / s; k^R stays in
+    bf16.  The scale and the codes are decided in float32 (the kernel's
+    precision; divisions correctly rounded), so this oracle reproduces them
+    exactly.  A row of zeros takes s = 1.
+
 Parity: every function below is pinned by tests that do not re-type its
 formula (closed forms, brute force, a library attention routine, identities,
 the pages' printed cache numbers).
@@ -162,6 +172,60 @@ def append_rows_from_hidden(h, w_dkv, w_kr, pos, norm_weight=None, eps: float = 
     c, k_raw = kv_from_hidden(h, w_dkv, w_kr, norm_weight, eps)
     rows = append_rows(c, k_raw, pos, base)
     return rows if store is None else round_to_storage(rows, store)
+
+
+# ---------------------------------------------------------------------------
+# Quantised latent (FP8 E4M3 codes + one float32 scale per row; see header)
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each 8-bit E4M3 code as float64: sign bit 7, exponent bits 6..3
+    (bias 7), mantissa bits 2..0; exponent 0 is subnormal (m/8 * 2^-6); the
+    code with every exponent and mantissa bit set is NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round each value to the nearest finite E4M3 value, ties to the code with
+    an even mantissa (round to nearest even), keeping the sign (a negative
+    value that rounds to zero gives -0, code 0x80); |x| up to the midpoint 464
+    above 448 rounds to +-448, beyond it raises (the quantiser never gets
+    there)."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.isnan(x)) or np.any(np.abs(x) >= 464.0):
+        raise ValueError("E4M3 encode: NaN or |x| >= 464")
+    pos = np.arange(0x7F, dtype=np.uint8)              # codes 0x00..0x7E: 0 .. 448, increasing
+    vals = e4m3_decode(pos)
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, len(vals) - 1)
+    lo = np.clip(hi - 1, 0, len(vals) - 1)
+    d_lo, d_hi = a - vals[lo], vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((pos[hi] & 1) == 0))
+    code = np.where(pick_hi, pos[hi], pos[lo]).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)   # the sign is kept, zero included
+
+
+def quantize_rows_fp8(c):
+    """(codes uint8 [N, d], scale float32 [N]) of latent rows c [N, d] (values
+    exact in float32): s = amax / 448 and y = c / s in float32, codes = E4M3(y)."""
+    c32 = np.asarray(c, dtype=np.float32)
+    amax = np.max(np.abs(c32), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (c32 / scale[..., None]).astype(np.float32)
+    return e4m3_encode(y), scale
+
+
+def dequantize_rows_fp8(codes, scale) -> np.ndarray:
+    """float64 latent values the quantised rows stand for: E4M3(code) * s."""
+    return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[..., None]
 
 
 # ---------------------------------------------------------------------------

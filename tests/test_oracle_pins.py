@@ -477,3 +477,66 @@ def test_rows_from_hidden_compose_and_scale():
     ulp = np.exp2(np.floor(np.log2(np.abs(rows))) - 7)
     assert np.all(np.abs(stored - rows) <= 0.5 * ulp * (1 + 1e-9))
     assert np.all(W.to_f64(W.f32_to_bf16_bits(stored.astype(np.float32)), "bf16") == stored)
+
+
+# ------------------------------------------------------ FP8 E4M3 latent (quantised cache)
+def test_e4m3_decode_table_matches_torch_and_printed_values():
+    """All 256 codes against torch's float8_e4m3fn (library routine), and the
+    format's landmark values: 2^-9 (smallest subnormal), 2^-6 (smallest
+    normal), 1.0 = 0x38, 448 = 0x7E (largest), NaN = 0x7F / 0xFF."""
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]) and np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+    assert O.e4m3_decode([0x01])[0] == 2.0 ** -9 and O.e4m3_decode([0x08])[0] == 2.0 ** -6
+    assert O.e4m3_decode([0x38])[0] == 1.0 and O.e4m3_decode([0x7E])[0] == 448.0
+    assert np.isnan(O.e4m3_decode([0x7F, 0xFF])).all()
+
+
+def test_e4m3_encode_matches_torch_and_brute_force():
+    """Round-to-nearest-even against torch's float32 -> float8_e4m3fn cast on
+    random values over the whole range, every midpoint between neighbouring
+    codes (exact ties), and against a brute-force nearest search."""
+    torch = pytest.importorskip("torch")
+    r = _rng(45)
+    vals = O.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    x = np.concatenate([r.uniform(-448, 448, 20000), np.exp2(r.uniform(-12, 8.8, 20000)) * r.choice([-1, 1], 20000),
+                        mids, -mids, vals, np.nextafter(mids, 0), np.nextafter(mids, 1000), [463.9, -463.9]])
+    x = x.astype(np.float32).astype(np.float64)
+    got = O.e4m3_encode(x)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+    # brute force on a subsample: the code's value is the nearest; a tie goes to the even mantissa
+    for xi, ci in zip(x[::97], got[::97]):
+        d = np.abs(vals - abs(xi))
+        best = np.flatnonzero(d == d.min())
+        want = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        assert (ci & 0x7F) == want and bool(ci & 0x80) == bool(np.signbit(xi))
+    with pytest.raises(ValueError):
+        O.e4m3_encode([464.0])
+
+
+def test_quantize_rows_fp8_properties():
+    """Per-row scale: the largest element maps to +-448 exactly; every element's
+    dequantised value is within half an E4M3 step of it (relative 2^-4 for
+    normal codes, 2^-10 s absolute below); zero rows take scale 1."""
+    r = _rng(46)
+    c = W.to_f64(W.to_storage(r.standard_normal((50, 512)).astype(np.float32), "bf16"), "bf16")
+    c[3] = 0.0
+    c[4, :] = 0.0
+    c[4, 7] = -2.5
+    codes, scale = O.quantize_rows_fp8(c)
+    assert codes.dtype == np.uint8 and scale.dtype == np.float32 and codes.shape == c.shape
+    assert scale[3] == 1.0 and np.all(codes[3] == 0)
+    deq = O.dequantize_rows_fp8(codes, scale)
+    amax_idx = np.argmax(np.abs(c), axis=1)
+    for i in range(len(c)):
+        if scale[i] != 1.0 or np.any(c[i]):
+            assert abs(O.e4m3_decode(codes[i, amax_idx[i]])) == 448.0
+    step = np.maximum(np.abs(deq) * 2.0 ** -3, 2.0 ** -9 * scale[:, None])   # one E4M3 step at that value
+    assert np.all(np.abs(deq - c) <= 0.5 * step * (1 + 1e-6) + 1e-12)
+    assert np.all(np.sign(deq) * np.sign(c) >= 0)
