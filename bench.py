@@ -24,6 +24,7 @@ METRIC = "MLA decode latent-cache tokens/s + % of HBM/MFMA roofline (V2 shapes, 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 ROW_BYTES = 1152               # one bf16 cache row [c_kv 512 ; k_R 64]
+FP8_ROW_BYTES = 644            # one FP8 cache row: 512 E4M3 codes + 64 bf16 k_R + fp32 scale
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_splitkv_v2_decode.json")
 # the attention kernel's sources: the counters are valid only for exactly these
 KERNEL_SRCS = [os.path.join(ROOT, "mla_latent_kv_24_amd", "csrc", f)
@@ -197,6 +198,9 @@ def main():
     ap.add_argument("--kv-proj", action="store_true",
                     help="instead of the decode step, time the cache rows made from hidden states "
                          "(KV down-projection + RMSNorm + RoPE) at a decode step and a prefill chunk")
+    ap.add_argument("--fp8-cache", action="store_true",
+                    help="run the decode step over the FP8 latent cache (E4M3 codes + per-row scale, "
+                         "bf16 RoPE keys: 644 B per row)")
     ap.add_argument("--page-rows", type=int, default=0,
                     help="run the decode step over a paged cache of pages of this many rows, "
                          "handed out in a seeded random order (0: contiguous sequence slots)")
@@ -219,10 +223,12 @@ def main():
     w = W.WORKLOADS[args.workload]
     log(f"[bench] generating {w.name} ...")
     inp = W.make_decode_inputs(w)
-    st = DecodeState(inp, page_rows=args.page_rows or None)
+    st = DecodeState(inp, page_rows=args.page_rows or None, fp8=args.fp8_cache)
     torch.cuda.synchronize()
     tokens = int(inp.seq_lens.sum())
     layout = f"paged ({args.page_rows}-row pages)" if args.page_rows else "contiguous"
+    if args.fp8_cache:
+        layout += ", FP8 latent"
     log(f"[bench] {w.name}: batch={w.batch} rows={tokens} n_h={w.n_h} splits={st.splits} cache={layout}")
 
     if args.copy_probe:
@@ -296,12 +302,13 @@ def main():
     ms_per_step = elapsed / args.steps * 1e3
     value = tokens * args.steps / elapsed
     n_h = w.n_h
-    alg_bytes = tokens * ROW_BYTES + w.batch * n_h * 576 * 2           # cache stream + absorbed queries
+    row_bytes = FP8_ROW_BYTES if args.fp8_cache else ROW_BYTES
+    alg_bytes = tokens * row_bytes + w.batch * n_h * 576 * 2           # cache stream + absorbed queries
     alg_flop = tokens * 2176 * n_h                                     # (2*576 + 2*512) per row per head
     achieved_gbs = alg_bytes / (attn_ms * 1e-3) / 1e9
     tflops = alg_flop / (attn_ms * 1e-3) / 1e12
     # the committed counter summary covers the contiguous kernel instance only
-    traffic = None if args.page_rows else pmc_traffic(tokens)
+    traffic = None if (args.page_rows or args.fp8_cache) else pmc_traffic(tokens)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -318,10 +325,12 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "n_h": n_h, "d_c": 512,
                    "d_hR": 64, "d_h": 128, "latent_rows": tokens, "splits": st.splits,
                    "cache_layout": "paged" if args.page_rows else "contiguous",
+                   "latent": "fp8_e4m3+row_scale" if args.fp8_cache else "bf16",
                    **({"page_rows": args.page_rows} if args.page_rows else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "splitkv_wide_kernel",
+                     "traffic": traffic,
+                     "kernel": "splitkv_fp8_wide_kernel" if args.fp8_cache else "splitkv_wide_kernel",
                      "kernel_us": round(attn_ms * 1e3, 2),
                      "mfma_tflops": round(tflops, 1),
                      "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},

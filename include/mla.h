@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 5
+#define MLA_ABI_VERSION 6
 
 typedef enum {
   MLA_OK = 0,
@@ -285,6 +285,49 @@ mla_status mla_prefill_unabsorbed_paged(const mla_dims* dims, mla_dtype dtype, i
                                         const void* w_uk, const void* w_uv, float* out,
                                         void* workspace, size_t workspace_bytes,
                                         void* stream);
+
+/* Quantised latent cache (the review's section 4 reports the served model's
+ * cache at about 6 bits per element without giving a format; this is an 8-bit
+ * one).  Row r holds
+ *   codes[r][0:d_c]  uint8  FP8 E4M3 codes (OCP: 1 sign, 4 exponent bits of
+ *                           bias 7, 3 mantissa bits; largest finite 448)
+ *   rope[r][0:d_hR]  bf16   k^R after RoPE (as in the bf16 cache)
+ *   scale[r]         float  per-row scale
+ * and stands for the row [E4M3(codes) * scale ; rope]; the attention is that
+ * of the bf16 entry points over these values.  Written by mla_append_kv_fp8:
+ *   s = max_e |c^KV_e| / 448 (1 for a row of zeros), code_e = E4M3(c^KV_e / s)
+ *   rounded to nearest even, both in fp32 with correctly rounded division.
+ * 644 bytes per row against 1,152 for bf16.  Rows are indexed as in the
+ * contiguous cache (sequence b at row b * cache_seq_stride). */
+typedef struct {
+  void* codes;
+  void* rope;
+  float* scale;
+} mla_fp8_cache;
+
+/* A1 into the FP8 cache: c_kv [n_tok][d_c] and k_r [n_tok][d_hR] (before RoPE)
+ * in bf16, pos, row as mla_append_kv (rows distinct).  n_tok = 0 is a no-op. */
+mla_status mla_append_kv_fp8(const mla_dims* dims, int32_t n_tok, const void* c_kv,
+                             const void* k_r, const int32_t* pos, const int64_t* row,
+                             const mla_fp8_cache* cache, void* stream);
+
+/* A3 over the FP8 cache: as mla_decode_partials with bf16 queries (absorbed
+ * query layout; 128 heads read hi only, other head counts hi + lo) and the
+ * same split plan and partials layout.  128 heads run the matrix-core kernel,
+ * other head counts a generic fp32 kernel. */
+mla_status mla_decode_partials_fp8(const mla_dims* dims, int32_t batch, const void* q_lat,
+                                   const mla_fp8_cache* cache, int64_t cache_seq_stride,
+                                   const int32_t* seq_lens, int32_t max_seq_len,
+                                   int32_t num_splits, float* z_part, float* lse_part,
+                                   void* stream);
+
+/* A3 + A4 + A5 over the FP8 cache (w_uv bf16); the workspace is
+ * mla_decode_workspace_bytes(dims, MLA_BF16, batch, max_seq_len). */
+mla_status mla_decode_fp8(const mla_dims* dims, int32_t batch, const void* q_lat,
+                          const mla_fp8_cache* cache, int64_t cache_seq_stride,
+                          const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv,
+                          float* out, float* out_latent, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -53,6 +53,14 @@ class PagedCache(ctypes.Structure):
 
 
 _PC = ctypes.POINTER(PagedCache)
+
+
+class FP8Cache(ctypes.Structure):
+    """mla_fp8_cache: codes uint8 [rows][d_c], rope bf16 [rows][d_hR], scale float [rows]."""
+    _fields_ = [("codes", _vp), ("rope", _vp), ("scale", _vp)]
+
+
+_FC = ctypes.POINTER(FP8Cache)
 _SIGS = {
     "mla_abi_version": (_i32, []),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -76,6 +84,9 @@ _SIGS = {
                                               _vp, _vp, _vp, _vp, _sz, _vp]),
     "mla_prefill": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _i64, _vp, _i32, _vp, _vp,
                                    _vp, _sz, _vp]),
+    "mla_append_kv_fp8": (ctypes.c_int, [_P, _i32, _vp, _vp, _vp, _vp, _FC, _vp]),
+    "mla_decode_partials_fp8": (ctypes.c_int, [_P, _i32, _vp, _FC, _i64, _vp, _i32, _i32, _vp, _vp, _vp]),
+    "mla_decode_fp8": (ctypes.c_int, [_P, _i32, _vp, _FC, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mla_decode_partials_paged": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _PC, _vp, _i32, _i32, _vp, _vp,
                                                  _vp]),
     "mla_decode_paged": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _PC, _vp, _i32, _vp, _vp, _vp, _vp,
@@ -322,3 +333,47 @@ def prefill_unabsorbed_paged(d: Dims, q_c, q_r, pool, block_table, prefix_lens, 
                                              ctypes.byref(pc), _ptr(prefix_lens), max_prefix_len, _ptr(w_uk),
                                              _ptr(w_uv), _ptr(out), _ptr(workspace), workspace.numel(),
                                              _stream(pool.device)), "mla_prefill_unabsorbed_paged")
+
+
+def fp8_cache_empty(rows: int, d_c: int = 512, d_hR: int = 64, device="cuda"):
+    """(codes, rope, scale) device tensors of an FP8 latent cache of `rows` rows."""
+    return (torch.empty((rows, d_c), dtype=torch.uint8, device=device),
+            torch.empty((rows, d_hR), dtype=torch.bfloat16, device=device),
+            torch.empty((rows,), dtype=torch.float32, device=device))
+
+
+def _fp8(cache) -> FP8Cache:
+    codes, rope, scale = cache
+    assert codes.dtype == torch.uint8 and rope.dtype == torch.bfloat16 and scale.dtype == torch.float32
+    return FP8Cache(_ptr(codes), _ptr(rope), _ptr(scale))
+
+
+def append_kv_fp8(d: Dims, c_kv, k_r, pos, row, cache) -> None:
+    """A1 into the FP8 cache (codes, rope, scale): c_kv, k_r bf16."""
+    assert pos.dtype == torch.int32 and row.dtype == torch.int64 and c_kv.dtype == torch.bfloat16
+    fc = _fp8(cache)
+    _check(_lib.mla_append_kv_fp8(ctypes.byref(d), c_kv.shape[0], _ptr(c_kv), _ptr(k_r), _ptr(pos), _ptr(row),
+                                  ctypes.byref(fc), _stream(c_kv.device)), "mla_append_kv_fp8")
+
+
+def decode_partials_fp8(d: Dims, q_lat, cache, stride: int, seq_lens, max_seq_len: int, splits: int,
+                        z_part, lse_part) -> None:
+    """A3 over the FP8 cache (bf16 absorbed queries)."""
+    assert seq_lens.dtype == torch.int32 and q_lat.dtype == torch.bfloat16
+    fc = _fp8(cache)
+    _check(_lib.mla_decode_partials_fp8(ctypes.byref(d), q_lat.shape[0], _ptr(q_lat), ctypes.byref(fc), stride,
+                                        _ptr(seq_lens), max_seq_len, splits, _ptr(z_part), _ptr(lse_part),
+                                        _stream(q_lat.device)), "mla_decode_partials_fp8")
+
+
+def decode_fp8(d: Dims, q_lat, cache, stride: int, seq_lens, max_seq_len: int, w_uv, out, out_latent=None,
+               workspace=None) -> None:
+    """A3 + A4 + A5 over the FP8 cache."""
+    assert seq_lens.dtype == torch.int32 and q_lat.dtype == torch.bfloat16
+    need = decode_workspace_bytes(d, BF16, q_lat.shape[0], max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
+    fc = _fp8(cache)
+    _check(_lib.mla_decode_fp8(ctypes.byref(d), q_lat.shape[0], _ptr(q_lat), ctypes.byref(fc), stride,
+                               _ptr(seq_lens), max_seq_len, _ptr(w_uv), _ptr(out), _ptr(out_latent),
+                               _ptr(workspace), workspace.numel(), _stream(q_lat.device)), "mla_decode_fp8")

@@ -532,4 +532,105 @@ mla_status mla_prefill_unabsorbed_paged(const mla_dims* dims, mla_dtype dtype, i
   return prefill_unabsorbed_impl(dims, dtype, batch, chunk, q_c, q_r, nullptr, 0, cache, prefix_lens, max_prefix_len,
                                  w_uk, w_uv, out, workspace, workspace_bytes, stream);
 }
+static mla_status check_fp8(const mla_fp8_cache* c) {
+  if (!c) return fail(MLA_ERR_INVALID_ARGUMENT, "FP8 cache descriptor is NULL");
+  if (!c->codes || !c->rope || !c->scale) return fail(MLA_ERR_INVALID_ARGUMENT, "FP8 cache: NULL array");
+  return MLA_OK;
+}
+
+mla_status mla_append_kv_fp8(const mla_dims* dims, int32_t n_tok, const void* c_kv, const void* k_r,
+                             const int32_t* pos, const int64_t* row, const mla_fp8_cache* cache, void* stream) {
+  mla_status st = check_dims(dims, MLA_BF16);
+  if (st != MLA_OK) return st;
+  if (n_tok < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "n_tok=%d < 0", n_tok);
+  if (n_tok == 0) return MLA_OK;
+  st = check_fp8(cache);
+  if (st != MLA_OK) return st;
+  if (!c_kv || !k_r || !pos || !row) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  mla::AppendArgs a{};
+  a.c_kv = c_kv;
+  a.k_r = k_r;
+  a.pos = pos;
+  a.row = row;
+  a.cache = cache->codes;
+  a.fp8_rope = cache->rope;
+  a.fp8_scale = cache->scale;
+  a.n_tok = n_tok;
+  a.d_c = dims->d_c;
+  a.d_r = dims->d_hR;
+  fill_rope(dims, a.rope);
+  return hip_status(mla::launch_append_fp8(a, static_cast<hipStream_t>(stream)), "mla_append_kv_fp8");
+}
+
+static mla_status fp8_partials(const mla_dims* dims, int32_t batch, const void* q_lat, const mla_fp8_cache* cache,
+                               int64_t stride, const int32_t* seq_lens, int32_t max_seq_len, int32_t S, float* z,
+                               float* lse, hipStream_t s, const char* who) {
+  mla::SplitArgs a{};
+  a.q_lat = q_lat;
+  a.cache = cache->codes;
+  a.fp8_rope = cache->rope;
+  a.fp8_scale = cache->scale;
+  a.lens = seq_lens;
+  a.z_part = z;
+  a.lse_part = lse;
+  a.stride = stride;
+  a.split_rows = split_rows(max_seq_len, S);
+  a.n_q = batch;
+  a.n_h = dims->n_h;
+  a.d_c = dims->d_c;
+  a.d_r = dims->d_hR;
+  a.num_splits = S;
+  a.max_len = max_seq_len;
+  a.q_per_seq = 1;
+  a.prefill = 0;
+  a.qscale = static_cast<float>(scale_of(dims) * 1.4426950408889634);
+  return hip_status(mla::launch_splitkv_fp8(a, s), who);
+}
+
+static mla_status check_fp8_decode(const mla_dims* dims, int32_t batch, const void* q_lat, const mla_fp8_cache* cache,
+                                   int64_t stride, const int32_t* seq_lens, int32_t max_seq_len) {
+  mla_status st = check_dims(dims, MLA_BF16);
+  if (st != MLA_OK) return st;
+  if (batch < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d < 1", batch);
+  if (max_seq_len < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "max_seq_len=%d < 1", max_seq_len);
+  if (stride < max_seq_len)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "cache_seq_stride=%lld < max_seq_len=%d", (long long)stride, max_seq_len);
+  st = check_fp8(cache);
+  if (st != MLA_OK) return st;
+  if (!q_lat || !seq_lens) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  return MLA_OK;
+}
+
+mla_status mla_decode_partials_fp8(const mla_dims* dims, int32_t batch, const void* q_lat, const mla_fp8_cache* cache,
+                                   int64_t cache_seq_stride, const int32_t* seq_lens, int32_t max_seq_len,
+                                   int32_t num_splits, float* z_part, float* lse_part, void* stream) {
+  mla_status st = check_fp8_decode(dims, batch, q_lat, cache, cache_seq_stride, seq_lens, max_seq_len);
+  if (st != MLA_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "num_splits=%d out of range [1,%d]", num_splits, kMaxSplits);
+  if (!z_part || !lse_part) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  return fp8_partials(dims, batch, q_lat, cache, cache_seq_stride, seq_lens, max_seq_len, num_splits, z_part, lse_part,
+                      static_cast<hipStream_t>(stream), "mla_decode_partials_fp8");
+}
+
+mla_status mla_decode_fp8(const mla_dims* dims, int32_t batch, const void* q_lat, const mla_fp8_cache* cache,
+                          int64_t cache_seq_stride, const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv,
+                          float* out, float* out_latent, void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status st = check_fp8_decode(dims, batch, q_lat, cache, cache_seq_stride, seq_lens, max_seq_len);
+  if (st != MLA_OK) return st;
+  if (!w_uv || !out || !workspace) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const int32_t S = plan_splits(dims, MLA_BF16, batch, max_seq_len);
+  const size_t need = partial_bytes(dims, batch, S);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", workspace_bytes, need);
+  float* z = static_cast<float*>(workspace);
+  float* lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        align256(static_cast<size_t>(batch) * S * dims->n_h * dims->d_c * sizeof(float)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = fp8_partials(dims, batch, q_lat, cache, cache_seq_stride, seq_lens, max_seq_len, S, z, lse, s,
+                    "mla_decode_fp8 (partials)");
+  if (st != MLA_OK) return st;
+  mla::CombineArgs a{z, lse, w_uv, out, out_latent, batch, dims->n_h, dims->d_c, dims->d_h, S};
+  return hip_status(mla::launch_combine(a, 1, s), "mla_decode_fp8 (combine)");
+}
 }  // extern "C"

@@ -35,6 +35,9 @@ struct AppendArgs {
   void* cache;
   int32_t n_tok, d_c, d_r;
   RopeTable rope;
+  // FP8 latent cache: `cache` receives the E4M3 codes, these the RoPE keys and scales
+  void* fp8_rope;
+  float* fp8_scale;
 };
 
 // Absorbed query layout (q_lat): fp32 [n_q][n_h][d_c + d_r] for fp32 storage;
@@ -81,6 +84,10 @@ struct SplitArgs {
   int64_t num_pages;
   int32_t bt_stride;
   int32_t page_shift;          // >= 5: a page holds whole 32-row tiles
+  // FP8 latent cache: `cache` holds the E4M3 codes [rows][d_c], these the bf16
+  // RoPE keys [rows][d_r] and the per-row scales [rows]
+  const void* fp8_rope;
+  const float* fp8_scale;
 };
 
 struct CombineArgs {
@@ -150,6 +157,8 @@ hipError_t launch_splitkv(const SplitArgs& a, int bf16, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, int bf16, hipStream_t st);
 hipError_t launch_prefill_unabsorbed(const ExpandArgs& e, const PrefillArgs& p, hipStream_t st);
 hipError_t launch_kv_project_append(const KvProjArgs& a, int bf16, hipStream_t st);
+hipError_t launch_append_fp8(const AppendArgs& a, hipStream_t st);
+hipError_t launch_splitkv_fp8(const SplitArgs& a, hipStream_t st);
 // split-K plan of launch_kv_project_append: slices and k per slice (a multiple of 64)
 void kv_project_plan(int32_t n_tok, int32_t d_model, int32_t& k_slices, int32_t& k_per_slice);
 bool splitkv_has_fast_path(int n_h, int bf16, int d_c, int d_r);

@@ -39,16 +39,6 @@ namespace mla {
 
 constexpr int NQ16 = (D_C + D_R) / 32;  // 16-head score k-steps of 32 elements
 
-// Query n -> (sequence, attended length), the length clamped to [0, min(max_len, stride)].
-__device__ __forceinline__ void query_range(const SplitArgs& a, int n, int& b, int64_t& len) {
-  b = n / a.q_per_seq;
-  int64_t L = a.prefill ? static_cast<int64_t>(a.lens[b]) + (n % a.q_per_seq) + 1
-                        : static_cast<int64_t>(a.lens[b]);
-  L = min(L, static_cast<int64_t>(a.max_len));
-  L = min(L, a.stride);
-  len = max(L, static_cast<int64_t>(0));
-}
-
 template <bool PAGED>
 __device__ __forceinline__ uint64_t row_addr(const SplitArgs& a, int b, int64_t r, int64_t row_bytes, bool& ok) {
   return cache_row_addr<PAGED>(a.cache, a.block_table, a.num_pages, a.bt_stride, a.page_shift, a.stride, b, r,
@@ -958,19 +948,6 @@ __global__ __launch_bounds__(256, 1) void splitkv_h16_kernel(SplitArgs a) {
 // instance).  One workgroup per (query, split, head); 256 rows per step: one
 // thread scores one row, then every thread accumulates two latent columns.
 // ------------------------------------------------------------------------
-__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
-  for (int o = 32; o > 0; o >>= 1) {
-    const float u = __shfl_xor(v, o);
-    v = is_max ? fmaxf(v, u) : v + u;
-  }
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  v = red[0];
-  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) v = is_max ? fmaxf(v, red[i]) : v + red[i];
-  return v;
-}
 
 template <typename T, bool PAGED>
 __global__ __launch_bounds__(256) void splitkv_generic_kernel(SplitArgs a) {

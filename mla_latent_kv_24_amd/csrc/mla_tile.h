@@ -99,4 +99,29 @@ __device__ __forceinline__ uint64_t cache_row_addr(const void* cache, const int3
   }
 }
 
+// Query n -> (sequence, attended length), the length clamped to [0, min(max_len, stride)].
+__device__ __forceinline__ void query_range(const SplitArgs& a, int n, int& b, int64_t& len) {
+  b = n / a.q_per_seq;
+  int64_t L = a.prefill ? static_cast<int64_t>(a.lens[b]) + (n % a.q_per_seq) + 1
+                        : static_cast<int64_t>(a.lens[b]);
+  L = min(L, static_cast<int64_t>(a.max_len));
+  L = min(L, a.stride);
+  len = max(L, static_cast<int64_t>(0));
+}
+
+// Sum (or max) of v over the workgroup (blockDim.x a multiple of 64, up to 256).
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const float u = __shfl_xor(v, o);
+    v = is_max ? fmaxf(v, u) : v + u;
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  v = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) v = is_max ? fmaxf(v, red[i]) : v + red[i];
+  return v;
+}
+
 }  // namespace mla

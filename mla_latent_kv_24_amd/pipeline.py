@@ -35,7 +35,7 @@ class DecodeState:
     """
 
     def __init__(self, inp: DecodeInputs, device="cuda", out_latent=False, page_rows=None,
-                 spare_pages=0, table_seed=0):
+                 spare_pages=0, table_seed=0, fp8=False):
         w = inp.w
         self.inp = inp
         self.device = device
@@ -47,7 +47,17 @@ class DecodeState:
         self.max_len = int(lens.max())
         self.total_rows = int(lens.sum())
         self.page_rows = page_rows
-        if page_rows is None:
+        self.fp8 = fp8
+        if fp8:
+            # FP8 latent cache (codes, RoPE keys, scales), rows as the contiguous layout
+            assert page_rows is None and w.dtype == "bf16"
+            self.cache = api.fp8_cache_empty(self.batch * self.stride, device=device)
+            self.cache[0].fill_(0x7F)                   # NaN codes past every length
+            self.cache[1].fill_(float("nan"))
+            self.cache[2].fill_(float("nan"))
+            self.block_table = None
+            row_of = lambda b, j: np.asarray(b, dtype=np.int64) * self.stride + np.asarray(j, dtype=np.int64)
+        elif page_rows is None:
             self.cache = torch.full((self.batch * self.stride, ROW), float("nan"), dtype=tdt, device=device)
             self.block_table = None
             row_of = lambda b, j: np.asarray(b, dtype=np.int64) * self.stride + np.asarray(j, dtype=np.int64)
@@ -87,12 +97,18 @@ class DecodeState:
     def _api_dtype(self):
         return api.BF16 if self.dt == "bf16" else api.F32
 
+    def _append(self, c, k, pos, rows):
+        if self.fp8:
+            api.append_kv_fp8(self.d, c, k, pos, rows, self.cache)
+        else:
+            api.append_kv(self.d, c, k, pos, rows, self.cache)
+
     def fill_cache(self):
-        api.append_kv(self.d, self.fill_c, self.fill_k, self.fill_pos, self.fill_rows, self.cache)
+        self._append(self.fill_c, self.fill_k, self.fill_pos, self.fill_rows)
 
     # --- the steps of one decode pass (A1, A2, A3, A4+A5)
     def append_new(self):
-        api.append_kv(self.d, self.new_c, self.new_k, self.new_pos, self.new_rows, self.cache)
+        self._append(self.new_c, self.new_k, self.new_pos, self.new_rows)
 
     def absorb(self):
         api.absorb_q(self.d, self.q_c, self.q_r, self.q_pos, self.w_uk, self.q_lat)
@@ -101,7 +117,10 @@ class DecodeState:
         S = self.splits if splits is None else splits
         z = self.z_part if z_part is None else z_part
         lse = self.lse_part if lse_part is None else lse_part
-        if self.block_table is None:
+        if self.fp8:
+            api.decode_partials_fp8(self.d, self.q_lat, self.cache, self.stride, self.seq_lens, self.max_len,
+                                    S, z, lse)
+        elif self.block_table is None:
             api.decode_partials(self.d, self.q_lat, self.cache, self.stride, self.seq_lens, self.max_len,
                                 S, z, lse)
         else:

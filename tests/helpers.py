@@ -6,6 +6,14 @@ from mla_latent_kv_24_amd import workloads as W
 
 TOL = {"bf16": 2e-2, "f32": 1e-4}   # max|gpu - ref| / rms(ref), per workload output
 
+# Short contexts (tens to a hundred rows) sit closer to the bf16 noise floor: the
+# three storage roundings of the path (absorbed query, cached RoPE key, softmax
+# weights P; each a relative 2^-9 perturbation) give a max|err|/rms of about
+# 2.5e-2 over 1M outputs at 100-165 rows, against about 1e-2 at 4-8K rows (fp64
+# emulation of exactly those roundings); the bf16 decode kernel's latent output
+# over 5 sequences of 65 rows measures 2.05e-2.  Config-shaped cases keep 2e-2.
+SHORT_CONTEXT_TOL = 4e-2
+
 
 def rel_err(gpu, ref):
     gpu = np.asarray(gpu, dtype=np.float64)
@@ -64,3 +72,18 @@ def absorbed_layout(q32, dtype):
     pair = np.stack([hi, lo], axis=-2)
     value = W.bf16_bits_to_f32(hi).astype(np.float64) + W.bf16_bits_to_f32(lo).astype(np.float64)
     return pair, value
+
+
+def oracle_decode_fp8(inp, b, heads=None):
+    """fp64 oracle for sequence b over the FP8 latent cache: the oracle's own
+    E4M3 codes and per-row scales of c^KV (dequantised exactly), the RoPE key
+    rounded to bf16 as stored.  Absorbed form (pinned to the unabsorbed one)."""
+    L = int(inp.seq_lens[b])
+    heads = np.arange(inp.w.n_h) if heads is None else np.asarray(heads)
+    codes, scale = O.quantize_rows_fp8(f64(inp.c_kv[b, :L], "bf16"))
+    c = O.dequantize_rows_fp8(codes, scale)
+    k_rot = O.cached_rope_key(f64(inp.k_raw[b, :L], "bf16"), np.arange(L), inp.w.rope_base, store="bf16")
+    q_rot = O.rope(f64(inp.q_r[b][heads], "bf16"), L - 1, inp.w.rope_base)
+    o, z, _ = O.attend_absorbed(f64(inp.q_c[b][heads], "bf16"), q_rot, c, k_rot, f64(inp.w_uk[heads], "bf16"),
+                                f64(inp.w_uv[heads], "bf16"))
+    return o, z

@@ -1,0 +1,124 @@
+"""GPU tests of the FP8 latent cache: A1's codes and scales bit for bit
+against the oracle's quantiser (both decide in fp32), and decode over the
+quantised cache against the oracle over its own dequantised rows, at the
+bf16 bar (the codes are shared, so the bar covers only the kernel's own
+roundings, as on the bf16 path)."""
+import numpy as np
+import pytest
+
+import oracle as O
+from mla_latent_kv_24_amd import workloads as W
+from helpers import SHORT_CONTEXT_TOL, TOL, f64, oracle_decode, oracle_decode_fp8, rel_err, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def api():
+    from mla_latent_kv_24_amd import api as A
+    return A
+
+
+@pytest.fixture(scope="module")
+def pipeline():
+    from mla_latent_kv_24_amd import pipeline as P
+    return P
+
+
+def dev(a, dtype):
+    from mla_latent_kv_24_amd.pipeline import to_device
+    return to_device(a, dtype)
+
+
+def test_append_fp8_codes_and_scales_bit_exact(api):
+    n, cap = 700, 1000
+    r = np.random.default_rng(60)
+    c = r.standard_normal((n, 512)).astype(np.float32) * r.choice([1e-3, 1.0, 40.0], (n, 1)).astype(np.float32)
+    c[0] = 0.0                                          # zero row: scale 1, codes 0
+    c[1] = 0.0
+    c[1, 17] = -3.0                                     # one element: it maps to -448
+    c[2] = -c[2]
+    c[3, ::2] = -0.0                                    # negative zeros keep their sign
+    c = W.to_storage(c, "bf16")
+    k = W.random_storage(61, (n, 64), "bf16")
+    pos = W.random_ints(62, 0, 131072, n).astype(np.int32)
+    rows = r.permutation(cap)[:n].astype(np.int64)
+    d = api.dims(128)
+    cache = api.fp8_cache_empty(cap)
+    cache[0].fill_(0x7F)
+    cache[1].fill_(float("nan"))
+    cache[2].fill_(float("nan"))
+    api.append_kv_fp8(d, dev(c, "bf16"), dev(k, "bf16"), torch.from_numpy(pos).cuda(), torch.from_numpy(rows).cuda(),
+                      cache)
+    torch.cuda.synchronize()
+    codes = cache[0].cpu().numpy()[rows]
+    scale = cache[2].cpu().numpy()[rows]
+    ref_codes, ref_scale = O.quantize_rows_fp8(f64(c, "bf16"))
+    assert np.array_equal(scale.view(np.uint32), ref_scale.view(np.uint32))
+    assert np.array_equal(codes, ref_codes)
+    assert scale[0] == 1.0 and np.all(codes[0] == 0) and codes[1, 17] == 0xFE
+    # the RoPE half: one rounding of the exact rotation to bf16
+    ref_k = O.cached_rope_key(f64(k, "bf16"), pos, 10000.0)
+    got_k = f64(to_np(cache[1])[rows], "bf16")
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref_k), 1e-30))) - 7)
+    assert np.all(np.abs(got_k - ref_k) <= ulp + 1e-30)
+    untouched = np.setdiff1d(np.arange(cap), rows)
+    assert np.all(cache[0].cpu().numpy()[untouched] == 0x7F)
+
+
+# 128 heads and 16 heads (matrix-core kernels) at several lengths, ragged
+# tails and ragged batches; 32 heads (generic kernel)
+CASES = [("v2_decode", dict(batch=3, seq_len=1000)), ("v2_decode", dict(batch=2, seq_len=4099)),
+         ("v2_decode", dict(batch=5, seq_len=65)), ("v2_decode", dict(batch=1, seq_len=1)),
+         ("v2_decode", dict(batch=2, seq_len=33)), ("lite_decode", dict(batch=3, seq_len=300)),
+         ("lite_decode", dict(batch=2, seq_len=4113)), ("lite_decode", dict(batch=3, seq_len=17)),
+         ("lite_ragged", dict(batch=6, seq_len=3000)), ("lite_decode", dict(batch=2, seq_len=300, n_h=32))]
+
+
+@pytest.mark.parametrize("name,changes", CASES, ids=[f"{c[0]}-{c[1]['batch']}x{c[1]['seq_len']}-h{c[1].get('n_h', '')}" for c in CASES])
+def test_decode_fp8(pipeline, name, changes):
+    w = W.scaled(W.WORKLOADS[name], **changes)
+    inp = W.make_decode_inputs(w)
+    print(f"fp8 decode {name} {changes}", flush=True)
+    st = pipeline.DecodeState(inp, out_latent=True, fp8=True)
+    st.absorb()
+    st.attention()
+    st.combine()
+    out = st.out.cpu().numpy()
+    lat = st.out_latent.cpu().numpy()
+    assert np.all(np.isfinite(out))                       # NaN codes past every length are never read
+    refs = [oracle_decode_fp8(inp, b) for b in range(w.batch)]
+    # the bf16 path's own bars: the short-context one below 256 rows (the same
+    # roundings; on the 5 x 65 case the bf16 kernel's latent is at 2.05e-2)
+    tol = TOL["bf16"] if w.seq_len >= 256 else SHORT_CONTEXT_TOL
+    e_out = rel_err(out, np.stack([r[0] for r in refs]))
+    e_lat = rel_err(lat, np.stack([r[1] for r in refs]))
+    print(f"fp8 parity: out {e_out:.3e}, latent {e_lat:.3e} (bar {tol})")
+    assert e_out < tol and e_lat < tol
+    # what the quantisation itself costs, against the bf16 cache's exact output
+    # (informational; E4M3 rounds each latent element by up to 2^-4 relative,
+    # about 3.6% rms, and the output's rms deviation is of that size)
+    exact = np.stack([oracle_decode(inp, b, absorbed=True)[0] for b in range(w.batch)])
+    q_rms = float(np.sqrt(np.mean((out - exact) ** 2)) / np.sqrt(np.mean(exact ** 2)))
+    print(f"fp8 cache vs exact bf16-cache output: max {rel_err(out, exact):.3e}, rms {q_rms:.3e}")
+    assert q_rms < 0.06
+
+
+def test_decode_fp8_fused_equals_partials(api, pipeline):
+    w = W.scaled(W.WORKLOADS["v2_decode"], batch=4, seq_len=2000)
+    st = pipeline.DecodeState(W.make_decode_inputs(w), out_latent=True, fp8=True)
+    st.absorb()
+    st.attention()
+    st.combine()
+    torch.cuda.synchronize()
+    out = torch.empty_like(st.out)
+    lat = torch.empty_like(st.out_latent)
+    api.decode_fp8(st.d, st.q_lat, st.cache, st.stride, st.seq_lens, st.max_len, st.w_uv, out, lat)
+    torch.cuda.synchronize()
+    assert torch.equal(out, st.out) and torch.equal(lat, st.out_latent)
+    # deterministic across calls
+    api.decode_fp8(st.d, st.q_lat, st.cache, st.stride, st.seq_lens, st.max_len, st.w_uv, out, lat)
+    torch.cuda.synchronize()
+    assert torch.equal(out, st.out)
