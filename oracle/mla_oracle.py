@@ -49,6 +49,10 @@ no body, and no page defines RoPE itself):
     (the one W^UK and W^UV consume); k^R is not normalised.  Both halves of
     the row are rounded to the storage dtype once, from their exact values.
 
+  * Query side: c^Q = RMSNorm(W^DQ h) * weight over the d_c' = 1,536 query
+    latent channels (as for c^KV), q^C = W^UQ c^Q and the decoupled RoPE
+    query q^R = W^QR c^Q (no page prints W^QR; the per-head 64-d RoPE query of
+    [R3] is read as coming from the query latent), RoPE applied at absorption.
   * Quantised latent cache (the pages report a cache of about 6 bits per
     element for the served model -- review section 4 -- without giving a
     format): c^KV is stored as FP8 E4M3 (the OCP 8-bit float: 1 sign, 4
@@ -172,6 +176,35 @@ def append_rows_from_hidden(h, w_dkv, w_kr, pos, norm_weight=None, eps: float = 
     c, k_raw = kv_from_hidden(h, w_dkv, w_kr, norm_weight, eps)
     rows = append_rows(c, k_raw, pos, base)
     return rows if store is None else round_to_storage(rows, store)
+
+
+# ---------------------------------------------------------------------------
+# The projections around the path: the query side ([R2] queries pass through a
+# 1,536-wide latent; [V3] c^Q; the latent normalised as c^KV is, [R2]) and the
+# output side ([R2] u_t = sum_i O_i U^V_i sum_j a_ij c_j)
+# ---------------------------------------------------------------------------
+def query_from_hidden(h, w_dq, w_uq, w_qr, n_h: int, norm_weight=None, eps: float = 1e-6):
+    """(q^C [N, n_h, d_h], q^R [N, n_h, d_h^R] before RoPE) of hidden states h [N, d_model]:
+    c^Q = RMSNorm(W^DQ h) * norm_weight (w_dq [d_c', d_model]),
+    q^C = W^UQ c^Q (w_uq [n_h d_h, d_c'], head i = rows i d_h ..), q^R = W^QR c^Q
+    (w_qr [n_h d_h^R, d_c'])."""
+    h = np.asarray(h, dtype=np.float64)
+    c_q = rms_norm(h @ np.asarray(w_dq, dtype=np.float64).T, norm_weight, eps)
+    q_c = c_q @ np.asarray(w_uq, dtype=np.float64).T
+    q_r = c_q @ np.asarray(w_qr, dtype=np.float64).T
+    return q_c.reshape(h.shape[0], n_h, -1), q_r.reshape(h.shape[0], n_h, -1)
+
+
+def output_projection(o, w_o) -> np.ndarray:
+    """u_t = sum_i O_i o_{t,i} with o [N, n_h, d_h] and w_o [d_model, n_h d_h],
+    O_i = columns i d_h .. (i+1) d_h - 1 of w_o."""
+    o = np.asarray(o, dtype=np.float64)
+    w_o = np.asarray(w_o, dtype=np.float64)
+    n_h, d_h = o.shape[1], o.shape[2]
+    u = np.zeros((o.shape[0], w_o.shape[0]))
+    for i in range(n_h):
+        u += o[:, i, :] @ w_o[:, i * d_h:(i + 1) * d_h].T
+    return u
 
 
 # ---------------------------------------------------------------------------

@@ -540,3 +540,60 @@ def test_quantize_rows_fp8_properties():
     step = np.maximum(np.abs(deq) * 2.0 ** -3, 2.0 ** -9 * scale[:, None])   # one E4M3 step at that value
     assert np.all(np.abs(deq - c) <= 0.5 * step * (1 + 1e-6) + 1e-12)
     assert np.all(np.sign(deq) * np.sign(c) >= 0)
+
+
+# --------------------------------------------- projections around the path ([R2], [V3])
+def test_query_from_hidden_bruteforce():
+    """Tiny dims against pure-Python loops: c^Q_o = norm(sum_k W^DQ[o][k] h[k]),
+    q^C_{i,d} = sum_o W^UQ[i d_h + d][o] c^Q_o, q^R likewise with W^QR."""
+    r = _rng(47)
+    N, D, CQ, H, DH, DR, eps = 2, 6, 4, 2, 3, 2, 1e-3
+    h = r.standard_normal((N, D))
+    w_dq = r.standard_normal((CQ, D))
+    w_uq = r.standard_normal((H * DH, CQ))
+    w_qr = r.standard_normal((H * DR, CQ))
+    g = r.uniform(0.5, 1.5, CQ)
+    q_c, q_r = O.query_from_hidden(h, w_dq, w_uq, w_qr, H, g, eps)
+    assert q_c.shape == (N, H, DH) and q_r.shape == (N, H, DR)
+    for t in range(N):
+        lat = [sum(w_dq[o][k] * h[t][k] for k in range(D)) for o in range(CQ)]
+        inv = 1.0 / math.sqrt(sum(v * v for v in lat) / CQ + eps)
+        cq = [lat[o] * inv * g[o] for o in range(CQ)]
+        for i in range(H):
+            for d in range(DH):
+                assert abs(q_c[t][i][d] - sum(w_uq[i * DH + d][o] * cq[o] for o in range(CQ))) < 1e-12
+            for d in range(DR):
+                assert abs(q_r[t][i][d] - sum(w_qr[i * DR + d][o] * cq[o] for o in range(CQ))) < 1e-12
+
+
+def test_query_from_hidden_is_scale_free():
+    """With eps = 0 the normalised query latent ignores the scale of h, so both
+    queries do too; doubling W^UQ doubles q^C and leaves q^R."""
+    r = _rng(48)
+    h = r.standard_normal((3, 32))
+    w_dq, w_uq, w_qr = r.standard_normal((16, 32)), r.standard_normal((4 * 8, 16)), r.standard_normal((4 * 2, 16))
+    a = O.query_from_hidden(h, w_dq, w_uq, w_qr, 4, None, 0.0)
+    b = O.query_from_hidden(5.0 * h, w_dq, w_uq, w_qr, 4, None, 0.0)
+    c = O.query_from_hidden(h, w_dq, 2.0 * w_uq, w_qr, 4, None, 0.0)
+    assert np.allclose(a[0], b[0], rtol=1e-13, atol=1e-13) and np.allclose(a[1], b[1], rtol=1e-13, atol=1e-13)
+    assert np.allclose(c[0], 2.0 * a[0], rtol=1e-13, atol=0) and np.array_equal(c[1], a[1])
+
+
+def test_output_projection_bruteforce_and_head_blocks():
+    """u_t[m] = sum_i sum_d W^O[m][i d_h + d] o_{t,i,d} (loops), which is the
+    flat product o_t . W^O^T with heads laid out in order; a head's block moves
+    only that head's contribution."""
+    r = _rng(49)
+    N, H, DH, DM = 2, 3, 4, 5
+    o = r.standard_normal((N, H, DH))
+    w_o = r.standard_normal((DM, H * DH))
+    u = O.output_projection(o, w_o)
+    for t in range(N):
+        for m in range(DM):
+            ref = sum(w_o[m][i * DH + d] * o[t][i][d] for i in range(H) for d in range(DH))
+            assert abs(u[t][m] - ref) < 1e-12
+    w2 = w_o.copy()
+    w2[:, DH:2 * DH] = 0.0                                       # drop head 1's block
+    o1 = np.zeros_like(o)
+    o1[:, 1] = o[:, 1]
+    assert np.allclose(O.output_projection(o, w2), u - O.output_projection(o1, w_o), rtol=0, atol=1e-12)
