@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 6
+#define MLA_ABI_VERSION 7
 
 typedef enum {
   MLA_OK = 0,
@@ -125,6 +125,42 @@ mla_status mla_append_kv_from_hidden(const mla_dims* dims, mla_dtype dtype, int3
 mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q,
                         const void* q_c, const void* q_r, const int32_t* q_pos,
                         const void* w_uk, void* q_lat, void* stream);
+
+/* The query path from hidden states into A2 (review section 2: queries pass
+ * through a 1,536-wide latent; DeepSeek-V3 report, Metode 1: c^Q; the latent
+ * normalised as c^KV is):
+ *   c^Q = RMSNorm(W^DQ h) * norm_weight,  q^C = W^UQ c^Q,  q^R = W^QR c^Q,
+ *   then q_lat = A2(q^C, q^R, q_pos, w_uk) exactly as mla_absorb_q.
+ *   h [n_q][d_model], w_dq [d_cq][d_model], norm_weight [d_cq] or NULL,
+ *   w_uq [n_h * d_h][d_cq] (head i = rows i*d_h ..), w_qr [n_h * d_hR][d_cq],
+ *   all bf16; q_pos, w_uk, q_lat as mla_absorb_q (bf16 layout).
+ * c^Q and q^C pass between the launches as bf16 (fp32 sums, one rounding
+ * each: they are matrix-core operands), q^R as fp32, in `workspace`
+ * (mla_absorb_q_from_hidden_workspace_bytes).
+ * n_q in [0, 65535] (0: no-op), d_cq <= 4096; the matrix-core kernels need
+ * d_model and d_cq to be multiples of 128, other shapes run generic kernels.
+ * W^UQ and W^UK are applied in turn, not composed: a composed per-head
+ * [d_cq][d_c] matrix would hold three times the bytes of the two factors. */
+size_t mla_absorb_q_from_hidden_workspace_bytes(const mla_dims* dims, int32_t n_q,
+                                                int32_t d_model, int32_t d_cq);
+mla_status mla_absorb_q_from_hidden(const mla_dims* dims, int32_t n_q, int32_t d_model,
+                                    int32_t d_cq, const void* h, const void* w_dq,
+                                    const void* norm_weight, double eps, const void* w_uq,
+                                    const void* w_qr, const int32_t* q_pos, const void* w_uk,
+                                    void* q_lat, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* The output projection after A5 (review section 2: u_t = sum_i O_i U^V_i
+ * sum_j a_ij c_j):  out[t] = W^O o_t, o [n_q][n_h][d_h] fp32 (A5's output),
+ * w_o [d_model][n_h * d_h] bf16 (O_i = columns i*d_h ..), out [n_q][d_model]
+ * fp32.  o is rounded once to bf16 for the matrix cores; the sums are fp32.
+ * workspace: mla_output_projection_workspace_bytes().  n_q in [0, 65535].
+ * W^O is applied after the lift, not folded into W^UV: O_i U^V_i would be a
+ * [d_model][d_c] matrix per head, four times the bytes of the two factors. */
+size_t mla_output_projection_workspace_bytes(const mla_dims* dims, int32_t n_q, int32_t d_model);
+mla_status mla_output_projection(const mla_dims* dims, int32_t n_q, int32_t d_model,
+                                 const float* o, const void* w_o, float* out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* Split-KV plan.  Sequence rows [0, len) are cut into `num_splits` ranges of
  * mla_split_rows(max_seq_len, num_splits) rows each (split s covers

@@ -69,6 +69,11 @@ _SIGS = {
     "mla_append_kv_from_hidden_workspace_bytes": (_sz, [_P, ctypes.c_int, _i32, _i32]),
     "mla_append_kv_from_hidden": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _vp,
                                                  ctypes.c_double, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mla_absorb_q_from_hidden_workspace_bytes": (_sz, [_P, _i32, _i32, _i32]),
+    "mla_absorb_q_from_hidden": (ctypes.c_int, [_P, _i32, _i32, _i32, _vp, _vp, _vp, ctypes.c_double, _vp, _vp,
+                                                _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mla_output_projection_workspace_bytes": (_sz, [_P, _i32, _i32]),
+    "mla_output_projection": (ctypes.c_int, [_P, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mla_absorb_q": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mla_decode_num_splits": (_i32, [_P, ctypes.c_int, _i32, _i32]),
     "mla_split_rows": (_i64, [_i32, _i32]),
@@ -377,3 +382,29 @@ def decode_fp8(d: Dims, q_lat, cache, stride: int, seq_lens, max_seq_len: int, w
     _check(_lib.mla_decode_fp8(ctypes.byref(d), q_lat.shape[0], _ptr(q_lat), ctypes.byref(fc), stride,
                                _ptr(seq_lens), max_seq_len, _ptr(w_uv), _ptr(out), _ptr(out_latent),
                                _ptr(workspace), workspace.numel(), _stream(q_lat.device)), "mla_decode_fp8")
+
+
+def absorb_q_from_hidden(d: Dims, h, w_dq, norm_weight, eps: float, w_uq, w_qr, q_pos, w_uk, q_lat,
+                         workspace=None) -> None:
+    """The query path into A2: c^Q = RMSNorm(w_dq @ h) * norm_weight, q^C = w_uq @ c^Q,
+    q^R = w_qr @ c^Q, then absorb_q (bf16 throughout; h [n_q, d_model], w_dq [d_cq, d_model])."""
+    assert q_pos.dtype == torch.int32 and h.dtype == torch.bfloat16
+    n_q, d_model = h.shape
+    d_cq = w_dq.shape[0]
+    if workspace is None:
+        need = _lib.mla_absorb_q_from_hidden_workspace_bytes(ctypes.byref(d), n_q, d_model, d_cq)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
+    _check(_lib.mla_absorb_q_from_hidden(ctypes.byref(d), n_q, d_model, d_cq, _ptr(h), _ptr(w_dq), _ptr(norm_weight),
+                                         float(eps), _ptr(w_uq), _ptr(w_qr), _ptr(q_pos), _ptr(w_uk), _ptr(q_lat),
+                                         _ptr(workspace), workspace.numel(), _stream(h.device)),
+           "mla_absorb_q_from_hidden")
+
+
+def output_projection(d: Dims, o, w_o, out, workspace=None) -> None:
+    """out [n_q, d_model] = W^O o for o [n_q, n_h, d_h] fp32 and w_o [d_model, n_h * d_h] bf16."""
+    n_q, d_model = out.shape
+    if workspace is None:
+        need = _lib.mla_output_projection_workspace_bytes(ctypes.byref(d), n_q, d_model)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=out.device)
+    _check(_lib.mla_output_projection(ctypes.byref(d), n_q, d_model, _ptr(o), _ptr(w_o), _ptr(out), _ptr(workspace),
+                                      workspace.numel(), _stream(out.device)), "mla_output_projection")

@@ -165,7 +165,7 @@ size_t mla_append_kv_from_hidden_workspace_bytes(const mla_dims* dims, mla_dtype
                                                  int32_t d_model) {
   if (check_dims(dims, dtype) != MLA_OK || n_tok < 1 || d_model < 1) return 0;
   int32_t slices = 1, kr = 0;
-  mla::kv_project_plan(n_tok, d_model, slices, kr);
+  mla::gemm_plan(n_tok, d_model, mla::ROWE, slices, kr);
   return static_cast<size_t>(slices) * n_tok * mla::ROWE * sizeof(float);
 }
 
@@ -196,25 +196,18 @@ mla_status mla_append_kv_from_hidden(const mla_dims* dims, mla_dtype dtype, int3
   a.part = static_cast<float*>(workspace);
   a.n_tok = n_tok;
   a.d_model = d_model;
-  mla::kv_project_plan(n_tok, d_model, a.k_slices, a.k_per_slice);
+  mla::gemm_plan(n_tok, d_model, mla::ROWE, a.k_slices, a.k_per_slice);
   a.eps = static_cast<float>(eps);
   fill_rope(dims, a.rope);
   return hip_status(mla::launch_kv_project_append(a, dtype == MLA_BF16, static_cast<hipStream_t>(stream)),
                     "mla_append_kv_from_hidden");
 }
 
-mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q, const void* q_c,
-                        const void* q_r, const int32_t* q_pos, const void* w_uk, void* q_lat,
-                        void* stream) {
-  mla_status st = check_dims(dims, dtype);
-  if (st != MLA_OK) return st;
-  if (n_q < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "n_q=%d < 0", n_q);
-  if (n_q == 0) return MLA_OK;
-  if (n_q > 65535 * 256) return fail(MLA_ERR_INVALID_ARGUMENT, "n_q=%d too large", n_q);
-  if (!q_c || !q_r || !q_pos || !w_uk || !q_lat) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  const int bf = dtype == MLA_BF16;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+static mla_status absorb_launch(const mla_dims* dims, int bf, int32_t n_q, const void* q_c, const void* q_r,
+                                const int32_t* q_pos, const void* w_uk, void* q_lat, hipStream_t s, const char* who,
+                                int q_r_f32 = 0) {
   mla::AbsorbArgs a{};
+  a.q_r_f32 = q_r_f32;
   a.q_c = q_c;
   a.w_uk = w_uk;
   a.q_lat = q_lat;
@@ -226,7 +219,7 @@ mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q, cons
   a.q_r = q_r;
   a.q_pos = q_pos;
   fill_rope(dims, a.rope);
-  mla_status r = hip_status(mla::launch_absorb(a, bf, s), "mla_absorb_q (latent)");
+  mla_status r = hip_status(mla::launch_absorb(a, bf, s), who);
   if (r != MLA_OK || mla::absorb_fuses_rope(bf, dims->d_c, dims->d_h, dims->d_hR)) return r;
   mla::RopeQArgs ra{};
   ra.q_r = q_r;
@@ -237,7 +230,150 @@ mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q, cons
   ra.d_c = dims->d_c;
   ra.d_r = dims->d_hR;
   fill_rope(dims, ra.rope);
-  return hip_status(mla::launch_rope_q(ra, bf, s), "mla_absorb_q (rope)");
+  return hip_status(mla::launch_rope_q(ra, bf, s), who);
+}
+
+mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q, const void* q_c, const void* q_r,
+                        const int32_t* q_pos, const void* w_uk, void* q_lat, void* stream) {
+  mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  if (n_q < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "n_q=%d < 0", n_q);
+  if (n_q == 0) return MLA_OK;
+  if (n_q > 65535 * 256) return fail(MLA_ERR_INVALID_ARGUMENT, "n_q=%d too large", n_q);
+  if (!q_c || !q_r || !q_pos || !w_uk || !q_lat) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  return absorb_launch(dims, dtype == MLA_BF16, n_q, q_c, q_r, q_pos, w_uk, q_lat, static_cast<hipStream_t>(stream),
+                       "mla_absorb_q");
+}
+
+// ---- the query path from hidden states: c^Q = RMSNorm(W^DQ h), [q^C ; q^R] =
+// [W^UQ ; W^QR] c^Q, then A2.  Workspace: slices of W^DQ h (fp32), c^Q and q^C
+// (bf16: matrix-core operands), q^R (fp32: only rotated).
+struct QPathLayout {
+  int32_t slices, kps;
+  size_t part, cq, qc, qr, total;
+};
+static QPathLayout qpath_layout(const mla_dims* d, int32_t n_q, int32_t d_model, int32_t d_cq) {
+  QPathLayout L{};
+  mla::gemm_plan(n_q, d_model, d_cq, L.slices, L.kps);
+  L.part = 0;
+  L.cq = align256(static_cast<size_t>(L.slices) * n_q * d_cq * sizeof(float));
+  L.qc = L.cq + align256(static_cast<size_t>(n_q) * d_cq * 2);
+  L.qr = L.qc + align256(static_cast<size_t>(n_q) * d->n_h * d->d_h * 2);
+  L.total = L.qr + align256(static_cast<size_t>(n_q) * d->n_h * d->d_hR * sizeof(float));
+  return L;
+}
+
+size_t mla_absorb_q_from_hidden_workspace_bytes(const mla_dims* dims, int32_t n_q, int32_t d_model, int32_t d_cq) {
+  if (check_dims(dims, MLA_BF16) != MLA_OK || n_q < 1 || d_model < 1 || d_cq < 1) return 0;
+  return qpath_layout(dims, n_q, d_model, d_cq).total;
+}
+
+mla_status mla_absorb_q_from_hidden(const mla_dims* dims, int32_t n_q, int32_t d_model, int32_t d_cq, const void* h,
+                                    const void* w_dq, const void* norm_weight, double eps, const void* w_uq,
+                                    const void* w_qr, const int32_t* q_pos, const void* w_uk, void* q_lat,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status st = check_dims(dims, MLA_BF16);
+  if (st != MLA_OK) return st;
+  if (n_q < 0 || n_q > 65535) return fail(MLA_ERR_INVALID_ARGUMENT, "n_q=%d out of range [0,65535]", n_q);
+  if (n_q == 0) return MLA_OK;
+  if (d_model < 1 || d_model > (1 << 20)) return fail(MLA_ERR_INVALID_ARGUMENT, "d_model=%d out of range", d_model);
+  if (d_cq < 1 || d_cq > 4096) return fail(MLA_ERR_INVALID_ARGUMENT, "d_cq=%d out of range [1,4096]", d_cq);
+  if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(MLA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (!h || !w_dq || !w_uq || !w_qr || !q_pos || !w_uk || !q_lat || !workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const QPathLayout L = qpath_layout(dims, n_q, d_model, d_cq);
+  if (workspace_bytes < L.total)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", workspace_bytes, L.total);
+  char* ws = static_cast<char*>(workspace);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  uint16_t* cq = reinterpret_cast<uint16_t*>(ws + L.cq);
+  uint16_t* qc = reinterpret_cast<uint16_t*>(ws + L.qc);
+  float* qr = reinterpret_cast<float*>(ws + L.qr);   // q^R stays fp32 up to its rotation
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  mla::GemmArgs g1{};
+  g1.x = h;
+  g1.w0 = w_dq;
+  g1.part = part;
+  g1.n = n_q;
+  g1.d_in = d_model;
+  g1.d_out = d_cq;
+  g1.split = d_cq;
+  g1.k_slices = L.slices;
+  g1.k_per_slice = L.kps;
+  st = hip_status(mla::launch_gemm_partial(g1, 1, s), "mla_absorb_q_from_hidden (W^DQ)");
+  if (st != MLA_OK) return st;
+  st = hip_status(mla::launch_rmsnorm_rows(part, L.slices, n_q, d_cq, norm_weight, static_cast<float>(eps), cq, s),
+                  "mla_absorb_q_from_hidden (RMSNorm)");
+  if (st != MLA_OK) return st;
+  mla::GemmArgs g2{};
+  g2.x = cq;
+  g2.w0 = w_uq;
+  g2.w1 = w_qr;
+  g2.out0 = qc;
+  g2.out1_f32 = qr;
+  g2.n = n_q;
+  g2.d_in = d_cq;
+  g2.d_out = dims->n_h * (dims->d_h + dims->d_hR);
+  g2.split = dims->n_h * dims->d_h;
+  g2.k_slices = 1;
+  g2.k_per_slice = (d_cq + 127) / 128 * 128;
+  st = hip_status(mla::launch_gemm_partial(g2, 1, s), "mla_absorb_q_from_hidden (W^UQ, W^QR)");
+  if (st != MLA_OK) return st;
+  return absorb_launch(dims, 1, n_q, qc, qr, q_pos, w_uk, q_lat, s, "mla_absorb_q_from_hidden (absorb)", 1);
+}
+
+// ---- the output projection: u = W^O o (o rounded once to bf16 for the matrix cores)
+struct OutLayout {
+  int32_t slices, kps;
+  size_t o16, part, total;
+};
+static OutLayout out_layout(const mla_dims* d, int32_t n_q, int32_t d_model) {
+  OutLayout L{};
+  const int32_t d_in = d->n_h * d->d_h;
+  mla::gemm_plan(n_q, d_in, d_model, L.slices, L.kps);
+  L.o16 = 0;
+  L.part = align256(static_cast<size_t>(n_q) * d_in * 2);
+  L.total = L.part + (L.slices > 1 ? align256(static_cast<size_t>(L.slices) * n_q * d_model * sizeof(float)) : 0);
+  return L;
+}
+
+size_t mla_output_projection_workspace_bytes(const mla_dims* dims, int32_t n_q, int32_t d_model) {
+  if (check_dims(dims, MLA_BF16) != MLA_OK || n_q < 1 || d_model < 1) return 0;
+  return out_layout(dims, n_q, d_model).total;
+}
+
+mla_status mla_output_projection(const mla_dims* dims, int32_t n_q, int32_t d_model, const float* o, const void* w_o,
+                                 float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status st = check_dims(dims, MLA_BF16);
+  if (st != MLA_OK) return st;
+  if (n_q < 0 || n_q > 65535) return fail(MLA_ERR_INVALID_ARGUMENT, "n_q=%d out of range [0,65535]", n_q);
+  if (n_q == 0) return MLA_OK;
+  if (d_model < 1 || d_model > (1 << 20)) return fail(MLA_ERR_INVALID_ARGUMENT, "d_model=%d out of range", d_model);
+  if (!o || !w_o || !out || !workspace) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const OutLayout L = out_layout(dims, n_q, d_model);
+  if (workspace_bytes < L.total)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", workspace_bytes, L.total);
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* o16 = reinterpret_cast<uint16_t*>(ws + L.o16);
+  float* part = (L.slices > 1) ? reinterpret_cast<float*>(ws + L.part) : out;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t n_in = static_cast<int64_t>(n_q) * dims->n_h * dims->d_h;
+  st = hip_status(mla::launch_to_bf16(o, n_in, o16, s), "mla_output_projection (bf16)");
+  if (st != MLA_OK) return st;
+  mla::GemmArgs g{};
+  g.x = o16;
+  g.w0 = w_o;
+  g.part = part;
+  g.n = n_q;
+  g.d_in = dims->n_h * dims->d_h;
+  g.d_out = d_model;
+  g.split = d_model;
+  g.k_slices = L.slices;
+  g.k_per_slice = L.kps;
+  st = hip_status(mla::launch_gemm_partial(g, 1, s), "mla_output_projection (W^O)");
+  if (st != MLA_OK || L.slices == 1) return st;
+  return hip_status(mla::launch_sum_slices(part, L.slices, static_cast<int64_t>(n_q) * d_model, out, s),
+                    "mla_output_projection (slices)");
 }
 
 int32_t mla_decode_num_splits(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t max_seq_len) {

@@ -59,6 +59,7 @@ struct AbsorbArgs {
   const void* q_r;       // [n_q][n_h][d_r] (storage dtype); used by the fused bf16 kernel
   const int32_t* q_pos;  // [n_q]
   RopeTable rope;
+  int32_t q_r_f32;       // fused bf16 kernel: q_r holds fp32 values instead
 };
 // true when launch_absorb also writes the RoPE part (no launch_rope_q needed)
 bool absorb_fuses_rope(int bf16, int d_c, int d_h, int d_r);
@@ -132,6 +133,33 @@ struct PrefillArgs {
   float qscale;                 // softmax_scale * log2(e)
   RopeTable rope;
 };
+
+// y[t][o] = sum_k x[t][k] W[o][k] for W = [w0 (rows 0..split-1); w1 (rows
+// split..d_out-1)], split-K over k.  part [k_slices][n][d_out] fp32; with one
+// slice and out0 set, the sums go straight out as bf16: rows of out0 [n][split]
+// and out1 [n][d_out - split] (or fp32 rows of out1_f32).
+struct GemmArgs {
+  const void* x;
+  const void* w0;
+  const void* w1;
+  float* part;
+  uint16_t* out0;
+  uint16_t* out1;
+  float* out1_f32;      // with out0: rows of the w1 part as fp32 here instead of out1
+  int32_t n, d_in, d_out, split, k_slices, k_per_slice;
+};
+// split-K plan: slices (k per slice a multiple of 128) for ~256 workgroups
+void gemm_plan(int32_t n, int32_t d_in, int32_t d_out, int32_t& k_slices, int32_t& k_per_slice);
+// bf16 storage with d_in % 128 == 0 and split, d_out multiples of 64 take the
+// matrix-core kernel; otherwise T = `bf16 ? uint16_t : float` generic kernels
+hipError_t launch_gemm_partial(const GemmArgs& a, int bf16, hipStream_t st);
+// out[t][o] = sum_s part[s][t][o] (fp32)
+hipError_t launch_sum_slices(const float* part, int32_t slices, int64_t n_elems, float* out, hipStream_t st);
+// per row t: v = sum_s part[s][t][:d]; out[t][:] = bf16(v / sqrt(mean(v^2) + eps) * weight)
+hipError_t launch_rmsnorm_rows(const float* part, int32_t slices, int32_t n, int32_t d, const void* weight, float eps,
+                               uint16_t* out, hipStream_t st);
+// out[i] = bf16(in[i])
+hipError_t launch_to_bf16(const float* in, int64_t n_elems, uint16_t* out, hipStream_t st);
 
 // Cache rows from hidden states: split-K partial sums of [W^DKV; W^KR] h, then
 // per token the sum over slices, the latent RMSNorm, RoPE and the row store.

@@ -136,16 +136,22 @@ __global__ __launch_bounds__(256, 2) void absorb_mfma_kernel(AbsorbArgs a) {
   // RoPE inputs of this workgroup's share of the pairs: column part pc rotates
   // pairs ABS_PAIRS pc .. +ABS_PAIRS-1 of its head for every query of the chunk
   constexpr int RITEMS = ABS_QCHUNK * ABS_PAIRS / 256;  // (query, pair) items per thread
-  const uint16_t* qr = static_cast<const uint16_t*>(a.q_r);
-  uint32_t xr[RITEMS];
+  // (q_r holds bf16 pairs, or fp32 pairs when q_r_f32 is set)
+  float2 xr[RITEMS];
   int32_t rpos[RITEMS];
 #pragma unroll
   for (int it = 0; it < RITEMS; ++it) {
     const int idx = tid + 256 * it, n = n_begin + idx / ABS_PAIRS, k = ABS_PAIRS * half_c + idx % ABS_PAIRS;
-    xr[it] = 0u;
+    xr[it] = make_float2(0.f, 0.f);
     rpos[it] = 0;
     if (n < n_end) {
-      xr[it] = *reinterpret_cast<const uint32_t*>(qr + (static_cast<int64_t>(n) * a.n_h + h) * D_R + 2 * k);
+      const int64_t e = (static_cast<int64_t>(n) * a.n_h + h) * D_R + 2 * k;
+      if (a.q_r_f32) {
+        xr[it] = *reinterpret_cast<const float2*>(static_cast<const float*>(a.q_r) + e);
+      } else {
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.q_r) + e);
+        xr[it] = make_float2(bf16_to_f32(static_cast<uint16_t>(x & 0xffffu)), bf16_to_f32(static_cast<uint16_t>(x >> 16)));
+      }
       rpos[it] = a.q_pos[n];
     }
   }
@@ -165,8 +171,7 @@ __global__ __launch_bounds__(256, 2) void absorb_mfma_kernel(AbsorbArgs a) {
       double sd, cd;
       sincos(static_cast<double>(rpos[it]) * a.rope.theta[k], &sd, &cd);
       const float cf = static_cast<float>(cd), sf = static_cast<float>(sd);
-      const float x0 = bf16_to_f32(static_cast<uint16_t>(xr[it] & 0xffffu));
-      const float x1 = bf16_to_f32(static_cast<uint16_t>(xr[it] >> 16));
+      const float x0 = xr[it].x, x1 = xr[it].y;
       const float y0 = x0 * cf - x1 * sf, y1 = x0 * sf + x1 * cf;
       const float h0 = bf16_to_f32(f32_to_bf16(y0)), h1 = bf16_to_f32(f32_to_bf16(y1));
       uint16_t* o = qout + (static_cast<int64_t>(n) * a.n_h + h) * rec + D_C + 2 * k;

@@ -174,3 +174,22 @@ def test_append_kv_from_hidden_validation():
     assert call(eps=-1.0) == 1
     assert call(h=None) == 1
     assert call(ws=need - 1) == 3
+
+
+def test_projection_entry_points_validation():
+    lib = api.raw()
+    d = ctypes.byref(api.dims(128))
+    need = lib.mla_absorb_q_from_hidden_workspace_bytes(d, 64, 5120, 1536)
+    assert need >= 64 * (1536 + 128 * 192) * 2
+
+    def q(n_q=64, dm=5120, dcq=1536, eps=1e-6, h=FAKE, ws=need):
+        return lib.mla_absorb_q_from_hidden(d, n_q, dm, dcq, h, FAKE, None, eps, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                                            None)
+
+    assert q(n_q=-1) == 1 and q(dcq=5000) == 1 and q(eps=float("inf")) == 1 and q(h=None) == 1
+    assert q(ws=need - 1) == 3
+    oneed = lib.mla_output_projection_workspace_bytes(d, 64, 5120)
+    assert oneed >= 64 * 128 * 128 * 2
+    assert lib.mla_output_projection(d, 64, 0, FAKE, FAKE, FAKE, FAKE, oneed, None) == 1
+    assert lib.mla_output_projection(d, 64, 5120, FAKE, None, FAKE, FAKE, oneed, None) == 1
+    assert lib.mla_output_projection(d, 64, 5120, FAKE, FAKE, FAKE, FAKE, oneed - 1, None) == 3
