@@ -130,33 +130,34 @@ def bench_prefill(args):
     print(json.dumps(line), flush=True)
 
 
-def bench_kv_proj(args):
-    """A1 from hidden states (mla_append_kv_from_hidden) at the V2 shapes:
-    d_model 5120 -> [c^KV (512, RMSNorm) ; k^R (64, RoPE)] rows, for the 64
-    tokens of a v2_decode step and a 4,096-token prefill chunk.  Reports the
-    time per call and its rate against the bytes the call must move (the
-    weights once, the hidden states once, the rows written) and its FLOP."""
+def bench_projections(args):
+    """The projections around the path at the V2 shapes (d_model 5,120, 128
+    heads, query latent 1,536): cache rows from hidden states
+    (mla_append_kv_from_hidden) for the 64 tokens of a v2_decode step and a
+    4,096-token chunk, the query path into the absorbed queries
+    (mla_absorb_q_from_hidden) and the output projection
+    (mla_output_projection) at the decode step.  Each is timed over K calls
+    and reported against the bytes it must move (weights once, activations in
+    and out) and its FLOP."""
     import numpy as np
     import torch
     from mla_latent_kv_24_amd import api, workloads as W
     from mla_latent_kv_24_amd.pipeline import to_device
-    d_model, res = 5120, {}
-    d = api.dims(128)
-    w_dkv = to_device(W.random_storage(1, (512, d_model), "bf16", d_model ** -0.5), "bf16")
-    w_kr = to_device(W.random_storage(2, (64, d_model), "bf16", d_model ** -0.5), "bf16")
-    gamma = to_device(W.to_storage(np.ones(512, np.float32), "bf16"), "bf16")
+    d_model, d_cq, n_h = 5120, 1536, 128
+    d = api.dims(n_h)
+    bf = lambda seed, shape, std=1.0: to_device(W.random_storage(seed, shape, "bf16", std), "bf16")
+    w_dkv, w_kr = bf(1, (512, d_model), d_model ** -0.5), bf(2, (64, d_model), d_model ** -0.5)
+    ones = lambda n: to_device(W.to_storage(np.ones(n, np.float32), "bf16"), "bf16")
+    w_dq, w_uq, w_qr = bf(4, (d_cq, d_model), d_model ** -0.5), bf(5, (n_h * 128, d_cq), d_cq ** -0.5), \
+        bf(6, (n_h * 64, d_cq), d_cq ** -0.5)
+    w_uk = bf(7, (n_h, 128, 512), 512 ** -0.5)
+    w_o = bf(8, (d_model, n_h * 128), (n_h * 128) ** -0.5)
     steps, warm = max(1, min(args.steps, 200)), max(1, args.warmup)
-    for name, n_tok in (("decode_step", 64), ("prefill_chunk", 4096)):
-        h = to_device(W.random_storage(3, (n_tok, d_model), "bf16"), "bf16")
-        pos = torch.arange(n_tok, dtype=torch.int32, device="cuda")
-        row = torch.arange(n_tok, dtype=torch.int64, device="cuda")
-        cache = torch.empty((n_tok, 576), dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty(api.append_kv_from_hidden_workspace_bytes(d, api.BF16, n_tok, d_model),
-                         dtype=torch.uint8, device="cuda")
-        fn = lambda: api.append_kv_from_hidden(d, h, w_dkv, w_kr, gamma, 1e-6, pos, row, cache, ws)
+
+    def timed(fn):
         t = time.perf_counter()
         while (time.perf_counter() - t) * 1e3 < min(args.settle_ms, 1000.0):
-            for _ in range(20):
+            for _ in range(10):
                 fn()
             torch.cuda.synchronize()
         for _ in range(warm):
@@ -168,16 +169,50 @@ def bench_kv_proj(args):
             fn()
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / steps * 1e3
-        alg_bytes = 576 * d_model * 2 + n_tok * d_model * 2 + n_tok * 576 * 2
-        flop = 2 * n_tok * d_model * 576
-        res[name] = {"n_tok": n_tok, "us": round(us, 2), "alg_bytes": alg_bytes,
-                     "gbs": round(alg_bytes / (us * 1e-6) / 1e9, 1),
-                     "tflops": round(flop / (us * 1e-6) / 1e12, 1)}
-    line = {"metric": "cache rows from hidden states (W^DKV, RMSNorm, W^KR, RoPE; d_model 5120)",
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    def entry(us, alg_bytes, flop, n_tok):
+        return {"n_tok": n_tok, "us": round(us, 2), "alg_bytes": alg_bytes,
+                "gbs": round(alg_bytes / (us * 1e-6) / 1e9, 1), "tflops": round(flop / (us * 1e-6) / 1e12, 1)}
+
+    res = {}
+    for name, n_tok in (("kv_rows_decode_step", 64), ("kv_rows_prefill_chunk", 4096)):
+        h = bf(3, (n_tok, d_model))
+        pos = torch.arange(n_tok, dtype=torch.int32, device="cuda")
+        row = torch.arange(n_tok, dtype=torch.int64, device="cuda")
+        cache = torch.empty((n_tok, 576), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(api.append_kv_from_hidden_workspace_bytes(d, api.BF16, n_tok, d_model),
+                         dtype=torch.uint8, device="cuda")
+        g_kv = ones(512)
+        us = timed(lambda: api.append_kv_from_hidden(d, h, w_dkv, w_kr, g_kv, 1e-6, pos, row, cache, ws))
+        res[name] = entry(us, 576 * d_model * 2 + n_tok * d_model * 2 + n_tok * 576 * 2, 2 * n_tok * d_model * 576, n_tok)
+    n_tok = 64
+    h = bf(9, (n_tok, d_model))
+    pos = torch.arange(n_tok, dtype=torch.int32, device="cuda")
+    q_lat = api.q_lat_empty(d, torch.bfloat16, n_tok)
+    g_q = ones(d_cq)
+    ws = torch.empty(api._lib.mla_absorb_q_from_hidden_workspace_bytes(ctypes_byref(d), n_tok, d_model, d_cq),
+                     dtype=torch.uint8, device="cuda")
+    us = timed(lambda: api.absorb_q_from_hidden(d, h, w_dq, g_q, 1e-6, w_uq, w_qr, pos, w_uk, q_lat, ws))
+    wbytes = (d_cq * d_model + n_h * 192 * d_cq + n_h * 128 * 512) * 2
+    flop = 2 * n_tok * (d_cq * d_model + n_h * 192 * d_cq + n_h * 128 * 512)
+    res["query_path_decode_step"] = entry(us, wbytes + n_tok * d_model * 2 + n_tok * n_h * 576 * 4, flop, n_tok)
+    o = torch.randn((n_tok, n_h, 128), dtype=torch.float32, device="cuda")
+    out = torch.empty((n_tok, d_model), dtype=torch.float32, device="cuda")
+    ws = torch.empty(api._lib.mla_output_projection_workspace_bytes(ctypes_byref(d), n_tok, d_model),
+                     dtype=torch.uint8, device="cuda")
+    us = timed(lambda: api.output_projection(d, o, w_o, out, ws))
+    res["output_projection_decode_step"] = entry(us, d_model * n_h * 128 * 2 + n_tok * n_h * 128 * 4 + n_tok * d_model * 4,
+                                                 2 * n_tok * n_h * 128 * d_model, n_tok)
+    line = {"metric": "projections around the attention (V2: d_model 5120, 128 heads, query latent 1536)",
             "unit": "us", "higher_is_better": False, "steps": steps, "warmup": warm, "dtype": "bf16",
             "data": "synthetic", **res, "hbm_peak_gbs": HBM_PEAK_GBS, "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS}
     print(json.dumps(line), flush=True)
+
+
+def ctypes_byref(x):
+    import ctypes
+    return ctypes.byref(x)
 
 
 def main():
@@ -195,9 +230,10 @@ def main():
     ap.add_argument("--prefill", action="store_true",
                     help="instead of the decode step, time the causal prefill of the v2_prefill "
                          "workload in both forms (absorbed, unabsorbed); one JSON line")
-    ap.add_argument("--kv-proj", action="store_true",
-                    help="instead of the decode step, time the cache rows made from hidden states "
-                         "(KV down-projection + RMSNorm + RoPE) at a decode step and a prefill chunk")
+    ap.add_argument("--projections", "--kv-proj", dest="projections", action="store_true",
+                    help="instead of the decode step, time the projections around the attention: cache rows "
+                         "from hidden states (decode step, prefill chunk), the query path and the output "
+                         "projection (decode step)")
     ap.add_argument("--fp8-cache", action="store_true",
                     help="run the decode step over the FP8 latent cache (E4M3 codes + per-row scale, "
                          "bf16 RoPE keys: 644 B per row)")
@@ -218,8 +254,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.prefill:
         return bench_prefill(args)
-    if args.kv_proj:
-        return bench_kv_proj(args)
+    if args.projections:
+        return bench_projections(args)
     w = W.WORKLOADS[args.workload]
     log(f"[bench] generating {w.name} ...")
     inp = W.make_decode_inputs(w)

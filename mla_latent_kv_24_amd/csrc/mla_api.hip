@@ -165,7 +165,7 @@ size_t mla_append_kv_from_hidden_workspace_bytes(const mla_dims* dims, mla_dtype
                                                  int32_t d_model) {
   if (check_dims(dims, dtype) != MLA_OK || n_tok < 1 || d_model < 1) return 0;
   int32_t slices = 1, kr = 0;
-  mla::gemm_plan(n_tok, d_model, mla::ROWE, slices, kr);
+  mla::gemm_plan(n_tok, d_model, mla::ROWE, mla::D_C, slices, kr);
   return static_cast<size_t>(slices) * n_tok * mla::ROWE * sizeof(float);
 }
 
@@ -196,7 +196,7 @@ mla_status mla_append_kv_from_hidden(const mla_dims* dims, mla_dtype dtype, int3
   a.part = static_cast<float*>(workspace);
   a.n_tok = n_tok;
   a.d_model = d_model;
-  mla::gemm_plan(n_tok, d_model, mla::ROWE, a.k_slices, a.k_per_slice);
+  mla::gemm_plan(n_tok, d_model, mla::ROWE, mla::D_C, a.k_slices, a.k_per_slice);
   a.eps = static_cast<float>(eps);
   fill_rope(dims, a.rope);
   return hip_status(mla::launch_kv_project_append(a, dtype == MLA_BF16, static_cast<hipStream_t>(stream)),
@@ -249,14 +249,18 @@ mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q, cons
 // [W^UQ ; W^QR] c^Q, then A2.  Workspace: slices of W^DQ h (fp32), c^Q and q^C
 // (bf16: matrix-core operands), q^R (fp32: only rotated).
 struct QPathLayout {
-  int32_t slices, kps;
+  int32_t slices, kps, slices2, kps2;
   size_t part, cq, qc, qr, total;
 };
 static QPathLayout qpath_layout(const mla_dims* d, int32_t n_q, int32_t d_model, int32_t d_cq) {
   QPathLayout L{};
-  mla::gemm_plan(n_q, d_model, d_cq, L.slices, L.kps);
-  L.part = 0;
-  L.cq = align256(static_cast<size_t>(L.slices) * n_q * d_cq * sizeof(float));
+  const int32_t d_out2 = d->n_h * (d->d_h + d->d_hR);
+  mla::gemm_plan(n_q, d_model, d_cq, d_cq, L.slices, L.kps);
+  mla::gemm_plan(n_q, d_cq, d_out2, d->n_h * d->d_h, L.slices2, L.kps2);
+  L.part = 0;   // partials of W^DQ h, then (reused) of [W^UQ ; W^QR] c^Q
+  L.cq = align256(std::max(static_cast<size_t>(L.slices) * n_q * d_cq,
+                           L.slices2 > 1 ? static_cast<size_t>(L.slices2) * n_q * d_out2 : size_t{0}) *
+                  sizeof(float));
   L.qc = L.cq + align256(static_cast<size_t>(n_q) * d_cq * 2);
   L.qr = L.qc + align256(static_cast<size_t>(n_q) * d->n_h * d->d_h * 2);
   L.total = L.qr + align256(static_cast<size_t>(n_q) * d->n_h * d->d_hR * sizeof(float));
@@ -309,16 +313,25 @@ mla_status mla_absorb_q_from_hidden(const mla_dims* dims, int32_t n_q, int32_t d
   g2.x = cq;
   g2.w0 = w_uq;
   g2.w1 = w_qr;
-  g2.out0 = qc;
-  g2.out1_f32 = qr;
+  if (L.slices2 == 1) {   // one slice: q^C (bf16) and q^R (fp32) straight from the product
+    g2.out0 = qc;
+    g2.out1_f32 = qr;
+  } else {
+    g2.part = part;
+  }
   g2.n = n_q;
   g2.d_in = d_cq;
   g2.d_out = dims->n_h * (dims->d_h + dims->d_hR);
   g2.split = dims->n_h * dims->d_h;
-  g2.k_slices = 1;
-  g2.k_per_slice = (d_cq + 127) / 128 * 128;
+  g2.k_slices = L.slices2;
+  g2.k_per_slice = L.kps2;
   st = hip_status(mla::launch_gemm_partial(g2, 1, s), "mla_absorb_q_from_hidden (W^UQ, W^QR)");
   if (st != MLA_OK) return st;
+  if (L.slices2 > 1) {
+    st = hip_status(mla::launch_slices_to_outputs(part, L.slices2, n_q, g2.d_out, g2.split, qc, qr, s),
+                    "mla_absorb_q_from_hidden (q^C, q^R)");
+    if (st != MLA_OK) return st;
+  }
   return absorb_launch(dims, 1, n_q, qc, qr, q_pos, w_uk, q_lat, s, "mla_absorb_q_from_hidden (absorb)", 1);
 }
 
@@ -330,7 +343,7 @@ struct OutLayout {
 static OutLayout out_layout(const mla_dims* d, int32_t n_q, int32_t d_model) {
   OutLayout L{};
   const int32_t d_in = d->n_h * d->d_h;
-  mla::gemm_plan(n_q, d_in, d_model, L.slices, L.kps);
+  mla::gemm_plan(n_q, d_in, d_model, d_model, L.slices, L.kps);
   L.o16 = 0;
   L.part = align256(static_cast<size_t>(n_q) * d_in * 2);
   L.total = L.part + (L.slices > 1 ? align256(static_cast<size_t>(L.slices) * n_q * d_model * sizeof(float)) : 0);

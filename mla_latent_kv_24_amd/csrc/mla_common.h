@@ -149,10 +149,13 @@ struct GemmArgs {
   int32_t n, d_in, d_out, split, k_slices, k_per_slice;
 };
 // split-K plan: slices (k per slice a multiple of 128) for ~256 workgroups
-void gemm_plan(int32_t n, int32_t d_in, int32_t d_out, int32_t& k_slices, int32_t& k_per_slice);
+void gemm_plan(int32_t n, int32_t d_in, int32_t d_out, int32_t split, int32_t& k_slices, int32_t& k_per_slice);
 // bf16 storage with d_in % 128 == 0 and split, d_out multiples of 64 take the
 // matrix-core kernel; otherwise T = `bf16 ? uint16_t : float` generic kernels
 hipError_t launch_gemm_partial(const GemmArgs& a, int bf16, hipStream_t st);
+// slice sums to two outputs: columns < split as bf16 rows of out0, the rest fp32 rows of out1
+hipError_t launch_slices_to_outputs(const float* part, int32_t slices, int32_t n, int32_t d_out, int32_t split,
+                                    uint16_t* out0, float* out1, hipStream_t st);
 // out[t][o] = sum_s part[s][t][o] (fp32)
 hipError_t launch_sum_slices(const float* part, int32_t slices, int64_t n_elems, float* out, hipStream_t st);
 // per row t: v = sum_s part[s][t][:d]; out[t][:] = bf16(v / sqrt(mean(v^2) + eps) * weight)

@@ -96,6 +96,147 @@ __global__ __launch_bounds__(256) void gemm_partial_mfma_kernel(GemmArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------
+// Few tokens (n <= 64, the decode step): the product streams the weights, so
+// a workgroup takes 256 outputs (wave w: 64 rows, as two 32-row MFMA tiles)
+// against all tokens (two 32-token tiles): every weight row is loaded once,
+// by its wave, into registers (two 128-deep batches in ping-pong), and the
+// activation chunk [64 tokens][128 k] is loaded once per workgroup into a
+// double-buffered LDS tile (16-B chunk kc of token row t at kc ^ (t & 15))
+// that all four waves read as the B operand.
+// ------------------------------------------------------------------------
+constexpr int S_OUT = 256;
+constexpr int S_XBYTES = 64 * 128 * 2;   // one activation chunk in LDS
+
+__global__ __launch_bounds__(256, 2) void gemm_stream_mfma_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2 * S_XBYTES];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, l32 = l & 31;
+  const int ob = blockIdx.x, s = blockIdx.z;
+  const int o0 = S_OUT * ob + 64 * w;   // the wave's 64 rows (one side of split)
+  const int64_t dk = a.d_in;
+  const uint16_t* wbase = (o0 < a.split) ? static_cast<const uint16_t*>(a.w0) + static_cast<int64_t>(o0) * dk
+                                         : static_cast<const uint16_t*>(a.w1) + static_cast<int64_t>(o0 - a.split) * dk;
+  const uint16_t* wr0 = wbase + static_cast<int64_t>(l32) * dk + 8 * g;         // rows o0 + l32
+  const uint16_t* wr1 = wbase + static_cast<int64_t>(32 + l32) * dk + 8 * g;    // rows o0 + 32 + l32
+  const int k0 = s * a.k_per_slice;
+  const int k1 = min(k0 + a.k_per_slice, a.d_in);
+  const int nchunks = (k1 - k0) / 128;
+
+  // activation chunk loads: thread tid moves 16-B chunks f = tid + 256 i: token
+  // t = f / 16, k-chunk kc = f % 16 (tokens past n load zeros)
+  const uint16_t* xg = static_cast<const uint16_t*>(a.x);
+  auto xload = [&](int c, u32x4* xv) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int f = tid + 256 * i, t = f >> 4, kc = f & 15;
+      xv[i] = (t < a.n) ? *reinterpret_cast<const u32x4*>(xg + static_cast<int64_t>(t) * dk + k0 + 128 * c + 8 * kc)
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto xstore = [&](int buf, const u32x4* xv) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int f = tid + 256 * i, t = f >> 4, kc = f & 15;
+      *reinterpret_cast<u32x4*>(xs + buf * S_XBYTES + 256 * t + 16 * (kc ^ (t & 15))) = xv[i];
+    }
+  };
+  auto wload = [&](int c, u32x4* av) {
+    const int kb = k0 + 128 * c;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      av[i] = *reinterpret_cast<const u32x4*>(wr0 + kb + 16 * i);
+      av[8 + i] = *reinterpret_cast<const u32x4*>(wr1 + kb + 16 * i);
+    }
+  };
+  f32x16 acc[2][2];   // [row tile u][token tile tt]
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[u][tt][j] = 0.f;
+  auto mfmas = [&](int buf, const u32x4* av) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      u32x4 bv[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int t = 32 * tt + l32;
+        bv[tt] = *reinterpret_cast<const u32x4*>(xs + buf * S_XBYTES + 256 * t + 16 * ((2 * i + g) ^ (t & 15)));
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          acc[u][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[8 * u + i]),
+                                                               __builtin_bit_cast(bf16x8, bv[tt]), acc[u][tt], 0, 0, 0);
+    }
+  };
+
+  u32x4 wa[16], wb[16], xv[4];
+  if (nchunks > 0) {
+    xload(0, xv);
+    wload(0, wa);
+    xstore(0, xv);
+  }
+  __syncthreads();
+  for (int c = 0; c < nchunks; c += 2) {
+    // chunk c from (wa, LDS buffer 0); chunk c + 1's loads in flight meanwhile
+    if (c + 1 < nchunks) {
+      xload(c + 1, xv);
+      wload(c + 1, wb);
+    }
+    mfmas(0, wa);
+    if (c + 1 < nchunks) xstore(1, xv);
+    __syncthreads();   // buffer 1 written; every wave done with buffer 0
+    if (c + 1 < nchunks) {
+      if (c + 2 < nchunks) {
+        xload(c + 2, xv);
+        wload(c + 2, wa);
+      }
+      mfmas(1, wb);
+      if (c + 2 < nchunks) xstore(0, xv);
+      __syncthreads();
+    }
+  }
+
+  // ---- results: lane holds output o0 + 32 u + 8 (j/4) + 4 g + j%4, token 32 tt + l32
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int t = 32 * tt + l32;
+    if (t >= a.n) continue;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int obase = o0 + 32 * u + 4 * g;
+      const f32x16& v = acc[u][tt];
+      if (a.out0) {
+        if (obase >= a.split && a.out1_f32) {
+          float* df = a.out1_f32 + static_cast<int64_t>(t) * (a.d_out - a.split) + (obase - a.split);
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq)
+            *reinterpret_cast<f32x4*>(df + 8 * jq) = f32x4{v[4 * jq], v[4 * jq + 1], v[4 * jq + 2], v[4 * jq + 3]};
+        } else {
+          uint16_t* dst = (obase < a.split) ? a.out0 + static_cast<int64_t>(t) * a.split + obase
+                                            : a.out1 + static_cast<int64_t>(t) * (a.d_out - a.split) + (obase - a.split);
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq)
+            *reinterpret_cast<uint2*>(dst + 8 * jq) =
+                make_uint2(pack_bf16x2(v[4 * jq], v[4 * jq + 1]), pack_bf16x2(v[4 * jq + 2], v[4 * jq + 3]));
+        }
+      } else {
+        float* dst = a.part + (static_cast<int64_t>(s) * a.n + t) * a.d_out + obase;
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq)
+          *reinterpret_cast<f32x4*>(dst + 8 * jq) = f32x4{v[4 * jq], v[4 * jq + 1], v[4 * jq + 2], v[4 * jq + 3]};
+      }
+    }
+  }
+}
+
+static bool use_stream(int32_t n, int32_t d_in, int32_t d_out, int32_t split) {
+  return n <= 64 && d_in % 128 == 0 && d_out % S_OUT == 0 && split % S_OUT == 0;
+}
+
 // Generic partials: grid (ceil(d_out / 64), tokens, k slices), one output per thread.
 template <typename T>
 __global__ __launch_bounds__(64) void gemm_partial_generic_kernel(GemmArgs a) {
@@ -121,9 +262,18 @@ __global__ __launch_bounds__(64) void gemm_partial_generic_kernel(GemmArgs a) {
   a.part[(static_cast<int64_t>(s) * a.n + t) * a.d_out + o] = acc;
 }
 
-void gemm_plan(int32_t n, int32_t d_in, int32_t d_out, int32_t& k_slices, int32_t& k_per_slice) {
-  const int64_t tiles = static_cast<int64_t>((d_out + G_OUT - 1) / G_OUT) * ((n + G_TOK - 1) / G_TOK);
-  int64_t s = (256 + tiles - 1) / tiles;
+// Split-K plan (slices of at least one 128-deep batch): the streaming kernel
+// aims at one round of 256 workgroups; the tile kernel at four workgroups per
+// CU, since each of its waves has about one load batch in flight.
+void gemm_plan(int32_t n, int32_t d_in, int32_t d_out, int32_t split, int32_t& k_slices, int32_t& k_per_slice) {
+  const bool stream = use_stream(n, d_in, d_out, split);
+  const int64_t tiles = stream ? d_out / S_OUT
+                               : static_cast<int64_t>((d_out + G_OUT - 1) / G_OUT) * ((n + G_TOK - 1) / G_TOK);
+  int64_t s = ((stream ? 256 : 1024) + tiles - 1) / tiles;
+  // the fp32 partials (n d_out 4 B per slice) stay within half the bytes the
+  // product moves anyway (weights and activations)
+  const int64_t cap = static_cast<int64_t>(d_in) * (d_out + n) / (4 * static_cast<int64_t>(std::max(n, 1)) * d_out);
+  s = std::min(s, std::max<int64_t>(1, cap));
   s = std::max<int64_t>(1, std::min<int64_t>(s, std::max(1, d_in / 128)));
   int64_t kr = (d_in + s - 1) / s;
   kr = (kr + 127) / 128 * 128;
@@ -134,7 +284,9 @@ void gemm_plan(int32_t n, int32_t d_in, int32_t d_out, int32_t& k_slices, int32_
 hipError_t launch_gemm_partial(const GemmArgs& a, int bf16, hipStream_t st) {
   if (a.n <= 0 || a.d_out <= 0) return hipSuccess;
   const bool mfma = bf16 && a.d_in % 128 == 0 && a.d_out % G_OUT == 0 && a.split % G_OUT == 0;
-  if (mfma) {
+  if (bf16 && use_stream(a.n, a.d_in, a.d_out, a.split)) {
+    gemm_stream_mfma_kernel<<<dim3(a.d_out / S_OUT, 1, a.k_slices), 256, 0, st>>>(a);
+  } else if (mfma) {
     const dim3 grid(a.d_out / G_OUT, (a.n + G_TOK - 1) / G_TOK, a.k_slices);
     gemm_partial_mfma_kernel<<<grid, 256, 0, st>>>(a);
   } else {
@@ -158,6 +310,33 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(const float* part, int3
   out[i] = v;
 }
 
+// Slice sums of [n][d_out] partials to two outputs: columns < split as bf16
+// rows of out0 [n][split], the rest as fp32 rows of out1 [n][d_out - split].
+__global__ __launch_bounds__(256) void slices_to_outputs_kernel(const float* part, int32_t slices, int32_t n,
+                                                                int32_t d_out, int32_t split, uint16_t* out0,
+                                                                float* out1) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t n_elems = static_cast<int64_t>(n) * d_out;
+  if (i >= n_elems) return;
+  float v = 0.f;
+  for (int s = 0; s < slices; ++s) v += part[s * n_elems + i];
+  const int64_t t = i / d_out;
+  const int o = static_cast<int>(i - t * d_out);
+  if (o < split)
+    out0[t * split + o] = f32_to_bf16(v);
+  else
+    out1[t * (d_out - split) + (o - split)] = v;
+}
+
+hipError_t launch_slices_to_outputs(const float* part, int32_t slices, int32_t n, int32_t d_out, int32_t split,
+                                    uint16_t* out0, float* out1, hipStream_t st) {
+  const int64_t n_elems = static_cast<int64_t>(n) * d_out;
+  if (n_elems <= 0) return hipSuccess;
+  slices_to_outputs_kernel<<<static_cast<unsigned>((n_elems + 255) / 256), 256, 0, st>>>(part, slices, n, d_out, split,
+                                                                                        out0, out1);
+  return hipGetLastError();
+}
+
 hipError_t launch_sum_slices(const float* part, int32_t slices, int64_t n_elems, float* out, hipStream_t st) {
   if (n_elems <= 0) return hipSuccess;
   sum_slices_kernel<<<static_cast<unsigned>((n_elems + 255) / 256), 256, 0, st>>>(part, slices, n_elems, out);
@@ -179,8 +358,16 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* part, in
   for (int i = 0; i < RN_PER; ++i) {
     const int o = tid + 256 * i;
     float x = 0.f;
-    if (o < d)
-      for (int s = 0; s < slices; ++s) x += part[s * ss + static_cast<int64_t>(t) * d + o];
+    if (o < d) {
+      const float* p = part + static_cast<int64_t>(t) * d + o;
+      for (int s0 = 0; s0 < slices; s0 += 8) {   // eight slice loads in flight, summed in order
+        float r[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = (s0 + j < slices) ? p[(s0 + j) * ss] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x += r[j];
+      }
+    }
     v[i] = x;
     sq = fmaf(x, x, sq);
   }
