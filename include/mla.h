@@ -365,6 +365,15 @@ mla_status mla_decode_fp8(const mla_dims* dims, int32_t batch, const void* q_lat
                           float* out, float* out_latent, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* A6 over the FP8 cache: mla_prefill's causal chunk (query i of sequence b at
+ * position prefix_lens[b] + i, bf16 absorbed queries [batch][chunk][n_h]...,
+ * w_uv bf16) over rows [E4M3(codes) * scale ; rope]; the workspace is
+ * mla_prefill_workspace_bytes(dims, MLA_BF16, batch, chunk, max_prefix_len). */
+mla_status mla_prefill_fp8(const mla_dims* dims, int32_t batch, int32_t chunk, const void* q_lat,
+                           const mla_fp8_cache* cache, int64_t cache_seq_stride,
+                           const int32_t* prefix_lens, int32_t max_prefix_len, const void* w_uv,
+                           float* out, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

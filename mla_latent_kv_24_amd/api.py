@@ -92,6 +92,7 @@ _SIGS = {
     "mla_append_kv_fp8": (ctypes.c_int, [_P, _i32, _vp, _vp, _vp, _vp, _FC, _vp]),
     "mla_decode_partials_fp8": (ctypes.c_int, [_P, _i32, _vp, _FC, _i64, _vp, _i32, _i32, _vp, _vp, _vp]),
     "mla_decode_fp8": (ctypes.c_int, [_P, _i32, _vp, _FC, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mla_prefill_fp8": (ctypes.c_int, [_P, _i32, _i32, _vp, _FC, _i64, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "mla_decode_partials_paged": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _PC, _vp, _i32, _i32, _vp, _vp,
                                                  _vp]),
     "mla_decode_paged": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _PC, _vp, _i32, _vp, _vp, _vp, _vp,
@@ -408,3 +409,17 @@ def output_projection(d: Dims, o, w_o, out, workspace=None) -> None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=out.device)
     _check(_lib.mla_output_projection(ctypes.byref(d), n_q, d_model, _ptr(o), _ptr(w_o), _ptr(out), _ptr(workspace),
                                       workspace.numel(), _stream(out.device)), "mla_output_projection")
+
+
+def prefill_fp8(d: Dims, q_lat, cache, stride: int, prefix_lens, max_prefix_len: int, w_uv, out,
+                workspace=None) -> None:
+    """A6 over the FP8 cache (codes, rope, scale); q_lat [B, chunk, n_h, 2, 576] bf16."""
+    assert prefix_lens.dtype == torch.int32 and q_lat.dtype == torch.bfloat16
+    B, chunk = q_lat.shape[0], q_lat.shape[1]
+    need = prefill_workspace_bytes(d, BF16, B, chunk, max_prefix_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
+    fc = _fp8(cache)
+    _check(_lib.mla_prefill_fp8(ctypes.byref(d), B, chunk, _ptr(q_lat), ctypes.byref(fc), stride, _ptr(prefix_lens),
+                                max_prefix_len, _ptr(w_uv), _ptr(out), _ptr(workspace), workspace.numel(),
+                                _stream(q_lat.device)), "mla_prefill_fp8")

@@ -713,7 +713,7 @@ mla_status mla_append_kv_fp8(const mla_dims* dims, int32_t n_tok, const void* c_
 
 static mla_status fp8_partials(const mla_dims* dims, int32_t batch, const void* q_lat, const mla_fp8_cache* cache,
                                int64_t stride, const int32_t* seq_lens, int32_t max_seq_len, int32_t S, float* z,
-                               float* lse, hipStream_t s, const char* who) {
+                               float* lse, hipStream_t s, const char* who, int32_t q_per_seq = 1, int prefill = 0) {
   mla::SplitArgs a{};
   a.q_lat = q_lat;
   a.cache = cache->codes;
@@ -724,14 +724,14 @@ static mla_status fp8_partials(const mla_dims* dims, int32_t batch, const void* 
   a.lse_part = lse;
   a.stride = stride;
   a.split_rows = split_rows(max_seq_len, S);
-  a.n_q = batch;
+  a.n_q = batch;   // queries (sequences x q_per_seq)
   a.n_h = dims->n_h;
   a.d_c = dims->d_c;
   a.d_r = dims->d_hR;
   a.num_splits = S;
   a.max_len = max_seq_len;
-  a.q_per_seq = 1;
-  a.prefill = 0;
+  a.q_per_seq = q_per_seq;
+  a.prefill = prefill;
   a.qscale = static_cast<float>(scale_of(dims) * 1.4426950408889634);
   return hip_status(mla::launch_splitkv_fp8(a, s), who);
 }
@@ -781,5 +781,37 @@ mla_status mla_decode_fp8(const mla_dims* dims, int32_t batch, const void* q_lat
   if (st != MLA_OK) return st;
   mla::CombineArgs a{z, lse, w_uv, out, out_latent, batch, dims->n_h, dims->d_c, dims->d_h, S};
   return hip_status(mla::launch_combine(a, 1, s), "mla_decode_fp8 (combine)");
+}
+mla_status mla_prefill_fp8(const mla_dims* dims, int32_t batch, int32_t chunk, const void* q_lat,
+                           const mla_fp8_cache* cache, int64_t cache_seq_stride, const int32_t* prefix_lens,
+                           int32_t max_prefix_len, const void* w_uv, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  mla_status st = check_dims(dims, MLA_BF16);
+  if (st != MLA_OK) return st;
+  if (batch < 1 || chunk < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d, chunk=%d must be >= 1", batch, chunk);
+  if (max_prefix_len < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "max_prefix_len=%d < 0", max_prefix_len);
+  const int64_t max_len = static_cast<int64_t>(max_prefix_len) + chunk;
+  if (max_len > cache_seq_stride)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "max_prefix_len + chunk = %lld > cache_seq_stride=%lld",
+                (long long)max_len, (long long)cache_seq_stride);
+  if (max_len > 0x7fffffff) return fail(MLA_ERR_INVALID_ARGUMENT, "prefix + chunk too large");
+  const int64_t n_q = static_cast<int64_t>(batch) * chunk;
+  if (n_q > 0x7fffffff / 2) return fail(MLA_ERR_INVALID_ARGUMENT, "batch*chunk too large");
+  st = check_fp8(cache);
+  if (st != MLA_OK) return st;
+  if (!q_lat || !prefix_lens || !w_uv || !out || !workspace) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const int32_t S = plan_splits(dims, MLA_BF16, n_q, max_len);
+  const size_t need = partial_bytes(dims, n_q, S);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", workspace_bytes, need);
+  float* z = static_cast<float*>(workspace);
+  float* lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        align256(static_cast<size_t>(n_q) * S * dims->n_h * dims->d_c * sizeof(float)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = fp8_partials(dims, static_cast<int32_t>(n_q), q_lat, cache, cache_seq_stride, prefix_lens,
+                    static_cast<int32_t>(max_len), S, z, lse, s, "mla_prefill_fp8 (partials)", chunk, 1);
+  if (st != MLA_OK) return st;
+  mla::CombineArgs a{z, lse, w_uv, out, nullptr, static_cast<int32_t>(n_q), dims->n_h, dims->d_c, dims->d_h, S};
+  return hip_status(mla::launch_combine(a, 1, s), "mla_prefill_fp8 (combine)");
 }
 }  // extern "C"

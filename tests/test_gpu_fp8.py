@@ -122,3 +122,37 @@ def test_decode_fp8_fused_equals_partials(api, pipeline):
     api.decode_fp8(st.d, st.q_lat, st.cache, st.stride, st.seq_lens, st.max_len, st.w_uv, out, lat)
     torch.cuda.synchronize()
     assert torch.equal(out, st.out)
+
+
+# Query lengths 2001..2065 and 1001..1070: every query ends in a ragged tile and
+# the chunk crosses a tile boundary.  Over 300..340 rows of the 128-head inputs
+# the bf16 path's own prefill sits at 2.75e-2 and the FP8 one at 4.0e-2 (one
+# query; the others 1.0e-2..2.6e-2): short contexts are below the 2e-2 bar's
+# reach for both caches.
+@pytest.mark.parametrize("n_h,prefix,chunk", [(128, 2000, 65), (16, 1000, 70)])
+def test_prefill_fp8(api, n_h, prefix, chunk):
+    """Causal prefill over the FP8 cache against the oracle's prefill on its own
+    dequantised rows (the RoPE key rounded to bf16 as stored)."""
+    base = W.WORKLOADS["v2_prefill"] if n_h == 128 else W.scaled(W.WORKLOADS["lite_decode"], batch=1)
+    pinp = W.make_prefill_inputs(W.scaled(base, seq_len=prefix + chunk, prefill_chunk=chunk, batch=1))
+    total = prefix + chunk
+    d = api.dims(n_h)
+    cache = api.fp8_cache_empty(total)
+    api.append_kv_fp8(d, dev(pinp.c_kv, "bf16"), dev(pinp.k_raw, "bf16"),
+                      torch.arange(total, dtype=torch.int32, device="cuda"),
+                      torch.arange(total, dtype=torch.int64, device="cuda"), cache)
+    q_lat = api.q_lat_empty(d, torch.bfloat16, 1, chunk)
+    api.absorb_q(d, dev(pinp.q_c, "bf16"), dev(pinp.q_r, "bf16"),
+                 torch.arange(prefix, total, dtype=torch.int32, device="cuda"), dev(pinp.w_uk, "bf16"),
+                 q_lat.view(chunk, n_h, 2, 576))
+    out = torch.empty((1, chunk, n_h, 128), dtype=torch.float32, device="cuda")
+    api.prefill_fp8(d, q_lat, cache, total, torch.tensor([prefix], dtype=torch.int32, device="cuda"), prefix,
+                    dev(pinp.w_uv, "bf16"), out)
+    got = out.cpu().numpy()[0]
+    codes, scale = O.quantize_rows_fp8(f64(pinp.c_kv, "bf16"))
+    ref = O.prefill(f64(pinp.q_c, "bf16"), f64(pinp.q_r, "bf16"), prefix, O.dequantize_rows_fp8(codes, scale),
+                    f64(pinp.k_raw, "bf16"), f64(pinp.w_uk, "bf16"), f64(pinp.w_uv, "bf16"), pinp.w.rope_base,
+                    store="bf16")
+    e = rel_err(got, ref)
+    print(f"fp8 prefill parity: {e:.3e}")
+    assert np.all(np.isfinite(got)) and e < TOL["bf16"]
