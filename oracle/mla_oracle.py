@@ -63,6 +63,19 @@ no body, and no page defines RoPE itself):
     precision; divisions correctly rounded), so this oracle reproduces them
     exactly.  A row of zeros takes s = 1.
 
+  * Long-context RoPE ([R2] section 6: the 4K-pretrained model is extended
+    with YaRN at scale s = 40 towards a 160K target, 40 x 4K; the pages give
+    no formula).  Taken as YaRN's published frequency interpolation (Peng et
+    al., 2023, "NTK-by-parts" with its attention temperature): pair k keeps
+    theta_k where its wavelength 2 pi / theta_k fits many times into the
+    pretraining context L = 4,096, is slowed to theta_k / s where it does not
+    fit once, and blends linearly in between -- with r_k = L theta_k / (2 pi)
+    and gamma_k = clip((r_k - alpha) / (beta - alpha), 0, 1),
+    theta'_k = (1 - gamma_k) theta_k / s + gamma_k theta_k, alpha = 1 and
+    beta = 32 (that paper's values; the pages give none).  The temperature
+    (sqrt(1/t) = 0.1 ln s + 1) multiplies the whole logit, content and RoPE
+    halves alike, by (0.1 ln s + 1)^2.  RoPE acts on q^R and k^R only ([R3]).
+
 Parity: every function below is pinned by tests that do not re-type its
 formula (closed forms, brute force, a library attention routine, identities,
 the pages' printed cache numbers).
@@ -78,18 +91,50 @@ ROPE_BASE = 10000.0
 # ---------------------------------------------------------------------------
 # RoPE ([R3] rotates query and key by position; convention: see header)
 # ---------------------------------------------------------------------------
-def rope(x: np.ndarray, pos, base: float = ROPE_BASE) -> np.ndarray:
+def rope_frequencies(d: int, base=ROPE_BASE) -> np.ndarray:
+    """Angular frequency of each of the d/2 pairs: base**(-2k/d) for a scalar
+    base; an array of d/2 frequencies (yarn_frequencies') is taken as given."""
+    if np.ndim(base) == 0:
+        k = np.arange(d // 2, dtype=np.float64)
+        return np.power(float(base), -2.0 * k / d)
+    theta = np.asarray(base, dtype=np.float64)
+    if theta.shape != (d // 2,):
+        raise ValueError(f"need {d // 2} pair frequencies, got shape {theta.shape}")
+    return theta
+
+
+def yarn_frequencies(d: int, base: float, factor: float, orig_ctx: float = 4096.0,
+                     alpha: float = 1.0, beta: float = 32.0) -> np.ndarray:
+    """Pair frequencies of the long-context RoPE (header: YaRN reading).
+    factor <= 1 leaves the plain frequencies."""
+    theta = rope_frequencies(d, base)
+    if factor <= 1.0:
+        return theta
+    turns = orig_ctx * theta / (2.0 * math.pi)          # wavelengths inside the context
+    gamma = np.clip((turns - alpha) / (beta - alpha), 0.0, 1.0)
+    return (1.0 - gamma) * (theta / factor) + gamma * theta
+
+
+def yarn_softmax_scale(d_h: int, d_r: int, factor: float) -> float:
+    """The score scale with YaRN's temperature: (0.1 ln s + 1)^2 / sqrt(d_h + d_r)
+    for s > 1, the plain scale otherwise."""
+    m = 0.1 * math.log(factor) + 1.0 if factor > 1.0 else 1.0
+    return m * m * default_scale(d_h, d_r)
+
+
+def rope(x: np.ndarray, pos, base=ROPE_BASE) -> np.ndarray:
     """Rotate the last axis of x (even length d) by position(s) `pos`.
 
     x: [..., d]; pos broadcasts against x.shape[:-1].
-    Pair k = (x[2k], x[2k+1]) is rotated by angle pos * base**(-2k/d).
+    Pair k = (x[2k], x[2k+1]) is rotated by angle pos * theta_k, theta_k =
+    base**(-2k/d), or the k-th entry of `base` when it is an array of pair
+    frequencies.
     """
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     if d % 2:
         raise ValueError("RoPE needs an even width")
-    k = np.arange(d // 2, dtype=np.float64)
-    theta = np.power(float(base), -2.0 * k / d)
+    theta = rope_frequencies(d, base)
     ang = np.asarray(pos, dtype=np.float64)[..., None] * theta
     cos, sin = np.cos(ang), np.sin(ang)
     xe, xo = x[..., 0::2], x[..., 1::2]

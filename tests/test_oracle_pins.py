@@ -597,3 +597,54 @@ def test_output_projection_bruteforce_and_head_blocks():
     o1 = np.zeros_like(o)
     o1[:, 1] = o[:, 1]
     assert np.allclose(O.output_projection(o, w2), u - O.output_projection(o1, w_o), rtol=0, atol=1e-12)
+
+
+# -------------------------------------------------------------------- YaRN
+# The long-context setting of the pages (scale 40 over a 4K pretraining
+# context) with d = 64, base 1e4, alpha 1, beta 32.  Pair k's wavelength
+# 2 pi 10^(k/8) fits r_k = 4096 / (2 pi 10^(k/8)) times into 4,096 positions:
+#   r_k > 32 <=> k < 8 log10(4096 / (64 pi)) = 10.47  -> pairs 0..10 keep theta_k
+#   r_k < 1  <=> k > 8 log10(4096 / (2 pi))  = 22.51  -> pairs 23..31 get theta_k / 40
+PLAIN_THETA = 10000.0 ** (-np.arange(32) / 32.0)
+
+
+def test_yarn_frequencies_regimes():
+    y = O.yarn_frequencies(64, 10000.0, 40.0, 4096.0)
+    assert np.allclose(y[:11], PLAIN_THETA[:11], rtol=1e-15, atol=0)
+    assert np.allclose(y[23:], PLAIN_THETA[23:] / 40.0, rtol=1e-15, atol=0)
+    mid = y[11:23] / PLAIN_THETA[11:23]
+    assert np.all((mid > 1 / 40.0) & (mid < 1.0))
+    ratio = y / PLAIN_THETA
+    assert np.all(np.diff(ratio) <= 1e-15) and np.all(np.diff(ratio[10:24]) < 0)
+    # no scaling: the plain frequencies, and RoPE unchanged
+    assert np.allclose(O.yarn_frequencies(64, 10000.0, 1.0), PLAIN_THETA, rtol=1e-15, atol=0)
+    x = _rng(31).standard_normal((5, 64))
+    assert np.allclose(O.rope(x, 777, O.yarn_frequencies(64, 10000.0, 1.0)), O.rope(x, 777), rtol=0, atol=1e-13)
+
+
+def test_yarn_ramp_quarter_point():
+    """A context where pair 16 (theta = 1/100) fits 8.75 times: a quarter of
+    the way up the ramp from alpha = 1 to beta = 32, so theta' = theta (0.75/40 + 0.25)."""
+    ctx = 8.75 * 2 * math.pi * 100.0
+    y = O.yarn_frequencies(64, 10000.0, 40.0, ctx)
+    assert abs(y[16] / PLAIN_THETA[16] - 0.26875) < 1e-14
+
+
+def test_yarn_rope_is_position_interpolation_on_long_wavelengths():
+    """On pairs 23..31 the long-context RoPE at position p is the plain RoPE
+    at p / 40; on pairs 0..10 it is the plain RoPE at p."""
+    y = O.yarn_frequencies(64, 10000.0, 40.0, 4096.0)
+    rng = _rng(32)
+    low = np.zeros((4, 64))
+    low[:, 46:] = rng.standard_normal((4, 18))
+    high = np.zeros((4, 64))
+    high[:, :22] = rng.standard_normal((4, 22))
+    for p in (1, 4095, 40000, 163839):
+        assert np.allclose(O.rope(low, p, y), O.rope(low, p / 40.0), rtol=0, atol=1e-12)
+        assert np.allclose(O.rope(high, p, y), O.rope(high, p), rtol=0, atol=1e-12)
+
+
+def test_yarn_softmax_scale():
+    assert O.yarn_softmax_scale(128, 64, 1.0) == 1.0 / math.sqrt(192.0)
+    # (1 + 0.1 ln 40)^2 / sqrt(192), ln 40 = 3.688879454113936
+    assert abs(O.yarn_softmax_scale(128, 64, 40.0) - 0.1352337788608801) < 1e-16
