@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 7
+#define MLA_ABI_VERSION 8
 
 typedef enum {
   MLA_OK = 0,
@@ -61,11 +61,27 @@ typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
  * d_hR decoupled RoPE dim (64), even
  * n_h  number of query heads (V2: 128, V2-Lite: 16)
  * rope_base   RoPE frequency base (10000)
- * softmax_scale  0 selects 1/sqrt(d_h + d_hR) */
+ * softmax_scale  0 selects the default: 1/sqrt(d_h + d_hR), times
+ *             (0.1 ln s + 1)^2 when yarn_factor s > 1
+ * Long-context RoPE (jiphyeonjeon.kr DeepSeek-V2 review, section 6: YaRN at
+ * scale 40 over the 4K pretraining context; the formula is YaRN's published
+ * frequency interpolation).  yarn_factor 0 or 1 keeps the plain frequencies
+ * theta_k = rope_base^(-2k/d_hR).  For s = yarn_factor > 1, with
+ * r_k = yarn_orig_ctx * theta_k / (2 pi) and
+ * g_k = clamp((r_k - yarn_alpha) / (yarn_beta - yarn_alpha), 0, 1),
+ * pair k rotates at (1 - g_k) theta_k / s + g_k theta_k.  Requires
+ * yarn_orig_ctx > 0 and 0 < yarn_alpha < yarn_beta (the pages' setting is
+ * s = 40 over 4,096 positions; alpha 1 and beta 32 are YaRN's published
+ * values).  The frequencies act wherever RoPE does (A1, A2, the unabsorbed
+ * prefill's query). */
 typedef struct {
   int32_t d_c, d_h, d_hR, n_h;
   double rope_base;
   double softmax_scale;
+  double yarn_factor;
+  double yarn_orig_ctx;
+  double yarn_alpha;
+  double yarn_beta;
 } mla_dims;
 
 int32_t mla_abi_version(void);

@@ -27,12 +27,17 @@ F32, BF16 = 0, 1
 class Dims(ctypes.Structure):
     _fields_ = [("d_c", ctypes.c_int32), ("d_h", ctypes.c_int32), ("d_hR", ctypes.c_int32),
                 ("n_h", ctypes.c_int32), ("rope_base", ctypes.c_double),
-                ("softmax_scale", ctypes.c_double)]
+                ("softmax_scale", ctypes.c_double), ("yarn_factor", ctypes.c_double),
+                ("yarn_orig_ctx", ctypes.c_double), ("yarn_alpha", ctypes.c_double),
+                ("yarn_beta", ctypes.c_double)]
 
 
 def dims(n_h: int, d_c: int = 512, d_h: int = 128, d_hR: int = 64, rope_base: float = 10000.0,
-         softmax_scale: float = 0.0) -> Dims:
-    return Dims(d_c, d_h, d_hR, n_h, rope_base, softmax_scale)
+         softmax_scale: float = 0.0, yarn_factor: float = 0.0, yarn_orig_ctx: float = 4096.0,
+         yarn_alpha: float = 1.0, yarn_beta: float = 32.0) -> Dims:
+    """Model dimensions; yarn_factor > 1 selects the long-context RoPE frequencies
+    and temperature (DeepSeek-V2: 40 over a 4,096-position pretraining context)."""
+    return Dims(d_c, d_h, d_hR, n_h, rope_base, softmax_scale, yarn_factor, yarn_orig_ctx, yarn_alpha, yarn_beta)
 
 
 class MLAError(RuntimeError):

@@ -50,16 +50,47 @@ mla_status check_dims(const mla_dims* d, mla_dtype dt) {
     return fail(MLA_ERR_INVALID_ARGUMENT, "rope_base must be finite and > 0");
   if (!(d->softmax_scale >= 0.0) || !std::isfinite(d->softmax_scale))
     return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  if (!(d->yarn_factor >= 0.0) || !std::isfinite(d->yarn_factor))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "yarn_factor must be finite and >= 0");
+  if (d->yarn_factor > 1.0) {
+    if (!(d->yarn_orig_ctx > 0.0) || !std::isfinite(d->yarn_orig_ctx))
+      return fail(MLA_ERR_INVALID_ARGUMENT, "yarn_orig_ctx must be finite and > 0");
+    if (!(d->yarn_alpha > 0.0) || !(d->yarn_beta > d->yarn_alpha) || !std::isfinite(d->yarn_beta))
+      return fail(MLA_ERR_INVALID_ARGUMENT, "YaRN needs 0 < yarn_alpha < yarn_beta (finite)");
+  }
   return MLA_OK;
 }
 
+// Long-context scaling in force: yarn_factor > 1.
+static bool yarn_on(const mla_dims* d) { return d->yarn_factor > 1.0; }
+
 double scale_of(const mla_dims* d) {
-  return d->softmax_scale > 0.0 ? d->softmax_scale : 1.0 / std::sqrt(static_cast<double>(d->d_h + d->d_hR));
+  if (d->softmax_scale > 0.0) return d->softmax_scale;
+  double s = 1.0 / std::sqrt(static_cast<double>(d->d_h + d->d_hR));
+  if (yarn_on(d)) {  // YaRN's temperature on the whole logit: (0.1 ln s + 1)^2
+    const double m = 0.1 * std::log(d->yarn_factor) + 1.0;
+    s *= m * m;
+  }
+  return s;
 }
 
+// Pair frequencies in fp64: plain base^(-2k/d_hR), or YaRN's blend between
+// theta / s (wavelengths longer than the pretraining context) and theta
+// (wavelengths that fit yarn_beta times or more), linear in the count of
+// wavelengths that fit.
 void fill_rope(const mla_dims* d, mla::RopeTable& t) {
   std::memset(&t, 0, sizeof(t));
-  for (int k = 0; k < d->d_hR / 2; ++k) t.theta[k] = std::pow(d->rope_base, -2.0 * k / d->d_hR);
+  constexpr double TWO_PI = 6.283185307179586476925;
+  for (int k = 0; k < d->d_hR / 2; ++k) {
+    const double th = std::pow(d->rope_base, -2.0 * k / d->d_hR);
+    if (!yarn_on(d)) {
+      t.theta[k] = th;
+      continue;
+    }
+    const double fits = d->yarn_orig_ctx * th / TWO_PI;
+    const double g = std::min(1.0, std::max(0.0, (fits - d->yarn_alpha) / (d->yarn_beta - d->yarn_alpha)));
+    t.theta[k] = (1.0 - g) * (th / d->yarn_factor) + g * th;
+  }
 }
 
 

@@ -41,7 +41,7 @@ class DecodeState:
         self.device = device
         self.dt = w.dtype
         tdt = torch_dtype(w.dtype)
-        self.d = api.dims(w.n_h, rope_base=w.rope_base)
+        self.d = api.dims(w.n_h, rope_base=w.rope_base, yarn_factor=w.yarn_factor)
         self.batch, self.stride = w.batch, inp.stride
         lens = inp.seq_lens.astype(np.int64)
         self.max_len = int(lens.max())
@@ -161,7 +161,7 @@ class PrefillState:
         w = inp.w
         self.inp = inp
         tdt = torch_dtype(w.dtype)
-        self.d = api.dims(w.n_h, rope_base=w.rope_base)
+        self.d = api.dims(w.n_h, rope_base=w.rope_base, yarn_factor=w.yarn_factor)
         self.dt = w.dtype
         total = inp.prefix + inp.chunk
         self.stride = total

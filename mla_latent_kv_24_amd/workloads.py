@@ -81,6 +81,7 @@ class Workload:
     d_cq: int = 0                # query latent width d_c' (v2 path)
     prefill_chunk: int = 0       # >0: causal prefill of this many tokens after seq_len-chunk prefix
     rope_base: float = 10000.0
+    yarn_factor: float = 0.0     # >1: long-context RoPE scale over a 4,096-position pretraining context
     seed: int = 0
 
     @property
@@ -99,7 +100,7 @@ WORKLOADS = {
     # V2 shaped decode: 64 x 8192, 128 heads, query latent 1536 from hidden 5120
     "v2_decode": Workload("v2_decode", "bf16", 64, 8192, 128, query_path="v2",
                           hidden=5120, d_cq=1536),
-    # V2 long context decode: 4 x 131072
+    # V2 long context decode: 4 x 131072 (plain RoPE, base 10000)
     "v2_long": Workload("v2_long", "bf16", 4, 131072, 128, query_path="v2",
                         hidden=5120, d_cq=1536),
     # V2 causal prefill: 4096-token chunk appended to a 4096-token prefix

@@ -25,6 +25,16 @@ def f64(a, dtype):
     return W.to_f64(a, dtype)
 
 
+def rope_freq(w):
+    """What the oracle's RoPE takes for workload w: the frequency base, or the
+    long-context pair frequencies when the workload extends its context."""
+    return O.yarn_frequencies(W.D_R, w.rope_base, w.yarn_factor) if w.yarn_factor > 1 else w.rope_base
+
+
+def score_scale(w):
+    return O.yarn_softmax_scale(W.D_H, W.D_R, w.yarn_factor)
+
+
 def to_np(t):
     import torch
     if t.dtype == torch.bfloat16:
@@ -42,9 +52,10 @@ def oracle_decode(inp, b, heads=None, absorbed=False):
     L = int(inp.seq_lens[b])
     heads = np.arange(inp.w.n_h) if heads is None else np.asarray(heads)
     c = f64(inp.c_kv[b, :L], dt)
-    k_rot = O.cached_rope_key(f64(inp.k_raw[b, :L], dt), np.arange(L), inp.w.rope_base, store=dt)
-    q_rot = O.rope(f64(inp.q_r[b][heads], dt), L - 1, inp.w.rope_base)
-    args = (f64(inp.q_c[b][heads], dt), q_rot, c, k_rot, f64(inp.w_uk[heads], dt), f64(inp.w_uv[heads], dt))
+    k_rot = O.cached_rope_key(f64(inp.k_raw[b, :L], dt), np.arange(L), rope_freq(inp.w), store=dt)
+    q_rot = O.rope(f64(inp.q_r[b][heads], dt), L - 1, rope_freq(inp.w))
+    args = (f64(inp.q_c[b][heads], dt), q_rot, c, k_rot, f64(inp.w_uk[heads], dt), f64(inp.w_uv[heads], dt),
+            score_scale(inp.w))
     if absorbed:
         o, z, _ = O.attend_absorbed(*args)
         return o, z
@@ -57,7 +68,8 @@ def oracle_prefill(pinp, queries, heads=None):
     heads = np.arange(pinp.w.n_h) if heads is None else np.asarray(heads)
     return O.prefill(f64(pinp.q_c[:, heads], dt), f64(pinp.q_r[:, heads], dt), pinp.prefix,
                      f64(pinp.c_kv, dt), f64(pinp.k_raw, dt), f64(pinp.w_uk[heads], dt),
-                     f64(pinp.w_uv[heads], dt), pinp.w.rope_base, query_idx=queries, store=dt)
+                     f64(pinp.w_uv[heads], dt), rope_freq(pinp.w), score_scale(pinp.w), query_idx=queries,
+                     store=dt)
 
 
 def absorbed_layout(q32, dtype):
@@ -82,8 +94,8 @@ def oracle_decode_fp8(inp, b, heads=None):
     heads = np.arange(inp.w.n_h) if heads is None else np.asarray(heads)
     codes, scale = O.quantize_rows_fp8(f64(inp.c_kv[b, :L], "bf16"))
     c = O.dequantize_rows_fp8(codes, scale)
-    k_rot = O.cached_rope_key(f64(inp.k_raw[b, :L], "bf16"), np.arange(L), inp.w.rope_base, store="bf16")
-    q_rot = O.rope(f64(inp.q_r[b][heads], "bf16"), L - 1, inp.w.rope_base)
+    k_rot = O.cached_rope_key(f64(inp.k_raw[b, :L], "bf16"), np.arange(L), rope_freq(inp.w), store="bf16")
+    q_rot = O.rope(f64(inp.q_r[b][heads], "bf16"), L - 1, rope_freq(inp.w))
     o, z, _ = O.attend_absorbed(f64(inp.q_c[b][heads], "bf16"), q_rot, c, k_rot, f64(inp.w_uk[heads], "bf16"),
-                                f64(inp.w_uv[heads], "bf16"))
+                                f64(inp.w_uv[heads], "bf16"), score_scale(inp.w))
     return o, z

@@ -56,6 +56,17 @@ def test_dims_validation():
     nan_base = api.dims(16, rope_base=float("nan"))
     assert lib.mla_append_kv(ctypes.byref(nan_base), 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert b"rope_base" in lib.mla_last_error()
+    for kw, word in ((dict(yarn_factor=float("nan")), b"yarn_factor"), (dict(yarn_factor=-2.0), b"yarn_factor"),
+                     (dict(yarn_factor=40.0, yarn_orig_ctx=0.0), b"yarn_orig_ctx"),
+                     (dict(yarn_factor=40.0, yarn_alpha=32.0, yarn_beta=1.0), b"yarn_alpha"),
+                     (dict(yarn_factor=40.0, yarn_alpha=0.0), b"yarn_alpha")):
+        y = api.dims(16, **kw)
+        assert lib.mla_append_kv(ctypes.byref(y), 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1, kw
+        assert word in lib.mla_last_error(), kw
+    # a factor of 1 (or 0) is the plain RoPE: the YaRN fields are not looked at
+    off = api.dims(16, yarn_factor=1.0, yarn_orig_ctx=0.0, yarn_alpha=5.0, yarn_beta=1.0)
+    assert lib.mla_append_kv(ctypes.byref(off), 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) != 1 or \
+        b"yarn" not in lib.mla_last_error()
 
 
 def test_null_and_size_validation():

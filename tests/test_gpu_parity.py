@@ -404,3 +404,126 @@ def test_prefill_unabsorbed_two_sequences(api):
                         store=dtype)
         assert np.all(np.isfinite(got[b]))
         assert rel_err(got[b], ref) < TOL["bf16"]
+
+
+# ------------------------------------------------------- long-context RoPE
+YARN = dict(yarn_factor=40.0)            # DeepSeek-V2's scale over 4,096 pretraining positions
+# Bars under YaRN's temperature, which multiplies every logit by
+# (0.1 ln 40 + 1)^2 = 1.87 and sharpens the softmax so that a few heads'
+# outputs are ~20x the tensor's rms; max|err|/rms then reads the bf16 roundings
+# of the score's operands large.  fp64 models of exactly those roundings, on
+# the cases below:
+#   * 128-head absorbed form (query high part and P in bf16; the model follows
+#     the kernel's fp32 scores, 32-row tiles with the lazy reference and
+#     256-row splits, and matches the device to 4e-3): 5.0e-2 end to end,
+#     1.7e-2 (decode) and 2.2e-2 (prefill) from P alone;
+#   * unabsorbed form (expanded keys and values in bf16): 3.5e-2 from those
+#     roundings, 7e-3 with plain RoPE.
+# The 16-head absorbed kernel scores with hi + lo and keeps the bf16 bar.
+YARN_WIDE_TOL = 4e-2    # 128 heads, against the oracle given the kernel's bf16 query
+YARN_BF16_TOL = 6e-2    # end to end where the score takes single bf16 operands
+
+
+def test_yarn_rows_and_absorbed_queries(api):
+    """A1's RoPE key and A2's absorbed query with the long-context frequencies,
+    element by element, at the bars of the plain-RoPE tests (positions up to
+    160K, where the interpolated pairs matter)."""
+    n, n_h = 200, 128
+    c = W.random_storage(41, (n, 512), "bf16")
+    k = W.random_storage(42, (n, 64), "bf16")
+    pos = W.random_ints(43, 0, 163840, n).astype(np.int32)
+    pos[:3] = [0, 4095, 163839]
+    d = api.dims(n_h, **YARN)
+    freq = O.yarn_frequencies(64, 10000.0, 40.0)
+    cache = torch.full((n, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
+    api.append_kv(d, dev(c, "bf16"), dev(k, "bf16"), torch.from_numpy(pos).cuda(),
+                  torch.arange(n, dtype=torch.int64, device="cuda"), cache)
+    g = f64(to_np(cache)[:, 512:], "bf16")
+    ref = O.cached_rope_key(f64(k, "bf16"), pos, freq)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    assert np.all(np.abs(g - ref) <= ulp + 1e-30)
+    assert np.max(np.abs(g - O.cached_rope_key(f64(k, "bf16"), pos))) > 0.5   # not the plain frequencies
+    q_c = W.random_storage(44, (n, n_h, 128), "bf16")
+    q_r = W.random_storage(45, (n, n_h, 64), "bf16")
+    w_uk = W.random_storage(46, (n_h, 128, 512), "bf16", 512 ** -0.5)
+    q_lat = api.q_lat_empty(d, torch.bfloat16, n)
+    api.absorb_q(d, dev(q_c, "bf16"), dev(q_r, "bf16"), torch.from_numpy(pos).cuda(), dev(w_uk, "bf16"), q_lat)
+    got = api.q_lat_value(q_lat).cpu().numpy().astype(np.float64)
+    ref = O.absorb_query(f64(q_c, "bf16"), f64(q_r, "bf16"), pos, f64(w_uk, "bf16"), freq)
+    rms = np.sqrt(np.mean(np.square(ref)))
+    assert np.all(np.abs(got - ref) <= 1e-5 * rms + 2.0 ** -17 * np.abs(ref) * (1 + 2.0 ** -8))
+
+
+def _latent_oracle(q_lat, c, k_rot, L, scale, w_uv):
+    """Output of one query (all heads) from its absorbed query q_lat [n_h, 576]
+    over rows 0..L-1: the oracle's latent-space attention, then W^UV."""
+    rows = np.concatenate([c[:L], k_rot[:L]], axis=1)
+    return O.project_uv(O.latent_attention(q_lat, rows, L, scale), w_uv)
+
+
+@pytest.mark.parametrize("n_h", [128, 16])
+def test_yarn_decode_and_prefill(pipeline, n_h):
+    """Decode and causal prefill with the long-context RoPE (frequencies and
+    temperature), end to end through append, absorption and attention, at the
+    bars above.  At 128 heads the attention is also checked against the
+    oracle given the query the kernel reads (the device's bf16 high part; A2
+    is pinned above).  The plain-RoPE oracle misses by many times the bar
+    (the fields are honoured)."""
+    base = W.WORKLOADS["v2_decode"] if n_h == 128 else W.WORKLOADS["lite_decode"]
+    w = W.scaled(base, batch=2, seq_len=6000, **YARN)
+    inp = W.make_decode_inputs(w)
+    print(f"yarn decode n_h={n_h}", flush=True)
+    st = pipeline.DecodeState(inp, out_latent=True)
+    st.absorb()
+    st.attention()
+    st.combine()
+    out = st.out.cpu().numpy()
+    exact = np.stack([oracle_decode(inp, b, absorbed=True)[0] for b in range(w.batch)])
+    plain = W.make_decode_inputs(W.scaled(w, yarn_factor=0.0))
+    e_plain = rel_err(out, np.stack([oracle_decode(plain, b, absorbed=True)[0] for b in range(w.batch)]))
+    freq, scale = O.yarn_frequencies(64, 10000.0, 40.0), O.yarn_softmax_scale(128, 64, 40.0)
+    if n_h == 16:
+        ref = exact
+    else:
+        hi = st.q_lat[:, :, 0, :].float().cpu().numpy().astype(np.float64)
+        ref = []
+        for b in range(w.batch):
+            L = int(inp.seq_lens[b])
+            k_rot = O.cached_rope_key(f64(inp.k_raw[b, :L], "bf16"), np.arange(L), freq, store="bf16")
+            ref.append(_latent_oracle(hi[b], f64(inp.c_kv[b, :L], "bf16"), k_rot, L, scale, f64(inp.w_uv, "bf16")))
+        ref = np.stack(ref)
+    e, e_end = rel_err(out, ref), rel_err(out, exact)
+    print(f"yarn decode: {e:.3e}; end to end {e_end:.3e}; plain-RoPE oracle {e_plain:.3e}", flush=True)
+    if n_h == 16:
+        assert e_end < TOL["bf16"]
+    else:
+        assert e < YARN_WIDE_TOL and e_end < YARN_BF16_TOL
+    assert e_plain > 5 * YARN_BF16_TOL
+
+    pbase = W.WORKLOADS["v2_prefill"] if n_h == 128 else W.scaled(W.WORKLOADS["lite_decode"], batch=1)
+    prefix, chunk = 5000, 65
+    pw = W.scaled(pbase, seq_len=prefix + chunk, prefill_chunk=chunk, batch=1, **YARN)
+    pinp = W.make_prefill_inputs(pw)
+    heads = None if n_h == 16 else [0, 37, 127]
+    exact = oracle_prefill(pinp, range(chunk), heads)
+    pst = pipeline.PrefillState(pinp)
+    pst.step()
+    got = pst.out.cpu().numpy()[0]
+    pst.attend_unabsorbed()
+    got_u = pst.out.cpu().numpy()[0]
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(got_u))
+    if n_h == 16:
+        e_a, e_u = rel_err(got, exact), rel_err(got_u, exact)
+        print(f"yarn prefill absorbed {e_a:.3e}; unabsorbed {e_u:.3e}", flush=True)
+        assert e_a < TOL["bf16"] and e_u < YARN_BF16_TOL
+        return
+    hi = pst.q_lat[0, :, :, 0, :].float().cpu().numpy().astype(np.float64)   # [chunk, n_h, 576]
+    total = prefix + chunk
+    c = f64(pinp.c_kv, "bf16")
+    k_rot = O.cached_rope_key(f64(pinp.k_raw, "bf16"), np.arange(total), freq, store="bf16")
+    wuv = f64(pinp.w_uv, "bf16")[heads]
+    ref = np.stack([_latent_oracle(hi[i][heads], c, k_rot, prefix + i + 1, scale, wuv) for i in range(chunk)])
+    g = got[:, heads]
+    e, e_end, e_u = rel_err(g, ref), rel_err(g, exact), rel_err(got_u[:, heads], exact)
+    print(f"yarn prefill absorbed: {e:.3e}; end to end {e_end:.3e}; unabsorbed end to end {e_u:.3e}", flush=True)
+    assert e < YARN_WIDE_TOL and e_end < YARN_BF16_TOL and e_u < YARN_BF16_TOL
