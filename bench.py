@@ -242,8 +242,8 @@ def main():
                          "handed out in a seeded random order (0: contiguous sequence slots)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding of the path is described, not built.", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sharding the path over several GPUs is not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
