@@ -214,7 +214,9 @@ mla_status mla_decode_partials(const mla_dims* dims, mla_dtype dtype, int32_t ba
  *   LSE = log sum_s exp(lse_s);  z = sum_s exp(lse_s - LSE) z_s
  *   out[n][i][:] = w_uv[i] @ z      (w_uv [n_h][d_h][d_c]; out fp32 [n_q][n_h][d_h])
  *   out_latent (optional, may be NULL): z, fp32 [n_q][n_h][d_c]
- * n_q queries, each with num_splits partials laid out as in A3. */
+ * n_q queries, each with num_splits partials laid out as in A3.  A query
+ * whose every split is empty (lse = -inf: a sequence of length 0) gets
+ * z = 0 and out = 0. */
 mla_status mla_combine_project(const mla_dims* dims, mla_dtype dtype, int32_t n_q,
                                int32_t num_splits, const float* z_part,
                                const float* lse_part, const void* w_uv, float* out,

@@ -138,6 +138,50 @@ def test_splitkv_partials_f32(api):
     _partials_case(api, "f32", 16, [5, 300], 2)
 
 
+@pytest.mark.parametrize("n_h,dtype", [(128, "bf16"), (16, "bf16"), (32, "bf16"), (8, "bf16"), (16, "f32")])
+def test_decode_empty_sequences(api, n_h, dtype):
+    """Sequences of length 0 inside a batch (every kernel family): all their
+    splits are empty (lse = -inf, z = 0); the combine then gives them z = 0 and
+    out = 0, while the other sequences meet the oracle."""
+    zg, lg = _partials_case(api, dtype, n_h, [0, 37, 0, 500], 3, seed=50)
+    assert np.all(np.isneginf(lg[[0, 2]])) and np.all(zg[[0, 2]] == 0)
+    w_uv = W.random_storage(51, (n_h, 128, 512), dtype, 512 ** -0.5)
+    out = torch.full((4, n_h, 128), float("nan"), dtype=torch.float32, device="cuda")
+    lat = torch.full((4, n_h, 512), float("nan"), dtype=torch.float32, device="cuda")
+    api.combine_project(api.dims(n_h), torch.from_numpy(zg).cuda(), torch.from_numpy(lg).cuda(),
+                        dev(w_uv, dtype), out, lat)
+    o, z = out.cpu().numpy(), lat.cpu().numpy()
+    assert np.all(o[[0, 2]] == 0) and np.all(z[[0, 2]] == 0)
+    for n in (1, 3):
+        z_ref = O.combine_partials(zg[n].astype(np.float64), lg[n].astype(np.float64))[0]
+        assert rel_err(z[n], z_ref) < 1e-5
+        assert rel_err(o[n], O.project_uv(z_ref, f64(w_uv, dtype))) < 1e-4
+
+
+@pytest.mark.parametrize("name,n_h,opts", [("v2_decode", 128, {}), ("lite_ragged", 16, {}),
+                                           ("v2_decode", 128, dict(fp8=True)), ("lite_ragged", 16, dict(fp8=True)),
+                                           ("v2_decode", 128, dict(page_rows=64)),
+                                           ("lite_ragged", 16, dict(page_rows=32))])
+def test_decode_zero_length_on_device(pipeline, name, n_h, opts):
+    """A device-side length set to 0 after the split plan is fixed (the FP8
+    and paged caches included): that sequence's output and latent are exactly
+    0, the others are bitwise what they were."""
+    w = W.scaled(W.WORKLOADS[name], batch=4, seq_len=900, n_h=n_h)
+    st = pipeline.DecodeState(W.make_decode_inputs(w), out_latent=True, **opts)
+    print(f"zero length {name} {opts}", flush=True)
+    st.absorb()
+    st.attention()
+    st.combine()
+    out0, lat0 = st.out.clone(), st.out_latent.clone()
+    st.seq_lens[2] = 0
+    st.attention()
+    st.combine()
+    torch.cuda.synchronize()
+    assert torch.all(st.out[2] == 0) and torch.all(st.out_latent[2] == 0)
+    keep = [0, 1, 3]
+    assert torch.equal(st.out[keep], out0[keep]) and torch.equal(st.out_latent[keep], lat0[keep])
+
+
 # ------------------------------------------------------ A4 + A5 combine/lift
 @pytest.mark.parametrize("dtype,n_h,S,n_q", [("bf16", 128, 4, 45), ("bf16", 16, 1, 45), ("bf16", 16, 64, 45),
                                              ("f32", 16, 3, 45), ("bf16", 128, 64, 4), ("bf16", 128, 5, 45),
