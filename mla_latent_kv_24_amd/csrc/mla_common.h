@@ -158,8 +158,9 @@ hipError_t launch_slices_to_outputs(const float* part, int32_t slices, int32_t n
                                     uint16_t* out0, float* out1, hipStream_t st);
 // out[t][o] = sum_s part[s][t][o] (fp32)
 hipError_t launch_sum_slices(const float* part, int32_t slices, int64_t n_elems, float* out, hipStream_t st);
-// per row t: v = sum_s part[s][t][:d]; out[t][:] = bf16(v / sqrt(mean(v^2) + eps) * weight)
-hipError_t launch_rmsnorm_rows(const float* part, int32_t slices, int32_t n, int32_t d, const void* weight, float eps,
+// per row t: v = sum_s part[s][t][:d]; out[t][:] = bf16(v / sqrt(mean(v^2) + eps) * weight);
+// the partials are scratch (slices 0 and 1 may be overwritten)
+hipError_t launch_rmsnorm_rows(float* part, int32_t slices, int32_t n, int32_t d, const void* weight, float eps,
                                uint16_t* out, hipStream_t st);
 // out[i] = bf16(in[i])
 hipError_t launch_to_bf16(const float* in, int64_t n_elems, uint16_t* out, hipStream_t st);

@@ -98,26 +98,27 @@ __global__ __launch_bounds__(256) void gemm_partial_mfma_kernel(GemmArgs a) {
 
 // ------------------------------------------------------------------------
 // Few tokens (n <= 64, the decode step): the product streams the weights, so
-// a workgroup takes 256 outputs (wave w: 64 rows, as two 32-row MFMA tiles)
-// against all tokens (two 32-token tiles): every weight row is loaded once,
-// by its wave, into registers (two 128-deep batches in ping-pong), and the
-// activation chunk [64 tokens][128 k] is loaded once per workgroup into a
+// a workgroup takes 128 RT outputs (wave w: 32 RT rows, as RT 32-row MFMA
+// tiles) against all tokens (two 32-token tiles): every weight row is loaded
+// once, by its wave, into registers (two 128-deep batches in ping-pong), and
+// the activation chunk [64 tokens][128 k] is loaded once per workgroup into a
 // double-buffered LDS tile (16-B chunk kc of token row t at kc ^ (t & 15))
-// that all four waves read as the B operand.
+// that all four waves read as the B operand.  RT = 2 halves the activation
+// traffic per weight byte; RT = 1 doubles the workgroups for narrow products.
 // ------------------------------------------------------------------------
-constexpr int S_OUT = 256;
 constexpr int S_XBYTES = 64 * 128 * 2;   // one activation chunk in LDS
 
+template <int RT>
 __global__ __launch_bounds__(256, 2) void gemm_stream_mfma_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[2 * S_XBYTES];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, l32 = l & 31;
   const int ob = blockIdx.x, s = blockIdx.z;
-  const int o0 = S_OUT * ob + 64 * w;   // the wave's 64 rows (one side of split)
+  const int o0 = 128 * RT * ob + 32 * RT * w;   // the wave's 32 RT rows (one side of split)
   const int64_t dk = a.d_in;
   const uint16_t* wbase = (o0 < a.split) ? static_cast<const uint16_t*>(a.w0) + static_cast<int64_t>(o0) * dk
                                          : static_cast<const uint16_t*>(a.w1) + static_cast<int64_t>(o0 - a.split) * dk;
   const uint16_t* wr0 = wbase + static_cast<int64_t>(l32) * dk + 8 * g;         // rows o0 + l32
-  const uint16_t* wr1 = wbase + static_cast<int64_t>(32 + l32) * dk + 8 * g;    // rows o0 + 32 + l32
+  const uint16_t* wr1 = wbase + static_cast<int64_t>(32 + l32) * dk + 8 * g;    // rows o0 + 32 + l32 (RT = 2)
   const int k0 = s * a.k_per_slice;
   const int k1 = min(k0 + a.k_per_slice, a.d_in);
   const int nchunks = (k1 - k0) / 128;
@@ -145,12 +146,12 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_mfma_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       av[i] = *reinterpret_cast<const u32x4*>(wr0 + kb + 16 * i);
-      av[8 + i] = *reinterpret_cast<const u32x4*>(wr1 + kb + 16 * i);
+      if (RT == 2) av[8 + i] = *reinterpret_cast<const u32x4*>(wr1 + kb + 16 * i);
     }
   };
-  f32x16 acc[2][2];   // [row tile u][token tile tt]
+  f32x16 acc[RT][2];   // [row tile u][token tile tt]
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < RT; ++u)
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_mfma_kernel(GemmArgs a) {
         bv[tt] = *reinterpret_cast<const u32x4*>(xs + buf * S_XBYTES + 256 * t + 16 * ((2 * i + g) ^ (t & 15)));
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < RT; ++u)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
           acc[u][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[8 * u + i]),
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_mfma_kernel(GemmArgs a) {
     }
   };
 
-  u32x4 wa[16], wb[16], xv[4];
+  u32x4 wa[8 * RT], wb[8 * RT], xv[4];
   if (nchunks > 0) {
     xload(0, xv);
     wload(0, wa);
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_mfma_kernel(GemmArgs a) {
     const int t = 32 * tt + l32;
     if (t >= a.n) continue;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < RT; ++u) {
       const int obase = o0 + 32 * u + 4 * g;
       const f32x16& v = acc[u][tt];
       if (a.out0) {
@@ -233,9 +234,6 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_mfma_kernel(GemmArgs a) {
   }
 }
 
-static bool use_stream(int32_t n, int32_t d_in, int32_t d_out, int32_t split) {
-  return n <= 64 && d_in % 128 == 0 && d_out % S_OUT == 0 && split % S_OUT == 0;
-}
 
 // Generic partials: grid (ceil(d_out / 64), tokens, k slices), one output per thread.
 template <typename T>
@@ -262,18 +260,16 @@ __global__ __launch_bounds__(64) void gemm_partial_generic_kernel(GemmArgs a) {
   a.part[(static_cast<int64_t>(s) * a.n + t) * a.d_out + o] = acc;
 }
 
-// Split-K plan (slices of at least one 128-deep batch): the streaming kernel
-// aims at one round of 256 workgroups; the tile kernel at four workgroups per
-// CU, since each of its waves has about one load batch in flight.
-void gemm_plan(int32_t n, int32_t d_in, int32_t d_out, int32_t split, int32_t& k_slices, int32_t& k_per_slice) {
-  const bool stream = use_stream(n, d_in, d_out, split);
-  const int64_t tiles = stream ? d_out / S_OUT
-                               : static_cast<int64_t>((d_out + G_OUT - 1) / G_OUT) * ((n + G_TOK - 1) / G_TOK);
-  int64_t s = ((stream ? 256 : 1024) + tiles - 1) / tiles;
-  // the fp32 partials (n d_out 4 B per slice) stay within half the bytes the
-  // product moves anyway (weights and activations)
+constexpr int64_t kGemmCUs = 256;   // MI355X compute units (the plans are device independent)
+
+// Split-K slices (each at least one 128-deep batch) for `tiles` output tiles:
+// `want` slices, at most the cap that keeps the fp32 partials (n d_out 4 B per
+// slice) within half the bytes the product moves anyway (weights and
+// activations).
+static void plan_slices(int32_t n, int32_t d_in, int32_t d_out, int64_t want, int32_t& k_slices,
+                        int32_t& k_per_slice) {
   const int64_t cap = static_cast<int64_t>(d_in) * (d_out + n) / (4 * static_cast<int64_t>(std::max(n, 1)) * d_out);
-  s = std::min(s, std::max<int64_t>(1, cap));
+  int64_t s = std::min(want, std::max<int64_t>(1, cap));
   s = std::max<int64_t>(1, std::min<int64_t>(s, std::max(1, d_in / 128)));
   int64_t kr = (d_in + s - 1) / s;
   kr = (kr + 127) / 128 * 128;
@@ -281,11 +277,54 @@ void gemm_plan(int32_t n, int32_t d_in, int32_t d_out, int32_t split, int32_t& k
   k_slices = static_cast<int32_t>((d_in + kr - 1) / kr);
 }
 
+// The streaming kernel's plan.  Its workgroups all move the same bytes, so the
+// plan keeps them within one round of the 256 CUs (a few past 256 would double
+// some CUs' share and set the time), and of the row-tile sizes takes the one
+// with the most workgroups, then the fewer partial bytes (none for one
+// slice), then RT = 2 (half the activation reads).  rt = 0: not applicable.
+static void stream_plan(int32_t n, int32_t d_in, int32_t d_out, int32_t split, int& rt, int32_t& k_slices,
+                        int32_t& k_per_slice) {
+  rt = 0;
+  int64_t best_wg = -1, best_part = 0;
+  for (int r = 2; r >= 1; --r) {
+    if (!(n <= 64 && d_in % 128 == 0 && d_out % (128 * r) == 0 && split % (128 * r) == 0)) continue;
+    const int64_t tiles = d_out / (128 * r);
+    int32_t S, kps;
+    plan_slices(n, d_in, d_out, std::max<int64_t>(1, kGemmCUs / tiles), S, kps);
+    const int64_t wg = std::min<int64_t>(tiles * S, kGemmCUs);
+    const int64_t part = S > 1 ? static_cast<int64_t>(S) * n * d_out : 0;
+    if (wg > best_wg || (wg == best_wg && part < best_part)) {
+      best_wg = wg;
+      best_part = part;
+      rt = r;
+      k_slices = S;
+      k_per_slice = kps;
+    }
+  }
+}
+
+// Split-K plan: the streaming kernel as above; the tile kernel at four
+// workgroups per CU, since each of its waves has about one load batch in flight.
+void gemm_plan(int32_t n, int32_t d_in, int32_t d_out, int32_t split, int32_t& k_slices, int32_t& k_per_slice) {
+  int rt;
+  stream_plan(n, d_in, d_out, split, rt, k_slices, k_per_slice);
+  if (rt > 0) return;
+  const int64_t tiles = static_cast<int64_t>((d_out + G_OUT - 1) / G_OUT) * ((n + G_TOK - 1) / G_TOK);
+  plan_slices(n, d_in, d_out, (4 * kGemmCUs + tiles - 1) / tiles, k_slices, k_per_slice);
+}
+
 hipError_t launch_gemm_partial(const GemmArgs& a, int bf16, hipStream_t st) {
   if (a.n <= 0 || a.d_out <= 0) return hipSuccess;
   const bool mfma = bf16 && a.d_in % 128 == 0 && a.d_out % G_OUT == 0 && a.split % G_OUT == 0;
-  if (bf16 && use_stream(a.n, a.d_in, a.d_out, a.split)) {
-    gemm_stream_mfma_kernel<<<dim3(a.d_out / S_OUT, 1, a.k_slices), 256, 0, st>>>(a);
+  int rt = 0;
+  if (bf16) {
+    int32_t S, kps;
+    stream_plan(a.n, a.d_in, a.d_out, a.split, rt, S, kps);
+  }
+  if (rt == 2) {
+    gemm_stream_mfma_kernel<2><<<dim3(a.d_out / 256, 1, a.k_slices), 256, 0, st>>>(a);
+  } else if (rt == 1) {
+    gemm_stream_mfma_kernel<1><<<dim3(a.d_out / 128, 1, a.k_slices), 256, 0, st>>>(a);
   } else if (mfma) {
     const dim3 grid(a.d_out / G_OUT, (a.n + G_TOK - 1) / G_TOK, a.k_slices);
     gemm_partial_mfma_kernel<<<grid, 256, 0, st>>>(a);
@@ -310,6 +349,31 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(const float* part, int3
   out[i] = v;
 }
 
+// Four elements per thread (n_elems a multiple of 4, 16-B aligned arrays),
+// the loads of SB slices in flight together; each element still sums its
+// slices in order, so the result is the scalar kernel's bit for bit.
+constexpr int SB = 4;
+__device__ __forceinline__ f32x4 sum_slices4(const float* part, int32_t slices, int64_t n_elems, int64_t i) {
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < slices; s0 += SB) {
+    f32x4 r[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j)
+      r[j] = (s0 + j < slices) ? *reinterpret_cast<const f32x4*>(part + (s0 + j) * n_elems + i)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < SB; ++j) v += r[j];
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(256) void sum_slices4_kernel(const float* part, int32_t slices, int64_t n_elems,
+                                                          float* out) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= n_elems) return;
+  *reinterpret_cast<f32x4*>(out + i) = sum_slices4(part, slices, n_elems, i);
+}
+
 // Slice sums of [n][d_out] partials to two outputs: columns < split as bf16
 // rows of out0 [n][split], the rest as fp32 rows of out1 [n][d_out - split].
 __global__ __launch_bounds__(256) void slices_to_outputs_kernel(const float* part, int32_t slices, int32_t n,
@@ -328,49 +392,77 @@ __global__ __launch_bounds__(256) void slices_to_outputs_kernel(const float* par
     out1[t * (d_out - split) + (o - split)] = v;
 }
 
+// Four elements per thread: d_out and split multiples of 4, 16-B aligned arrays.
+__global__ __launch_bounds__(256) void slices_to_outputs4_kernel(const float* part, int32_t slices, int32_t n,
+                                                                 int32_t d_out, int32_t split, uint16_t* out0,
+                                                                 float* out1) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  const int64_t n_elems = static_cast<int64_t>(n) * d_out;
+  if (i >= n_elems) return;
+  const f32x4 v = sum_slices4(part, slices, n_elems, i);
+  const int64_t t = i / d_out;
+  const int o = static_cast<int>(i - t * d_out);
+  if (o < split)
+    *reinterpret_cast<uint2*>(out0 + t * split + o) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  else
+    *reinterpret_cast<f32x4*>(out1 + t * (d_out - split) + (o - split)) = v;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 hipError_t launch_slices_to_outputs(const float* part, int32_t slices, int32_t n, int32_t d_out, int32_t split,
                                     uint16_t* out0, float* out1, hipStream_t st) {
   const int64_t n_elems = static_cast<int64_t>(n) * d_out;
   if (n_elems <= 0) return hipSuccess;
-  slices_to_outputs_kernel<<<static_cast<unsigned>((n_elems + 255) / 256), 256, 0, st>>>(part, slices, n, d_out, split,
-                                                                                        out0, out1);
+  if (d_out % 4 == 0 && split % 4 == 0 && aligned16(part) && (reinterpret_cast<uintptr_t>(out0) & 7) == 0 &&
+      aligned16(out1))
+    slices_to_outputs4_kernel<<<static_cast<unsigned>((n_elems / 4 + 255) / 256), 256, 0, st>>>(
+        part, slices, n, d_out, split, out0, out1);
+  else
+    slices_to_outputs_kernel<<<static_cast<unsigned>((n_elems + 255) / 256), 256, 0, st>>>(part, slices, n, d_out,
+                                                                                          split, out0, out1);
   return hipGetLastError();
 }
 
 hipError_t launch_sum_slices(const float* part, int32_t slices, int64_t n_elems, float* out, hipStream_t st) {
   if (n_elems <= 0) return hipSuccess;
-  sum_slices_kernel<<<static_cast<unsigned>((n_elems + 255) / 256), 256, 0, st>>>(part, slices, n_elems, out);
+  if (n_elems % 4 == 0 && aligned16(part) && aligned16(out))
+    sum_slices4_kernel<<<static_cast<unsigned>((n_elems / 4 + 255) / 256), 256, 0, st>>>(part, slices, n_elems, out);
+  else
+    sum_slices_kernel<<<static_cast<unsigned>((n_elems + 255) / 256), 256, 0, st>>>(part, slices, n_elems, out);
   return hipGetLastError();
 }
 
 // One workgroup per row: the slices summed in order, the mean square reduced
 // over the workgroup, the row normalised, weighted (bf16 weight or none) and
-// stored as bf16.  d <= 256 * RN_PER.
+// stored as bf16.  d <= 256 * RN_PER.  A thread's loads of RN_SB slices of all
+// its columns are in flight together.
 constexpr int RN_PER = 16;
+constexpr int RN_SB = 8;
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* part, int32_t slices, int32_t n, int32_t d,
                                                            const uint16_t* weight, float eps, uint16_t* out) {
   __shared__ float red[4];
   const int t = blockIdx.x, tid = threadIdx.x;
   const int64_t ss = static_cast<int64_t>(n) * d;
+  const float* p = part + static_cast<int64_t>(t) * d + tid;
   float v[RN_PER];
+#pragma unroll
+  for (int i = 0; i < RN_PER; ++i) v[i] = 0.f;
+  for (int s0 = 0; s0 < slices; s0 += RN_SB) {
+    float r[RN_SB][RN_PER];
+#pragma unroll
+    for (int j = 0; j < RN_SB; ++j)
+#pragma unroll
+      for (int i = 0; i < RN_PER; ++i)
+        r[j][i] = (tid + 256 * i < d && s0 + j < slices) ? p[(s0 + j) * ss + 256 * i] : 0.f;
+#pragma unroll
+    for (int j = 0; j < RN_SB; ++j)
+#pragma unroll
+      for (int i = 0; i < RN_PER; ++i) v[i] += r[j][i];   // each column in slice order
+  }
   float sq = 0.f;
 #pragma unroll
-  for (int i = 0; i < RN_PER; ++i) {
-    const int o = tid + 256 * i;
-    float x = 0.f;
-    if (o < d) {
-      const float* p = part + static_cast<int64_t>(t) * d + o;
-      for (int s0 = 0; s0 < slices; s0 += 8) {   // eight slice loads in flight, summed in order
-        float r[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) r[j] = (s0 + j < slices) ? p[(s0 + j) * ss] : 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x += r[j];
-      }
-    }
-    v[i] = x;
-    sq = fmaf(x, x, sq);
-  }
+  for (int i = 0; i < RN_PER; ++i) sq = fmaf(v[i], v[i], sq);
   for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
   if ((tid & 63) == 0) red[tid >> 6] = sq;
   __syncthreads();
@@ -383,11 +475,73 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* part, in
   }
 }
 
-hipError_t launch_rmsnorm_rows(const float* part, int32_t slices, int32_t n, int32_t d, const void* weight, float eps,
+// Two passes for several slices and d a multiple of 256, so that the slice
+// loads spread over n * d / 256 workgroups instead of n:
+//   rowsum_kernel, per (row t, 256-column chunk c): one thread per column sums
+//     the slices in order (all loads in flight) and writes the sum over slice
+//     0's element, which only it reads; the chunk's sum of squares goes to
+//     slice 1's element (t, 256 c), which only this workgroup reads, after
+//     every thread of it has read its slices;
+//   rownorm_kernel, per row: the chunks' sums of squares in chunk order, then
+//     the row normalised, weighted and stored as bf16.
+constexpr int RS_BATCH = 16;
+__global__ __launch_bounds__(256) void rowsum_kernel(float* part, int32_t slices, int32_t n, int32_t d) {
+  __shared__ float red[4];
+  const int t = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  const int64_t ss = static_cast<int64_t>(n) * d;
+  float* p = part + static_cast<int64_t>(t) * d + 256 * c + tid;
+  float v = 0.f;
+  for (int s0 = 0; s0 < slices; s0 += RS_BATCH) {
+    float r[RS_BATCH];
+#pragma unroll
+    for (int j = 0; j < RS_BATCH; ++j) r[j] = (s0 + j < slices) ? p[(s0 + j) * ss] : 0.f;
+#pragma unroll
+    for (int j = 0; j < RS_BATCH; ++j) v += r[j];
+  }
+  float sq = v * v;
+  for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+  if ((tid & 63) == 0) red[tid >> 6] = sq;
+  __syncthreads();   // every thread has read its slices
+  p[0] = v;
+  if (tid == 0) p[ss] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ __launch_bounds__(256) void rownorm_kernel(const float* part, int32_t n, int32_t d, const uint16_t* weight,
+                                                      float eps, uint16_t* out) {
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int64_t ss = static_cast<int64_t>(n) * d;
+  const float* row = part + static_cast<int64_t>(t) * d;
+  const int chunks = d / 256;   // <= RN_PER
+  float cs[RN_PER], x[RN_PER], wv[RN_PER];  // every load in flight together
+#pragma unroll
+  for (int c = 0; c < RN_PER; ++c) cs[c] = (c < chunks) ? row[ss + 256 * c] : 0.f;
+#pragma unroll
+  for (int i = 0; i < RN_PER; ++i) {
+    x[i] = (i < chunks) ? row[tid + 256 * i] : 0.f;
+    wv[i] = (i < chunks && weight) ? bf16_to_f32(weight[tid + 256 * i]) : 1.f;
+  }
+  float sq = 0.f;
+#pragma unroll
+  for (int c = 0; c < RN_PER; ++c) sq += cs[c];   // chunk order
+  const float inv = 1.0f / sqrtf(sq / static_cast<float>(d) + eps);
+#pragma unroll
+  for (int i = 0; i < RN_PER; ++i) {
+    const int o = tid + 256 * i;
+    if (i < chunks) out[static_cast<int64_t>(t) * d + o] = f32_to_bf16(x[i] * inv * wv[i]);
+  }
+}
+
+hipError_t launch_rmsnorm_rows(float* part, int32_t slices, int32_t n, int32_t d, const void* weight, float eps,
                                uint16_t* out, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   if (d > 256 * RN_PER) return hipErrorInvalidValue;
-  rmsnorm_rows_kernel<<<n, 256, 0, st>>>(part, slices, n, d, static_cast<const uint16_t*>(weight), eps, out);
+  const uint16_t* wt = static_cast<const uint16_t*>(weight);
+  if (slices >= 2 && d % 256 == 0) {
+    rowsum_kernel<<<dim3(n, d / 256), 256, 0, st>>>(part, slices, n, d);
+    rownorm_kernel<<<n, 256, 0, st>>>(part, n, d, wt, eps, out);
+  } else {
+    rmsnorm_rows_kernel<<<n, 256, 0, st>>>(part, slices, n, d, wt, eps, out);
+  }
   return hipGetLastError();
 }
 
@@ -396,9 +550,22 @@ __global__ __launch_bounds__(256) void to_bf16_kernel(const float* in, int64_t n
   if (i < n_elems) out[i] = f32_to_bf16(in[i]);
 }
 
+// Eight elements per thread (n_elems a multiple of 8, 16-B aligned arrays).
+__global__ __launch_bounds__(256) void to_bf16_x8_kernel(const float* in, int64_t n_elems, uint16_t* out) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (i >= n_elems) return;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(in + i);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(in + i + 4);
+  *reinterpret_cast<u32x4*>(out + i) =
+      u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+}
+
 hipError_t launch_to_bf16(const float* in, int64_t n_elems, uint16_t* out, hipStream_t st) {
   if (n_elems <= 0) return hipSuccess;
-  to_bf16_kernel<<<static_cast<unsigned>((n_elems + 255) / 256), 256, 0, st>>>(in, n_elems, out);
+  if (n_elems % 8 == 0 && aligned16(in) && aligned16(out))
+    to_bf16_x8_kernel<<<static_cast<unsigned>((n_elems / 8 + 255) / 256), 256, 0, st>>>(in, n_elems, out);
+  else
+    to_bf16_kernel<<<static_cast<unsigned>((n_elems + 255) / 256), 256, 0, st>>>(in, n_elems, out);
   return hipGetLastError();
 }
 
