@@ -335,6 +335,38 @@ def main():
         torch.cuda.synchronize()
         parts[nm] = round(e0.elapsed_time(e1) / (rounds * REPS) * 1e3, 2)   # microseconds
 
+    # Informational, after the timed region:
+    # * the same step with the 256 MB Infinity Cache flushed before each one
+    #   by reading 512 MB outside the events (clean lines, as when the other
+    #   layers' caches stream in between; a write flush would leave dirty lines
+    #   for the step to write back): the attention kernel and the whole step;
+    # * a 1 GiB device-to-device copy, the board's plain streaming rate.
+    F = min(args.steps, 50)
+    flush_buf = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")   # 512 MB
+    flush_sum = torch.zeros((), dtype=torch.float32, device="cuda")
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(F)]
+    for i in range(F):
+        torch.sum(flush_buf, dim=0, out=flush_sum)
+        s0, a0, a1, s1 = fev[i]
+        s0.record()
+        run_step(a0, a1)
+        s1.record()
+    torch.cuda.synchronize()
+    flushed_attn_us = float(np.mean([a0.elapsed_time(a1) for _, a0, a1, _ in fev])) * 1e3
+    flushed_step_us = float(np.mean([s0.elapsed_time(s1) for s0, _, _, s1 in fev])) * 1e3
+    del flush_buf
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9   # bytes read + written
+    del src, dst
+
     ms_per_step = elapsed / args.steps * 1e3
     value = tokens * args.steps / elapsed
     n_h = w.n_h
@@ -371,6 +403,10 @@ def main():
                      "mfma_tflops": round(tflops, 1),
                      "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
         "step_breakdown_us": parts,
+        "generated_tokens_per_s": round(w.batch / (ms_per_step * 1e-3), 1),   # one per sequence per step
+        "cache_flushed": {"kernel_us": round(flushed_attn_us, 2), "step_us": round(flushed_step_us, 2),
+                          "achieved_gbs": round(alg_bytes / (flushed_attn_us * 1e-6) / 1e9, 1), "steps": F},
+        "copy_gbs": round(copy_gbs, 1),
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
