@@ -204,3 +204,30 @@ def test_projection_entry_points_validation():
     assert lib.mla_output_projection(d, 64, 0, FAKE, FAKE, FAKE, FAKE, oneed, None) == 1
     assert lib.mla_output_projection(d, 64, 5120, FAKE, None, FAKE, FAKE, oneed, None) == 1
     assert lib.mla_output_projection(d, 64, 5120, FAKE, FAKE, FAKE, FAKE, oneed - 1, None) == 3
+
+
+def test_fp8_entry_points_validation():
+    """The FP8 cache's entry points reject bad descriptors and sizes before any
+    device work (no GPU needed: every pointer here is fake)."""
+    lib = api.raw()
+    d = ctypes.byref(api.dims(128))
+    good = api.FP8Cache(FAKE, FAKE, FAKE)
+    no_scale = api.FP8Cache(FAKE, FAKE, None)
+    for cache, word in ((None, b"descriptor"), (no_scale, b"NULL array")):
+        c = ctypes.byref(cache) if cache is not None else None
+        assert lib.mla_append_kv_fp8(d, 4, FAKE, FAKE, FAKE, FAKE, c, None) == 1
+        assert word in lib.mla_last_error()
+        assert lib.mla_decode_partials_fp8(d, 2, FAKE, c, 100, FAKE, 100, 1, FAKE, FAKE, None) == 1
+        assert lib.mla_prefill_fp8(d, 1, 8, FAKE, c, 100, FAKE, 10, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+        assert word in lib.mla_last_error()
+    g = ctypes.byref(good)
+    assert lib.mla_append_kv_fp8(d, 0, None, None, None, None, None, None) == 0          # no-op
+    assert lib.mla_append_kv_fp8(d, -1, FAKE, FAKE, FAKE, FAKE, g, None) == 1
+    assert lib.mla_decode_partials_fp8(d, 2, FAKE, g, 50, FAKE, 100, 1, FAKE, FAKE, None) == 1   # stride < max len
+    # prefill: prefix + chunk beyond the stride, empty chunk, workspace too small
+    assert lib.mla_prefill_fp8(d, 1, 8, FAKE, g, 100, FAKE, 95, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert b"cache_seq_stride" in lib.mla_last_error()
+    assert lib.mla_prefill_fp8(d, 1, 0, FAKE, g, 100, FAKE, 10, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.mla_prefill_fp8(d, 1, 8, FAKE, g, 100, FAKE, 10, FAKE, FAKE, FAKE, 16, None) == 3
+    f32 = ctypes.byref(api.dims(128, d_hR=32))
+    assert lib.mla_prefill_fp8(f32, 1, 8, FAKE, g, 100, FAKE, 10, FAKE, FAKE, FAKE, 1 << 30, None) == 2
