@@ -183,10 +183,11 @@ __global__ __launch_bounds__(256) void combine_generic_kernel(CombineArgs a) {
 hipError_t launch_combine(const CombineArgs& a, int bf16, hipStream_t st) {
   if (a.n_q <= 0) return hipSuccess;
   if (bf16 && a.d_c == D_C && a.d_h == D_H && a.num_splits <= CMB_MAX_SPLITS) {
-    // query block: the largest of 32, 16, 8, 4 that still gives >= 256
-    // workgroups (W^UV is read once per block, the partials once in all)
+    // query block: the largest of 32, 16, ..., 1 that still gives >= 256
+    // workgroups (W^UV is read once per block, mostly from the L2 of the XCD
+    // that holds the head's blocks; the partials once in all)
     int qb = 32;
-    while (qb > 4 && static_cast<int64_t>(a.n_h) * ((a.n_q + qb - 1) / qb) < 256) qb >>= 1;
+    while (qb > 1 && static_cast<int64_t>(a.n_h) * ((a.n_q + qb - 1) / qb) < 256) qb >>= 1;
     const dim3 grid(a.n_h, (a.n_q + qb - 1) / qb);
     if (a.num_splits <= 4)
       combine_mfma_kernel<4><<<grid, 256, 0, st>>>(a, qb);
