@@ -314,7 +314,8 @@ def main():
         run_step(*ev[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    attn_times = [a.elapsed_time(b) for a, b in ev]
+    attn_ms = float(np.mean(attn_times))
 
     # Per-stage breakdown (informational, after the timed region): each stage
     # captured as REPS back-to-back launches, bracketed by HIP events.
@@ -400,6 +401,7 @@ def main():
                      "traffic": traffic,
                      "kernel": "splitkv_fp8_wide_kernel" if args.fp8_cache else "splitkv_wide_kernel",
                      "kernel_us": round(attn_ms * 1e3, 2),
+                     "kernel_us_median": round(float(np.median(attn_times)) * 1e3, 2),
                      "mfma_tflops": round(tflops, 1),
                      "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
         "step_breakdown_us": parts,
