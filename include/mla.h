@@ -383,10 +383,19 @@ mla_status mla_decode_fp8(const mla_dims* dims, int32_t batch, const void* q_lat
                           float* out, float* out_latent, void* workspace,
                           size_t workspace_bytes, void* stream);
 
-/* A6 over the FP8 cache: mla_prefill's causal chunk (query i of sequence b at
- * position prefix_lens[b] + i, bf16 absorbed queries [batch][chunk][n_h]...,
- * w_uv bf16) over rows [E4M3(codes) * scale ; rope]; the workspace is
- * mla_prefill_workspace_bytes(dims, MLA_BF16, batch, chunk, max_prefix_len). */
+/* A6 over the FP8 cache: mla_prefill's causal chunk over rows
+ * [E4M3(codes) * scale ; rope].  Query i of sequence b sits at position
+ * prefix_lens[b] + i and attends rows 0..prefix_lens[b] + i, which must be
+ * written (mla_append_kv_fp8) at rows b * cache_seq_stride + j.
+ *   q_lat    bf16 absorbed queries [batch][chunk][n_h][2][d_c + d_hR] (A2)
+ *   prefix_lens [batch] (device), each in [0, max_prefix_len]
+ *   w_uv     bf16 [n_h][d_h][d_c];  out fp32 [batch][chunk][n_h][d_h]
+ *   workspace at least mla_prefill_workspace_bytes(dims, MLA_BF16, batch,
+ *            chunk, max_prefix_len) bytes (the split partials)
+ * Errors: bf16 dims only (MLA_ERR_UNSUPPORTED otherwise), NULL pointers or
+ * arrays in the descriptor, chunk < 1, max_prefix_len + chunk beyond
+ * cache_seq_stride (MLA_ERR_INVALID_ARGUMENT), a short workspace
+ * (MLA_ERR_WORKSPACE_TOO_SMALL). */
 mla_status mla_prefill_fp8(const mla_dims* dims, int32_t batch, int32_t chunk, const void* q_lat,
                            const mla_fp8_cache* cache, int64_t cache_seq_stride,
                            const int32_t* prefix_lens, int32_t max_prefix_len, const void* w_uv,
