@@ -156,3 +156,24 @@ def test_prefill_fp8(api, n_h, prefix, chunk):
     e = rel_err(got, ref)
     print(f"fp8 prefill parity: {e:.3e}")
     assert np.all(np.isfinite(got)) and e < TOL["bf16"]
+
+
+def test_decode_fp8_long_context_rope(pipeline):
+    """The FP8 cache under the long-context RoPE (YaRN at scale 40: its pair
+    frequencies in the appended keys and the absorbed queries, its temperature
+    in the score), 16 heads over 6,000 rows, against the oracle on its own
+    dequantised rows with the same frequencies and scale.  The 16-head kernel
+    scores with hi + lo queries, so the bf16 bar applies."""
+    w = W.scaled(W.WORKLOADS["lite_decode"], batch=2, seq_len=6000, yarn_factor=40.0)
+    inp = W.make_decode_inputs(w)
+    st = pipeline.DecodeState(inp, out_latent=True, fp8=True)
+    st.absorb()
+    st.attention()
+    st.combine()
+    out = st.out.cpu().numpy()
+    refs = [oracle_decode_fp8(inp, b) for b in range(w.batch)]
+    e = rel_err(out, np.stack([r[0] for r in refs]))
+    plain = W.make_decode_inputs(W.scaled(w, yarn_factor=0.0))
+    e_plain = rel_err(out, np.stack([oracle_decode_fp8(plain, b)[0] for b in range(w.batch)]))
+    print(f"fp8 yarn decode: {e:.3e} (plain-RoPE oracle {e_plain:.3e})")
+    assert e < TOL["bf16"] and e_plain > 10 * TOL["bf16"]
