@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 8
+#define MLA_ABI_VERSION 9
 
 typedef enum {
   MLA_OK = 0,
@@ -130,17 +130,19 @@ mla_status mla_append_kv_from_hidden(const mla_dims* dims, mla_dtype dtype, int3
  * Each absorbed query row v (d_c + d_hR values) is formed in fp32:
  *     v[0:d_c] = sum_d q_c[n][i][d] * w_uk[i][d][:]   (fp32 sum)
  *     v[d_c:]  = RoPE(q_r[n][i], q_pos[n])
- * and written to q_lat in the "absorbed query layout" of the storage dtype:
- *   MLA_F32:  float    [n_q][n_h][d_c + d_hR]      q_lat[n][i][e] = v[e]
- *   MLA_BF16: bfloat16 [n_q][n_h][2][d_c + d_hR]   part 0 = hi = bf16(v),
- *             part 1 = lo = bf16(v - hi), both rounded to nearest even, so
- *             hi + lo carries v to ~2^-17 relative.  hi is the matrix-core
- *             operand; lo refines it where a path needs more precision.
- * Both layouts take (d_c + d_hR) * 4 bytes per head.  q_c, q_r and w_uk have
- * the storage dtype. */
+ * and stored as one row per (query, head) in the storage dtype:
+ *   q_lat    [n_q][n_h][d_c + d_hR]  v (MLA_F32), or hi = bf16(v) (MLA_BF16)
+ *   q_lat_lo [n_q][n_h][d_c + d_hR]  optional, MLA_BF16 only (NULL otherwise):
+ *            lo = bf16(v - hi); both rounded to nearest even, so hi + lo
+ *            carries v to ~2^-17 relative.  NULL: lo is not written.
+ * q_c, q_r and w_uk have the storage dtype.
+ * Why a second plane: the matrix cores take bf16 operands, and a score from
+ * the rounded query alone is off by a relative ~2^-9 per row; the attention
+ * entry points below refine the score with lo wherever that would show (see
+ * mla_precise_rows), and read nothing else of it. */
 mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q,
                         const void* q_c, const void* q_r, const int32_t* q_pos,
-                        const void* w_uk, void* q_lat, void* stream);
+                        const void* w_uk, void* q_lat, void* q_lat_lo, void* stream);
 
 /* The query path from hidden states into A2 (review section 2: queries pass
  * through a 1,536-wide latent; DeepSeek-V3 report, Metode 1: c^Q; the latent
@@ -149,7 +151,7 @@ mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q,
  *   then q_lat = A2(q^C, q^R, q_pos, w_uk) exactly as mla_absorb_q.
  *   h [n_q][d_model], w_dq [d_cq][d_model], norm_weight [d_cq] or NULL,
  *   w_uq [n_h * d_h][d_cq] (head i = rows i*d_h ..), w_qr [n_h * d_hR][d_cq],
- *   all bf16; q_pos, w_uk, q_lat as mla_absorb_q (bf16 layout).
+ *   all bf16; q_pos, w_uk, q_lat, q_lat_lo as mla_absorb_q (bf16).
  * c^Q and q^C pass between the launches as bf16 (fp32 sums, one rounding
  * each: they are matrix-core operands), q^R as fp32, in `workspace`
  * (mla_absorb_q_from_hidden_workspace_bytes).
@@ -163,8 +165,8 @@ mla_status mla_absorb_q_from_hidden(const mla_dims* dims, int32_t n_q, int32_t d
                                     int32_t d_cq, const void* h, const void* w_dq,
                                     const void* norm_weight, double eps, const void* w_uq,
                                     const void* w_qr, const int32_t* q_pos, const void* w_uk,
-                                    void* q_lat, void* workspace, size_t workspace_bytes,
-                                    void* stream);
+                                    void* q_lat, void* q_lat_lo, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /* The output projection after A5 (review section 2: u_t = sum_i O_i U^V_i
  * sum_j a_ij c_j):  out[t] = W^O o_t, o [n_q][n_h][d_h] fp32 (A5's output),
@@ -186,15 +188,30 @@ int32_t mla_decode_num_splits(const mla_dims* dims, mla_dtype dtype, int32_t bat
                               int32_t max_seq_len);
 int64_t mla_split_rows(int32_t max_seq_len, int32_t num_splits);
 
+/* Precision of the bf16 attention (review section 3: l_ij and a_ij per head).
+ * A query that attends fewer rows than mla_precise_rows() is scored with
+ * hi + lo of its absorbed query and its softmax weights enter the value
+ * product as a bf16 hi + lo pair: the result then matches the exact
+ * attention of the stored values to ~1e-5 of the output rms.  Longer queries
+ * (32 to 128 heads, plain RoPE) score with hi alone and round each weight to
+ * bf16 once (a relative ~2^-9 on each score and weight, which averages out
+ * over thousands of rows).  Returns 0 for MLA_F32 (exact fp32, no lo plane),
+ * INT32_MAX where every query takes hi + lo (16 heads, n_h without a
+ * matrix-core kernel, and yarn_factor > 1, whose temperature sharpens the
+ * softmax so that single bf16 operands show at every length).  Callers pass
+ * q_lat_lo to the calls below whenever some query attends fewer rows; without
+ * it, lo reads as zero (the hi-only score). */
+int32_t mla_precise_rows(const mla_dims* dims, mla_dtype dtype);
+
 /* A3 -- split-KV latent attention.  For query n (one per sequence), split s
  * and head i, over rows j of split s (review section 3, softmax_j restricted
  * to a range of j and re-associated):
  *   lse_part[n][s][i]      = log sum_j exp(l_ij)                (natural log)
  *   z_part[n][s][i][0:d_c] = sum_j exp(l_ij - lse) * c_j        (fp32)
  * An empty split stores lse = -inf and z = 0.
- *   q_lat: batch queries in the absorbed query layout of `dtype` (output of
- *   A2).  The bf16 MFMA kernels use hi alone for n_h >= 32 and hi + lo for
- *   n_h = 16; every other path uses hi + lo.  The cache has the storage dtype.
+ *   q_lat, q_lat_lo: the batch's absorbed queries (A2; q_lat_lo optional,
+ *   bf16 only, read by the queries that mla_precise_rows() names).  The cache
+ *   has the storage dtype.
  *   cache rows of sequence b start at row b * cache_seq_stride
  *   seq_lens [batch]: 1 <= len <= min(max_seq_len, cache_seq_stride)
  *   max_seq_len (host) bounds every len; it fixes the split rows.
@@ -204,7 +221,7 @@ int64_t mla_split_rows(int32_t max_seq_len, int32_t num_splits);
  * A device-side length outside [1, stride] is clamped for memory safety
  * (len < 1 behaves as an empty sequence: lse = -inf for every split). */
 mla_status mla_decode_partials(const mla_dims* dims, mla_dtype dtype, int32_t batch,
-                               const void* q_lat, const void* cache,
+                               const void* q_lat, const void* q_lat_lo, const void* cache,
                                int64_t cache_seq_stride, const int32_t* seq_lens,
                                int32_t max_seq_len, int32_t num_splits,
                                float* z_part, float* lse_part, void* stream);
@@ -227,7 +244,8 @@ mla_status mla_combine_project(const mla_dims* dims, mla_dtype dtype, int32_t n_
 size_t mla_decode_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t batch,
                                   int32_t max_seq_len);
 mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch,
-                      const void* q_lat, const void* cache, int64_t cache_seq_stride,
+                      const void* q_lat, const void* q_lat_lo, const void* cache,
+                      int64_t cache_seq_stride,
                       const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv,
                       float* out, float* out_latent, void* workspace,
                       size_t workspace_bytes, void* stream);
@@ -237,15 +255,16 @@ mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch,
  * sits at position prefix_lens[b] + i and attends to rows 0..prefix_lens[b]+i
  * (inclusive causal mask), with the same score, softmax and W^UV lift as
  * decode (review section 3).
- *   q_lat: batch * chunk queries in the absorbed query layout (query index
- *   b * chunk + i), prefix_lens [batch] (device,
+ *   q_lat, q_lat_lo: batch * chunk absorbed queries (A2; query index
+ *   b * chunk + i; q_lat_lo as in mla_decode_partials), prefix_lens [batch] (device,
  *   0 <= prefix <= max_prefix_len), max_prefix_len (host) with
  *   max_prefix_len + chunk <= cache_seq_stride,
  *   out fp32 [batch][chunk][n_h][d_h]. */
 size_t mla_prefill_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t batch,
                                    int32_t chunk, int32_t max_prefix_len);
 mla_status mla_prefill(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk,
-                       const void* q_lat, const void* cache, int64_t cache_seq_stride,
+                       const void* q_lat, const void* q_lat_lo, const void* cache,
+                       int64_t cache_seq_stride,
                        const int32_t* prefix_lens, int32_t max_prefix_len,
                        const void* w_uv, float* out, void* workspace,
                        size_t workspace_bytes, void* stream);
@@ -266,8 +285,10 @@ mla_status mla_prefill(const mla_dims* dims, mla_dtype dtype, int32_t batch, int
  *   batch * n_h * round_up(max_prefix_len + chunk, 128) rows of 1,152 B).
  * bf16 storage and n_h a multiple of 8 only (else MLA_ERR_UNSUPPORTED).
  * Precision: queries that see few keys (a workgroup of 256 queries whose
- * first one sees fewer than 2,048) take every operand as a bf16 hi + lo pair;
- * longer ones round k^C, v^C, RoPE(q^R) and the softmax weights to bf16 once. */
+ * first one sees fewer than 2,048), and every query when yarn_factor > 1,
+ * take every operand as a bf16 hi + lo pair; longer ones round k^C, v^C,
+ * RoPE(q^R) and the softmax weights to bf16 once.
+ * A device-side prefix outside [0, max_prefix_len] is clamped into it. */
 size_t mla_prefill_unabsorbed_workspace_bytes(const mla_dims* dims, mla_dtype dtype,
                                               int32_t batch, int32_t chunk,
                                               int32_t max_prefix_len);
@@ -307,7 +328,8 @@ typedef struct {
 /* mla_decode_partials over a paged cache (max_seq_len <= max_pages *
  * page_rows); the split plan and the partials' layout are unchanged. */
 mla_status mla_decode_partials_paged(const mla_dims* dims, mla_dtype dtype, int32_t batch,
-                                     const void* q_lat, const mla_paged_cache* cache,
+                                     const void* q_lat, const void* q_lat_lo,
+                                     const mla_paged_cache* cache,
                                      const int32_t* seq_lens, int32_t max_seq_len,
                                      int32_t num_splits, float* z_part, float* lse_part,
                                      void* stream);
@@ -316,7 +338,8 @@ mla_status mla_decode_partials_paged(const mla_dims* dims, mla_dtype dtype, int3
  * the place of cache_seq_stride; the workspace is mla_decode_workspace_bytes()
  * for the same dims, dtype, batch and max_seq_len. */
 mla_status mla_decode_paged(const mla_dims* dims, mla_dtype dtype, int32_t batch,
-                            const void* q_lat, const mla_paged_cache* cache,
+                            const void* q_lat, const void* q_lat_lo,
+                            const mla_paged_cache* cache,
                             const int32_t* seq_lens, int32_t max_seq_len,
                             const void* w_uv, float* out, float* out_latent,
                             void* workspace, size_t workspace_bytes, void* stream);
@@ -324,7 +347,7 @@ mla_status mla_decode_paged(const mla_dims* dims, mla_dtype dtype, int32_t batch
 /* mla_prefill over a paged cache (max_prefix_len + chunk <= max_pages *
  * page_rows); the workspace is mla_prefill_workspace_bytes(). */
 mla_status mla_prefill_paged(const mla_dims* dims, mla_dtype dtype, int32_t batch,
-                             int32_t chunk, const void* q_lat,
+                             int32_t chunk, const void* q_lat, const void* q_lat_lo,
                              const mla_paged_cache* cache, const int32_t* prefix_lens,
                              int32_t max_prefix_len, const void* w_uv, float* out,
                              void* workspace, size_t workspace_bytes, void* stream);
@@ -365,12 +388,12 @@ mla_status mla_append_kv_fp8(const mla_dims* dims, int32_t n_tok, const void* c_
                              const void* k_r, const int32_t* pos, const int64_t* row,
                              const mla_fp8_cache* cache, void* stream);
 
-/* A3 over the FP8 cache: as mla_decode_partials with bf16 queries (absorbed
- * query layout; 128 heads read hi only, other head counts hi + lo) and the
- * same split plan and partials layout.  128 heads run the matrix-core kernel,
- * other head counts a generic fp32 kernel. */
+/* A3 over the FP8 cache: as mla_decode_partials with bf16 absorbed queries
+ * (q_lat, optional q_lat_lo, read as there) and the same split plan and
+ * partials layout.  128 and 16 heads run matrix-core kernels, other head
+ * counts a generic fp32 kernel. */
 mla_status mla_decode_partials_fp8(const mla_dims* dims, int32_t batch, const void* q_lat,
-                                   const mla_fp8_cache* cache, int64_t cache_seq_stride,
+                                   const void* q_lat_lo, const mla_fp8_cache* cache, int64_t cache_seq_stride,
                                    const int32_t* seq_lens, int32_t max_seq_len,
                                    int32_t num_splits, float* z_part, float* lse_part,
                                    void* stream);
@@ -378,7 +401,7 @@ mla_status mla_decode_partials_fp8(const mla_dims* dims, int32_t batch, const vo
 /* A3 + A4 + A5 over the FP8 cache (w_uv bf16); the workspace is
  * mla_decode_workspace_bytes(dims, MLA_BF16, batch, max_seq_len). */
 mla_status mla_decode_fp8(const mla_dims* dims, int32_t batch, const void* q_lat,
-                          const mla_fp8_cache* cache, int64_t cache_seq_stride,
+                          const void* q_lat_lo, const mla_fp8_cache* cache, int64_t cache_seq_stride,
                           const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv,
                           float* out, float* out_latent, void* workspace,
                           size_t workspace_bytes, void* stream);
@@ -387,7 +410,8 @@ mla_status mla_decode_fp8(const mla_dims* dims, int32_t batch, const void* q_lat
  * [E4M3(codes) * scale ; rope].  Query i of sequence b sits at position
  * prefix_lens[b] + i and attends rows 0..prefix_lens[b] + i, which must be
  * written (mla_append_kv_fp8) at rows b * cache_seq_stride + j.
- *   q_lat    bf16 absorbed queries [batch][chunk][n_h][2][d_c + d_hR] (A2)
+ *   q_lat    bf16 absorbed queries [batch][chunk][n_h][d_c + d_hR] (A2), and
+ *            q_lat_lo their optional lo plane (as mla_decode_partials)
  *   prefix_lens [batch] (device), each in [0, max_prefix_len]
  *   w_uv     bf16 [n_h][d_h][d_c];  out fp32 [batch][chunk][n_h][d_h]
  *   workspace at least mla_prefill_workspace_bytes(dims, MLA_BF16, batch,
@@ -397,7 +421,7 @@ mla_status mla_decode_fp8(const mla_dims* dims, int32_t batch, const void* q_lat
  * cache_seq_stride (MLA_ERR_INVALID_ARGUMENT), a short workspace
  * (MLA_ERR_WORKSPACE_TOO_SMALL). */
 mla_status mla_prefill_fp8(const mla_dims* dims, int32_t batch, int32_t chunk, const void* q_lat,
-                           const mla_fp8_cache* cache, int64_t cache_seq_stride,
+                           const void* q_lat_lo, const mla_fp8_cache* cache, int64_t cache_seq_stride,
                            const int32_t* prefix_lens, int32_t max_prefix_len, const void* w_uv,
                            float* out, void* workspace, size_t workspace_bytes, void* stream);
 

@@ -76,33 +76,34 @@ _SIGS = {
                                                  ctypes.c_double, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mla_absorb_q_from_hidden_workspace_bytes": (_sz, [_P, _i32, _i32, _i32]),
     "mla_absorb_q_from_hidden": (ctypes.c_int, [_P, _i32, _i32, _i32, _vp, _vp, _vp, ctypes.c_double, _vp, _vp,
-                                                _vp, _vp, _vp, _vp, _sz, _vp]),
+                                                _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mla_output_projection_workspace_bytes": (_sz, [_P, _i32, _i32]),
     "mla_output_projection": (ctypes.c_int, [_P, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "mla_absorb_q": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mla_absorb_q": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mla_precise_rows": (_i32, [_P, ctypes.c_int]),
     "mla_decode_num_splits": (_i32, [_P, ctypes.c_int, _i32, _i32]),
     "mla_split_rows": (_i64, [_i32, _i32]),
-    "mla_decode_partials": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _i64, _vp, _i32, _i32,
+    "mla_decode_partials": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _vp, _i64, _vp, _i32, _i32,
                                            _vp, _vp, _vp]),
     "mla_combine_project": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mla_decode_workspace_bytes": (_sz, [_P, ctypes.c_int, _i32, _i32]),
-    "mla_decode": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp,
+    "mla_decode": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp,
                                   _vp, _sz, _vp]),
     "mla_prefill_workspace_bytes": (_sz, [_P, ctypes.c_int, _i32, _i32, _i32]),
     "mla_prefill_unabsorbed_workspace_bytes": (_sz, [_P, ctypes.c_int, _i32, _i32, _i32]),
     "mla_prefill_unabsorbed": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i32,
                                               _vp, _vp, _vp, _vp, _sz, _vp]),
-    "mla_prefill": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _i64, _vp, _i32, _vp, _vp,
+    "mla_prefill": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp,
                                    _vp, _sz, _vp]),
     "mla_append_kv_fp8": (ctypes.c_int, [_P, _i32, _vp, _vp, _vp, _vp, _FC, _vp]),
-    "mla_decode_partials_fp8": (ctypes.c_int, [_P, _i32, _vp, _FC, _i64, _vp, _i32, _i32, _vp, _vp, _vp]),
-    "mla_decode_fp8": (ctypes.c_int, [_P, _i32, _vp, _FC, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "mla_prefill_fp8": (ctypes.c_int, [_P, _i32, _i32, _vp, _FC, _i64, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
-    "mla_decode_partials_paged": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _PC, _vp, _i32, _i32, _vp, _vp,
-                                                 _vp]),
-    "mla_decode_paged": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _PC, _vp, _i32, _vp, _vp, _vp, _vp,
+    "mla_decode_partials_fp8": (ctypes.c_int, [_P, _i32, _vp, _vp, _FC, _i64, _vp, _i32, _i32, _vp, _vp, _vp]),
+    "mla_decode_fp8": (ctypes.c_int, [_P, _i32, _vp, _vp, _FC, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mla_prefill_fp8": (ctypes.c_int, [_P, _i32, _i32, _vp, _vp, _FC, _i64, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "mla_decode_partials_paged": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _PC, _vp, _i32, _i32, _vp,
+                                                 _vp, _vp]),
+    "mla_decode_paged": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _PC, _vp, _i32, _vp, _vp, _vp, _vp,
                                         _sz, _vp]),
-    "mla_prefill_paged": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _PC, _vp, _i32, _vp, _vp, _vp,
+    "mla_prefill_paged": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _PC, _vp, _i32, _vp, _vp, _vp,
                                          _sz, _vp]),
     "mla_prefill_unabsorbed_paged": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _PC, _vp, _i32,
                                                     _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -174,30 +175,73 @@ def append_kv_from_hidden(d: Dims, h, w_dkv, w_kr, norm_weight, eps: float, pos,
            "mla_append_kv_from_hidden")
 
 
-def q_lat_empty(d: Dims, storage: torch.dtype, *lead: int, device="cuda") -> torch.Tensor:
-    """Absorbed query buffer in the layout of `storage`: fp32 [*lead, n_h, 576], or
-    for bf16 the hi/lo pair [*lead, n_h, 2, 576]."""
-    row = d.d_c + d.d_hR
-    if storage == torch.bfloat16:
-        return torch.empty((*lead, d.n_h, 2, row), dtype=torch.bfloat16, device=device)
-    if storage == torch.float32:
-        return torch.empty((*lead, d.n_h, row), dtype=torch.float32, device=device)
-    raise TypeError(f"storage dtype must be bfloat16 or float32, got {storage}")
+class QLat:
+    """Absorbed queries (A2's output, mla.h): `hi` [*lead, n_h, d_c + d_hR] in the
+    storage dtype and, for bf16, an optional `lo` plane of the same shape
+    (lo = bf16(v - hi)); the attention calls read lo for the queries that
+    mla_precise_rows() names."""
+
+    def __init__(self, hi: torch.Tensor, lo: torch.Tensor | None = None):
+        if lo is not None:
+            assert lo.shape == hi.shape and lo.dtype == hi.dtype == torch.bfloat16
+        self.hi, self.lo = hi, lo
+
+    @property
+    def shape(self):
+        return self.hi.shape
+
+    @property
+    def dtype(self):
+        return self.hi.dtype
+
+    @property
+    def device(self):
+        return self.hi.device
+
+    def view(self, *shape) -> "QLat":
+        return QLat(self.hi.view(*shape), None if self.lo is None else self.lo.view(*shape))
+
+    def __getitem__(self, idx) -> "QLat":
+        return QLat(self.hi[idx], None if self.lo is None else self.lo[idx])
 
 
-def q_lat_value(q_lat: torch.Tensor) -> torch.Tensor:
-    """fp32 value of an absorbed query buffer (hi + lo for the bf16 layout)."""
-    if q_lat.dtype == torch.bfloat16:
-        return q_lat[..., 0, :].float() + q_lat[..., 1, :].float()
+def q_lat_empty(d: Dims, storage: torch.dtype, *lead: int, device="cuda", lo: bool = True) -> QLat:
+    """Absorbed query buffers [*lead, n_h, d_c + d_hR] of `storage` dtype, with the
+    bf16 lo plane when `lo` (ignored for float32)."""
+    if storage not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"storage dtype must be bfloat16 or float32, got {storage}")
+    shape = (*lead, d.n_h, d.d_c + d.d_hR)
+    hi = torch.empty(shape, dtype=storage, device=device)
+    return QLat(hi, torch.empty_like(hi) if (lo and storage == torch.bfloat16) else None)
+
+
+def q_lat_value(q_lat) -> torch.Tensor:
+    """fp32 value of absorbed queries (hi + lo where the lo plane exists)."""
+    if isinstance(q_lat, QLat):
+        v = q_lat.hi.float()
+        return v + q_lat.lo.float() if q_lat.lo is not None else v
     return q_lat.float()
 
 
+def _q(q_lat):
+    """(hi, lo) device pointers of absorbed queries (a QLat or a bare hi tensor)."""
+    if isinstance(q_lat, QLat):
+        return _ptr(q_lat.hi), _ptr(q_lat.lo)
+    return _ptr(q_lat), None
+
+
+def precise_rows(d: Dims, dtype: int) -> int:
+    """mla_precise_rows: queries attending fewer rows read the lo plane."""
+    return _lib.mla_precise_rows(ctypes.byref(d), dtype)
+
+
 def absorb_q(d: Dims, q_c, q_r, q_pos, w_uk, q_lat) -> None:
-    """A2: q_lat[n, i] = [q_c[n, i] @ w_uk[i]; RoPE(q_r[n, i], q_pos[n])] in the
-    absorbed query layout of the storage dtype (see q_lat_empty)."""
+    """A2: q_lat[n, i] = [q_c[n, i] @ w_uk[i]; RoPE(q_r[n, i], q_pos[n])] (hi, and lo
+    when the QLat has that plane)."""
     assert q_pos.dtype == torch.int32 and q_lat.dtype == w_uk.dtype
+    hi, lo = _q(q_lat)
     _check(_lib.mla_absorb_q(ctypes.byref(d), _dtype(w_uk), q_c.shape[0], _ptr(q_c), _ptr(q_r),
-                             _ptr(q_pos), _ptr(w_uk), _ptr(q_lat), _stream(q_lat.device)),
+                             _ptr(q_pos), _ptr(w_uk), hi, lo, _stream(q_lat.device)),
            "mla_absorb_q")
 
 
@@ -213,7 +257,7 @@ def decode_partials(d: Dims, q_lat, cache, stride: int, seq_lens, max_seq_len: i
                     z_part, lse_part) -> None:
     """A3: split-KV partials (z_part [B, S, n_h, d_c] fp32, lse_part [B, S, n_h] fp32)."""
     assert seq_lens.dtype == torch.int32 and q_lat.dtype == cache.dtype
-    _check(_lib.mla_decode_partials(ctypes.byref(d), _dtype(cache), q_lat.shape[0], _ptr(q_lat),
+    _check(_lib.mla_decode_partials(ctypes.byref(d), _dtype(cache), q_lat.shape[0], *_q(q_lat),
                                     _ptr(cache), stride, _ptr(seq_lens), max_seq_len, splits,
                                     _ptr(z_part), _ptr(lse_part), _stream(cache.device)),
            "mla_decode_partials")
@@ -239,7 +283,7 @@ def decode(d: Dims, q_lat, cache, stride: int, seq_lens, max_seq_len: int, w_uv,
     need = decode_workspace_bytes(d, dt, q_lat.shape[0], max_seq_len)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=cache.device)
-    _check(_lib.mla_decode(ctypes.byref(d), dt, q_lat.shape[0], _ptr(q_lat), _ptr(cache), stride,
+    _check(_lib.mla_decode(ctypes.byref(d), dt, q_lat.shape[0], *_q(q_lat), _ptr(cache), stride,
                            _ptr(seq_lens), max_seq_len, _ptr(w_uv), _ptr(out), _ptr(out_latent),
                            _ptr(workspace), workspace.numel(), _stream(cache.device)), "mla_decode")
 
@@ -250,14 +294,14 @@ def prefill_workspace_bytes(d: Dims, dtype: int, batch: int, chunk: int, max_pre
 
 def prefill(d: Dims, q_lat, cache, stride: int, prefix_lens, max_prefix_len: int, w_uv, out,
             workspace=None) -> None:
-    """A6: causal prefill; q_lat [B, chunk, n_h, ...] (absorbed query layout), out [B, chunk, n_h, d_h]."""
+    """A6: causal prefill; q_lat [B, chunk, n_h, 576] (QLat), out [B, chunk, n_h, d_h]."""
     assert prefix_lens.dtype == torch.int32 and q_lat.dtype == cache.dtype
     dt = _dtype(cache)
     B, chunk = q_lat.shape[0], q_lat.shape[1]
     need = prefill_workspace_bytes(d, dt, B, chunk, max_prefix_len)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=cache.device)
-    _check(_lib.mla_prefill(ctypes.byref(d), dt, B, chunk, _ptr(q_lat), _ptr(cache), stride,
+    _check(_lib.mla_prefill(ctypes.byref(d), dt, B, chunk, *_q(q_lat), _ptr(cache), stride,
                             _ptr(prefix_lens), max_prefix_len, _ptr(w_uv), _ptr(out),
                             _ptr(workspace), workspace.numel(), _stream(cache.device)),
            "mla_prefill")
@@ -296,7 +340,7 @@ def decode_partials_paged(d: Dims, q_lat, pool, block_table, seq_lens, max_seq_l
     """decode_partials() over a paged cache (see paged_cache)."""
     assert seq_lens.dtype == torch.int32 and q_lat.dtype == pool.dtype
     pc = paged_cache(pool, block_table)
-    _check(_lib.mla_decode_partials_paged(ctypes.byref(d), _dtype(pool), q_lat.shape[0], _ptr(q_lat),
+    _check(_lib.mla_decode_partials_paged(ctypes.byref(d), _dtype(pool), q_lat.shape[0], *_q(q_lat),
                                           ctypes.byref(pc), _ptr(seq_lens), max_seq_len, splits, _ptr(z_part),
                                           _ptr(lse_part), _stream(pool.device)), "mla_decode_partials_paged")
 
@@ -310,7 +354,7 @@ def decode_paged(d: Dims, q_lat, pool, block_table, seq_lens, max_seq_len: int, 
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=pool.device)
     pc = paged_cache(pool, block_table)
-    _check(_lib.mla_decode_paged(ctypes.byref(d), dt, q_lat.shape[0], _ptr(q_lat), ctypes.byref(pc),
+    _check(_lib.mla_decode_paged(ctypes.byref(d), dt, q_lat.shape[0], *_q(q_lat), ctypes.byref(pc),
                                  _ptr(seq_lens), max_seq_len, _ptr(w_uv), _ptr(out), _ptr(out_latent),
                                  _ptr(workspace), workspace.numel(), _stream(pool.device)), "mla_decode_paged")
 
@@ -325,7 +369,7 @@ def prefill_paged(d: Dims, q_lat, pool, block_table, prefix_lens, max_prefix_len
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=pool.device)
     pc = paged_cache(pool, block_table)
-    _check(_lib.mla_prefill_paged(ctypes.byref(d), dt, B, chunk, _ptr(q_lat), ctypes.byref(pc),
+    _check(_lib.mla_prefill_paged(ctypes.byref(d), dt, B, chunk, *_q(q_lat), ctypes.byref(pc),
                                   _ptr(prefix_lens), max_prefix_len, _ptr(w_uv), _ptr(out),
                                   _ptr(workspace), workspace.numel(), _stream(pool.device)), "mla_prefill_paged")
 
@@ -372,7 +416,7 @@ def decode_partials_fp8(d: Dims, q_lat, cache, stride: int, seq_lens, max_seq_le
     """A3 over the FP8 cache (bf16 absorbed queries)."""
     assert seq_lens.dtype == torch.int32 and q_lat.dtype == torch.bfloat16
     fc = _fp8(cache)
-    _check(_lib.mla_decode_partials_fp8(ctypes.byref(d), q_lat.shape[0], _ptr(q_lat), ctypes.byref(fc), stride,
+    _check(_lib.mla_decode_partials_fp8(ctypes.byref(d), q_lat.shape[0], *_q(q_lat), ctypes.byref(fc), stride,
                                         _ptr(seq_lens), max_seq_len, splits, _ptr(z_part), _ptr(lse_part),
                                         _stream(q_lat.device)), "mla_decode_partials_fp8")
 
@@ -385,7 +429,7 @@ def decode_fp8(d: Dims, q_lat, cache, stride: int, seq_lens, max_seq_len: int, w
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
     fc = _fp8(cache)
-    _check(_lib.mla_decode_fp8(ctypes.byref(d), q_lat.shape[0], _ptr(q_lat), ctypes.byref(fc), stride,
+    _check(_lib.mla_decode_fp8(ctypes.byref(d), q_lat.shape[0], *_q(q_lat), ctypes.byref(fc), stride,
                                _ptr(seq_lens), max_seq_len, _ptr(w_uv), _ptr(out), _ptr(out_latent),
                                _ptr(workspace), workspace.numel(), _stream(q_lat.device)), "mla_decode_fp8")
 
@@ -401,7 +445,7 @@ def absorb_q_from_hidden(d: Dims, h, w_dq, norm_weight, eps: float, w_uq, w_qr, 
         need = _lib.mla_absorb_q_from_hidden_workspace_bytes(ctypes.byref(d), n_q, d_model, d_cq)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
     _check(_lib.mla_absorb_q_from_hidden(ctypes.byref(d), n_q, d_model, d_cq, _ptr(h), _ptr(w_dq), _ptr(norm_weight),
-                                         float(eps), _ptr(w_uq), _ptr(w_qr), _ptr(q_pos), _ptr(w_uk), _ptr(q_lat),
+                                         float(eps), _ptr(w_uq), _ptr(w_qr), _ptr(q_pos), _ptr(w_uk), *_q(q_lat),
                                          _ptr(workspace), workspace.numel(), _stream(h.device)),
            "mla_absorb_q_from_hidden")
 
@@ -418,13 +462,13 @@ def output_projection(d: Dims, o, w_o, out, workspace=None) -> None:
 
 def prefill_fp8(d: Dims, q_lat, cache, stride: int, prefix_lens, max_prefix_len: int, w_uv, out,
                 workspace=None) -> None:
-    """A6 over the FP8 cache (codes, rope, scale); q_lat [B, chunk, n_h, 2, 576] bf16."""
+    """A6 over the FP8 cache (codes, rope, scale); q_lat [B, chunk, n_h, 576] bf16 (QLat)."""
     assert prefix_lens.dtype == torch.int32 and q_lat.dtype == torch.bfloat16
     B, chunk = q_lat.shape[0], q_lat.shape[1]
     need = prefill_workspace_bytes(d, BF16, B, chunk, max_prefix_len)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
     fc = _fp8(cache)
-    _check(_lib.mla_prefill_fp8(ctypes.byref(d), B, chunk, _ptr(q_lat), ctypes.byref(fc), stride, _ptr(prefix_lens),
+    _check(_lib.mla_prefill_fp8(ctypes.byref(d), B, chunk, *_q(q_lat), ctypes.byref(fc), stride, _ptr(prefix_lens),
                                 max_prefix_len, _ptr(w_uv), _ptr(out), _ptr(workspace), workspace.numel(),
                                 _stream(q_lat.device)), "mla_prefill_fp8")

@@ -37,6 +37,11 @@ constexpr int kMaxSplits = 65535;
 // unabsorbed prefill: a workgroup whose first query sees fewer keys than this
 // takes the hi + lo products
 constexpr int kPreciseBelow = 2048;
+// absorbed path, 32 to 128 heads: a query that attends fewer rows than this
+// scores with hi + lo and carries its softmax weights as hi + lo (the
+// 16-head-group body); longer ones take the wide kernels' single bf16 operands
+constexpr int kPreciseRows = 4096;
+constexpr int32_t kAllPrecise = 0x7fffffff;
 
 mla_status check_dims(const mla_dims* d, mla_dtype dt) {
   if (!d) return fail(MLA_ERR_INVALID_ARGUMENT, "dims is NULL");
@@ -100,6 +105,16 @@ int64_t split_rows(int32_t max_seq_len, int32_t num_splits) {
   return (r + mla::TILE - 1) / mla::TILE * mla::TILE;
 }
 
+// Attended length below which a query reads the lo plane (mla_precise_rows).
+// bf16 only: 16 heads, the generic kernels and the long-context temperature
+// (which sharpens the softmax so that single bf16 operands show at every
+// length) always use hi + lo.
+int32_t precise_rows_of(const mla_dims* d, mla_dtype dt) {
+  if (dt != MLA_BF16) return 0;
+  if (yarn_on(d) || d->n_h == 16 || !mla::splitkv_has_fast_path(d->n_h, 1, d->d_c, d->d_hR)) return kAllPrecise;
+  return kPreciseRows;
+}
+
 // Split plan.  The MFMA kernels hold one workgroup per CU (their LDS ring),
 // so the plan aims at one round of kNumCUs workgroups and, for batches of
 // fewer than four rounds of queries, caps a split at kMaxSplitRows rows, which
@@ -110,10 +125,17 @@ int32_t plan_splits(const mla_dims* d, mla_dtype dt, int64_t n_q, int64_t max_le
   if (n_q <= 0 || max_len <= 0) return 1;
   const bool fast = mla::splitkv_has_fast_path(d->n_h, dt == MLA_BF16, d->d_c, d->d_hR);
   const int64_t target = static_cast<int64_t>(kNumCUs) * (fast ? 1 : 2);
-  int64_t s = (target + n_q - 1) / n_q;
+  // when every query takes the 16-head-group path, each (query, split) is
+  // n_h / 16 workgroups
+  const int64_t units =
+      (fast && mla::splitkv_all_precise(d->n_h, static_cast<int32_t>(std::min<int64_t>(max_len, kAllPrecise)),
+                                        precise_rows_of(d, dt)))
+          ? n_q * (d->n_h / 16)
+          : n_q;
+  int64_t s = (target + units - 1) / units;
   // (with four or more rounds of queries, e.g. a prefill chunk, the hardware
   // scheduler already balances whole queries and splitting only adds partials)
-  if (fast && n_q < 4 * static_cast<int64_t>(kNumCUs))
+  if (fast && units < 4 * static_cast<int64_t>(kNumCUs))
     s = std::max<int64_t>(s, (max_len + kMaxSplitRows - 1) / kMaxSplitRows);
   const int64_t max_s = std::max<int64_t>(1, (max_len + kMinSplitRows - 1) / kMinSplitRows);
   s = std::min(std::max<int64_t>(s, 1), max_s);
@@ -121,6 +143,13 @@ int32_t plan_splits(const mla_dims* d, mla_dtype dt, int64_t n_q, int64_t max_le
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// The lo plane of the absorbed queries exists for bf16 storage only.
+mla_status check_lo(mla_dtype dt, const void* q_lat_lo) {
+  if (q_lat_lo && dt != MLA_BF16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "q_lat_lo is for bf16 storage only (pass NULL with MLA_F32)");
+  return MLA_OK;
+}
 
 int32_t page_shift_of(int32_t page_rows) {
   int32_t k = 0;
@@ -235,13 +264,14 @@ mla_status mla_append_kv_from_hidden(const mla_dims* dims, mla_dtype dtype, int3
 }
 
 static mla_status absorb_launch(const mla_dims* dims, int bf, int32_t n_q, const void* q_c, const void* q_r,
-                                const int32_t* q_pos, const void* w_uk, void* q_lat, hipStream_t s, const char* who,
-                                int q_r_f32 = 0) {
+                                const int32_t* q_pos, const void* w_uk, void* q_lat, void* q_lat_lo, hipStream_t s,
+                                const char* who, int q_r_f32 = 0) {
   mla::AbsorbArgs a{};
   a.q_r_f32 = q_r_f32;
   a.q_c = q_c;
   a.w_uk = w_uk;
   a.q_lat = q_lat;
+  a.q_lat_lo = q_lat_lo;
   a.n_q = n_q;
   a.n_h = dims->n_h;
   a.d_c = dims->d_c;
@@ -256,6 +286,7 @@ static mla_status absorb_launch(const mla_dims* dims, int bf, int32_t n_q, const
   ra.q_r = q_r;
   ra.q_pos = q_pos;
   ra.q_lat = q_lat;
+  ra.q_lat_lo = q_lat_lo;
   ra.n_q = n_q;
   ra.n_h = dims->n_h;
   ra.d_c = dims->d_c;
@@ -265,15 +296,17 @@ static mla_status absorb_launch(const mla_dims* dims, int bf, int32_t n_q, const
 }
 
 mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q, const void* q_c, const void* q_r,
-                        const int32_t* q_pos, const void* w_uk, void* q_lat, void* stream) {
+                        const int32_t* q_pos, const void* w_uk, void* q_lat, void* q_lat_lo, void* stream) {
   mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  st = check_lo(dtype, q_lat_lo);
   if (st != MLA_OK) return st;
   if (n_q < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "n_q=%d < 0", n_q);
   if (n_q == 0) return MLA_OK;
   if (n_q > 65535 * 256) return fail(MLA_ERR_INVALID_ARGUMENT, "n_q=%d too large", n_q);
   if (!q_c || !q_r || !q_pos || !w_uk || !q_lat) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  return absorb_launch(dims, dtype == MLA_BF16, n_q, q_c, q_r, q_pos, w_uk, q_lat, static_cast<hipStream_t>(stream),
-                       "mla_absorb_q");
+  return absorb_launch(dims, dtype == MLA_BF16, n_q, q_c, q_r, q_pos, w_uk, q_lat, q_lat_lo,
+                       static_cast<hipStream_t>(stream), "mla_absorb_q");
 }
 
 // ---- the query path from hidden states: c^Q = RMSNorm(W^DQ h), [q^C ; q^R] =
@@ -306,7 +339,7 @@ size_t mla_absorb_q_from_hidden_workspace_bytes(const mla_dims* dims, int32_t n_
 mla_status mla_absorb_q_from_hidden(const mla_dims* dims, int32_t n_q, int32_t d_model, int32_t d_cq, const void* h,
                                     const void* w_dq, const void* norm_weight, double eps, const void* w_uq,
                                     const void* w_qr, const int32_t* q_pos, const void* w_uk, void* q_lat,
-                                    void* workspace, size_t workspace_bytes, void* stream) {
+                                    void* q_lat_lo, void* workspace, size_t workspace_bytes, void* stream) {
   mla_status st = check_dims(dims, MLA_BF16);
   if (st != MLA_OK) return st;
   if (n_q < 0 || n_q > 65535) return fail(MLA_ERR_INVALID_ARGUMENT, "n_q=%d out of range [0,65535]", n_q);
@@ -363,7 +396,7 @@ mla_status mla_absorb_q_from_hidden(const mla_dims* dims, int32_t n_q, int32_t d
                     "mla_absorb_q_from_hidden (q^C, q^R)");
     if (st != MLA_OK) return st;
   }
-  return absorb_launch(dims, 1, n_q, qc, qr, q_pos, w_uk, q_lat, s, "mla_absorb_q_from_hidden (absorb)", 1);
+  return absorb_launch(dims, 1, n_q, qc, qr, q_pos, w_uk, q_lat, q_lat_lo, s, "mla_absorb_q_from_hidden (absorb)", 1);
 }
 
 // ---- the output projection: u = W^O o (o rounded once to bf16 for the matrix cores)
@@ -427,8 +460,13 @@ int32_t mla_decode_num_splits(const mla_dims* dims, mla_dtype dtype, int32_t bat
 
 int64_t mla_split_rows(int32_t max_seq_len, int32_t num_splits) { return split_rows(max_seq_len, num_splits); }
 
+int32_t mla_precise_rows(const mla_dims* dims, mla_dtype dtype) {
+  if (check_dims(dims, dtype) != MLA_OK) return 0;
+  return precise_rows_of(dims, dtype);
+}
+
 static mla_status run_partials(const mla_dims* dims, mla_dtype dtype, int64_t n_q, const void* q_lat,
-                               const void* cache, int64_t stride, const int32_t* lens, int32_t max_len,
+                               const void* q_lat_lo, const void* cache, int64_t stride, const int32_t* lens, int32_t max_len,
                                int32_t q_per_seq, int prefill, int32_t num_splits, float* z_part,
                                float* lse_part, hipStream_t s, const char* who,
                                const mla_paged_cache* paged = nullptr) {
@@ -440,6 +478,7 @@ static mla_status run_partials(const mla_dims* dims, mla_dtype dtype, int64_t n_
     a.page_shift = page_shift_of(paged->page_rows);
   }
   a.q_lat = q_lat;
+  a.q_lat_lo = q_lat_lo;
   a.cache = cache;
   a.lens = lens;
   a.z_part = z_part;
@@ -455,14 +494,17 @@ static mla_status run_partials(const mla_dims* dims, mla_dtype dtype, int64_t n_
   a.q_per_seq = q_per_seq;
   a.prefill = prefill;
   a.qscale = static_cast<float>(scale_of(dims) * 1.4426950408889634);
+  a.precise_below = precise_rows_of(dims, dtype);
   return hip_status(mla::launch_splitkv(a, dtype == MLA_BF16, s), who);
 }
 
 mla_status mla_decode_partials(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat,
-                               const void* cache, int64_t cache_seq_stride, const int32_t* seq_lens,
-                               int32_t max_seq_len, int32_t num_splits, float* z_part, float* lse_part,
-                               void* stream) {
+                               const void* q_lat_lo, const void* cache, int64_t cache_seq_stride,
+                               const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, float* z_part,
+                               float* lse_part, void* stream) {
   mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  st = check_lo(dtype, q_lat_lo);
   if (st != MLA_OK) return st;
   if (batch < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d < 1", batch);
   if (max_seq_len < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "max_seq_len=%d < 1", max_seq_len);
@@ -471,14 +513,17 @@ mla_status mla_decode_partials(const mla_dims* dims, mla_dtype dtype, int32_t ba
   if (num_splits < 1 || num_splits > kMaxSplits)
     return fail(MLA_ERR_INVALID_ARGUMENT, "num_splits=%d out of range [1,%d]", num_splits, kMaxSplits);
   if (!q_lat || !cache || !seq_lens || !z_part || !lse_part) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  return run_partials(dims, dtype, batch, q_lat, cache, cache_seq_stride, seq_lens, max_seq_len, 1, 0,
+  return run_partials(dims, dtype, batch, q_lat, q_lat_lo, cache, cache_seq_stride, seq_lens, max_seq_len, 1, 0,
                       num_splits, z_part, lse_part, static_cast<hipStream_t>(stream), "mla_decode_partials");
 }
 
 mla_status mla_decode_partials_paged(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat,
-                                     const mla_paged_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
-                                     int32_t num_splits, float* z_part, float* lse_part, void* stream) {
+                                     const void* q_lat_lo, const mla_paged_cache* cache, const int32_t* seq_lens,
+                                     int32_t max_seq_len, int32_t num_splits, float* z_part, float* lse_part,
+                                     void* stream) {
   mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  st = check_lo(dtype, q_lat_lo);
   if (st != MLA_OK) return st;
   if (batch < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d < 1", batch);
   if (max_seq_len < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "max_seq_len=%d < 1", max_seq_len);
@@ -488,8 +533,8 @@ mla_status mla_decode_partials_paged(const mla_dims* dims, mla_dtype dtype, int3
   if (num_splits < 1 || num_splits > kMaxSplits)
     return fail(MLA_ERR_INVALID_ARGUMENT, "num_splits=%d out of range [1,%d]", num_splits, kMaxSplits);
   if (!q_lat || !seq_lens || !z_part || !lse_part) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  return run_partials(dims, dtype, batch, q_lat, cache->pool, cap, seq_lens, max_seq_len, 1, 0, num_splits, z_part,
-                      lse_part, static_cast<hipStream_t>(stream), "mla_decode_partials_paged", cache);
+  return run_partials(dims, dtype, batch, q_lat, q_lat_lo, cache->pool, cap, seq_lens, max_seq_len, 1, 0, num_splits,
+                      z_part, lse_part, static_cast<hipStream_t>(stream), "mla_decode_partials_paged", cache);
 }
 
 mla_status mla_combine_project(const mla_dims* dims, mla_dtype dtype, int32_t n_q, int32_t num_splits,
@@ -511,10 +556,12 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t
 }
 
 static mla_status decode_impl(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat,
-                              const void* cache, int64_t cache_seq_stride, const mla_paged_cache* paged,
+                              const void* q_lat_lo, const void* cache, int64_t cache_seq_stride, const mla_paged_cache* paged,
                               const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv, float* out,
                               float* out_latent, void* workspace, size_t workspace_bytes, void* stream) {
   mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  st = check_lo(dtype, q_lat_lo);
   if (st != MLA_OK) return st;
   if (batch < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d < 1", batch);
   if (max_seq_len < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "max_seq_len=%d < 1", max_seq_len);
@@ -535,27 +582,28 @@ static mla_status decode_impl(const mla_dims* dims, mla_dtype dtype, int32_t bat
   float* lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         align256(static_cast<size_t>(batch) * S * dims->n_h * dims->d_c * sizeof(float)));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = run_partials(dims, dtype, batch, q_lat, cache, cache_seq_stride, seq_lens, max_seq_len, 1, 0, S, z, lse, s,
-                    "mla_decode (partials)", paged);
+  st = run_partials(dims, dtype, batch, q_lat, q_lat_lo, cache, cache_seq_stride, seq_lens, max_seq_len, 1, 0, S, z,
+                    lse, s, "mla_decode (partials)", paged);
   if (st != MLA_OK) return st;
   mla::CombineArgs a{z, lse, w_uv, out, out_latent, batch, dims->n_h, dims->d_c, dims->d_h, S};
   return hip_status(mla::launch_combine(a, dtype == MLA_BF16, s), "mla_decode (combine)");
 }
 
-mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat, const void* cache,
-                      int64_t cache_seq_stride, const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv,
-                      float* out, float* out_latent, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(dims, dtype, batch, q_lat, cache, cache_seq_stride, nullptr, seq_lens, max_seq_len, w_uv, out,
-                     out_latent, workspace, workspace_bytes, stream);
+mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat, const void* q_lat_lo,
+                      const void* cache, int64_t cache_seq_stride, const int32_t* seq_lens, int32_t max_seq_len,
+                      const void* w_uv, float* out, float* out_latent, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return decode_impl(dims, dtype, batch, q_lat, q_lat_lo, cache, cache_seq_stride, nullptr, seq_lens, max_seq_len,
+                     w_uv, out, out_latent, workspace, workspace_bytes, stream);
 }
 
 mla_status mla_decode_paged(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat,
-                            const mla_paged_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
-                            const void* w_uv, float* out, float* out_latent, void* workspace,
+                            const void* q_lat_lo, const mla_paged_cache* cache, const int32_t* seq_lens,
+                            int32_t max_seq_len, const void* w_uv, float* out, float* out_latent, void* workspace,
                             size_t workspace_bytes, void* stream) {
   if (!cache) return fail(MLA_ERR_INVALID_ARGUMENT, "paged cache descriptor is NULL");
-  return decode_impl(dims, dtype, batch, q_lat, nullptr, 0, cache, seq_lens, max_seq_len, w_uv, out, out_latent,
-                     workspace, workspace_bytes, stream);
+  return decode_impl(dims, dtype, batch, q_lat, q_lat_lo, nullptr, 0, cache, seq_lens, max_seq_len, w_uv, out,
+                     out_latent, workspace, workspace_bytes, stream);
 }
 
 size_t mla_prefill_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk,
@@ -567,11 +615,13 @@ size_t mla_prefill_workspace_bytes(const mla_dims* dims, mla_dtype dtype, int32_
 }
 
 static mla_status prefill_impl(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk,
-                               const void* q_lat, const void* cache, int64_t cache_seq_stride,
+                               const void* q_lat, const void* q_lat_lo, const void* cache, int64_t cache_seq_stride,
                                const mla_paged_cache* paged, const int32_t* prefix_lens, int32_t max_prefix_len,
                                const void* w_uv, float* out, void* workspace, size_t workspace_bytes,
                                void* stream) {
   mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  st = check_lo(dtype, q_lat_lo);
   if (st != MLA_OK) return st;
   if (batch < 1 || chunk < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d, chunk=%d must be >= 1", batch, chunk);
   if (max_prefix_len < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "max_prefix_len=%d < 0", max_prefix_len);
@@ -597,27 +647,28 @@ static mla_status prefill_impl(const mla_dims* dims, mla_dtype dtype, int32_t ba
   float* lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         align256(static_cast<size_t>(n_q) * S * dims->n_h * dims->d_c * sizeof(float)));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = run_partials(dims, dtype, n_q, q_lat, cache, cache_seq_stride, prefix_lens, static_cast<int32_t>(max_len),
-                    chunk, 1, S, z, lse, s, "mla_prefill (partials)", paged);
+  st = run_partials(dims, dtype, n_q, q_lat, q_lat_lo, cache, cache_seq_stride, prefix_lens,
+                    static_cast<int32_t>(max_len), chunk, 1, S, z, lse, s, "mla_prefill (partials)", paged);
   if (st != MLA_OK) return st;
   mla::CombineArgs a{z, lse, w_uv, out, nullptr, static_cast<int32_t>(n_q), dims->n_h, dims->d_c, dims->d_h, S};
   return hip_status(mla::launch_combine(a, dtype == MLA_BF16, s), "mla_prefill (combine)");
 }
 
 mla_status mla_prefill(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk, const void* q_lat,
-                       const void* cache, int64_t cache_seq_stride, const int32_t* prefix_lens,
+                       const void* q_lat_lo, const void* cache, int64_t cache_seq_stride, const int32_t* prefix_lens,
                        int32_t max_prefix_len, const void* w_uv, float* out, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  return prefill_impl(dims, dtype, batch, chunk, q_lat, cache, cache_seq_stride, nullptr, prefix_lens, max_prefix_len,
-                      w_uv, out, workspace, workspace_bytes, stream);
+  return prefill_impl(dims, dtype, batch, chunk, q_lat, q_lat_lo, cache, cache_seq_stride, nullptr, prefix_lens,
+                      max_prefix_len, w_uv, out, workspace, workspace_bytes, stream);
 }
 
 mla_status mla_prefill_paged(const mla_dims* dims, mla_dtype dtype, int32_t batch, int32_t chunk, const void* q_lat,
-                             const mla_paged_cache* cache, const int32_t* prefix_lens, int32_t max_prefix_len,
-                             const void* w_uv, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+                             const void* q_lat_lo, const mla_paged_cache* cache, const int32_t* prefix_lens,
+                             int32_t max_prefix_len, const void* w_uv, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   if (!cache) return fail(MLA_ERR_INVALID_ARGUMENT, "paged cache descriptor is NULL");
-  return prefill_impl(dims, dtype, batch, chunk, q_lat, nullptr, 0, cache, prefix_lens, max_prefix_len, w_uv, out,
-                      workspace, workspace_bytes, stream);
+  return prefill_impl(dims, dtype, batch, chunk, q_lat, q_lat_lo, nullptr, 0, cache, prefix_lens, max_prefix_len, w_uv,
+                      out, workspace, workspace_bytes, stream);
 }
 
 
@@ -688,7 +739,7 @@ static mla_status prefill_unabsorbed_impl(const mla_dims* dims, mla_dtype dtype,
   p.n_h = dims->n_h;
   p.chunk = chunk;
   p.max_len = static_cast<int32_t>(max_len);
-  p.precise_below = kPreciseBelow;
+  p.precise_below = yarn_on(dims) ? kAllPrecise : kPreciseBelow;   // YaRN: hi + lo everywhere
   p.qscale = static_cast<float>(scale_of(dims) * 1.4426950408889634);
   fill_rope(dims, p.rope);
   return hip_status(mla::launch_prefill_unabsorbed(e, p, static_cast<hipStream_t>(stream)), "mla_prefill_unabsorbed");
@@ -742,11 +793,13 @@ mla_status mla_append_kv_fp8(const mla_dims* dims, int32_t n_tok, const void* c_
   return hip_status(mla::launch_append_fp8(a, static_cast<hipStream_t>(stream)), "mla_append_kv_fp8");
 }
 
-static mla_status fp8_partials(const mla_dims* dims, int32_t batch, const void* q_lat, const mla_fp8_cache* cache,
+static mla_status fp8_partials(const mla_dims* dims, int32_t batch, const void* q_lat, const void* q_lat_lo,
+                               const mla_fp8_cache* cache,
                                int64_t stride, const int32_t* seq_lens, int32_t max_seq_len, int32_t S, float* z,
                                float* lse, hipStream_t s, const char* who, int32_t q_per_seq = 1, int prefill = 0) {
   mla::SplitArgs a{};
   a.q_lat = q_lat;
+  a.q_lat_lo = q_lat_lo;
   a.cache = cache->codes;
   a.fp8_rope = cache->rope;
   a.fp8_scale = cache->scale;
@@ -764,6 +817,7 @@ static mla_status fp8_partials(const mla_dims* dims, int32_t batch, const void* 
   a.q_per_seq = q_per_seq;
   a.prefill = prefill;
   a.qscale = static_cast<float>(scale_of(dims) * 1.4426950408889634);
+  a.precise_below = precise_rows_of(dims, MLA_BF16);
   return hip_status(mla::launch_splitkv_fp8(a, s), who);
 }
 
@@ -781,7 +835,8 @@ static mla_status check_fp8_decode(const mla_dims* dims, int32_t batch, const vo
   return MLA_OK;
 }
 
-mla_status mla_decode_partials_fp8(const mla_dims* dims, int32_t batch, const void* q_lat, const mla_fp8_cache* cache,
+mla_status mla_decode_partials_fp8(const mla_dims* dims, int32_t batch, const void* q_lat, const void* q_lat_lo,
+                                   const mla_fp8_cache* cache,
                                    int64_t cache_seq_stride, const int32_t* seq_lens, int32_t max_seq_len,
                                    int32_t num_splits, float* z_part, float* lse_part, void* stream) {
   mla_status st = check_fp8_decode(dims, batch, q_lat, cache, cache_seq_stride, seq_lens, max_seq_len);
@@ -789,11 +844,12 @@ mla_status mla_decode_partials_fp8(const mla_dims* dims, int32_t batch, const vo
   if (num_splits < 1 || num_splits > kMaxSplits)
     return fail(MLA_ERR_INVALID_ARGUMENT, "num_splits=%d out of range [1,%d]", num_splits, kMaxSplits);
   if (!z_part || !lse_part) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  return fp8_partials(dims, batch, q_lat, cache, cache_seq_stride, seq_lens, max_seq_len, num_splits, z_part, lse_part,
-                      static_cast<hipStream_t>(stream), "mla_decode_partials_fp8");
+  return fp8_partials(dims, batch, q_lat, q_lat_lo, cache, cache_seq_stride, seq_lens, max_seq_len, num_splits, z_part,
+                      lse_part, static_cast<hipStream_t>(stream), "mla_decode_partials_fp8");
 }
 
-mla_status mla_decode_fp8(const mla_dims* dims, int32_t batch, const void* q_lat, const mla_fp8_cache* cache,
+mla_status mla_decode_fp8(const mla_dims* dims, int32_t batch, const void* q_lat, const void* q_lat_lo,
+                          const mla_fp8_cache* cache,
                           int64_t cache_seq_stride, const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv,
                           float* out, float* out_latent, void* workspace, size_t workspace_bytes, void* stream) {
   mla_status st = check_fp8_decode(dims, batch, q_lat, cache, cache_seq_stride, seq_lens, max_seq_len);
@@ -807,14 +863,14 @@ mla_status mla_decode_fp8(const mla_dims* dims, int32_t batch, const void* q_lat
   float* lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         align256(static_cast<size_t>(batch) * S * dims->n_h * dims->d_c * sizeof(float)));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = fp8_partials(dims, batch, q_lat, cache, cache_seq_stride, seq_lens, max_seq_len, S, z, lse, s,
+  st = fp8_partials(dims, batch, q_lat, q_lat_lo, cache, cache_seq_stride, seq_lens, max_seq_len, S, z, lse, s,
                     "mla_decode_fp8 (partials)");
   if (st != MLA_OK) return st;
   mla::CombineArgs a{z, lse, w_uv, out, out_latent, batch, dims->n_h, dims->d_c, dims->d_h, S};
   return hip_status(mla::launch_combine(a, 1, s), "mla_decode_fp8 (combine)");
 }
 mla_status mla_prefill_fp8(const mla_dims* dims, int32_t batch, int32_t chunk, const void* q_lat,
-                           const mla_fp8_cache* cache, int64_t cache_seq_stride, const int32_t* prefix_lens,
+                           const void* q_lat_lo, const mla_fp8_cache* cache, int64_t cache_seq_stride, const int32_t* prefix_lens,
                            int32_t max_prefix_len, const void* w_uv, float* out, void* workspace,
                            size_t workspace_bytes, void* stream) {
   mla_status st = check_dims(dims, MLA_BF16);
@@ -839,7 +895,7 @@ mla_status mla_prefill_fp8(const mla_dims* dims, int32_t batch, int32_t chunk, c
   float* lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         align256(static_cast<size_t>(n_q) * S * dims->n_h * dims->d_c * sizeof(float)));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = fp8_partials(dims, static_cast<int32_t>(n_q), q_lat, cache, cache_seq_stride, prefix_lens,
+  st = fp8_partials(dims, static_cast<int32_t>(n_q), q_lat, q_lat_lo, cache, cache_seq_stride, prefix_lens,
                     static_cast<int32_t>(max_len), S, z, lse, s, "mla_prefill_fp8 (partials)", chunk, 1);
   if (st != MLA_OK) return st;
   mla::CombineArgs a{z, lse, w_uv, out, nullptr, static_cast<int32_t>(n_q), dims->n_h, dims->d_c, dims->d_h, S};

@@ -40,13 +40,16 @@ struct AppendArgs {
   float* fp8_scale;
 };
 
-// Absorbed query layout (q_lat): fp32 [n_q][n_h][d_c + d_r] for fp32 storage;
-// for bf16 storage [n_q][n_h][2][d_c + d_r] bf16, the fp32 value v split as
-// hi = bf16(v) (part 0) and lo = bf16(v - hi) (part 1).
+// Absorbed queries: q_lat [n_q][n_h][d_c + d_r] in the storage dtype (fp32, or
+// bf16 = RNE of the fp32 value v), and for bf16 an optional second plane
+// q_lat_lo of the same shape holding bf16(v - bf16(v)), so that hi + lo
+// carries v to ~2^-17.  Kernels that refine their score with lo take it as 0
+// when the plane is absent.
 struct RopeQArgs {
   const void* q_r;       // [n_q][n_h][d_r] (storage dtype)
   const int32_t* q_pos;  // [n_q]
-  void* q_lat;           // absorbed query layout above
+  void* q_lat;           // absorbed queries (hi plane for bf16)
+  void* q_lat_lo;        // bf16 lo plane or NULL
   int32_t n_q, n_h, d_c, d_r;
   RopeTable rope;
 };
@@ -54,7 +57,8 @@ struct RopeQArgs {
 struct AbsorbArgs {
   const void* q_c;   // [n_q][n_h][d_h] (storage dtype)
   const void* w_uk;  // [n_h][d_h][d_c] (storage dtype)
-  void* q_lat;       // absorbed query layout above
+  void* q_lat;       // absorbed queries (hi plane for bf16)
+  void* q_lat_lo;    // bf16 lo plane or NULL (not written)
   int32_t n_q, n_h, d_c, d_h, d_r;
   const void* q_r;       // [n_q][n_h][d_r] (storage dtype); used by the fused bf16 kernel
   const int32_t* q_pos;  // [n_q]
@@ -65,7 +69,8 @@ struct AbsorbArgs {
 bool absorb_fuses_rope(int bf16, int d_c, int d_h, int d_r);
 
 struct SplitArgs {
-  const void* q_lat;      // absorbed query layout above
+  const void* q_lat;      // absorbed queries (hi plane for bf16)
+  const void* q_lat_lo;   // bf16 lo plane or NULL (read as zeros)
   const void* cache;      // rows of d_c + d_r
   const int32_t* lens;    // decode: seq_lens[batch]; prefill: prefix_lens[batch]
   float* z_part;          // [n_q][num_splits][n_h][d_c]
@@ -78,6 +83,9 @@ struct SplitArgs {
   int32_t q_per_seq;      // 1 for decode, chunk for prefill
   int32_t prefill;        // 0 decode, 1 causal prefill
   float qscale;           // softmax_scale * log2(e)
+  // queries that attend fewer rows than this take the 16-head-group body,
+  // which scores with hi + lo and carries the softmax weights as hi + lo
+  int32_t precise_below;
   // paged cache (block_table != NULL): `cache` is the page pool, row r of
   // sequence b is row r & (2^page_shift - 1) of page block_table[b][r >> page_shift],
   // and stride = bt_stride << page_shift bounds the attended length
@@ -194,6 +202,9 @@ hipError_t launch_splitkv_fp8(const SplitArgs& a, hipStream_t st);
 // split-K plan of launch_kv_project_append: slices and k per slice (a multiple of 64)
 void kv_project_plan(int32_t n_tok, int32_t d_model, int32_t& k_slices, int32_t& k_per_slice);
 bool splitkv_has_fast_path(int n_h, int bf16, int d_c, int d_r);
+// every query of a launch takes the 16-head-group (hi + lo) path: the grouped
+// kernel runs it over (query, split, head group)
+bool splitkv_all_precise(int n_h, int32_t max_len, int32_t precise_below);
 
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -215,30 +226,30 @@ template <>
 __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, int64_t i) {
   return bf16_to_f32(p[i]);
 }
-// element e of (query n, head h) in the absorbed query layout
+// element e of (query n, head h) of the absorbed queries: the storage value,
+// plus for bf16 the lo plane's refinement when that plane is present
 template <typename T>
-__device__ __forceinline__ void store_q(void* q_lat, int64_t nh, int row_e, int e, float v);
+__device__ __forceinline__ void store_q(void* q_lat, void* q_lo, int64_t nh, int row_e, int e, float v);
 template <>
-__device__ __forceinline__ void store_q<float>(void* q_lat, int64_t nh, int row_e, int e, float v) {
+__device__ __forceinline__ void store_q<float>(void* q_lat, void*, int64_t nh, int row_e, int e, float v) {
   static_cast<float*>(q_lat)[nh * row_e + e] = v;
 }
 template <>
-__device__ __forceinline__ void store_q<uint16_t>(void* q_lat, int64_t nh, int row_e, int e, float v) {
-  uint16_t* q = static_cast<uint16_t*>(q_lat) + nh * 2 * row_e;
+__device__ __forceinline__ void store_q<uint16_t>(void* q_lat, void* q_lo, int64_t nh, int row_e, int e, float v) {
   const uint16_t hi = f32_to_bf16(v);
-  q[e] = hi;
-  q[row_e + e] = f32_to_bf16(v - bf16_to_f32(hi));
+  static_cast<uint16_t*>(q_lat)[nh * row_e + e] = hi;
+  if (q_lo) static_cast<uint16_t*>(q_lo)[nh * row_e + e] = f32_to_bf16(v - bf16_to_f32(hi));
 }
 template <typename T>
-__device__ __forceinline__ float load_q(const void* q_lat, int64_t nh, int row_e, int e);
+__device__ __forceinline__ float load_q(const void* q_lat, const void* q_lo, int64_t nh, int row_e, int e);
 template <>
-__device__ __forceinline__ float load_q<float>(const void* q_lat, int64_t nh, int row_e, int e) {
+__device__ __forceinline__ float load_q<float>(const void* q_lat, const void*, int64_t nh, int row_e, int e) {
   return static_cast<const float*>(q_lat)[nh * row_e + e];
 }
 template <>
-__device__ __forceinline__ float load_q<uint16_t>(const void* q_lat, int64_t nh, int row_e, int e) {
-  const uint16_t* q = static_cast<const uint16_t*>(q_lat) + nh * 2 * row_e;
-  return bf16_to_f32(q[e]) + bf16_to_f32(q[row_e + e]);
+__device__ __forceinline__ float load_q<uint16_t>(const void* q_lat, const void* q_lo, int64_t nh, int row_e, int e) {
+  const float h = bf16_to_f32(static_cast<const uint16_t*>(q_lat)[nh * row_e + e]);
+  return q_lo ? h + bf16_to_f32(static_cast<const uint16_t*>(q_lo)[nh * row_e + e]) : h;
 }
 
 // RoPE of the interleaved pair (x0, x1) by angle pos * theta: the angle and

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void splitkv_fp8_generic_kernel(SplitArgs a) {
     if (tid == 0) *lse_o = NEG_INF;
     return;
   }
-  for (int e = tid; e < ROWE; e += 256) q[e] = load_q<uint16_t>(a.q_lat, static_cast<int64_t>(n) * a.n_h + h, ROWE, e);
+  for (int e = tid; e < ROWE; e += 256) q[e] = load_q<uint16_t>(a.q_lat, a.q_lat_lo, static_cast<int64_t>(n) * a.n_h + h, ROWE, e);
   __syncthreads();
   const int64_t base_row = static_cast<int64_t>(b) * a.stride;
   const uint8_t* codes = static_cast<const uint8_t*>(a.cache);
@@ -142,6 +142,302 @@ __global__ __launch_bounds__(256) void splitkv_fp8_generic_kernel(SplitArgs a) {
   zo[tid] = z0 * inv;
   zo[tid + 256] = z1 * inv;
   if (tid == 0) *lse_o = (m + log2f(lsum)) * LN2;
+}
+
+// ------------------------------------------------------------------------
+// 16 heads over the FP8 cache, and the precise path of the 128-head kernel
+// (queries that attend fewer than precise_below rows, one 16-head group at a
+// time): the 16-head bf16 kernel's design (mla_splitkv.hip:
+// each wave streams every fourth 16-row tile into LDS buffers of its own, with
+// its own online softmax and Z, merged through LDS at the end) on the FP8
+// tile, which per row is 644 bytes instead of 1,152: this shape is a stream of
+// the cache, so the bytes are the time.  The smaller tiles leave room for
+// three buffers per wave (two tiles in flight while one is computed).
+//   * a tile buffer (11 KB) holds the 16 rows' codes (8 KB; row t at 512 t,
+//     chunk k at k ^ t), RoPE keys (2 KB; row t at 128 t, chunk k of 8 at
+//     k ^ ((t >> 1) & 7)) and scales (64 B; lanes 0-3 of the wave's DMA);
+//   * score (v_mfma_f32_16x16x32_bf16, queries hi then lo): the latent
+//     products accumulate apart from the RoPE ones, and a row's score is
+//     s_t latent + rope;
+//   * value: the K = 32 product pairs 4 rows with P hi and the same rows with
+//     P lo (P = p s_t split as bf16 hi + lo), so its operand is 4 distinct
+//     rows' codes of the lane's column, used twice.  One byte-transpose read
+//     serves two column blocks: lane pairs 0-3 address the 4 rows in block c,
+//     pairs 4-7 the same rows in block c + 1.
+// ------------------------------------------------------------------------
+constexpr int H8_TILE = 16;
+constexpr int NQ16 = (D_C + D_R) / 32;   // 16-head score k-steps of 32 elements
+constexpr int H8_CODES = 0, H8_ROPE = 8192, H8_SCALE = 10240, H8_BUF = 11264;
+constexpr int H8_LOADS = 11;   // DMAs per lane per tile: 8 code, 2 RoPE, 1 scale
+constexpr int H8_ZPAD = D_C * 4 + 16;   // merge: bytes per staged head row
+constexpr int H8_NB = 3;      // LDS tile buffers per wave
+constexpr int H8_SMEM = (4 * 16 * H8_ZPAD + 2 * 4 * 16 * 4 > 4 * H8_NB * H8_BUF) ? 4 * 16 * H8_ZPAD + 2 * 4 * 16 * 4
+                                                                                 : 4 * H8_NB * H8_BUF;
+
+// Heads h0..h0+15 of query n over split `split` (sequence b, attended length
+// len): the 16-head kernel's body, also the precise path of the 128-head
+// kernel.  smem: at least H8_SMEM bytes of LDS; the caller separates two
+// calls with a barrier.
+__device__ __forceinline__ void h8_group(const SplitArgs& a, uint8_t* smem, int n, int split, int h0, int b,
+                                         int64_t len) {
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q4 = l >> 4, j16 = l & 15;
+  const int64_t lo = static_cast<int64_t>(split) * a.split_rows;
+  const int64_t hi = min(lo + a.split_rows, len);
+  float* zo = a.z_part + ((static_cast<int64_t>(n) * a.num_splits + split) * a.n_h + h0) * D_C;
+  float* lse_o = a.lse_part + (static_cast<int64_t>(n) * a.num_splits + split) * a.n_h + h0;
+  if (lo >= hi) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    for (int idx = tid; idx < 16 * D_C / 4; idx += 256) reinterpret_cast<f32x4*>(zo)[idx] = zero;
+    if (tid < 16) lse_o[tid] = NEG_INF;
+    return;
+  }
+  const int64_t ntiles = (hi - lo + H8_TILE - 1) / H8_TILE;
+  const int my_tiles = static_cast<int>((ntiles > w) ? (ntiles - w + 3) / 4 : 0);  // wave-uniform
+
+  // ---- absorbed queries (B operands): head h0 + j16, elements 32 s + 8 q4 .. +7
+  // of the hi plane and of the lo plane (zeros without one)
+  u32x4 qh[NQ16], ql[NQ16];
+  {
+    const int64_t qo = (static_cast<int64_t>(n) * a.n_h + h0 + j16) * ROWE + 8 * q4;
+    const uint16_t* q = static_cast<const uint16_t*>(a.q_lat) + qo;
+#pragma unroll
+    for (int s = 0; s < NQ16; ++s) qh[s] = *reinterpret_cast<const u32x4*>(q + 32 * s);
+    if (a.q_lat_lo) {
+      const uint16_t* ql_src = static_cast<const uint16_t*>(a.q_lat_lo) + qo;
+#pragma unroll
+      for (int s = 0; s < NQ16; ++s) ql[s] = *reinterpret_cast<const u32x4*>(ql_src + 32 * s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NQ16; ++s) ql[s] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // ---- this wave's tile DMAs: its k-th tile (split tile w + 4k) goes to
+  // buffer H8_NB w + k % H8_NB.  Code slot f = 64 i + l holds global chunk
+  // (t, p ^ t) with (t, p) = (f / 32, f % 32); RoPE slot f = 64 i + l holds
+  // (t, p ^ ((t >> 1) & 7)) with (t, p) = (f / 8, f % 8); scale lane l fetches
+  // bytes 16 l .. (rows 4l..4l+3).  Each buffer resource spans the tile's rows
+  // inside the split, so rows past its end arrive as zeros.
+  const int64_t row0 = static_cast<int64_t>(b) * a.stride + lo;
+  const uint64_t gc = reinterpret_cast<uint64_t>(a.cache) + static_cast<uint64_t>(row0) * D_C;
+  const uint64_t gr = reinterpret_cast<uint64_t>(a.fp8_rope) + static_cast<uint64_t>(row0) * (2 * D_R);
+  const uint64_t gs = reinterpret_cast<uint64_t>(a.fp8_scale) + static_cast<uint64_t>(row0) * 4;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint8_t*)smem));
+  auto mk_rsrc = [&](uint64_t ga, int64_t bytes) {
+    const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(ga & 0xffffffffu)),
+                      __builtin_amdgcn_readfirstlane(static_cast<int>((ga >> 32) & 0xffffu)),
+                      __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), 0x00020000};
+    return rs;
+  };
+  auto issue = [&](int k, int slot) {
+    const int64_t it = w + 4 * static_cast<int64_t>(k);
+    const int64_t rows = min(static_cast<int64_t>(H8_TILE), hi - lo - it * H8_TILE);
+    const uint64_t off = static_cast<uint64_t>(it) * H8_TILE;
+    const i32x4 rc = mk_rsrc(gc + off * D_C, rows * D_C);
+    const i32x4 rr = mk_rsrc(gr + off * 2 * D_R, rows * 2 * D_R);
+    const i32x4 rsc = mk_rsrc(gs + off * 4, rows * 4);
+    const uint32_t dst = lds0 + static_cast<uint32_t>((H8_NB * w + slot) * H8_BUF);
+    // the lane index passes through an empty asm so that the source offsets
+    // are formed here, not hoisted out of the loop into live registers
+    int lx = l;
+    asm volatile("" : "+v"(lx));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int f = 64 * i + lx;
+      const int t = f >> 5, p = f & 31;
+      dma16(dst + H8_CODES + 1024u * i, 16 * (32 * t + (p ^ t)), rc, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int f = 64 * i + lx;
+      const int t = f >> 3, p = f & 7;
+      dma16(dst + H8_ROPE + 1024u * i, 16 * (8 * t + (p ^ ((t >> 1) & 7))), rr, 0);
+    }
+    dma16(dst + H8_SCALE, 16 * lx, rsc, 0);
+  };
+  if (my_tiles > 0) issue(0, 0);
+  if (my_tiles > 1) issue(1, 1);
+  if (my_tiles > 2) issue(2, 2);
+  vm_wait<0>();
+
+  // ---- per-lane LDS operand offsets
+  // score A, latent step s: row j16, codes 32 s + 8 q4 .. +7 = half q4 & 1 of chunk 2 s + q4 / 2
+  const int sc_row = H8_CODES + 512 * j16 + 8 * (q4 & 1);
+  // score A, RoPE step r: row j16, elements 32 r + 8 q4 = chunk 4 r + q4 of the row's 8
+  int sr_off[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) sr_off[r] = H8_ROPE + 128 * j16 + 16 * ((4 * r + q4) ^ ((j16 >> 1) & 7));
+  // value A (byte transpose) of column blocks c, c + 1 (c even): lane pair
+  // jp = (l & 15) / 2 of group q4 addresses row 4 q4 + jp % 4, half l & 1 of
+  // block c + jp / 4's chunk; the lane receives bytes 0-3 = its column of
+  // block c over the 4 rows, bytes 4-7 = block c + 1's
+  const int tr_row = 4 * q4 + (((l & 15) >> 1) & 3);
+  const int tr_blk = (l & 15) >> 3;
+  const int tr_base = H8_CODES + 512 * tr_row + 8 * (l & 1);
+  auto vread = [&](const uint8_t* buf, int c) {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) i32x2*)(buf + tr_base + 16 * ((c + tr_blk) ^ tr_row)));
+  };
+  // 4 codes (one dword) -> the K = 32 operand: the 4 rows' bf16 values, twice
+  auto dup4 = [](uint32_t x) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
+    const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
+    return __builtin_bit_cast(bf16x8, u32x4{ua, ub, ua, ub});
+  };
+
+  f32x4 zacc[32];  // Z^T of c-block c: columns 16 c + 4 q4 + i of head j16
+#pragma unroll
+  for (int c = 0; c < 32; ++c) zacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = NEG_INF, l_run = 0.f;
+  const float qscale = a.qscale;
+
+  int slot = 0;   // k % H8_NB
+  for (int k = 0; k < my_tiles; ++k) {
+    // this tile has landed (the next two tiles' loads may stay in flight)
+    if (k + 2 < my_tiles)
+      vm_wait<2 * H8_LOADS>();
+    else if (k + 1 < my_tiles)
+      vm_wait<H8_LOADS>();
+    else
+      vm_wait<0>();
+    const uint8_t* buf = smem + (H8_NB * w + slot) * H8_BUF;
+    const int64_t it = w + 4 * static_cast<int64_t>(k);
+    const int valid = static_cast<int>(min(hi - lo - it * H8_TILE, static_cast<int64_t>(H8_TILE)));
+
+    // -------------------------------------------------- score
+    constexpr int PF = 4;
+    f32x4 slat = {0.f, 0.f, 0.f, 0.f}, srope = {0.f, 0.f, 0.f, 0.f};
+    {
+      uint2 kb[PF];
+#pragma unroll
+      for (int s = 0; s < PF; ++s) kb[s] = *reinterpret_cast<const uint2*>(buf + sc_row + 16 * ((2 * s + (q4 >> 1)) ^ j16));
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const uint2 raw = kb[s % PF];
+        if (s + PF < 16)
+          kb[s % PF] = *reinterpret_cast<const uint2*>(buf + sc_row + 16 * ((2 * (s + PF) + (q4 >> 1)) ^ j16));
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, fp8x8_to_bf16(raw.x, raw.y));
+        slat = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, __builtin_bit_cast(bf16x8, qh[s]), slat, 0, 0, 0);
+        slat = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, __builtin_bit_cast(bf16x8, ql[s]), slat, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(buf + sr_off[r]));
+        srope = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, __builtin_bit_cast(bf16x8, qh[16 + r]), srope, 0, 0, 0);
+        srope = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, __builtin_bit_cast(bf16x8, ql[16 + r]), srope, 0, 0, 0);
+      }
+    }
+    // first value operands: independent of P, so their latency overlaps the softmax
+    constexpr int VPF = 4;   // reads (pairs of column blocks) in flight
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    i32x2 vb[VPF];
+#pragma unroll
+    for (int c = 0; c < VPF; ++c) vb[c] = vread(buf, 2 * c);
+    const f32x4 sv = *reinterpret_cast<const f32x4*>(buf + H8_SCALE + 16 * q4);   // rows 4 q4 .. +3
+
+    // -------------------------------------------------- online softmax (log2)
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (4 * q4 + i < valid) ? fmaf(sv[i], slat[i], srope[i]) : NEG_INF;
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = pair_max32(mx);
+    mx = pair_max16(mx);
+    const float mt = mx * qscale;
+    const bool need = mt > m_run + RESCALE_TAU;
+    if (__ballot(need)) {
+      const float m_new = need ? mt : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) zacc[c] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = -m_run;
+    i16x4 ph, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(x[i], qscale, neg_m));
+      l_run += pv;
+      const float ps = pv * sv[i];   // the row's scale folds into its weight
+      const uint16_t h16 = f32_to_bf16(ps);
+      ph[i] = static_cast<short>(h16);
+      pl[i] = static_cast<short>(f32_to_bf16(ps - bf16_to_f32(h16)));
+    }
+    const bf16x8 pp = cat(ph, pl);
+
+    // -------------------------------------------------- value Z^T += rows^T . P^T
+#pragma unroll
+    for (int cp = 0; cp < 16; ++cp) {
+      const i32x2 raw = vb[cp % VPF];
+      if (cp + VPF < 16) vb[cp % VPF] = vread(buf, 2 * (cp + VPF));
+      zacc[2 * cp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dup4(static_cast<uint32_t>(raw[0])), pp, zacc[2 * cp], 0,
+                                                             0, 0);
+      zacc[2 * cp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dup4(static_cast<uint32_t>(raw[1])), pp,
+                                                                 zacc[2 * cp + 1], 0, 0, 0);
+    }
+
+    // the buffer is free once this wave's reads of it returned: refill it
+    if (k + H8_NB < my_tiles) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+      issue(k + H8_NB, slot);
+    }
+    slot = (slot + 1 == H8_NB) ? 0 : slot + 1;
+  }
+
+  // ---- merge the four waves (as the bf16 kernel)
+  float lt = pair_sum32(l_run);
+  lt = pair_sum16(lt);
+  __syncthreads();
+  float* mst = reinterpret_cast<float*>(smem + 4 * 16 * H8_ZPAD);
+  float* lst = mst + 64;
+  if (q4 == 0) {
+    mst[16 * w + j16] = m_run;
+    lst[16 * w + j16] = lt;
+  }
+  __syncthreads();
+  float M = NEG_INF;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) M = fmaxf(M, mst[16 * v + j16]);
+  float L = 0.f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float mv = mst[16 * v + j16];
+    if (mv != NEG_INF) L += lst[16 * v + j16] * __builtin_amdgcn_exp2f(mv - M);
+  }
+  const float f = (m_run != NEG_INF && L > 0.f) ? __builtin_amdgcn_exp2f(m_run - M) / L : 0.f;
+  {
+    uint8_t* row = smem + w * 16 * H8_ZPAD + j16 * H8_ZPAD + 16 * q4;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      const f32x4 v = {zacc[c][0] * f, zacc[c][1] * f, zacc[c][2] * f, zacc[c][3] * f};
+      *reinterpret_cast<f32x4*>(row + 64 * c) = v;
+    }
+  }
+  if (w == 0 && q4 == 0) lse_o[j16] = (L > 0.f) ? (M + log2f(L)) * LN2 : NEG_INF;
+  __syncthreads();
+  for (int idx = tid; idx < 16 * (D_C / 4); idx += 256) {
+    const int h = idx >> 7, c4 = idx & 127;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(smem + h * H8_ZPAD + 16 * c4);
+#pragma unroll
+    for (int v = 1; v < 4; ++v) acc += *reinterpret_cast<const f32x4*>(smem + v * 16 * H8_ZPAD + h * H8_ZPAD + 16 * c4);
+    *reinterpret_cast<f32x4*>(zo + h * D_C + 4 * c4) = acc;
+  }
+}
+
+// n_h a multiple of 16: one workgroup per (query, split, group of 16 heads).
+__global__ __launch_bounds__(256, 1) void splitkv_fp8_h16_kernel(SplitArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[H8_SMEM];
+  const int n = blockIdx.x;
+  int b;
+  int64_t len;
+  query_range(a, n, b, len);
+  h8_group(a, smem, n, blockIdx.y, 16 * blockIdx.z, b, len);
 }
 
 // ------------------------------------------------------------------------
@@ -190,7 +486,9 @@ __global__ __launch_bounds__(256, 1) void splitkv_fp8_wide_kernel(SplitArgs a) {
   constexpr int A_OFF = P_OFF + 4 * 2 * 64 * 16;   // rescale factors: [head % 32][head group] floats
   constexpr int I_OFF = A_OFF + 128 * 4;           // 1 / l per head (128 floats)
   constexpr int T_OFF = I_OFF + 128 * 4;           // per-thread DMA source chunk indices, u16 [5][256]
-  __shared__ __attribute__((aligned(16))) uint8_t smem[T_OFF + 5 * 256 * 2];
+  // (the precise path's 16-head groups need H8_SMEM bytes; one workgroup per CU either way)
+  constexpr int SMEM = (T_OFF + 5 * 256 * 2 > H8_SMEM) ? T_OFF + 5 * 256 * 2 : H8_SMEM;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int g32 = l >> 5, l32 = l & 31;
@@ -207,6 +505,13 @@ __global__ __launch_bounds__(256, 1) void splitkv_fp8_wide_kernel(SplitArgs a) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int idx = tid; idx < 128 * D_C / 4; idx += 256) reinterpret_cast<f32x4*>(zo)[idx] = zero;
     if (tid < 128) lse_o[tid] = NEG_INF;
+    return;
+  }
+  if (len < a.precise_below) {  // few rows: 16-head groups with hi + lo products (uniform)
+    for (int g = 0; g < 8; ++g) {
+      if (g) __syncthreads();
+      h8_group(a, smem, n, split, 16 * g, b, len);
+    }
     return;
   }
 
@@ -278,7 +583,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_fp8_wide_kernel(SplitArgs a) {
   u32x4 qreg[NQ];
   {
     const uint16_t* qh = static_cast<const uint16_t*>(a.q_lat) +
-                         (static_cast<int64_t>(n) * 128 + 32 * w + l32) * 2 * ROWE + 8 * g32;
+                         (static_cast<int64_t>(n) * 128 + 32 * w + l32) * ROWE + 8 * g32;
 #pragma unroll
     for (int s = 0; s < NQ; ++s) qreg[s] = *reinterpret_cast<const u32x4*>(qh + 16 * s);
   }
@@ -548,289 +853,12 @@ __global__ __launch_bounds__(256, 1) void splitkv_fp8_wide_kernel(SplitArgs a) {
   }
 }
 
-// ------------------------------------------------------------------------
-// 16 heads over the FP8 cache: the 16-head bf16 kernel's design (mla_splitkv.hip:
-// each wave streams every fourth 16-row tile into LDS buffers of its own, with
-// its own online softmax and Z, merged through LDS at the end) on the FP8
-// tile, which per row is 644 bytes instead of 1,152: this shape is a stream of
-// the cache, so the bytes are the time.  The smaller tiles leave room for
-// three buffers per wave (two tiles in flight while one is computed).
-//   * a tile buffer (11 KB) holds the 16 rows' codes (8 KB; row t at 512 t,
-//     chunk k at k ^ t), RoPE keys (2 KB; row t at 128 t, chunk k of 8 at
-//     k ^ ((t >> 1) & 7)) and scales (64 B; lanes 0-3 of the wave's DMA);
-//   * score (v_mfma_f32_16x16x32_bf16, queries hi then lo): the latent
-//     products accumulate apart from the RoPE ones, and a row's score is
-//     s_t latent + rope;
-//   * value: the K = 32 product pairs 4 rows with P hi and the same rows with
-//     P lo (P = p s_t split as bf16 hi + lo), so its operand is 4 distinct
-//     rows' codes of the lane's column, used twice.  One byte-transpose read
-//     serves two column blocks: lane pairs 0-3 address the 4 rows in block c,
-//     pairs 4-7 the same rows in block c + 1.
-// ------------------------------------------------------------------------
-constexpr int H8_TILE = 16;
-constexpr int NQ16 = (D_C + D_R) / 32;   // 16-head score k-steps of 32 elements
-constexpr int H8_CODES = 0, H8_ROPE = 8192, H8_SCALE = 10240, H8_BUF = 11264;
-constexpr int H8_LOADS = 11;   // DMAs per lane per tile: 8 code, 2 RoPE, 1 scale
-constexpr int H8_ZPAD = D_C * 4 + 16;   // merge: bytes per staged head row
-constexpr int H8_NB = 3;      // LDS tile buffers per wave
-constexpr int H8_SMEM = (4 * 16 * H8_ZPAD + 2 * 4 * 16 * 4 > 4 * H8_NB * H8_BUF) ? 4 * 16 * H8_ZPAD + 2 * 4 * 16 * 4
-                                                                                 : 4 * H8_NB * H8_BUF;
-
-__global__ __launch_bounds__(256, 1) void splitkv_fp8_h16_kernel(SplitArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[H8_SMEM];
-  const int tid = threadIdx.x, l = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int q4 = l >> 4, j16 = l & 15;
-  const int n = blockIdx.x, split = blockIdx.y;
-  int b;
-  int64_t len;
-  query_range(a, n, b, len);
-  const int64_t lo = static_cast<int64_t>(split) * a.split_rows;
-  const int64_t hi = min(lo + a.split_rows, len);
-  float* zo = a.z_part + (static_cast<int64_t>(n) * a.num_splits + split) * 16 * D_C;
-  float* lse_o = a.lse_part + (static_cast<int64_t>(n) * a.num_splits + split) * 16;
-  if (lo >= hi) {
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    for (int idx = tid; idx < 16 * D_C / 4; idx += 256) reinterpret_cast<f32x4*>(zo)[idx] = zero;
-    if (tid < 16) lse_o[tid] = NEG_INF;
-    return;
-  }
-  const int64_t ntiles = (hi - lo + H8_TILE - 1) / H8_TILE;
-  const int my_tiles = static_cast<int>((ntiles > w) ? (ntiles - w + 3) / 4 : 0);  // wave-uniform
-
-  // ---- absorbed queries (B operands): head j16, elements 32 s + 8 q4 .. +7
-  u32x4 qh[NQ16], ql[NQ16];
-  {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q_lat) + (static_cast<int64_t>(n) * 16 + j16) * 2 * ROWE + 8 * q4;
-#pragma unroll
-    for (int s = 0; s < NQ16; ++s) {
-      qh[s] = *reinterpret_cast<const u32x4*>(q + 32 * s);
-      ql[s] = *reinterpret_cast<const u32x4*>(q + ROWE + 32 * s);
-    }
-  }
-
-  // ---- this wave's tile DMAs: its k-th tile (split tile w + 4k) goes to
-  // buffer H8_NB w + k % H8_NB.  Code slot f = 64 i + l holds global chunk
-  // (t, p ^ t) with (t, p) = (f / 32, f % 32); RoPE slot f = 64 i + l holds
-  // (t, p ^ ((t >> 1) & 7)) with (t, p) = (f / 8, f % 8); scale lane l fetches
-  // bytes 16 l .. (rows 4l..4l+3).  Each buffer resource spans the tile's rows
-  // inside the split, so rows past its end arrive as zeros.
-  const int64_t row0 = static_cast<int64_t>(b) * a.stride + lo;
-  const uint64_t gc = reinterpret_cast<uint64_t>(a.cache) + static_cast<uint64_t>(row0) * D_C;
-  const uint64_t gr = reinterpret_cast<uint64_t>(a.fp8_rope) + static_cast<uint64_t>(row0) * (2 * D_R);
-  const uint64_t gs = reinterpret_cast<uint64_t>(a.fp8_scale) + static_cast<uint64_t>(row0) * 4;
-  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) uint8_t*)smem));
-  auto mk_rsrc = [&](uint64_t ga, int64_t bytes) {
-    const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(ga & 0xffffffffu)),
-                      __builtin_amdgcn_readfirstlane(static_cast<int>((ga >> 32) & 0xffffu)),
-                      __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), 0x00020000};
-    return rs;
-  };
-  auto issue = [&](int k, int slot) {
-    const int64_t it = w + 4 * static_cast<int64_t>(k);
-    const int64_t rows = min(static_cast<int64_t>(H8_TILE), hi - lo - it * H8_TILE);
-    const uint64_t off = static_cast<uint64_t>(it) * H8_TILE;
-    const i32x4 rc = mk_rsrc(gc + off * D_C, rows * D_C);
-    const i32x4 rr = mk_rsrc(gr + off * 2 * D_R, rows * 2 * D_R);
-    const i32x4 rsc = mk_rsrc(gs + off * 4, rows * 4);
-    const uint32_t dst = lds0 + static_cast<uint32_t>((H8_NB * w + slot) * H8_BUF);
-    // the lane index passes through an empty asm so that the source offsets
-    // are formed here, not hoisted out of the loop into live registers
-    int lx = l;
-    asm volatile("" : "+v"(lx));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int f = 64 * i + lx;
-      const int t = f >> 5, p = f & 31;
-      dma16(dst + H8_CODES + 1024u * i, 16 * (32 * t + (p ^ t)), rc, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int f = 64 * i + lx;
-      const int t = f >> 3, p = f & 7;
-      dma16(dst + H8_ROPE + 1024u * i, 16 * (8 * t + (p ^ ((t >> 1) & 7))), rr, 0);
-    }
-    dma16(dst + H8_SCALE, 16 * lx, rsc, 0);
-  };
-  if (my_tiles > 0) issue(0, 0);
-  if (my_tiles > 1) issue(1, 1);
-  if (my_tiles > 2) issue(2, 2);
-  vm_wait<0>();
-
-  // ---- per-lane LDS operand offsets
-  // score A, latent step s: row j16, codes 32 s + 8 q4 .. +7 = half q4 & 1 of chunk 2 s + q4 / 2
-  const int sc_row = H8_CODES + 512 * j16 + 8 * (q4 & 1);
-  // score A, RoPE step r: row j16, elements 32 r + 8 q4 = chunk 4 r + q4 of the row's 8
-  int sr_off[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) sr_off[r] = H8_ROPE + 128 * j16 + 16 * ((4 * r + q4) ^ ((j16 >> 1) & 7));
-  // value A (byte transpose) of column blocks c, c + 1 (c even): lane pair
-  // jp = (l & 15) / 2 of group q4 addresses row 4 q4 + jp % 4, half l & 1 of
-  // block c + jp / 4's chunk; the lane receives bytes 0-3 = its column of
-  // block c over the 4 rows, bytes 4-7 = block c + 1's
-  const int tr_row = 4 * q4 + (((l & 15) >> 1) & 3);
-  const int tr_blk = (l & 15) >> 3;
-  const int tr_base = H8_CODES + 512 * tr_row + 8 * (l & 1);
-  auto vread = [&](const uint8_t* buf, int c) {
-    typedef int i32x2 __attribute__((ext_vector_type(2)));
-    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-        (__attribute__((address_space(3))) i32x2*)(buf + tr_base + 16 * ((c + tr_blk) ^ tr_row)));
-  };
-  // 4 codes (one dword) -> the K = 32 operand: the 4 rows' bf16 values, twice
-  auto dup4 = [](uint32_t x) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
-    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
-    const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
-    return __builtin_bit_cast(bf16x8, u32x4{ua, ub, ua, ub});
-  };
-
-  f32x4 zacc[32];  // Z^T of c-block c: columns 16 c + 4 q4 + i of head j16
-#pragma unroll
-  for (int c = 0; c < 32; ++c) zacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = NEG_INF, l_run = 0.f;
-  const float qscale = a.qscale;
-
-  int slot = 0;   // k % H8_NB
-  for (int k = 0; k < my_tiles; ++k) {
-    // this tile has landed (the next two tiles' loads may stay in flight)
-    if (k + 2 < my_tiles)
-      vm_wait<2 * H8_LOADS>();
-    else if (k + 1 < my_tiles)
-      vm_wait<H8_LOADS>();
-    else
-      vm_wait<0>();
-    const uint8_t* buf = smem + (H8_NB * w + slot) * H8_BUF;
-    const int64_t it = w + 4 * static_cast<int64_t>(k);
-    const int valid = static_cast<int>(min(hi - lo - it * H8_TILE, static_cast<int64_t>(H8_TILE)));
-
-    // -------------------------------------------------- score
-    constexpr int PF = 4;
-    f32x4 slat = {0.f, 0.f, 0.f, 0.f}, srope = {0.f, 0.f, 0.f, 0.f};
-    {
-      uint2 kb[PF];
-#pragma unroll
-      for (int s = 0; s < PF; ++s) kb[s] = *reinterpret_cast<const uint2*>(buf + sc_row + 16 * ((2 * s + (q4 >> 1)) ^ j16));
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const uint2 raw = kb[s % PF];
-        if (s + PF < 16)
-          kb[s % PF] = *reinterpret_cast<const uint2*>(buf + sc_row + 16 * ((2 * (s + PF) + (q4 >> 1)) ^ j16));
-        const bf16x8 kv = __builtin_bit_cast(bf16x8, fp8x8_to_bf16(raw.x, raw.y));
-        slat = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, __builtin_bit_cast(bf16x8, qh[s]), slat, 0, 0, 0);
-        slat = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, __builtin_bit_cast(bf16x8, ql[s]), slat, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(buf + sr_off[r]));
-        srope = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, __builtin_bit_cast(bf16x8, qh[16 + r]), srope, 0, 0, 0);
-        srope = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, __builtin_bit_cast(bf16x8, ql[16 + r]), srope, 0, 0, 0);
-      }
-    }
-    // first value operands: independent of P, so their latency overlaps the softmax
-    constexpr int VPF = 4;   // reads (pairs of column blocks) in flight
-    typedef int i32x2 __attribute__((ext_vector_type(2)));
-    i32x2 vb[VPF];
-#pragma unroll
-    for (int c = 0; c < VPF; ++c) vb[c] = vread(buf, 2 * c);
-    const f32x4 sv = *reinterpret_cast<const f32x4*>(buf + H8_SCALE + 16 * q4);   // rows 4 q4 .. +3
-
-    // -------------------------------------------------- online softmax (log2)
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (4 * q4 + i < valid) ? fmaf(sv[i], slat[i], srope[i]) : NEG_INF;
-    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = pair_max32(mx);
-    mx = pair_max16(mx);
-    const float mt = mx * qscale;
-    const bool need = mt > m_run + RESCALE_TAU;
-    if (__ballot(need)) {
-      const float m_new = need ? mt : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int c = 0; c < 32; ++c) zacc[c] *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = -m_run;
-    i16x4 ph, pl;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pv = __builtin_amdgcn_exp2f(fmaf(x[i], qscale, neg_m));
-      l_run += pv;
-      const float ps = pv * sv[i];   // the row's scale folds into its weight
-      const uint16_t h16 = f32_to_bf16(ps);
-      ph[i] = static_cast<short>(h16);
-      pl[i] = static_cast<short>(f32_to_bf16(ps - bf16_to_f32(h16)));
-    }
-    const bf16x8 pp = cat(ph, pl);
-
-    // -------------------------------------------------- value Z^T += rows^T . P^T
-#pragma unroll
-    for (int cp = 0; cp < 16; ++cp) {
-      const i32x2 raw = vb[cp % VPF];
-      if (cp + VPF < 16) vb[cp % VPF] = vread(buf, 2 * (cp + VPF));
-      zacc[2 * cp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dup4(static_cast<uint32_t>(raw[0])), pp, zacc[2 * cp], 0,
-                                                             0, 0);
-      zacc[2 * cp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dup4(static_cast<uint32_t>(raw[1])), pp,
-                                                                 zacc[2 * cp + 1], 0, 0, 0);
-    }
-
-    // the buffer is free once this wave's reads of it returned: refill it
-    if (k + H8_NB < my_tiles) {
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt at their maxima
-      issue(k + H8_NB, slot);
-    }
-    slot = (slot + 1 == H8_NB) ? 0 : slot + 1;
-  }
-
-  // ---- merge the four waves (as the bf16 kernel)
-  float lt = pair_sum32(l_run);
-  lt = pair_sum16(lt);
-  __syncthreads();
-  float* mst = reinterpret_cast<float*>(smem + 4 * 16 * H8_ZPAD);
-  float* lst = mst + 64;
-  if (q4 == 0) {
-    mst[16 * w + j16] = m_run;
-    lst[16 * w + j16] = lt;
-  }
-  __syncthreads();
-  float M = NEG_INF;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) M = fmaxf(M, mst[16 * v + j16]);
-  float L = 0.f;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const float mv = mst[16 * v + j16];
-    if (mv != NEG_INF) L += lst[16 * v + j16] * __builtin_amdgcn_exp2f(mv - M);
-  }
-  const float f = (m_run != NEG_INF && L > 0.f) ? __builtin_amdgcn_exp2f(m_run - M) / L : 0.f;
-  {
-    uint8_t* row = smem + w * 16 * H8_ZPAD + j16 * H8_ZPAD + 16 * q4;
-#pragma unroll
-    for (int c = 0; c < 32; ++c) {
-      const f32x4 v = {zacc[c][0] * f, zacc[c][1] * f, zacc[c][2] * f, zacc[c][3] * f};
-      *reinterpret_cast<f32x4*>(row + 64 * c) = v;
-    }
-  }
-  if (w == 0 && q4 == 0) lse_o[j16] = (L > 0.f) ? (M + log2f(L)) * LN2 : NEG_INF;
-  __syncthreads();
-  for (int idx = tid; idx < 16 * (D_C / 4); idx += 256) {
-    const int h = idx >> 7, c4 = idx & 127;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(smem + h * H8_ZPAD + 16 * c4);
-#pragma unroll
-    for (int v = 1; v < 4; ++v) acc += *reinterpret_cast<const f32x4*>(smem + v * 16 * H8_ZPAD + h * H8_ZPAD + 16 * c4);
-    *reinterpret_cast<f32x4*>(zo + h * D_C + 4 * c4) = acc;
-  }
-}
-
 hipError_t launch_splitkv_fp8(const SplitArgs& a, hipStream_t st) {
   if (a.n_q <= 0) return hipSuccess;
-  if (a.n_h == 128) {
+  if (a.n_h == 16 || (a.n_h == 128 && splitkv_all_precise(a.n_h, a.max_len, a.precise_below))) {
+    splitkv_fp8_h16_kernel<<<dim3(a.n_q, a.num_splits, a.n_h / 16), 256, 0, st>>>(a);
+  } else if (a.n_h == 128) {
     splitkv_fp8_wide_kernel<<<dim3(a.n_q, a.num_splits), 256, 0, st>>>(a);
-  } else if (a.n_h == 16) {
-    splitkv_fp8_h16_kernel<<<dim3(a.n_q, a.num_splits), 256, 0, st>>>(a);
   } else {
     splitkv_fp8_generic_kernel<<<dim3(a.n_q, a.num_splits, a.n_h), 256, 0, st>>>(a);
   }

@@ -67,8 +67,11 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
   const int b = blockIdx.z;
   const int h0 = blockIdx.y * XB_HEADS;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * XB_ROWS;
-  int64_t L = static_cast<int64_t>(a.prefix_lens[b]) + a.chunk;
-  L = min(L, static_cast<int64_t>(a.max_len));
+  // the prefix clamped to [0, max_len - chunk] exactly as the attention kernel
+  // clamps it, so that every row the attention reads is expanded
+  int64_t prefix = a.prefix_lens[b];
+  prefix = max(min(prefix, static_cast<int64_t>(a.max_len - a.chunk)), static_cast<int64_t>(0));
+  int64_t L = prefix + a.chunk;
   L = min(L, a.stride);
   if (row0 >= L) return;  // uniform over the workgroup
   const int nrows = static_cast<int>(min(static_cast<int64_t>(XB_ROWS), L - row0));
@@ -479,8 +482,9 @@ hipError_t launch_prefill_unabsorbed(const ExpandArgs& e_in, const PrefillArgs& 
   if (p.chunk <= 0 || p.batch <= 0) return hipSuccess;
   ExpandArgs e = e_in;
   // a hi + lo workgroup's first query sees < precise_below keys, so all its
-  // keys lie below precise_below + PQ - 1
-  e.lo_rows = p.precise_below + PQ;
+  // keys lie below precise_below + PQ - 1 (every row when all workgroups are)
+  const int64_t lo_rows = static_cast<int64_t>(p.precise_below) + PQ;
+  e.lo_rows = static_cast<int32_t>(lo_rows < 0x7fffffff ? lo_rows : 0x7fffffff);
   const dim3 g1(static_cast<unsigned>(e.rows_cap / XB_ROWS), e.n_h / XB_HEADS, e.batch);
   if (e.block_table)
     expand_kv_kernel<true><<<g1, 256, 0, st>>>(e);

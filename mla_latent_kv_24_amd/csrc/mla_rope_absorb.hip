@@ -5,8 +5,9 @@
 // on xyznot.com, Metode 1: only c^KV and k^R are cached).
 // A2 folds U^K_i into the query, q~_i = (U^K_i)^T q^C_i (review section 2), and
 // rotates the per-head RoPE query by the token position (review section 3).
-// Both are formed in fp32 and written in the absorbed query layout: fp32 for
-// fp32 storage, a bf16 hi/lo pair (the matrix-core operand format) for bf16.
+// Both are formed in fp32 and stored in the storage dtype: fp32, or bf16
+// hi = bf16(v) (the matrix-core operand) with, when the caller provides the
+// plane, lo = bf16(v - hi) beside it.
 #include "mla_common.h"
 
 namespace mla {
@@ -55,8 +56,8 @@ __global__ __launch_bounds__(256) void rope_q_kernel(RopeQArgs a) {
     const float x0 = load_as_f32(src, h * a.d_r + 2 * k);
     const float x1 = load_as_f32(src, h * a.d_r + 2 * k + 1);
     const int64_t nh = static_cast<int64_t>(n) * a.n_h + h;
-    store_q<T>(a.q_lat, nh, row_e, a.d_c + 2 * k, x0 * cs[k] - x1 * sn[k]);
-    store_q<T>(a.q_lat, nh, row_e, a.d_c + 2 * k + 1, x0 * sn[k] + x1 * cs[k]);
+    store_q<T>(a.q_lat, a.q_lat_lo, nh, row_e, a.d_c + 2 * k, x0 * cs[k] - x1 * sn[k]);
+    store_q<T>(a.q_lat, a.q_lat_lo, nh, row_e, a.d_c + 2 * k + 1, x0 * sn[k] + x1 * cs[k]);
   }
 }
 
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(256) void absorb_generic_kernel(AbsorbArgs a) {
   for (int c = threadIdx.x; c < a.d_c; c += blockDim.x) {
     float acc = 0.f;
     for (int d = 0; d < a.d_h; ++d) acc = fmaf(q[d], load_as_f32(w, static_cast<int64_t>(d) * a.d_c + c), acc);
-    store_q<T>(a.q_lat, nh, a.d_c + a.d_r, c, acc);
+    store_q<T>(a.q_lat, a.q_lat_lo, nh, a.d_c + a.d_r, c, acc);
   }
 }
 
@@ -89,7 +90,8 @@ __global__ __launch_bounds__(256) void absorb_generic_kernel(AbsorbArgs a) {
 // transpose read in distinct banks), rotates its RoPE pairs,
 // and runs 32-query blocks through v_mfma_f32_32x32x16_bf16: A = q_c rows from
 // global memory (d contiguous), B = W^UK columns via ds_read_b64_tr_b16.
-// Results are staged in LDS so the hi/lo bf16 pairs leave as 16-byte stores.
+// Results are staged in LDS so that hi (and lo, when its plane is given)
+// leave as 16-byte stores.
 constexpr int ABS_QCHUNK = 256;
 constexpr int ABS_COLS = 128;                      // latent columns per workgroup (a quarter of d_c)
 constexpr int ABS_PARTS = D_C / ABS_COLS;          // workgroups per head
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(256, 2) void absorb_mfma_kernel(AbsorbArgs a) {
   const int g = l >> 5;  // k-half of the 32x32x16 operand
   const uint16_t* qc = static_cast<const uint16_t*>(a.q_c);
   uint16_t* qout = static_cast<uint16_t*>(a.q_lat);
-  const int64_t rec = 2 * ROWE;  // bf16 elements per (query, head) record: hi row, lo row
+  uint16_t* qlo = static_cast<uint16_t*>(a.q_lat_lo);   // NULL: hi only
 
   // ---- issue: W^UK slab (16 chunks of 16 B per thread) and the first query block
   constexpr int WCH = ABS_COLS / 8;             // 16-B chunks per W row of the slab
@@ -174,9 +176,9 @@ __global__ __launch_bounds__(256, 2) void absorb_mfma_kernel(AbsorbArgs a) {
       const float x0 = xr[it].x, x1 = xr[it].y;
       const float y0 = x0 * cf - x1 * sf, y1 = x0 * sf + x1 * cf;
       const float h0 = bf16_to_f32(f32_to_bf16(y0)), h1 = bf16_to_f32(f32_to_bf16(y1));
-      uint16_t* o = qout + (static_cast<int64_t>(n) * a.n_h + h) * rec + D_C + 2 * k;
-      *reinterpret_cast<uint32_t*>(o) = bf16_pair(y0, y1);
-      *reinterpret_cast<uint32_t*>(o + ROWE) = bf16_pair(y0 - h0, y1 - h1);
+      const int64_t e = (static_cast<int64_t>(n) * a.n_h + h) * ROWE + D_C + 2 * k;
+      *reinterpret_cast<uint32_t*>(qout + e) = bf16_pair(y0, y1);
+      if (qlo) *reinterpret_cast<uint32_t*>(qlo + e) = bf16_pair(y0 - h0, y1 - h1);
     }
   }
   __syncthreads();
@@ -226,9 +228,9 @@ __global__ __launch_bounds__(256, 2) void absorb_mfma_kernel(AbsorbArgs a) {
           const float h1 = bf16_to_f32(static_cast<uint16_t>(hw[e] >> 16));
           lw[e] = bf16_pair(v[2 * e] - h0, v[2 * e + 1] - h1);
         }
-        uint16_t* o = qout + (static_cast<int64_t>(n) * a.n_h + h) * rec + half_c * ABS_COLS + 8 * k;
-        *reinterpret_cast<uint4*>(o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        *reinterpret_cast<uint4*>(o + ROWE) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        const int64_t o = (static_cast<int64_t>(n) * a.n_h + h) * ROWE + half_c * ABS_COLS + 8 * k;
+        *reinterpret_cast<uint4*>(qout + o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        if (qlo) *reinterpret_cast<uint4*>(qlo + o) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       }
     }
     __syncthreads();  // stage reused by the next block

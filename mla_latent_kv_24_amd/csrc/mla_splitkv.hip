@@ -49,6 +49,267 @@ __device__ __forceinline__ uint64_t row_addr(const SplitArgs& a, int b, int64_t 
 // the combine then turns every output of the query into NaN.
 constexpr float POS_INF = __builtin_huge_valf();
 
+// ------------------------------------------------------------------------
+// n_h = 16 (the V2-Lite shape), and the precise path of every head count.
+// Per cache row the matrix work of 16 heads is an eighth of the 128-head
+// case, so this body is a stream of the cache: what counts is bytes in
+// flight and little LDS traffic.  Each wave owns every fourth 16-row tile of
+// the split (tiles w, w+4, ...) with its own online softmax and its own Z for
+// the group's 16 heads x 512 columns (128 accumulators), and two LDS buffers
+// that its own DMAs fill (one tile scored while the next lands), so the loop
+// has no workgroup barrier.  The four waves' (m, l, Z) merge through LDS at
+// the end.
+//   score: v_mfma_f32_16x16x32_bf16, A = tile rows, B = absorbed queries (hi,
+//          then lo: the two products sum to the fp32 query to ~2^-16);
+//   value: v_mfma_f32_16x16x32_bf16, A = tile columns by transpose reads
+//          (each read twice along K), B = P^T straight from the score
+//          accumulator (lane l holds rows 4(l/16)+i of head l%16 in both),
+//          hi in the first half of K and lo in the second.
+// Neither product rounds an operand that the result depends on beyond the
+// stored values, so this body matches the exact softmax to ~1e-5 of the
+// output rms at any length.  The wider kernels score with the bf16 query
+// alone and pack the weights once to bf16 (a relative 2^-9 on each score and
+// weight); over few rows, and under the long-context temperature, that shows
+// at the 1e-2 level of max|err|/rms, so queries that attend fewer than
+// `precise_below` rows run this body one 16-head group at a time instead.
+// ------------------------------------------------------------------------
+constexpr int T16 = 16;                          // rows per tile
+constexpr int T16_BYTES = T16 * ROWB;            // 18,432 B
+constexpr int T16_LOADS = T16_BYTES / (16 * 64);  // 18 DMA chunks per lane per tile
+constexpr int ZPAD = D_C * 4 + 16;               // merge: bytes per staged head row
+
+// Heads h0..h0+15 of query n over split `split` (sequence b, attended length
+// len): the 16-head kernel's body, also the precise path of the wider kernels
+// (every query row scored with hi + lo, every softmax weight carried as hi +
+// lo).  smem: at least 8 * T16_BYTES of LDS; the caller separates two calls
+// with a barrier.
+template <bool PAGED>
+__device__ __forceinline__ void h16_group(const SplitArgs& a, uint8_t* smem, int n, int split, int h0, int b,
+                                          int64_t len) {
+  static_assert(4 * 16 * ZPAD + 2 * 4 * 16 * 4 <= 8 * T16_BYTES, "merge staging must fit the buffers");
+  static_assert(T16_BYTES == T16_LOADS * 16 * 64, "tile must split evenly over 64 lanes");
+
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: DMA addresses go to SGPRs
+  const int q4 = l >> 4, j16 = l & 15;
+  const int64_t lo = static_cast<int64_t>(split) * a.split_rows;
+  const int64_t hi = min(lo + a.split_rows, len);
+  float* zo = a.z_part + ((static_cast<int64_t>(n) * a.num_splits + split) * a.n_h + h0) * D_C;
+  float* lse_o = a.lse_part + (static_cast<int64_t>(n) * a.num_splits + split) * a.n_h + h0;
+
+  if (lo >= hi) {  // empty split (uniform over the workgroup)
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    for (int idx = tid; idx < 16 * D_C / 4; idx += 256) reinterpret_cast<f32x4*>(zo)[idx] = zero;
+    if (tid < 16) lse_o[tid] = NEG_INF;
+    return;
+  }
+  const int64_t ntiles = (hi - lo + T16 - 1) / T16;
+  const int my_tiles = static_cast<int>((ntiles > w) ? (ntiles - w + 3) / 4 : 0);  // wave-uniform
+
+  // ---- absorbed queries (B operands): head h0 + j16, elements 32 s + 8 q4 .. +7
+  // of the hi plane and of the lo plane (zeros without one)
+  u32x4 qh[NQ16], ql[NQ16];
+  {
+    const int64_t qo = (static_cast<int64_t>(n) * a.n_h + h0 + j16) * ROWE + 8 * q4;
+    const uint16_t* q = static_cast<const uint16_t*>(a.q_lat) + qo;
+#pragma unroll
+    for (int s = 0; s < NQ16; ++s) qh[s] = *reinterpret_cast<const u32x4*>(q + 32 * s);
+    if (a.q_lat_lo) {
+      const uint16_t* ql_src = static_cast<const uint16_t*>(a.q_lat_lo) + qo;
+#pragma unroll
+      for (int s = 0; s < NQ16; ++s) ql[s] = *reinterpret_cast<const u32x4*>(ql_src + 32 * s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NQ16; ++s) ql[s] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // ---- this wave's tile DMAs: its k-th tile (split tile w + 4k) goes to
+  // buffer 2w + (k & 1).  LDS chunk f = 64 i + l of a buffer receives global
+  // chunk (t, p ^ swz(t)) with (t, p) = (f / 72, f % 72).  The buffer resource
+  // spans the tile's rows inside the split, so rows past its end arrive as zeros.
+  const uint8_t* gsplit =
+      static_cast<const uint8_t*>(a.cache) + (static_cast<int64_t>(b) * a.stride + lo) * ROWB;
+  const uint64_t gaddr = reinterpret_cast<uint64_t>(gsplit);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint8_t*)smem));
+  bool bad = false;  // one of this wave's tiles sits in a page outside the pool (wave-uniform)
+  auto issue = [&](int k) {
+    const int64_t it = w + 4 * static_cast<int64_t>(k);
+    uint64_t ga = gaddr + static_cast<uint64_t>(it) * T16_BYTES;
+    int64_t rows = min(static_cast<int64_t>(T16), hi - lo - it * T16);
+    if constexpr (PAGED) {
+      bool ok = true;
+      if (rows > 0) ga = row_addr<true>(a, b, lo + it * T16, ROWB, ok);
+      if (!ok) {
+        rows = 0;
+        bad = true;
+      }
+    }
+    const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(ga & 0xffffffffu)),
+                      __builtin_amdgcn_readfirstlane(static_cast<int>((ga >> 32) & 0xffffu)),
+                      __builtin_amdgcn_readfirstlane(static_cast<int>(rows * ROWB)), 0x00020000};
+    const uint32_t dst = lds0 + static_cast<uint32_t>((2 * w + (k & 1)) * T16_BYTES);
+    // the lane index passes through an empty asm so that the 18 source offsets
+    // are formed here, not hoisted out of the loop into 18 live registers
+    int lx = l;
+    asm volatile("" : "+v"(lx));
+#pragma unroll
+    for (int i = 0; i < T16_LOADS; ++i) {
+      const int f = 64 * i + lx;
+      const int t = f / 72, p = f - 72 * t;
+      dma16(dst + 1024u * i, 16 * (72 * t + (p ^ swz(t))), rs, 0);
+    }
+  };
+  if (my_tiles > 0) issue(0);
+  if (my_tiles > 1) issue(1);
+  // queries and the first two tiles resident: after this the compiler has no
+  // load of its own in flight, so the loop carries no waits but the explicit ones
+  vm_wait<0>();
+
+  // ---- per-lane LDS operand offsets
+  // score A: row j16, elements 32 s + 8 q4 .. +7 -> chunk 4 s + q4
+  int sc_off[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) sc_off[m] = j16 * ROWB + 16 * ((4 * m + q4) ^ swz(j16));
+  // value A (transpose reads): rows 4 q4 + (j16 >> 2), columns 16 cb + 4 (j16 & 3)
+  int tr_off[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) tr_off[p] = tile_off(4 * q4 + (j16 >> 2), 16 * p + 4 * (j16 & 3));
+
+  f32x4 zacc[32];  // Z^T of c-block cb: columns 16 cb + 4 q4 + i of head j16
+#pragma unroll
+  for (int c = 0; c < 32; ++c) zacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = NEG_INF, l_run = 0.f;
+  const float qscale = a.qscale;
+
+  for (int k = 0; k < my_tiles; ++k) {
+    // this tile has landed (the next one's loads may stay in flight)
+    if (k + 1 < my_tiles)
+      vm_wait<T16_LOADS>();
+    else
+      vm_wait<0>();
+    const uint8_t* buf = smem + (2 * w + (k & 1)) * T16_BYTES;
+    const int64_t it = w + 4 * static_cast<int64_t>(k);
+    const int valid = static_cast<int>(min(hi - lo - it * T16, static_cast<int64_t>(T16)));
+
+    // -------------------------------------------------- score S^T = rows . q
+    constexpr int PF = 4;
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    {
+      u32x4 kb[PF];
+#pragma unroll
+      for (int s = 0; s < PF; ++s) kb[s] = *reinterpret_cast<const u32x4*>(buf + sc_off[s & 1] + 128 * (s >> 1));
+#pragma unroll
+      for (int s = 0; s < NQ16; ++s) {
+        const u32x4 kv = kb[s % PF];
+        if (s + PF < NQ16)
+          kb[s % PF] = *reinterpret_cast<const u32x4*>(buf + sc_off[(s + PF) & 1] + 128 * ((s + PF) >> 1));
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
+                                                       __builtin_bit_cast(bf16x8, qh[s]), sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
+                                                       __builtin_bit_cast(bf16x8, ql[s]), sacc, 0, 0, 0);
+      }
+    }
+    // first value operands: independent of P, so their latency overlaps the softmax
+    constexpr int VPF = 4;
+    i16x4 vb[VPF];
+#pragma unroll
+    for (int c = 0; c < VPF; ++c) vb[c] = tr_read(buf + 128 * (c >> 2) + tr_off[c & 3]);
+
+    // -------------------------------------------------- online softmax (log2)
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (4 * q4 + i < valid) ? sacc[i] : NEG_INF;
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = pair_max32(mx);
+    mx = pair_max16(mx);
+    const float mt = mx * qscale;  // scale > 0 commutes with max
+    const bool need = mt > m_run + RESCALE_TAU;
+    if (__ballot(need)) {
+      const float m_new = need ? mt : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) zacc[c] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = -m_run;
+    i16x4 ph, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(x[i], qscale, neg_m));
+      l_run += pv;
+      const uint16_t h16 = f32_to_bf16(pv);
+      ph[i] = static_cast<short>(h16);
+      pl[i] = static_cast<short>(f32_to_bf16(pv - bf16_to_f32(h16)));
+    }
+    // one K = 32 product covers both parts: k < 4 pairs the tile rows with
+    // P hi, k >= 4 pairs the same rows with P lo
+    const bf16x8 pp = cat(ph, pl);
+
+    // -------------------------------------------------- value Z^T += rows^T . P^T
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      const i16x4 va = vb[c % VPF];
+      if (c + VPF < 32) vb[c % VPF] = tr_read(buf + 128 * ((c + VPF) >> 2) + tr_off[(c + VPF) & 3]);
+      zacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat(va, va), pp, zacc[c], 0, 0, 0);
+    }
+
+    // the buffer is free once this wave's reads of it returned: refill it
+    if (k + 2 < my_tiles) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+      issue(k + 2);
+    }
+  }
+
+  // ---- merge the four waves: M = max m_w, L = sum_w 2^(m_w - M) l_w,
+  // z = sum_w 2^(m_w - M) Z_w / L.  A wave without tiles has m = -inf, l = 0.
+  float lt = pair_sum32(l_run);
+  lt = pair_sum16(lt);
+  if (PAGED && bad) lt = __builtin_nanf("");  // carried into L by the merge
+  __syncthreads();  // every wave is done with its buffers
+  float* mst = reinterpret_cast<float*>(smem + 4 * 16 * ZPAD);
+  float* lst = mst + 64;
+  if (q4 == 0) {
+    mst[16 * w + j16] = m_run;
+    lst[16 * w + j16] = lt;
+  }
+  __syncthreads();
+  float M = NEG_INF;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) M = fmaxf(M, mst[16 * v + j16]);
+  float L = 0.f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float mv = mst[16 * v + j16];
+    if (mv != NEG_INF) L += lst[16 * v + j16] * __builtin_amdgcn_exp2f(mv - M);
+  }
+  float f = (m_run != NEG_INF && L > 0.f) ? __builtin_amdgcn_exp2f(m_run - M) / L : 0.f;
+  float lse = (L > 0.f) ? (M + log2f(L)) * LN2 : NEG_INF;
+  if (PAGED && L != L) {
+    f = __builtin_nanf("");
+    lse = POS_INF;
+  }
+  {
+    uint8_t* row = smem + w * 16 * ZPAD + j16 * ZPAD + 16 * q4;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      const f32x4 v = {zacc[c][0] * f, zacc[c][1] * f, zacc[c][2] * f, zacc[c][3] * f};
+      *reinterpret_cast<f32x4*>(row + 64 * c) = v;
+    }
+  }
+  if (w == 0 && q4 == 0) lse_o[j16] = lse;
+  __syncthreads();
+  for (int idx = tid; idx < 16 * (D_C / 4); idx += 256) {
+    const int h = idx >> 7, c4 = idx & 127;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(smem + h * ZPAD + 16 * c4);
+#pragma unroll
+    for (int v = 1; v < 4; ++v) acc += *reinterpret_cast<const f32x4*>(smem + v * 16 * ZPAD + h * ZPAD + 16 * c4);
+    *reinterpret_cast<f32x4*>(zo + h * D_C + 4 * c4) = acc;
+  }
+}
+
 template <int CG, bool PAGED>
 __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
     SplitArgs a) {
@@ -63,6 +324,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
   static_assert(TILE_BYTES == LOADS * 16 * 256, "tile must split evenly over 256 threads");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_BYTES + 9 * 256 * 4];  // tile ring + DMA offset table
+  static_assert(4 * TILE_BYTES + 9 * 256 * 4 >= 8 * T16_BYTES, "the precise path's buffers must fit");
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int hg = w % NHG, cg = w / NHG;
@@ -82,6 +344,13 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
       zo[static_cast<int64_t>(h0 + hh) * D_C + c] = 0.f;
     }
     if (cg == 0 && l < HPW) lse_o[h0 + l] = NEG_INF;
+    return;
+  }
+  if (len < a.precise_below) {  // few rows: 16-head groups with hi + lo products (uniform)
+    for (int g = 0; g < NHG * HPW / 16; ++g) {
+      if (g) __syncthreads();
+      h16_group<PAGED>(a, smem, n, split, 16 * g, b, len);
+    }
     return;
   }
 
@@ -138,12 +407,12 @@ __global__ __launch_bounds__(256, 1) void splitkv_mfma_kernel(
   if (ntiles > 1) issue_direct(1);
   if (ntiles > 2) issue_direct(2);
 
-  // ---- absorbed queries -> B-operand registers: the hi part of the bf16
-  // hi/lo layout (the register file has no room for lo at 32 heads per wave)
+  // ---- absorbed queries -> B-operand registers: the hi plane (the register
+  // file has no room for lo at 32 heads per wave)
   u32x4 qreg[NQ];
   {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q_lat) + static_cast<int64_t>(n) * a.n_h * 2 * ROWE;
-    const uint16_t* qh = q + (h0 + (l & 31)) * 2 * ROWE + 8 * g32;
+    const uint16_t* q = static_cast<const uint16_t*>(a.q_lat) + static_cast<int64_t>(n) * a.n_h * ROWE;
+    const uint16_t* qh = q + (h0 + (l & 31)) * ROWE + 8 * g32;
 #pragma unroll
     for (int s = 0; s < NQ; ++s) qreg[s] = *reinterpret_cast<const u32x4*>(qh + 16 * s);
   }
@@ -374,6 +643,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
   constexpr int I_OFF = A_OFF + 128 * 4;           // 1 / l per head (128 floats)
   constexpr int T_OFF = I_OFF + 128 * 4;           // per-thread DMA source chunk indices, u16 [LOADS][256]
   __shared__ __attribute__((aligned(16))) uint8_t smem[T_OFF + LOADS * 256 * 2];
+  static_assert(T_OFF + LOADS * 256 * 2 >= 8 * T16_BYTES, "the precise path's buffers must fit");
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int g32 = l >> 5, j16 = l & 15, l32 = l & 31;
@@ -390,6 +660,13 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int idx = tid; idx < 128 * D_C / 4; idx += 256) reinterpret_cast<f32x4*>(zo)[idx] = zero;
     if (tid < 128) lse_o[tid] = NEG_INF;
+    return;
+  }
+  if (len < a.precise_below) {  // few rows: 16-head groups with hi + lo products (uniform)
+    for (int g = 0; g < 8; ++g) {
+      if (g) __syncthreads();
+      h16_group<PAGED>(a, smem, n, split, 16 * g, b, len);
+    }
     return;
   }
 
@@ -447,11 +724,11 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
     }
   }
 
-  // ---- this wave's 32 absorbed queries: the hi parts are the B operands
+  // ---- this wave's 32 absorbed queries: the hi plane gives the B operands
   u32x4 qreg[NQ];
   {
     const uint16_t* qh = static_cast<const uint16_t*>(a.q_lat) +
-                         (static_cast<int64_t>(n) * 128 + 32 * w + l32) * 2 * ROWE + 8 * g32;
+                         (static_cast<int64_t>(n) * 128 + 32 * w + l32) * ROWE + 8 * g32;
 #pragma unroll
     for (int s = 0; s < NQ; ++s) qreg[s] = *reinterpret_cast<const u32x4*>(qh + 16 * s);
   }
@@ -698,249 +975,15 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
   }
 }
 
-// ------------------------------------------------------------------------
-// n_h = 16 (the V2-Lite shape).  Per cache row the matrix work is an eighth of
-// the 128-head case, so this kernel is a stream of the cache: what counts is
-// bytes in flight and little LDS traffic.  Each wave owns every fourth 16-row
-// tile of the split (tiles w, w+4, ...) with its own online softmax and its
-// own Z for all 16 heads x 512 columns (128 AGPRs), and two LDS buffers that
-// its own DMAs fill (one tile scored while the next lands), so the loop has
-// no workgroup barrier.  The four waves' (m, l, Z) merge through LDS at the
-// end.
-//   score: v_mfma_f32_16x16x32_bf16, A = tile rows, B = absorbed queries (hi,
-//          then lo: the two products sum to the fp32 query to ~2^-16);
-//   value: v_mfma_f32_16x16x32_bf16, A = tile columns by transpose reads
-//          (each read twice along K), B = P^T straight from the score
-//          accumulator (lane l holds rows 4(l/16)+i of head l%16 in both),
-//          hi in the first half of K and lo in the second.
-// ------------------------------------------------------------------------
-constexpr int T16 = 16;                          // rows per tile
-constexpr int T16_BYTES = T16 * ROWB;            // 18,432 B
-constexpr int T16_LOADS = T16_BYTES / (16 * 64);  // 18 DMA chunks per lane per tile
-constexpr int ZPAD = D_C * 4 + 16;               // merge: bytes per staged head row
-
+// n_h a multiple of 16: one workgroup per (query, split, group of 16 heads).
 template <bool PAGED>
 __global__ __launch_bounds__(256, 1) void splitkv_h16_kernel(SplitArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[8 * T16_BYTES];
-  static_assert(4 * 16 * ZPAD + 2 * 4 * 16 * 4 <= 8 * T16_BYTES, "merge staging must fit the buffers");
-  static_assert(T16_BYTES == T16_LOADS * 16 * 64, "tile must split evenly over 64 lanes");
-
-  const int tid = threadIdx.x, l = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: DMA addresses go to SGPRs
-  const int q4 = l >> 4, j16 = l & 15;
-  const int n = blockIdx.x, split = blockIdx.y;
+  const int n = blockIdx.x;
   int b;
   int64_t len;
   query_range(a, n, b, len);
-  const int64_t lo = static_cast<int64_t>(split) * a.split_rows;
-  const int64_t hi = min(lo + a.split_rows, len);
-  float* zo = a.z_part + (static_cast<int64_t>(n) * a.num_splits + split) * 16 * D_C;
-  float* lse_o = a.lse_part + (static_cast<int64_t>(n) * a.num_splits + split) * 16;
-
-  if (lo >= hi) {  // empty split (uniform over the workgroup)
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    for (int idx = tid; idx < 16 * D_C / 4; idx += 256) reinterpret_cast<f32x4*>(zo)[idx] = zero;
-    if (tid < 16) lse_o[tid] = NEG_INF;
-    return;
-  }
-  const int64_t ntiles = (hi - lo + T16 - 1) / T16;
-  const int my_tiles = static_cast<int>((ntiles > w) ? (ntiles - w + 3) / 4 : 0);  // wave-uniform
-
-  // ---- absorbed queries (B operands): head j16, elements 32 s + 8 q4 .. +7
-  u32x4 qh[NQ16], ql[NQ16];
-  {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q_lat) + (static_cast<int64_t>(n) * 16 + j16) * 2 * ROWE + 8 * q4;
-#pragma unroll
-    for (int s = 0; s < NQ16; ++s) {
-      qh[s] = *reinterpret_cast<const u32x4*>(q + 32 * s);
-      ql[s] = *reinterpret_cast<const u32x4*>(q + ROWE + 32 * s);
-    }
-  }
-
-  // ---- this wave's tile DMAs: its k-th tile (split tile w + 4k) goes to
-  // buffer 2w + (k & 1).  LDS chunk f = 64 i + l of a buffer receives global
-  // chunk (t, p ^ swz(t)) with (t, p) = (f / 72, f % 72).  The buffer resource
-  // spans the tile's rows inside the split, so rows past its end arrive as zeros.
-  const uint8_t* gsplit =
-      static_cast<const uint8_t*>(a.cache) + (static_cast<int64_t>(b) * a.stride + lo) * ROWB;
-  const uint64_t gaddr = reinterpret_cast<uint64_t>(gsplit);
-  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) uint8_t*)smem));
-  bool bad = false;  // one of this wave's tiles sits in a page outside the pool (wave-uniform)
-  auto issue = [&](int k) {
-    const int64_t it = w + 4 * static_cast<int64_t>(k);
-    uint64_t ga = gaddr + static_cast<uint64_t>(it) * T16_BYTES;
-    int64_t rows = min(static_cast<int64_t>(T16), hi - lo - it * T16);
-    if constexpr (PAGED) {
-      bool ok = true;
-      if (rows > 0) ga = row_addr<true>(a, b, lo + it * T16, ROWB, ok);
-      if (!ok) {
-        rows = 0;
-        bad = true;
-      }
-    }
-    const i32x4 rs = {__builtin_amdgcn_readfirstlane(static_cast<int>(ga & 0xffffffffu)),
-                      __builtin_amdgcn_readfirstlane(static_cast<int>((ga >> 32) & 0xffffu)),
-                      __builtin_amdgcn_readfirstlane(static_cast<int>(rows * ROWB)), 0x00020000};
-    const uint32_t dst = lds0 + static_cast<uint32_t>((2 * w + (k & 1)) * T16_BYTES);
-    // the lane index passes through an empty asm so that the 18 source offsets
-    // are formed here, not hoisted out of the loop into 18 live registers
-    int lx = l;
-    asm volatile("" : "+v"(lx));
-#pragma unroll
-    for (int i = 0; i < T16_LOADS; ++i) {
-      const int f = 64 * i + lx;
-      const int t = f / 72, p = f - 72 * t;
-      dma16(dst + 1024u * i, 16 * (72 * t + (p ^ swz(t))), rs, 0);
-    }
-  };
-  if (my_tiles > 0) issue(0);
-  if (my_tiles > 1) issue(1);
-  // queries and the first two tiles resident: after this the compiler has no
-  // load of its own in flight, so the loop carries no waits but the explicit ones
-  vm_wait<0>();
-
-  // ---- per-lane LDS operand offsets
-  // score A: row j16, elements 32 s + 8 q4 .. +7 -> chunk 4 s + q4
-  int sc_off[2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m) sc_off[m] = j16 * ROWB + 16 * ((4 * m + q4) ^ swz(j16));
-  // value A (transpose reads): rows 4 q4 + (j16 >> 2), columns 16 cb + 4 (j16 & 3)
-  int tr_off[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) tr_off[p] = tile_off(4 * q4 + (j16 >> 2), 16 * p + 4 * (j16 & 3));
-
-  f32x4 zacc[32];  // Z^T of c-block cb: columns 16 cb + 4 q4 + i of head j16
-#pragma unroll
-  for (int c = 0; c < 32; ++c) zacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = NEG_INF, l_run = 0.f;
-  const float qscale = a.qscale;
-
-  for (int k = 0; k < my_tiles; ++k) {
-    // this tile has landed (the next one's loads may stay in flight)
-    if (k + 1 < my_tiles)
-      vm_wait<T16_LOADS>();
-    else
-      vm_wait<0>();
-    const uint8_t* buf = smem + (2 * w + (k & 1)) * T16_BYTES;
-    const int64_t it = w + 4 * static_cast<int64_t>(k);
-    const int valid = static_cast<int>(min(hi - lo - it * T16, static_cast<int64_t>(T16)));
-
-    // -------------------------------------------------- score S^T = rows . q
-    constexpr int PF = 4;
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-    {
-      u32x4 kb[PF];
-#pragma unroll
-      for (int s = 0; s < PF; ++s) kb[s] = *reinterpret_cast<const u32x4*>(buf + sc_off[s & 1] + 128 * (s >> 1));
-#pragma unroll
-      for (int s = 0; s < NQ16; ++s) {
-        const u32x4 kv = kb[s % PF];
-        if (s + PF < NQ16)
-          kb[s % PF] = *reinterpret_cast<const u32x4*>(buf + sc_off[(s + PF) & 1] + 128 * ((s + PF) >> 1));
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
-                                                       __builtin_bit_cast(bf16x8, qh[s]), sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
-                                                       __builtin_bit_cast(bf16x8, ql[s]), sacc, 0, 0, 0);
-      }
-    }
-    // first value operands: independent of P, so their latency overlaps the softmax
-    constexpr int VPF = 4;
-    i16x4 vb[VPF];
-#pragma unroll
-    for (int c = 0; c < VPF; ++c) vb[c] = tr_read(buf + 128 * (c >> 2) + tr_off[c & 3]);
-
-    // -------------------------------------------------- online softmax (log2)
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (4 * q4 + i < valid) ? sacc[i] : NEG_INF;
-    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = pair_max32(mx);
-    mx = pair_max16(mx);
-    const float mt = mx * qscale;  // scale > 0 commutes with max
-    const bool need = mt > m_run + RESCALE_TAU;
-    if (__ballot(need)) {
-      const float m_new = need ? mt : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
-      l_run *= alpha;
-#pragma unroll
-      for (int c = 0; c < 32; ++c) zacc[c] *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = -m_run;
-    i16x4 ph, pl;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pv = __builtin_amdgcn_exp2f(fmaf(x[i], qscale, neg_m));
-      l_run += pv;
-      const uint16_t h16 = f32_to_bf16(pv);
-      ph[i] = static_cast<short>(h16);
-      pl[i] = static_cast<short>(f32_to_bf16(pv - bf16_to_f32(h16)));
-    }
-    // one K = 32 product covers both parts: k < 4 pairs the tile rows with
-    // P hi, k >= 4 pairs the same rows with P lo
-    const bf16x8 pp = cat(ph, pl);
-
-    // -------------------------------------------------- value Z^T += rows^T . P^T
-#pragma unroll
-    for (int c = 0; c < 32; ++c) {
-      const i16x4 va = vb[c % VPF];
-      if (c + VPF < 32) vb[c % VPF] = tr_read(buf + 128 * ((c + VPF) >> 2) + tr_off[(c + VPF) & 3]);
-      zacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat(va, va), pp, zacc[c], 0, 0, 0);
-    }
-
-    // the buffer is free once this wave's reads of it returned: refill it
-    if (k + 2 < my_tiles) {
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt at their maxima
-      issue(k + 2);
-    }
-  }
-
-  // ---- merge the four waves: M = max m_w, L = sum_w 2^(m_w - M) l_w,
-  // z = sum_w 2^(m_w - M) Z_w / L.  A wave without tiles has m = -inf, l = 0.
-  float lt = pair_sum32(l_run);
-  lt = pair_sum16(lt);
-  if (PAGED && bad) lt = __builtin_nanf("");  // carried into L by the merge
-  __syncthreads();  // every wave is done with its buffers
-  float* mst = reinterpret_cast<float*>(smem + 4 * 16 * ZPAD);
-  float* lst = mst + 64;
-  if (q4 == 0) {
-    mst[16 * w + j16] = m_run;
-    lst[16 * w + j16] = lt;
-  }
-  __syncthreads();
-  float M = NEG_INF;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) M = fmaxf(M, mst[16 * v + j16]);
-  float L = 0.f;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const float mv = mst[16 * v + j16];
-    if (mv != NEG_INF) L += lst[16 * v + j16] * __builtin_amdgcn_exp2f(mv - M);
-  }
-  float f = (m_run != NEG_INF && L > 0.f) ? __builtin_amdgcn_exp2f(m_run - M) / L : 0.f;
-  float lse = (L > 0.f) ? (M + log2f(L)) * LN2 : NEG_INF;
-  if (PAGED && L != L) {
-    f = __builtin_nanf("");
-    lse = POS_INF;
-  }
-  {
-    uint8_t* row = smem + w * 16 * ZPAD + j16 * ZPAD + 16 * q4;
-#pragma unroll
-    for (int c = 0; c < 32; ++c) {
-      const f32x4 v = {zacc[c][0] * f, zacc[c][1] * f, zacc[c][2] * f, zacc[c][3] * f};
-      *reinterpret_cast<f32x4*>(row + 64 * c) = v;
-    }
-  }
-  if (w == 0 && q4 == 0) lse_o[j16] = lse;
-  __syncthreads();
-  for (int idx = tid; idx < 16 * (D_C / 4); idx += 256) {
-    const int h = idx >> 7, c4 = idx & 127;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(smem + h * ZPAD + 16 * c4);
-#pragma unroll
-    for (int v = 1; v < 4; ++v) acc += *reinterpret_cast<const f32x4*>(smem + v * 16 * ZPAD + h * ZPAD + 16 * c4);
-    *reinterpret_cast<f32x4*>(zo + h * D_C + 4 * c4) = acc;
-  }
+  h16_group<PAGED>(a, smem, n, blockIdx.y, 16 * blockIdx.z, b, len);
 }
 
 // ------------------------------------------------------------------------
@@ -969,7 +1012,7 @@ __global__ __launch_bounds__(256) void splitkv_generic_kernel(SplitArgs a) {
     if (tid == 0) *lse_o = NEG_INF;
     return;
   }
-  for (int e = tid; e < row_e; e += 256) q[e] = load_q<T>(a.q_lat, static_cast<int64_t>(n) * a.n_h + h, row_e, e);
+  for (int e = tid; e < row_e; e += 256) q[e] = load_q<T>(a.q_lat, a.q_lat_lo, static_cast<int64_t>(n) * a.n_h + h, row_e, e);
   __syncthreads();
   // a row of a bad page reads as zeros (as in the MFMA kernels) and poisons the split
   bool bad = false;
@@ -1025,12 +1068,23 @@ bool splitkv_has_fast_path(int n_h, int bf16, int d_c, int d_r) {
   return bf16 && d_c == D_C && d_r == D_R && (n_h == 16 || n_h == 32 || n_h == 64 || n_h == 128);
 }
 
+// Every query takes the precise path when no attended length reaches
+// precise_below; the grouped 16-head kernel then runs it with one workgroup
+// per (query, split, head group).
+bool splitkv_all_precise(int n_h, int32_t max_len, int32_t precise_below) {
+  return n_h % 16 == 0 && max_len < precise_below;
+}
+
 template <bool PAGED>
 static void launch_splitkv_as(const SplitArgs& a, int bf16, hipStream_t st) {
   if (splitkv_has_fast_path(a.n_h, bf16, a.d_c, a.d_r)) {
     dim3 grid(a.n_q, a.num_splits);
+    if (a.n_h == 16 || splitkv_all_precise(a.n_h, a.max_len, a.precise_below)) {
+      grid.z = a.n_h / 16;
+      splitkv_h16_kernel<PAGED><<<grid, 256, 0, st>>>(a);
+      return;
+    }
     switch (a.n_h) {
-      case 16: splitkv_h16_kernel<PAGED><<<grid, 256, 0, st>>>(a); break;
       case 32: splitkv_mfma_kernel<4, PAGED><<<grid, 256, 0, st>>>(a); break;
       case 64: splitkv_mfma_kernel<2, PAGED><<<grid, 256, 0, st>>>(a); break;
       default: splitkv_wide_kernel<PAGED><<<grid, 256, 0, st>>>(a); break;

@@ -35,7 +35,7 @@ class DecodeState:
     """
 
     def __init__(self, inp: DecodeInputs, device="cuda", out_latent=False, page_rows=None,
-                 spare_pages=0, table_seed=0, fp8=False):
+                 spare_pages=0, table_seed=0, fp8=False, q_lo=None):
         w = inp.w
         self.inp = inp
         self.device = device
@@ -85,7 +85,11 @@ class DecodeState:
         self.q_pos = self.new_pos
         self.w_uk = to_device(inp.w_uk, w.dtype, device)
         self.w_uv = to_device(inp.w_uv, w.dtype, device)
-        self.q_lat = api.q_lat_empty(self.d, tdt, self.batch, device=device)
+        # the lo plane of the absorbed queries only where a query reads it (q_lo=None:
+        # some sequence is shorter than mla_precise_rows)
+        if q_lo is None:
+            q_lo = int(lens.min()) < api.precise_rows(self.d, self._api_dtype())
+        self.q_lat = api.q_lat_empty(self.d, tdt, self.batch, device=device, lo=q_lo)
         self.out = torch.empty((self.batch, w.n_h, 128), dtype=torch.float32, device=device)
         self.out_latent = (torch.empty((self.batch, w.n_h, D_C), dtype=torch.float32, device=device)
                            if out_latent else None)
@@ -157,7 +161,7 @@ class DecodeState:
 class PrefillState:
     """One sequence: prefix rows appended first, then the chunk's rows; chunk queries."""
 
-    def __init__(self, inp: PrefillInputs, device="cuda"):
+    def __init__(self, inp: PrefillInputs, device="cuda", q_lo=None):
         w = inp.w
         self.inp = inp
         tdt = torch_dtype(w.dtype)
@@ -177,9 +181,11 @@ class PrefillState:
         self.prefix_lens = torch.tensor([inp.prefix], dtype=torch.int32, device=device)
         self.w_uk = to_device(inp.w_uk, w.dtype, device)
         self.w_uv = to_device(inp.w_uv, w.dtype, device)
-        self.q_lat = api.q_lat_empty(self.d, tdt, 1, inp.chunk, device=device)
-        self.out = torch.empty((1, inp.chunk, w.n_h, 128), dtype=torch.float32, device=device)
         dtc = api.BF16 if w.dtype == "bf16" else api.F32
+        if q_lo is None:   # the first query attends prefix + 1 rows
+            q_lo = inp.prefix + 1 < api.precise_rows(self.d, dtc)
+        self.q_lat = api.q_lat_empty(self.d, tdt, 1, inp.chunk, device=device, lo=q_lo)
+        self.out = torch.empty((1, inp.chunk, w.n_h, 128), dtype=torch.float32, device=device)
         ws = api.prefill_workspace_bytes(self.d, dtc, 1, inp.chunk, inp.prefix)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
         self.workspace_x = None            # expanded rows of the unabsorbed form, on first use

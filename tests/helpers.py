@@ -6,14 +6,6 @@ from mla_latent_kv_24_amd import workloads as W
 
 TOL = {"bf16": 2e-2, "f32": 1e-4}   # max|gpu - ref| / rms(ref), per workload output
 
-# Short contexts (tens to a hundred rows) sit closer to the bf16 noise floor: the
-# three storage roundings of the path (absorbed query, cached RoPE key, softmax
-# weights P; each a relative 2^-9 perturbation) give a max|err|/rms of about
-# 2.5e-2 over 1M outputs at 100-165 rows, against about 1e-2 at 4-8K rows (fp64
-# emulation of exactly those roundings); the bf16 decode kernel's latent output
-# over 5 sequences of 65 rows measures 2.05e-2.  Config-shaped cases keep 2e-2.
-SHORT_CONTEXT_TOL = 4e-2
-
 
 def rel_err(gpu, ref):
     gpu = np.asarray(gpu, dtype=np.float64)
@@ -74,16 +66,15 @@ def oracle_prefill(pinp, queries, heads=None):
 
 def absorbed_layout(q32, dtype):
     """Absorbed query input for the device: fp32 as is, or for bf16 storage the
-    hi/lo pair (hi = bf16(q), lo = bf16(q - hi)) on a new axis -2.  Returns the
-    storage array and the fp64 value it carries (what the oracle is given)."""
+    hi plane (bf16(q)) and the lo plane (bf16(q - hi)).  Returns (hi, lo or
+    None, the fp64 value hi + lo carries: what the oracle is given)."""
     q32 = np.asarray(q32, dtype=np.float32)
     if dtype != "bf16":
-        return q32, q32.astype(np.float64)
+        return q32, None, q32.astype(np.float64)
     hi = W.f32_to_bf16_bits(q32)
     lo = W.f32_to_bf16_bits(q32 - W.bf16_bits_to_f32(hi))
-    pair = np.stack([hi, lo], axis=-2)
     value = W.bf16_bits_to_f32(hi).astype(np.float64) + W.bf16_bits_to_f32(lo).astype(np.float64)
-    return pair, value
+    return hi, lo, value
 
 
 def oracle_decode_fp8(inp, b, heads=None):

@@ -52,7 +52,7 @@ def test_dims_validation():
     assert lib.mla_append_kv(ctypes.byref(odd), 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert lib.mla_append_kv(ctypes.byref(d), 7, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1  # dtype
     zero_heads = api.dims(0)
-    assert lib.mla_absorb_q(ctypes.byref(zero_heads), 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.mla_absorb_q(ctypes.byref(zero_heads), 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1
     nan_base = api.dims(16, rope_base=float("nan"))
     assert lib.mla_append_kv(ctypes.byref(nan_base), 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert b"rope_base" in lib.mla_last_error()
@@ -75,9 +75,9 @@ def test_null_and_size_validation():
     assert lib.mla_append_kv(d, 1, 0, None, None, None, None, None, None) == 0      # n_tok = 0: no-op
     assert lib.mla_append_kv(d, 1, -1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert lib.mla_append_kv(d, 1, 4, None, FAKE, FAKE, FAKE, FAKE, None) == 1
-    assert lib.mla_absorb_q(d, 1, 2, FAKE, None, FAKE, FAKE, FAKE, None) == 1
+    assert lib.mla_absorb_q(d, 1, 2, FAKE, None, FAKE, FAKE, FAKE, None, None) == 1
     # decode partials: batch, lengths, stride, splits
-    args = lambda B, st, L, S: (d, 1, B, FAKE, FAKE, st, FAKE, L, S, FAKE, FAKE, None)
+    args = lambda B, st, L, S: (d, 1, B, FAKE, None, FAKE, st, FAKE, L, S, FAKE, FAKE, None)
     assert lib.mla_decode_partials(*args(0, 100, 10, 1)) == 1
     assert lib.mla_decode_partials(*args(2, 100, 0, 1)) == 1
     assert lib.mla_decode_partials(*args(2, 9, 10, 1)) == 1      # stride < max_seq_len
@@ -93,13 +93,13 @@ def test_workspace_validation():
     need = lib.mla_decode_workspace_bytes(d, 1, 64, 8192)
     S = lib.mla_decode_num_splits(d, 1, 64, 8192)
     assert need >= 64 * S * 128 * 512 * 4
-    st = lib.mla_decode(d, 1, 64, FAKE, FAKE, 8192, FAKE, 8192, FAKE, FAKE, None, FAKE, need - 1, None)
+    st = lib.mla_decode(d, 1, 64, FAKE, None, FAKE, 8192, FAKE, 8192, FAKE, FAKE, None, FAKE, need - 1, None)
     assert st == 3
     assert b"workspace" in lib.mla_last_error()
     pneed = lib.mla_prefill_workspace_bytes(d, 1, 1, 4096, 4096)
     assert pneed >= 4096 * 128 * 512 * 4
-    assert lib.mla_prefill(d, 1, 1, 4096, FAKE, FAKE, 8191, FAKE, 4096, FAKE, FAKE, FAKE, pneed, None) == 1
-    assert lib.mla_prefill(d, 1, 1, 4096, FAKE, FAKE, 8192, FAKE, 4096, FAKE, FAKE, FAKE, pneed - 1, None) == 3
+    assert lib.mla_prefill(d, 1, 1, 4096, FAKE, None, FAKE, 8191, FAKE, 4096, FAKE, FAKE, FAKE, pneed, None) == 1
+    assert lib.mla_prefill(d, 1, 1, 4096, FAKE, None, FAKE, 8192, FAKE, 4096, FAKE, FAKE, FAKE, pneed - 1, None) == 3
 
 
 def test_split_plan_covers_every_row():
@@ -128,7 +128,7 @@ def test_paged_validation():
         return api.PagedCache(pool, table, num_pages, page_rows, max_pages)
 
     def dec(c, max_len=200):
-        return lib.mla_decode_paged(d, 1, 2, FAKE, ctypes.byref(c) if c is not None else None, FAKE, max_len,
+        return lib.mla_decode_paged(d, 1, 2, FAKE, None, ctypes.byref(c) if c is not None else None, FAKE, max_len,
                                     FAKE, FAKE, None, FAKE, 1 << 30, None)
 
     assert dec(None) == 1
@@ -137,14 +137,14 @@ def test_paged_validation():
         assert dec(bad) == 1
     assert dec(pc(page_rows=64, max_pages=3), max_len=193) == 1      # 193 rows need 4 pages of 64
     assert b"max_pages" in lib.mla_last_error()
-    assert lib.mla_decode_partials_paged(d, 1, 2, FAKE, ctypes.byref(pc()), FAKE, 200, 0, FAKE, FAKE, None) == 1
-    assert lib.mla_prefill_paged(d, 1, 1, 100, FAKE, ctypes.byref(pc(page_rows=32, max_pages=4)), FAKE, 29,
+    assert lib.mla_decode_partials_paged(d, 1, 2, FAKE, None, ctypes.byref(pc()), FAKE, 200, 0, FAKE, FAKE, None) == 1
+    assert lib.mla_prefill_paged(d, 1, 1, 100, FAKE, None, ctypes.byref(pc(page_rows=32, max_pages=4)), FAKE, 29,
                                  FAKE, FAKE, FAKE, 1 << 30, None) == 1   # 29 + 100 > 128
     assert lib.mla_prefill_unabsorbed_paged(ctypes.byref(api.dims(12)), 1, 1, 8, FAKE, FAKE, ctypes.byref(pc()),
                                             FAKE, 0, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 2   # n_h % 8
     # a workspace too small is still caught after the descriptor passes
     need = lib.mla_decode_workspace_bytes(d, 1, 2, 200)
-    assert lib.mla_decode_paged(d, 1, 2, FAKE, ctypes.byref(pc()), FAKE, 200, FAKE, FAKE, None, FAKE,
+    assert lib.mla_decode_paged(d, 1, 2, FAKE, None, ctypes.byref(pc()), FAKE, 200, FAKE, FAKE, None, FAKE,
                                 need - 1, None) == 3
 
 
@@ -194,8 +194,8 @@ def test_projection_entry_points_validation():
     assert need >= 64 * (1536 + 128 * 192) * 2
 
     def q(n_q=64, dm=5120, dcq=1536, eps=1e-6, h=FAKE, ws=need):
-        return lib.mla_absorb_q_from_hidden(d, n_q, dm, dcq, h, FAKE, None, eps, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
-                                            None)
+        return lib.mla_absorb_q_from_hidden(d, n_q, dm, dcq, h, FAKE, None, eps, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                            FAKE, ws, None)
 
     assert q(n_q=-1) == 1 and q(dcq=5000) == 1 and q(eps=float("inf")) == 1 and q(h=None) == 1
     assert q(ws=need - 1) == 3
@@ -217,17 +217,50 @@ def test_fp8_entry_points_validation():
         c = ctypes.byref(cache) if cache is not None else None
         assert lib.mla_append_kv_fp8(d, 4, FAKE, FAKE, FAKE, FAKE, c, None) == 1
         assert word in lib.mla_last_error()
-        assert lib.mla_decode_partials_fp8(d, 2, FAKE, c, 100, FAKE, 100, 1, FAKE, FAKE, None) == 1
-        assert lib.mla_prefill_fp8(d, 1, 8, FAKE, c, 100, FAKE, 10, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+        assert lib.mla_decode_partials_fp8(d, 2, FAKE, None, c, 100, FAKE, 100, 1, FAKE, FAKE, None) == 1
+        assert lib.mla_prefill_fp8(d, 1, 8, FAKE, None, c, 100, FAKE, 10, FAKE, FAKE, FAKE, 1 << 30, None) == 1
         assert word in lib.mla_last_error()
     g = ctypes.byref(good)
     assert lib.mla_append_kv_fp8(d, 0, None, None, None, None, None, None) == 0          # no-op
     assert lib.mla_append_kv_fp8(d, -1, FAKE, FAKE, FAKE, FAKE, g, None) == 1
-    assert lib.mla_decode_partials_fp8(d, 2, FAKE, g, 50, FAKE, 100, 1, FAKE, FAKE, None) == 1   # stride < max len
+    assert lib.mla_decode_partials_fp8(d, 2, FAKE, None, g, 50, FAKE, 100, 1, FAKE, FAKE, None) == 1   # stride < max len
     # prefill: prefix + chunk beyond the stride, empty chunk, workspace too small
-    assert lib.mla_prefill_fp8(d, 1, 8, FAKE, g, 100, FAKE, 95, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.mla_prefill_fp8(d, 1, 8, FAKE, None, g, 100, FAKE, 95, FAKE, FAKE, FAKE, 1 << 30, None) == 1
     assert b"cache_seq_stride" in lib.mla_last_error()
-    assert lib.mla_prefill_fp8(d, 1, 0, FAKE, g, 100, FAKE, 10, FAKE, FAKE, FAKE, 1 << 30, None) == 1
-    assert lib.mla_prefill_fp8(d, 1, 8, FAKE, g, 100, FAKE, 10, FAKE, FAKE, FAKE, 16, None) == 3
+    assert lib.mla_prefill_fp8(d, 1, 0, FAKE, None, g, 100, FAKE, 10, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.mla_prefill_fp8(d, 1, 8, FAKE, None, g, 100, FAKE, 10, FAKE, FAKE, FAKE, 16, None) == 3
     f32 = ctypes.byref(api.dims(128, d_hR=32))
-    assert lib.mla_prefill_fp8(f32, 1, 8, FAKE, g, 100, FAKE, 10, FAKE, FAKE, FAKE, 1 << 30, None) == 2
+    assert lib.mla_prefill_fp8(f32, 1, 8, FAKE, None, g, 100, FAKE, 10, FAKE, FAKE, FAKE, 1 << 30, None) == 2
+
+
+def test_lo_plane_rules():
+    """The absorbed queries' lo plane: bf16 only (rejected with MLA_F32 before
+    any launch), and the attended length below which the attention reads it."""
+    lib = api.raw()
+    d = ctypes.byref(api.dims(128))
+    assert lib.mla_absorb_q(d, 0, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert b"q_lat_lo" in lib.mla_last_error()
+    assert lib.mla_decode_partials(d, 0, 2, FAKE, FAKE, FAKE, 100, FAKE, 10, 1, FAKE, FAKE, None) == 1
+    assert lib.mla_decode(d, 0, 2, FAKE, FAKE, FAKE, 100, FAKE, 10, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert lib.mla_prefill(d, 0, 1, 8, FAKE, FAKE, FAKE, 100, FAKE, 10, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    all_rows = 2 ** 31 - 1
+    assert api.precise_rows(api.dims(128), api.BF16) == 4096
+    assert api.precise_rows(api.dims(64), api.BF16) == 4096
+    assert api.precise_rows(api.dims(32), api.BF16) == 4096
+    assert api.precise_rows(api.dims(16), api.BF16) == all_rows
+    assert api.precise_rows(api.dims(8), api.BF16) == all_rows          # generic kernels: always hi + lo
+    assert api.precise_rows(api.dims(128, yarn_factor=40.0), api.BF16) == all_rows
+    assert api.precise_rows(api.dims(128), api.F32) == 0
+    assert api.precise_rows(api.dims(128, d_c=256), api.BF16) == 0      # bad dims
+
+
+def test_split_plan_of_the_precise_path():
+    """When every query takes the 16-head-group path, each (query, split) is
+    n_h / 16 workgroups and the plan counts them."""
+    d = api.dims(128)
+    assert api.num_splits(d, api.BF16, 64, 8192) == 4     # wide kernel: 64 x 4 workgroups
+    assert api.num_splits(d, api.BF16, 64, 2048) == 1     # grouped: 64 x 1 x 8 = 512 workgroups
+    assert api.num_splits(d, api.BF16, 8, 3000) == 4      # grouped: 8 x 4 x 8 = 256
+    y = api.dims(128, yarn_factor=40.0)
+    assert api.num_splits(y, api.BF16, 64, 8192) == 2     # grouped; the 4,096-row cap sets it
+    assert api.num_splits(y, api.BF16, 4, 131072) == 32   # 131,072 rows / 4,096

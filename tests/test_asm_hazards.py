@@ -7,9 +7,10 @@ assembly with the library's own flags and check:
   * no instruction reads a VGPR written by such an MFMA within 18 wait states
     (an XDL result needs ~11-12 on gfx950; 18 leaves margin), except the next
     MFMA of the same accumulate chain;
-  * the kernels that stream tiles by LDS DMA have no scratch reload between
-    their first and last MFMA: a spill reload is a VMEM access, and the
-    loops' explicit vmcnt bookkeeping of their DMAs assumes none.
+  * the kernels that stream tiles by LDS DMA have no scratch reload inside
+    any loop that issues MFMAs (the tile loops of the fast path and of the
+    16-head-group path): a spill reload is a VMEM access whose own wait would
+    also drain the DMAs in flight.
 """
 import os
 import re
@@ -139,12 +140,38 @@ def test_wide_kernel_has_vgpr_score_mfmas(asm, name):
     assert sum(1 for s in body if re.match(r"v_mfma\S*\s+a\[", s)) >= 32
 
 
+def mfma_loops(text):
+    """Bodies (instruction lists) of the loops of a function's assembly that
+    issue MFMAs: from a loop header label to the branch back to it."""
+    lines = text.splitlines()
+    label_at = {}
+    for i, raw in enumerate(lines):
+        m = re.match(r"^(\.LBB\d+_\d+):", raw.strip())
+        if m:
+            label_at[m.group(1)] = i
+    loops = []
+    for i, raw in enumerate(lines):
+        m = re.search(r"\bs_(?:cbranch_\w+|branch)\s+(\.LBB\d+_\d+)", raw)
+        if m and m.group(1) in label_at and label_at[m.group(1)] < i:
+            body = _instructions("\n".join(lines[label_at[m.group(1)]:i + 1]))
+            if any(x.startswith("v_mfma") for x in body):
+                loops.append(body)
+    return loops
+
+
+def test_loop_finder_sees_a_backedge():
+    text = "\n".join(["k:", ".LBB0_1:", "  v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]",
+                      "  scratch_load_dword v1, off, off", "  s_cbranch_scc1 .LBB0_1", "  s_endpgm"])
+    loops = mfma_loops(text)
+    assert len(loops) == 1 and any(x.startswith("scratch_load") for x in loops[0])
+
+
 @pytest.mark.parametrize("name", STREAMING)
-def test_streaming_kernel_loop_has_no_scratch_reloads(asm, name):
-    body = _instructions(_function(asm, name))
-    idx = [i for i, s in enumerate(body) if s.startswith("v_mfma")]
-    inside = body[idx[0]:idx[-1]]
-    assert not [s for s in inside if s.startswith("scratch_load")]
+def test_streaming_kernel_loops_have_no_scratch_reloads(asm, name):
+    loops = mfma_loops(_function(asm, name))
+    assert loops
+    for body in loops:
+        assert not [s for s in body if s.startswith("scratch_load")]
 
 
 PREFILL = ["_ZN3mla19prefill_attn_kernelILb1EEEvNS_11PrefillArgsE",

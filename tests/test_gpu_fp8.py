@@ -8,7 +8,7 @@ import pytest
 
 import oracle as O
 from mla_latent_kv_24_amd import workloads as W
-from helpers import SHORT_CONTEXT_TOL, TOL, f64, oracle_decode, oracle_decode_fp8, rel_err, to_np
+from helpers import TOL, f64, oracle_decode, oracle_decode_fp8, rel_err, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -69,12 +69,14 @@ def test_append_fp8_codes_and_scales_bit_exact(api):
 
 
 # 128 heads and 16 heads (matrix-core kernels) at several lengths, ragged
-# tails and ragged batches; 32 heads (generic kernel)
+# tails and ragged batches (at 128 heads one that mixes queries under and over
+# the precise-path threshold); 32 heads (generic kernel)
 CASES = [("v2_decode", dict(batch=3, seq_len=1000)), ("v2_decode", dict(batch=2, seq_len=4099)),
          ("v2_decode", dict(batch=5, seq_len=65)), ("v2_decode", dict(batch=1, seq_len=1)),
          ("v2_decode", dict(batch=2, seq_len=33)), ("lite_decode", dict(batch=3, seq_len=300)),
          ("lite_decode", dict(batch=2, seq_len=4113)), ("lite_decode", dict(batch=3, seq_len=17)),
-         ("lite_ragged", dict(batch=6, seq_len=3000)), ("lite_decode", dict(batch=2, seq_len=300, n_h=32))]
+         ("lite_ragged", dict(batch=6, seq_len=3000)), ("lite_decode", dict(batch=2, seq_len=300, n_h=32)),
+         ("v2_decode", dict(batch=6, seq_len=9000, ragged=True))]
 
 
 @pytest.mark.parametrize("name,changes", CASES, ids=[f"{c[0]}-{c[1]['batch']}x{c[1]['seq_len']}-h{c[1].get('n_h', '')}" for c in CASES])
@@ -90,9 +92,7 @@ def test_decode_fp8(pipeline, name, changes):
     lat = st.out_latent.cpu().numpy()
     assert np.all(np.isfinite(out))                       # NaN codes past every length are never read
     refs = [oracle_decode_fp8(inp, b) for b in range(w.batch)]
-    # the bf16 path's own bars: the short-context one below 256 rows (the same
-    # roundings; on the 5 x 65 case the bf16 kernel's latent is at 2.05e-2)
-    tol = TOL["bf16"] if w.seq_len >= 256 else SHORT_CONTEXT_TOL
+    tol = TOL["bf16"]
     e_out = rel_err(out, np.stack([r[0] for r in refs]))
     e_lat = rel_err(lat, np.stack([r[1] for r in refs]))
     print(f"fp8 parity: out {e_out:.3e}, latent {e_lat:.3e} (bar {tol})")
@@ -124,12 +124,10 @@ def test_decode_fp8_fused_equals_partials(api, pipeline):
     assert torch.equal(out, st.out)
 
 
-# Query lengths 2001..2065 and 1001..1070: every query ends in a ragged tile and
-# the chunk crosses a tile boundary.  Over 300..340 rows of the 128-head inputs
-# the bf16 path's own prefill sits at 2.75e-2 and the FP8 one at 4.0e-2 (one
-# query; the others 1.0e-2..2.6e-2): short contexts are below the 2e-2 bar's
-# reach for both caches.
-@pytest.mark.parametrize("n_h,prefix,chunk", [(128, 2000, 65), (16, 1000, 70)])
+# Query lengths 2001..2065, 301..340, 4061..4130 (straddling the precise-path
+# threshold of 4,096 rows) and 1001..1070: every query ends in a ragged tile
+# and the chunk crosses a tile boundary.
+@pytest.mark.parametrize("n_h,prefix,chunk", [(128, 2000, 65), (128, 300, 40), (128, 4060, 70), (16, 1000, 70)])
 def test_prefill_fp8(api, n_h, prefix, chunk):
     """Causal prefill over the FP8 cache against the oracle's prefill on its own
     dequantised rows (the RoPE key rounded to bf16 as stored)."""
@@ -144,7 +142,7 @@ def test_prefill_fp8(api, n_h, prefix, chunk):
     q_lat = api.q_lat_empty(d, torch.bfloat16, 1, chunk)
     api.absorb_q(d, dev(pinp.q_c, "bf16"), dev(pinp.q_r, "bf16"),
                  torch.arange(prefix, total, dtype=torch.int32, device="cuda"), dev(pinp.w_uk, "bf16"),
-                 q_lat.view(chunk, n_h, 2, 576))
+                 q_lat.view(chunk, n_h, 576))
     out = torch.empty((1, chunk, n_h, 128), dtype=torch.float32, device="cuda")
     api.prefill_fp8(d, q_lat, cache, total, torch.tensor([prefix], dtype=torch.int32, device="cuda"), prefix,
                     dev(pinp.w_uv, "bf16"), out)

@@ -136,7 +136,7 @@ def test_prefill_paged_equals_contiguous(api, page_rows):
     q_pos = np.concatenate([np.arange(p, p + C) for p in prefixes]).astype(np.int32)
     q_lat = api.q_lat_empty(d, torch.bfloat16, 2, C)
     api.absorb_q(d, q_c.view(2 * C, n_h, 128), q_r.view(2 * C, n_h, 64), torch.from_numpy(q_pos).cuda(),
-                 dev(w_uk, dtype), q_lat.view(2 * C, n_h, 2, 576))
+                 dev(w_uk, dtype), q_lat.view(2 * C, n_h, 576))
     outs = {}
     for form in ("absorbed", "unabsorbed"):
         for layout in ("contiguous", "paged"):
@@ -175,7 +175,7 @@ def test_prefill_paged_bad_page(api):
     q_pos = np.concatenate([np.arange(p, p + C) for p in prefixes]).astype(np.int32)
     q_lat = api.q_lat_empty(d, torch.bfloat16, 2, C)
     api.absorb_q(d, q_c.view(2 * C, n_h, 128), q_r.view(2 * C, n_h, 64), torch.from_numpy(q_pos).cuda(),
-                 dev(w_uk, dtype), q_lat.view(2 * C, n_h, 2, 576))
+                 dev(w_uk, dtype), q_lat.view(2 * C, n_h, 576))
     good = torch.empty((2, C, n_h, 128), dtype=torch.float32, device="cuda")
     api.prefill_paged(d, q_lat, pool, table, plen, max(prefixes), dev(w_uv, dtype), good)
     orig = int(table[0, 2])
