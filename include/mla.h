@@ -250,6 +250,25 @@ mla_status mla_decode(const mla_dims* dims, mla_dtype dtype, int32_t batch,
                       float* out, float* out_latent, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* mla_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, split plan and kernels as mla_decode, bitwise the same
+ * output, with the split partials kept in a library-owned device array of
+ * MLA_NOALLOC_SCRATCH_BYTES per GPU instead of a caller workspace.  The array
+ * is reserved on every GPU the library runs on and held until the process
+ * ends; nothing in it needs clearing (every split writes its own partials).
+ * Calls that overlap on one GPU (concurrent streams, threads) share the array
+ * and race: serialise them.  A batch whose partials
+ * (mla_decode_workspace_bytes) exceed the array returns
+ * MLA_ERR_WORKSPACE_TOO_SMALL before any launch; other errors as mla_decode.
+ * Makes no hipMalloc / hipFree call. */
+#define MLA_NOALLOC_SCRATCH_BYTES (128u << 20)
+mla_status mla_decode_noalloc(const mla_dims* dims, mla_dtype dtype, int32_t batch,
+                              const void* q_lat, const void* q_lat_lo, const void* cache,
+                              int64_t cache_seq_stride, const int32_t* seq_lens,
+                              int32_t max_seq_len, const void* w_uv, float* out,
+                              float* out_latent, void* stream);
+
 /* A6 -- causal prefill of a chunk of `chunk` new tokens per sequence.  Their
  * rows must already be in the cache (mla_append_kv).  Query i of sequence b
  * sits at position prefix_lens[b] + i and attends to rows 0..prefix_lens[b]+i

@@ -89,6 +89,8 @@ _SIGS = {
     "mla_decode_workspace_bytes": (_sz, [_P, ctypes.c_int, _i32, _i32]),
     "mla_decode": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp,
                                   _vp, _sz, _vp]),
+    "mla_decode_noalloc": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp,
+                                          _vp]),
     "mla_prefill_workspace_bytes": (_sz, [_P, ctypes.c_int, _i32, _i32, _i32]),
     "mla_prefill_unabsorbed_workspace_bytes": (_sz, [_P, ctypes.c_int, _i32, _i32, _i32]),
     "mla_prefill_unabsorbed": (ctypes.c_int, [_P, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i32,
@@ -286,6 +288,19 @@ def decode(d: Dims, q_lat, cache, stride: int, seq_lens, max_seq_len: int, w_uv,
     _check(_lib.mla_decode(ctypes.byref(d), dt, q_lat.shape[0], *_q(q_lat), _ptr(cache), stride,
                            _ptr(seq_lens), max_seq_len, _ptr(w_uv), _ptr(out), _ptr(out_latent),
                            _ptr(workspace), workspace.numel(), _stream(cache.device)), "mla_decode")
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def decode_noalloc(d: Dims, q_lat, cache, stride: int, seq_lens, max_seq_len: int, w_uv, out,
+                   out_latent=None) -> None:
+    """decode() with the split partials in the library's own device array (no
+    workspace, no allocation; calls on one GPU must not overlap)."""
+    assert seq_lens.dtype == torch.int32 and q_lat.dtype == cache.dtype
+    _check(_lib.mla_decode_noalloc(ctypes.byref(d), _dtype(cache), q_lat.shape[0], *_q(q_lat), _ptr(cache), stride,
+                                   _ptr(seq_lens), max_seq_len, _ptr(w_uv), _ptr(out), _ptr(out_latent),
+                                   _stream(cache.device)), "mla_decode_noalloc")
 
 
 def prefill_workspace_bytes(d: Dims, dtype: int, batch: int, chunk: int, max_prefix_len: int) -> int:

@@ -1,10 +1,12 @@
 // Host side of the C ABI declared in include/mla.h: argument validation (always
 // before any launch), the split-KV plan, workspace layout and launches.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/mla.h"
@@ -902,3 +904,62 @@ mla_status mla_prefill_fp8(const mla_dims* dims, int32_t batch, int32_t chunk, c
   return hip_status(mla::launch_combine(a, 1, s), "mla_prefill_fp8 (combine)");
 }
 }  // extern "C"
+
+// ---- allocation-free decode: the split partials live in this file-scope
+// device array (one copy per GPU, held until the process ends).  Host code
+// never uses the array's name as an address: the per-device pointer comes
+// from hipGetSymbolAddress, taken once per device on its first call.
+static __device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+mla_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "mla_decode_noalloc (hipGetDevice)");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e, "mla_decode_noalloc (hipGetSymbolAddress)");
+      if (!p) return fail(MLA_ERR_HIP, "mla_decode_noalloc: no device address for the scratch array");
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MLA_OK;
+}
+}  // namespace
+
+extern "C" mla_status mla_decode_noalloc(const mla_dims* dims, mla_dtype dtype, int32_t batch, const void* q_lat,
+                                         const void* q_lat_lo, const void* cache, int64_t cache_seq_stride,
+                                         const int32_t* seq_lens, int32_t max_seq_len, const void* w_uv,
+                                         float* out, float* out_latent, void* stream) {
+  mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  st = check_lo(dtype, q_lat_lo);
+  if (st != MLA_OK) return st;
+  if (batch < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch=%d < 1", batch);
+  if (max_seq_len < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "max_seq_len=%d < 1", max_seq_len);
+  if (cache_seq_stride < max_seq_len)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "cache_seq_stride=%lld < max_seq_len=%d", (long long)cache_seq_stride, max_seq_len);
+  if (!q_lat || !cache || !seq_lens || !w_uv || !out) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  // every argument is checked before the device is touched
+  const size_t need = partial_bytes(dims, batch, plan_splits(dims, dtype, batch, max_seq_len));
+  if (need > MLA_NOALLOC_SCRATCH_BYTES)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
+                "mla_decode_noalloc: the split partials of batch %d, max_seq_len %d take %zu B, beyond the "
+                "library's %zu-B scratch array (use mla_decode with a workspace)",
+                batch, max_seq_len, need, static_cast<size_t>(MLA_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != MLA_OK) return st;
+  return decode_impl(dims, dtype, batch, q_lat, q_lat_lo, cache, cache_seq_stride, nullptr, seq_lens, max_seq_len,
+                     w_uv, out, out_latent, ws, MLA_NOALLOC_SCRATCH_BYTES, stream);
+}

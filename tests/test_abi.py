@@ -264,3 +264,20 @@ def test_split_plan_of_the_precise_path():
     y = api.dims(128, yarn_factor=40.0)
     assert api.num_splits(y, api.BF16, 64, 8192) == 2     # grouped; the 4,096-row cap sets it
     assert api.num_splits(y, api.BF16, 4, 131072) == 32   # 131,072 rows / 4,096
+
+
+def test_noalloc_decode_validates_before_touching_the_device():
+    """mla_decode_noalloc checks every argument, and that the plan's partials
+    fit the library's scratch array, before any device call (none here)."""
+    lib = api.raw()
+    d = ctypes.byref(api.dims(128))
+    cap = 128 << 20
+    assert lib.mla_decode_workspace_bytes(d, 1, 64, 8192) <= cap          # the V2 decode step fits
+    assert lib.mla_decode_workspace_bytes(d, 1, 1024, 8192) > cap
+    call = lambda B, L, q=FAKE, lo=None, dt=1, stride=8192: lib.mla_decode_noalloc(
+        d, dt, B, q, lo, FAKE, stride, FAKE, L, FAKE, FAKE, None, None)
+    assert call(1024, 8192) == 3 and b"scratch" in lib.mla_last_error()
+    assert call(4, 8192, q=None) == 1
+    assert call(0, 8192) == 1 and call(4, 0) == 1
+    assert call(4, 8192, stride=100) == 1
+    assert call(4, 8192, lo=FAKE, dt=0) == 1 and b"q_lat_lo" in lib.mla_last_error()
