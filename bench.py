@@ -76,9 +76,10 @@ def cpu_baseline(inp, budget_s=12.0):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "host_cpus": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"{n_seq} of {inp.w.batch} sequences ({rows} cache rows, all {inp.w.n_h} heads), "
-                      f"unabsorbed fp64 numpy, {dt:.1f} s"}
+                      f"unabsorbed fp64 numpy on {threads} BLAS threads, {dt:.1f} s"}
 
 
 def bench_prefill(args):
@@ -274,21 +275,29 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copy probe: 1 GiB device-to-device copy done")
 
-    # The step: append, absorb, the attention kernel between the two HIP
-    # events that time it inside the timed region, then the combine; each a
-    # plain launch on torch's current stream.  (Events cannot be recorded
-    # inside a captured HIP graph here, and replaying the other stages as
-    # graphs around the eager attention launch measured ~7 us slower per
-    # graph than plain launches: the host enqueues far ahead of the GPU.)
-    def run_step(e0=None, e1=None):
-        st.append_new()
-        st.absorb()
-        if e0 is not None:
-            e0.record()
-        st.attention()
-        if e1 is not None:
-            e1.record()
-        st.combine()
+    # The step: append (A1), absorb (A2), the attention kernel (A3), then the
+    # combine (A4 + A5); each a plain launch on torch's current stream.  Events
+    # (HIP, recorded on that stream) may bracket any stage: `ev` maps a stage
+    # to its (start, end) pair.  Events cannot be recorded inside a captured
+    # HIP graph here, and replaying the other stages as graphs around an eager
+    # attention launch measured ~7 us slower per graph than plain launches.
+    STAGES = (("append_kv", st.append_new), ("absorb_q", st.absorb),
+              ("splitkv_attention", st.attention), ("combine_project", st.combine))
+
+    def run_step(ev=None):
+        for nm, fn in STAGES:
+            pair = ev.get(nm) if ev else None
+            if pair:
+                pair[0].record()
+            fn()
+            if pair:
+                pair[1].record()
+
+    def new_events(names):
+        return {nm: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for nm in names}
+
+    def mean_us(evs, nm):
+        return float(np.mean([e[nm][0].elapsed_time(e[nm][1]) for e in evs])) * 1e3
 
     # Settle: at its 1400 W limit the board's clock needs about a second of
     # this load to reach its sustained value; the first ~10 ms run at a
@@ -306,56 +315,60 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # The timed region: K steps back to back, the attention kernel between two events.
+    ev = [new_events(["splitkv_attention"]) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        run_step(*ev[i])
+        run_step(ev[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    attn_times = [a.elapsed_time(b) for a, b in ev]
+    attn_times = [e["splitkv_attention"][0].elapsed_time(e["splitkv_attention"][1]) for e in ev]
     attn_ms = float(np.mean(attn_times))
+    log(f"[bench] timed region: {elapsed / args.steps * 1e3:.4f} ms per step")
 
-    # Per-stage breakdown (informational, after the timed region): each stage
-    # captured as REPS back-to-back launches, bracketed by HIP events.
+    # After the timed region:
+    # * B steps with the 256 MB Infinity Cache flushed before each one by
+    #   reading 512 MB outside the events (clean lines, as when the other
+    #   layers' caches stream in between; a write flush would leave dirty
+    #   lines for the step to write back): the roofline's timing;
+    # * each stage alone, as graphs of 10 back-to-back launches of that stage
+    #   (informational: the attention kernel alone, back to back, holds the
+    #   board at its power limit without the lighter stages between, and runs
+    #   slower than inside the step; the stages' times inside the step come
+    #   from a kernel trace, since events around every stage add a few us to
+    #   each);
+    # * a 1 GiB device-to-device copy, the board's plain streaming rate.
+    B = min(args.steps, 100)
+    flush_buf = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")   # 512 MB
+    flush_sum = torch.zeros((), dtype=torch.float32, device="cuda")
+    fev = [new_events(["splitkv_attention", "step"]) for _ in range(B)]
+    for i in range(B):
+        torch.sum(flush_buf, dim=0, out=flush_sum)
+        fev[i]["step"][0].record()
+        run_step(fev[i])
+        fev[i]["step"][1].record()
+    torch.cuda.synchronize()
+    flushed = {nm: round(mean_us(fev, nm), 2) for nm in ("splitkv_attention", "step")}
+    flushed_attn_times = [e["splitkv_attention"][0].elapsed_time(e["splitkv_attention"][1]) for e in fev]
+    flushed_attn_us = float(np.mean(flushed_attn_times)) * 1e3
+    del flush_buf
+
     REPS = 10
-    stages = (("append_kv", st.append_new), ("absorb_q", st.absorb),
-              ("splitkv_attention", st.attention), ("combine_project", st.combine))
-    parts = {}
-    for nm, fn in stages:
+    alone = {}
+    for nm, fn in STAGES:
         g = st.capture(fn, repeat=REPS)
         g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        rounds = max(1, args.steps // REPS)
+        rounds = max(1, min(args.steps, 100) // REPS)
         e0.record()
         for _ in range(rounds):
             g.replay()
         e1.record()
         torch.cuda.synchronize()
-        parts[nm] = round(e0.elapsed_time(e1) / (rounds * REPS) * 1e3, 2)   # microseconds
+        alone[nm] = round(e0.elapsed_time(e1) / (rounds * REPS) * 1e3, 2)
 
-    # Informational, after the timed region:
-    # * the same step with the 256 MB Infinity Cache flushed before each one
-    #   by reading 512 MB outside the events (clean lines, as when the other
-    #   layers' caches stream in between; a write flush would leave dirty lines
-    #   for the step to write back): the attention kernel and the whole step;
-    # * a 1 GiB device-to-device copy, the board's plain streaming rate.
-    F = min(args.steps, 50)
-    flush_buf = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")   # 512 MB
-    flush_sum = torch.zeros((), dtype=torch.float32, device="cuda")
-    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(F)]
-    for i in range(F):
-        torch.sum(flush_buf, dim=0, out=flush_sum)
-        s0, a0, a1, s1 = fev[i]
-        s0.record()
-        run_step(a0, a1)
-        s1.record()
-    torch.cuda.synchronize()
-    flushed_attn_us = float(np.mean([a0.elapsed_time(a1) for _, a0, a1, _ in fev])) * 1e3
-    flushed_step_us = float(np.mean([s0.elapsed_time(s1) for s0, _, _, s1 in fev])) * 1e3
-    del flush_buf
     src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -374,8 +387,11 @@ def main():
     row_bytes = FP8_ROW_BYTES if args.fp8_cache else ROW_BYTES
     alg_bytes = tokens * row_bytes + w.batch * n_h * 576 * 2           # cache stream + absorbed queries
     alg_flop = tokens * 2176 * n_h                                     # (2*576 + 2*512) per row per head
-    achieved_gbs = alg_bytes / (attn_ms * 1e-3) / 1e9
-    tflops = alg_flop / (attn_ms * 1e-3) / 1e12
+    # the roofline uses the attention kernel with the Infinity Cache flushed
+    # before each step; the back-to-back time of the timed region is reported beside it
+    kern_s = flushed_attn_us * 1e-6
+    achieved_gbs = alg_bytes / kern_s / 1e9
+    tflops = alg_flop / kern_s / 1e12
     # the committed counter summary covers the contiguous kernel instance only
     traffic = None if (args.page_rows or args.fp8_cache) else pmc_traffic(tokens)
     line = {
@@ -400,14 +416,18 @@ def main():
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "kernel": "splitkv_fp8_wide_kernel" if args.fp8_cache else "splitkv_wide_kernel",
-                     "kernel_us": round(attn_ms * 1e3, 2),
-                     "kernel_us_median": round(float(np.median(attn_times)) * 1e3, 2),
+                     "alg_bytes_per_launch": alg_bytes,
+                     "timing": f"mean of {B} launches, each after a 512 MB read that evicts the Infinity Cache",
+                     "kernel_us": round(flushed_attn_us, 2),
+                     "kernel_us_median": round(float(np.median(flushed_attn_times)) * 1e3, 2),
+                     "kernel_us_back_to_back": round(attn_ms * 1e3, 2),
+                     "kernel_us_back_to_back_median": round(float(np.median(attn_times)) * 1e3, 2),
+                     "frac_back_to_back": round(alg_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "mfma_tflops": round(tflops, 1),
                      "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
-        "step_breakdown_us": parts,
+        "stage_alone_back_to_back_us": alone,
         "generated_tokens_per_s": round(w.batch / (ms_per_step * 1e-3), 1),   # one per sequence per step
-        "cache_flushed": {"kernel_us": round(flushed_attn_us, 2), "step_us": round(flushed_step_us, 2),
-                          "achieved_gbs": round(alg_bytes / (flushed_attn_us * 1e-6) / 1e9, 1), "steps": F},
+        "cache_flushed": {"stages_us": flushed, "achieved_gbs": round(achieved_gbs, 1), "steps": B},
         "copy_gbs": round(copy_gbs, 1),
     }
     if not args.no_cpu_baseline:
