@@ -25,7 +25,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 ROW_BYTES = 1152               # one bf16 cache row [c_kv 512 ; k_R 64]
 FP8_ROW_BYTES = 644            # one FP8 cache row: 512 E4M3 codes + 64 bf16 k_R + fp32 scale
-PMC_FILE = os.path.join(ROOT, "profiles", "pmc_splitkv_v2_decode.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_splitkv_traffic.json")
 # the attention kernel's sources: the counters are valid only for exactly these
 KERNEL_SRCS = [os.path.join(ROOT, "mla_latent_kv_24_amd", "csrc", f)
                for f in ("mla_splitkv.hip", "mla_tile.h", "mla_common.h")]
@@ -42,13 +42,14 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def pmc_traffic(per_launch_units):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was
-    taken on the current kernel source (else None)."""
+def pmc_traffic(workload):
+    """HBM bytes per launch of the attention kernel on `workload` from the
+    committed rocprofv3 --pmc summary, if it was taken on the current kernel
+    source (else None)."""
     if not os.path.exists(PMC_FILE):
         return None
-    d = json.load(open(PMC_FILE))
-    if d.get("kernel_sha") != kernel_hash():
+    d = json.load(open(PMC_FILE)).get(workload)
+    if not d or d.get("kernel_sha") != kernel_hash():
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -392,8 +393,11 @@ def main():
     kern_s = flushed_attn_us * 1e-6
     achieved_gbs = alg_bytes / kern_s / 1e9
     tflops = alg_flop / kern_s / 1e12
+    # the kernel that runs the attention: 32 heads per wave at n_h = 128, one
+    # 16-head group per workgroup at n_h = 16
+    attn_kernel = "splitkv_{}{}_kernel".format("fp8_" if args.fp8_cache else "", "wide" if n_h == 128 else "h16")
     # the committed counter summary covers the contiguous kernel instance only
-    traffic = None if (args.page_rows or args.fp8_cache) else pmc_traffic(tokens)
+    traffic = None if (args.page_rows or args.fp8_cache) else pmc_traffic(args.workload)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -415,7 +419,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "splitkv_fp8_wide_kernel" if args.fp8_cache else "splitkv_wide_kernel",
+                     "kernel": attn_kernel,
                      "alg_bytes_per_launch": alg_bytes,
                      "timing": f"mean of {B} launches, each after a 512 MB read that evicts the Infinity Cache",
                      "kernel_us": round(flushed_attn_us, 2),
