@@ -433,11 +433,13 @@ __device__ __forceinline__ void h8_group(const SplitArgs& a, uint8_t* smem, int 
 // n_h a multiple of 16: one workgroup per (query, split, group of 16 heads).
 __global__ __launch_bounds__(256, 1) void splitkv_fp8_h16_kernel(SplitArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[H8_SMEM];
-  const int n = blockIdx.x;
+  int n = blockIdx.x, split = blockIdx.y, g = blockIdx.z;
+  if (!a.prefill && gridDim.x * gridDim.y * gridDim.z > LPT_MIN_GRID)
+    longest_first_unit(a, reinterpret_cast<int*>(smem), n, split, g);
   int b;
   int64_t len;
   query_range(a, n, b, len);
-  h8_group(a, smem, n, blockIdx.y, 16 * blockIdx.z, b, len);
+  h8_group(a, smem, n, split, 16 * g, b, len);
 }
 
 // ------------------------------------------------------------------------

@@ -975,15 +975,19 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
   }
 }
 
-// n_h a multiple of 16: one workgroup per (query, split, group of 16 heads).
+// n_h a multiple of 16: one workgroup per (query, split, group of 16 heads),
+// one workgroup per compute unit.  A decode launch of more workgroups than
+// compute units takes its units longest first.
 template <bool PAGED>
 __global__ __launch_bounds__(256, 1) void splitkv_h16_kernel(SplitArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[8 * T16_BYTES];
-  const int n = blockIdx.x;
+  int n = blockIdx.x, split = blockIdx.y, g = blockIdx.z;
+  if (!a.prefill && gridDim.x * gridDim.y * gridDim.z > LPT_MIN_GRID)
+    longest_first_unit(a, reinterpret_cast<int*>(smem), n, split, g);
   int b;
   int64_t len;
   query_range(a, n, b, len);
-  h16_group<PAGED>(a, smem, n, blockIdx.y, 16 * blockIdx.z, b, len);
+  h16_group<PAGED>(a, smem, n, split, 16 * g, b, len);
 }
 
 // ------------------------------------------------------------------------

@@ -109,6 +109,158 @@ __device__ __forceinline__ void query_range(const SplitArgs& a, int n, int& b, i
   len = max(L, static_cast<int64_t>(0));
 }
 
+// Grids of more workgroups than this (one per compute unit of the MI355X's
+// 256) take their decode units longest first.
+constexpr unsigned LPT_MIN_GRID = 256;
+
+// Exclusive prefix sum of v over a workgroup of 256 threads, in thread order;
+// `total` gets the sum over the workgroup.  red: 4 ints of LDS.  Every thread
+// of the workgroup must call it (it holds two barriers).
+__device__ __forceinline__ int block_excl_scan256(int v, int* red, int& total) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (l >= o) x += y;
+  }
+  __syncthreads();  // red is free
+  if (l == 63) red[w] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = red[i];
+    if (i < w) before += t;
+    total += t;
+  }
+  return before + x - v;
+}
+
+// Longest-first order of the units of a decode launch.  Unit (query n, split s)
+// covers min(max(len_n - s R, 0), R) rows, R = split_rows.  With more
+// workgroups than the compute units hold at once, the hardware hands them out
+// in order of their linear index as compute units free up, so with ragged
+// lengths a long unit handed out late sets the end of the launch.  Workgroup
+// k = x + X (y + Y z) of a grid (X, Y, G) takes the unit of rank k / G and head
+// group k % G, the ranks running over
+//   the full units (R rows), by query and then split;
+//   the partial units (1 .. R-1 rows), longest first in 32 length classes
+//     (class c holds the lengths with floor(32 rows / R) = 31 - c), by query
+//     within a class;
+//   the empty units, by query and then split.
+// Each workgroup works the order out from the lengths (three scans), so the
+// mapping adds no launch and no buffer; it is a permutation of the units.
+// blockDim.x = 256; scratch: 48 ints of LDS, free again when it returns.
+__device__ __forceinline__ void longest_first_unit(const SplitArgs& a, int* scratch, int& n_out, int& split_out,
+                                                   int& g_out) {
+  int* hist = scratch;       // [32] partial units per length class
+  int* red = scratch + 32;   // [4] scan
+  int* res = scratch + 40;   // [2] the unit found
+  const int tid = threadIdx.x;
+  const int G = gridDim.z;
+  const int k = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int r = k / G;
+  g_out = k - r * G;
+  const int S = a.num_splits;
+  const int64_t R = a.split_rows;
+  const int c = (a.n_q + 255) / 256;  // queries per thread, contiguous
+  const int n0 = min(tid * c, a.n_q), n1 = min(n0 + c, a.n_q);
+  // full, partial and empty units of query n; the partial unit's length class
+  auto counts = [&](int n, int& f, int& p, int& cls) {
+    int b;
+    int64_t L;
+    query_range(a, n, b, L);
+    f = static_cast<int>(min(L / R, static_cast<int64_t>(S)));
+    const int64_t rem = L - f * R;  // < R when f < S
+    p = (rem > 0 && f < S) ? 1 : 0;
+    cls = p ? 31 - static_cast<int>(rem * 32 / R) : 0;
+  };
+  if (tid < 32) hist[tid] = 0;
+  __syncthreads();
+  int sF = 0, sE = 0;
+  for (int n = n0; n < n1; ++n) {
+    int f, p, cls;
+    counts(n, f, p, cls);
+    sF += f;
+    sE += S - f - p;
+    if (p) atomicAdd(&hist[cls], 1);
+  }
+  int F;
+  const int exF = block_excl_scan256(sF, red, F);  // its barriers also publish hist
+  if (r < F) {
+    if (exF <= r && r < exF + sF) {
+      int acc = exF;
+      for (int n = n0; n < n1; ++n) {
+        int f, p, cls;
+        counts(n, f, p, cls);
+        if (r < acc + f) {
+          res[0] = n;
+          res[1] = r - acc;
+          break;
+        }
+        acc += f;
+      }
+    }
+  } else {
+    int P = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) P += hist[i];
+    if (r < F + P) {
+      const int j = r - F;
+      int cb = 0, cum = 0;  // the class holding rank j, and the ranks before it
+      while (j >= cum + hist[cb]) cum += hist[cb++];
+      const int i = j - cum;
+      int cnt = 0;
+      for (int n = n0; n < n1; ++n) {
+        int f, p, cls;
+        counts(n, f, p, cls);
+        cnt += (p && cls == cb) ? 1 : 0;
+      }
+      int tot;
+      const int ex = block_excl_scan256(cnt, red, tot);
+      if (ex <= i && i < ex + cnt) {
+        int acc = ex;
+        for (int n = n0; n < n1; ++n) {
+          int f, p, cls;
+          counts(n, f, p, cls);
+          if (p && cls == cb) {
+            if (acc == i) {
+              res[0] = n;
+              res[1] = f;
+              break;
+            }
+            ++acc;
+          }
+        }
+      }
+    } else {
+      const int j = r - F - P;
+      int E;
+      const int ex = block_excl_scan256(sE, red, E);
+      if (ex <= j && j < ex + sE) {
+        int acc = ex;
+        for (int n = n0; n < n1; ++n) {
+          int f, p, cls;
+          counts(n, f, p, cls);
+          const int e = S - f - p;
+          if (j < acc + e) {
+            res[0] = n;
+            res[1] = f + p + (j - acc);
+            break;
+          }
+          acc += e;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  n_out = res[0];
+  split_out = res[1];
+  __syncthreads();  // scratch is free again
+}
+
 // Sum (or max) of v over the workgroup (blockDim.x a multiple of 64, up to 256).
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
   for (int o = 32; o > 0; o >>= 1) {

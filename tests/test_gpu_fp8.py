@@ -70,13 +70,15 @@ def test_append_fp8_codes_and_scales_bit_exact(api):
 
 # 128 heads and 16 heads (matrix-core kernels) at several lengths, ragged
 # tails and ragged batches (at 128 heads one that mixes queries under and over
-# the precise-path threshold); 32 heads (generic kernel)
+# the precise-path threshold; at 16 heads one of more workgroups than compute
+# units, which take their units longest first); 32 heads (generic kernel)
 CASES = [("v2_decode", dict(batch=3, seq_len=1000)), ("v2_decode", dict(batch=2, seq_len=4099)),
          ("v2_decode", dict(batch=5, seq_len=65)), ("v2_decode", dict(batch=1, seq_len=1)),
          ("v2_decode", dict(batch=2, seq_len=33)), ("lite_decode", dict(batch=3, seq_len=300)),
          ("lite_decode", dict(batch=2, seq_len=4113)), ("lite_decode", dict(batch=3, seq_len=17)),
          ("lite_ragged", dict(batch=6, seq_len=3000)), ("lite_decode", dict(batch=2, seq_len=300, n_h=32)),
-         ("v2_decode", dict(batch=6, seq_len=9000, ragged=True))]
+         ("v2_decode", dict(batch=6, seq_len=9000, ragged=True)),
+         ("lite_ragged", dict(batch=100, seq_len=5000))]   # 300 workgroups: units longest first
 
 
 @pytest.mark.parametrize("name,changes", CASES, ids=[f"{c[0]}-{c[1]['batch']}x{c[1]['seq_len']}-h{c[1].get('n_h', '')}" for c in CASES])

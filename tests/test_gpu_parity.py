@@ -110,8 +110,9 @@ def _partials_case(api, dtype, n_h, lens, splits, stride=None, seed=20, tol=None
     for b, L in enumerate(lens):
         cache_np[b, L:] = nan                       # poison past each length
     cache = dev(cache_np.reshape(B * stride, 576), dtype)
-    z = torch.empty((B, splits, n_h, 512), dtype=torch.float32, device="cuda")
-    lse = torch.empty((B, splits, n_h), dtype=torch.float32, device="cuda")
+    # NaN everywhere first: a unit that no workgroup computed shows up
+    z = torch.full((B, splits, n_h, 512), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, splits, n_h), float("nan"), dtype=torch.float32, device="cuda")
     seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
     api.decode_partials(api.dims(n_h), q_in, cache, stride, seq, max_len, splits, z, lse)
     torch.cuda.synchronize()
@@ -151,6 +152,20 @@ def test_splitkv_partials_wide_and_mixed(api, n_h, lens, splits):
     assert api.precise_rows(api.dims(n_h), api.BF16) == 4096
     _partials_case(api, "bf16", n_h, lens, splits, seed=60 + n_h,
                    tol=lambda L: 1e-4 if L < 4096 else TOL["bf16"])
+
+
+@pytest.mark.parametrize("n_h", [16, 128])
+def test_longest_first_order_covers_every_unit(api, n_h):
+    """A decode launch of more workgroups than compute units (40 queries x 8
+    splits, x 8 head groups at 128 heads) takes its (query, split) units
+    longest first: full splits, partial ones by length class, empty ones.
+    Lengths hit every kind: 0, 1, exact multiples of the 256-row split, one
+    row past one, the maximum, and random ones.  Every unit is computed exactly
+    once: all partials (NaN-filled before) match the oracle."""
+    rng = np.random.default_rng(70 + n_h)
+    lens = [0, 1, 256, 257, 512, 2000, 1999, 255, 768, 1024] + rng.integers(1, 2001, 30).tolist()
+    assert api.split_rows(2000, 8) == 256
+    _partials_case(api, "bf16", n_h, lens, 8, seed=71 + n_h, tol=lambda L: 1e-4)
 
 
 def test_splitkv_partials_f32(api):
