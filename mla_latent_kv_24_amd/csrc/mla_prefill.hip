@@ -346,32 +346,49 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
       return cat(tr_read(bu + tr_off[0][cbg & 1]), tr_read(bu + tr_off[1][cbg & 1]));
     };
     // ---- score: elements 0..127 (k^C hi: k-steps 0..7), 256..383 (k^C lo:
-    // 16..23), 512..575 (k^R: 32..35)
+    // 16..23), 512..575 (k^R: 32..35).  The operands are read KPF k-steps
+    // ahead of their products (the order: k^C hi, with each k^C lo right
+    // after its hi part, then k^R).
+    constexpr int NK = PRECISE ? 20 : 12;
+    constexpr int KPF = 4;
+    auto kstep = [](int i) {
+      if (PRECISE) return i < 16 ? ((i & 1) ? 16 + (i >> 1) : (i >> 1)) : 32 + (i - 16);
+      return i < 8 ? i : 32 + (i - 8);
+    };
     f32x16 sacc[PF_QBW];
+    {
+      bf16x8 kb[KPF];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 kv = kread(s);
+      for (int i = 0; i < KPF; ++i) kb[i] = kread(kstep(i));
 #pragma unroll
-      for (int k = 0; k < PF_QBW; ++k) {
-        if (s == 0)
-          pf_mfma0(sacc[k], kv, qc[k][0]);
-        else
-          pf_mfma_qa(sacc[k], kv, qc[k][s]);
-      }
-      if constexpr (PRECISE) {
-        const bf16x8 kl = kread(16 + s);
+      for (int i = 0; i < NK; ++i) {
+        const bf16x8 kv = kb[i % KPF];
+        if (i + KPF < NK) kb[i % KPF] = kread(kstep(i + KPF));
+        const int ks = kstep(i);
 #pragma unroll
-        for (int k = 0; k < PF_QBW; ++k) pf_mfma_qa(sacc[k], kl, qc[k][s]);
+        for (int k = 0; k < PF_QBW; ++k) {
+          if (ks == 0)
+            pf_mfma0(sacc[k], kv, qc[k][0]);
+          else if (ks < 8)
+            pf_mfma_qa(sacc[k], kv, qc[k][ks]);
+          else if (ks < 32)
+            pf_mfma_qa(sacc[k], kv, qc[k][ks - 16]);  // k^C lo against the same query part
+          else {
+            pf_mfma_qa(sacc[k], kv, qrh[k][ks - 32]);
+            if constexpr (PRECISE) pf_mfma_qa(sacc[k], kv, qrl[k][ks - 32]);
+          }
+        }
       }
     }
+    // the value operands (v^C hi) do not depend on P: their transpose reads
+    // are issued now and land while the softmax runs
+    constexpr int NVA = PRECISE ? 1 : 8;
+    bf16x8 va[NVA];
+    if constexpr (!PRECISE) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 kv = kread(32 + s);
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int k = 0; k < PF_QBW; ++k) {
-        pf_mfma_qa(sacc[k], kv, qrh[k][s]);
-        if constexpr (PRECISE) pf_mfma_qa(sacc[k], kv, qrl[k][s]);
-      }
+        for (int u = 0; u < 2; ++u) va[2 * db + u] = vread(4 + db, u);
     }
     pf_drain();
     // ---- causal mask, online softmax (log2, lazy rescale) and P^T
@@ -418,7 +435,7 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const bf16x8 vh = vread(4 + db, u);
+        const bf16x8 vh = PRECISE ? vread(4 + db, u) : va[(2 * db + u) % NVA];
 #pragma unroll
         for (int k = 0; k < PF_QBW; ++k) {
           pf_mfma_vv(oacc[k][db], vh, ph[k][u]);
