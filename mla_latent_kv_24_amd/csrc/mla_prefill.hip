@@ -211,8 +211,7 @@ template <bool PRECISE>
 __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillArgs a) {
   constexpr int NBUF = 4;
   constexpr int LOADS = TILE_BYTES / (16 * 256);  // 9 DMA chunks per thread per tile
-  constexpr int T_OFF = NBUF * TILE_BYTES;        // per-thread DMA source chunk indices, u16 [LOADS][256]
-  __shared__ __attribute__((aligned(16))) uint8_t smem[T_OFF + LOADS * 256 * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * TILE_BYTES];
 
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -240,7 +239,6 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
   const uint32_t lds_w = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
                              (__attribute__((address_space(3))) uint8_t*)smem)) +
                          1024u * static_cast<uint32_t>(w);
-  uint16_t* otab = reinterpret_cast<uint16_t*>(smem + T_OFF);
   auto tile_rsrc = [&](int64_t it) {
     const uint64_t ga = gaddr + static_cast<uint64_t>(it) * TILE_BYTES;
     const int64_t rows = max(min(static_cast<int64_t>(TILE), kend - it * TILE), static_cast<int64_t>(0));
@@ -249,32 +247,29 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
                       __builtin_amdgcn_readfirstlane(static_cast<int>(rows * ROWB)), 0x00020000};
     return rs;
   };
-  // Without the lo products, the lo chunks (32..63 of the 72) are not
-  // fetched: their lanes take an offset past the buffer range, which reads
-  // zeros without touching memory and keeps every wave's load count fixed.
-  auto issue_chunks = [&](int64_t it, const uint32_t* ch) {
-    const i32x4 rs = tile_rsrc(it);
-    const uint32_t dst = lds_w + static_cast<uint32_t>((it & (NBUF - 1)) * TILE_BYTES);
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      int off = static_cast<int>(ch[i] << 4);
-      if constexpr (!PRECISE) {
-        const uint32_t q = ch[i] % 72;
-        if (q >= 32 && q < 64) off = 0x7ffffff0;
-      }
-      dma16(dst + 4096u * i, off, rs, 0);
-    }
+  // A thread's i-th chunk of a tile: the global chunk index, or NO_CHUNK for a
+  // lo chunk (32..63 of the 72) that the hi-only instance does not fetch: its
+  // lanes take an offset past the buffer range, which reads zeros without
+  // touching memory and keeps every wave's load count fixed.
+  constexpr uint32_t NO_CHUNK = 0xffffu;
+  auto issue_one = [&](const i32x4& rs, uint32_t dst, int i, uint32_t c) {
+    dma16(dst + 4096u * i, c == NO_CHUNK ? 0x7ffffff0 : static_cast<int>(c << 4), rs, 0);
   };
-  if (dma_wave) {
-    uint32_t ch[LOADS];
+  auto tile_dst = [&](int64_t it) { return lds_w + static_cast<uint32_t>((it & (NBUF - 1)) * TILE_BYTES); };
+  uint32_t ch[LOADS];  // kept in registers (the DMA waves have room for them)
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int f = tid + 256 * i;
-      const int t = f / 72, p = f - 72 * t;
-      ch[i] = static_cast<uint32_t>(72 * t + (p ^ swz(t)));
-      otab[i * 256 + tid] = static_cast<uint16_t>(ch[i]);
+  for (int i = 0; i < LOADS; ++i) {
+    const int f = tid + 256 * i;
+    const int t = f / 72, p = f - 72 * t;
+    const int q = p ^ swz(t);
+    ch[i] = (!PRECISE && q >= 32 && q < 64) ? NO_CHUNK : static_cast<uint32_t>(72 * t + q);
+  }
+  if (dma_wave) {
+    for (int64_t it = 0; it < min(ntiles, static_cast<int64_t>(3)); ++it) {
+      const i32x4 rs = tile_rsrc(it);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) issue_one(rs, tile_dst(it), i, ch[i]);
     }
-    for (int64_t it = 0; it < min(ntiles, static_cast<int64_t>(3)); ++it) issue_chunks(it, ch);
   }
 
   // ---- score B operands per query block k: q^C (8 k-steps), RoPE(q^R) hi and
@@ -336,7 +331,9 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
   const float qscale = a.qscale;
 
   // One tile for this wave's two query blocks; PRECISE adds the lo products.
-  auto tile = [&](const uint8_t* buf, int64_t it) {
+  // dma: this wave moves tile it+3 (its nine chunks go out one after each of
+  // the first nine score products)
+  auto tile = [&](const uint8_t* buf, int64_t it, bool dma) {
     auto kread = [&](int s) -> bf16x8 {
       return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(buf + sc_off[s & 3] + 128 * (s >> 2)));
     };
@@ -356,6 +353,8 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
       return i < 8 ? i : 32 + (i - 8);
     };
     f32x16 sacc[PF_QBW];
+    i32x4 rs3 = {0, 0, 0, 0};
+    if (dma) rs3 = tile_rsrc(it + 3);
     {
       bf16x8 kb[KPF];
 #pragma unroll
@@ -378,6 +377,7 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
             if constexpr (PRECISE) pf_mfma_qa(sacc[k], kv, qrl[k][ks - 32]);
           }
         }
+        if (dma && i < LOADS) issue_one(rs3, tile_dst(it + 3), i, ch[i]);
       }
     }
     // the value operands (v^C hi) do not depend on P: their transpose reads
@@ -459,15 +459,17 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
       vm_wait<0>();
     __syncthreads();
     // every wave passed this barrier, so buffer (it+3)&3 == (it-1)&3 is free:
-    // its refill starts before this tile's products
-    if (dma_wave && it + 3 < ntiles) {
-      uint32_t ch[LOADS];
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) ch[i] = otab[i * 256 + tid];
-      issue_chunks(it + 3, ch);
-    }
+    // its refill goes out between this tile's score products (or at once
+    // from a wave whose queries have no keys left)
+    const bool dma = dma_wave && it + 3 < ntiles;
     const uint8_t* buf = smem + (it & (NBUF - 1)) * TILE_BYTES;
-    if (it < my_tiles) tile(buf, it);
+    if (it < my_tiles) {
+      tile(buf, it, dma);
+    } else if (dma) {
+      const i32x4 rs = tile_rsrc(it + 3);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) issue_one(rs, tile_dst(it + 3), i, ch[i]);
+    }
   }
 
   pf_drain();  // the last output products have landed
