@@ -196,9 +196,9 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
 
 // ------------------------------------------------------------------------
 // Causal flash attention over the expanded rows.  Wave w owns queries
-// q0 + 64 w .. +63 as two blocks of 32 (the N side of every product):
+// q0 + 32 w .. +31 (PF_QBW blocks of 32; the N side of every product):
 //   score S^T = K . Q^T: A = tile rows (k^C hi [lo], k^R), B = [q^C; RoPE(q^R)
-//   hi [lo]] held in VGPRs;
+//   hi [lo]] held in AGPRs;
 //   value O^T += V^T . P^T: A = v^C hi [lo] columns by transpose reads, B = P^T
 //   hi [lo] straight from the score accumulator (the transpose read fetches
 //   exactly the keys whose scores the lane holds).
