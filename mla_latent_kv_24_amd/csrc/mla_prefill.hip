@@ -65,8 +65,20 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = l >> 5, l32 = l & 31;
   const int b = blockIdx.z;
-  const int h0 = blockIdx.y * XB_HEADS;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * XB_ROWS;
+  // Workgroups go to the 8 XCDs round robin by linear index.  With the head
+  // groups a multiple of 8, XCD x takes head groups x, x + 8, ... one at a
+  // time over all row blocks, so the 32 workgroups that an XCD runs together
+  // share one head group's W^UK and W^UV rows (2 MB) in its L2, instead of
+  // four groups' 8 MB streaming from the memory-side cache.
+  int rb = blockIdx.x, hg = blockIdx.y;
+  if (gridDim.y % 8 == 0) {
+    const int k = blockIdx.x + gridDim.x * blockIdx.y;
+    const int x = k % 8, j = k / 8;
+    hg = x + 8 * (j / gridDim.x);
+    rb = j % gridDim.x;
+  }
+  const int h0 = hg * XB_HEADS;
+  const int64_t row0 = static_cast<int64_t>(rb) * XB_ROWS;
   // the prefix clamped to [0, max_len - chunk] exactly as the attention kernel
   // clamps it, so that every row the attention reads is expanded
   int64_t prefix = a.prefix_lens[b];
@@ -217,8 +229,19 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g32 = l >> 5, l32 = l & 31, j16 = l & 15;
   const int nqb = (a.chunk + PQ - 1) / PQ;
-  const int qb = nqb - 1 - static_cast<int>(blockIdx.x);  // latest (longest) query blocks first
-  const int h = blockIdx.y, b = blockIdx.z;
+  // Workgroups go to the 8 XCDs round robin by linear index.  With the heads
+  // a multiple of 8, all query blocks of head h run on XCD h % 8, so its L2
+  // holds the head's expanded rows for all of them.  Within a head the
+  // latest (longest) query blocks come first.
+  int qi = blockIdx.x, h = blockIdx.y;
+  if (gridDim.y % 8 == 0) {
+    const int k = blockIdx.x + gridDim.x * blockIdx.y;
+    const int x = k % 8, j = k / 8;
+    h = x + 8 * (j / gridDim.x);
+    qi = j % gridDim.x;
+  }
+  const int qb = nqb - 1 - qi;
+  const int b = blockIdx.z;
   int64_t prefix = a.prefix_lens[b];
   prefix = max(min(prefix, static_cast<int64_t>(a.max_len - a.chunk)), static_cast<int64_t>(0));
   const int prefix32 = static_cast<int>(prefix);
