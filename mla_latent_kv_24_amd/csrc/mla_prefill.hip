@@ -93,8 +93,9 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
   };
 
   // ---- c rows -> LDS.  LDS chunk f = 256 i + tid is row 4 i + w, slot l, and
-  // holds the row's global chunk l ^ (row & 7): the swizzle spreads the eight
-  // rows that one operand read touches over distinct banks.  The block's rows
+  // holds the row's global chunk l ^ (row & 15): the swizzle spreads the 16
+  // rows that one pass of an operand read touches over distinct banks (with
+  // row & 7, rows r and r + 8 met in the same banks).  The block's rows
   // come as four 32-row runs (one page each when paged), each through a buffer
   // resource that spans the run's valid rows, so rows past the sequence (and
   // the rows of a page outside the pool) arrive as zeros.  bad_runs marks the
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
 #pragma unroll
       for (int i = 8 * k; i < 8 * k + 8; ++i) {
         const int r = 4 * i + w;  // row of the block; 32 k <= r < 32 k + 32
-        dma16(lds0 + 4096u * i, (r - 32 * k) * ROWB + 16 * (l ^ (r & 7)), rs, 0);
+        dma16(lds0 + 4096u * i, (r - 32 * k) * ROWB + 16 * (l ^ (r & 15)), rs, 0);
       }
     }
   }
@@ -139,16 +140,30 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
   __syncthreads();
 
   // B operand: row 32 rb + l32, elements 16 s + 8 g .. +7 (chunk 2 s + g)
-  const int cx = l32 & 7;
+  const int cx = l32 & 15;
   auto cread = [&](int rb, int s) -> u32x4 {
     return *reinterpret_cast<const u32x4*>(smem + (32 * rb + l32) * (D_C * 2) + 16 * ((2 * s + g) ^ cx));
   };
   // A operand rows: this wave's dims 64 w + 32 db + l32; U^K for dims < 128, U^V above
   const uint16_t* wsrc = static_cast<const uint16_t*>(w < 2 ? a.w_uk : a.w_uv);
   const int dloc = 64 * (w & 1) + l32;
+  // head hh's W rows for this lane (db adds 32 rows)
+  auto w_rows = [&](int hh) { return wsrc + (static_cast<int64_t>(h0 + hh) * D_H + dloc) * D_C + 8 * g; };
+  // the first XPF k-steps of a head's W operands; the next head's go out
+  // before this head's stores, so that their waits do not also wait for the
+  // stores (loads and stores share one counter)
+  u32x4 wa[XPF][2];
+  auto w_first = [&](int hh) {
+    const uint16_t* wr = w_rows(hh);
+#pragma unroll
+    for (int s = 0; s < XPF; ++s)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) wa[s][db] = *reinterpret_cast<const u32x4*>(wr + 32 * db * D_C + 16 * s);
+  };
+  w_first(0);
   for (int hh = 0; hh < XB_HEADS; ++hh) {
     const int h = h0 + hh;
-    const uint16_t* wr = wsrc + (static_cast<int64_t>(h) * D_H + dloc) * D_C + 8 * g;  // db adds 32 rows
+    const uint16_t* wr = w_rows(hh);
     f32x16 acc[2][4];
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -156,11 +171,6 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][rb][r] = 0.f;
-    u32x4 wa[XPF][2];
-#pragma unroll
-    for (int s = 0; s < XPF; ++s)
-#pragma unroll
-      for (int db = 0; db < 2; ++db) wa[s][db] = *reinterpret_cast<const u32x4*>(wr + 32 * db * D_C + 16 * s);
 #pragma unroll
     for (int s = 0; s < D_C / 16; ++s) {
       const u32x4 a0 = wa[s % XPF][0], a1 = wa[s % XPF][1];
@@ -176,6 +186,7 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
         acc[1][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), bv, acc[1][rb], 0, 0, 0);
       }
     }
+    if (hh + 1 < XB_HEADS) w_first(hh + 1);
     // lane l holds dims 8 jq + 4 g + (0..3) of block (db) for row 32 rb + l32:
     // hi at element d, lo at element 256 + d of the expanded row.  Only the
     // hi + lo attention workgroups read lo, and their keys all lie below
