@@ -187,32 +187,50 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
       }
     }
     if (hh + 1 < XB_HEADS) w_first(hh + 1);
-    // lane l holds dims 8 jq + 4 g + (0..3) of block (db) for row 32 rb + l32:
-    // hi at element d, lo at element 256 + d of the expanded row.  Only the
-    // hi + lo attention workgroups read lo, and their keys all lie below
-    // lo_rows; past it the lo parts are left unwritten.
+    // lane l holds dims 8 jq + 4 g + (0..3) of block (db) for row 32 rb + l32.
+    // One v_permlane32_swap per pair of values (jq = 2q and 2q + 1) trades the
+    // lane pair (l, l + 32)'s halves, after which lane g holds run q: the 8
+    // consecutive dims 8 (2q + g) .. +7, stored as 16 B: hi at element d, lo
+    // at element 256 + d of the expanded row.  Only the hi + lo attention
+    // workgroups read lo, and their keys all lie below lo_rows; past it the
+    // lo parts are left unwritten.
     uint16_t* xh = static_cast<uint16_t*>(a.x) + (static_cast<int64_t>(b) * a.n_h + h) * a.rows_cap * ROWE;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const int r = 32 * rb + l32;
-      if (r >= nrows) continue;
       uint16_t* xr = xh + (row0 + r) * ROWE;
       const bool pz = (bad_runs >> rb) & 1;  // row of a page outside the pool
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+      for (int db = 0; db < 2; ++db) {
+        const f32x16& v = acc[db][rb];
+        float run[2][8];
 #pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          const int d = 64 * w + 32 * db + 8 * jq + 4 * g;
-          const f32x16& v = acc[db][rb];
-          const float nan = __builtin_nanf("");
-          const float x0 = pz ? nan : v[4 * jq], x1 = pz ? nan : v[4 * jq + 1], x2 = pz ? nan : v[4 * jq + 2],
-                      x3 = pz ? nan : v[4 * jq + 3];
-          const uint32_t h01 = pack_bf16x2(x0, x1), h23 = pack_bf16x2(x2, x3);
-          const uint32_t l01 = pack_bf16x2(x0 - __uint_as_float(h01 << 16), x1 - __uint_as_float(h01 & 0xffff0000u));
-          const uint32_t l23 = pack_bf16x2(x2 - __uint_as_float(h23 << 16), x3 - __uint_as_float(h23 & 0xffff0000u));
-          *reinterpret_cast<uint2*>(xr + d) = make_uint2(h01, h23);
-          if (row0 + r < a.lo_rows) *reinterpret_cast<uint2*>(xr + 2 * D_H + d) = make_uint2(l01, l23);
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[8 * q + e]),
+                                                             __float_as_uint(v[8 * q + 4 + e]), false, false);
+            run[q][e] = __uint_as_float(sw[0]);
+            run[q][4 + e] = __uint_as_float(sw[1]);
+          }
+        if (r < nrows) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int d = 64 * w + 32 * db + 8 * (2 * q + g);
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x0 = pz ? __builtin_nanf("") : run[q][2 * e];
+              const float x1 = pz ? __builtin_nanf("") : run[q][2 * e + 1];
+              hw[e] = pack_bf16x2(x0, x1);
+              lw[e] = pack_bf16x2(x0 - __uint_as_float(hw[e] << 16), x1 - __uint_as_float(hw[e] & 0xffff0000u));
+            }
+            *reinterpret_cast<uint4*>(xr + d) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            if (row0 + r < a.lo_rows)
+              *reinterpret_cast<uint4*>(xr + 2 * D_H + d) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+          }
         }
+      }
     }
   }
 }
