@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla.so")
 SOURCES = ["mla_api.hip", "mla_rope_absorb.hip", "mla_splitkv.hip", "mla_combine.hip", "mla_prefill.hip",
-           "mla_gemm.hip", "mla_kvproj.hip", "mla_fp8.hip"]
+           "mla_gemm.hip", "mla_gemm_lds.hip", "mla_kvproj.hip", "mla_fp8.hip"]
 ARCH = "gfx950"
 
 

@@ -227,7 +227,7 @@ size_t mla_append_kv_from_hidden_workspace_bytes(const mla_dims* dims, mla_dtype
                                                  int32_t d_model) {
   if (check_dims(dims, dtype) != MLA_OK || n_tok < 1 || d_model < 1) return 0;
   int32_t slices = 1, kr = 0;
-  mla::gemm_plan(n_tok, d_model, mla::ROWE, mla::D_C, slices, kr);
+  mla::kv_project_plan(n_tok, d_model, dtype == MLA_BF16, slices, kr);
   return static_cast<size_t>(slices) * n_tok * mla::ROWE * sizeof(float);
 }
 
@@ -258,7 +258,7 @@ mla_status mla_append_kv_from_hidden(const mla_dims* dims, mla_dtype dtype, int3
   a.part = static_cast<float*>(workspace);
   a.n_tok = n_tok;
   a.d_model = d_model;
-  mla::gemm_plan(n_tok, d_model, mla::ROWE, mla::D_C, a.k_slices, a.k_per_slice);
+  mla::kv_project_plan(n_tok, d_model, dtype == MLA_BF16, a.k_slices, a.k_per_slice);
   a.eps = static_cast<float>(eps);
   fill_rope(dims, a.rope);
   return hip_status(mla::launch_kv_project_append(a, dtype == MLA_BF16, static_cast<hipStream_t>(stream)),

@@ -199,8 +199,13 @@ hipError_t launch_prefill_unabsorbed(const ExpandArgs& e, const PrefillArgs& p, 
 hipError_t launch_kv_project_append(const KvProjArgs& a, int bf16, hipStream_t st);
 hipError_t launch_append_fp8(const AppendArgs& a, hipStream_t st);
 hipError_t launch_splitkv_fp8(const SplitArgs& a, hipStream_t st);
-// split-K plan of launch_kv_project_append: slices and k per slice (a multiple of 64)
-void kv_project_plan(int32_t n_tok, int32_t d_model, int32_t& k_slices, int32_t& k_per_slice);
+// split-K plan of launch_kv_project_append for the storage dtype: slices and k per slice
+void kv_project_plan(int32_t n_tok, int32_t d_model, int bf16, int32_t& k_slices, int32_t& k_per_slice);
+// LDS-tiled product (mla_gemm_lds.hip): split-K partials of [w0 ; w1] x^T
+// for n >= 256 activation rows, d_in % 64 == 0, d_out % 192 == 0
+bool gemm_lds_applies(int32_t n, int32_t d_in, int32_t d_out);
+void gemm_lds_plan(int32_t n, int32_t d_in, int32_t d_out, int32_t& k_slices, int32_t& k_per_slice);
+hipError_t launch_gemm_lds_partial(const GemmArgs& g, hipStream_t st);
 bool splitkv_has_fast_path(int n_h, int bf16, int d_c, int d_r);
 // every query of a launch takes the 16-head-group (hi + lo) path: the grouped
 // kernel runs it over (query, split, head group)

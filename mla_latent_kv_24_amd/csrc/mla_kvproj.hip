@@ -6,7 +6,8 @@
 //   row = [ RMSNorm(x[0:d_c]) * weight ; RoPE(x[d_c:], pos) ]
 // Two launches:
 //   the split-K partial sums of x, fp32 [slice][token][576], by the shared
-//     projection kernels (mla_gemm.hip);
+//     projection kernels (mla_gemm.hip; from 256 tokens on, the LDS-tiled
+//     product of mla_gemm_lds.hip);
 //   kvproj_finalize_kernel: per token, one thread per output sums the slices
 //     in a fixed order, the latent's mean square is reduced over the
 //     workgroup, and the row is stored in the cache's dtype (RoPE angle in
@@ -61,6 +62,16 @@ __global__ __launch_bounds__(ROWE) void kvproj_finalize_kernel(KvProjArgs a) {
   }
 }
 
+// bf16 chunks of 256 tokens or more take the LDS-tiled product (three
+// 192-output tiles per 256 tokens, split K for about one round of the CUs);
+// fewer tokens, or fp32, the weight-streaming and generic kernels.
+void kv_project_plan(int32_t n_tok, int32_t d_model, int bf16, int32_t& k_slices, int32_t& k_per_slice) {
+  if (bf16 && gemm_lds_applies(n_tok, d_model, ROWE))
+    gemm_lds_plan(n_tok, d_model, ROWE, k_slices, k_per_slice);
+  else
+    gemm_plan(n_tok, d_model, ROWE, D_C, k_slices, k_per_slice);
+}
+
 hipError_t launch_kv_project_append(const KvProjArgs& a, int bf16, hipStream_t st) {
   if (a.n_tok <= 0) return hipSuccess;
   GemmArgs g{};
@@ -74,7 +85,8 @@ hipError_t launch_kv_project_append(const KvProjArgs& a, int bf16, hipStream_t s
   g.split = D_C;
   g.k_slices = a.k_slices;
   g.k_per_slice = a.k_per_slice;
-  hipError_t e = launch_gemm_partial(g, bf16, st);
+  hipError_t e = (bf16 && gemm_lds_applies(a.n_tok, a.d_model, ROWE)) ? launch_gemm_lds_partial(g, st)
+                                                                        : launch_gemm_partial(g, bf16, st);
   if (e != hipSuccess) return e;
   if (bf16)
     kvproj_finalize_kernel<uint16_t><<<a.n_tok, ROWE, 0, st>>>(a);

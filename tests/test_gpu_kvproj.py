@@ -53,9 +53,12 @@ def _check_rows(got, exact, dtype):
 
 # V2 decode step (64 tokens of hidden 5120), V2-Lite (2048), a ragged token
 # block, a d_model the MFMA tiling takes in 5 slices of 128, the generic bf16
-# path (d_model not a multiple of 128), fp32 storage, a prefill chunk
+# path (d_model not a multiple of 128), fp32 storage, a prefill chunk; from
+# 256 tokens the LDS-tiled product, also with one token past a tile and k
+# slices of 5, 5 and 3 stages of 64 (d_model 832)
 CASES = [("bf16", 64, 5120, True), ("bf16", 1, 2048, False), ("bf16", 300, 2048, True),
-         ("bf16", 70, 640, True), ("bf16", 5, 200, True), ("f32", 9, 300, True), ("bf16", 4096, 5120, True)]
+         ("bf16", 70, 640, True), ("bf16", 5, 200, True), ("f32", 9, 300, True), ("bf16", 4096, 5120, True),
+         ("bf16", 257, 832, False)]
 
 
 @pytest.mark.parametrize("dtype,n_tok,d_model,weighted", CASES)
