@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla.so")
 SOURCES = ["mla_api.hip", "mla_rope_absorb.hip", "mla_splitkv.hip", "mla_combine.hip", "mla_prefill.hip",
-           "mla_gemm.hip", "mla_gemm_lds.hip", "mla_kvproj.hip", "mla_fp8.hip"]
+           "mla_gemm.hip", "mla_gemm_lds.hip", "mla_kvproj.hip", "mla_fp8.hip",
+           "mla_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -36,14 +37,24 @@ def common_flags() -> list[str]:
             "-I", INCLUDE, "-I", CSRC, "-Wno-unused-command-line-argument"]
 
 
-def build(verbose: bool = False) -> str:
+PROBE_LIB = os.path.join(PKG, "libmla_probe.so")
+
+
+def build(verbose: bool = False, probe: bool = False) -> str:
+    """Compile and link libmla.so; with probe=True, libmla_probe.so instead:
+    the same library with per-phase cycle stamps in the 128-head decode
+    kernel and the read, LDS and MFMA probe kernels of mla_probe.hip
+    (MLA_PHASE_STAMPS, driven by probe.py), a measurement build that the
+    product never loads."""
     cc = hipcc()
-    objdir = os.path.join(PKG, "_build")
+    objdir = os.path.join(PKG, "_build_probe" if probe else "_build")
     os.makedirs(objdir, exist_ok=True)
+    extra = ["-DMLA_PHASE_STAMPS"] if probe else []
+    out_lib = PROBE_LIB if probe else LIB
 
     def compile_one(src: str) -> str:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [cc, *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *common_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,14 +64,14 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = out_lib + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out_lib)
+    return out_lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, probe="--probe" in sys.argv))

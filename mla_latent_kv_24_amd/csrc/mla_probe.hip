@@ -1,0 +1,107 @@
+// Measurement kernels of the probe build (build.py --probe defines
+// MLA_PHASE_STAMPS); the product library compiles this file to nothing.
+//   probe_read_kernel: a plain streaming read (16-B loads, 8 in flight per
+//     lane), the board's read ceiling for a kernel that does nothing else;
+//   probe_lds_kernel: conflict-free ds_read_b128 from a 64 KB LDS buffer,
+//     bytes per shader cycle per CU;
+//   probe_mfma_kernel: four independent chains of v_mfma_f32_32x32x16_bf16
+//     per wave on random operands, the matrix cores' rate and the shader
+//     clock under that load.
+#include "mla_common.h"
+
+#ifdef MLA_PHASE_STAMPS
+
+namespace mla {
+
+__global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* p, int64_t n16, uint32_t* sink) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = p[i + k * stride];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= v[k];
+  }
+  for (; i < n16; i += stride) acc ^= p[i];
+  const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  if (x == 0x9e3779b9u) sink[blockIdx.x] = x;  // data-dependent: the loads stay
+}
+
+__global__ __launch_bounds__(256) void probe_lds_kernel(int iters, uint64_t* out) {
+  __shared__ u32x4 buf[4096];  // 64 KB
+  const int t = threadIdx.x;
+  for (int i = t; i < 4096; i += 256) buf[i] = u32x4{static_cast<uint32_t>(i), 1u, 2u, 3u};
+  __syncthreads();
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc ^= buf[(t + 256 * k + 64 * it) & 4095];  // consecutive 16 B per lane
+  }
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  if (t == 0) {
+    out[2 * blockIdx.x] = c1 - c0;
+    out[2 * blockIdx.x + 1] = static_cast<uint64_t>(iters) * 16 * 256 * 16;  // bytes read by the workgroup
+  }
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9e3779b9u) out[2 * blockIdx.x] = 0;
+}
+
+__global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, uint64_t* out, float* sink) {
+  // random operand bits per lane (a hash of the lane and block)
+  uint32_t h = (blockIdx.x * 256u + threadIdx.x) * 2654435761u + 0x7f4a7c15u;
+  u32x4 ra, rb;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    h ^= h << 13;
+    h ^= h >> 17;
+    h ^= h << 5;
+    ra[k] = h & 0xbfffbfffu;  // finite bf16 pairs
+    h ^= h << 13;
+    h ^= h >> 17;
+    h ^= h << 5;
+    rb[k] = h & 0xbfffbfffu;
+  }
+  const bf16x8 a = __builtin_bit_cast(bf16x8, ra), b = __builtin_bit_cast(bf16x8, rb);
+  f32x16 c[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[k][r] = 0.f;
+  const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[k], 0, 0, 0);
+  }
+  const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = c1 - c0;
+    out[2 * blockIdx.x + 1] = r1 - r0;
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s += c[k][0];
+  if (s != s) sink[blockIdx.x] = s;  // the products stay
+}
+
+}  // namespace mla
+
+// Host entry points of the probe build.  Each launches on `stream` and returns
+// the launch status; the caller times the launch with events.
+extern "C" int mla_probe_read(const void* p, int64_t bytes, void* sink, int32_t workgroups, void* stream) {
+  mla::probe_read_kernel<<<workgroups, 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const mla::u32x4*>(p), bytes / 16, static_cast<uint32_t*>(sink));
+  return static_cast<int>(hipGetLastError());
+}
+extern "C" int mla_probe_lds(int32_t iters, void* out, int32_t workgroups, void* stream) {
+  mla::probe_lds_kernel<<<workgroups, 256, 0, static_cast<hipStream_t>(stream)>>>(iters, static_cast<uint64_t*>(out));
+  return static_cast<int>(hipGetLastError());
+}
+extern "C" int mla_probe_mfma(int32_t iters, void* out, void* sink, int32_t workgroups, void* stream) {
+  mla::probe_mfma_kernel<<<workgroups, 256, 0, static_cast<hipStream_t>(stream)>>>(iters, static_cast<uint64_t*>(out),
+                                                                                    static_cast<float*>(sink));
+  return static_cast<int>(hipGetLastError());
+}
+
+#endif  // MLA_PHASE_STAMPS

@@ -37,6 +37,12 @@
 
 namespace mla {
 
+#ifdef MLA_PHASE_STAMPS
+// Measurement build only (build.py --probe): per-wave cycle sums of the
+// 128-head kernel's tile loop, by phase, for the first 1,024 workgroups.
+__device__ uint64_t g_phase_stamps[1024 * 4 * 8];
+#endif
+
 constexpr int NQ16 = (D_C + D_R) / 32;  // 16-head score k-steps of 32 elements
 
 template <bool PAGED>
@@ -843,11 +849,26 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
   //            woven in (its factor is read by every wave in the next phase 1).
   // The DMA of tile t+3 is issued between score MFMAs (measured faster than
   // between value MFMAs).
+#ifdef MLA_PHASE_STAMPS
+  // cycle sums per phase: 0 wait + barrier, 1 phase 1, 2 barrier, 3 phase 2
+  uint64_t ps_acc[4] = {0, 0, 0, 0};
+  uint64_t ps_prev = __builtin_amdgcn_s_memtime();
+  const uint64_t ps_t0 = ps_prev, ps_rt0 = __builtin_amdgcn_s_memrealtime();
+  auto ps_tick = [&](int k) {
+    const uint64_t now = __builtin_amdgcn_s_memtime();
+    ps_acc[k] += now - ps_prev;
+    ps_prev = now;
+  };
+#define MLA_TICK(k) ps_tick(k)
+#else
+#define MLA_TICK(k)
+#endif
   auto step = [&](int64_t t, f32x16& sx, f32x16& sn) {
     // tile t+1 must have landed (only the nine loads of tile t+2 may still be
     // in flight); every wave is done with tile t-1, whose buffer takes tile t+3
     vm_wait<LOADS>();
     __syncthreads();
+    MLA_TICK(0);
     const i32x4 rs3 = tile_rsrc(t + 3);
     const uint8_t* nb = smem + ((t + 1) & (NBUF - 1)) * TILE_BYTES;
     const uint8_t* cbuf = smem + (t & (NBUF - 1)) * TILE_BYTES;
@@ -894,7 +915,9 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    MLA_TICK(1);
     __syncthreads();  // P^T of every head group visible
+    MLA_TICK(2);
 
     // ---- phase 2
     {
@@ -942,6 +965,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
   // copies: their position stays after phase 2, far behind sB's last MFMA.
   for (int64_t t = 0; t < ntiles; ++t) {
     step(t, sA, sB);
+    MLA_TICK(3);
 #pragma unroll
     for (int j = 0; j < 16; ++j) asm volatile("v_mov_b32 %0, %1" : "=v"(sA[j]) : "v"(sB[j]));
   }
@@ -973,6 +997,20 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
         *reinterpret_cast<f32x4*>(zrow + 32 * cb + 8 * jj) = v;
       }
   }
+#ifdef MLA_PHASE_STAMPS
+  {
+    const uint64_t t1 = __builtin_amdgcn_s_memtime(), rt1 = __builtin_amdgcn_s_memrealtime();
+    const int wg = blockIdx.x + gridDim.x * blockIdx.y;
+    if (l == 0 && wg < 1024) {
+      uint64_t* o = g_phase_stamps + (static_cast<int64_t>(wg) * 4 + w) * 8;
+      for (int k = 0; k < 4; ++k) o[k] = ps_acc[k];
+      o[4] = t1 - ps_t0;    // shader cycles from the loop's start to the end
+      o[5] = rt1 - ps_rt0;  // the same span in 100 MHz ticks
+      o[6] = static_cast<uint64_t>(ntiles);
+    }
+  }
+#endif
+#undef MLA_TICK
 }
 
 // n_h a multiple of 16: one workgroup per (query, split, group of 16 heads),
@@ -1112,3 +1150,12 @@ hipError_t launch_splitkv(const SplitArgs& a, int bf16, hipStream_t st) {
 }
 
 }  // namespace mla
+
+#ifdef MLA_PHASE_STAMPS
+// Copies the phase stamps of the last 128-head decode launch to host memory
+// (1,024 x 4 x 8 uint64); measurement build only.
+extern "C" int mla_probe_phase_stamps(void* host) {
+  return static_cast<int>(hipMemcpyFromSymbol(host, HIP_SYMBOL(mla::g_phase_stamps),
+                                              sizeof(uint64_t) * 1024 * 4 * 8, 0, hipMemcpyDeviceToHost));
+}
+#endif
