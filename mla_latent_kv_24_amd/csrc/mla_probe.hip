@@ -85,6 +85,73 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, uint64_t* ou
   if (s != s) sink[blockIdx.x] = s;  // the products stay
 }
 
+// Does VALU work overlap matrix-core work on a SIMD?  Per iteration a wave
+// issues NM v_mfma_f32_32x32x16_bf16 (four independent chains) and/or NV
+// v_fma_f32 (16 independent chains), all unrolled so that every operand stays
+// in registers; mode 0: every wave does both, one MFMA then NV/NM FMAs; mode 1:
+// waves 0-3 only the MFMAs, waves 4-7 only the FMAs (one of each per SIMD);
+// mode 2: every wave only the MFMAs; mode 3: every wave only the FMAs.  Each
+// wave's cycles over the loop go to out.
+template <int NM, int NV>
+__global__ __launch_bounds__(512) void probe_overlap_kernel(int iters, int mode, uint64_t* out, float* sink) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t h = (blockIdx.x * 512u + threadIdx.x) * 2654435761u + 0x7f4a7c15u;
+  u32x4 ra, rb;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    h ^= h << 13;
+    h ^= h >> 17;
+    h ^= h << 5;
+    ra[k] = h & 0xbfffbfffu;
+    h ^= h << 13;
+    h ^= h >> 17;
+    h ^= h << 5;
+    rb[k] = h & 0xbfffbfffu;
+  }
+  const bf16x8 a = __builtin_bit_cast(bf16x8, ra), b = __builtin_bit_cast(bf16x8, rb);
+  f32x16 c[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[k][r] = 0.f;
+  float x[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) x[k] = static_cast<float>(threadIdx.x + k) * 1e-3f;
+  const float fa = 0.999f, fb = 1e-4f;
+  const bool do_m = mode == 0 || mode == 2 || (mode == 1 && w < 4);
+  const bool do_v = mode == 0 || mode == 3 || (mode == 1 && w >= 4);
+  constexpr int PER = NV / NM;
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  if (do_m && do_v) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        c[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[m & 3], 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < PER; ++v) x[(m * PER + v) & 15] = fmaf(x[(m * PER + v) & 15], fa, fb);
+      }
+    }
+  } else if (do_m) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) c[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[m & 3], 0, 0, 0);
+    }
+  } else {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) x[v & 15] = fmaf(x[v & 15], fa, fb);
+    }
+  }
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  if ((threadIdx.x & 63) == 0) out[blockIdx.x * 8 + w] = c1 - c0;
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s += c[k][0];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) s += x[k];
+  if (s != s) sink[blockIdx.x] = s;
+}
+
 }  // namespace mla
 
 // Host entry points of the probe build.  Each launches on `stream` and returns
@@ -101,6 +168,21 @@ extern "C" int mla_probe_lds(int32_t iters, void* out, int32_t workgroups, void*
 extern "C" int mla_probe_mfma(int32_t iters, void* out, void* sink, int32_t workgroups, void* stream) {
   mla::probe_mfma_kernel<<<workgroups, 256, 0, static_cast<hipStream_t>(stream)>>>(iters, static_cast<uint64_t*>(out),
                                                                                     static_cast<float*>(sink));
+  return static_cast<int>(hipGetLastError());
+}
+
+// nv is 64 or 128 FMAs per 8 MFMAs per iteration
+extern "C" int mla_probe_overlap(int32_t iters, int32_t mode, int32_t nv, void* out, void* sink, int32_t workgroups,
+                                 void* stream) {
+  auto* o = static_cast<uint64_t*>(out);
+  auto* k = static_cast<float*>(sink);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (nv == 64)
+    mla::probe_overlap_kernel<8, 64><<<workgroups, 512, 0, st>>>(iters, mode, o, k);
+  else if (nv == 128)
+    mla::probe_overlap_kernel<8, 128><<<workgroups, 512, 0, st>>>(iters, mode, o, k);
+  else
+    return static_cast<int>(hipErrorInvalidValue);
   return static_cast<int>(hipGetLastError());
 }
 

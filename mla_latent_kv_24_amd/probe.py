@@ -5,6 +5,7 @@
     python3 -m mla_latent_kv_24_amd.probe read        # streaming-read ceiling
     python3 -m mla_latent_kv_24_amd.probe lds         # ds_read_b128 bytes per cycle per CU
     python3 -m mla_latent_kv_24_amd.probe mfma        # bf16 MFMA rate and clock on random operands
+    python3 -m mla_latent_kv_24_amd.probe overlap     # does VALU work overlap MFMA work on a SIMD?
 
 The probe library is the product library built with MLA_PHASE_STAMPS: the
 128-head kernel sums s_memtime cycles per phase of each tile step (the wait
@@ -39,7 +40,9 @@ def _lib():
     lib.mla_probe_read.argtypes = [vp, i64, vp, i32, vp]
     lib.mla_probe_lds.argtypes = [i32, vp, i32, vp]
     lib.mla_probe_mfma.argtypes = [i32, vp, vp, i32, vp]
-    for f in (lib.mla_probe_phase_stamps, lib.mla_probe_read, lib.mla_probe_lds, lib.mla_probe_mfma):
+    lib.mla_probe_overlap.argtypes = [i32, i32, i32, vp, vp, i32, vp]
+    for f in (lib.mla_probe_phase_stamps, lib.mla_probe_read, lib.mla_probe_lds, lib.mla_probe_mfma,
+              lib.mla_probe_overlap):
         f.restype = ctypes.c_int
     return lib
 
@@ -147,14 +150,34 @@ def mfma(lib):
             "cycles_per_mfma": round(float(d[:, 0].mean()) / (iters * 4), 2)}
 
 
+def overlap(lib):
+    """Cycles per iteration (8 MFMAs and/or 64 or 128 FMAs) of each wave, two waves per SIMD: each kind alone,
+    split over the SIMD's two waves, and mixed in every wave.  MFMA and VALU overlap iff split/mixed take about
+    the larger of the parts rather than their sum."""
+    iters, wg = 2000, CUS  # 8 waves per workgroup, one workgroup per CU: two waves per SIMD
+    out_t = torch.zeros(8 * wg, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(wg, dtype=torch.float32, device="cuda")
+    res = {"probe": "overlap", "mfma": "v_mfma_f32_32x32x16_bf16", "valu": "v_fma_f32", "waves_per_simd": 2,
+           "unit": "cycles per iteration of each wave (mean over waves 0-3 / 4-7)"}
+    cases = [("both_waves_8_mfma", 2, 64), ("both_waves_64_fma", 3, 64), ("both_waves_128_fma", 3, 128),
+             ("one_wave_8_mfma_other_64_fma", 1, 64), ("one_wave_8_mfma_other_128_fma", 1, 128),
+             ("both_waves_8_mfma_and_64_fma", 0, 64), ("both_waves_8_mfma_and_128_fma", 0, 128)]
+    for name, mode, nv in cases:
+        _timed(lambda: lib.mla_probe_overlap(iters, mode, nv, ctypes.c_void_p(out_t.data_ptr()),
+                                             ctypes.c_void_p(sink.data_ptr()), wg, _stream()), 3)
+        d = out_t.view(wg, 8).cpu().numpy().astype(np.float64) / iters
+        res[name] = [round(float(d[:, :4].mean()), 1), round(float(d[:, 4:].mean()), 1)]
+    return res
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["phases", "read", "lds", "mfma"])
+    ap.add_argument("what", choices=["phases", "read", "lds", "mfma", "overlap"])
     ap.add_argument("--workload", default="v2_decode")
     args = ap.parse_args()
     lib = _lib()
     res = {"phases": lambda: phases(lib, args.workload), "read": lambda: read(lib), "lds": lambda: lds(lib),
-           "mfma": lambda: mfma(lib)}[args.what]()
+           "mfma": lambda: mfma(lib), "overlap": lambda: overlap(lib)}[args.what]()
     print(json.dumps(res), flush=True)
 
 
