@@ -219,9 +219,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {  // round to nearest 
   __bf16 h = static_cast<__bf16>(f);
   return __builtin_bit_cast(uint16_t, h);
 }
-// bf16 pair (round to nearest even), lo in the low half
+// bf16 pair (round to nearest even), lo in the low half: one v_cvt_pk_bf16_f32
+// (the conversion of each half alone is the same instruction, so the bits are
+// those of f32_to_bf16 on each value)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 template <typename T>
 __device__ __forceinline__ float load_as_f32(const T* p, int64_t i);

@@ -6,6 +6,7 @@
     python3 -m mla_latent_kv_24_amd.probe lds         # ds_read_b128 bytes per cycle per CU
     python3 -m mla_latent_kv_24_amd.probe mfma        # bf16 MFMA rate and clock on random operands
     python3 -m mla_latent_kv_24_amd.probe overlap     # does VALU work overlap MFMA work on a SIMD?
+    python3 -m mla_latent_kv_24_amd.probe floor       # the V2 decode attention's bytes and products alone
 
 The probe library is the product library built with MLA_PHASE_STAMPS: the
 128-head kernel sums s_memtime cycles per phase of each tile step (the wait
@@ -41,8 +42,9 @@ def _lib():
     lib.mla_probe_lds.argtypes = [i32, vp, i32, vp]
     lib.mla_probe_mfma.argtypes = [i32, vp, vp, i32, vp]
     lib.mla_probe_overlap.argtypes = [i32, i32, i32, vp, vp, i32, vp]
+    lib.mla_probe_floor.argtypes = [vp, i64, i32, vp, vp, i32, vp]
     for f in (lib.mla_probe_phase_stamps, lib.mla_probe_read, lib.mla_probe_lds, lib.mla_probe_mfma,
-              lib.mla_probe_overlap):
+              lib.mla_probe_overlap, lib.mla_probe_floor):
         f.restype = ctypes.c_int
     return lib
 
@@ -170,14 +172,52 @@ def overlap(lib):
     return res
 
 
+def floor(lib):
+    """The decode attention's work at v2_decode with nothing else: 256 workgroups (one per CU) stream 64 tiles
+    of 36,864 B each (603,979,776 B, the cache of 64 sequences x 8,192 rows) and issue 68 bf16 32x32x16
+    products per tile and wave (1.4603e11 FLOP, 2,176 x 128 per row).  Mode both / products alone / loads
+    alone; each after a 1.5 s settle on its own load, timed back to back and after a 512 MB read that evicts
+    the Infinity Cache (the attention kernel's roofline protocol)."""
+    tiles, wg = 64, CUS
+    nbytes = wg * tiles * 36864
+    data = torch.randn(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    out_t = torch.zeros(2 * wg, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(wg, dtype=torch.float32, device="cuda")
+    flush_buf = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")
+    flush_sum = torch.zeros((), dtype=torch.float32, device="cuda")
+    res = {"probe": "floor", "bytes": nbytes, "flop": 2176 * 128 * (nbytes // 1152), "workgroups": wg,
+           "tiles_per_workgroup": tiles, "mfma_per_tile_and_wave": 68}
+    for mode, name in ((0, "loads_and_products"), (1, "products_alone"), (2, "loads_alone")):
+        def launch():
+            assert lib.mla_probe_floor(ctypes.c_void_p(data.data_ptr()), tiles, mode, ctypes.c_void_p(out_t.data_ptr()),
+                                       ctypes.c_void_p(sink.data_ptr()), wg, _stream()) == 0
+        b2b = _timed(launch, 20) * 1e3
+        d = out_t.view(wg, 2).cpu().numpy().astype(np.float64)
+        ghz = float((d[:, 0] / (d[:, 1] * 10.0)).mean())
+        ts = []
+        for _ in range(20):
+            torch.sum(flush_buf, dim=0, out=flush_sum)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        us = float(np.mean(ts))
+        res[name] = {"us_flushed": round(us, 1), "us_back_to_back": round(b2b, 1), "shader_clock_ghz": round(ghz, 3),
+                     "tb_s": round(nbytes / (us * 1e-6) / 1e12, 2) if mode != 1 else None,
+                     "pflop_s": round(res["flop"] / (us * 1e-6) / 1e15, 3) if mode != 2 else None}
+    return res
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["phases", "read", "lds", "mfma", "overlap"])
+    ap.add_argument("what", choices=["phases", "read", "lds", "mfma", "overlap", "floor"])
     ap.add_argument("--workload", default="v2_decode")
     args = ap.parse_args()
     lib = _lib()
     res = {"phases": lambda: phases(lib, args.workload), "read": lambda: read(lib), "lds": lambda: lds(lib),
-           "mfma": lambda: mfma(lib), "overlap": lambda: overlap(lib)}[args.what]()
+           "mfma": lambda: mfma(lib), "overlap": lambda: overlap(lib), "floor": lambda: floor(lib)}[args.what]()
     print(json.dumps(res), flush=True)
 
 
