@@ -276,13 +276,14 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copy probe: 1 GiB device-to-device copy done")
 
-    # The step: append (A1), absorb (A2), the attention kernel (A3), then the
-    # combine (A4 + A5); each a plain launch on torch's current stream.  Events
+    # The step: append (A1) and absorb (A2) in one call (one launch on the bf16
+    # fast path), the attention kernel (A3), then the combine (A4 + A5); each a
+    # plain launch on torch's current stream.  Events
     # (HIP, recorded on that stream) may bracket any stage: `ev` maps a stage
     # to its (start, end) pair.  Events cannot be recorded inside a captured
     # HIP graph here, and replaying the other stages as graphs around an eager
     # attention launch measured ~7 us slower per graph than plain launches.
-    STAGES = (("append_kv", st.append_new), ("absorb_q", st.absorb),
+    STAGES = (("append_absorb", st.append_absorb),
               ("splitkv_attention", st.attention), ("combine_project", st.combine))
 
     def run_step(ev=None):

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 9
+#define MLA_ABI_VERSION 10
 
 typedef enum {
   MLA_OK = 0,
@@ -143,6 +143,24 @@ mla_status mla_append_kv_from_hidden(const mla_dims* dims, mla_dtype dtype, int3
 mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q,
                         const void* q_c, const void* q_r, const int32_t* q_pos,
                         const void* w_uk, void* q_lat, void* q_lat_lo, void* stream);
+
+/* A1 + A2 of one decode step in one call (the review's section 3: the step's
+ * new token is cached as [c^KV ; RoPE(k^R)] and its query absorbed; the two
+ * are independent, both precede the attention).  Exactly
+ *     mla_append_kv(dims, dtype, n_tok, c_kv, k_r, pos, row, cache, stream);
+ *     mla_absorb_q(dims, dtype, n_q, q_c, q_r, q_pos, w_uk, q_lat, q_lat_lo, stream);
+ * with the same arguments, layouts, results (bit for bit) and errors, except
+ * that n_tok = 0 or n_q = 0 skips that half only, and its pointers may then be
+ * NULL.  Where the absorbed query has its bf16 matrix-core kernel (MLA_BF16,
+ * d_c = 512, d_h = 128, d_hR = 64) both run in that kernel's one launch: its
+ * workgroups also write the cache rows, whose loads overlap the W^UK stream;
+ * otherwise the two calls' launches run in order.  The cache rows must not
+ * overlap q_c, q_r, w_uk, q_lat or q_lat_lo. */
+mla_status mla_append_absorb(const mla_dims* dims, mla_dtype dtype, int32_t n_tok,
+                             const void* c_kv, const void* k_r, const int32_t* pos,
+                             const int64_t* row, void* cache, int32_t n_q, const void* q_c,
+                             const void* q_r, const int32_t* q_pos, const void* w_uk,
+                             void* q_lat, void* q_lat_lo, void* stream);
 
 /* The query path from hidden states into A2 (review section 2: queries pass
  * through a 1,536-wide latent; DeepSeek-V3 report, Metode 1: c^Q; the latent

@@ -80,6 +80,8 @@ _SIGS = {
     "mla_output_projection_workspace_bytes": (_sz, [_P, _i32, _i32]),
     "mla_output_projection": (ctypes.c_int, [_P, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mla_absorb_q": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mla_append_absorb": (ctypes.c_int, [_P, ctypes.c_int, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
+                                         _vp, _vp, _vp, _vp]),
     "mla_precise_rows": (_i32, [_P, ctypes.c_int]),
     "mla_decode_num_splits": (_i32, [_P, ctypes.c_int, _i32, _i32]),
     "mla_split_rows": (_i64, [_i32, _i32]),
@@ -245,6 +247,18 @@ def absorb_q(d: Dims, q_c, q_r, q_pos, w_uk, q_lat) -> None:
     _check(_lib.mla_absorb_q(ctypes.byref(d), _dtype(w_uk), q_c.shape[0], _ptr(q_c), _ptr(q_r),
                              _ptr(q_pos), _ptr(w_uk), hi, lo, _stream(q_lat.device)),
            "mla_absorb_q")
+
+
+def append_absorb(d: Dims, c_kv, k_r, pos, row, cache, q_c, q_r, q_pos, w_uk, q_lat) -> None:
+    """A1 + A2 of a decode step in one call: append_kv(c_kv, k_r, pos, row, cache)
+    and absorb_q(q_c, q_r, q_pos, w_uk, q_lat), bit for bit (one launch on the
+    bf16 fast path)."""
+    assert pos.dtype == torch.int32 and row.dtype == torch.int64 and q_pos.dtype == torch.int32
+    assert q_lat.dtype == w_uk.dtype == cache.dtype
+    hi, lo = _q(q_lat)
+    _check(_lib.mla_append_absorb(ctypes.byref(d), _dtype(cache), c_kv.shape[0], _ptr(c_kv), _ptr(k_r), _ptr(pos),
+                                  _ptr(row), _ptr(cache), q_c.shape[0], _ptr(q_c), _ptr(q_r), _ptr(q_pos),
+                                  _ptr(w_uk), hi, lo, _stream(cache.device)), "mla_append_absorb")
 
 
 def num_splits(d: Dims, dtype: int, batch: int, max_seq_len: int) -> int:

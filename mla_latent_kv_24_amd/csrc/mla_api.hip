@@ -267,8 +267,16 @@ mla_status mla_append_kv_from_hidden(const mla_dims* dims, mla_dtype dtype, int3
 
 static mla_status absorb_launch(const mla_dims* dims, int bf, int32_t n_q, const void* q_c, const void* q_r,
                                 const int32_t* q_pos, const void* w_uk, void* q_lat, void* q_lat_lo, hipStream_t s,
-                                const char* who, int q_r_f32 = 0) {
+                                const char* who, int q_r_f32 = 0, const mla::AppendArgs* fused_append = nullptr) {
   mla::AbsorbArgs a{};
+  if (fused_append) {  // the caller checked that the fused bf16 kernel runs
+    a.app_c = fused_append->c_kv;
+    a.app_k = fused_append->k_r;
+    a.app_pos = fused_append->pos;
+    a.app_row = fused_append->row;
+    a.app_cache = fused_append->cache;
+    a.app_n = fused_append->n_tok;
+  }
   a.q_r_f32 = q_r_f32;
   a.q_c = q_c;
   a.w_uk = w_uk;
@@ -309,6 +317,44 @@ mla_status mla_absorb_q(const mla_dims* dims, mla_dtype dtype, int32_t n_q, cons
   if (!q_c || !q_r || !q_pos || !w_uk || !q_lat) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
   return absorb_launch(dims, dtype == MLA_BF16, n_q, q_c, q_r, q_pos, w_uk, q_lat, q_lat_lo,
                        static_cast<hipStream_t>(stream), "mla_absorb_q");
+}
+
+mla_status mla_append_absorb(const mla_dims* dims, mla_dtype dtype, int32_t n_tok, const void* c_kv,
+                             const void* k_r, const int32_t* pos, const int64_t* row, void* cache, int32_t n_q,
+                             const void* q_c, const void* q_r, const int32_t* q_pos, const void* w_uk, void* q_lat,
+                             void* q_lat_lo, void* stream) {
+  mla_status st = check_dims(dims, dtype);
+  if (st != MLA_OK) return st;
+  st = check_lo(dtype, q_lat_lo);
+  if (st != MLA_OK) return st;
+  if (n_tok < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "n_tok=%d < 0", n_tok);
+  if (n_q < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "n_q=%d < 0", n_q);
+  if (n_q > 65535 * 256) return fail(MLA_ERR_INVALID_ARGUMENT, "n_q=%d too large", n_q);
+  if (n_tok > 0 && (!c_kv || !k_r || !pos || !row || !cache))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (n_q > 0 && (!q_c || !q_r || !q_pos || !w_uk || !q_lat))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int bf = dtype == MLA_BF16;
+  mla::AppendArgs ap{};
+  ap.c_kv = c_kv;
+  ap.k_r = k_r;
+  ap.pos = pos;
+  ap.row = row;
+  ap.cache = cache;
+  ap.n_tok = n_tok;
+  ap.d_c = dims->d_c;
+  ap.d_r = dims->d_hR;
+  fill_rope(dims, ap.rope);
+  if (n_q > 0 && n_tok > 0 && mla::absorb_fuses_rope(bf, dims->d_c, dims->d_h, dims->d_hR))
+    return absorb_launch(dims, bf, n_q, q_c, q_r, q_pos, w_uk, q_lat, q_lat_lo, s, "mla_append_absorb", 0, &ap);
+  // other shapes: the two launches of mla_append_kv and mla_absorb_q
+  if (n_tok > 0) {
+    st = hip_status(mla::launch_append(ap, bf, s), "mla_append_absorb");
+    if (st != MLA_OK) return st;
+  }
+  if (n_q == 0) return MLA_OK;
+  return absorb_launch(dims, bf, n_q, q_c, q_r, q_pos, w_uk, q_lat, q_lat_lo, s, "mla_append_absorb");
 }
 
 // ---- the query path from hidden states: c^Q = RMSNorm(W^DQ h), [q^C ; q^R] =

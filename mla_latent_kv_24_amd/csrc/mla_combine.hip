@@ -22,11 +22,14 @@ constexpr int ZSTRIDE = 1040;        // bytes per staged z row (512 bf16 + 16 B 
 //   out[n][d] = sum_c (hi[n][c] + lo[n][c]) * w_uv[h][d][c]
 // A = z rows from LDS (c contiguous; rows past the block's queries are never
 // stored), B = w_uv rows from global (c contiguous).
-// The kernel is a stream of the partials and of W^UV: the wave's whole W^UV
-// slice (32 rows x 512 columns, 128 VGPRs) is requested first, so that it
-// arrives while the partials are combined; the split weights are formed by all
-// threads (8 per query row); the partial loads of G splits x 16 / G row chunks
-// are in flight together (G = 4 for few splits, 16 for many).
+// The kernel is a stream of the partials and of W^UV.  The split weights are
+// formed by all threads (8 per query row).  With at most G = 4 splits a
+// thread's first two row chunks of partials are requested, then the wave's
+// whole W^UV slice (32 rows x 512 columns, 128 VGPRs), which arrives while the
+// partials are combined; two batches of two row chunks stay in flight (one
+// combined while the next lands).  With more splits (G = 16) W^UV comes first
+// and the partial loads of G splits x 16 / G row chunks are in flight
+// together.
 // ------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int qb) {
@@ -45,8 +48,10 @@ __global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int
   const int d = 32 * w + (l & 31);
   const uint16_t* wrow = static_cast<const uint16_t*>(a.w_uv) + (static_cast<int64_t>(h) * D_H + d) * D_C + 8 * g;
   u32x4 bw[KS];
+  auto load_w = [&]() {
 #pragma unroll
-  for (int s = 0; s < KS; ++s) bw[s] = *reinterpret_cast<const u32x4*>(wrow + 16 * s);
+    for (int s = 0; s < KS; ++s) bw[s] = *reinterpret_cast<const u32x4*>(wrow + 16 * s);
+  };
 
   // ---- split weights exp(lse_s - LSE): thread (row r, phase p) covers splits
   // p, p+8, ...; max and sum are reduced over the row's 8 adjacent lanes
@@ -77,47 +82,85 @@ __global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int
   // tid takes units tid + 256 j; consecutive lanes read consecutive 16 B
   const int units = rows * (D_C / 4);
   const int64_t zs = static_cast<int64_t>(a.n_h) * D_C;  // split stride (floats)
-  for (int j0 = 0; j0 < 16; j0 += UB) {
-    if (tid + 256 * j0 >= units) break;
-    f32x4 acc[UB];
+  auto emit = [&](int u, const f32x4& acc) {
+    if (u >= units) return;
+    const int r = u >> 7, c4 = 4 * (u & 127);
+    if (a.out_latent)
+      *reinterpret_cast<f32x4*>(a.out_latent + (static_cast<int64_t>(n0 + r) * a.n_h + h) * D_C + c4) = acc;
+    uint16_t hi4[4], lo4[4];
 #pragma unroll
-    for (int i = 0; i < UB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < S; s0 += G) {
-      f32x4 v[UB][G];
-#pragma unroll
-      for (int i = 0; i < UB; ++i) {
-        const int u = tid + 256 * (j0 + i);
-        const float* zp = a.z_part + ((static_cast<int64_t>(n0 + (u >> 7)) * S + s0) * a.n_h + h) * D_C + 4 * (u & 127);
-#pragma unroll
-        for (int gg = 0; gg < G; ++gg)
-          v[i][gg] = (u < units && s0 + gg < S) ? *reinterpret_cast<const f32x4*>(zp + gg * zs)
-                                                : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int i = 0; i < UB; ++i) {
-        const int r = (tid + 256 * (j0 + i)) >> 7;
-#pragma unroll
-        for (int gg = 0; gg < G; ++gg)
-          if (s0 + gg < S) acc[i] += wts[r & 31][s0 + gg] * v[i][gg];
-      }
+    for (int e = 0; e < 4; ++e) {
+      hi4[e] = f32_to_bf16(acc[e]);
+      lo4[e] = f32_to_bf16(acc[e] - bf16_to_f32(hi4[e]));
     }
+    *reinterpret_cast<uint2*>(zhi + r * ZSTRIDE + 2 * c4) =
+        make_uint2(hi4[0] | (static_cast<uint32_t>(hi4[1]) << 16), hi4[2] | (static_cast<uint32_t>(hi4[3]) << 16));
+    *reinterpret_cast<uint2*>(zlo + r * ZSTRIDE + 2 * c4) =
+        make_uint2(lo4[0] | (static_cast<uint32_t>(lo4[1]) << 16), lo4[2] | (static_cast<uint32_t>(lo4[3]) << 16));
+  };
+  if (G == 4 && S <= G) {
+    // all splits of a unit in one batch of PB units; two batches in flight
+    constexpr int PB = 2;
+    f32x4 va[PB][G], vb[PB][G];
+    auto load_b = [&](int j0, f32x4 (&v)[PB][G]) {
 #pragma unroll
-    for (int i = 0; i < UB; ++i) {
-      const int u = tid + 256 * (j0 + i);
-      if (u >= units) continue;
-      const int r = u >> 7, c4 = 4 * (u & 127);
-      if (a.out_latent)
-        *reinterpret_cast<f32x4*>(a.out_latent + (static_cast<int64_t>(n0 + r) * a.n_h + h) * D_C + c4) = acc[i];
-      uint16_t hi4[4], lo4[4];
+      for (int i = 0; i < PB; ++i) {
+        const int u = tid + 256 * (j0 + i);
+        const float* zp = a.z_part + ((static_cast<int64_t>(n0 + (u >> 7)) * S) * a.n_h + h) * D_C + 4 * (u & 127);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hi4[e] = f32_to_bf16(acc[i][e]);
-        lo4[e] = f32_to_bf16(acc[i][e] - bf16_to_f32(hi4[e]));
+        for (int gg = 0; gg < G; ++gg)
+          v[i][gg] = (u < units && gg < S) ? *reinterpret_cast<const f32x4*>(zp + gg * zs) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      *reinterpret_cast<uint2*>(zhi + r * ZSTRIDE + 2 * c4) =
-          make_uint2(hi4[0] | (static_cast<uint32_t>(hi4[1]) << 16), hi4[2] | (static_cast<uint32_t>(hi4[3]) << 16));
-      *reinterpret_cast<uint2*>(zlo + r * ZSTRIDE + 2 * c4) =
-          make_uint2(lo4[0] | (static_cast<uint32_t>(lo4[1]) << 16), lo4[2] | (static_cast<uint32_t>(lo4[3]) << 16));
+    };
+    auto fold_b = [&](int j0, const f32x4 (&v)[PB][G]) {
+#pragma unroll
+      for (int i = 0; i < PB; ++i) {
+        const int u = tid + 256 * (j0 + i);
+        const int r = u >> 7;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg)
+          if (gg < S) acc += wts[r & 31][gg] * v[i][gg];
+        emit(u, acc);
+      }
+    };
+    load_b(0, va);
+    load_w();
+#pragma unroll
+    for (int j0 = 0; j0 < 16; j0 += 2 * PB) {
+      if (j0 + PB < 16) load_b(j0 + PB, vb);
+      fold_b(j0, va);
+      if (j0 + 2 * PB < 16) load_b(j0 + 2 * PB, va);
+      fold_b(j0 + PB, vb);
+    }
+  } else {
+    load_w();
+    for (int j0 = 0; j0 < 16; j0 += UB) {
+      if (tid + 256 * j0 >= units) break;
+      f32x4 acc[UB];
+#pragma unroll
+      for (int i = 0; i < UB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < S; s0 += G) {
+        f32x4 v[UB][G];
+#pragma unroll
+        for (int i = 0; i < UB; ++i) {
+          const int u = tid + 256 * (j0 + i);
+          const float* zp = a.z_part + ((static_cast<int64_t>(n0 + (u >> 7)) * S + s0) * a.n_h + h) * D_C + 4 * (u & 127);
+#pragma unroll
+          for (int gg = 0; gg < G; ++gg)
+            v[i][gg] = (u < units && s0 + gg < S) ? *reinterpret_cast<const f32x4*>(zp + gg * zs)
+                                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int i = 0; i < UB; ++i) {
+          const int r = (tid + 256 * (j0 + i)) >> 7;
+#pragma unroll
+          for (int gg = 0; gg < G; ++gg)
+            if (s0 + gg < S) acc[i] += wts[r & 31][s0 + gg] * v[i][gg];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < UB; ++i) emit(tid + 256 * (j0 + i), acc[i]);
     }
   }
   __syncthreads();

@@ -64,6 +64,15 @@ struct AbsorbArgs {
   const int32_t* q_pos;  // [n_q]
   RopeTable rope;
   int32_t q_r_f32;       // fused bf16 kernel: q_r holds fp32 values instead
+  // A1 in the same launch (fused bf16 kernel only; app_n = 0: none): the bf16
+  // cache rows cache[app_row[t]] = [app_c[t] ; RoPE(app_k[t], app_pos[t])],
+  // t < app_n, written by the launch's workgroups besides their A2 work
+  const void* app_c;        // [app_n][d_c]
+  const void* app_k;        // [app_n][d_r] (pre-RoPE)
+  const int32_t* app_pos;   // [app_n]
+  const int64_t* app_row;   // [app_n]
+  void* app_cache;          // [*][d_c + d_r]
+  int32_t app_n;
 };
 // true when launch_absorb also writes the RoPE part (no launch_rope_q needed)
 bool absorb_fuses_rope(int bf16, int d_c, int d_h, int d_r);

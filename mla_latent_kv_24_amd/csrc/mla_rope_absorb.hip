@@ -99,8 +99,38 @@ constexpr int ABS_WSTRIDE = ABS_COLS * 2 + 64;     // bytes per staged W row (bf
 constexpr int ABS_SSTRIDE = ABS_COLS * 4 + 16;     // bytes per staged fp32 output row
 constexpr int ABS_PAIRS = D_R / 2 / ABS_PARTS;     // RoPE pairs rotated per workgroup
 
-__device__ __forceinline__ uint32_t bf16_pair(float lo_elem, float hi_elem) {
-  return static_cast<uint32_t>(f32_to_bf16(lo_elem)) | (static_cast<uint32_t>(f32_to_bf16(hi_elem)) << 16);
+// Fused A1 (mla_append_absorb): the workgroup with linear index k writes the
+// appended rows t = k, k + (grid size), ...; per row, threads 0..63 copy the
+// latent as 16-B pieces and threads 64..95 rotate one RoPE pair each (fp64
+// angle, as append_kernel).  The first row's loads are issued before the A2
+// loads, so that they land while the slab streams in.
+struct AppendPiece {
+  uint4 c;       // latent piece (threads 0..63)
+  uint32_t k;    // pre-RoPE pair (threads 64..95)
+  int32_t pos;
+};
+__device__ __forceinline__ AppendPiece append_load(const AbsorbArgs& a, int t, int tid) {
+  AppendPiece p{make_uint4(0, 0, 0, 0), 0u, 0};
+  if (tid < D_C / 8) {
+    p.c = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.app_c) + static_cast<int64_t>(t) * D_C + 8 * tid);
+  } else if (tid < D_C / 8 + D_R / 2) {
+    const int k = tid - D_C / 8;
+    p.k = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.app_k) + static_cast<int64_t>(t) * D_R + 2 * k);
+    p.pos = a.app_pos[t];
+  }
+  return p;
+}
+__device__ __forceinline__ void append_store(const AbsorbArgs& a, int t, int tid, const AppendPiece& p) {
+  uint16_t* dst = static_cast<uint16_t*>(a.app_cache) + a.app_row[t] * ROWE;
+  if (tid < D_C / 8) {
+    *reinterpret_cast<uint4*>(dst + 8 * tid) = p.c;
+  } else if (tid < D_C / 8 + D_R / 2) {
+    const int k = tid - D_C / 8;
+    float y0, y1;
+    rope_pair(bf16_to_f32(static_cast<uint16_t>(p.k & 0xffffu)), bf16_to_f32(static_cast<uint16_t>(p.k >> 16)),
+              p.pos, a.rope.theta[k], y0, y1);
+    *reinterpret_cast<uint32_t*>(dst + D_C + 2 * k) = pack_bf16x2(y0, y1);
+  }
 }
 
 __global__ __launch_bounds__(256, 2) void absorb_mfma_kernel(AbsorbArgs a) {
@@ -114,6 +144,12 @@ __global__ __launch_bounds__(256, 2) void absorb_mfma_kernel(AbsorbArgs a) {
   const uint16_t* qc = static_cast<const uint16_t*>(a.q_c);
   uint16_t* qout = static_cast<uint16_t*>(a.q_lat);
   uint16_t* qlo = static_cast<uint16_t*>(a.q_lat_lo);   // NULL: hi only
+
+  // ---- fused A1: this workgroup's first appended row, loads in flight
+  const int wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int nwg = gridDim.x * gridDim.y * gridDim.z;
+  AppendPiece app{};
+  if (wg < a.app_n) app = append_load(a, wg, tid);
 
   // ---- issue: W^UK slab (16 chunks of 16 B per thread) and the first query block
   constexpr int WCH = ABS_COLS / 8;             // 16-B chunks per W row of the slab
@@ -177,9 +213,15 @@ __global__ __launch_bounds__(256, 2) void absorb_mfma_kernel(AbsorbArgs a) {
       const float y0 = x0 * cf - x1 * sf, y1 = x0 * sf + x1 * cf;
       const float h0 = bf16_to_f32(f32_to_bf16(y0)), h1 = bf16_to_f32(f32_to_bf16(y1));
       const int64_t e = (static_cast<int64_t>(n) * a.n_h + h) * ROWE + D_C + 2 * k;
-      *reinterpret_cast<uint32_t*>(qout + e) = bf16_pair(y0, y1);
-      if (qlo) *reinterpret_cast<uint32_t*>(qlo + e) = bf16_pair(y0 - h0, y1 - h1);
+      *reinterpret_cast<uint32_t*>(qout + e) = pack_bf16x2(y0, y1);
+      if (qlo) *reinterpret_cast<uint32_t*>(qlo + e) = pack_bf16x2(y0 - h0, y1 - h1);
     }
+  }
+  // fused A1: the first row (its loads have landed with the slab's), then any
+  // further rows of this workgroup (more rows than workgroups)
+  if (wg < a.app_n) {
+    append_store(a, wg, tid, app);
+    for (int t = wg + nwg; t < a.app_n; t += nwg) append_store(a, t, tid, append_load(a, t, tid));
   }
   __syncthreads();
 
@@ -223,10 +265,10 @@ __global__ __launch_bounds__(256, 2) void absorb_mfma_kernel(AbsorbArgs a) {
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          hw[e] = bf16_pair(v[2 * e], v[2 * e + 1]);
+          hw[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
           const float h0 = bf16_to_f32(static_cast<uint16_t>(hw[e] & 0xffffu));
           const float h1 = bf16_to_f32(static_cast<uint16_t>(hw[e] >> 16));
-          lw[e] = bf16_pair(v[2 * e] - h0, v[2 * e + 1] - h1);
+          lw[e] = pack_bf16x2(v[2 * e] - h0, v[2 * e + 1] - h1);
         }
         const int64_t o = (static_cast<int64_t>(n) * a.n_h + h) * ROWE + half_c * ABS_COLS + 8 * k;
         *reinterpret_cast<uint4*>(qout + o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);

@@ -117,6 +117,15 @@ class DecodeState:
     def absorb(self):
         api.absorb_q(self.d, self.q_c, self.q_r, self.q_pos, self.w_uk, self.q_lat)
 
+    def append_absorb(self):
+        """A1 and A2 of the step in one call (one launch on the bf16 fast path)."""
+        if self.fp8:
+            self.append_new()
+            self.absorb()
+        else:
+            api.append_absorb(self.d, self.new_c, self.new_k, self.new_pos, self.new_rows, self.cache,
+                              self.q_c, self.q_r, self.q_pos, self.w_uk, self.q_lat)
+
     def attention(self, splits=None, z_part=None, lse_part=None):
         S = self.splits if splits is None else splits
         z = self.z_part if z_part is None else z_part
@@ -137,9 +146,8 @@ class DecodeState:
                             self.w_uv, self.out, self.out_latent)
 
     def step(self):
-        """One decode step of one layer: append the new rows, absorb, attend, combine."""
-        self.append_new()
-        self.absorb()
+        """One decode step of one layer: append the new rows and absorb (one call), attend, combine."""
+        self.append_absorb()
         self.attention()
         self.combine()
         return self.out

@@ -69,6 +69,22 @@ def test_dims_validation():
         b"yarn" not in lib.mla_last_error()
 
 
+def test_append_absorb_validation():
+    """mla_append_absorb checks what mla_append_kv and mla_absorb_q check; an empty
+    half may pass NULL pointers, a non-empty one may not."""
+    lib = api.raw()
+    d = ctypes.byref(api.dims(128))
+    f = lib.mla_append_absorb
+    assert f(d, 1, 0, None, None, None, None, None, 0, None, None, None, None, None, None, None) == 0  # both empty
+    assert f(d, 1, -1, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert f(d, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert f(d, 1, 2, None, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert f(d, 1, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, None, None, None) == 1  # q_lat NULL
+    assert f(d, 0, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1  # lo with f32
+    assert f(d, 7, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1  # dtype
+    assert f(None, 1, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+
+
 def test_null_and_size_validation():
     lib = api.raw()
     d = ctypes.byref(api.dims(128))

@@ -95,6 +95,61 @@ def test_absorb_q(api, dtype, n_h, n_q):
         assert torch.equal(q_hi.hi, q_lat.hi)
 
 
+# ------------------------------------------- A1 + A2 in one call (one launch)
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy() if t.dtype == torch.bfloat16 else t.view(torch.int32).cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype,n_h,n_tok,n_q,lo", [
+    ("bf16", 128, 64, 64, False),    # the V2 decode step: one row per sequence
+    ("bf16", 128, 600, 3, True),     # more rows than the launch's 512 workgroups
+    ("bf16", 16, 100, 37, True),     # 64 workgroups: several rows each
+    ("bf16", 16, 32, 32, False),
+    ("bf16", 128, 0, 7, True),       # empty halves
+    ("bf16", 128, 5, 0, False),
+    ("bf16", 8, 9, 5, True),         # no fused kernel: the two launches
+    ("f32", 16, 9, 4, False)])
+def test_append_absorb_matches_separate_calls(api, dtype, n_h, n_tok, n_q, lo):
+    """mla_append_absorb writes the cache rows and absorbed queries of
+    mla_append_kv followed by mla_absorb_q, bit for bit."""
+    cap = 1000
+    c = W.random_storage(51, (max(n_tok, 1), 512), dtype)[:n_tok]
+    k = W.random_storage(52, (max(n_tok, 1), 64), dtype)[:n_tok]
+    pos = W.random_ints(53, 0, 131072, max(n_tok, 1)).astype(np.int32)[:n_tok]
+    rows = np.random.default_rng(54).permutation(cap)[:n_tok].astype(np.int64)
+    q_c = W.random_storage(55, (max(n_q, 1), n_h, 128), dtype)[:n_q]
+    q_r = W.random_storage(56, (max(n_q, 1), n_h, 64), dtype)[:n_q]
+    qpos = W.random_ints(57, 0, 131072, max(n_q, 1)).astype(np.int32)[:n_q]
+    w_uk = W.random_storage(58, (n_h, 128, 512), dtype, 512 ** -0.5)
+    d = api.dims(n_h)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    t = lambda a: dev(a, dtype)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    outs = []
+    for fused in (False, True):
+        cache = torch.full((cap, 576), float("nan"), dtype=tdt, device="cuda")
+        q_lat = api.q_lat_empty(d, tdt, n_q, lo=lo)
+        q_lat.hi.fill_(float("nan"))
+        if q_lat.lo is not None:
+            q_lat.lo.fill_(float("nan"))
+        args = (t(c), t(k), i32(pos), i32(rows))
+        if fused:
+            api.append_absorb(d, *args, cache, t(q_c), t(q_r), i32(qpos), t(w_uk), q_lat)
+        else:
+            if n_tok:
+                api.append_kv(d, *args, cache)
+            if n_q:
+                api.absorb_q(d, t(q_c), t(q_r), i32(qpos), t(w_uk), q_lat)
+        torch.cuda.synchronize()
+        outs.append((_bits(cache), _bits(q_lat.hi), None if q_lat.lo is None else _bits(q_lat.lo)))
+    (c0, h0, l0), (c1, h1, l1) = outs
+    assert np.array_equal(c0, c1)
+    assert np.array_equal(h0, h1)
+    assert (l0 is None and l1 is None) or np.array_equal(l0, l1)
+    if n_tok:   # and the rows are the appended ones (the rest stays NaN)
+        assert np.array_equal(c1[rows][:, :512], c.view(np.int16) if dtype == "bf16" else c.view(np.int32))
+
+
 # ---------------------------------------------------- A3 split-KV partials
 def _partials_case(api, dtype, n_h, lens, splits, stride=None, seed=20, tol=None):
     B = len(lens)
