@@ -678,7 +678,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
 
   // ---- tile DMA: LDS chunk f = tid + 256 i of a tile receives global chunk
   // (t, p ^ swz(t)) with (t, p) = (f / 72, f % 72).  Each thread keeps its nine
-  // source chunk indices in its own LDS slots (live in registers across the
+  // source chunk byte offsets in its own LDS slots (live in registers across the
   // loop they would be spilled, and a spill reload is a VMEM access that fences
   // the DMAs); only the thread itself reads them, so no barrier is needed.
   const uint8_t* gsplit =
@@ -709,9 +709,9 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
                       __builtin_amdgcn_readfirstlane(static_cast<int>(rows * ROWB)), 0x00020000};
     return rs;
   };
-  auto dma = [&](int64_t it, const i32x4& rs, int i, uint32_t chunk) {
-    dma16(lds_w + static_cast<uint32_t>((it & (NBUF - 1)) * TILE_BYTES) + 4096u * i,
-          static_cast<int>(chunk << 4), rs, 0);
+  // (a chunk's byte offset in the tile, chunk << 4 < 36,864, fits the u16 slot)
+  auto dma = [&](int64_t it, const i32x4& rs, int i, uint32_t off) {
+    dma16(lds_w + static_cast<uint32_t>((it & (NBUF - 1)) * TILE_BYTES) + 4096u * i, static_cast<int>(off), rs, 0);
   };
   {
     uint32_t ch[LOADS];
@@ -719,7 +719,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
     for (int i = 0; i < LOADS; ++i) {
       const int f = tid + 256 * i;
       const int t = f / 72, p = f - 72 * t;
-      ch[i] = static_cast<uint32_t>(72 * t + (p ^ swz(t)));
+      ch[i] = static_cast<uint32_t>(72 * t + (p ^ swz(t))) << 4;
       otab[i * 256 + tid] = static_cast<uint16_t>(ch[i]);
     }
 #pragma unroll
@@ -863,6 +863,12 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
 #else
 #define MLA_TICK(k)
 #endif
+  // this lane's P^T slot reads: one base register, offsets 1024 i in the
+  // instruction (the empty asm keeps the compiler from folding P_OFF, past the
+  // 16-bit offset field, into each address)
+  int pslot_off = P_OFF + 16 * l;
+  asm volatile("" : "+v"(pslot_off));
+  const uint8_t* pslot = smem + pslot_off;
   auto step = [&](int64_t t, f32x16& sx, f32x16& sn) {
     // tile t+1 must have landed (only the nine loads of tile t+2 may still be
     // in flight); every wave is done with tile t-1, whose buffer takes tile t+3
@@ -941,7 +947,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
       }
       u32x4 pv[8];  // [hb][u] at 2 hb + u
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pv[i] = *reinterpret_cast<const u32x4*>(smem + P_OFF + 1024 * i + 16 * l);
+      for (int i = 0; i < 8; ++i) pv[i] = *reinterpret_cast<const u32x4*>(pslot + 1024 * i);
       const int valid1 = tile_valid(t + 1);
       bf16x8 va[2][2];
       va[0][0] = va0;
@@ -966,8 +972,15 @@ __global__ __launch_bounds__(256, 1) void splitkv_wide_kernel(SplitArgs a) {
   for (int64_t t = 0; t < ntiles; ++t) {
     step(t, sA, sB);
     MLA_TICK(3);
+    // (as eight 64-bit moves of register pairs)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) asm volatile("v_mov_b32 %0, %1" : "=v"(sA[j]) : "v"(sB[j]));
+    for (int j = 0; j < 8; ++j) {
+      f32x2_t d;
+      const f32x2_t v = {sB[2 * j], sB[2 * j + 1]};
+      asm volatile("v_mov_b64 %0, %1" : "=v"(d) : "v"(v));
+      sA[2 * j] = d[0];
+      sA[2 * j + 1] = d[1];
+    }
   }
 
   // ---- finalize: lse per head from its score wave; Z normalised by every
