@@ -9,7 +9,7 @@
 // A chunk of queries shares every key, so per (key, query, head) the score
 // is a 192-deep product and the value a 128-wide one: 640 multiply-adds
 // against the absorbed form's 1,088.  Two kernels:
-//   expand_kv_kernel: per (sequence, 128-row block, 8 heads) an MFMA GEMM
+//   expand_kv_kernel: per (sequence, 128-row block, 8 to 32 heads) an MFMA GEMM
 //     [k^C; v^C] = [U^K_i; U^V_i] c^T with the rows' c staged in LDS; results
 //     leave as hi/lo bf16 rows that keep the cache-row geometry (the layout
 //     is in mla_common.h), with k^R copied in;
@@ -46,38 +46,53 @@ __device__ __forceinline__ void pf_mfma_vv(f32x16& acc, const bf16x8& a, const b
 __device__ __forceinline__ void pf_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 constexpr int XB_ROWS = 128;  // rows per expansion workgroup
-constexpr int XB_HEADS = 8;   // heads per expansion workgroup
-constexpr int XPF = 8;        // expansion: W operand prefetch depth (k-steps)
+constexpr int XB_HEADS = 8;   // heads per head group (a workgroup takes 1, 2 or 4 groups)
+constexpr int XB_WAVES = 8;   // expansion waves (two per SIMD)
+constexpr int XPF = 4;        // expansion: W operand prefetch depth (k-steps)
 constexpr int PF_WAVES = 8;   // attention waves per workgroup (two per SIMD)
 constexpr int PF_QBW = 1;     // query blocks of 32 per attention wave
 constexpr int PQ = 32 * PF_QBW * PF_WAVES;  // queries per attention workgroup (256)
 static_assert(XB_ROWS == XROWS_ALIGN, "expanded rows come in whole expansion blocks");
 
 // ------------------------------------------------------------------------
-// Expansion.  Wave w computes output dims 64w .. 64w+63 of [k^C | v^C]
-// (256 dims) for all 128 rows: A = W rows (U^K or U^V, d_c contiguous, from
-// global), B = c^T (rows from LDS), 2 x 4 blocks of 32 x 32 accumulators.
+// Expansion.  A workgroup stages its 128 rows' c in LDS once and expands
+// them for a range of 8, 16 or 32 heads.  Eight waves, two per SIMD: wave w
+// computes output dims 64 (w & 3) .. +63 of [k^C | v^C] (256 dims) for all
+// 128 rows of every other head of the range (parity w >> 2), so one SIMD
+// runs two heads' products side by side: A = W rows (U^K or U^V, d_c
+// contiguous, from global), B = c^T (rows from LDS), 2 x 4 blocks of 32 x 32
+// accumulators.
 // ------------------------------------------------------------------------
 template <bool PAGED>
-__global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
+__global__ __launch_bounds__(64 * XB_WAVES, 1) void expand_kv_kernel(ExpandArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[XB_ROWS * D_C * 2];  // c rows, 1024 B each
   const int tid = threadIdx.x, l = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = wv & 3, hp = wv >> 2;
   const int g = l >> 5, l32 = l & 31;
   const int b = blockIdx.z;
-  // Workgroups go to the 8 XCDs round robin by linear index.  With the head
-  // groups a multiple of 8, XCD x takes head groups x, x + 8, ... one at a
-  // time over all row blocks, so the 32 workgroups that an XCD runs together
-  // share one head group's W^UK and W^UV rows (2 MB) in its L2, instead of
-  // four groups' 8 MB streaming from the memory-side cache.
+  // Workgroups go to the 8 XCDs round robin by linear index.  The mapping
+  // below gives the workgroups that an XCD runs together one head range, so
+  // that they share its W^UK and W^UV rows in the XCD's L2 instead of several
+  // ranges streaming from the memory-side cache: with the head ranges a
+  // multiple of 8, XCD x takes ranges x, x + 8, ... over all row blocks; with
+  // 8 / gy XCDs per range (gy ranges), each takes a share of the row blocks.
+  const int nhw = a.heads_per_wg;  // heads h0 .. h0 + nhw - 1, one head group at a time
+  const int gx = gridDim.x, gy = gridDim.y;
   int rb = blockIdx.x, hg = blockIdx.y;
-  if (gridDim.y % 8 == 0) {
-    const int k = blockIdx.x + gridDim.x * blockIdx.y;
+  if (gy % 8 == 0) {
+    const int k = blockIdx.x + gx * blockIdx.y;
     const int x = k % 8, j = k / 8;
-    hg = x + 8 * (j / gridDim.x);
-    rb = j % gridDim.x;
+    hg = x + 8 * (j / gx);
+    rb = j % gx;
+  } else if (8 % gy == 0 && gx % (8 / gy) == 0) {
+    // 8 / gy XCDs share a head range, each over its own share of the row blocks
+    const int k = blockIdx.x + gx * blockIdx.y;
+    const int x = k % 8, j = k / 8;
+    hg = x % gy;
+    rb = (x / gy) * (gx / (8 / gy)) + j;
   }
-  const int h0 = hg * XB_HEADS;
+  const int h0 = hg * nhw;
   const int64_t row0 = static_cast<int64_t>(rb) * XB_ROWS;
   // the prefix clamped to [0, max_len - chunk] exactly as the attention kernel
   // clamps it, so that every row the attention reads is expanded
@@ -92,7 +107,7 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
                                  ROWB, ok);
   };
 
-  // ---- c rows -> LDS.  LDS chunk f = 256 i + tid is row 4 i + w, slot l, and
+  // ---- c rows -> LDS.  LDS chunk f = 512 i + tid is row 8 i + wv, slot l, and
   // holds the row's global chunk l ^ (row & 15): the swizzle spreads the 16
   // rows that one pass of an operand read touches over distinct banks (with
   // row & 7, rows r and r + 8 met in the same banks).  The block's rows
@@ -104,7 +119,7 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
   {
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
                               (__attribute__((address_space(3))) uint8_t*)smem)) +
-                          1024u * static_cast<uint32_t>(w);
+                          1024u * static_cast<uint32_t>(wv);
 #pragma unroll
     for (int k = 0; k < XB_ROWS / 32; ++k) {
       const int rows = max(min(nrows - 32 * k, 32), 0);
@@ -115,24 +130,23 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
                         __builtin_amdgcn_readfirstlane(static_cast<int>((ga >> 32) & 0xffffu)),
                         __builtin_amdgcn_readfirstlane(ok ? rows * ROWB : 0), 0x00020000};
 #pragma unroll
-      for (int i = 8 * k; i < 8 * k + 8; ++i) {
-        const int r = 4 * i + w;  // row of the block; 32 k <= r < 32 k + 32
-        dma16(lds0 + 4096u * i, (r - 32 * k) * ROWB + 16 * (l ^ (r & 15)), rs, 0);
+      for (int i = 4 * k; i < 4 * k + 4; ++i) {
+        const int r = 8 * i + wv;  // row of the block; 32 k <= r < 32 k + 32
+        dma16(lds0 + 8192u * i, (r - 32 * k) * ROWB + 16 * (l ^ (r & 15)), rs, 0);
       }
     }
   }
 
   // ---- k^R (the last d_hR elements of the cache row) into each head's row
   uint16_t* xb = static_cast<uint16_t*>(a.x) + (static_cast<int64_t>(b) * a.n_h + h0) * a.rows_cap * ROWE;
-  for (int idx = tid; idx < XB_ROWS * 8; idx += 256) {
+  for (int idx = tid; idx < XB_ROWS * 8; idx += 64 * XB_WAVES) {
     const int r = idx >> 3, c = idx & 7;
     if (r < nrows) {
       bool ok;
       const uint64_t ga = row_at(row0 + r, ok);
       const u32x4 nan8 = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
       const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(ga + 2 * D_C + 16 * c) : nan8;
-#pragma unroll
-      for (int hh = 0; hh < XB_HEADS; ++hh)
+      for (int hh = 0; hh < nhw; ++hh)
         *reinterpret_cast<u32x4*>(xb + (hh * a.rows_cap + row0 + r) * ROWE + D_C + 8 * c) = v;
     }
   }
@@ -160,8 +174,8 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
 #pragma unroll
       for (int db = 0; db < 2; ++db) wa[s][db] = *reinterpret_cast<const u32x4*>(wr + 32 * db * D_C + 16 * s);
   };
-  w_first(0);
-  for (int hh = 0; hh < XB_HEADS; ++hh) {
+  w_first(hp);
+  for (int hh = hp; hh < nhw; hh += 2) {
     const int h = h0 + hh;
     const uint16_t* wr = w_rows(hh);
     f32x16 acc[2][4];
@@ -186,7 +200,7 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(ExpandArgs a) {
         acc[1][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), bv, acc[1][rb], 0, 0, 0);
       }
     }
-    if (hh + 1 < XB_HEADS) w_first(hh + 1);
+    if (hh + 2 < nhw) w_first(hh + 2);
     // lane l holds dims 8 jq + 4 g + (0..3) of block (db) for row 32 rb + l32.
     // One v_permlane32_swap per pair of values (jq = 2q and 2q + 1) trades the
     // lane pair (l, l + 32)'s halves, after which lane g holds run q: the 8
@@ -350,6 +364,10 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
         if constexpr (PRECISE)
           qrl[k][s][pp] = pack_bf16x2(y0 - __uint_as_float(hi << 16), y1 - __uint_as_float(hi & 0xffff0000u));
       }
+      // one AGPR tuple each from here on (built a lane pair at a time, they
+      // were otherwise regathered before every product)
+      asm volatile("" : "+a"(qrh[k][s]));
+      if constexpr (PRECISE) asm volatile("" : "+a"(qrl[k][s]));
     }
   }
   vm_wait<0>();  // queries and the first tiles resident: the loop carries no compiler waits
@@ -556,11 +574,19 @@ hipError_t launch_prefill_unabsorbed(const ExpandArgs& e_in, const PrefillArgs& 
   // keys lie below precise_below + PQ - 1 (every row when all workgroups are)
   const int64_t lo_rows = static_cast<int64_t>(p.precise_below) + PQ;
   e.lo_rows = static_cast<int32_t>(lo_rows < 0x7fffffff ? lo_rows : 0x7fffffff);
-  const dim3 g1(static_cast<unsigned>(e.rows_cap / XB_ROWS), e.n_h / XB_HEADS, e.batch);
+  // up to 4 head groups per workgroup (c rows loaded once for all of them)
+  // while the grid still fills one round of the compute units
+  const int nhg = e.n_h / XB_HEADS;
+  const int64_t nrb = e.rows_cap / XB_ROWS;
+  int hpw = 1;
+  for (int c = 4; c >= 2; c /= 2)
+    if (nhg % c == 0 && nrb * (nhg / c) * e.batch >= 256) { hpw = c; break; }
+  e.heads_per_wg = XB_HEADS * hpw;
+  const dim3 g1(static_cast<unsigned>(nrb), nhg / hpw, e.batch);
   if (e.block_table)
-    expand_kv_kernel<true><<<g1, 256, 0, st>>>(e);
+    expand_kv_kernel<true><<<g1, 64 * XB_WAVES, 0, st>>>(e);
   else
-    expand_kv_kernel<false><<<g1, 256, 0, st>>>(e);
+    expand_kv_kernel<false><<<g1, 64 * XB_WAVES, 0, st>>>(e);
   const hipError_t r = hipGetLastError();
   if (r != hipSuccess) return r;
   const dim3 g2((p.chunk + PQ - 1) / PQ, p.n_h, p.batch);
