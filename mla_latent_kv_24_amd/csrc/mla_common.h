@@ -132,7 +132,6 @@ struct ExpandArgs {
   int64_t rows_cap;             // expanded rows per (sequence, head)
   int32_t batch, n_h, chunk, max_len;  // max_len: host bound on prefix + chunk
   int32_t lo_rows;              // lo parts are written for rows below this only
-  int32_t heads_per_wg;         // heads per expansion workgroup (8, 16 or 32; set at launch)
   // paged cache, as SplitArgs (block_table != NULL)
   const int32_t* block_table;
   int64_t num_pages;

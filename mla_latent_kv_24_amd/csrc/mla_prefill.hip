@@ -77,8 +77,8 @@ __global__ __launch_bounds__(64 * XB_WAVES, 1) void expand_kv_kernel(ExpandArgs 
   // ranges streaming from the memory-side cache: with the head ranges a
   // multiple of 8, XCD x takes ranges x, x + 8, ... over all row blocks; with
   // 8 / gy XCDs per range (gy ranges), each takes a share of the row blocks.
-  const int nhw = a.heads_per_wg;  // heads h0 .. h0 + nhw - 1, one head group at a time
   const int gx = gridDim.x, gy = gridDim.y;
+  const int nhw = a.n_h / gy;  // heads h0 .. h0 + nhw - 1 (8, 16 or 32)
   int rb = blockIdx.x, hg = blockIdx.y;
   if (gy % 8 == 0) {
     const int k = blockIdx.x + gx * blockIdx.y;
@@ -581,7 +581,6 @@ hipError_t launch_prefill_unabsorbed(const ExpandArgs& e_in, const PrefillArgs& 
   int hpw = 1;
   for (int c = 4; c >= 2; c /= 2)
     if (nhg % c == 0 && nrb * (nhg / c) * e.batch >= 256) { hpw = c; break; }
-  e.heads_per_wg = XB_HEADS * hpw;
   const dim3 g1(static_cast<unsigned>(nrb), nhg / hpw, e.batch);
   if (e.block_table)
     expand_kv_kernel<true><<<g1, 64 * XB_WAVES, 0, st>>>(e);
