@@ -101,6 +101,11 @@ __global__ __launch_bounds__(64 * XB_WAVES, 1) void expand_kv_kernel(ExpandArgs 
   int64_t L = prefix + a.chunk;
   L = min(L, a.stride);
   if (row0 >= L) return;  // uniform over the workgroup
+  // lo_rows = precise_below + PQ (or INT_MAX when every workgroup is hi + lo).
+  // A sequence whose first query already sees precise_below keys has no
+  // hi + lo workgroup, so nothing reads its lo parts
+  const bool any_precise = a.lo_rows == 0x7fffffff || prefix + 1 + PQ < a.lo_rows;
+  const int64_t lo_rows = any_precise ? a.lo_rows : 0;
   const int nrows = static_cast<int>(min(static_cast<int64_t>(XB_ROWS), L - row0));
   auto row_at = [&](int64_t r, bool& ok) {
     return cache_row_addr<PAGED>(a.cache, a.block_table, a.num_pages, a.bt_stride, a.page_shift, a.stride, b, r,
@@ -206,8 +211,8 @@ __global__ __launch_bounds__(64 * XB_WAVES, 1) void expand_kv_kernel(ExpandArgs 
     // lane pair (l, l + 32)'s halves, after which lane g holds run q: the 8
     // consecutive dims 8 (2q + g) .. +7, stored as 16 B: hi at element d, lo
     // at element 256 + d of the expanded row.  Only the hi + lo attention
-    // workgroups read lo, and their keys all lie below lo_rows; past it the
-    // lo parts are left unwritten.
+    // workgroups read lo, and their keys all lie below lo_rows; past it (and
+    // in a sequence without such workgroups) the lo parts are left unwritten.
     uint16_t* xh = static_cast<uint16_t*>(a.x) + (static_cast<int64_t>(b) * a.n_h + h) * a.rows_cap * ROWE;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(64 * XB_WAVES, 1) void expand_kv_kernel(ExpandArgs 
               lw[e] = pack_bf16x2(x0 - __uint_as_float(hw[e] << 16), x1 - __uint_as_float(hw[e] & 0xffff0000u));
             }
             *reinterpret_cast<uint4*>(xr + d) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            if (row0 + r < a.lo_rows)
+            if (row0 + r < lo_rows)
               *reinterpret_cast<uint4*>(xr + 2 * D_H + d) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
           }
         }
