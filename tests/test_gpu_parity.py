@@ -580,6 +580,42 @@ def test_prefill_unabsorbed_two_sequences(api):
         assert rel_err(got[b], ref) < TOL["bf16"]
 
 
+# The expansion gives a workgroup 8, 16 or 32 heads (as many as still leave
+# 256 workgroups) and maps workgroups to XCDs by head range.  The small shapes
+# above take 8 heads and the full v2_prefill 32; these batches take 16 (batch
+# 2, 16 row blocks) and 32 over an odd count of row blocks (batch 4, 17 row
+# blocks: the plain mapping), with prefixes on both sides of the hi + lo
+# threshold's row range.
+@pytest.mark.parametrize("prefixes", [(1800, 1750), (1800, 1750, 1900, 1650)])
+def test_prefill_unabsorbed_head_ranges(api, prefixes):
+    import dataclasses
+    C, n_h, dtype = 200, 128, "bf16"
+    pinps = [W.make_prefill_inputs(W.scaled(W.WORKLOADS["v2_prefill"], seq_len=p + C, prefill_chunk=C,
+                                            seed=11 + b)) for b, p in enumerate(prefixes)]
+    w_uk, w_uv = pinps[0].w_uk, pinps[0].w_uv
+    pinps = [dataclasses.replace(pi, w_uk=w_uk, w_uv=w_uv) for pi in pinps]
+    stride = max(prefixes) + C
+    d = api.dims(n_h)
+    cache = torch.full((len(prefixes) * stride, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
+    for b, pi in enumerate(pinps):
+        tot = pi.prefix + pi.chunk
+        api.append_kv(d, dev(pi.c_kv, dtype), dev(pi.k_raw, dtype),
+                      torch.arange(tot, dtype=torch.int32, device="cuda"),
+                      torch.arange(tot, dtype=torch.int64, device="cuda") + b * stride, cache)
+    q_c = dev(np.stack([pi.q_c for pi in pinps]), dtype)
+    q_r = dev(np.stack([pi.q_r for pi in pinps]), dtype)
+    out = torch.empty((len(prefixes), C, n_h, 128), dtype=torch.float32, device="cuda")
+    plen = torch.tensor(prefixes, dtype=torch.int32, device="cuda")
+    api.prefill_unabsorbed(d, q_c, q_r, cache, stride, plen, max(prefixes), dev(w_uk, dtype), dev(w_uv, dtype), out)
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    queries, heads = [0, 1, 63, 100, C - 1], [0, 7, 8, 15, 16, 31, 64, 127]
+    for b, pi in enumerate(pinps):
+        ref = oracle_prefill(pi, queries, heads)
+        g = got[b][queries][:, heads]
+        assert rel_err(g, ref) < TOL["bf16"], (prefixes, b, rel_err(g, ref))
+
+
 # ------------------------------------------------------- long-context RoPE
 YARN = dict(yarn_factor=40.0)            # DeepSeek-V2's scale over 4,096 pretraining positions
 # YaRN's temperature multiplies every logit by (0.1 ln 40 + 1)^2 = 1.87 and
