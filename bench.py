@@ -42,14 +42,14 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def pmc_traffic(workload):
+def pmc_traffic(workload, splits):
     """HBM bytes per launch of the attention kernel on `workload` from the
     committed rocprofv3 --pmc summary, if it was taken on the current kernel
-    source (else None)."""
+    source and at the same split count (else None)."""
     if not os.path.exists(PMC_FILE):
         return None
     d = json.load(open(PMC_FILE)).get(workload)
-    if not d or d.get("kernel_sha") != kernel_hash():
+    if not d or d.get("kernel_sha") != kernel_hash() or d.get("splits") != splits:
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -398,7 +398,7 @@ def main():
     # 16-head group per workgroup at n_h = 16
     attn_kernel = "splitkv_{}{}_kernel".format("fp8_" if args.fp8_cache else "", "wide" if n_h == 128 else "h16")
     # the committed counter summary covers the contiguous kernel instance only
-    traffic = None if (args.page_rows or args.fp8_cache) else pmc_traffic(args.workload)
+    traffic = None if (args.page_rows or args.fp8_cache) else pmc_traffic(args.workload, st.splits)
     line = {
         "metric": METRIC,
         "value": round(value, 1),

@@ -34,7 +34,12 @@ mla_status hip_status(hipError_t e, const char* where) {
 
 constexpr int kNumCUs = 256;     // MI355X compute units (the plan is device independent)
 constexpr int kMinSplitRows = 256;
-constexpr int kMaxSplitRows = 4096;  // rows per split at most (MFMA paths)
+// rows per split at most (MFMA paths, fewer than four rounds of queries): a
+// sweep of the ragged 16-head batch (128 sequences of U[1, 32768] rows) gave
+// its attention 496 / 472 / 480 / 469 / 492 us at 8 / 10 / 12 / 14 / 16
+// splits (Infinity Cache flushed), the combine 17.5 / 19.8 / 20.4 / 22.0 /
+// 25.5 us; 3,328 rows give it 10
+constexpr int kMaxSplitRows = 3328;
 constexpr int kMaxSplits = 65535;
 // unabsorbed prefill: a workgroup whose first query sees fewer keys than this
 // takes the hi + lo products

@@ -129,10 +129,10 @@ def test_split_plan_covers_every_row():
     assert api.num_splits(d, api.BF16, 4096, 8192) == 1          # 16 rounds of queries: no cap
     assert api.num_splits(api.dims(16), api.BF16, 1, 100) == 1
     assert api.num_splits(api.dims(16), api.BF16, 32, 4096) == 8   # one round of 256
-    assert api.num_splits(api.dims(16), api.BF16, 128, 32768) == 8  # ragged: 4096-row cap
+    assert api.num_splits(api.dims(16), api.BF16, 128, 32768) == 10  # ragged: 3,328-row cap
     for B, L in ((1, 100), (3, 5000), (64, 8192), (128, 32768), (4, 131072), (4096, 8192)):
         S = api.num_splits(d, api.BF16, B, L)
-        assert api.split_rows(L, S) <= 4096 or B >= 1024
+        assert api.split_rows(L, S) <= 3328 or B >= 1024
 
 
 def test_paged_validation():
@@ -278,8 +278,8 @@ def test_split_plan_of_the_precise_path():
     assert api.num_splits(d, api.BF16, 64, 2048) == 1     # grouped: 64 x 1 x 8 = 512 workgroups
     assert api.num_splits(d, api.BF16, 8, 3000) == 4      # grouped: 8 x 4 x 8 = 256
     y = api.dims(128, yarn_factor=40.0)
-    assert api.num_splits(y, api.BF16, 64, 8192) == 2     # grouped; the 4,096-row cap sets it
-    assert api.num_splits(y, api.BF16, 4, 131072) == 32   # 131,072 rows / 4,096
+    assert api.num_splits(y, api.BF16, 64, 8192) == 3     # grouped; the 3,328-row cap sets it
+    assert api.num_splits(y, api.BF16, 4, 131072) == 40   # 131,072 rows / 3,328
 
 
 def test_noalloc_decode_validates_before_touching_the_device():
