@@ -6,6 +6,8 @@
 // is the value up-projection moved outside the weighted sum
 // (jiphyeonjeon.kr DeepSeek-V2 review, section 2: sum_j a_ij U^V_i c_j =
 // U^V_i sum_j a_ij c_j).
+#include <algorithm>
+
 #include "mla_common.h"
 
 namespace mla {
@@ -15,7 +17,8 @@ constexpr int CMB_MAX_SPLITS = 128;   // weights staged in LDS for the MFMA path
 constexpr int ZSTRIDE = 1040;        // bytes per staged z row (512 bf16 + 16 B pad)
 
 // ------------------------------------------------------------------------
-// bf16 MFMA path.  Grid (head, block of qb <= 32 queries); 4 waves, wave w owns
+// bf16 MFMA path.  Grid (head, nblk blocks of qb <= 32 queries, taken in turn
+// with W^UV loaded once); 4 waves, wave w owns
 // the 32 output dims d = 32w..32w+31.  z is combined in fp32, optionally
 // written out, then split into bf16 hi + lo parts (z = hi + lo to ~2^-16
 // relative) so the 32x32x16 MFMA lift keeps fp32-level accuracy:
@@ -27,19 +30,18 @@ constexpr int ZSTRIDE = 1040;        // bytes per staged z row (512 bf16 + 16 B 
 // thread's first two row chunks of partials are requested, then the wave's
 // whole W^UV slice (32 rows x 512 columns, 128 VGPRs), which arrives while the
 // partials are combined; two batches of two row chunks stay in flight (one
-// combined while the next lands).  With more splits (G = 16) W^UV comes first
-// and the partial loads of G splits x 16 / G row chunks are in flight
-// together.
+// combined while the next lands).  With more splits (G = 16), or one (G = 1:
+// a prefill chunk, one split per query), W^UV comes first and the partial
+// loads of G splits x 16 / G row chunks are in flight together.
 // ------------------------------------------------------------------------
-template <int G>
-__global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int qb) {
+template <int G, bool MULTI>
+__global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int qb, int nblk) {
   __shared__ float wts[32][CMB_MAX_SPLITS];
   __shared__ __attribute__((aligned(16))) uint8_t zhi[32 * ZSTRIDE];
   __shared__ __attribute__((aligned(16))) uint8_t zlo[32 * ZSTRIDE];
   constexpr int KS = D_C / 16;  // MFMA k-steps of the lift
   constexpr int UB = 16 / G;    // row chunks per batch
-  const int h = blockIdx.x, n0 = blockIdx.y * qb;
-  const int rows = min(qb, a.n_q - n0);
+  const int h = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int S = a.num_splits;
 
@@ -52,6 +54,14 @@ __global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int
 #pragma unroll
     for (int s = 0; s < KS; ++s) bw[s] = *reinterpret_cast<const u32x4*>(wrow + 16 * s);
   };
+
+  // query blocks blockIdx.y * nblk .. +nblk-1 in turn; W^UV stays in registers
+  // (MULTI = false: one block, the decode step's kernel as it was without the loop)
+  for (int blk = 0; blk < (MULTI ? nblk : 1); ++blk) {
+  const int n0 = (blockIdx.y * nblk + blk) * qb;
+  if (n0 >= a.n_q) break;  // uniform over the workgroup
+  const int rows = min(qb, a.n_q - n0);
+  const bool first = !MULTI || blk == 0;
 
   // ---- split weights exp(lse_s - LSE): thread (row r, phase p) covers splits
   // p, p+8, ...; max and sum are reduced over the row's 8 adjacent lanes
@@ -125,7 +135,7 @@ __global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int
       }
     };
     load_b(0, va);
-    load_w();
+    if (first) load_w();
 #pragma unroll
     for (int j0 = 0; j0 < 16; j0 += 2 * PB) {
       if (j0 + PB < 16) load_b(j0 + PB, vb);
@@ -134,7 +144,7 @@ __global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int
       fold_b(j0 + PB, vb);
     }
   } else {
-    load_w();
+    if (first) load_w();
     for (int j0 = 0; j0 < 16; j0 += UB) {
       if (tid + 256 * j0 >= units) break;
       f32x4 acc[UB];
@@ -181,6 +191,8 @@ __global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int
   for (int j = 0; j < 16; ++j) {
     const int r = 8 * (j >> 2) + 4 * g + (j & 3);
     if (r < rows) a.out[(static_cast<int64_t>(n0 + r) * a.n_h + h) * D_H + d] = acc[j];
+  }
+  if constexpr (MULTI) __syncthreads();  // the next block rewrites the weights and the staged z
   }
 }
 
@@ -231,11 +243,26 @@ hipError_t launch_combine(const CombineArgs& a, int bf16, hipStream_t st) {
     // that holds the head's blocks; the partials once in all)
     int qb = 32;
     while (qb > 1 && static_cast<int64_t>(a.n_h) * ((a.n_q + qb - 1) / qb) < 256) qb >>= 1;
-    const dim3 grid(a.n_h, (a.n_q + qb - 1) / qb);
-    if (a.num_splits <= 4)
-      combine_mfma_kernel<4><<<grid, 256, 0, st>>>(a, qb);
-    else
-      combine_mfma_kernel<16><<<grid, 256, 0, st>>>(a, qb);
+    // many query blocks (a prefill chunk): a workgroup takes several in turn,
+    // so that W^UV is read once per workgroup for all of them, keeping about
+    // four rounds of the 256 CUs
+    const int64_t blocks = (a.n_q + qb - 1) / qb;
+    const int nblk = static_cast<int>(std::max<int64_t>(1, blocks * a.n_h / 1024));
+    const dim3 grid(a.n_h, static_cast<unsigned>((blocks + nblk - 1) / nblk));
+    if (nblk > 1) {
+      if (a.num_splits == 1)
+        combine_mfma_kernel<1, true><<<grid, 256, 0, st>>>(a, qb, nblk);
+      else if (a.num_splits <= 4)
+        combine_mfma_kernel<4, true><<<grid, 256, 0, st>>>(a, qb, nblk);
+      else
+        combine_mfma_kernel<16, true><<<grid, 256, 0, st>>>(a, qb, nblk);
+    } else if (a.num_splits == 1) {
+      combine_mfma_kernel<1, false><<<grid, 256, 0, st>>>(a, qb, nblk);
+    } else if (a.num_splits <= 4) {
+      combine_mfma_kernel<4, false><<<grid, 256, 0, st>>>(a, qb, nblk);
+    } else {
+      combine_mfma_kernel<16, false><<<grid, 256, 0, st>>>(a, qb, nblk);
+    }
   } else if (bf16) {
     combine_generic_kernel<uint16_t><<<dim3(a.n_q, a.n_h), 256, 0, st>>>(a);
   } else {
