@@ -45,6 +45,20 @@ __device__ __forceinline__ void pf_mfma_vv(f32x16& acc, const bf16x8& a, const b
 }
 __device__ __forceinline__ void pf_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
+// s_waitcnt for the tile ring: `later` (0..K) tiles of L DMA chunks each may
+// stay in flight (later is wave-uniform: scalar branches)
+template <int L, int K>
+__device__ __forceinline__ void vm_wait_tiles(int64_t later) {
+  if constexpr (K == 0) {
+    vm_wait<0>();
+  } else {
+    if (later >= K)
+      vm_wait<K * L>();
+    else
+      vm_wait_tiles<L, K - 1>(later);
+  }
+}
+
 constexpr int XB_ROWS = 128;  // rows per expansion workgroup
 constexpr int XB_HEADS = 8;   // heads per head group (a workgroup takes 1, 2 or 4 groups)
 constexpr int XB_WAVES = 8;   // expansion waves (two per SIMD)
@@ -269,9 +283,19 @@ __global__ __launch_bounds__(64 * XB_WAVES, 1) void expand_kv_kernel(ExpandArgs 
 // ------------------------------------------------------------------------
 template <bool PRECISE>
 __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillArgs a) {
+  // ring of NBUF tiles, AHEAD = NBUF - 1 of them requested ahead of the one in
+  // use (the hi-only layout's 20 KB tiles would leave room for eight, which
+  // measured no faster than four)
   constexpr int NBUF = 4;
-  constexpr int LOADS = TILE_BYTES / (16 * 256);  // 9 DMA chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * TILE_BYTES];
+  constexpr int AHEAD = NBUF - 1;
+  // LDS row: the expanded row as stored (1,152 B) for hi + lo, or its hi
+  // parts and k^R alone (k^C hi, v^C hi, k^R: 640 B) for the hi-only instance
+  constexpr int RB = PRECISE ? ROWB : 640;
+  constexpr int NCH = RB / 16;                    // 16-B chunks per LDS row
+  constexpr int TB = TILE * RB;                   // LDS bytes per tile
+  constexpr int LOADS = TB / (16 * 256);          // DMA chunks per thread per tile: 9 or 5
+  static_assert(TB == LOADS * 16 * 256, "a tile must split evenly over the 256 DMA threads");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * TB];
 
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -303,8 +327,7 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
   // the one that matches its first query's key count (uniform)
   if ((prefix + q0 + 1 < a.precise_below) != PRECISE) return;
 
-  // ---- tile DMA (as in the decode kernels): LDS chunk f = tid + 256 i of a
-  // tile receives global chunk (t, p ^ swz(t)), (t, p) = (f / 72, f % 72)
+  // ---- tile DMA (as in the decode kernels), into the LDS row layout above
   const uint8_t* xh = static_cast<const uint8_t*>(a.x) + (static_cast<int64_t>(b) * a.n_h + h) * a.rows_cap * ROWB;
   const uint64_t gaddr = reinterpret_cast<uint64_t>(xh);
   const uint32_t lds_w = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
@@ -318,30 +341,33 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
                       __builtin_amdgcn_readfirstlane(static_cast<int>(rows * ROWB)), 0x00020000};
     return rs;
   };
-  // A thread's i-th chunk of a tile: the global chunk index, or NO_CHUNK for a
-  // lo chunk (32..63 of the 72) that the hi-only instance does not fetch: its
-  // lanes take an offset past the buffer range, which reads zeros without
-  // touching memory and keeps every wave's load count fixed.
-  constexpr uint32_t NO_CHUNK = 0xffffu;
+  // A thread's i-th chunk of a tile: LDS chunk f = tid + 256 i, row t = f / NCH,
+  // slot p = f % NCH, holds the row's chunk p ^ swz(t); in the hi-only layout
+  // slots 32..39 hold k^R, the expanded row's chunks 64..71 (its lo chunks
+  // 32..63 are never fetched).  Both layouts keep a row stride of 32 mod 64
+  // dwords, so the swizzle spreads the banks as in the decode kernels.
   auto issue_one = [&](const i32x4& rs, uint32_t dst, int i, uint32_t c) {
-    dma16(dst + 4096u * i, c == NO_CHUNK ? 0x7ffffff0 : static_cast<int>(c << 4), rs, 0);
+    dma16(dst + 4096u * i, static_cast<int>(c << 4), rs, 0);
   };
-  auto tile_dst = [&](int64_t it) { return lds_w + static_cast<uint32_t>((it & (NBUF - 1)) * TILE_BYTES); };
+  auto tile_dst = [&](int64_t it) { return lds_w + static_cast<uint32_t>((it & (NBUF - 1)) * TB); };
   uint32_t ch[LOADS];  // kept in registers (the DMA waves have room for them)
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int f = tid + 256 * i;
-    const int t = f / 72, p = f - 72 * t;
+    const int t = f / NCH, p = f - NCH * t;
     const int q = p ^ swz(t);
-    ch[i] = (!PRECISE && q >= 32 && q < 64) ? NO_CHUNK : static_cast<uint32_t>(72 * t + q);
+    ch[i] = static_cast<uint32_t>(72 * t + ((!PRECISE && q >= 32) ? q + 32 : q));
   }
-  if (dma_wave) {
-    for (int64_t it = 0; it < min(ntiles, static_cast<int64_t>(3)); ++it) {
+  // the first three tiles now, the rest of the ring once the queries are in
+  auto issue_tiles = [&](int64_t t0, int64_t t1) {
+    if (!dma_wave) return;
+    for (int64_t it = t0; it < min(ntiles, t1); ++it) {
       const i32x4 rs = tile_rsrc(it);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) issue_one(rs, tile_dst(it), i, ch[i]);
     }
-  }
+  };
+  issue_tiles(0, 3);
 
   // ---- score B operands per query block k: q^C (8 k-steps), RoPE(q^R) hi and
   // lo (4 k-steps).  Lanes past the chunk take its last query (never stored).
@@ -376,18 +402,22 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
     }
   }
   vm_wait<0>();  // queries and the first tiles resident: the loop carries no compiler waits
+  issue_tiles(3, AHEAD);
 
   // ---- per-lane LDS operand offsets (as in the 32-head decode kernel)
   int sc_off[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) sc_off[m] = l32 * ROWB + 16 * ((2 * m + g32) ^ swz(l32));
+  for (int m = 0; m < 4; ++m) sc_off[m] = l32 * RB + 16 * ((2 * m + g32) ^ swz(l32));
   int tr_off[2][2];
   {
     const int hf = (l >> 4) & 1;
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int p = 0; p < 2; ++p) tr_off[r][p] = tile_off(4 * g32 + (j16 >> 2) + 8 * r, 32 * p + 16 * hf + 4 * (j16 & 3));
+      for (int p = 0; p < 2; ++p) {
+        const int t = 4 * g32 + (j16 >> 2) + 8 * r, e = 32 * p + 16 * hf + 4 * (j16 & 3);
+        tr_off[r][p] = t * RB + 16 * ((e >> 3) ^ swz(t)) + 2 * (e & 7);  // element e of LDS row t
+      }
   }
 
   f32x16 oacc[PF_QBW][4];  // O^T of query block k, dims 32 db .. +31
@@ -406,15 +436,18 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
   const float qscale = a.qscale;
 
   // One tile for this wave's two query blocks; PRECISE adds the lo products.
-  // dma: this wave moves tile it+3 (its nine chunks go out one after each of
-  // the first nine score products)
+  // dma: this wave moves tile it+AHEAD (its LOADS chunks go out one after each
+  // of the first score products)
   auto tile = [&](const uint8_t* buf, int64_t it, bool dma) {
+    // k-step s reads elements 16 s .. +15 (128-B group s >> 2 of the stored
+    // row); in the hi-only layout k^R's groups 8, 9 sit at 4, 5
     auto kread = [&](int s) -> bf16x8 {
-      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(buf + sc_off[s & 3] + 128 * (s >> 2)));
+      const int grp = (!PRECISE && s >= 32) ? (s >> 2) - 4 : (s >> 2);
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(buf + sc_off[s & 3] + 128 * grp));
     };
     // value A: 32 columns of the expanded row from column block cbg, keys of half u
     auto vread = [&](int cbg, int u) -> bf16x8 {
-      const uint8_t* bu = buf + 128 * (cbg >> 1) + 16 * u * ROWB;
+      const uint8_t* bu = buf + 128 * (cbg >> 1) + 16 * u * RB;
       return cat(tr_read(bu + tr_off[0][cbg & 1]), tr_read(bu + tr_off[1][cbg & 1]));
     };
     // ---- score: elements 0..127 (k^C hi: k-steps 0..7), 256..383 (k^C lo:
@@ -429,7 +462,7 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
     };
     f32x16 sacc[PF_QBW];
     i32x4 rs3 = {0, 0, 0, 0};
-    if (dma) rs3 = tile_rsrc(it + 3);
+    if (dma) rs3 = tile_rsrc(it + AHEAD);
     {
       bf16x8 kb[KPF];
 #pragma unroll
@@ -452,7 +485,7 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
             if constexpr (PRECISE) pf_mfma_qa(sacc[k], kv, qrl[k][ks - 32]);
           }
         }
-        if (dma && i < LOADS) issue_one(rs3, tile_dst(it + 3), i, ch[i]);
+        if (dma && i < LOADS) issue_one(rs3, tile_dst(it + AHEAD), i, ch[i]);
       }
     }
     // the value operands (v^C hi) do not depend on P: their transpose reads
@@ -525,25 +558,21 @@ __global__ __launch_bounds__(64 * PF_WAVES, 1) void prefill_attn_kernel(PrefillA
   };
 
   for (int64_t it = 0; it < ntiles; ++it) {
-    // tile `it` must have landed: the loads of the (up to 2) later tiles may stay in flight
-    if (it + 2 < ntiles)
-      vm_wait<2 * LOADS>();
-    else if (it + 1 < ntiles)
-      vm_wait<LOADS>();
-    else
-      vm_wait<0>();
+    // tile `it` must have landed: the loads of the (up to AHEAD - 1) later
+    // tiles may stay in flight
+    vm_wait_tiles<LOADS, AHEAD - 1>(min(static_cast<int64_t>(AHEAD - 1), ntiles - 1 - it));
     __syncthreads();
-    // every wave passed this barrier, so buffer (it+3)&3 == (it-1)&3 is free:
+    // every wave passed this barrier, so buffer (it+AHEAD) % NBUF == (it-1) % NBUF is free:
     // its refill goes out between this tile's score products (or at once
     // from a wave whose queries have no keys left)
-    const bool dma = dma_wave && it + 3 < ntiles;
-    const uint8_t* buf = smem + (it & (NBUF - 1)) * TILE_BYTES;
+    const bool dma = dma_wave && it + AHEAD < ntiles;
+    const uint8_t* buf = smem + (it & (NBUF - 1)) * TB;
     if (it < my_tiles) {
       tile(buf, it, dma);
     } else if (dma) {
-      const i32x4 rs = tile_rsrc(it + 3);
+      const i32x4 rs = tile_rsrc(it + AHEAD);
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) issue_one(rs, tile_dst(it + 3), i, ch[i]);
+      for (int i = 0; i < LOADS; ++i) issue_one(rs, tile_dst(it + AHEAD), i, ch[i]);
     }
   }
 
