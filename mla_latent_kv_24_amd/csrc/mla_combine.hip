@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int
   };
 
   // query blocks blockIdx.y * nblk .. +nblk-1 in turn; W^UV stays in registers
-  // (MULTI = false: one block, the decode step's kernel as it was without the loop)
+  // (MULTI = false: one block and no loop-end barrier, as the decode steps launch it)
   for (int blk = 0; blk < (MULTI ? nblk : 1); ++blk) {
   const int n0 = (blockIdx.y * nblk + blk) * qb;
   if (n0 >= a.n_q) break;  // uniform over the workgroup
