@@ -55,6 +55,20 @@ __global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int
     for (int s = 0; s < KS; ++s) bw[s] = *reinterpret_cast<const u32x4*>(wrow + 16 * s);
   };
 
+  // one split over several blocks: a block's 16 row chunks per thread are
+  // requested while the previous block is lifted (z_part[n][0][h][:])
+  f32x4 v1[16];
+  auto load1 = [&](int nb, int rb, f32x4 (&v)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int u = tid + 256 * i;
+      v[i] = (u < rb * (D_C / 4))
+                 ? *reinterpret_cast<const f32x4*>(a.z_part + (static_cast<int64_t>(nb + (u >> 7)) * a.n_h + h) * D_C +
+                                                   4 * (u & 127))
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
   // query blocks blockIdx.y * nblk .. +nblk-1 in turn; W^UV stays in registers
   // (MULTI = false: one block and no loop-end barrier, as the decode steps launch it)
   for (int blk = 0; blk < (MULTI ? nblk : 1); ++blk) {
@@ -108,7 +122,24 @@ __global__ __launch_bounds__(256, 1) void combine_mfma_kernel(CombineArgs a, int
     *reinterpret_cast<uint2*>(zlo + r * ZSTRIDE + 2 * c4) =
         make_uint2(lo4[0] | (static_cast<uint32_t>(lo4[1]) << 16), lo4[2] | (static_cast<uint32_t>(lo4[3]) << 16));
   };
-  if (G == 4 && S <= G) {
+  if constexpr (G == 1 && MULTI) {
+    if (first) {
+      load1(n0, rows, v1);
+      load_w();
+    }
+    f32x4 cur[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cur[i] = v1[i];
+    const int n1 = n0 + qb;
+    if (blk + 1 < nblk && n1 < a.n_q) load1(n1, min(qb, a.n_q - n1), v1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int u = tid + 256 * i;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc += wts[(u >> 7) & 31][0] * cur[i];
+      emit(u, acc);
+    }
+  } else if (G == 4 && S <= G) {
     // all splits of a unit in one batch of PB units; two batches in flight
     constexpr int PB = 2;
     f32x4 va[PB][G], vb[PB][G];

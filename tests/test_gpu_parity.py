@@ -274,7 +274,10 @@ def test_decode_zero_length_on_device(pipeline, name, n_h, opts):
 # ------------------------------------------------------ A4 + A5 combine/lift
 @pytest.mark.parametrize("dtype,n_h,S,n_q", [("bf16", 128, 4, 45), ("bf16", 16, 1, 45), ("bf16", 16, 64, 45),
                                              ("f32", 16, 3, 45), ("bf16", 128, 64, 4), ("bf16", 128, 5, 45),
-                                             ("bf16", 128, 17, 33), ("bf16", 16, 16, 32)])
+                                             ("bf16", 128, 17, 33), ("bf16", 16, 16, 32),
+                                             # 21 blocks of 32 queries, two per workgroup (the last
+                                             # workgroup takes one, the last block 10 queries)
+                                             ("bf16", 128, 1, 650), ("bf16", 128, 2, 650)])
 def test_combine_project(api, dtype, n_h, S, n_q):
     Z = np.random.default_rng(40).standard_normal((n_q, S, n_h, 512)).astype(np.float32)
     lse = (np.random.default_rng(41).standard_normal((n_q, S, n_h)) * 3).astype(np.float32)
