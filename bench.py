@@ -239,6 +239,8 @@ def main():
     ap.add_argument("--fp8-cache", action="store_true",
                     help="run the decode step over the FP8 latent cache (E4M3 codes + per-row scale, "
                          "bf16 RoPE keys: 644 B per row)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="split count of the attention (default: the library's plan)")
     ap.add_argument("--page-rows", type=int, default=0,
                     help="run the decode step over a paged cache of pages of this many rows, "
                          "handed out in a seeded random order (0: contiguous sequence slots)")
@@ -262,6 +264,11 @@ def main():
     log(f"[bench] generating {w.name} ...")
     inp = W.make_decode_inputs(w)
     st = DecodeState(inp, page_rows=args.page_rows or None, fp8=args.fp8_cache)
+    if args.splits:
+        # an explicit split count instead of the plan's (partials sized to match)
+        st.splits = args.splits
+        st.z_part = torch.empty((st.batch, st.splits, w.n_h, 512), dtype=torch.float32, device="cuda")
+        st.lse_part = torch.empty((st.batch, st.splits, w.n_h), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     tokens = int(inp.seq_lens.sum())
     layout = f"paged ({args.page_rows}-row pages)" if args.page_rows else "contiguous"
